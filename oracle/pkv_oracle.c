@@ -1,0 +1,509 @@
+/*
+ * pkv_oracle.c - plain, slow CPU oracle for the paged int8 ("C8") KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  It shares no code, header,
+ * table or helper with the GPU library; the two agree only because both
+ * implement the same definitions, stated below.
+ *
+ * Sources (web pages; sections named as printed on them):
+ *  [P1] "Mojo Opset" README (XPU-Forces/mojo_opset), "Op List" table:
+ *       MojoStorePagedKVCache, MojoPagedDecodeGQA, MojoDequant, MojoDynamicQuant.
+ *  [P2] PR #379 "feat: [MLU] add mlu experimental ops; fix post norm bug",
+ *       its code-review summary and the four review passes (Must fix /
+ *       Suggestions / Notes) on MojoStorePagedKVCacheC8 and
+ *       MojoDequantFromPagedKVCache.
+ *
+ * Definitions implemented (each function repeats the one it follows):
+ *  - store, per-token mode: dynamic symmetric int8 quantization (the
+ *    MojoDynamicQuant row of [P1]) with scale = absmax/127 per token and KV
+ *    head, q = clamp(round_half_even(x/scale), -128, 127) ([P2] pass 2 and
+ *    pass 3 Notes give round(x/scale).clamp(-128,127); torch.round rounds half
+ *    to even), the division done in fp32 ([P2] pass 4, Must fix: cast to
+ *    float32 before dividing).
+ *  - store, per-block mode: one fp32 scale per (block, KV head) ([P2] passes
+ *    1 and 2 name a per-block scale layout for quant_mode != 0).
+ *  - dequant: fp32 product of the int8 code and its scale, then bf16 ([P2]
+ *    pass 1 and 4 Must fix: the multiply must run in fp32); rows written at a
+ *    per-sequence offset that defaults to the exclusive prefix sum of the
+ *    context lengths ([P2] pass 1 Must fix on context_seq_offset).
+ *  - decode: grouped-query attention of one new query per sequence over the
+ *    paged cache ([P1] MojoPagedDecodeGQA), generalised to a causal chunk of
+ *    q_len new queries, accumulated in fp64 over the dequantized values.
+ *
+ * Cache layout (the boundary contract; element (block, head, slot, channel)):
+ *   K  [NB][Hkv][BS][D]   int8, or bf16 in mode 2
+ *   V  [NB][Hkv][D][BS]   int8, or bf16 in mode 2 (channel-major page)
+ *   scales mode 0: [NB][Hkv][BS] fp32;  mode 1: [NB][Hkv] fp32;  mode 2: none
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define MODE_PER_TOKEN 0
+#define MODE_PER_BLOCK 1
+#define MODE_BF16 2
+
+/* ------------------------------------------------------------------------- */
+/* bf16 <-> floating point                                                    */
+/* ------------------------------------------------------------------------- */
+
+static float bf16_to_float(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16; /* bf16 is the upper half of an fp32 */
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Nearest bf16 to x, ties to the even significand.  Written from the
+ * definition: find the bf16 grid spacing at x, take the two neighbours on the
+ * grid and keep the nearer one.  Every step is exact in double. */
+uint16_t oracle_bf16_round(double x)
+{
+    if (isnan(x))
+        return 0x7fc0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);              /* a in [2^(e-1), 2^e) */
+    int E = e - 1;             /* unbiased exponent of a */
+    if (E < -126)
+        E = -126;              /* subnormals share the smallest normal spacing */
+    double spacing = ldexp(1.0, E - 7); /* 8 significant bits */
+    double n = a / spacing;    /* exact: power-of-two division */
+    double lo = floor(n);
+    double rem = n - lo;
+    double k = lo;
+    if (rem > 0.5 || (rem == 0.5 && fmod(lo, 2.0) != 0.0))
+        k = lo + 1.0;
+    double r = k * spacing;
+    const double max_bf16 = ldexp(255.0, 127 - 7); /* (2 - 2^-7) * 2^127 */
+    if (r > max_bf16)
+        return sign | 0x7f80;   /* rounds beyond the largest finite: infinity */
+    float rf = (float)r;        /* exact: r is on the bf16 grid */
+    uint32_t u;
+    memcpy(&u, &rf, sizeof u);
+    return sign | (uint16_t)(u >> 16);
+}
+
+/* ------------------------------------------------------------------------- */
+/* layout helpers                                                             */
+/* ------------------------------------------------------------------------- */
+
+typedef struct {
+    int mode, nb, hkv, bs, d;
+    void *k, *v;
+    float *ks, *vs;
+} cache_t;
+
+static int64_t k_index(const cache_t *c, int64_t blk, int h, int slot, int ch)
+{
+    return ((blk * c->hkv + h) * c->bs + slot) * (int64_t)c->d + ch;
+}
+
+static int64_t v_index(const cache_t *c, int64_t blk, int h, int slot, int ch)
+{
+    return ((blk * c->hkv + h) * (int64_t)c->d + ch) * c->bs + slot;
+}
+
+static int64_t tok_scale_index(const cache_t *c, int64_t blk, int h, int slot)
+{
+    return (blk * c->hkv + h) * c->bs + slot;
+}
+
+static int64_t blk_scale_index(const cache_t *c, int64_t blk, int h)
+{
+    return blk * c->hkv + h;
+}
+
+/* ------------------------------------------------------------------------- */
+/* quantization primitives                                                    */
+/* ------------------------------------------------------------------------- */
+
+/* q = clamp(round_half_even(fl32(x / s)), -128, 127); q = 0 when s == 0. */
+static int8_t quant_one(float x, float s)
+{
+    if (s == 0.0f)
+        return 0;
+    float r = nearbyintf(x / s); /* default rounding mode: to nearest, ties even */
+    if (r > 127.0f)
+        r = 127.0f;
+    if (r < -128.0f)
+        r = -128.0f;
+    return (int8_t)r;
+}
+
+/* fl32(absmax / 127) */
+static float absmax_scale(float absmax)
+{
+    return absmax / 127.0f;
+}
+
+/* ------------------------------------------------------------------------- */
+/* store                                                                      */
+/* ------------------------------------------------------------------------- */
+
+/* Per-token (mode 0) and bf16 (mode 2) store of one token of one KV head
+ * into (blk, slot). x points at D bf16 values. */
+static void store_token(cache_t *c, int is_v, int64_t blk, int h, int slot, const uint16_t *x)
+{
+    if (c->mode == MODE_BF16) {
+        uint16_t *dst = (uint16_t *)(is_v ? c->v : c->k);
+        for (int ch = 0; ch < c->d; ch++)
+            dst[is_v ? v_index(c, blk, h, slot, ch) : k_index(c, blk, h, slot, ch)] = x[ch];
+        return;
+    }
+    float absmax = 0.0f;
+    for (int ch = 0; ch < c->d; ch++) {
+        float a = fabsf(bf16_to_float(x[ch]));
+        if (a > absmax)
+            absmax = a;
+    }
+    float s = absmax_scale(absmax);
+    int8_t *dst = (int8_t *)(is_v ? c->v : c->k);
+    for (int ch = 0; ch < c->d; ch++)
+        dst[is_v ? v_index(c, blk, h, slot, ch) : k_index(c, blk, h, slot, ch)] =
+            quant_one(bf16_to_float(x[ch]), s);
+    (is_v ? c->vs : c->ks)[tok_scale_index(c, blk, h, slot)] = s;
+}
+
+/* Per-block (mode 1) store of the new tokens of sequence b that fall in its
+ * logical block j, for KV head h.  Positions [lo, hi) are new; positions
+ * [j*BS, lo) already hold codes under the block's current scale s_old.
+ *   s = max(s_old, fl32(absmax_new / 127))
+ *   if s > s_old: every old code is re-quantized, q <- quant(fl32(q * s_old), s)
+ *   new codes:    q = quant(x, s)
+ * x_first points at the bf16 row [Hkv][D] of the token at position lo. */
+static void store_block(cache_t *c, int is_v, int64_t blk, int h, int j, int lo, int hi,
+                        const uint16_t *x_first, int64_t row_stride)
+{
+    int8_t *dst = (int8_t *)(is_v ? c->v : c->k);
+    float *sc = is_v ? c->vs : c->ks;
+    int n_old = lo - j * c->bs;
+    float s_old = n_old > 0 ? sc[blk_scale_index(c, blk, h)] : 0.0f;
+    float absmax = 0.0f;
+    for (int p = lo; p < hi; p++) {
+        const uint16_t *x = x_first + (int64_t)(p - lo) * row_stride + (int64_t)h * c->d;
+        for (int ch = 0; ch < c->d; ch++) {
+            float a = fabsf(bf16_to_float(x[ch]));
+            if (a > absmax)
+                absmax = a;
+        }
+    }
+    float s_new = absmax_scale(absmax);
+    float s = s_new > s_old ? s_new : s_old;
+    if (n_old > 0 && s > s_old) {
+        for (int slot = 0; slot < n_old; slot++)
+            for (int ch = 0; ch < c->d; ch++) {
+                int64_t i = is_v ? v_index(c, blk, h, slot, ch) : k_index(c, blk, h, slot, ch);
+                float old_value = (float)dst[i] * s_old; /* fl32 */
+                dst[i] = quant_one(old_value, s);
+            }
+    }
+    for (int p = lo; p < hi; p++) {
+        int slot = p - j * c->bs;
+        const uint16_t *x = x_first + (int64_t)(p - lo) * row_stride + (int64_t)h * c->d;
+        for (int ch = 0; ch < c->d; ch++) {
+            int64_t i = is_v ? v_index(c, blk, h, slot, ch) : k_index(c, blk, h, slot, ch);
+            dst[i] = quant_one(bf16_to_float(x[ch]), s);
+        }
+    }
+    sc[blk_scale_index(c, blk, h)] = s;
+}
+
+/*
+ * Store T new tokens (k_new, v_new: bf16 [T][Hkv][D]).
+ *
+ * Slot of token t:
+ *  - slot_mapping != NULL: slot = slot_mapping[t]; block = slot / BS,
+ *    offset = slot % BS; a negative slot means "skip" (padding token).
+ *  - otherwise token i of sequence b is t = cu_q_lens[b] + i (cu_q_lens NULL:
+ *    one token per sequence, t = b); its position is
+ *    p = context_lengths[b] - q_len_b + i, its block
+ *    block_table[b][p / BS] and its offset p % BS.
+ * Mode 1 requires the block-table form.
+ * Returns 0, or -1 on an argument it cannot serve.
+ */
+int oracle_store(int mode, int nb, int hkv, int bs, int d, void *k_cache, void *v_cache,
+                 float *k_scale, float *v_scale, const uint16_t *k_new, const uint16_t *v_new,
+                 int num_tokens, const int64_t *slot_mapping, const int32_t *cu_q_lens,
+                 const int32_t *context_lengths, const int32_t *block_table, int batch, int mbs)
+{
+    cache_t c = {mode, nb, hkv, bs, d, k_cache, v_cache, k_scale, v_scale};
+    const int64_t row = (int64_t)hkv * d;
+    if (mode < 0 || mode > 2 || bs <= 0 || d <= 0 || hkv <= 0)
+        return -1;
+    if (slot_mapping) {
+        if (mode == MODE_PER_BLOCK)
+            return -1;
+        for (int t = 0; t < num_tokens; t++) {
+            int64_t slot = slot_mapping[t];
+            if (slot < 0)
+                continue;
+            for (int h = 0; h < hkv; h++) {
+                store_token(&c, 0, slot / bs, h, (int)(slot % bs), k_new + t * row + (int64_t)h * d);
+                store_token(&c, 1, slot / bs, h, (int)(slot % bs), v_new + t * row + (int64_t)h * d);
+            }
+        }
+        return 0;
+    }
+    if (!context_lengths || !block_table)
+        return -1;
+    for (int b = 0; b < batch; b++) {
+        int qlen = cu_q_lens ? cu_q_lens[b + 1] - cu_q_lens[b] : 1;
+        int t0 = cu_q_lens ? cu_q_lens[b] : b;
+        int ctx = context_lengths[b];
+        int prior = ctx - qlen;
+        if (qlen <= 0)
+            continue;
+        if (mode != MODE_PER_BLOCK) {
+            for (int i = 0; i < qlen; i++) {
+                int p = prior + i;
+                int64_t blk = block_table[(int64_t)b * mbs + p / bs];
+                for (int h = 0; h < hkv; h++) {
+                    store_token(&c, 0, blk, h, p % bs, k_new + (int64_t)(t0 + i) * row + (int64_t)h * d);
+                    store_token(&c, 1, blk, h, p % bs, v_new + (int64_t)(t0 + i) * row + (int64_t)h * d);
+                }
+            }
+        } else {
+            for (int j = prior / bs; j * bs < ctx; j++) {
+                int lo = prior > j * bs ? prior : j * bs;
+                int hi = ctx < (j + 1) * bs ? ctx : (j + 1) * bs;
+                int64_t blk = block_table[(int64_t)b * mbs + j];
+                int64_t t_lo = t0 + (lo - prior);
+                for (int h = 0; h < hkv; h++) {
+                    store_block(&c, 0, blk, h, j, lo, hi, k_new + t_lo * row, row);
+                    store_block(&c, 1, blk, h, j, lo, hi, v_new + t_lo * row, row);
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* dequant                                                                    */
+/* ------------------------------------------------------------------------- */
+
+/* Dequantized value of cache element (blk, h, slot, ch) as an fp32:
+ * fl32(float(q) * s); mode 2 returns the stored bf16 value. */
+static float deq_f32(const cache_t *c, int is_v, int64_t blk, int h, int slot, int ch)
+{
+    int64_t i = is_v ? v_index(c, blk, h, slot, ch) : k_index(c, blk, h, slot, ch);
+    if (c->mode == MODE_BF16)
+        return bf16_to_float(((const uint16_t *)(is_v ? c->v : c->k))[i]);
+    const float *sc = is_v ? c->vs : c->ks;
+    float s = c->mode == MODE_PER_TOKEN ? sc[tok_scale_index(c, blk, h, slot)]
+                                        : sc[blk_scale_index(c, blk, h)];
+    return (float)((const int8_t *)(is_v ? c->v : c->k))[i] * s;
+}
+
+/* Exact dequantized value in fp64: double(q) * double(s) (no rounding). */
+static double deq_f64(const cache_t *c, int is_v, int64_t blk, int h, int slot, int ch)
+{
+    int64_t i = is_v ? v_index(c, blk, h, slot, ch) : k_index(c, blk, h, slot, ch);
+    if (c->mode == MODE_BF16)
+        return (double)bf16_to_float(((const uint16_t *)(is_v ? c->v : c->k))[i]);
+    const float *sc = is_v ? c->vs : c->ks;
+    float s = c->mode == MODE_PER_TOKEN ? sc[tok_scale_index(c, blk, h, slot)]
+                                        : sc[blk_scale_index(c, blk, h)];
+    return (double)((const int8_t *)(is_v ? c->v : c->k))[i] * (double)s;
+}
+
+/*
+ * Gather every sequence's cache back to bf16.
+ * out[(off_b + p) * token_stride + h * head_stride + ch] = bf16(fl32(q * s))
+ * for p < context_lengths[b]; off_b = seq_offsets[b], or the exclusive prefix
+ * sum of context_lengths when seq_offsets is NULL.  Other rows untouched.
+ */
+int oracle_dequant(int mode, int nb, int hkv, int bs, int d, const void *k_cache,
+                   const void *v_cache, const float *k_scale, const float *v_scale,
+                   const int32_t *block_table, int mbs, const int32_t *context_lengths,
+                   const int64_t *seq_offsets, int batch, uint16_t *k_out, uint16_t *v_out,
+                   int64_t token_stride, int64_t head_stride)
+{
+    cache_t c = {mode, nb, hkv, bs, d, (void *)k_cache, (void *)v_cache, (float *)k_scale,
+                 (float *)v_scale};
+    int64_t off = 0;
+    for (int b = 0; b < batch; b++) {
+        int64_t base = seq_offsets ? seq_offsets[b] : off;
+        for (int p = 0; p < context_lengths[b]; p++) {
+            int64_t blk = block_table[(int64_t)b * mbs + p / bs];
+            for (int h = 0; h < hkv; h++)
+                for (int ch = 0; ch < d; ch++) {
+                    int64_t o = (base + p) * token_stride + h * head_stride + ch;
+                    if (k_out)
+                        k_out[o] = oracle_bf16_round(deq_f32(&c, 0, blk, h, p % bs, ch));
+                    if (v_out)
+                        v_out[o] = oracle_bf16_round(deq_f32(&c, 1, blk, h, p % bs, ch));
+                }
+        }
+        off += context_lengths[b];
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* decode attention                                                           */
+/* ------------------------------------------------------------------------- */
+
+typedef struct {
+    cache_t c;
+    const uint16_t *q;
+    int hq;
+    const int32_t *block_table;
+    int mbs;
+    const int32_t *context_lengths;
+    const int32_t *cu_q_lens;
+    int batch;
+    double scale;
+    uint16_t *out;
+    double *out_f64;
+    double *lse;
+    int next_item; /* shared work counter, guarded by mu */
+    pthread_mutex_t mu;
+} decode_job;
+
+/*
+ * One (sequence b, KV head h) item.  For each new query i < q_len_b of the
+ * sequence and each of the G = Hq/Hkv query heads hq = h*G + g:
+ *   keys t = 0 .. prior_b + i (causal; prior_b = ctx_b - q_len_b)
+ *   l_t = scale * sum_ch Q[ch] * K^[t][ch]            (fp64)
+ *   m = max_t l_t,  w_t = exp(l_t - m),  L = sum_t w_t
+ *   out[ch] = (sum_t w_t * V^[t][ch]) / L,  lse = m + ln L
+ * with K^, V^ the exact fp64 dequantized values.  No keys: out = 0, lse = -inf.
+ */
+static void decode_item(decode_job *J, int b, int h, double *l)
+{
+    const cache_t *c = &J->c;
+    int g_count = J->hq / c->hkv;
+    int d = c->d;
+    int qlen = J->cu_q_lens ? J->cu_q_lens[b + 1] - J->cu_q_lens[b] : 1;
+    int row0 = J->cu_q_lens ? J->cu_q_lens[b] : b;
+    int ctx = J->context_lengths[b];
+    int prior = ctx - qlen;
+    double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+    for (int i = 0; i < qlen; i++) {
+        int nkeys = prior + i + 1;
+        if (nkeys < 0)
+            nkeys = 0;
+        for (int g = 0; g < g_count; g++) {
+            int hq = h * g_count + g;
+            int64_t o = ((int64_t)(row0 + i) * J->hq + hq) * d;
+            const uint16_t *qv = J->q + o;
+            for (int ch = 0; ch < d; ch++)
+                acc[ch] = 0.0;
+            if (nkeys == 0) {
+                for (int ch = 0; ch < d; ch++) {
+                    J->out[o + ch] = oracle_bf16_round(0.0);
+                    if (J->out_f64)
+                        J->out_f64[o + ch] = 0.0;
+                }
+                if (J->lse)
+                    J->lse[(int64_t)(row0 + i) * J->hq + hq] = -INFINITY;
+                continue;
+            }
+            double m = -INFINITY;
+            for (int t = 0; t < nkeys; t++) {
+                int64_t blk = J->block_table[(int64_t)b * J->mbs + t / c->bs];
+                double dot = 0.0;
+                for (int ch = 0; ch < d; ch++)
+                    dot += (double)bf16_to_float(qv[ch]) * deq_f64(c, 0, blk, h, t % c->bs, ch);
+                l[t] = J->scale * dot;
+                if (l[t] > m)
+                    m = l[t];
+            }
+            double sum = 0.0;
+            for (int t = 0; t < nkeys; t++) {
+                int64_t blk = J->block_table[(int64_t)b * J->mbs + t / c->bs];
+                double w = exp(l[t] - m);
+                sum += w;
+                for (int ch = 0; ch < d; ch++)
+                    acc[ch] += w * deq_f64(c, 1, blk, h, t % c->bs, ch);
+            }
+            for (int ch = 0; ch < d; ch++) {
+                double y = acc[ch] / sum;
+                J->out[o + ch] = oracle_bf16_round(y);
+                if (J->out_f64)
+                    J->out_f64[o + ch] = y;
+            }
+            if (J->lse)
+                J->lse[(int64_t)(row0 + i) * J->hq + hq] = m + log(sum);
+        }
+    }
+    free(acc);
+}
+
+static void *decode_worker(void *arg)
+{
+    decode_job *J = (decode_job *)arg;
+    int max_ctx = 1;
+    for (int b = 0; b < J->batch; b++)
+        if (J->context_lengths[b] > max_ctx)
+            max_ctx = J->context_lengths[b];
+    double *l = (double *)malloc(sizeof(double) * (size_t)max_ctx);
+    int items = J->batch * J->c.hkv;
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int it = J->next_item++;
+        pthread_mutex_unlock(&J->mu);
+        if (it >= items)
+            break;
+        decode_item(J, it / J->c.hkv, it % J->c.hkv, l);
+    }
+    free(l);
+    return NULL;
+}
+
+/*
+ * Attention of every new query over the paged cache.
+ * q: bf16 [Tq][Hq][D] with Tq = cu_q_lens[batch] (or batch when cu_q_lens is
+ * NULL, one query per sequence).  Writes out (bf16 [Tq][Hq][D], the fp64
+ * result rounded once), and when non-NULL out_f64 (the fp64 result) and lse
+ * (natural-log sum of exponentials, fp64 [Tq][Hq]).  Work items are spread
+ * over nthreads threads; the arithmetic of each item does not depend on it.
+ */
+int oracle_decode(int mode, int nb, int hkv, int bs, int d, const void *k_cache,
+                  const void *v_cache, const float *k_scale, const float *v_scale,
+                  const uint16_t *q, int hq, const int32_t *block_table, int mbs,
+                  const int32_t *context_lengths, const int32_t *cu_q_lens, int batch,
+                  double scale, uint16_t *out, double *out_f64, double *lse, int nthreads)
+{
+    if (hkv <= 0 || hq % hkv != 0 || !out)
+        return -1;
+    decode_job J;
+    memset(&J, 0, sizeof J);
+    J.c = (cache_t){mode, nb, hkv, bs, d, (void *)k_cache, (void *)v_cache, (float *)k_scale,
+                    (float *)v_scale};
+    J.q = q;
+    J.hq = hq;
+    J.block_table = block_table;
+    J.mbs = mbs;
+    J.context_lengths = context_lengths;
+    J.cu_q_lens = cu_q_lens;
+    J.batch = batch;
+    J.scale = scale;
+    J.out = out;
+    J.out_f64 = out_f64;
+    J.lse = lse;
+    pthread_mutex_init(&J.mu, NULL);
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads == 1) {
+        decode_worker(&J);
+    } else {
+        pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+        for (int i = 0; i < nthreads; i++)
+            pthread_create(&th[i], NULL, decode_worker, &J);
+        for (int i = 0; i < nthreads; i++)
+            pthread_join(th[i], NULL);
+        free(th);
+    }
+    pthread_mutex_destroy(&J.mu);
+    return 0;
+}
