@@ -1,0 +1,331 @@
+"""Benchmark of the paged int8 KV-cache decode step on one MI355X.
+
+A step is one pass of the hot path over one batch: store the batch's new K/V tokens into the paged
+cache (quantized), then grouped-query decode attention of the new queries over the cache.  The
+default workload is the Qwen3-8B-shaped decode batch (batch 32, 32/8 heads, head_dim 128,
+block_size 16, context lengths ~ U[1024, 4096], int8 per-token scales); ``--config`` selects
+another one.  Inputs are seeded and synthetic and are resident in HBM before timing starts.
+
+To keep the 256 MB Infinity Cache from serving the working set, the step cycles over R replicas of
+the cache (R chosen so the replicas hold >= 768 MB of touched bytes).
+
+Prints ONE JSON line (rank 0):
+  value       decode-attention HBM GB/s of the whole step (algorithmic bytes / step time)
+  roofline    the dominant kernel (split-KV decode, partial + merge) against 8 TB/s
+  cpu_baseline the CPU oracle on the same workload (store + fp64 attention), timed on this host
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 * 2 ** 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1, help="workload index (0..4); 1 = Qwen3-8B decode")
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-baseline sample")
+    ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = auto)")
+    return ap.parse_args()
+
+
+def step_bytes(w):
+    """Algorithmic HBM bytes of one step: every cache byte the attention must read once, plus the
+    queries, outputs, block-table entries and context lengths it reads, plus the store's input and
+    output.  Split-KV partials are overhead and excluded."""
+    ctx = w.context_lengths.astype(np.int64)
+    hkv, d, bs = w.num_kv_heads, w.head_dim, w.block_size
+    if w.quant_mode == 0:
+        per_tok = hkv * (2 * d + 8)
+        kv = int(ctx.sum()) * per_tok
+    elif w.quant_mode == 1:
+        kv = int(ctx.sum()) * hkv * 2 * d + int(np.ceil(ctx / bs).sum()) * hkv * 8
+    else:
+        kv = int(ctx.sum()) * hkv * 4 * d
+    tq = w.num_new_tokens if not w.decode_only else w.batch
+    qo = 2 * tq * w.num_q_heads * d * 2
+    meta = int(np.ceil(ctx / bs).sum()) * 4 + w.batch * 4
+    decode = kv + qo + meta
+    t = w.num_new_tokens
+    if w.quant_mode == 2:
+        store = t * hkv * d * 2 * 2 * 2
+    elif w.quant_mode == 0:
+        store = t * hkv * d * 2 * 2 + t * hkv * (d + 4) * 2
+    else:  # per block: new tokens in and out, plus the touched old codes read and rewritten
+        store = t * hkv * d * 2 * 2 + t * hkv * d * 2
+    return decode, store
+
+
+def cpu_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return model, n
+
+
+def traffic_record(kernel_key):
+    """HBM traffic of the dominant kernel measured with rocprofv3 counters (committed under
+    profiles/), valid only while the kernel sources hash to the recorded value."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel_key)
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for f in rec.get("sources", []):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec.get("sources_sha256"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gen
+    import paged_kv_cache_c8_amd as pkv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = gen.make_config(args.config)
+    t = gen.gen_tensors(w, device=dev)
+    k_prior, k_new = gen.split_prior_new(w, t["k_all"])
+    v_prior, v_new = gen.split_prior_new(w, t["v_all"])
+    i32 = lambda x: torch.as_tensor(np.ascontiguousarray(x, dtype=np.int32), device=dev)
+    bt, ctx, prior, cu_prior = i32(w.block_table), i32(w.context_lengths), i32(w.prior_lengths), i32(w.cu_prior)
+    cu_q = None if w.decode_only else i32(w.cu_q_lens)
+    q = t["q"]
+    decode_bytes, store_bytes = step_bytes(w)
+    touched = decode_bytes + store_bytes
+    reps = args.replicas or max(1, int(np.ceil(3 * MALL_BYTES / touched)))
+
+    caches = []
+    for _ in range(reps):
+        c = pkv.Cache(w.quant_mode, w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, device=dev)
+        if int(w.prior_lengths.sum()):
+            pkv.store_c8(c, k_prior, v_prior, cu_q_lens=cu_prior, context_lengths=prior, block_table=bt,
+                         max_q_len=int(w.prior_lengths.max()))
+        caches.append(c)
+    scale = 1.0 / float(np.sqrt(w.head_dim))
+    mql = w.max_q_len if cu_q is not None else 1
+    ws_bytes = pkv.decode_workspace_size(w.batch, w.num_q_heads, caches[0], w.max_blocks_per_seq, mql,
+                                         split_tokens=args.split_tokens)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    plan = pkv.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_blocks_per_seq,
+                           w.block_size, mql, w.quant_mode, split_tokens=args.split_tokens)
+
+    def store(c):
+        if w.decode_only:
+            pkv.store_c8(c, k_new, v_new, context_lengths=ctx, block_table=bt)
+        else:
+            pkv.store_c8(c, k_new, v_new, cu_q_lens=cu_q, context_lengths=ctx, block_table=bt,
+                         max_q_len=w.max_q_len)
+
+    def decode(c):
+        pkv.decode_gqa(q, c, bt, ctx, scale, cu_q_lens=cu_q, max_q_len=mql, out=out, workspace=workspace,
+                       split_tokens=args.split_tokens)
+
+    def step(i):
+        c = caches[i % reps]
+        store(c)
+        decode(c)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- whole-step timing
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(args.steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # ---- dominant kernel: the decode call, bracketed by events on the launch stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        c = caches[i % reps]
+        store(c)
+        evs[i][0].record()
+        decode(c)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    step_s = ms_per_step * 1e-3
+    value = touched / step_s / 1e9
+    new_tokens = w.num_new_tokens if not w.decode_only else int((w.context_lengths > 0).sum())
+    achieved = decode_bytes / (dec_ms * 1e-3) / 1e9
+    kernel_key = f"decode.config{args.config}"
+    traffic = traffic_record(kernel_key)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, t, args.cpu_seconds, touched, new_tokens)
+
+    dtype = {0: "int8", 1: "int8", 2: "bf16"}[w.quant_mode]
+    res = {
+        "metric": "decode-attn HBM GB/s (% of peak) + tokens/s, int8 paged-KV GQA",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, random block tables)",
+        "config": {
+            "workload": w.name,
+            "batch": w.batch, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size, "quant_mode": w.quant_mode,
+            "sum_context": int(w.context_lengths.sum()), "new_tokens": new_tokens,
+            "cache_replicas": reps, "split_tokens": plan["split_tokens"], "num_splits": plan["num_splits"],
+            "parallelism": "single-gpu",
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(new_tokens / step_s, 1),
+        "kv_tokens_per_s": round(float(w.context_lengths.sum()) / step_s, 1),
+        "bytes_per_step": touched,
+        "wall_s_timed": round(wall, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pkv_decode_gqa (split-KV partial + log-sum-exp merge)",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": decode_bytes,
+            "avg_launch_ms": round(dec_ms, 5),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, t, budget_s, touched, new_tokens):
+    """The oracle as it stands (plain C, fp64 attention), timed on this host's cores on a bounded
+    sample of the same workload: whole steps (store of the new tokens + attention of every query)
+    over as many sequences as fit in the time budget."""
+    import torch
+
+    import oracle
+
+    model, ncores = cpu_info()
+    nthreads = max(1, min(ncores, 16))
+    bits = lambda x: x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    # a sample of sequences small enough for the budget: estimate fp64 multiply-adds per sequence
+    g = w.num_q_heads // w.num_kv_heads
+    qlen = np.maximum(w.q_lens, 1)
+    macs = w.context_lengths.astype(np.float64) * w.num_kv_heads * g * qlen * 2 * w.head_dim
+    est_rate = 2.0e8 * nthreads  # conservative multiply-adds per second
+    order = np.arange(w.batch)
+    sel, acc = [], 0.0
+    for b in order:
+        if acc + macs[b] > est_rate * budget_s / 3 and sel:
+            break
+        sel.append(b)
+        acc += macs[b]
+    sel = np.array(sel)
+    import dataclasses
+
+    ws = dataclasses.replace(w, batch=len(sel), context_lengths=w.context_lengths[sel].copy(),
+                             q_lens=w.q_lens[sel].copy(), block_table=w.block_table[sel].copy())
+    cu_ctx = w.cu_context
+    kv_idx = np.concatenate([np.arange(cu_ctx[b], cu_ctx[b + 1]) for b in sel])
+    dev = t["q"].device
+    idx = lambda a: torch.as_tensor(a, device=dev)
+    k_all = bits(t["k_all"].index_select(0, idx(kv_idx)))
+    v_all = bits(t["v_all"].index_select(0, idx(kv_idx)))
+    if w.decode_only:
+        qh = bits(t["q"].index_select(0, idx(sel)))
+    else:
+        cu_q = w.cu_q_lens
+        qh = bits(t["q"].index_select(0, idx(np.concatenate([np.arange(cu_q[b], cu_q[b + 1]) for b in sel]))))
+    hc = oracle.HostCache(w.quant_mode, w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+    cu_s = ws.cu_context
+    prior = ws.prior_lengths
+    pri = np.concatenate([np.arange(cu_s[b], cu_s[b] + prior[b]) for b in range(ws.batch)]).astype(np.int64)
+    new = np.concatenate([np.arange(cu_s[b] + prior[b], cu_s[b + 1]) for b in range(ws.batch)]).astype(np.int64)
+    if len(pri):
+        oracle.store(hc, k_all[pri], v_all[pri], cu_q_lens=ws.cu_prior.astype(np.int32), context_lengths=prior,
+                     block_table=ws.block_table)
+    cu = None if ws.decode_only else ws.cu_q_lens
+    kn, vn = np.ascontiguousarray(k_all[new]), np.ascontiguousarray(v_all[new])
+    scale = 1.0 / np.sqrt(w.head_dim)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        s0 = time.perf_counter()
+        oracle.store(hc, kn, vn, cu_q_lens=cu, context_lengths=ws.context_lengths, block_table=ws.block_table)
+        oracle.decode(hc, qh, ws.num_q_heads, ws.block_table, ws.context_lengths, scale, cu_q_lens=cu,
+                      nthreads=nthreads, want_f64=False)
+        times.append(time.perf_counter() - s0)
+        if time.perf_counter() - t_start > budget_s * 0.5 or len(times) >= 20:
+            break
+    sec = float(np.median(times))
+    frac = float(ws.context_lengths.sum()) / float(w.context_lengths.sum())
+    # the sample's step time scaled to the whole batch (attention work is linear in context)
+    full_step = sec / frac
+    _, store_b = step_bytes(ws)
+    return {
+        "value": round(touched / full_step / 1e9, 4),
+        "unit": "GB/s",
+        "cores": nthreads,
+        "kind": "oracle",
+        "cpu_model": model,
+        "host_cores_visible": ncores,
+        "sample": f"{len(sel)} of {w.batch} sequences ({int(ws.context_lengths.sum())} of "
+                  f"{int(w.context_lengths.sum())} context tokens), {len(times)} timed steps of store + "
+                  f"fp64 attention; scaled to the full batch by context share",
+        "sample_step_s": round(sec, 4),
+        "tokens_per_s": round(new_tokens / full_step, 2),
+    }
+
+
+if __name__ == "__main__":
+    main()

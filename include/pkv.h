@@ -1,0 +1,199 @@
+/*
+ * pkv.h - C ABI of libpkv: an int8 ("C8") paged KV cache for one AMD Instinct
+ * MI355X (gfx950).  Three operations, after the pages that define them:
+ *
+ *   pkv_store_c8    quantize new bf16 K/V tokens and write them into the
+ *                   block-table-indexed cache (MojoStorePagedKVCacheC8 in
+ *                   Mojo Opset PR #379; its bf16 sibling MojoStorePagedKVCache
+ *                   in the README's Op List).
+ *   pkv_dequant     gather a sequence's cache back to bf16 rows
+ *                   (MojoDequantFromPagedKVCache in PR #379).
+ *   pkv_decode_gqa  grouped-query attention of the new queries over the paged
+ *                   cache (MojoPagedDecodeGQA in the README's Op List), with
+ *                   split-KV partitions and a log-sum-exp merge.
+ *
+ * Conventions shared by every call
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library never allocates: scratch space for decode is the caller's
+ *    workspace, sized by pkv_decode_workspace_size.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream) and returns a pkv_status.  Only host-checkable conditions are
+ *    reported (null pointers, unsupported shapes, modes or alignments, a small
+ *    workspace, a failed launch).  When a call returns an error nothing has
+ *    been launched.
+ *  - Device-resident index data (block_table, context_lengths, cu_q_lens,
+ *    slot_mapping, seq_offsets) are preconditions, not checked: reading them
+ *    on the host would need a synchronisation.  They must be in range.
+ *  - context_lengths[b] counts every position of sequence b AFTER the call's
+ *    new tokens are stored; the new tokens of b occupy positions
+ *    [context_lengths[b] - q_len_b, context_lengths[b]).
+ *  - Results are deterministic: fixed split plan, fixed merge order, no
+ *    floating-point atomics.  Calls are reentrant; the only state kept is the
+ *    device's compute-unit count.
+ *
+ * Cache layout (caller-owned; element (block, kv head, slot, channel)):
+ *   K       [num_blocks][num_kv_heads][block_size][head_dim]  (token-major page)
+ *   V       [num_blocks][num_kv_heads][head_dim][block_size]  (channel-major page)
+ *   scales  PKV_QUANT_PER_TOKEN: float [num_blocks][num_kv_heads][block_size]
+ *           PKV_QUANT_PER_BLOCK: float [num_blocks][num_kv_heads]
+ *           PKV_QUANT_NONE_BF16: none (K and V hold bf16)
+ *   int8 codes for the quantized modes, bf16 for PKV_QUANT_NONE_BF16.
+ *   K, V: 16-byte aligned; scales: 4-byte aligned.
+ *   Supported: head_dim 64 or 128; block_size 16, 32, 64 or 128.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent arguments */
+    PKV_ERR_UNSUPPORTED = -2, /* head_dim / block_size / mode outside the supported set */
+    PKV_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+    PKV_ERR_HIP = -4          /* a kernel launch or device query failed */
+} pkv_status;
+
+typedef enum {
+    /* one fp32 scale per token and KV head: scale = absmax/127 of the token's
+       head_dim values (dynamic symmetric quantization, MojoDynamicQuant in the
+       README's Op List) */
+    PKV_QUANT_PER_TOKEN = 0,
+    /* one fp32 scale per block and KV head (PR #379's per-block scale layout
+       for quant_mode != 0): absmax/127 of every value the block holds */
+    PKV_QUANT_PER_BLOCK = 1,
+    /* no quantization: K and V pages hold bf16 */
+    PKV_QUANT_NONE_BF16 = 2
+} pkv_quant_mode;
+
+/* A caller-owned paged cache.  Shapes travel with the pointers. */
+typedef struct {
+    void *k;        /* int8 (or bf16) pages, layout above */
+    void *v;        /* int8 (or bf16) pages, layout above */
+    float *k_scale; /* NULL in PKV_QUANT_NONE_BF16 */
+    float *v_scale; /* NULL in PKV_QUANT_NONE_BF16 */
+    int32_t num_blocks;
+    int32_t num_kv_heads;
+    int32_t block_size;
+    int32_t head_dim;
+    int32_t quant_mode; /* pkv_quant_mode */
+} pkv_cache_t;
+
+/* Human-readable name of a pkv_status. Never NULL. */
+const char *pkv_status_string(int status);
+
+/* ABI version of this header (major * 100 + minor). */
+int pkv_version(void);
+
+/*
+ * pkv_store_c8 - quantize new tokens and write them into the cache.
+ *
+ * k_new, v_new  bf16 [num_tokens][num_kv_heads][head_dim], row-major.
+ * Slot of new token t, in one of two forms:
+ *  - slot_mapping != NULL (int64 [num_tokens]): block = slot / block_size,
+ *    slot in block = slot % block_size; a negative entry skips the token.
+ *    cu_q_lens, context_lengths and block_table are then ignored.
+ *    Not available with PKV_QUANT_PER_BLOCK.
+ *  - slot_mapping == NULL: cu_q_lens (int32 [batch + 1], prefix sums of the
+ *    per-sequence new-token counts; NULL means one new token per sequence,
+ *    token b belongs to sequence b, num_tokens == batch), context_lengths
+ *    (int32 [batch]) and block_table (int32 [batch][max_blocks_per_seq]):
+ *    token i of sequence b lands at position
+ *    p = context_lengths[b] - q_len_b + i, block block_table[b][p/block_size].
+ * max_q_len     host-known upper bound of the per-sequence new-token counts
+ *               (used to size the per-block launch; <= 0 means num_tokens).
+ * quant_mode    must equal cache->quant_mode.
+ *
+ * Per token (mode 0), for each token and KV head independently:
+ *   scale = fl32(absmax / 127),  code = clamp(rne(fl32(x / scale)), -128, 127)
+ *   (code 0 when scale == 0); rne rounds halves to even (PR #379 reviews:
+ *   symmetric int8 codes, x over the scale, rounded and clamped; the division
+ *   in fp32).
+ * Per block (mode 1), for each (sequence, block touched, KV head):
+ *   s = max(s_old, fl32(absmax_new / 127)) where s_old is the block's scale
+ *   when positions before the new tokens already live in the block; if s
+ *   grows, the block's existing codes are re-quantized from fl32(code * s_old);
+ *   the new tokens are quantized with s.  Precondition: no physical block is
+ *   shared between sequences.
+ * bf16 (mode 2): the values are copied.
+ *
+ * num_tokens == 0 returns PKV_OK without launching anything.
+ */
+int pkv_store_c8(const pkv_cache_t *cache, const void *k_new, const void *v_new,
+                 int32_t num_tokens, const int64_t *slot_mapping, const int32_t *cu_q_lens,
+                 const int32_t *context_lengths, const int32_t *block_table, int32_t batch,
+                 int32_t max_blocks_per_seq, int32_t max_q_len, int32_t quant_mode, void *stream);
+
+/*
+ * pkv_dequant - gather every sequence's cache back to bf16
+ * (MojoDequantFromPagedKVCache, PR #379).
+ *
+ * For b < batch, position p < context_lengths[b], KV head h, channel c:
+ *   out[(off_b + p) * token_stride + h * head_stride + c] = bf16_rne(fl32(code * scale))
+ * (the product in fp32, PR #379 reviews), or the stored bf16 value in mode 2.
+ * off_b = seq_offsets[b] (int64 [batch]) or, when seq_offsets is NULL, the
+ * exclusive prefix sum of context_lengths.  Rows outside every sequence (the
+ * padding of a padded layout) are not written.  Strides are in elements;
+ * channels are contiguous.  k_out or v_out may be NULL to skip that half.
+ */
+int pkv_dequant(const pkv_cache_t *cache, const int32_t *block_table, int32_t max_blocks_per_seq,
+                const int32_t *context_lengths, const int64_t *seq_offsets, int32_t batch,
+                void *k_out, void *v_out, int64_t token_stride, int64_t head_stride, void *stream);
+
+/* Optional knobs of pkv_decode_gqa (pass NULL for the defaults). */
+typedef struct {
+    int32_t split_tokens; /* keys per split-KV partition; 0 = planned from the shapes.
+                             Rounded up to a multiple of 128. */
+    int32_t kernel;       /* 0 = choose; 1 = VALU split-KV kernel; 2 = MFMA kernel */
+    int32_t reserved[6];  /* must be zero */
+} pkv_decode_opts_t;
+
+/* Bytes of workspace pkv_decode_gqa needs for these shapes (0 when it needs
+ * none).  Depends on the current device's compute-unit count. */
+size_t pkv_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
+                                 int32_t max_q_len, int32_t quant_mode,
+                                 const pkv_decode_opts_t *opts);
+
+/*
+ * pkv_decode_gqa - attention of the new queries over the paged cache
+ * (MojoPagedDecodeGQA, README Op List).
+ *
+ * q        bf16 [Tq][num_q_heads][head_dim]; Tq = batch when cu_q_lens is NULL
+ *          (one query per sequence), else cu_q_lens[batch].
+ * Query i < q_len_b of sequence b sits at position p = context_lengths[b] -
+ * q_len_b + i and attends to keys 0..p (causal within its chunk).  Query head
+ * hq reads KV head hq / G, G = num_q_heads / num_kv_heads.
+ *   out = softmax(scale * q K^T) V   over the dequantized keys and values,
+ * accumulated in fp32 and written as bf16 [Tq][num_q_heads][head_dim].
+ * lse_out  optional fp32 [Tq][num_q_heads]: natural log of the softmax
+ *          denominator of the scaled logits; -inf for a sequence with no keys
+ *          (whose output is 0).
+ * max_q_len host-known upper bound of q_len_b (1 for pure decode).
+ * workspace / workspace_bytes: caller scratch of at least
+ *          pkv_decode_workspace_size(...) bytes, 256-byte aligned.
+ */
+int pkv_decode_gqa(const void *q, int32_t num_q_heads, const pkv_cache_t *cache,
+                   const int32_t *block_table, int32_t max_blocks_per_seq,
+                   const int32_t *context_lengths, const int32_t *cu_q_lens, int32_t batch,
+                   int32_t max_q_len, float scale, void *out, float *lse_out, void *workspace,
+                   size_t workspace_bytes, const pkv_decode_opts_t *opts, void *stream);
+
+/* The split plan pkv_decode_gqa would use, for tests and benchmarks.
+ * Writes the keys per partition, the number of partitions per row group and
+ * the kernel (1 VALU, 2 MFMA); any output pointer may be NULL. */
+int pkv_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t max_blocks_per_seq, int32_t block_size, int32_t max_q_len,
+                    int32_t quant_mode, const pkv_decode_opts_t *opts, int32_t *split_tokens,
+                    int32_t *num_splits, int32_t *kernel);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -41,8 +41,11 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        build(force=False)
-        L = ctypes.CDLL(_LIB)
+        path = os.environ.get("PKV_ORACLE_LIB")  # a differently built copy (e.g. with AddressSanitizer)
+        if not path:
+            build(force=False)
+            path = _LIB
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I = ctypes.c_int
         L.oracle_bf16_round.argtypes = [ctypes.c_double]

@@ -245,6 +245,8 @@ int oracle_store(int mode, int nb, int hkv, int bs, int d, void *k_cache, void *
             int64_t slot = slot_mapping[t];
             if (slot < 0)
                 continue;
+            if (slot / bs >= nb)
+                return -1;
             for (int h = 0; h < hkv; h++) {
                 store_token(&c, 0, slot / bs, h, (int)(slot % bs), k_new + t * row + (int64_t)h * d);
                 store_token(&c, 1, slot / bs, h, (int)(slot % bs), v_new + t * row + (int64_t)h * d);
@@ -264,17 +266,29 @@ int oracle_store(int mode, int nb, int hkv, int bs, int d, void *k_cache, void *
         if (mode != MODE_PER_BLOCK) {
             for (int i = 0; i < qlen; i++) {
                 int p = prior + i;
+                if (p < 0)
+                    continue; /* inactive decode slot (context length 0): nothing to store */
+                if (p / bs >= mbs)
+                    return -1;
                 int64_t blk = block_table[(int64_t)b * mbs + p / bs];
+                if (blk < 0 || blk >= nb)
+                    return -1;
                 for (int h = 0; h < hkv; h++) {
                     store_token(&c, 0, blk, h, p % bs, k_new + (int64_t)(t0 + i) * row + (int64_t)h * d);
                     store_token(&c, 1, blk, h, p % bs, v_new + (int64_t)(t0 + i) * row + (int64_t)h * d);
                 }
             }
         } else {
+            if (prior < 0)
+                continue; /* inactive decode slot */
             for (int j = prior / bs; j * bs < ctx; j++) {
                 int lo = prior > j * bs ? prior : j * bs;
                 int hi = ctx < (j + 1) * bs ? ctx : (j + 1) * bs;
+                if (j >= mbs)
+                    return -1;
                 int64_t blk = block_table[(int64_t)b * mbs + j];
+                if (blk < 0 || blk >= nb)
+                    return -1;
                 int64_t t_lo = t0 + (lo - prior);
                 for (int h = 0; h < hkv; h++) {
                     store_block(&c, 0, blk, h, j, lo, hi, k_new + t_lo * row, row);
@@ -332,8 +346,12 @@ int oracle_dequant(int mode, int nb, int hkv, int bs, int d, const void *k_cache
     int64_t off = 0;
     for (int b = 0; b < batch; b++) {
         int64_t base = seq_offsets ? seq_offsets[b] : off;
+        if (context_lengths[b] > mbs * bs)
+            return -1;
         for (int p = 0; p < context_lengths[b]; p++) {
             int64_t blk = block_table[(int64_t)b * mbs + p / bs];
+            if (blk < 0 || blk >= nb)
+                return -1;
             for (int h = 0; h < hkv; h++)
                 for (int ch = 0; ch < d; ch++) {
                     int64_t o = (base + p) * token_stride + h * head_stride + ch;
@@ -476,6 +494,13 @@ int oracle_decode(int mode, int nb, int hkv, int bs, int d, const void *k_cache,
 {
     if (hkv <= 0 || hq % hkv != 0 || !out)
         return -1;
+    for (int b = 0; b < batch; b++) {
+        if (context_lengths[b] > mbs * bs)
+            return -1;
+        for (int j = 0; j * bs < context_lengths[b]; j++)
+            if (block_table[(int64_t)b * mbs + j] < 0 || block_table[(int64_t)b * mbs + j] >= nb)
+                return -1;
+    }
     decode_job J;
     memset(&J, 0, sizeof J);
     J.c = (cache_t){mode, nb, hkv, bs, d, (void *)k_cache, (void *)v_cache, (float *)k_scale,

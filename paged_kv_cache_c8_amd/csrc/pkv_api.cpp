@@ -1,0 +1,274 @@
+// pkv_api.cpp - the C ABI of libpkv (include/pkv.h): argument validation, split planning and
+// kernel launches on the caller's stream.  No allocation, no host synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kDefaultCUs = 256;  // MI355X, used when no device is visible (planning only)
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return kDefaultCUs;
+    int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = kDefaultCUs;
+    g_cus[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int x) {
+    int l = 0;
+    while ((1 << l) < x) ++l;
+    return l;
+}
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int check_cache(const pkv_cache_t* c) {
+    if (!c || !c->k || !c->v) return PKV_ERR_INVALID_ARG;
+    if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return PKV_ERR_INVALID_ARG;
+    if (c->head_dim != 64 && c->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (!pow2(c->block_size) || c->block_size < 16 || c->block_size > 128) return PKV_ERR_UNSUPPORTED;
+    if (c->quant_mode < 0 || c->quant_mode > 2) return PKV_ERR_UNSUPPORTED;
+    if (c->quant_mode != PKV_QUANT_NONE_BF16 && (!c->k_scale || !c->v_scale)) return PKV_ERR_INVALID_ARG;
+    if (!aligned(c->k, 16) || !aligned(c->v, 16)) return PKV_ERR_INVALID_ARG;
+    if (c->k_scale && !aligned(c->k_scale, 4)) return PKV_ERR_INVALID_ARG;
+    if (c->v_scale && !aligned(c->v_scale, 4)) return PKV_ERR_INVALID_ARG;
+    return PKV_OK;
+}
+
+struct DecodePlan {
+    int rg;
+    int nrg;
+    int nsplit;
+    int split_len;
+    int kernel;
+    size_t ws_bytes;
+};
+
+int pow2_at_least(int x) {
+    int p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t mbs, int32_t bs,
+              int32_t max_q_len, int32_t mode, const pkv_decode_opts_t* opts, DecodePlan* p) {
+    if (batch < 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || mbs <= 0) return PKV_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (!pow2(bs) || bs < 16 || bs > 128) return PKV_ERR_UNSUPPORTED;
+    if (mode < 0 || mode > 2) return PKV_ERR_UNSUPPORTED;
+    if (max_q_len < 1) max_q_len = 1;
+    if (opts) {
+        for (int i = 0; i < 6; ++i)
+            if (opts->reserved[i] != 0) return PKV_ERR_INVALID_ARG;
+        if (opts->split_tokens < 0) return PKV_ERR_INVALID_ARG;
+        if (opts->kernel < 0 || opts->kernel > 2) return PKV_ERR_INVALID_ARG;
+        if (opts->kernel == 2) return PKV_ERR_UNSUPPORTED;
+    }
+    const int g = hq / hkv;
+    const int64_t rows = (int64_t)max_q_len * g;
+    p->rg = pow2_at_least((int)(rows < 8 ? rows : 8));
+    p->nrg = (int)cdiv(rows, p->rg);
+    p->kernel = 1;
+    const int64_t max_ctx = (int64_t)mbs * bs;
+    const int64_t items = (int64_t)batch * hkv * p->nrg;
+    int64_t L;
+    if (opts && opts->split_tokens > 0) {
+        L = cdiv(opts->split_tokens, 128) * 128;
+    } else {
+        // Aim for ~16 workgroups per compute unit counting every (possibly empty) split, with
+        // partitions of 256..2048 keys: long enough to amortise the per-workgroup query load and
+        // partial write, short enough to spread a few long sequences over the whole chip.
+        const int64_t target = 16LL * device_cus();
+        const int64_t want_splits = items > 0 ? (target + items - 1) / items : 1;
+        L = cdiv(cdiv(max_ctx, want_splits), 128) * 128;
+        if (L < 256) L = 256;
+        if (L > 2048) L = 2048;
+    }
+    if (L >= max_ctx) L = cdiv(max_ctx, 128) * 128;
+    if (L > 0x40000000LL) return PKV_ERR_INVALID_ARG;
+    p->split_len = (int)L;
+    p->nsplit = (int)cdiv(max_ctx, L);
+    p->ws_bytes = p->nsplit > 1 ? (size_t)(items * p->nsplit * p->rg) * (size_t)(head_dim + 1) * 4 + 256 : 0;
+    return PKV_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+    switch (status) {
+        case PKV_OK: return "PKV_OK";
+        case PKV_ERR_INVALID_ARG: return "PKV_ERR_INVALID_ARG: invalid argument";
+        case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED: unsupported shape or mode";
+        case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE: workspace missing or too small";
+        case PKV_ERR_HIP: return "PKV_ERR_HIP: HIP launch or device query failed";
+        default: return "PKV_ERR_UNKNOWN";
+    }
+}
+
+int pkv_version(void) { return 100; }
+
+int pkv_store_c8(const pkv_cache_t* cache, const void* k_new, const void* v_new, int32_t num_tokens,
+                 const int64_t* slot_mapping, const int32_t* cu_q_lens, const int32_t* context_lengths,
+                 const int32_t* block_table, int32_t batch, int32_t max_blocks_per_seq,
+                 int32_t max_q_len, int32_t quant_mode, void* stream) {
+    int st = check_cache(cache);
+    if (st != PKV_OK) return st;
+    if (quant_mode != cache->quant_mode) return PKV_ERR_INVALID_ARG;
+    if (num_tokens < 0) return PKV_ERR_INVALID_ARG;
+    if (num_tokens == 0) return PKV_OK;
+    if (!k_new || !v_new || !aligned(k_new, 4) || !aligned(v_new, 4)) return PKV_ERR_INVALID_ARG;
+    if (slot_mapping) {
+        if (quant_mode == PKV_QUANT_PER_BLOCK) return PKV_ERR_UNSUPPORTED;
+    } else {
+        if (!context_lengths || !block_table || batch < 0 || max_blocks_per_seq <= 0)
+            return PKV_ERR_INVALID_ARG;
+        if (!cu_q_lens && num_tokens != batch) return PKV_ERR_INVALID_ARG;
+    }
+    pkv::StoreArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.k = cache->k;
+    a.v = cache->v;
+    a.ks = cache->k_scale;
+    a.vs = cache->v_scale;
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.slot_mapping = slot_mapping;
+    a.cu_q = cu_q_lens;
+    a.ctx = context_lengths;
+    a.bt = block_table;
+    a.num_tokens = num_tokens;
+    a.hkv = cache->num_kv_heads;
+    a.bs = cache->block_size;
+    a.log2bs = ilog2(cache->block_size);
+    a.mbs = max_blocks_per_seq;
+    a.batch = batch;
+    int q = cu_q_lens ? (max_q_len > 0 ? max_q_len : num_tokens) : 1;
+    a.nbt = (int)((q + cache->block_size - 2) / cache->block_size + 1);
+    if (a.nbt > max_blocks_per_seq && !slot_mapping) a.nbt = max_blocks_per_seq;
+    return hip_status(pkv::launch_store(a, cache->head_dim, quant_mode, static_cast<hipStream_t>(stream)));
+}
+
+int pkv_dequant(const pkv_cache_t* cache, const int32_t* block_table, int32_t max_blocks_per_seq,
+                const int32_t* context_lengths, const int64_t* seq_offsets, int32_t batch, void* k_out,
+                void* v_out, int64_t token_stride, int64_t head_stride, void* stream) {
+    int st = check_cache(cache);
+    if (st != PKV_OK) return st;
+    if (!block_table || !context_lengths || batch < 0 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID_ARG;
+    if (!k_out && !v_out) return PKV_ERR_INVALID_ARG;
+    if (token_stride <= 0 || head_stride <= 0) return PKV_ERR_INVALID_ARG;
+    if ((k_out && !aligned(k_out, 2)) || (v_out && !aligned(v_out, 2))) return PKV_ERR_INVALID_ARG;
+    if (batch == 0) return PKV_OK;
+    pkv::DequantArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.k = cache->k;
+    a.v = cache->v;
+    a.ks = cache->k_scale;
+    a.vs = cache->v_scale;
+    a.bt = block_table;
+    a.ctx = context_lengths;
+    a.seq_off = seq_offsets;
+    a.k_out = static_cast<uint16_t*>(k_out);
+    a.v_out = static_cast<uint16_t*>(v_out);
+    a.token_stride = token_stride;
+    a.head_stride = head_stride;
+    a.hkv = cache->num_kv_heads;
+    a.bs = cache->block_size;
+    a.log2bs = ilog2(cache->block_size);
+    a.mbs = max_blocks_per_seq;
+    a.batch = batch;
+    a.vec_ok = (token_stride % 8 == 0) && (head_stride % 8 == 0) && (!k_out || aligned(k_out, 16)) &&
+               (!v_out || aligned(v_out, 16));
+    return hip_status(pkv::launch_dequant(a, cache->head_dim, cache->quant_mode, static_cast<hipStream_t>(stream)));
+}
+
+size_t pkv_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
+                                 int32_t max_q_len, int32_t quant_mode, const pkv_decode_opts_t* opts) {
+    DecodePlan p;
+    if (make_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size, max_q_len,
+                  quant_mode, opts, &p) != PKV_OK)
+        return 0;
+    return p.ws_bytes;
+}
+
+int pkv_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t max_blocks_per_seq, int32_t block_size, int32_t max_q_len, int32_t quant_mode,
+                    const pkv_decode_opts_t* opts, int32_t* split_tokens, int32_t* num_splits,
+                    int32_t* kernel) {
+    DecodePlan p;
+    int st = make_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
+                       max_q_len, quant_mode, opts, &p);
+    if (st != PKV_OK) return st;
+    if (split_tokens) *split_tokens = p.split_len;
+    if (num_splits) *num_splits = p.nsplit;
+    if (kernel) *kernel = p.kernel;
+    return PKV_OK;
+}
+
+int pkv_decode_gqa(const void* q, int32_t num_q_heads, const pkv_cache_t* cache, const int32_t* block_table,
+                   int32_t max_blocks_per_seq, const int32_t* context_lengths, const int32_t* cu_q_lens,
+                   int32_t batch, int32_t max_q_len, float scale, void* out, float* lse_out,
+                   void* workspace, size_t workspace_bytes, const pkv_decode_opts_t* opts, void* stream) {
+    int st = check_cache(cache);
+    if (st != PKV_OK) return st;
+    if (!q || !out || !block_table || !context_lengths) return PKV_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(out, 2) || (lse_out && !aligned(lse_out, 4))) return PKV_ERR_INVALID_ARG;
+    if (!cu_q_lens) max_q_len = 1;
+    if (max_q_len < 1) return PKV_ERR_INVALID_ARG;
+    DecodePlan p;
+    st = make_plan(batch, num_q_heads, cache->num_kv_heads, cache->head_dim, max_blocks_per_seq,
+                   cache->block_size, max_q_len, cache->quant_mode, opts, &p);
+    if (st != PKV_OK) return st;
+    if (batch == 0) return PKV_OK;
+    if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 16)))
+        return PKV_ERR_WORKSPACE;
+    pkv::DecodeArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = cache->k;
+    a.v = cache->v;
+    a.ks = cache->k_scale;
+    a.vs = cache->v_scale;
+    a.bt = block_table;
+    a.ctx = context_lengths;
+    a.cu = cu_q_lens;
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse_out;
+    a.hq = num_q_heads;
+    a.hkv = cache->num_kv_heads;
+    a.g = num_q_heads / cache->num_kv_heads;
+    a.bs = cache->block_size;
+    a.log2bs = ilog2(cache->block_size);
+    a.mbs = max_blocks_per_seq;
+    a.nrg = p.nrg;
+    a.nsplit = p.nsplit;
+    a.split_len = p.split_len;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    if (p.nsplit > 1) {
+        const int64_t items = (int64_t)batch * a.hkv * p.nrg;
+        float* ws = static_cast<float*>(workspace);
+        a.part_o = ws;
+        a.part_lse = ws + items * p.nsplit * p.rg * cache->head_dim;
+    }
+    return hip_status(pkv::launch_decode_valu(a, batch, cache->head_dim, p.rg, cache->quant_mode,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// pkv_device.h - device-side helpers shared by the libpkv kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------------------------
+// bf16
+// ---------------------------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Nearest bf16 (ties to the even significand) of a finite or infinite fp32; NaN -> quiet NaN.
+// Adding 0x7fff plus the lowest kept bit carries into the kept half exactly when the discarded
+// half is above the midpoint, or at the midpoint with an odd kept half.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------------------------
+// int8 quantization (per token / per block): code = clamp(rne(fl32(x / s)), -128, 127), 0 if s == 0.
+// The division is IEEE correctly rounded (the library is built with correctly rounded fp32
+// division and without denormal flushing) and rintf rounds halves to even.
+// ---------------------------------------------------------------------------------------------
+
+__device__ __forceinline__ int quant_code(float x, float s) {
+    if (s == 0.0f) return 0;
+    float r = __builtin_rintf(x / s);
+    r = fminf(fmaxf(r, -128.0f), 127.0f);
+    return (int)r;
+}
+
+__device__ __forceinline__ float absmax_scale(float absmax) { return absmax / 127.0f; }
+
+// ---------------------------------------------------------------------------------------------
+// Cross-lane exchange.  Within a row of 16 lanes, DPP moves data without LDS traffic:
+//   stride 1: quad_perm [1,0,3,2]     stride 2: quad_perm [2,3,0,1]
+//   stride 4: row_half_mirror (lane i <-> 7 - i in each half row; flips bit 2 and the bits below)
+//   stride 8: row_mirror      (lane i <-> 15 - i; flips bit 3 and the bits below)
+// Each is a perfect matching whose partner differs in the stride bit, which is all that the
+// butterfly reductions below require.  Strides 16 and 32 cross rows and use __shfl_xor (ds_bpermute).
+// ---------------------------------------------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+template <int S>
+__device__ __forceinline__ float lane_xchg(float x) {
+    if constexpr (S == 1) return dpp_mov<0xB1>(x);
+    else if constexpr (S == 2) return dpp_mov<0x4E>(x);
+    else if constexpr (S == 4) return dpp_mov<0x141>(x);
+    else if constexpr (S == 8) return dpp_mov<0x140>(x);
+    else return __shfl_xor(x, S, kWave);
+}
+
+template <int N>  // reduce over aligned groups of N lanes (N power of two <= 64)
+__device__ __forceinline__ float group_max(float x) {
+    if constexpr (N >= 2) x = fmaxf(x, lane_xchg<1>(x));
+    if constexpr (N >= 4) x = fmaxf(x, lane_xchg<2>(x));
+    if constexpr (N >= 8) x = fmaxf(x, lane_xchg<4>(x));
+    if constexpr (N >= 16) x = fmaxf(x, lane_xchg<8>(x));
+    if constexpr (N >= 32) x = fmaxf(x, lane_xchg<16>(x));
+    if constexpr (N >= 64) x = fmaxf(x, lane_xchg<32>(x));
+    return x;
+}
+
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (N >= 2) x += lane_xchg<1>(x);
+    if constexpr (N >= 4) x += lane_xchg<2>(x);
+    if constexpr (N >= 8) x += lane_xchg<4>(x);
+    if constexpr (N >= 16) x += lane_xchg<8>(x);
+    if constexpr (N >= 32) x += lane_xchg<16>(x);
+    if constexpr (N >= 64) x += lane_xchg<32>(x);
+    return x;
+}
+
+// ---------------------------------------------------------------------------------------------
+// 16-byte global loads (kept as four dwords)
+// ---------------------------------------------------------------------------------------------
+
+struct u32x4 {
+    uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    return {v.x, v.y, v.z, v.w};
+}
+
+__device__ __forceinline__ uint32_t word(const u32x4& v, int i) {
+    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// element e (0..15) of 16 int8 codes, as float (exact)
+__device__ __forceinline__ float i8_at(const u32x4& v, int e) {
+    return (float)(int8_t)((word(v, e >> 2) >> (8 * (e & 3))) & 0xffu);
+}
+
+// element e (0..7) of 8 bf16 values, as float (exact)
+__device__ __forceinline__ float bf16_at(const u32x4& v, int e) {
+    const uint32_t w = word(v, e >> 1);
+    return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+}
+
+}  // namespace pkv

@@ -1,0 +1,80 @@
+// pkv_internal.h - argument blocks and kernel launchers shared between the C-ABI layer
+// (pkv_api.cpp) and the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct StoreArgs {
+    void* k;
+    void* v;
+    float* ks;
+    float* vs;
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    const int64_t* slot_mapping;
+    const int32_t* cu_q;
+    const int32_t* ctx;
+    const int32_t* bt;
+    int num_tokens;
+    int hkv;
+    int bs;
+    int log2bs;
+    int mbs;
+    int batch;
+    int nbt;  // blocks a sequence's new tokens can touch (per-block launch)
+};
+
+struct DequantArgs {
+    const void* k;
+    const void* v;
+    const float* ks;
+    const float* vs;
+    const int32_t* bt;
+    const int32_t* ctx;
+    const int64_t* seq_off;
+    uint16_t* k_out;
+    uint16_t* v_out;
+    int64_t token_stride;
+    int64_t head_stride;
+    int hkv;
+    int bs;
+    int log2bs;
+    int mbs;
+    int batch;
+    int vec_ok;  // outputs and strides allow 16-byte stores
+};
+
+struct DecodeArgs {
+    const uint16_t* q;
+    const void* k;
+    const void* v;
+    const float* ks;
+    const float* vs;
+    const int32_t* bt;
+    const int32_t* ctx;
+    const int32_t* cu;
+    uint16_t* out;
+    float* lse;
+    float* part_o;    // [items][nsplit][RG][D]
+    float* part_lse;  // [items][nsplit][RG]  (base-2 log-sum-exp)
+    int hq;
+    int hkv;
+    int g;
+    int bs;
+    int log2bs;
+    int mbs;
+    int nrg;
+    int nsplit;
+    int split_len;
+    float scale_log2;  // softmax scale * log2(e)
+};
+
+hipError_t launch_store(const StoreArgs& a, int head_dim, int mode, hipStream_t stream);
+hipError_t launch_dequant(const DequantArgs& a, int head_dim, int mode, hipStream_t stream);
+hipError_t launch_decode_valu(const DecodeArgs& a, int batch, int head_dim, int rg, int mode,
+                              hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,117 @@
+"""The C-ABI library loads, exports every symbol include/pkv.h declares, and rejects bad arguments
+on the host before launching anything (CPU only: no compute call reaches a kernel)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_c8_amd as pkv
+
+    if not os.path.exists(pkv.LIB_PATH):
+        pytest.fail("libpkv.so is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+    return pkv
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported(pkv):
+    names = declared_functions()
+    assert names, "no declarations found"
+    assert sorted(names) == sorted(pkv.EXPORTS)
+    lib = pkv.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", pkv.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+
+
+def test_status_strings_and_version(pkv):
+    lib = pkv.lib()
+    assert lib.pkv_version() == 100
+    for s in (0, -1, -2, -3, -4):
+        assert lib.pkv_status_string(s)
+    assert b"UNKNOWN" in lib.pkv_status_string(-99)
+
+
+def test_plan_is_deterministic_and_bounded(pkv):
+    p = pkv.decode_plan(32, 32, 8, 128, 256, 16, 1, 0)
+    assert p == pkv.decode_plan(32, 32, 8, 128, 256, 16, 1, 0)
+    assert p["split_tokens"] % 128 == 0 and p["num_splits"] * p["split_tokens"] >= 256 * 16
+    forced = pkv.decode_plan(8, 64, 8, 128, 1024, 128, 1, 0, split_tokens=1000)
+    assert forced["split_tokens"] == 1024 and forced["num_splits"] == 128
+    one = pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 0, split_tokens=100000)
+    assert one["num_splits"] == 1
+
+
+def _cache_struct(pkv, mode=0, hd=128, bs=16, k=16, v=32, ks=64, vs=128):
+    return pkv._CacheT(k, v, ks, vs, 4, 2, bs, hd, mode)
+
+
+def test_store_rejects_bad_arguments(pkv):
+    lib = pkv.lib()
+    P = 4096  # a fake, aligned device address: never dereferenced because validation fails first
+    c = _cache_struct(pkv)
+    r = lambda *a: lib.pkv_store_c8(*a)
+    assert r(None, P, P, 1, None, None, P, P, 1, 1, 1, 0, None) == -1          # no cache
+    assert r(ctypes.byref(c), P, P, 1, None, None, P, P, 1, 1, 1, 1, None) == -1  # mode mismatch
+    assert r(ctypes.byref(c), P, P, -1, None, None, P, P, 1, 1, 1, 0, None) == -1  # negative tokens
+    assert r(ctypes.byref(c), P, P, 0, None, None, P, P, 1, 1, 1, 0, None) == 0    # nothing to do
+    assert r(ctypes.byref(c), None, P, 1, None, None, P, P, 1, 1, 1, 0, None) == -1  # no k_new
+    assert r(ctypes.byref(c), P, P, 2, None, None, P, P, 1, 1, 1, 0, None) == -1   # decode: T != B
+    assert r(ctypes.byref(c), P, P, 1, None, None, None, P, 1, 1, 1, 0, None) == -1  # no ctx
+    bad_hd = _cache_struct(pkv, hd=96)
+    assert r(ctypes.byref(bad_hd), P, P, 1, None, None, P, P, 1, 1, 1, 0, None) == -2
+    bad_bs = _cache_struct(pkv, bs=24)
+    assert r(ctypes.byref(bad_bs), P, P, 1, None, None, P, P, 1, 1, 1, 0, None) == -2
+    per_block = _cache_struct(pkv, mode=1)
+    assert r(ctypes.byref(per_block), P, P, 1, P, None, None, None, 0, 0, 1, 1, None) == -2  # slots
+    misaligned = _cache_struct(pkv, k=17)
+    assert r(ctypes.byref(misaligned), P, P, 1, None, None, P, P, 1, 1, 1, 0, None) == -1
+    noscale = _cache_struct(pkv, ks=0)
+    assert r(ctypes.byref(noscale), P, P, 1, None, None, P, P, 1, 1, 1, 0, None) == -1
+
+
+def test_dequant_and_decode_reject_bad_arguments(pkv):
+    lib = pkv.lib()
+    P = 4096
+    c = _cache_struct(pkv)
+    assert lib.pkv_dequant(ctypes.byref(c), P, 1, P, None, 1, None, None, 256, 128, None) == -1
+    assert lib.pkv_dequant(ctypes.byref(c), P, 1, P, None, 1, P, P, 0, 128, None) == -1
+    assert lib.pkv_dequant(ctypes.byref(c), None, 1, P, None, 1, P, P, 256, 128, None) == -1
+    o = pkv._opts()
+    dec = lambda *a: lib.pkv_decode_gqa(*a)
+    # Hq not a multiple of Hkv
+    assert dec(P, 3, ctypes.byref(c), P, 8, P, None, 1, 1, 1.0, P, None, P, 1 << 30, ctypes.byref(o), None) == -1
+    # missing output
+    assert dec(P, 4, ctypes.byref(c), P, 8, P, None, 1, 1, 1.0, None, None, P, 1 << 30, ctypes.byref(o), None) == -1
+    # workspace too small for a split plan
+    need = lib.pkv_decode_workspace_size(64, 32, 2, 128, 1024, 16, 1, 0, ctypes.byref(o))
+    assert need > 0
+    assert dec(P, 32, ctypes.byref(c), P, 1024, P, None, 64, 1, 1.0, P, None, P, need - 1,
+               ctypes.byref(o), None) == -3
+    assert dec(P, 32, ctypes.byref(c), P, 1024, P, None, 64, 1, 1.0, P, None, None, 0,
+               ctypes.byref(o), None) == -3
+    # reserved option fields must be zero
+    o2 = pkv._opts()
+    o2.reserved[0] = 1
+    assert dec(P, 4, ctypes.byref(c), P, 8, P, None, 1, 1, 1.0, P, None, P, 1 << 30, ctypes.byref(o2), None) == -1
+    # unsupported head_dim
+    bad = _cache_struct(pkv, hd=80)
+    assert dec(P, 4, ctypes.byref(bad), P, 8, P, None, 1, 1, 1.0, P, None, P, 1 << 30, ctypes.byref(o), None) == -2
+    # empty batch is a no-op
+    assert dec(P, 4, ctypes.byref(c), P, 8, P, None, 0, 1, 1.0, P, None, None, 0, ctypes.byref(o), None) == 0

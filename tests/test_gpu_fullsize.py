@@ -1,0 +1,79 @@
+"""Parity at the benchmark workloads' full sizes, in the launch configuration bench.py times
+(default split plan).  The oracle recomputes the store and the attention of sampled sequences
+from the same seeded bf16 inputs; the GPU results for those sequences must match (codes and
+scales bit-exact over every page of the sequence, attention within tolerance)."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+from tests.gpu_harness import Run, oracle_run, sub_workload
+from tests.helpers import attention_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(idx, n_sample):
+    w = gen.make_config(idx)
+    r = Run(w, with_oracle=False)
+    r.store_prior()
+    r.store_new()
+    out, lse = r.decode()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(100 + idx)
+    sel = np.arange(w.batch) if n_sample >= w.batch else np.sort(rng.choice(w.batch, n_sample, replace=False))
+    print(f"config {idx} ({w.name}): checking sequences {sel.tolist()}", flush=True)
+    ws, th = sub_workload(w, sel, r.t)
+    hc, (ob, o64, olse) = oracle_run(ws, th, nthreads=16)
+    # cache pages of the sampled sequences
+    gk, gv = r.cache.k, r.cache.v
+    for j, b in enumerate(sel):
+        nblk = -(-int(w.context_lengths[b]) // w.block_size)
+        blks = torch.as_tensor(w.block_table[b, :nblk].astype(np.int64), device=gk.device)
+        n = int(w.context_lengths[b])
+        host_blks = w.block_table[b, :nblk]
+        for name, g_arr, h_arr, tok_axis in (("K", gk, hc.k, 2), ("V", gv, hc.v, 3)):
+            g = g_arr.index_select(0, blks).cpu()
+            g = (g.view(torch.int16).numpy().view(np.uint16) if w.quant_mode == 2 else g.numpy())
+            h = h_arr[host_blks]
+            # flatten the block/slot axes to positions and keep the defined ones
+            g = np.moveaxis(g, tok_axis, 1).reshape(nblk * w.block_size, *np.moveaxis(g, tok_axis, 1).shape[2:])[:n]
+            h = np.moveaxis(h, tok_axis, 1).reshape(nblk * w.block_size, *np.moveaxis(h, tok_axis, 1).shape[2:])[:n]
+            assert np.array_equal(g, h), f"{name} codes differ for sequence {b}"
+        if w.quant_mode == 0:
+            for g_s, h_s in ((r.cache.k_scale, hc.k_scale), (r.cache.v_scale, hc.v_scale)):
+                g = g_s.index_select(0, blks).cpu().numpy().transpose(0, 2, 1).reshape(-1, w.num_kv_heads)[:n]
+                h = h_s[host_blks].transpose(0, 2, 1).reshape(-1, w.num_kv_heads)[:n]
+                assert np.array_equal(g.view(np.uint32), h.view(np.uint32))
+        elif w.quant_mode == 1:
+            for g_s, h_s in ((r.cache.k_scale, hc.k_scale), (r.cache.v_scale, hc.v_scale)):
+                g = g_s.index_select(0, blks).cpu().numpy()
+                assert np.array_equal(g.view(np.uint32), h_s[host_blks].view(np.uint32))
+    # attention rows of the sampled sequences
+    if w.decode_only:
+        rows = sel
+    else:
+        cu = w.cu_q_lens
+        rows = np.concatenate([np.arange(cu[b], cu[b + 1]) for b in sel])
+    got = out[torch.as_tensor(rows, device=out.device)].float().cpu().numpy().astype(np.float64)
+    max_abs, rel, elem_ok = attention_close(got, o64)
+    print(f"config {idx}: max_abs={max_abs:.3e} rel={rel:.3e}", flush=True)
+    assert max_abs <= 1e-2 and rel <= 1e-2 and elem_ok
+    gl = lse[torch.as_tensor(rows, device=lse.device)].cpu().numpy().astype(np.float64)
+    assert np.allclose(gl, olse, rtol=1e-5, atol=1e-4)
+
+
+def test_qwen3_8b_decode_full():
+    _check(1, 32)
+
+
+def test_long_context_decode_sampled():
+    _check(2, 2)
+
+
+def test_bf16_large_batch_sampled():
+    _check(3, 24)
+
+
+def test_chunked_per_block_sampled():
+    _check(4, 12)

@@ -1,0 +1,246 @@
+"""GPU parity: libpkv (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Bars: int8 codes and fp32 scales bit-exact; dequant bit-exact; attention within max-abs 1e-2 and
+norm-relative 1e-2 of the oracle's fp64 result (elementwise |g - o| <= 1e-2 + 1e-2 |o|); lse within
+1e-4 + 1e-5 |lse|.  Sizes span several 128-key chunks, several splits and ragged tails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+import paged_kv_cache_c8_amd as pkv
+from tests.gpu_harness import Run, bits, i32
+
+pytestmark = pytest.mark.gpu
+
+
+def _wl(mode, d, bs, g, ctx, ql=None, hkv=2, seed=0, **kw):
+    return gen.custom_workload(f"m{mode}-d{d}-bs{bs}-g{g}", batch=len(ctx), num_q_heads=hkv * g,
+                               num_kv_heads=hkv, head_dim=d, block_size=bs, quant_mode=mode,
+                               context_lengths=ctx, q_lens=ql, seed=seed, **kw)
+
+
+def test_tiny_config_end_to_end():
+    r = Run(gen.make_config(0))
+    r.store_prior()
+    r.store_new()
+    r.assert_cache_equal()
+    out, lse = r.decode()
+    r.assert_decode_close(out, lse)
+
+
+DECODE_CASES = [
+    # mode, D, BS, G, context lengths
+    (0, 128, 16, 4, [1, 2, 15, 16, 17, 127, 128, 129, 300, 1000]),
+    (0, 128, 128, 8, [1, 129, 257, 700, 1500]),
+    (0, 64, 16, 4, [37, 100, 5, 260]),
+    (0, 64, 32, 8, [33, 64, 65, 500]),
+    (0, 128, 64, 2, [63, 64, 65, 900]),
+    (0, 128, 16, 1, [50, 333]),
+    (0, 128, 16, 5, [40, 257, 129]),
+    (0, 128, 16, 16, [77, 600]),
+    (2, 128, 16, 4, [1, 16, 17, 129, 513]),
+    (2, 64, 128, 8, [200, 1, 129]),
+    (1, 128, 16, 4, [20, 129, 300]),
+    (1, 64, 64, 8, [65, 1, 200]),
+]
+
+
+@pytest.mark.parametrize("mode,d,bs,g,ctx", DECODE_CASES)
+def test_decode_matches_oracle(mode, d, bs, g, ctx):
+    r = Run(_wl(mode, d, bs, g, ctx, seed=len(ctx) + d + bs + g))
+    r.store_prior()
+    r.store_new()
+    r.assert_cache_equal()
+    out, lse = r.decode()
+    ref = r.oracle_decode()
+    r.assert_decode_close(out, lse, ref)
+    # several partitions of the keys: the same result within rounding
+    for split in (128, 256):
+        o2, l2 = r.decode(split_tokens=split)
+        r.assert_decode_close(o2, l2, ref)
+
+
+CHUNK_CASES = [
+    # mode, D, BS, G, context lengths, q_lens
+    (1, 128, 16, 5, [20, 40, 16, 300], [3, 16, 1, 7]),
+    (1, 128, 16, 4, [1, 17, 33, 129], [1, 16, 2, 9]),
+    (0, 128, 16, 4, [70, 9, 200], [5, 9, 16]),
+    (0, 64, 32, 2, [300, 31], [12, 31]),
+    (2, 128, 16, 8, [50, 129], [4, 13]),
+]
+
+
+@pytest.mark.parametrize("mode,d,bs,g,ctx,ql", CHUNK_CASES)
+def test_chunked_store_and_causal_decode(mode, d, bs, g, ctx, ql):
+    r = Run(_wl(mode, d, bs, g, ctx, ql, seed=sum(ctx)))
+    r.store_prior()
+    r.store_new()
+    r.assert_cache_equal()
+    out, lse = r.decode()
+    ref = r.oracle_decode()
+    r.assert_decode_close(out, lse, ref)
+    o2, l2 = r.decode(split_tokens=128)
+    r.assert_decode_close(o2, l2, ref)
+
+
+def test_split_count_agreement_and_determinism():
+    r = Run(_wl(0, 128, 16, 4, [3000, 1200, 4096, 64], seed=5), with_oracle=False)
+    r.store_prior()
+    r.store_new()
+    one, l1 = r.decode(split_tokens=4096)
+    many, lm = r.decode(split_tokens=128)
+    default, ld = r.decode()
+    default2, ld2 = r.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(default.view(torch.int16), default2.view(torch.int16))
+    assert torch.equal(ld, ld2)
+    # within one bf16 step of each other, lse within 1e-5 relative
+    for o, l in ((many, lm), (default, ld)):
+        diff = (o.float() - one.float()).abs()
+        step = one.float().abs().clamp_min(2.0 ** -126) * 2.0 ** -7
+        assert bool((diff <= step + 1e-6).all())
+        assert torch.allclose(l, l1, rtol=1e-5, atol=1e-5)
+
+
+def test_block_permutation_invariance_on_gpu():
+    ctx = [700, 45, 1300]
+    w1 = _wl(0, 128, 16, 4, ctx, seed=1)
+    w2 = _wl(0, 128, 16, 4, ctx, seed=2)
+    assert not np.array_equal(w1.block_table, w2.block_table)
+    r1 = Run(w1, with_oracle=False)
+    r2 = Run(w2, with_oracle=False, tensors=r1.t)
+    for r in (r1, r2):
+        r.store_prior()
+        r.store_new()
+    o1, l1 = r1.decode()
+    o2, l2 = r2.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_inactive_sequences_give_zero_and_minus_inf():
+    r = Run(_wl(0, 128, 16, 4, [0, 50, 0, 300], seed=3))
+    r.store_prior()
+    r.store_new()
+    r.assert_cache_equal()
+    for split in (0, 128):
+        out, lse = r.decode(split_tokens=split)
+        torch.cuda.synchronize()
+        assert bool((out[0] == 0).all()) and bool((out[2] == 0).all())
+        assert bool(torch.isneginf(lse[0]).all()) and bool(torch.isneginf(lse[2]).all())
+        r.assert_decode_close(out, lse)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_exhaustive_bf16_sweep_through_store(d):
+    """Every finite bf16 value as the absmax of one token (others: seeded values below it)."""
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    b = b[((b >> 7) & 0xFF) != 0xFF]
+    vals = (b.astype(np.uint32) << 16).view(np.float32)
+    vals = vals[vals != 0]
+    rng = np.random.default_rng(d)
+    frac = rng.uniform(-1, 1, size=(len(vals), d - 1)).astype(np.float32)
+    others = ((np.abs(vals)[:, None] * frac).view(np.uint32) & 0xFFFF0000).view(np.float32)
+    rows = np.concatenate([vals[:, None], others], axis=1)
+    rows_bits = (rows.view(np.uint32) >> 16).astype(np.uint16).reshape(-1, 1, d)
+    t = len(rows)
+    bs = 16
+    nb = -(-t // bs)
+    dev = torch.device("cuda")
+    x = torch.from_numpy(rows_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    cache = pkv.Cache(0, nb, 1, bs, d, device=dev)
+    slots = torch.arange(t, dtype=torch.int64, device=dev)
+    pkv.store_c8(cache, x, x, slot_mapping=slots)
+    hc = oracle.HostCache(0, nb, 1, bs, d)
+    oracle.store(hc, rows_bits, rows_bits, slot_mapping=np.arange(t, dtype=np.int64))
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.k.cpu().numpy(), hc.k)
+    assert np.array_equal(cache.v.cpu().numpy(), hc.v)
+    assert np.array_equal(cache.k_scale.cpu().numpy().view(np.uint32), hc.k_scale.view(np.uint32))
+    assert np.array_equal(cache.v_scale.cpu().numpy().view(np.uint32), hc.v_scale.view(np.uint32))
+
+
+def test_slot_mapping_store_with_skips():
+    dev = torch.device("cuda")
+    w = _wl(0, 128, 32, 4, [10, 70], seed=8)
+    t = gen.gen_tensors(w, device=dev)
+    n = w.total_tokens
+    rng = np.random.default_rng(0)
+    slots = rng.permutation(w.num_blocks * w.block_size)[:n].astype(np.int64)
+    slots[::7] = -1
+    cache = pkv.Cache(0, w.num_blocks, 2, 32, 128, device=dev)
+    pkv.store_c8(cache, t["k_all"], t["v_all"], slot_mapping=torch.as_tensor(slots, device=dev))
+    hc = oracle.HostCache(0, w.num_blocks, 2, 32, 128)
+    oracle.store(hc, bits(t["k_all"]), bits(t["v_all"]), slot_mapping=slots)
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.k.cpu().numpy(), hc.k)
+    assert np.array_equal(cache.v.cpu().numpy(), hc.v)
+    assert np.array_equal(cache.k_scale.cpu().numpy().view(np.uint32), hc.k_scale.view(np.uint32))
+
+
+@pytest.mark.parametrize("mode,d,bs", [(0, 128, 16), (1, 128, 16), (2, 128, 16), (0, 64, 128),
+                                       (1, 64, 32), (2, 64, 64)])
+def test_dequant_bit_exact(mode, d, bs):
+    ql = [1, 5, 16] if mode == 1 else None
+    w = _wl(mode, d, bs, 2, [1, 40, 300], ql, seed=d + bs)
+    r = Run(w)
+    r.store_prior()
+    r.store_new()
+    k, v = pkv.dequant(r.cache, r.bt, r.ctx)
+    ko, vo = oracle.dequant(r.hc, w.block_table, w.context_lengths)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(k).reshape(-1), ko[:k.numel()])
+    assert np.array_equal(bits(v).reshape(-1), vo[:v.numel()])
+
+
+def test_dequant_padded_offsets_and_strides():
+    w = _wl(0, 128, 16, 2, [5, 0, 40, 17], seed=4)
+    r = Run(w)
+    r.store_prior()
+    r.store_new()
+    pad = np.array([3, 7, 2, 5])
+    offs = np.zeros(4, np.int64)
+    offs[1:] = np.cumsum(w.context_lengths + pad)[:-1]
+    rows = int((offs + w.context_lengths + pad).max())
+    hkv, d = 2, 128
+    for token_stride, head_stride in ((d, rows * d), (hkv * d + 8, d), (hkv * d + 3, d + 1)):
+        n = rows * max(token_stride, 1) + hkv * head_stride + d
+        kd = torch.full((n,), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        vd = torch.full((n,), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        pkv.dequant(r.cache, r.bt, r.ctx, seq_offsets=torch.as_tensor(offs, device="cuda"), k_out=kd,
+                    v_out=vd, token_stride=token_stride, head_stride=head_stride)
+        ko = np.full(n, 0xFFFF, np.uint16)
+        vo = np.full(n, 0xFFFF, np.uint16)
+        oracle.dequant(r.hc, w.block_table, w.context_lengths, seq_offsets=offs, k_out=ko, v_out=vo,
+                       token_stride=token_stride, head_stride=head_stride)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(kd), ko)
+        assert np.array_equal(bits(vd), vo)
+
+
+def test_per_block_rescale_sequence_matches_oracle():
+    """Several chunk stores into the same blocks (scales grow, codes re-quantized)."""
+    dev = torch.device("cuda")
+    bs, d, hkv = 16, 128, 2
+    steps = [(0, 5), (5, 9), (9, 30), (30, 31), (31, 64)]
+    total = steps[-1][1]
+    bt = np.array([[3, 0, 2, 1]], np.int32)
+    g = torch.Generator(device=dev).manual_seed(3)
+    growth = torch.linspace(0.5, 8.0, total, device=dev)[:, None, None]
+    x = (torch.randn(total, hkv, d, generator=g, device=dev) * growth).to(torch.bfloat16)
+    cache = pkv.Cache(1, 4, hkv, bs, d, device=dev)
+    hc = oracle.HostCache(1, 4, hkv, bs, d)
+    for lo, hi in steps:
+        cu = np.array([0, hi - lo], np.int32)
+        ctx = np.array([hi], np.int32)
+        pkv.store_c8(cache, x[lo:hi], x[lo:hi], cu_q_lens=i32(cu, dev), context_lengths=i32(ctx, dev),
+                     block_table=i32(bt, dev), max_q_len=hi - lo)
+        oracle.store(hc, bits(x[lo:hi]), bits(x[lo:hi]), cu_q_lens=cu, context_lengths=ctx, block_table=bt)
+        torch.cuda.synchronize()
+        assert np.array_equal(cache.k.cpu().numpy(), hc.k), (lo, hi)
+        assert np.array_equal(cache.v.cpu().numpy(), hc.v), (lo, hi)
+        assert np.array_equal(cache.k_scale.cpu().numpy().view(np.uint32), hc.k_scale.view(np.uint32))

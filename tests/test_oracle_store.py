@@ -267,3 +267,26 @@ def test_slot_mapping_rejected_for_per_block():
     x = np.zeros((1, 1, 8), np.uint16)
     with pytest.raises(ValueError):
         oracle.store(c, x, x, slot_mapping=np.zeros(1, np.int64))
+
+
+def test_inactive_decode_slot_stores_nothing():
+    """A decode batch slot with context length 0 has no position: its row is ignored and no
+    memory outside the live blocks changes."""
+    import torch
+    from tests.helpers import torch_bf16_to_bits
+
+    w = custom_workload("inactive", batch=3, num_q_heads=2, num_kv_heads=2, head_dim=16, block_size=16,
+                        quant_mode=0, context_lengths=[0, 5, 0], seed=2)
+    x = torch_bf16_to_bits(torch.randn(3, 2, 16, generator=torch.Generator().manual_seed(0)).to(torch.bfloat16))
+    for mode in (0, 1, 2):
+        c = oracle.HostCache(mode, w.num_blocks, 2, 16, 16, fill=7)
+        ref = c.copy()
+        oracle.store(c, x, x, context_lengths=w.context_lengths, block_table=w.block_table)
+        blk, slot = w.block_table[1, 0], 4
+        # per-token and bf16 modes touch only the new token's slot; the per-block mode may also
+        # re-quantize the earlier slots of that block
+        ok = (lambda s: s == slot) if mode != 1 else (lambda s: s <= slot)
+        changed_k = np.argwhere(c.k != ref.k)
+        assert len(changed_k) and all(b == blk and ok(s) for b, _, s, _ in changed_k)
+        changed_v = np.argwhere(c.v != ref.v)
+        assert len(changed_v) and all(b == blk and ok(s) for b, _, _, s in changed_v)
