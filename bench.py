@@ -40,6 +40,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1, help="workload index (0..4); 1 = Qwen3-8B decode")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--kernel", type=int, default=0, help="0 = library choice, 1 = VALU, 2 = MFMA")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-baseline sample")
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = auto)")
@@ -142,11 +143,11 @@ def main():
     scale = 1.0 / float(np.sqrt(w.head_dim))
     mql = w.max_q_len if cu_q is not None else 1
     ws_bytes = pkv.decode_workspace_size(w.batch, w.num_q_heads, caches[0], w.max_blocks_per_seq, mql,
-                                         split_tokens=args.split_tokens)
-    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+                                         split_tokens=args.split_tokens, kernel=args.kernel)
+    workspace = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)  # zero-filled once
     out = torch.empty_like(q)
     plan = pkv.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_blocks_per_seq,
-                           w.block_size, mql, w.quant_mode, split_tokens=args.split_tokens)
+                           w.block_size, mql, w.quant_mode, split_tokens=args.split_tokens, kernel=args.kernel)
 
     def store(c):
         if w.decode_only:
@@ -157,7 +158,7 @@ def main():
 
     def decode(c):
         pkv.decode_gqa(q, c, bt, ctx, scale, cu_q_lens=cu_q, max_q_len=mql, out=out, workspace=workspace,
-                       split_tokens=args.split_tokens)
+                       split_tokens=args.split_tokens, kernel=args.kernel)
 
     def step(i):
         c = caches[i % reps]
@@ -224,6 +225,7 @@ def main():
             "head_dim": w.head_dim, "block_size": w.block_size, "quant_mode": w.quant_mode,
             "sum_context": int(w.context_lengths.sum()), "new_tokens": new_tokens,
             "cache_replicas": reps, "split_tokens": plan["split_tokens"], "num_splits": plan["num_splits"],
+            "kernel": {1: "valu", 2: "mfma"}[plan["kernel"]],
             "parallelism": "single-gpu",
         },
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),

@@ -38,7 +38,7 @@
  *           PKV_QUANT_PER_BLOCK: float [num_blocks][num_kv_heads]
  *           PKV_QUANT_NONE_BF16: none (K and V hold bf16)
  *   int8 codes for the quantized modes, bf16 for PKV_QUANT_NONE_BF16.
- *   K, V: 16-byte aligned; scales: 4-byte aligned.
+ *   K, V and the scale arrays: 16-byte aligned.
  *   Supported: head_dim 64 or 128; block_size 16, 32, 64 or 128.
  */
 #ifndef PKV_H
@@ -148,8 +148,9 @@ int pkv_dequant(const pkv_cache_t *cache, const int32_t *block_table, int32_t ma
 /* Optional knobs of pkv_decode_gqa (pass NULL for the defaults). */
 typedef struct {
     int32_t split_tokens; /* keys per split-KV partition; 0 = planned from the shapes.
-                             Rounded up to a multiple of 128. */
-    int32_t kernel;       /* 0 = choose; 1 = VALU split-KV kernel; 2 = MFMA kernel */
+                             Rounded up to a multiple of 128, at most 4096. */
+    int32_t kernel;       /* 0 = choose (the MFMA kernel); 1 = VALU split-KV kernel
+                             (dot2 + DPP reductions); 2 = MFMA kernel */
     int32_t reserved[6];  /* must be zero */
 } pkv_decode_opts_t;
 
@@ -176,7 +177,9 @@ size_t pkv_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num
  *          (whose output is 0).
  * max_q_len host-known upper bound of q_len_b (1 for pure decode).
  * workspace / workspace_bytes: caller scratch of at least
- *          pkv_decode_workspace_size(...) bytes, 256-byte aligned.
+ *          pkv_decode_workspace_size(...) bytes, 16-byte aligned (split
+ *          partials; no initial contents needed).  Calls that run
+ *          concurrently must not share a workspace.
  */
 int pkv_decode_gqa(const void *q, int32_t num_q_heads, const pkv_cache_t *cache,
                    const int32_t *block_table, int32_t max_blocks_per_seq,

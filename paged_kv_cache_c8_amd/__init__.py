@@ -204,7 +204,7 @@ def decode_gqa(q, cache: Cache, block_table, context_lengths, scale, *, cu_q_len
                                                cache.block_size, max_q_len, cache.quant_mode,
                                                ctypes.byref(o)))
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # tickets start at zero
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().pkv_decode_gqa(_ptr(q), hq, cache.ref, _ptr(block_table), mbs, _ptr(context_lengths),
                               _ptr(cu_q_lens), batch, int(max_q_len), float(scale), _ptr(out),

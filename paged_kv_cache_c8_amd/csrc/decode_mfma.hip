@@ -1,0 +1,455 @@
+// decode_mfma.hip - grouped-query attention over the paged cache on the matrix cores (gfx950).
+//
+// Same result as decode_valu.hip (MojoPagedDecodeGQA, Mojo Opset README Op List), built for the
+// HBM roofline of MI355X: at 8 TB/s a compute unit has about 80 SIMD-cycles per (key, KV head),
+// while int8 -> fp16 conversion plus dot products on the vector ALUs need more than that, so
+// both contractions of every key block run as v_mfma_f32_16x16x32_{f16,bf16} and the vector
+// ALUs only convert codes and do the softmax bookkeeping.
+//
+// One wave per (sequence, KV head, row group, key split); no barriers in the main loop.  A row
+// group is RT tiles of 16 query rows (row r = i * G + g: query i of the chunk, head g of the KV
+// head's group); the keys of the split are walked in blocks of 32, the next block's K, V and
+// scales in flight while the current one computes.
+//
+//   scores  S^T (keys x rows) = K . Q^T: K is the A operand - lane (rho, kg) holds 32 (int8) /
+//           16 (bf16) contiguous bytes of one token-major K row - and the query tile is B.  The
+//           key behind row slot rho of score tile u is 8*(rho/4) + 4u + rho%4, so that in the
+//           output lane (n, g) holds keys 8g .. 8g+7 of query row n.  int8 codes become fp16 exactly
+//           (byte permute into 0x64xx, subtract 1152); the query row is pre-scaled by a power of two
+//           into fp16's normal range and the factor removed with the per-key K scale.
+//   softmax online over blocks, per query row (lane column n; rows meet across lanes n+16k).
+//           The weights p * s_v / S (S = running max of the V scales, so the fp16 weights stay in
+//           [0, 1]) of keys 8g .. 8g+7 are exactly lane (n, g)'s slice of the P operand.
+//   P.V     O (rows x channels) += P . V: the channel-major V page gives the 8 keys of one channel
+//           as 8 contiguous bytes - the B operand - with no transpose.  When a row's running max
+//           or S grows, its accumulator row is rescaled (rows 4g+i of lane g; factors fetched from
+//           the lanes that own those rows).
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int BLK = 32;                 // keys per block
+constexpr int MAX_SPLIT = 4096;         // keys per split (planner limit)
+constexpr int MAX_SPLIT_BLOCKS = MAX_SPLIT / 16;
+
+template <int D, int MODE>
+struct MCfg {
+    static constexpr int ESZ = MODE == 2 ? 2 : 1;
+    static constexpr int KS = D / 32;        // 32-channel k-steps of the score MFMA
+    static constexpr int DT = D / 16;        // 16-channel tiles of the output
+    static constexpr int KB = 8 * KS * ESZ;  // K bytes per lane per score tile
+    static constexpr int KL = KB / 16;       // 16-byte K loads per lane per score tile
+    static constexpr int VW = 2 * ESZ;       // V dwords per lane per channel tile (8 keys)
+};
+
+template <int D, int MODE>
+struct BlockRegs {
+    using C = MCfg<D, MODE>;
+    u32x4 k[2][C::KL];
+    uint32_t v[C::DT][C::VW];
+    float ks[8];
+    float vs[8];
+};
+
+// four int8 codes -> two fp16 pairs, exactly
+__device__ __forceinline__ void codes_to_h2(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    const uint32_t u = w ^ 0x80808080u;  // code + 128 as an unsigned byte
+    const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+    lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - bias);
+    hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - bias);
+}
+
+// eight int8 codes (two dwords) -> an fp16 MFMA operand
+__device__ __forceinline__ h8 codes_to_h8(uint32_t w0, uint32_t w1) {
+    uint32_t r[4];
+    codes_to_h2(w0, r[0], r[1]);
+    codes_to_h2(w1, r[2], r[3]);
+    return __builtin_bit_cast(h8, r);
+}
+
+__device__ __forceinline__ float xor16_max(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16, kWave));
+    return fmaxf(x, __shfl_xor(x, 32, kWave));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+    x += __shfl_xor(x, 16, kWave);
+    return x + __shfl_xor(x, 32, kWave);
+}
+
+template <int D, int MODE, int RT>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
+    using C = MCfg<D, MODE>;
+    __shared__ int bt_s[MAX_SPLIT_BLOCKS];
+
+    const int lane = threadIdx.x;
+    const int n = lane & 15;   // query row within a tile (score/P layout), channel (output layout)
+    const int g = lane >> 4;   // lane group
+
+    int wi = blockIdx.x;
+    const int s = wi % a.nsplit;
+    wi /= a.nsplit;
+    const int item = wi;
+    const int rg = wi % a.nrg;
+    wi /= a.nrg;
+    const int h = wi % a.hkv;
+    const int b = wi / a.hkv;
+
+    const int qlen = a.cu ? a.cu[b + 1] - a.cu[b] : 1;
+    const int qrow0 = a.cu ? a.cu[b] : b;
+    const int ctx = a.ctx[b];
+    const int prior = ctx - qlen;
+    const int nrows = qlen * a.g;
+    const int r0 = rg * (16 * RT);
+    if (r0 >= nrows) return;
+    const int nvalid = min(16 * RT, nrows - r0);
+    const int kmax = prior + (r0 + nvalid - 1) / a.g + 1;
+    const int t_begin = s * a.split_len;
+
+    if (kmax <= 0) {  // inactive sequence: zero output, lse = -inf
+        if (s == 0) {
+            for (int o = lane; o < nvalid * D; o += kWave) {
+                const int j = o / D, d = o % D;
+                const int r = r0 + j;
+                const int64_t orow = (int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g;
+                a.out[orow * D + d] = 0;
+                if (d == 0 && a.lse) a.lse[orow] = -INFINITY;
+            }
+        }
+        return;
+    }
+    if (t_begin >= kmax) return;
+    const int t_end = min(t_begin + a.split_len, kmax);
+
+    const int blk0 = t_begin >> a.log2bs;
+    const int nblk = ((t_end - 1) >> a.log2bs) - blk0 + 1;
+    for (int i = lane; i < nblk; i += kWave) bt_s[i] = a.bt[(int64_t)b * a.mbs + blk0 + i];
+
+    // ---- query tiles (B operand of the score MFMA): lane (n, g) holds row n's channels
+    //      g*8*KS .. +8*KS, k-step m taking the 8 channels g*8*KS + 8m .. +8
+    uint32_t qb[RT][C::KS][4];
+    float rowmul[RT];
+    int lim[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int j = rt * 16 + n;
+        const bool rv = j < nvalid;
+        const int r = r0 + j;
+        lim[rt] = rv ? prior + r / a.g : -1;
+        uint32_t raw[C::KS][4];
+        if (rv) {
+            const uint16_t* qp = a.q + ((int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g) * D + g * 8 * C::KS;
+#pragma unroll
+            for (int m = 0; m < C::KS; ++m) {
+                const u32x4 w = load16(qp + 8 * m);
+                raw[m][0] = w.x; raw[m][1] = w.y; raw[m][2] = w.z; raw[m][3] = w.w;
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < C::KS; ++m) raw[m][0] = raw[m][1] = raw[m][2] = raw[m][3] = 0;
+        }
+        if constexpr (MODE == 2) {
+#pragma unroll
+            for (int m = 0; m < C::KS; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qb[rt][m][e] = raw[m][e];
+            rowmul[rt] = a.scale_log2;
+        } else {
+            float mx = 0.0f;
+#pragma unroll
+            for (int m = 0; m < C::KS; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    mx = fmaxf(mx, fmaxf(fabsf(bf16_to_f32(raw[m][e] & 0xffffu)), fabsf(bf16_to_f32(raw[m][e] >> 16))));
+            mx = xor16_max(mx);
+            int ex = 0;
+            if (mx > 0.0f) (void)frexpf(mx, &ex);       // mx in [2^(ex-1), 2^ex)
+            const int k = min(120, max(-120, 15 - ex));  // mx * 2^k in [2^14, 2^15)
+            const float up = ldexpf(1.0f, k);
+#pragma unroll
+            for (int m = 0; m < C::KS; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const h2 v = {(_Float16)(bf16_to_f32(raw[m][e] & 0xffffu) * up),
+                                  (_Float16)(bf16_to_f32(raw[m][e] >> 16) * up)};
+                    qb[rt][m][e] = __builtin_bit_cast(uint32_t, v);
+                }
+            rowmul[rt] = ldexpf(a.scale_log2, -k);
+        }
+    }
+
+    float m_run[RT], l_run[RT];
+    f4 acc[RT][C::DT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        m_run[rt] = -INFINITY;
+        l_run[rt] = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) acc[rt][dt] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+    float s_run = 0.0f;  // running max of the V scales (1 for bf16 pages)
+
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k);
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v);
+    const int rho = lane & 15;
+    const int kg = lane >> 4;
+    __syncthreads();  // bt_s
+
+    auto load_block = [&](int T, BlockRegs<D, MODE>& R) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            int t = T + 8 * (rho >> 2) + 4 * u + (rho & 3);
+            if (t >= t_end) t = t_begin;  // in-bounds stand-in, masked later
+            const int64_t page = (int64_t)bt_s[(t >> a.log2bs) - blk0] * a.hkv + h;
+            const uint8_t* kp = kbase + ((page * a.bs + (t & (a.bs - 1))) * D) * C::ESZ + kg * C::KB;
+#pragma unroll
+            for (int l = 0; l < C::KL; ++l) R.k[u][l] = load16(kp + 16 * l);
+        }
+        int t0 = T + 8 * g;
+        if (t0 >= t_end) t0 = t_begin;
+        const int64_t page = (int64_t)bt_s[(t0 >> a.log2bs) - blk0] * a.hkv + h;
+        const int slot0 = t0 & (a.bs - 1);
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+            const uint8_t* vp = vbase + (((page * D + dt * 16 + n) * a.bs) + slot0) * C::ESZ;
+            if constexpr (C::VW == 2) {
+                const uint2 w = *reinterpret_cast<const uint2*>(vp);
+                R.v[dt][0] = w.x; R.v[dt][1] = w.y;
+            } else {
+                const uint4 w = *reinterpret_cast<const uint4*>(vp);
+                R.v[dt][0] = w.x; R.v[dt][1] = w.y; R.v[dt][2] = w.z; R.v[dt][3] = w.w;
+            }
+        }
+        if constexpr (MODE == 0) {
+            const float4* kq = reinterpret_cast<const float4*>(a.ks + page * a.bs + slot0);
+            const float4* vq = reinterpret_cast<const float4*>(a.vs + page * a.bs + slot0);
+            const float4 k0 = kq[0], k1 = kq[1], v0 = vq[0], v1 = vq[1];
+            R.ks[0] = k0.x; R.ks[1] = k0.y; R.ks[2] = k0.z; R.ks[3] = k0.w;
+            R.ks[4] = k1.x; R.ks[5] = k1.y; R.ks[6] = k1.z; R.ks[7] = k1.w;
+            R.vs[0] = v0.x; R.vs[1] = v0.y; R.vs[2] = v0.z; R.vs[3] = v0.w;
+            R.vs[4] = v1.x; R.vs[5] = v1.y; R.vs[6] = v1.z; R.vs[7] = v1.w;
+        } else if constexpr (MODE == 1) {
+            const float kk = a.ks[page], vv = a.vs[page];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { R.ks[e] = kk; R.vs[e] = vv; }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { R.ks[e] = 1.0f; R.vs[e] = 1.0f; }
+        }
+    };
+
+    BlockRegs<D, MODE> cur, nxt;
+    load_block(t_begin, cur);
+
+    for (int T = t_begin; T < t_end; T += BLK) {
+        if (T + BLK < t_end) load_block(T + BLK, nxt);
+
+        // ------------------------------------------------ scores: two 16-key tiles per row tile
+        f4 sc[RT][2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) sc[rt][u] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < C::KS; ++m) {
+                if constexpr (MODE == 2) {
+                    const u32x4 w = cur.k[u][m];  // 8 bf16 = one 16-byte load per k-step
+                    const uint32_t r[4] = {w.x, w.y, w.z, w.w};
+                    const b8 av = __builtin_bit_cast(b8, r);
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        sc[rt][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            av, __builtin_bit_cast(b8, qb[rt][m]), sc[rt][u], 0, 0, 0);
+                } else {
+                    const u32x4 w = cur.k[u][m / 2];  // 8 codes per k-step: dwords (2m, 2m+1)
+                    const h8 av = (m & 1) ? codes_to_h8(w.z, w.w) : codes_to_h8(w.x, w.y);
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        sc[rt][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            av, __builtin_bit_cast(h8, qb[rt][m]), sc[rt][u], 0, 0, 0);
+                }
+            }
+        }
+
+        // ------------------------------------------------ online softmax, P operand
+        float vmax = 0.0f;
+        if constexpr (MODE != 2) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (T + 8 * g + e < t_end) vmax = fmaxf(vmax, cur.vs[e]);
+            vmax = xor16_max(vmax);
+        }
+        const float s_new = MODE == 2 ? 1.0f : fmaxf(s_run, vmax);
+        const float sf = (MODE == 2 || s_run == 0.0f) ? 1.0f : s_run / s_new;
+        const float inv_s = s_new > 0.0f ? 1.0f / s_new : 0.0f;
+        s_run = s_new;
+
+        uint32_t pa[RT][4];
+        float factor[RT];
+        bool any_rescale = false;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float sv[8];
+            float bmax = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int t = T + 8 * g + e;
+                const float raw = sc[rt][e >> 2][e & 3];
+                sv[e] = (t < t_end && t <= lim[rt]) ? raw * cur.ks[e] * rowmul[rt] : -INFINITY;
+                bmax = fmaxf(bmax, sv[e]);
+            }
+            bmax = xor16_max(bmax);
+            const float m_new = fmaxf(m_run[rt], bmax);
+            const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run[rt] - m_new);
+            float p[8];
+            float psum = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p[e] = (sv[e] == -INFINITY) ? 0.0f : exp2f(sv[e] - m_new);
+                psum += p[e];
+            }
+            psum = xor16_sum(psum);
+            l_run[rt] = l_run[rt] * alpha + psum;
+            m_run[rt] = m_new;
+            factor[rt] = alpha * sf;
+            any_rescale |= factor[rt] != 1.0f;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                if constexpr (MODE == 2) {
+                    pa[rt][e2] = f32_to_bf16_rne(p[2 * e2]) | (f32_to_bf16_rne(p[2 * e2 + 1]) << 16);
+                } else {
+                    const h2 w = {(_Float16)(p[2 * e2] * (cur.vs[2 * e2] * inv_s)),
+                                  (_Float16)(p[2 * e2 + 1] * (cur.vs[2 * e2 + 1] * inv_s))};
+                    pa[rt][e2] = __builtin_bit_cast(uint32_t, w);
+                }
+            }
+        }
+
+        // ------------------------------------------------ rescale rows whose max or S grew
+        if (__any(any_rescale)) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float f = __shfl(factor[rt], 4 * g + i, kWave);  // factor of row 4g+i
+#pragma unroll
+                    for (int dt = 0; dt < C::DT; ++dt) acc[rt][dt][i] *= f;
+                }
+            }
+        }
+
+        // ------------------------------------------------ P.V over the 32 keys
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+            if constexpr (MODE == 2) {
+                uint32_t r[4] = {cur.v[dt][0], cur.v[dt][1], cur.v[dt][2], cur.v[dt][3]};
+                // bf16 slots past the keys may hold any bit pattern: zero them
+                const int tk = T + 8 * g;
+                if (tk + 8 > t_end) {
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        if (tk + 2 * e2 >= t_end) r[e2] = 0;
+                        else if (tk + 2 * e2 + 1 >= t_end) r[e2] &= 0xffffu;
+                    }
+                }
+                const b8 bv = __builtin_bit_cast(b8, r);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, pa[rt]), bv,
+                                                                          acc[rt][dt], 0, 0, 0);
+            } else {
+                const h8 bv = codes_to_h8(cur.v[dt][0], cur.v[dt][1]);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, pa[rt]), bv,
+                                                                         acc[rt][dt], 0, 0, 0);
+            }
+        }
+        cur = nxt;
+    }
+
+    // ---- normalise and write: lane (channel n, group g) holds rows 4g+i of every channel tile
+    const bool split_mode = a.nsplit > 1;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = rt * 16 + 4 * g + i;  // row within the group
+            const float l = __shfl(l_run[rt], 4 * g + i, kWave);
+            const float m = __shfl(m_run[rt], 4 * g + i, kWave);
+            if (j >= nvalid) continue;
+            const float mul = l > 0.0f ? s_run / l : 0.0f;
+            const int r = r0 + j;
+            const int64_t orow = (int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g;
+            const int64_t prow = ((int64_t)item * a.nsplit + s) * a.prs + j;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) {
+                const float o = acc[rt][dt][i] * mul;
+                const int d = dt * 16 + n;
+                if (!split_mode) a.out[orow * D + d] = (uint16_t)f32_to_bf16_rne(o);
+                else a.part_o[prow * D + d] = o;
+            }
+            if (n == 0) {
+                const float lse2 = l > 0.0f ? m + log2f(l) : -INFINITY;
+                if (!split_mode) {
+                    if (a.lse) a.lse[orow] = lse2 * kLn2;
+                } else {
+                    a.part_lse[prow] = lse2;
+                }
+            }
+        }
+    }
+}
+
+template <int D, int MODE, int RT>
+hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream) {
+    const int64_t items = (int64_t)batch * a.hkv * a.nrg;
+    const int64_t grid = items * a.nsplit;
+    if (grid == 0) return hipSuccess;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_mfma_kernel<D, MODE, RT>), dim3((unsigned)grid), dim3(64), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    return launch_merge(a, batch, D, 16 * RT, stream);
+}
+
+template <int D, int MODE>
+hipError_t launch_rt(const DecodeArgs& a, int batch, int rt, hipStream_t stream) {
+    switch (rt) {
+        case 1: return launch_one<D, MODE, 1>(a, batch, stream);
+        case 2: return launch_one<D, MODE, 2>(a, batch, stream);
+        case 3: return launch_one<D, MODE, 3>(a, batch, stream);
+        case 4: return launch_one<D, MODE, 4>(a, batch, stream);
+        case 5: return launch_one<D, MODE, 5>(a, batch, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int D>
+hipError_t launch_mode(const DecodeArgs& a, int batch, int rt, int mode, hipStream_t stream) {
+    switch (mode) {
+        case 0: return launch_rt<D, 0>(a, batch, rt, stream);
+        case 1: return launch_rt<D, 1>(a, batch, rt, stream);
+        case 2: return launch_rt<D, 2>(a, batch, rt, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int batch, int head_dim, int row_tiles, int mode,
+                              hipStream_t stream) {
+    if (a.split_len > MAX_SPLIT || (a.split_len % 128) != 0) return hipErrorInvalidValue;
+    if (head_dim == 64) return launch_mode<64>(a, batch, row_tiles, mode, stream);
+    if (head_dim == 128) return launch_mode<128>(a, batch, row_tiles, mode, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

@@ -43,17 +43,22 @@ int check_cache(const pkv_cache_t* c) {
     if (c->quant_mode < 0 || c->quant_mode > 2) return PKV_ERR_UNSUPPORTED;
     if (c->quant_mode != PKV_QUANT_NONE_BF16 && (!c->k_scale || !c->v_scale)) return PKV_ERR_INVALID_ARG;
     if (!aligned(c->k, 16) || !aligned(c->v, 16)) return PKV_ERR_INVALID_ARG;
-    if (c->k_scale && !aligned(c->k_scale, 4)) return PKV_ERR_INVALID_ARG;
-    if (c->v_scale && !aligned(c->v_scale, 4)) return PKV_ERR_INVALID_ARG;
+    if (c->k_scale && !aligned(c->k_scale, 16)) return PKV_ERR_INVALID_ARG;
+    if (c->v_scale && !aligned(c->v_scale, 16)) return PKV_ERR_INVALID_ARG;
     return PKV_OK;
 }
 
+constexpr int64_t kMaxSplit = 4096;      // keys per split the decode kernel accepts
+constexpr int64_t kMaxSplitRows = 4096;  // splits x rows one merge can combine
+
 struct DecodePlan {
-    int rg;
+    int kernel;        // 1 VALU, 2 MFMA
+    int rg;            // VALU: rows per row group (1, 2, 4, 8); MFMA: 16-row tiles per group (1..5)
+    int rows_per_item; // query rows one row group covers
+    int prs;           // partial rows stored per (item, split)
     int nrg;
     int nsplit;
     int split_len;
-    int kernel;
     size_t ws_bytes;
 };
 
@@ -70,18 +75,30 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
     if (!pow2(bs) || bs < 16 || bs > 128) return PKV_ERR_UNSUPPORTED;
     if (mode < 0 || mode > 2) return PKV_ERR_UNSUPPORTED;
     if (max_q_len < 1) max_q_len = 1;
+    int kernel = 2;
     if (opts) {
         for (int i = 0; i < 6; ++i)
             if (opts->reserved[i] != 0) return PKV_ERR_INVALID_ARG;
         if (opts->split_tokens < 0) return PKV_ERR_INVALID_ARG;
         if (opts->kernel < 0 || opts->kernel > 2) return PKV_ERR_INVALID_ARG;
-        if (opts->kernel == 2) return PKV_ERR_UNSUPPORTED;
+        if (opts->kernel != 0) kernel = opts->kernel;
     }
     const int g = hq / hkv;
     const int64_t rows = (int64_t)max_q_len * g;
-    p->rg = pow2_at_least((int)(rows < 8 ? rows : 8));
-    p->nrg = (int)cdiv(rows, p->rg);
-    p->kernel = 1;
+    if (rows > (1 << 20)) return PKV_ERR_UNSUPPORTED;
+    p->kernel = kernel;
+    if (kernel == 1) {
+        p->rg = pow2_at_least((int)(rows < 8 ? rows : 8));
+        p->rows_per_item = p->rg;
+        p->nrg = (int)cdiv(rows, p->rg);
+        p->prs = p->rg;
+    } else {
+        // up to five 16-row tiles (80 rows) per wave; more rows take several row groups
+        p->nrg = (int)cdiv(rows, 80);
+        p->rg = (int)cdiv(cdiv(rows, p->nrg), 16);
+        p->rows_per_item = 16 * p->rg;
+        p->prs = (int)(rows < p->rows_per_item ? rows : p->rows_per_item);
+    }
     const int64_t max_ctx = (int64_t)mbs * bs;
     const int64_t items = (int64_t)batch * hkv * p->nrg;
     int64_t L;
@@ -97,11 +114,14 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
         if (L < 256) L = 256;
         if (L > 2048) L = 2048;
     }
+    if (L > kMaxSplit) L = kMaxSplit;
     if (L >= max_ctx) L = cdiv(max_ctx, 128) * 128;
-    if (L > 0x40000000LL) return PKV_ERR_INVALID_ARG;
+    // the merge keeps one weight per (split, row) in LDS
+    while (cdiv(max_ctx, L) * 8 > kMaxSplitRows && L < kMaxSplit) L += 128;
+    if (cdiv(max_ctx, L) * 8 > kMaxSplitRows) return PKV_ERR_UNSUPPORTED;
     p->split_len = (int)L;
     p->nsplit = (int)cdiv(max_ctx, L);
-    p->ws_bytes = p->nsplit > 1 ? (size_t)(items * p->nsplit * p->rg) * (size_t)(head_dim + 1) * 4 + 256 : 0;
+    p->ws_bytes = p->nsplit > 1 ? (size_t)(items * p->nsplit * p->prs) * (size_t)(head_dim + 1) * 4 : 0;
     return PKV_OK;
 }
 
@@ -265,10 +285,13 @@ int pkv_decode_gqa(const void* q, int32_t num_q_heads, const pkv_cache_t* cache,
         const int64_t items = (int64_t)batch * a.hkv * p.nrg;
         float* ws = static_cast<float*>(workspace);
         a.part_o = ws;
-        a.part_lse = ws + items * p.nsplit * p.rg * cache->head_dim;
+        a.part_lse = ws + items * p.nsplit * p.prs * cache->head_dim;
     }
-    return hip_status(pkv::launch_decode_valu(a, batch, cache->head_dim, p.rg, cache->quant_mode,
-                                              static_cast<hipStream_t>(stream)));
+    a.prs = p.prs;
+    hipStream_t st_ = static_cast<hipStream_t>(stream);
+    if (p.kernel == 1)
+        return hip_status(pkv::launch_decode_valu(a, batch, cache->head_dim, p.rg, cache->quant_mode, st_));
+    return hip_status(pkv::launch_decode_mfma(a, batch, cache->head_dim, p.rg, cache->quant_mode, st_));
 }
 
 }  // extern "C"

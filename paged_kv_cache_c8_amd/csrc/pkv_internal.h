@@ -69,6 +69,7 @@ struct DecodeArgs {
     int nrg;
     int nsplit;
     int split_len;
+    int prs;           // partial rows per (item, split) in part_o / part_lse
     float scale_log2;  // softmax scale * log2(e)
 };
 
@@ -76,5 +77,9 @@ hipError_t launch_store(const StoreArgs& a, int head_dim, int mode, hipStream_t 
 hipError_t launch_dequant(const DequantArgs& a, int head_dim, int mode, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs& a, int batch, int head_dim, int rg, int mode,
                               hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int batch, int head_dim, int row_tiles, int mode,
+                              hipStream_t stream);
+// log-sum-exp merge of the split partials; rows_per_item = query rows of one row group
+hipError_t launch_merge(const DecodeArgs& a, int batch, int head_dim, int rows_per_item, hipStream_t stream);
 
 }  // namespace pkv

@@ -156,6 +156,7 @@ class Run:
         ob, o64, olse = ref if ref is not None else self.oracle_decode()
         got = out.float().cpu().numpy().astype(np.float64)
         max_abs, rel, elem_ok = attention_close(got, o64, atol, rtol)
+        print(f"[{self.w.name}] attention vs oracle: max_abs={max_abs:.2e} rel={rel:.2e}", flush=True)
         assert max_abs <= atol and rel <= rtol and elem_ok, (max_abs, rel, elem_ok)
         gl = lse.cpu().numpy().astype(np.float64)
         fin = np.isfinite(olse)

@@ -54,8 +54,12 @@ def test_plan_is_deterministic_and_bounded(pkv):
     assert p["split_tokens"] % 128 == 0 and p["num_splits"] * p["split_tokens"] >= 256 * 16
     forced = pkv.decode_plan(8, 64, 8, 128, 1024, 128, 1, 0, split_tokens=1000)
     assert forced["split_tokens"] == 1024 and forced["num_splits"] == 128
+    capped = pkv.decode_plan(8, 64, 8, 128, 1024, 128, 1, 0, split_tokens=100000)
+    assert capped["split_tokens"] == 4096 and capped["num_splits"] == 32
     one = pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 0, split_tokens=100000)
     assert one["num_splits"] == 1
+    assert pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 0)["kernel"] == 2
+    assert pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 0, kernel=1)["kernel"] == 1
 
 
 def _cache_struct(pkv, mode=0, hd=128, bs=16, k=16, v=32, ks=64, vs=128):
@@ -82,6 +86,8 @@ def test_store_rejects_bad_arguments(pkv):
     assert r(ctypes.byref(per_block), P, P, 1, P, None, None, None, 0, 0, 1, 1, None) == -2  # slots
     misaligned = _cache_struct(pkv, k=17)
     assert r(ctypes.byref(misaligned), P, P, 1, None, None, P, P, 1, 1, 1, 0, None) == -1
+    misaligned_scale = _cache_struct(pkv, ks=68)
+    assert r(ctypes.byref(misaligned_scale), P, P, 1, None, None, P, P, 1, 1, 1, 0, None) == -1
     noscale = _cache_struct(pkv, ks=0)
     assert r(ctypes.byref(noscale), P, P, 1, None, None, P, P, 1, 1, 1, 0, None) == -1
 

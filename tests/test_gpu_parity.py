@@ -48,18 +48,22 @@ DECODE_CASES = [
 ]
 
 
+KERNELS = [1, 2]  # VALU split-KV kernel, MFMA kernel
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("mode,d,bs,g,ctx", DECODE_CASES)
-def test_decode_matches_oracle(mode, d, bs, g, ctx):
+def test_decode_matches_oracle(mode, d, bs, g, ctx, kernel):
     r = Run(_wl(mode, d, bs, g, ctx, seed=len(ctx) + d + bs + g))
     r.store_prior()
     r.store_new()
     r.assert_cache_equal()
-    out, lse = r.decode()
+    out, lse = r.decode(kernel=kernel)
     ref = r.oracle_decode()
     r.assert_decode_close(out, lse, ref)
     # several partitions of the keys: the same result within rounding
     for split in (128, 256):
-        o2, l2 = r.decode(split_tokens=split)
+        o2, l2 = r.decode(split_tokens=split, kernel=kernel)
         r.assert_decode_close(o2, l2, ref)
 
 
@@ -73,35 +77,39 @@ CHUNK_CASES = [
 ]
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("mode,d,bs,g,ctx,ql", CHUNK_CASES)
-def test_chunked_store_and_causal_decode(mode, d, bs, g, ctx, ql):
+def test_chunked_store_and_causal_decode(mode, d, bs, g, ctx, ql, kernel):
     r = Run(_wl(mode, d, bs, g, ctx, ql, seed=sum(ctx)))
     r.store_prior()
     r.store_new()
     r.assert_cache_equal()
-    out, lse = r.decode()
+    out, lse = r.decode(kernel=kernel)
     ref = r.oracle_decode()
     r.assert_decode_close(out, lse, ref)
-    o2, l2 = r.decode(split_tokens=128)
+    o2, l2 = r.decode(split_tokens=128, kernel=kernel)
     r.assert_decode_close(o2, l2, ref)
 
 
-def test_split_count_agreement_and_determinism():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_split_count_agreement_and_determinism(kernel):
     r = Run(_wl(0, 128, 16, 4, [3000, 1200, 4096, 64], seed=5), with_oracle=False)
     r.store_prior()
     r.store_new()
-    one, l1 = r.decode(split_tokens=4096)
-    many, lm = r.decode(split_tokens=128)
-    default, ld = r.decode()
-    default2, ld2 = r.decode()
+    one, l1 = r.decode(split_tokens=4096, kernel=kernel)
+    many, lm = r.decode(split_tokens=128, kernel=kernel)
+    default, ld = r.decode(kernel=kernel)
+    default2, ld2 = r.decode(kernel=kernel)
     torch.cuda.synchronize()
     assert torch.equal(default.view(torch.int16), default2.view(torch.int16))
     assert torch.equal(ld, ld2)
-    # within one bf16 step of each other, lse within 1e-5 relative
+    # Partitions differ only in rounding: the softmax weights enter the P.V dot products as fp16
+    # (relative rounding <= 2^-11, dependent on the running max and so on the split boundaries)
+    # and the output is rounded to bf16 (one step <= 2^-7 relative).  The lse is all fp32.
     for o, l in ((many, lm), (default, ld)):
         diff = (o.float() - one.float()).abs()
-        step = one.float().abs().clamp_min(2.0 ** -126) * 2.0 ** -7
-        assert bool((diff <= step + 1e-6).all())
+        bound = one.float().abs() * 2.0 ** -7 + 2.0 ** -10 * float(one.float().abs().max())
+        assert bool((diff <= bound).all()), float((diff - bound).max())
         assert torch.allclose(l, l1, rtol=1e-5, atol=1e-5)
 
 
@@ -122,13 +130,14 @@ def test_block_permutation_invariance_on_gpu():
     assert torch.equal(l1, l2)
 
 
-def test_inactive_sequences_give_zero_and_minus_inf():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_inactive_sequences_give_zero_and_minus_inf(kernel):
     r = Run(_wl(0, 128, 16, 4, [0, 50, 0, 300], seed=3))
     r.store_prior()
     r.store_new()
     r.assert_cache_equal()
     for split in (0, 128):
-        out, lse = r.decode(split_tokens=split)
+        out, lse = r.decode(split_tokens=split, kernel=kernel)
         torch.cuda.synchronize()
         assert bool((out[0] == 0).all()) and bool((out[2] == 0).all())
         assert bool(torch.isneginf(lse[0]).all()) and bool(torch.isneginf(lse[2]).all())
