@@ -44,7 +44,30 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-baseline sample")
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = auto)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain device copy of known size (for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+def calibrate_copy(steps):
+    """A plain 1 GiB device-to-device copy, repeated: the reference against which rocprofv3's
+    FETCH_SIZE / WRITE_SIZE readings of the decode kernel are scaled to bytes."""
+    import torch
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                      "ms_per_launch": round(ms, 4), "gbs_read_plus_write": round(2 * n / ms / 1e6, 1)}))
 
 
 def step_bytes(w):
@@ -109,6 +132,9 @@ def traffic_record(kernel_key):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(max(args.steps, 1))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)

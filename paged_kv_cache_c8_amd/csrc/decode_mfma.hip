@@ -24,6 +24,8 @@
 //           as 8 contiguous bytes - the B operand - with no transpose.  When a row's running max
 //           or S grows, its accumulator row is rescaled (rows 4g+i of lane g; factors fetched from
 //           the lanes that own those rows).
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -59,29 +61,31 @@ struct BlockRegs {
     float vs[8];
 };
 
-// four int8 codes -> two fp16 pairs, exactly
-__device__ __forceinline__ void codes_to_h2(uint32_t w, uint32_t& lo, uint32_t& hi) {
-    const uint32_t u = w ^ 0x80808080u;  // code + 128 as an unsigned byte
-    const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-    lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - bias);
-    hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - bias);
-}
-
-// eight int8 codes (two dwords) -> an fp16 MFMA operand
-__device__ __forceinline__ h8 codes_to_h8(uint32_t w0, uint32_t w1) {
-    uint32_t r[4];
-    codes_to_h2(w0, r[0], r[1]);
-    codes_to_h2(w1, r[2], r[3]);
+// eight int8 codes (two dwords) -> an fp16 MFMA operand holding 1152 + code (exact): the byte
+// permute alone, the constant 1152 removed from the accumulated results instead of every value
+__device__ __forceinline__ h8 biased_h8(uint32_t w0, uint32_t w1) {
+    const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;  // code + 128 as unsigned bytes
+    const uint32_t r[4] = {__builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u),
+                           __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u),
+                           __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u),
+                           __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)};
     return __builtin_bit_cast(h8, r);
 }
 
+// Reductions over the four lanes n, n+16, n+32, n+48 (one query row).  gfx950's permlane swaps
+// exchange 16-lane rows (odd rows of one copy with even rows of the other) and 32-lane halves
+// in the VALU, instead of a round trip through the LDS crossbar.
 __device__ __forceinline__ float xor16_max(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16, kWave));
-    return fmaxf(x, __shfl_xor(x, 32, kWave));
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 __device__ __forceinline__ float xor16_sum(float x) {
-    x += __shfl_xor(x, 16, kWave);
-    return x + __shfl_xor(x, 32, kWave);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
 template <int D, int MODE, int RT>
@@ -128,21 +132,21 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     if (t_begin >= kmax) return;
     const int t_end = min(t_begin + a.split_len, kmax);
 
-    const int blk0 = t_begin >> a.log2bs;
-    const int nblk = ((t_end - 1) >> a.log2bs) - blk0 + 1;
-    for (int i = lane; i < nblk; i += kWave) bt_s[i] = a.bt[(int64_t)b * a.mbs + blk0 + i];
-
     // ---- query tiles (B operand of the score MFMA): lane (n, g) holds row n's channels
-    //      g*8*KS .. +8*KS, k-step m taking the 8 channels g*8*KS + 8m .. +8
+    //      g*8*KS .. +8*KS, k-step m taking the 8 channels g*8*KS + 8m .. +8.
+    //      int8 pages: the K operand carries 1152 + code, so every score carries 1152 * sum(q) of
+    //      its row in excess; qbias holds that amount (the row's fp16 values summed in fp32).
     uint32_t qb[RT][C::KS][4];
-    float rowmul[RT];
+    float rowmul[RT], qbias[RT];
     int lim[RT];
+    bool causal = false;  // some row of the group cannot see every key of the split
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int j = rt * 16 + n;
         const bool rv = j < nvalid;
         const int r = r0 + j;
-        lim[rt] = rv ? prior + r / a.g : -1;
+        lim[rt] = rv ? prior + r / a.g : 0x7fffffff;
+        causal |= lim[rt] < t_end - 1;
         uint32_t raw[C::KS][4];
         if (rv) {
             const uint16_t* qp = a.q + ((int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g) * D + g * 8 * C::KS;
@@ -161,6 +165,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) qb[rt][m][e] = raw[m][e];
             rowmul[rt] = a.scale_log2;
+            qbias[rt] = 0.0f;
         } else {
             float mx = 0.0f;
 #pragma unroll
@@ -173,6 +178,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
             if (mx > 0.0f) (void)frexpf(mx, &ex);       // mx in [2^(ex-1), 2^ex)
             const int k = min(120, max(-120, 15 - ex));  // mx * 2^k in [2^14, 2^15)
             const float up = ldexpf(1.0f, k);
+            float qs = 0.0f;
 #pragma unroll
             for (int m = 0; m < C::KS; ++m)
 #pragma unroll
@@ -180,63 +186,86 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
                     const h2 v = {(_Float16)(bf16_to_f32(raw[m][e] & 0xffffu) * up),
                                   (_Float16)(bf16_to_f32(raw[m][e] >> 16) * up)};
                     qb[rt][m][e] = __builtin_bit_cast(uint32_t, v);
+                    qs += (float)v.x + (float)v.y;
                 }
+            qbias[rt] = 1152.0f * xor16_sum(qs);
             rowmul[rt] = ldexpf(a.scale_log2, -k);
         }
     }
+    causal = __any(causal);
 
-    float m_run[RT], l_run[RT];
+    // ---- block-table slice of the split (the wave reads back its own LDS writes in order)
+    const int blk0 = t_begin >> a.log2bs;
+    const int nblk = ((t_end - 1) >> a.log2bs) - blk0 + 1;
+    for (int i = lane; i < nblk; i += kWave) bt_s[i] = a.bt[(int64_t)b * a.mbs + blk0 + i];
+    __builtin_amdgcn_wave_barrier();
+
+    // softmax state per row (lane column n), lazily rescaled: m_ref only moves when a block's max
+    // exceeds it by more than 8 (weights stay <= 2^8), s_ref when a V scale exceeds 16x it.
+    float m_ref[RT], l_run[RT];
     f4 acc[RT][C::DT];
+    f4 pacc[RT];  // per-row sums of the fp16 weights, to remove the 1152 code bias
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        m_run[rt] = -INFINITY;
+        m_ref[rt] = -INFINITY;
         l_run[rt] = 0.0f;
+        pacc[rt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) acc[rt][dt] = f4{0.f, 0.f, 0.f, 0.f};
     }
-    float s_run = 0.0f;  // running max of the V scales (1 for bf16 pages)
+    float s_ref = MODE == 2 ? 1.0f : 0.0f;
 
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k);
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v);
     const int rho = lane & 15;
     const int kg = lane >> 4;
-    __syncthreads();  // bt_s
+    const int64_t page_bytes = (int64_t)a.hkv * a.bs * D * C::ESZ;  // one physical block, all heads
+    const int64_t head_bytes = (int64_t)h * a.bs * D * C::ESZ;
+    const int krow_off = 8 * (rho >> 2) + (rho & 3);                 // score tile u adds 4u
+    const int k_lane_bytes = kg * C::KB;
+    const int v_lane_bytes = n * a.bs * C::ESZ;                      // channel n of each 16-channel tile
 
     auto load_block = [&](int T, BlockRegs<D, MODE>& R) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            int t = T + 8 * (rho >> 2) + 4 * u + (rho & 3);
+        {
+            int t = T + krow_off;  // keys t and t + 4 share a page (same 8-key group)
             if (t >= t_end) t = t_begin;  // in-bounds stand-in, masked later
-            const int64_t page = (int64_t)bt_s[(t >> a.log2bs) - blk0] * a.hkv + h;
-            const uint8_t* kp = kbase + ((page * a.bs + (t & (a.bs - 1))) * D) * C::ESZ + kg * C::KB;
+            const uint8_t* kp = kbase + (int64_t)bt_s[(t >> a.log2bs) - blk0] * page_bytes + head_bytes +
+                                (t & (a.bs - 1)) * (D * C::ESZ) + k_lane_bytes;
 #pragma unroll
-            for (int l = 0; l < C::KL; ++l) R.k[u][l] = load16(kp + 16 * l);
+            for (int u = 0; u < 2; ++u) {
+                int tu = T + krow_off + 4 * u;
+                const uint8_t* kpu = (tu < t_end) ? kp + u * 4 * D * C::ESZ : kp;
+#pragma unroll
+                for (int l = 0; l < C::KL; ++l) R.k[u][l] = load16(kpu + 16 * l);
+            }
         }
         int t0 = T + 8 * g;
         if (t0 >= t_end) t0 = t_begin;
-        const int64_t page = (int64_t)bt_s[(t0 >> a.log2bs) - blk0] * a.hkv + h;
+        const int64_t bt0 = bt_s[(t0 >> a.log2bs) - blk0];
         const int slot0 = t0 & (a.bs - 1);
+        const uint8_t* vp = vbase + bt0 * page_bytes + head_bytes + v_lane_bytes + slot0 * C::ESZ;
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-            const uint8_t* vp = vbase + (((page * D + dt * 16 + n) * a.bs) + slot0) * C::ESZ;
+            const uint8_t* vpd = vp + (int64_t)dt * 16 * a.bs * C::ESZ;
             if constexpr (C::VW == 2) {
-                const uint2 w = *reinterpret_cast<const uint2*>(vp);
+                const uint2 w = *reinterpret_cast<const uint2*>(vpd);
                 R.v[dt][0] = w.x; R.v[dt][1] = w.y;
             } else {
-                const uint4 w = *reinterpret_cast<const uint4*>(vp);
+                const uint4 w = *reinterpret_cast<const uint4*>(vpd);
                 R.v[dt][0] = w.x; R.v[dt][1] = w.y; R.v[dt][2] = w.z; R.v[dt][3] = w.w;
             }
         }
+        const int64_t sidx = (bt0 * a.hkv + h) * a.bs + slot0;
         if constexpr (MODE == 0) {
-            const float4* kq = reinterpret_cast<const float4*>(a.ks + page * a.bs + slot0);
-            const float4* vq = reinterpret_cast<const float4*>(a.vs + page * a.bs + slot0);
+            const float4* kq = reinterpret_cast<const float4*>(a.ks + sidx);
+            const float4* vq = reinterpret_cast<const float4*>(a.vs + sidx);
             const float4 k0 = kq[0], k1 = kq[1], v0 = vq[0], v1 = vq[1];
             R.ks[0] = k0.x; R.ks[1] = k0.y; R.ks[2] = k0.z; R.ks[3] = k0.w;
             R.ks[4] = k1.x; R.ks[5] = k1.y; R.ks[6] = k1.z; R.ks[7] = k1.w;
             R.vs[0] = v0.x; R.vs[1] = v0.y; R.vs[2] = v0.z; R.vs[3] = v0.w;
             R.vs[4] = v1.x; R.vs[5] = v1.y; R.vs[6] = v1.z; R.vs[7] = v1.w;
         } else if constexpr (MODE == 1) {
-            const float kk = a.ks[page], vv = a.vs[page];
+            const float kk = a.ks[bt0 * a.hkv + h], vv = a.vs[bt0 * a.hkv + h];
 #pragma unroll
             for (int e = 0; e < 8; ++e) { R.ks[e] = kk; R.vs[e] = vv; }
         } else {
@@ -245,13 +274,11 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         }
     };
 
-    BlockRegs<D, MODE> cur, nxt;
-    load_block(t_begin, cur);
-
-    for (int T = t_begin; T < t_end; T += BLK) {
-        if (T + BLK < t_end) load_block(T + BLK, nxt);
-
-        // ------------------------------------------------ scores: two 16-key tiles per row tile
+    // One 32-key block on registers R (loaded one block earlier).
+    auto process = [&](int T, const BlockRegs<D, MODE>& R) {
+        // masked: the block runs past the split's keys or past a row's causal limit
+        const bool MASKED = causal || T + BLK > t_end;
+        // -------------------------------------------- scores: two 16-key tiles per row tile
         f4 sc[RT][2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -260,7 +287,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int m = 0; m < C::KS; ++m) {
                 if constexpr (MODE == 2) {
-                    const u32x4 w = cur.k[u][m];  // 8 bf16 = one 16-byte load per k-step
+                    const u32x4 w = R.k[u][m];  // 8 bf16 = one 16-byte load per k-step
                     const uint32_t r[4] = {w.x, w.y, w.z, w.w};
                     const b8 av = __builtin_bit_cast(b8, r);
 #pragma unroll
@@ -268,8 +295,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
                         sc[rt][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             av, __builtin_bit_cast(b8, qb[rt][m]), sc[rt][u], 0, 0, 0);
                 } else {
-                    const u32x4 w = cur.k[u][m / 2];  // 8 codes per k-step: dwords (2m, 2m+1)
-                    const h8 av = (m & 1) ? codes_to_h8(w.z, w.w) : codes_to_h8(w.x, w.y);
+                    const u32x4 w = R.k[u][m / 2];  // 8 codes per k-step: dwords (2m, 2m+1)
+                    const h8 av = (m & 1) ? biased_h8(w.z, w.w) : biased_h8(w.x, w.y);
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt)
                         sc[rt][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -278,61 +305,76 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
             }
         }
 
-        // ------------------------------------------------ online softmax, P operand
-        float vmax = 0.0f;
+        // -------------------------------------------- V-scale reference
+        float sf = 1.0f;
+        bool s_moved = false;
+        float vscale[8];
         if constexpr (MODE != 2) {
+            float vmax = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                if (T + 8 * g + e < t_end) vmax = fmaxf(vmax, cur.vs[e]);
+                if (!MASKED || T + 8 * g + e < t_end) vmax = fmaxf(vmax, R.vs[e]);
             vmax = xor16_max(vmax);
+            if (vmax > 16.0f * s_ref) {  // (also the first block: s_ref == 0)
+                sf = s_ref > 0.0f ? s_ref * __builtin_amdgcn_rcpf(vmax) : 0.0f;
+                s_ref = vmax;
+                s_moved = true;
+            }
+            const float inv = s_ref > 0.0f ? __builtin_amdgcn_rcpf(s_ref) : 0.0f;
+            // slots past the keys may never have been written: their scales must not reach the weights
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vscale[e] = (!MASKED || T + 8 * g + e < t_end) ? R.vs[e] * inv : 0.0f;
         }
-        const float s_new = MODE == 2 ? 1.0f : fmaxf(s_run, vmax);
-        const float sf = (MODE == 2 || s_run == 0.0f) ? 1.0f : s_run / s_new;
-        const float inv_s = s_new > 0.0f ? 1.0f / s_new : 0.0f;
-        s_run = s_new;
 
+        // -------------------------------------------- online softmax, P operand
         uint32_t pa[RT][4];
         float factor[RT];
-        bool any_rescale = false;
+        bool any_rescale = s_moved;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             float sv[8];
             float bmax = -INFINITY;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int t = T + 8 * g + e;
-                const float raw = sc[rt][e >> 2][e & 3];
-                sv[e] = (t < t_end && t <= lim[rt]) ? raw * cur.ks[e] * rowmul[rt] : -INFINITY;
+                const float raw = sc[rt][e >> 2][e & 3] - qbias[rt];
+                sv[e] = raw * (R.ks[e] * rowmul[rt]);
+                if (MASKED) {
+                    const int t = T + 8 * g + e;
+                    if (!(t < t_end && t <= lim[rt])) sv[e] = -INFINITY;
+                }
                 bmax = fmaxf(bmax, sv[e]);
             }
             bmax = xor16_max(bmax);
-            const float m_new = fmaxf(m_run[rt], bmax);
-            const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run[rt] - m_new);
+            float alpha = 1.0f;
+            if (bmax > m_ref[rt] + 8.0f) {  // (also the first block: m_ref == -inf)
+                alpha = __builtin_amdgcn_exp2f(m_ref[rt] - bmax);
+                m_ref[rt] = bmax;
+            }
             float p[8];
             float psum = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                p[e] = (sv[e] == -INFINITY) ? 0.0f : exp2f(sv[e] - m_new);
+                p[e] = __builtin_amdgcn_exp2f(sv[e] - m_ref[rt]);
+                // a row with no visible key yet keeps m_ref = -inf: its masked keys weigh 0
+                if (MASKED && sv[e] == -INFINITY) p[e] = 0.0f;
                 psum += p[e];
             }
             psum = xor16_sum(psum);
             l_run[rt] = l_run[rt] * alpha + psum;
-            m_run[rt] = m_new;
             factor[rt] = alpha * sf;
-            any_rescale |= factor[rt] != 1.0f;
+            any_rescale |= alpha != 1.0f;
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
                 if constexpr (MODE == 2) {
                     pa[rt][e2] = f32_to_bf16_rne(p[2 * e2]) | (f32_to_bf16_rne(p[2 * e2 + 1]) << 16);
                 } else {
-                    const h2 w = {(_Float16)(p[2 * e2] * (cur.vs[2 * e2] * inv_s)),
-                                  (_Float16)(p[2 * e2 + 1] * (cur.vs[2 * e2 + 1] * inv_s))};
+                    const h2 w = {(_Float16)(p[2 * e2] * vscale[2 * e2]), (_Float16)(p[2 * e2 + 1] * vscale[2 * e2 + 1])};
                     pa[rt][e2] = __builtin_bit_cast(uint32_t, w);
                 }
             }
         }
 
-        // ------------------------------------------------ rescale rows whose max or S grew
+        // -------------------------------------------- rescale rows whose reference moved
         if (__any(any_rescale)) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
@@ -341,18 +383,18 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
                     const float f = __shfl(factor[rt], 4 * g + i, kWave);  // factor of row 4g+i
 #pragma unroll
                     for (int dt = 0; dt < C::DT; ++dt) acc[rt][dt][i] *= f;
+                    pacc[rt][i] *= f;
                 }
             }
         }
 
-        // ------------------------------------------------ P.V over the 32 keys
+        // -------------------------------------------- P.V over the 32 keys (+ the weight sums)
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
             if constexpr (MODE == 2) {
-                uint32_t r[4] = {cur.v[dt][0], cur.v[dt][1], cur.v[dt][2], cur.v[dt][3]};
-                // bf16 slots past the keys may hold any bit pattern: zero them
-                const int tk = T + 8 * g;
-                if (tk + 8 > t_end) {
+                uint32_t r[4] = {R.v[dt][0], R.v[dt][1], R.v[dt][2], R.v[dt][3]};
+                if (MASKED) {  // bf16 slots past the keys may hold any bit pattern
+                    const int tk = T + 8 * g;
 #pragma unroll
                     for (int e2 = 0; e2 < 4; ++e2) {
                         if (tk + 2 * e2 >= t_end) r[e2] = 0;
@@ -365,14 +407,36 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
                     acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, pa[rt]), bv,
                                                                           acc[rt][dt], 0, 0, 0);
             } else {
-                const h8 bv = codes_to_h8(cur.v[dt][0], cur.v[dt][1]);
+                const h8 bv = biased_h8(R.v[dt][0], R.v[dt][1]);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
                     acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, pa[rt]), bv,
                                                                          acc[rt][dt], 0, 0, 0);
             }
         }
-        cur = nxt;
+        if constexpr (MODE != 2) {
+            const uint32_t ones[4] = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
+            const h8 bo = __builtin_bit_cast(h8, ones);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                pacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, pa[rt]), bo, pacc[rt], 0, 0, 0);
+        }
+    };
+
+    // Two register sets, alternating: the loads of block k+1 stay in flight while block k computes,
+    // and no register set is ever copied (a copy would wait for those loads).  Loads past the
+    // split's last block read the in-bounds stand-in, so every iteration issues the same loads.
+    BlockRegs<D, MODE> ra, rb;
+    load_block(t_begin, ra);
+    for (int T = t_begin;;) {
+        load_block(T + BLK, rb);
+        process(T, ra);
+        T += BLK;
+        if (T >= t_end) break;
+        load_block(T + BLK, ra);
+        process(T, rb);
+        T += BLK;
+        if (T >= t_end) break;
     }
 
     // ---- normalise and write: lane (channel n, group g) holds rows 4g+i of every channel tile
@@ -383,15 +447,16 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         for (int i = 0; i < 4; ++i) {
             const int j = rt * 16 + 4 * g + i;  // row within the group
             const float l = __shfl(l_run[rt], 4 * g + i, kWave);
-            const float m = __shfl(m_run[rt], 4 * g + i, kWave);
+            const float m = __shfl(m_ref[rt], 4 * g + i, kWave);
             if (j >= nvalid) continue;
-            const float mul = l > 0.0f ? s_run / l : 0.0f;
+            const float mul = l > 0.0f ? s_ref / l : 0.0f;
+            const float bias = MODE == 2 ? 0.0f : 1152.0f * pacc[rt][i];
             const int r = r0 + j;
             const int64_t orow = (int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g;
             const int64_t prow = ((int64_t)item * a.nsplit + s) * a.prs + j;
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt) {
-                const float o = acc[rt][dt][i] * mul;
+                const float o = (acc[rt][dt][i] - bias) * mul;
                 const int d = dt * 16 + n;
                 if (!split_mode) a.out[orow * D + d] = (uint16_t)f32_to_bf16_rne(o);
                 else a.part_o[prow * D + d] = o;
@@ -425,9 +490,8 @@ hipError_t launch_rt(const DecodeArgs& a, int batch, int rt, hipStream_t stream)
     switch (rt) {
         case 1: return launch_one<D, MODE, 1>(a, batch, stream);
         case 2: return launch_one<D, MODE, 2>(a, batch, stream);
-        case 3: return launch_one<D, MODE, 3>(a, batch, stream);
-        case 4: return launch_one<D, MODE, 4>(a, batch, stream);
-        case 5: return launch_one<D, MODE, 5>(a, batch, stream);
+        case 3: if constexpr (D == 64) return launch_one<D, MODE, 3>(a, batch, stream);
+                return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }

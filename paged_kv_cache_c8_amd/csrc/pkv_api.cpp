@@ -53,7 +53,7 @@ constexpr int64_t kMaxSplitRows = 4096;  // splits x rows one merge can combine
 
 struct DecodePlan {
     int kernel;        // 1 VALU, 2 MFMA
-    int rg;            // VALU: rows per row group (1, 2, 4, 8); MFMA: 16-row tiles per group (1..5)
+    int rg;            // VALU: rows per row group (1, 2, 4, 8); MFMA: 16-row tiles per group (1..3)
     int rows_per_item; // query rows one row group covers
     int prs;           // partial rows stored per (item, split)
     int nrg;
@@ -93,8 +93,11 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
         p->nrg = (int)cdiv(rows, p->rg);
         p->prs = p->rg;
     } else {
-        // up to five 16-row tiles (80 rows) per wave; more rows take several row groups
-        p->nrg = (int)cdiv(rows, 80);
+        // up to three (head_dim 64) or two (head_dim 128) 16-row tiles per wave, so the wave's
+        // accumulators and double-buffered key blocks stay in registers; more rows take several
+        // row groups
+        const int64_t max_rows = head_dim == 64 ? 48 : 32;
+        p->nrg = (int)cdiv(rows, max_rows);
         p->rg = (int)cdiv(cdiv(rows, p->nrg), 16);
         p->rows_per_item = 16 * p->rg;
         p->prs = (int)(rows < p->rows_per_item ? rows : p->rows_per_item);

@@ -253,3 +253,26 @@ def test_per_block_rescale_sequence_matches_oracle():
         assert np.array_equal(cache.k.cpu().numpy(), hc.k), (lo, hi)
         assert np.array_equal(cache.v.cpu().numpy(), hc.v), (lo, hi)
         assert np.array_equal(cache.k_scale.cpu().numpy().view(np.uint32), hc.k_scale.view(np.uint32))
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_unwritten_slots_do_not_reach_the_output(mode, kernel):
+    """Slots past each sequence's keys hold whatever the pool held before (here NaN scales, NaN
+    bf16 values or the largest code): the decode reads them only as in-bounds stand-ins and must
+    give them zero weight."""
+    w = _wl(mode, 128, 16, 4, [1, 17, 100, 531], seed=77)
+    r = Run(w)
+    if mode == 2:
+        r.cache.k.fill_(float("nan"))
+        r.cache.v.fill_(float("nan"))
+    else:
+        r.cache.k.fill_(127)
+        r.cache.v.fill_(127)
+        r.cache.k_scale.fill_(float("nan"))
+        r.cache.v_scale.fill_(float("nan"))
+    r.store_prior()
+    r.store_new()
+    out, lse = r.decode(kernel=kernel)
+    assert torch.isfinite(out.float()).all()
+    r.assert_decode_close(out, lse)
