@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1, help="workload index (0..4); 1 = Qwen3-8B decode")
     ap.add_argument("--split-tokens", type=int, default=0)
-    ap.add_argument("--kernel", type=int, default=0, help="0 = library choice, 1 = VALU, 2 = MFMA")
+    ap.add_argument("--kernel", type=int, default=0, help="0 = library choice, 1 = VALU, 2 = MFMA fp16 scores, 3 = MFMA int8 scores")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-baseline sample")
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = auto)")
@@ -251,7 +251,7 @@ def main():
             "head_dim": w.head_dim, "block_size": w.block_size, "quant_mode": w.quant_mode,
             "sum_context": int(w.context_lengths.sum()), "new_tokens": new_tokens,
             "cache_replicas": reps, "split_tokens": plan["split_tokens"], "num_splits": plan["num_splits"],
-            "kernel": {1: "valu", 2: "mfma"}[plan["kernel"]],
+            "kernel": {1: "valu", 2: "mfma-f16", 3: "mfma-i8"}[plan["kernel"]],
             "parallelism": "single-gpu",
         },
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),

@@ -149,8 +149,11 @@ int pkv_dequant(const pkv_cache_t *cache, const int32_t *block_table, int32_t ma
 typedef struct {
     int32_t split_tokens; /* keys per split-KV partition; 0 = planned from the shapes.
                              Rounded up to a multiple of 128, at most 4096. */
-    int32_t kernel;       /* 0 = choose (the MFMA kernel); 1 = VALU split-KV kernel
-                             (dot2 + DPP reductions); 2 = MFMA kernel */
+    int32_t kernel;       /* 0 = choose (3 for int8 caches, 2 for bf16); 1 = VALU split-KV kernel
+                             (dot2 + DPP reductions); 2 = MFMA kernel with fp16 / bf16
+                             scores; 3 = MFMA kernel with exact int8 scores and key
+                             subsets packed into the tile columns (int8 caches; a bf16
+                             cache falls back to 2) */
     int32_t reserved[6];  /* must be zero */
 } pkv_decode_opts_t;
 
@@ -189,7 +192,7 @@ int pkv_decode_gqa(const void *q, int32_t num_q_heads, const pkv_cache_t *cache,
 
 /* The split plan pkv_decode_gqa would use, for tests and benchmarks.
  * Writes the keys per partition, the number of partitions per row group and
- * the kernel (1 VALU, 2 MFMA); any output pointer may be NULL. */
+ * the kernel (1 VALU, 2 or 3 MFMA); any output pointer may be NULL. */
 int pkv_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                     int32_t max_blocks_per_seq, int32_t block_size, int32_t max_q_len,
                     int32_t quant_mode, const pkv_decode_opts_t *opts, int32_t *split_tokens,

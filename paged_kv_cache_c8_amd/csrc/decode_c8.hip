@@ -1,0 +1,540 @@
+// decode_c8.hip - grouped-query attention over the int8 paged cache (per-token or per-block
+// scales) on the matrix cores of gfx950.
+//
+// Same result as decode_valu.hip and decode_mfma.hip (MojoPagedDecodeGQA, Mojo Opset README Op
+// List; the cache of PR #379's MojoStorePagedKVCacheC8), with the vector-ALU work per key cut to
+// what the HBM roofline of MI355X leaves room for:
+//
+//  * Scores on the int8 matrix cores, with no conversion of the K codes.  Each query row is
+//    multiplied by a power of two and rounded to integers q in [-2^14, 2^14]; q = 256 hi + lo
+//    with int8 hi and lo (exact), and v_mfma_i32_16x16x64_i8 forms K.hi, shifted left by 8, then
+//    accumulates K.lo on top: the exact integer dot product of the codes with q.  The K scale and
+//    the power of two come back in the fp32 softmax.
+//  * Keys are walked in blocks of 64.  Lane group g (lanes 16g .. 16g+15) owns the 16 keys
+//    16g .. 16g+15 of the block: it loads them as 16 consecutive bytes of each channel row of the
+//    channel-major V page (one 16-byte load per 16 channels).  The block is cut into four key
+//    subsets s = (v, e) = (s / 2, s % 2); subset s holds keys 16g + 8v + 4e + i (i < 4) of every
+//    lane group, so that after its score MFMA lane (g, n) holds the weights of exactly those keys.
+//  * The 16 columns of every MFMA tile are (row r, subset class j): column n = J r + j with
+//    J = 16 / rows in {1, 2, 4}; class j takes the subsets with s % J == j.  Each column runs its
+//    own online softmax (running max, weight sum, V-scale reference), so every lane's softmax
+//    values are real (row, key) pairs even when a KV head has only 4 query rows; the J partial
+//    softmaxes of a row are merged once, after the last block.
+//  * P.V as O^T (channels x columns) += V^T P^T on v_mfma_f32_16x16x32_f16, one per 8 keys of
+//    each lane group (v = 0, 1) and 16 channels; a code c enters as the fp16 value 1152 + c
+//    (exact: a byte permute) and 1152 times the weight sums (an all-ones MFMA) is taken off at
+//    the end.  The weights are p * s_v / S with S the column's running max V scale, so they stay
+//    in [0, 2^8] in fp16.
+//
+// One wave per (sequence, KV head, row group, key split), no barriers in the loop.  The K, V and
+// scale loads of block k+1 are issued while block k computes; past the split's keys they read
+// in-bounds stand-ins (the split's last page) that the masks give zero weight.
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef int i4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int BLK = 64;                  // keys per block (four 16-key subsets)
+constexpr int MAX_SPLIT = 4096;          // keys per split (planner limit)
+constexpr int MAX_SPLIT_PAGES = MAX_SPLIT / 16;
+constexpr int WPB = 1;                   // independent waves per workgroup
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+
+// eight int8 codes (two dwords) -> the fp16 MFMA operand 1152 + code (exact)
+__device__ __forceinline__ h8 biased_h8(uint32_t w0, uint32_t w1) {
+    const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;  // code + 128 as unsigned bytes
+    const uint32_t r[4] = {__builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u),
+                           __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u),
+                           __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u),
+                           __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)};
+    return __builtin_bit_cast(h8, r);
+}
+
+// max / sum over the four lanes n, n+16, n+32, n+48 (gfx950 permlane swaps, no LDS)
+__device__ __forceinline__ float col_max(float x) {
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+__device__ __forceinline__ float col_sum(float x) {
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
+template <int D, int J>
+struct C8Regs {
+    i4 k[4][D / 64];         // per subset: the lane's 16 * (D/64) code bytes of one K row
+    f4 ks[4 / J], vs[4 / J]; // per slot: the scales of the lane's 4 keys (per-block mode: .x)
+};
+
+template <int D>
+struct C8V {
+    u32x4 v[D / 16];         // per channel tile: the lane group's 16 keys of one channel
+};
+
+template <int D, int MODE, int J, int RT>
+__global__ __launch_bounds__(64 * WPB) void decode_c8_kernel(DecodeArgs a, int total) {
+    static_assert(MODE == 0 || MODE == 1, "int8 cache modes only");
+    static_assert(J == 1 || RT == 1, "several row tiles only with one subset class");
+    constexpr int KSTEP = D / 64;                     // 64-channel steps of the score MFMA
+    constexpr int DT = D / 16;                        // 16-channel output tiles
+    constexpr int NSLOT = 4 / J;                      // subsets per column per block
+    constexpr int ROWS = J > 1 ? 16 / J : 16 * RT;    // query rows per wave
+    __shared__ int bt_all[WPB][MAX_SPLIT_PAGES];
+
+    const int lane = threadIdx.x & 63;
+    int* const bt_s = bt_all[threadIdx.x >> 6];
+    const int n = lane & 15;  // column (scores, weights, accumulators); channel (V operand)
+    const int g = lane >> 4;  // lane group
+    const int jcol = n % J;   // subset class of the lane's column
+
+    int wi = blockIdx.x * WPB + (threadIdx.x >> 6);
+    if (wi >= total) return;
+    const int s = wi % a.nsplit;
+    wi /= a.nsplit;
+    const int item = wi;
+    const int rg = wi % a.nrg;
+    wi /= a.nrg;
+    const int h = wi % a.hkv;
+    const int b = wi / a.hkv;
+
+    const int qlen = a.cu ? a.cu[b + 1] - a.cu[b] : 1;
+    const int qrow0 = a.cu ? a.cu[b] : b;
+    const int ctx = a.ctx[b];
+    const int prior = ctx - qlen;
+    const int nrows = qlen * a.g;
+    const int r0 = rg * ROWS;
+    if (r0 >= nrows) return;
+    const int nvalid = min(ROWS, nrows - r0);
+    const int kmax = prior + (r0 + nvalid - 1) / a.g + 1;  // keys the group's last row sees
+    const int t_begin = s * a.split_len;
+
+    if (kmax <= 0) {  // inactive sequence: zero output, lse = -inf
+        if (s == 0) {
+            for (int o = lane; o < nvalid * D; o += kWave) {
+                const int j = o / D, d = o % D;
+                const int r = r0 + j;
+                const int64_t orow = (int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g;
+                a.out[orow * D + d] = 0;
+                if (d == 0 && a.lse) a.lse[orow] = -INFINITY;
+            }
+        }
+        return;
+    }
+    if (t_begin >= kmax) return;
+    const int t_end = min(t_begin + a.split_len, kmax);
+
+    // ---- query rows as int8 hi / lo parts (B operand of the score MFMA): lane (n, g) holds the
+    //      16 * KSTEP channels g*16*KSTEP .. of its column's row, k-step m taking 16 of them.
+    i4 qhi[RT][KSTEP], qlo[RT][KSTEP];
+    float rowmul[RT];  // |softmax scale| * log2(e) / 2^k: integer score units -> log2 units
+    int lim[RT];       // last key the row may see
+    bool causal = false;
+    const float sgn = a.scale_log2 < 0.0f ? -1.0f : 1.0f;  // a negative scale flips the query
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int j = J > 1 ? n / J : rt * 16 + n;
+        const bool rv = j < nvalid;
+        const int r = r0 + j;
+        lim[rt] = rv ? prior + r / a.g : 0x7fffffff;
+        causal |= lim[rt] < t_end - 1;
+        float x[16 * KSTEP];
+        if (rv) {
+            const uint16_t* qp =
+                a.q + ((int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g) * D + g * 16 * KSTEP;
+#pragma unroll
+            for (int l = 0; l < 2 * KSTEP; ++l) {
+                const u32x4 w = load16(qp + 8 * l);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[8 * l + e] = sgn * bf16_at(w, e);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16 * KSTEP; ++e) x[e] = 0.0f;
+        }
+        float mx = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16 * KSTEP; ++e) mx = fmaxf(mx, fabsf(x[e]));
+        mx = col_max(mx);
+        int ex = 0;
+        if (mx > 0.0f) (void)frexpf(mx, &ex);        // mx in [2^(ex-1), 2^ex)
+        const int k = min(120, max(-120, 14 - ex));  // |x| * 2^k < 2^14
+        const float up = ldexpf(1.0f, k);
+#pragma unroll
+        for (int m = 0; m < KSTEP; ++m) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                uint32_t hw = 0, lw = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int qi = (int)__builtin_rintf(x[16 * m + 4 * w + e] * up);  // |qi| <= 2^14
+                    const int lo = ((qi + 128) & 255) - 128;
+                    const int hi = (qi - lo) >> 8;                                  // |hi| <= 64
+                    hw |= (uint32_t)(hi & 255) << (8 * e);
+                    lw |= (uint32_t)(lo & 255) << (8 * e);
+                }
+                qhi[rt][m][w] = (int)hw;
+                qlo[rt][m][w] = (int)lw;
+            }
+        }
+        rowmul[rt] = fabsf(a.scale_log2) * ldexpf(1.0f, -k);
+    }
+    causal = __any(causal);
+
+    // ---- block-table slice of the split (the wave reads back its own LDS writes in order)
+    const int blk0 = t_begin >> a.log2bs;
+    const int lastpg = (t_end - 1) >> a.log2bs;
+    const int nblk = lastpg - blk0 + 1;
+    for (int i = lane; i < nblk; i += kWave) bt_s[i] = a.bt[(int64_t)b * a.mbs + blk0 + i];
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- per-column softmax state, lazily rescaled: the reference max (log2 units) moves only when
+    //      a block's max passes it by more than 8, the V-scale reference when a scale passes 16x it
+    float mr[RT], lsum[RT];
+    f4 acc[RT][DT];
+    f4 pacc[RT];  // column weight sums (every row of the tile), for the 1152 code bias
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        mr[rt] = -INFINITY;
+        lsum[rt] = 0.0f;
+        pacc[rt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[rt][dt] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+    float sref = 0.0f;  // the column's V-scale reference
+    float sinv = 0.0f;
+
+    const uint8_t* kb = reinterpret_cast<const uint8_t*>(a.k) + (int64_t)h * a.bs * D;
+    const uint8_t* vb = reinterpret_cast<const uint8_t*>(a.v) + (int64_t)h * a.bs * D;
+    const int64_t page_bytes = (int64_t)a.hkv * a.bs * D;  // one physical block, all heads
+    const int rho = lane & 15;                             // score A operand: key row slot
+    const int kchunk = rho >> 2;                           // ... whose key is 16 kchunk + 8v + 4e + rho % 4
+    const int k_lane = (rho & 3) * D + g * 16 * KSTEP;      // its channels g*16*KSTEP ..
+    const int v_lane = n * a.bs;                           // V operand: channel row n of a tile
+
+    // Page and first slot of the 16-key chunk c of the block at T (keys past the split's last
+    // page read that page again: in bounds, masked later).
+    auto chunk = [&](int T, int c, int& pid, int& sl) {
+        const int t = T + 16 * c;
+        pid = bt_s[min(t >> a.log2bs, lastpg) - blk0];
+        sl = t & (a.bs - 1);
+    };
+    auto load_k = [&](int T, C8Regs<D, J>& R) {
+        int pid, sl;
+        chunk(T, kchunk, pid, sl);
+        const uint8_t* kp = kb + (int64_t)pid * page_bytes + sl * D + k_lane;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int m = 0; m < KSTEP; ++m) {
+                const u32x4 w = load16(kp + (8 * (q >> 1) + 4 * (q & 1)) * D + 16 * m);
+                R.k[q][m] = i4{(int)w.x, (int)w.y, (int)w.z, (int)w.w};
+            }
+        }
+    };
+    auto load_s = [&](int T, C8Regs<D, J>& R) {
+        int pid, sl;
+        chunk(T, g, pid, sl);
+#pragma unroll
+        for (int u = 0; u < NSLOT; ++u) {  // scales of the lane's keys 16g + 8v + 4e + i, s = (v, e)
+            const int q = J * u + jcol;
+            if constexpr (MODE == 0) {
+                const int64_t si = ((int64_t)pid * a.hkv + h) * a.bs + sl + 8 * (q >> 1) + 4 * (q & 1);
+                R.ks[u] = *reinterpret_cast<const f4*>(a.ks + si);
+                R.vs[u] = *reinterpret_cast<const f4*>(a.vs + si);
+            } else {
+                const int64_t si = (int64_t)pid * a.hkv + h;
+                R.ks[u][0] = a.ks[si];
+                R.vs[u][0] = a.vs[si];
+            }
+        }
+    };
+    auto load_v = [&](int T, C8V<D>& R) {
+        int pid, sl;
+        chunk(T, g, pid, sl);
+        const uint8_t* vp = vb + (int64_t)pid * page_bytes + sl + v_lane;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) R.v[dt] = load16(vp + (int64_t)dt * 16 * a.bs);
+    };
+
+    const uint32_t ones_w[4] = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
+    const h8 ones = __builtin_bit_cast(h8, ones_w);
+
+    // K and the scales of the next block are loaded as soon as the current block has consumed
+    // them (K after the scores, the scales after the softmax); V, consumed last, alternates
+    // between two buffers and is loaded first.  Every load is in flight for about one block and
+    // no register is copied.
+    // key of value i of slot u of lane (g, n): subset q = J u + jcol = (v, e) holds 16g + 8v + 4e + i
+    auto key_of = [&](int T, int u, int i) {
+        const int q = J * u + jcol;
+        return T + 16 * g + 8 * (q >> 1) + 4 * (q & 1) + i;
+    };
+    C8Regs<D, J> R;
+    C8V<D> v0, v1;
+    load_k(t_begin, R);
+    load_s(t_begin, R);
+    load_v(t_begin, v0);
+    auto block = [&](const int T, const C8V<D>& VC, C8V<D>& VN) {
+        // masked: the block runs past the split's keys or past some row's causal limit
+        const bool MASKED = causal || T + BLK > t_end;
+        load_v(T + BLK, VN);  // past the split's end: in-bounds stand-ins, never weighted
+
+        // -------------------------------------------- scores: one int32 tile per subset
+        i4 sc[RT][4];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                i4 c = i4{0, 0, 0, 0};
+#pragma unroll
+                for (int m = 0; m < KSTEP; ++m)
+                    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[q][m], qhi[rt][m], c, 0, 0, 0);
+                c = c * 256;
+#pragma unroll
+                for (int m = 0; m < KSTEP; ++m)
+                    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[q][m], qlo[rt][m], c, 0, 0, 0);
+                sc[rt][q] = c;
+            }
+        }
+        load_k(T + BLK, R);
+
+        // -------------------------------------------- V-scale reference of the column
+        float vsl[NSLOT][4];
+#pragma unroll
+        for (int u = 0; u < NSLOT; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vsl[u][i] = MODE == 0 ? R.vs[u][i] : R.vs[u][0];
+        float sf = 1.0f;
+        bool s_moved = false;
+        {
+            float vmax = 0.0f;
+#pragma unroll
+            for (int u = 0; u < NSLOT; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (!MASKED || key_of(T, u, i) < t_end) vmax = fmaxf(vmax, vsl[u][i]);
+            vmax = col_max(vmax);
+            if (vmax > 16.0f * sref) {  // (also the first block: sref == 0)
+                sf = sref > 0.0f ? sref * __builtin_amdgcn_rcpf(vmax) : 0.0f;
+                sref = vmax;
+                sinv = __builtin_amdgcn_rcpf(vmax);
+                s_moved = true;
+            }
+        }
+        // slots past the keys may never have been written: their scales must not reach a weight
+#pragma unroll
+        for (int u = 0; u < NSLOT; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                vsl[u][i] = (!MASKED || key_of(T, u, i) < t_end) ? vsl[u][i] * sinv : 0.0f;
+
+        // -------------------------------------------- online softmax per column, P operands
+        uint32_t wpk[RT][NSLOT][2];
+        float factor[RT];
+        bool any_rescale = s_moved;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float x[NSLOT][4];
+            float bmax = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < NSLOT; ++u) {
+                i4 S = sc[rt][J * u];
+#pragma unroll
+                for (int c = 1; c < J; ++c)
+                    if (jcol == c) S = sc[rt][J * u + c];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x[u][i] = (float)S[i] * (MODE == 0 ? R.ks[u][i] : R.ks[u][0]);
+                    if (MASKED) {
+                        const int t = key_of(T, u, i);
+                        if (!(t < t_end && t <= lim[rt])) x[u][i] = -INFINITY;
+                    }
+                    bmax = fmaxf(bmax, x[u][i]);
+                }
+            }
+            bmax = col_max(bmax) * rowmul[rt];
+            float alpha = 1.0f;
+            if (bmax > mr[rt] + 8.0f) {  // (also the first block: mr == -inf)
+                alpha = __builtin_amdgcn_exp2f(mr[rt] - bmax);
+                mr[rt] = bmax;
+            }
+            float ps = 0.0f;
+#pragma unroll
+            for (int u = 0; u < NSLOT; ++u) {
+                float p[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[u][i], rowmul[rt], -mr[rt]));
+                    // a column with no visible key yet keeps mr = -inf: its masked keys weigh 0
+                    if (MASKED && x[u][i] == -INFINITY) p[i] = 0.0f;
+                    ps += p[i];
+                }
+                const h4 w = {(_Float16)(p[0] * vsl[u][0]), (_Float16)(p[1] * vsl[u][1]),
+                              (_Float16)(p[2] * vsl[u][2]), (_Float16)(p[3] * vsl[u][3])};
+                const auto wb = __builtin_bit_cast(uint2, w);
+                wpk[rt][u][0] = wb.x;
+                wpk[rt][u][1] = wb.y;
+            }
+            lsum[rt] = lsum[rt] * alpha + ps;
+            factor[rt] = alpha * sf;
+            any_rescale |= alpha != 1.0f;
+        }
+
+        load_s(T + BLK, R);
+
+        // -------------------------------------------- rescale the columns whose references moved
+        if (__any(any_rescale)) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= factor[rt];
+                pacc[rt] *= factor[rt];
+            }
+        }
+
+        // -------------------------------------------- P.V (+ weight sums): per lane group, keys
+        //      16g + 8v .. +8 of subset pair (v, 0), (v, 1)
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            h8 bq[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                uint32_t ww[4];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int q = 2 * v + e;  // subset of keys 16g + 8v + 4e ..
+                    const int u = q / J;
+                    const bool mine = J == 1 || jcol == q % J;  // else the subset is another class's
+                    ww[2 * e] = mine ? wpk[rt][u][0] : 0u;
+                    ww[2 * e + 1] = mine ? wpk[rt][u][1] : 0u;
+                }
+                bq[rt] = __builtin_bit_cast(h8, ww);
+            }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const h8 av = v == 0 ? biased_h8(VC.v[dt].x, VC.v[dt].y) : biased_h8(VC.v[dt].z, VC.v[dt].w);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bq[rt], acc[rt][dt], 0, 0, 0);
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                pacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, bq[rt], pacc[rt], 0, 0, 0);
+        }
+    };
+    for (int T = t_begin;;) {
+        block(T, v0, v1);
+        T += BLK;
+        if (T >= t_end) break;
+        block(T, v1, v0);
+        T += BLK;
+        if (T >= t_end) break;
+    }
+
+    // ---- merge the J columns of each row, normalise, write.  Lane (g, n) holds channels
+    //      16 dt + 4g + i of column n.
+    const bool split_mode = a.nsplit > 1;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const float l = col_sum(lsum[rt]);
+        float M = mr[rt];
+        if constexpr (J >= 2) M = fmaxf(M, lane_xchg<1>(M));
+        if constexpr (J >= 4) M = fmaxf(M, lane_xchg<2>(M));
+        const float f = mr[rt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr[rt] - M);
+        float L = l * f;
+        if constexpr (J >= 2) L += lane_xchg<1>(L);
+        if constexpr (J >= 4) L += lane_xchg<2>(L);
+        const float cm = f * sref;
+        const float bias = 1152.0f * pacc[rt][0];
+        f4 o[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v = (acc[rt][dt][i] - bias) * cm;
+                if constexpr (J >= 2) v += lane_xchg<1>(v);
+                if constexpr (J >= 4) v += lane_xchg<2>(v);
+                o[dt][i] = v;
+            }
+        }
+        const int j = J > 1 ? n / J : rt * 16 + n;  // row within the group
+        if (jcol != 0 || j >= nvalid) continue;
+        const float mul = L > 0.0f ? 1.0f / L : 0.0f;
+        const int r = r0 + j;
+        const int64_t orow = (int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g;
+        const int64_t prow = ((int64_t)item * a.nsplit + s) * a.prs + j;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int d = dt * 16 + 4 * g;
+            if (!split_mode) {
+                uint2 pk;
+                pk.x = f32_to_bf16_rne(o[dt][0] * mul) | (f32_to_bf16_rne(o[dt][1] * mul) << 16);
+                pk.y = f32_to_bf16_rne(o[dt][2] * mul) | (f32_to_bf16_rne(o[dt][3] * mul) << 16);
+                *reinterpret_cast<uint2*>(a.out + orow * D + d) = pk;
+            } else {
+                *reinterpret_cast<f4*>(a.part_o + prow * D + d) = o[dt] * mul;
+            }
+        }
+        if (g == 0) {
+            const float lse2 = L > 0.0f ? M + log2f(L) : -INFINITY;
+            if (!split_mode) {
+                if (a.lse) a.lse[orow] = lse2 * kLn2;
+            } else {
+                a.part_lse[prow] = lse2;
+            }
+        }
+    }
+}
+
+template <int D, int MODE, int J, int RT>
+hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream) {
+    const int64_t items = (int64_t)batch * a.hkv * a.nrg;
+    const int64_t grid = items * a.nsplit;
+    if (grid == 0) return hipSuccess;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    const int64_t wgs = (grid + WPB - 1) / WPB;
+    hipLaunchKernelGGL((decode_c8_kernel<D, MODE, J, RT>), dim3((unsigned)wgs), dim3(64 * WPB), 0, stream, a,
+                       (int)grid);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    constexpr int ROWS = J > 1 ? 16 / J : 16 * RT;
+    return launch_merge(a, batch, D, ROWS, stream);
+}
+
+template <int D, int MODE>
+hipError_t launch_shape(const DecodeArgs& a, int batch, int j, int rt, hipStream_t stream) {
+    if (j == 4 && rt == 1) return launch_one<D, MODE, 4, 1>(a, batch, stream);
+    if (j == 2 && rt == 1) return launch_one<D, MODE, 2, 1>(a, batch, stream);
+    if (j == 1 && rt == 1) return launch_one<D, MODE, 1, 1>(a, batch, stream);
+    if (j == 1 && rt == 2) return launch_one<D, MODE, 1, 2>(a, batch, stream);
+    return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t launch_mode(const DecodeArgs& a, int batch, int j, int rt, int mode, hipStream_t stream) {
+    if (mode == 0) return launch_shape<D, 0>(a, batch, j, rt, stream);
+    if (mode == 1) return launch_shape<D, 1>(a, batch, j, rt, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode_c8(const DecodeArgs& a, int batch, int head_dim, int classes, int row_tiles,
+                            int mode, hipStream_t stream) {
+    if (a.split_len > MAX_SPLIT || (a.split_len % BLK) != 0) return hipErrorInvalidValue;
+    if (head_dim == 64) return launch_mode<64>(a, batch, classes, row_tiles, mode, stream);
+    if (head_dim == 128) return launch_mode<128>(a, batch, classes, row_tiles, mode, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

@@ -52,8 +52,9 @@ constexpr int64_t kMaxSplit = 4096;      // keys per split the decode kernel acc
 constexpr int64_t kMaxSplitRows = 4096;  // splits x rows one merge can combine
 
 struct DecodePlan {
-    int kernel;        // 1 VALU, 2 MFMA
-    int rg;            // VALU: rows per row group (1, 2, 4, 8); MFMA: 16-row tiles per group (1..3)
+    int kernel;        // 1 VALU, 2 MFMA (fp16 / bf16 scores), 3 MFMA (int8 scores, int8 cache only)
+    int rg;            // VALU: rows per row group (1, 2, 4, 8); MFMA: 16-row tiles per group
+    int classes;       // kernel 3: key-subset classes per column tile (1, 2, 4)
     int rows_per_item; // query rows one row group covers
     int prs;           // partial rows stored per (item, split)
     int nrg;
@@ -75,19 +76,39 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
     if (!pow2(bs) || bs < 16 || bs > 128) return PKV_ERR_UNSUPPORTED;
     if (mode < 0 || mode > 2) return PKV_ERR_UNSUPPORTED;
     if (max_q_len < 1) max_q_len = 1;
-    int kernel = 2;
+    int kernel = mode == 2 ? 2 : 3;  // int8 pages: exact int8 scores; bf16 pages: bf16 scores
     if (opts) {
         for (int i = 0; i < 6; ++i)
             if (opts->reserved[i] != 0) return PKV_ERR_INVALID_ARG;
         if (opts->split_tokens < 0) return PKV_ERR_INVALID_ARG;
-        if (opts->kernel < 0 || opts->kernel > 2) return PKV_ERR_INVALID_ARG;
+        if (opts->kernel < 0 || opts->kernel > 3) return PKV_ERR_INVALID_ARG;
         if (opts->kernel != 0) kernel = opts->kernel;
     }
+    if (kernel == 3 && mode == 2) kernel = 2;  // the int8-score kernel needs int8 pages
     const int g = hq / hkv;
     const int64_t rows = (int64_t)max_q_len * g;
     if (rows > (1 << 20)) return PKV_ERR_UNSUPPORTED;
     p->kernel = kernel;
-    if (kernel == 1) {
+    p->classes = 1;
+    if (kernel == 3) {
+        // columns of a 16-wide tile = (row, key-subset class): 4 classes for up to 4 rows, 2 for
+        // up to 8, else one class and one or two 16-row tiles per row group
+        if (rows <= 4) {
+            p->classes = 4;
+            p->rg = 1;
+            p->rows_per_item = 4;
+        } else if (rows <= 8) {
+            p->classes = 2;
+            p->rg = 1;
+            p->rows_per_item = 8;
+        } else {
+            p->classes = 1;
+            p->rg = rows <= 16 ? 1 : 2;
+            p->rows_per_item = 16 * p->rg;
+        }
+        p->nrg = (int)cdiv(rows, p->rows_per_item);
+        p->prs = (int)(rows < p->rows_per_item ? rows : p->rows_per_item);
+    } else if (kernel == 1) {
         p->rg = pow2_at_least((int)(rows < 8 ? rows : 8));
         p->rows_per_item = p->rg;
         p->nrg = (int)cdiv(rows, p->rg);
@@ -294,6 +315,9 @@ int pkv_decode_gqa(const void* q, int32_t num_q_heads, const pkv_cache_t* cache,
     hipStream_t st_ = static_cast<hipStream_t>(stream);
     if (p.kernel == 1)
         return hip_status(pkv::launch_decode_valu(a, batch, cache->head_dim, p.rg, cache->quant_mode, st_));
+    if (p.kernel == 3)
+        return hip_status(
+            pkv::launch_decode_c8(a, batch, cache->head_dim, p.classes, p.rg, cache->quant_mode, st_));
     return hip_status(pkv::launch_decode_mfma(a, batch, cache->head_dim, p.rg, cache->quant_mode, st_));
 }
 

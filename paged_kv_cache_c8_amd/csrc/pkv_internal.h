@@ -79,6 +79,9 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int batch, int head_dim, int 
                               hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int batch, int head_dim, int row_tiles, int mode,
                               hipStream_t stream);
+// int8 cache (modes 0, 1): classes = subset classes per column tile (1, 2, 4), row_tiles = 1 or 2
+hipError_t launch_decode_c8(const DecodeArgs& a, int batch, int head_dim, int classes, int row_tiles,
+                            int mode, hipStream_t stream);
 // log-sum-exp merge of the split partials; rows_per_item = query rows of one row group
 hipError_t launch_merge(const DecodeArgs& a, int batch, int head_dim, int rows_per_item, hipStream_t stream);
 

@@ -58,8 +58,11 @@ def test_plan_is_deterministic_and_bounded(pkv):
     assert capped["split_tokens"] == 4096 and capped["num_splits"] == 32
     one = pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 0, split_tokens=100000)
     assert one["num_splits"] == 1
-    assert pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 0)["kernel"] == 2
+    assert pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 0)["kernel"] == 3  # int8 pages: int8 scores
+    assert pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 2)["kernel"] == 2  # bf16 pages
+    assert pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 2, kernel=3)["kernel"] == 2
     assert pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 0, kernel=1)["kernel"] == 1
+    assert pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 0, kernel=2)["kernel"] == 2
 
 
 def _cache_struct(pkv, mode=0, hd=128, bs=16, k=16, v=32, ks=64, vs=128):

@@ -13,12 +13,12 @@ from tests.helpers import attention_close
 pytestmark = pytest.mark.gpu
 
 
-def _check(idx, n_sample):
+def _check(idx, n_sample, kernel=0):
     w = gen.make_config(idx)
     r = Run(w, with_oracle=False)
     r.store_prior()
     r.store_new()
-    out, lse = r.decode()
+    out, lse = r.decode(kernel=kernel)
     torch.cuda.synchronize()
     rng = np.random.default_rng(100 + idx)
     sel = np.arange(w.batch) if n_sample >= w.batch else np.sort(rng.choice(w.batch, n_sample, replace=False))
@@ -77,3 +77,8 @@ def test_bf16_large_batch_sampled():
 
 def test_chunked_per_block_sampled():
     _check(4, 12)
+
+
+@pytest.mark.parametrize("idx,n_sample", [(1, 32), (2, 2), (4, 12)])
+def test_int8_score_kernel_full_sizes(idx, n_sample):
+    _check(idx, n_sample, kernel=3)

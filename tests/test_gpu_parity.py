@@ -48,7 +48,7 @@ DECODE_CASES = [
 ]
 
 
-KERNELS = [1, 2]  # VALU split-KV kernel, MFMA kernel
+KERNELS = [1, 2, 3]  # VALU split-KV kernel, MFMA kernel (fp16 scores), MFMA kernel (int8 scores)
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
