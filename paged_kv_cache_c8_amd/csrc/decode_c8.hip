@@ -98,10 +98,13 @@ __global__ __launch_bounds__(64 * WPB) void decode_c8_kernel(DecodeArgs a, int t
     const int g = lane >> 4;  // lane group
     const int jcol = n % J;   // subset class of the lane's column
 
+    // item fastest: consecutive workgroups go round-robin over the XCDs, so each XCD gets an
+    // even share of the items (and of their keys) whatever the number of empty splits
     int wi = blockIdx.x * WPB + (threadIdx.x >> 6);
     if (wi >= total) return;
-    const int s = wi % a.nsplit;
-    wi /= a.nsplit;
+    const int items = total / a.nsplit;
+    const int s = wi / items;
+    wi %= items;
     const int item = wi;
     const int rg = wi % a.nrg;
     wi /= a.nrg;
@@ -134,13 +137,12 @@ __global__ __launch_bounds__(64 * WPB) void decode_c8_kernel(DecodeArgs a, int t
     if (t_begin >= kmax) return;
     const int t_end = min(t_begin + a.split_len, kmax);
 
-    // ---- query rows as int8 hi / lo parts (B operand of the score MFMA): lane (n, g) holds the
-    //      16 * KSTEP channels g*16*KSTEP .. of its column's row, k-step m taking 16 of them.
-    i4 qhi[RT][KSTEP], qlo[RT][KSTEP];
-    float rowmul[RT];  // |softmax scale| * log2(e) / 2^k: integer score units -> log2 units
-    int lim[RT];       // last key the row may see
+    // ---- query rows (B operand of the score MFMA): lane (n, g) holds the 16 * KSTEP channels
+    //      g*16*KSTEP .. of its column's row, k-step m taking 16 of them.  The raw bf16 loads are
+    //      issued first; they are quantized while the first key block is in flight.
+    int lim[RT];  // last key the row may see
     bool causal = false;
-    const float sgn = a.scale_log2 < 0.0f ? -1.0f : 1.0f;  // a negative scale flips the query
+    u32x4 qraw[RT][2 * KSTEP];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int j = J > 1 ? n / J : rt * 16 + n;
@@ -148,55 +150,16 @@ __global__ __launch_bounds__(64 * WPB) void decode_c8_kernel(DecodeArgs a, int t
         const int r = r0 + j;
         lim[rt] = rv ? prior + r / a.g : 0x7fffffff;
         causal |= lim[rt] < t_end - 1;
-        float x[16 * KSTEP];
-        if (rv) {
-            const uint16_t* qp =
-                a.q + ((int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g) * D + g * 16 * KSTEP;
+        const uint16_t* qp = a.q + ((int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g) * D + g * 16 * KSTEP;
 #pragma unroll
-            for (int l = 0; l < 2 * KSTEP; ++l) {
-                const u32x4 w = load16(qp + 8 * l);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[8 * l + e] = sgn * bf16_at(w, e);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 16 * KSTEP; ++e) x[e] = 0.0f;
-        }
-        float mx = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 16 * KSTEP; ++e) mx = fmaxf(mx, fabsf(x[e]));
-        mx = col_max(mx);
-        int ex = 0;
-        if (mx > 0.0f) (void)frexpf(mx, &ex);        // mx in [2^(ex-1), 2^ex)
-        const int k = min(120, max(-120, 14 - ex));  // |x| * 2^k < 2^14
-        const float up = ldexpf(1.0f, k);
-#pragma unroll
-        for (int m = 0; m < KSTEP; ++m) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                uint32_t hw = 0, lw = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int qi = (int)__builtin_rintf(x[16 * m + 4 * w + e] * up);  // |qi| <= 2^14
-                    const int lo = ((qi + 128) & 255) - 128;
-                    const int hi = (qi - lo) >> 8;                                  // |hi| <= 64
-                    hw |= (uint32_t)(hi & 255) << (8 * e);
-                    lw |= (uint32_t)(lo & 255) << (8 * e);
-                }
-                qhi[rt][m][w] = (int)hw;
-                qlo[rt][m][w] = (int)lw;
-            }
-        }
-        rowmul[rt] = fabsf(a.scale_log2) * ldexpf(1.0f, -k);
+        for (int l = 0; l < 2 * KSTEP; ++l) qraw[rt][l] = rv ? load16(qp + 8 * l) : u32x4{0u, 0u, 0u, 0u};
     }
     causal = __any(causal);
 
-    // ---- block-table slice of the split (the wave reads back its own LDS writes in order)
     const int blk0 = t_begin >> a.log2bs;
     const int lastpg = (t_end - 1) >> a.log2bs;
     const int nblk = lastpg - blk0 + 1;
-    for (int i = lane; i < nblk; i += kWave) bt_s[i] = a.bt[(int64_t)b * a.mbs + blk0 + i];
-    __builtin_amdgcn_wave_barrier();
+    const int32_t* btb = a.bt + (int64_t)b * a.mbs;
 
     // ---- per-column softmax state, lazily rescaled: the reference max (log2 units) moves only when
     //      a block's max passes it by more than 8, the V-scale reference when a scale passes 16x it
@@ -224,14 +187,9 @@ __global__ __launch_bounds__(64 * WPB) void decode_c8_kernel(DecodeArgs a, int t
 
     // Page and first slot of the 16-key chunk c of the block at T (keys past the split's last
     // page read that page again: in bounds, masked later).
-    auto chunk = [&](int T, int c, int& pid, int& sl) {
-        const int t = T + 16 * c;
-        pid = bt_s[min(t >> a.log2bs, lastpg) - blk0];
-        sl = t & (a.bs - 1);
-    };
-    auto load_k = [&](int T, C8Regs<D, J>& R) {
-        int pid, sl;
-        chunk(T, kchunk, pid, sl);
+    auto chunk_page = [&](int T, int c) { return min((T + 16 * c) >> a.log2bs, lastpg); };
+    auto load_k_at = [&](int T, int pid, C8Regs<D, J>& R) {
+        const int sl = (T + 16 * kchunk) & (a.bs - 1);
         const uint8_t* kp = kb + (int64_t)pid * page_bytes + sl * D + k_lane;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -242,9 +200,8 @@ __global__ __launch_bounds__(64 * WPB) void decode_c8_kernel(DecodeArgs a, int t
             }
         }
     };
-    auto load_s = [&](int T, C8Regs<D, J>& R) {
-        int pid, sl;
-        chunk(T, g, pid, sl);
+    auto load_s_at = [&](int T, int pid, C8Regs<D, J>& R) {
+        const int sl = (T + 16 * g) & (a.bs - 1);
 #pragma unroll
         for (int u = 0; u < NSLOT; ++u) {  // scales of the lane's keys 16g + 8v + 4e + i, s = (v, e)
             const int q = J * u + jcol;
@@ -259,13 +216,15 @@ __global__ __launch_bounds__(64 * WPB) void decode_c8_kernel(DecodeArgs a, int t
             }
         }
     };
-    auto load_v = [&](int T, C8V<D>& R) {
-        int pid, sl;
-        chunk(T, g, pid, sl);
+    auto load_v_at = [&](int T, int pid, C8V<D>& R) {
+        const int sl = (T + 16 * g) & (a.bs - 1);
         const uint8_t* vp = vb + (int64_t)pid * page_bytes + sl + v_lane;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) R.v[dt] = load16(vp + (int64_t)dt * 16 * a.bs);
     };
+    auto load_k = [&](int T, C8Regs<D, J>& R) { load_k_at(T, bt_s[chunk_page(T, kchunk) - blk0], R); };
+    auto load_s = [&](int T, C8Regs<D, J>& R) { load_s_at(T, bt_s[chunk_page(T, g) - blk0], R); };
+    auto load_v = [&](int T, C8V<D>& R) { load_v_at(T, bt_s[chunk_page(T, g) - blk0], R); };
 
     const uint32_t ones_w[4] = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
     const h8 ones = __builtin_bit_cast(h8, ones_w);
@@ -279,15 +238,68 @@ __global__ __launch_bounds__(64 * WPB) void decode_c8_kernel(DecodeArgs a, int t
         const int q = J * u + jcol;
         return T + 16 * g + 8 * (q >> 1) + 4 * (q & 1) + i;
     };
+    // ---- first block: its page ids straight from the block table, its loads issued before the
+    //      block-table slice goes to LDS and before the query is quantized
     C8Regs<D, J> R;
     C8V<D> v0, v1;
-    load_k(t_begin, R);
-    load_s(t_begin, R);
-    load_v(t_begin, v0);
+    {
+        const int pk = btb[chunk_page(t_begin, kchunk)];
+        const int pv = btb[chunk_page(t_begin, g)];
+        load_v_at(t_begin, pv, v0);
+        load_k_at(t_begin, pk, R);
+        load_s_at(t_begin, pv, R);
+    }
+    // block-table slice of the split (the wave reads back its own LDS writes in order)
+    for (int i = lane; i < nblk; i += kWave) bt_s[i] = btb[blk0 + i];
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- quantize the query rows: q * 2^k rounded to integers in [-2^14, 2^14], split exactly as
+    //      256 hi + lo with int8 hi and lo
+    i4 qhi[RT][KSTEP], qlo[RT][KSTEP];
+    float rowmul[RT];  // |softmax scale| * log2(e) / 2^k: integer score units -> log2 units
+    const float sgn = a.scale_log2 < 0.0f ? -1.0f : 1.0f;  // a negative scale flips the query
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        float x[16 * KSTEP];
+#pragma unroll
+        for (int l = 0; l < 2 * KSTEP; ++l)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[8 * l + e] = sgn * bf16_at(qraw[rt][l], e);
+        float mx = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16 * KSTEP; ++e) mx = fmaxf(mx, fabsf(x[e]));
+        mx = col_max(mx);
+        int ex = 0;
+        if (mx > 0.0f) (void)frexpf(mx, &ex);        // mx in [2^(ex-1), 2^ex)
+        const int k = min(120, max(-120, 14 - ex));  // |x| * 2^k < 2^14
+        const float up = ldexpf(1.0f, k);
+#pragma unroll
+        for (int m = 0; m < KSTEP; ++m) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                uint32_t hw = 0, lw = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int qi = (int)__builtin_rintf(x[16 * m + 4 * w + e] * up);  // |qi| <= 2^14
+                    const int lo = ((qi + 128) & 255) - 128;
+                    const int hi = (qi - lo) >> 8;                                  // |hi| <= 64
+                    hw |= (uint32_t)(hi & 255) << (8 * e);
+                    lw |= (uint32_t)(lo & 255) << (8 * e);
+                }
+                qhi[rt][m][w] = (int)hw;
+                qlo[rt][m][w] = (int)lw;
+            }
+        }
+        rowmul[rt] = fabsf(a.scale_log2) * ldexpf(1.0f, -k);
+    }
+
     auto block = [&](const int T, const C8V<D>& VC, C8V<D>& VN) {
         // masked: the block runs past the split's keys or past some row's causal limit
         const bool MASKED = causal || T + BLK > t_end;
         load_v(T + BLK, VN);  // past the split's end: in-bounds stand-ins, never weighted
+        // keep the next block's loads ahead of this block's waits (the scheduler would otherwise
+        // sink them below the first score MFMA, whose wait then drains every load in flight)
+        __builtin_amdgcn_sched_barrier(0);
 
         // -------------------------------------------- scores: one int32 tile per subset
         i4 sc[RT][4];
@@ -307,6 +319,7 @@ __global__ __launch_bounds__(64 * WPB) void decode_c8_kernel(DecodeArgs a, int t
             }
         }
         load_k(T + BLK, R);
+        __builtin_amdgcn_sched_barrier(0);
 
         // -------------------------------------------- V-scale reference of the column
         float vsl[NSLOT][4];
@@ -391,6 +404,7 @@ __global__ __launch_bounds__(64 * WPB) void decode_c8_kernel(DecodeArgs a, int t
         }
 
         load_s(T + BLK, R);
+        __builtin_amdgcn_sched_barrier(0);
 
         // -------------------------------------------- rescale the columns whose references moved
         if (__any(any_rescale)) {

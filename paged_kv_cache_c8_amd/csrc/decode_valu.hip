@@ -40,7 +40,6 @@ constexpr int CH = 128;            // keys per chunk
 constexpr int RED_FLOATS = 8192;   // LDS floats for the final cross-group reduction
 constexpr int MAX_SPLIT = 4096;    // keys per split (planner limit)
 constexpr int MAX_SPLIT_BLOCKS = MAX_SPLIT / 16;
-constexpr int MERGE_ROWS = 4096;   // splits x rows one merge combines (planner limit)
 
 template <int D, int RG, int MODE>
 struct Cfg {
@@ -507,106 +506,6 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     }
 }
 
-// Log-sum-exp merge of split partials.  One workgroup per (sequence, KV head, row group, 8 rows).
-// Every load is independent: the lse values first (one per thread), then each thread walks the
-// splits of one split group and one 4-channel column, and the split groups meet in LDS.
-constexpr int MRG = 8;  // rows per merge workgroup
-
-template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int rows_per_item) {
-    constexpr int COLS = D / 4;           // float4 columns
-    constexpr int SGRP = 256 / COLS;      // split groups (8 for head_dim 128, 16 for 64)
-    __shared__ float wts[MERGE_ROWS];     // [split][row] merge weights
-    __shared__ __attribute__((aligned(16))) float4 red4[SGRP * MRG * COLS];
-    __shared__ float row_w[MRG], row_mx[MRG];
-    const int tid = threadIdx.x;
-    const int nrb = (rows_per_item + MRG - 1) / MRG;
-    int wi = blockIdx.x;
-    const int jb = wi % nrb;
-    wi /= nrb;
-    const int item = wi;
-    const int rg = wi % a.nrg;
-    wi /= a.nrg;
-    const int h = wi % a.hkv;
-    const int b = wi / a.hkv;
-    const int qlen = a.cu ? a.cu[b + 1] - a.cu[b] : 1;
-    const int qrow0 = a.cu ? a.cu[b] : b;
-    const int prior = a.ctx[b] - qlen;
-    const int nrows = qlen * a.g;
-    const int r0 = rg * rows_per_item;
-    if (r0 >= nrows) return;
-    const int nvalid_item = min(rows_per_item, nrows - r0);
-    // the split count the partial kernel saw: keys needed by the item's last row
-    const int kmax = prior + (r0 + nvalid_item - 1) / a.g + 1;
-    if (kmax <= 0) return;  // written by the partial kernel
-    const int j0 = jb * MRG;
-    if (j0 >= nvalid_item) return;
-    const int nv = min(MRG, nvalid_item - j0);
-    const int nact = min(a.nsplit, (kmax + a.split_len - 1) / a.split_len);
-    const int64_t ibase = (int64_t)item * a.nsplit * a.prs + j0;  // row j0 of split 0
-
-    for (int i = tid; i < nact * MRG; i += blockDim.x) {
-        const int sp = i / MRG, j = i % MRG;
-        wts[i] = j < nv ? a.part_lse[ibase + (int64_t)sp * a.prs + j] : -INFINITY;
-    }
-    __syncthreads();
-    if (tid < MRG) {
-        const int j = tid;
-        float mx = -INFINITY;
-        for (int sp = 0; sp < nact; ++sp) mx = fmaxf(mx, wts[sp * MRG + j]);
-        float wsum = 0.0f;
-        for (int sp = 0; sp < nact; ++sp) {
-            const float l2 = wts[sp * MRG + j];
-            const float w = (l2 == -INFINITY) ? 0.0f : exp2f(l2 - mx);
-            wts[sp * MRG + j] = w;
-            wsum += w;
-        }
-        row_w[j] = wsum;
-        row_mx[j] = mx;
-    }
-    __syncthreads();
-
-    const int col = tid % COLS;
-    const int sg = tid / COLS;
-    float4 acc[MRG];
-#pragma unroll
-    for (int j = 0; j < MRG; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4* po = reinterpret_cast<const float4*>(a.part_o + ibase * D) + col;
-    for (int sp = sg; sp < nact; sp += SGRP) {
-#pragma unroll
-        for (int j = 0; j < MRG; ++j) {
-            if (j < nv) {
-                const float w = wts[sp * MRG + j];
-                const float4 v = po[((int64_t)sp * a.prs + j) * COLS];
-                acc[j].x = fmaf(w, v.x, acc[j].x);
-                acc[j].y = fmaf(w, v.y, acc[j].y);
-                acc[j].z = fmaf(w, v.z, acc[j].z);
-                acc[j].w = fmaf(w, v.w, acc[j].w);
-            }
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < MRG; ++j) red4[(sg * MRG + j) * COLS + col] = acc[j];
-    __syncthreads();
-    for (int o = tid; o < nv * COLS; o += blockDim.x) {
-        const int j = o / COLS, cc = o % COLS;
-        float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int g2 = 0; g2 < SGRP; ++g2) {
-            const float4 v = red4[(g2 * MRG + j) * COLS + cc];
-            sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
-        }
-        const float wsum = row_w[j];
-        const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-        const int r = r0 + j0 + j;
-        const int64_t orow = (int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g;
-        uint2 packed;
-        packed.x = f32_to_bf16_rne(sum.x * inv) | (f32_to_bf16_rne(sum.y * inv) << 16);
-        packed.y = f32_to_bf16_rne(sum.z * inv) | (f32_to_bf16_rne(sum.w * inv) << 16);
-        *reinterpret_cast<uint2*>(a.out + orow * D + cc * 4) = packed;
-        if (cc == 0 && a.lse) a.lse[orow] = wsum > 0.0f ? (row_mx[j] + log2f(wsum)) * kLn2 : -INFINITY;
-    }
-}
-
 template <int D, int RG, int MODE>
 hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream) {
     const int64_t items = (int64_t)batch * a.hkv * a.nrg;
@@ -641,20 +540,6 @@ hipError_t launch_mode(const DecodeArgs& a, int batch, int rg, int mode, hipStre
 }
 
 }  // namespace
-
-hipError_t launch_merge(const DecodeArgs& a, int batch, int head_dim, int rows_per_item, hipStream_t stream) {
-    const int nrb = (rows_per_item + MRG - 1) / MRG;
-    const int64_t grid = (int64_t)batch * a.hkv * a.nrg * nrb;
-    if (grid == 0) return hipSuccess;
-    if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    if (head_dim == 64)
-        hipLaunchKernelGGL((merge_kernel<64>), dim3((unsigned)grid), dim3(256), 0, stream, a, rows_per_item);
-    else if (head_dim == 128)
-        hipLaunchKernelGGL((merge_kernel<128>), dim3((unsigned)grid), dim3(256), 0, stream, a, rows_per_item);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
-}
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int batch, int head_dim, int rg, int mode,
                               hipStream_t stream) {

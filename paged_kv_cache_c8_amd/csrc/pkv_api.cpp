@@ -49,7 +49,7 @@ int check_cache(const pkv_cache_t* c) {
 }
 
 constexpr int64_t kMaxSplit = 4096;      // keys per split the decode kernel accepts
-constexpr int64_t kMaxSplitRows = 4096;  // splits x rows one merge can combine
+constexpr int64_t kMaxSplits = 1 << 16;   // key splits per row group
 
 struct DecodePlan {
     int kernel;        // 1 VALU, 2 MFMA (fp16 / bf16 scores), 3 MFMA (int8 scores, int8 cache only)
@@ -140,9 +140,7 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
     }
     if (L > kMaxSplit) L = kMaxSplit;
     if (L >= max_ctx) L = cdiv(max_ctx, 128) * 128;
-    // the merge keeps one weight per (split, row) in LDS
-    while (cdiv(max_ctx, L) * 8 > kMaxSplitRows && L < kMaxSplit) L += 128;
-    if (cdiv(max_ctx, L) * 8 > kMaxSplitRows) return PKV_ERR_UNSUPPORTED;
+    if (cdiv(max_ctx, L) > kMaxSplits) return PKV_ERR_UNSUPPORTED;
     p->split_len = (int)L;
     p->nsplit = (int)cdiv(max_ctx, L);
     p->ws_bytes = p->nsplit > 1 ? (size_t)(items * p->nsplit * p->prs) * (size_t)(head_dim + 1) * 4 : 0;
