@@ -147,14 +147,22 @@ int pkv_dequant(const pkv_cache_t *cache, const int32_t *block_table, int32_t ma
 
 /* Optional knobs of pkv_decode_gqa (pass NULL for the defaults). */
 typedef struct {
-    int32_t split_tokens; /* keys per split-KV partition; 0 = planned from the shapes.
-                             Rounded up to a multiple of 128, at most 4096. */
+    int32_t split_tokens; /* keys per fixed split-KV partition, rounded up to a multiple
+                             of 128, at most 4096; 0 = sized from the shapes.  A value
+                             > 0 selects fixed splits.  The balanced partition cuts all
+                             key blocks of all query groups into as many equal ranges as
+                             the GPU holds waves of the kernel at once. */
     int32_t kernel;       /* 0 = choose (3 for int8 caches, 2 for bf16); 1 = VALU split-KV kernel
                              (dot2 + DPP reductions); 2 = MFMA kernel with fp16 / bf16
                              scores; 3 = MFMA kernel with exact int8 scores and key
                              subsets packed into the tile columns (int8 caches; a bf16
                              cache falls back to 2) */
-    int32_t reserved[6];  /* must be zero */
+    int32_t partition;    /* how the keys are cut into work (int8-score kernel):
+                             0 = planned (balanced for long contexts with few query
+                             groups, else fixed splits); 1 = fixed splits of
+                             split_tokens keys; 2 = balanced partition whenever the
+                             shapes allow it (at most 4096 sequences). */
+    int32_t reserved[5];  /* must be zero */
 } pkv_decode_opts_t;
 
 /* Bytes of workspace pkv_decode_gqa needs for these shapes (0 when it needs
@@ -191,8 +199,9 @@ int pkv_decode_gqa(const void *q, int32_t num_q_heads, const pkv_cache_t *cache,
                    size_t workspace_bytes, const pkv_decode_opts_t *opts, void *stream);
 
 /* The split plan pkv_decode_gqa would use, for tests and benchmarks.
- * Writes the keys per partition, the number of partitions per row group and
- * the kernel (1 VALU, 2 or 3 MFMA); any output pointer may be NULL. */
+ * Writes the keys per partition and the number of partitions per row group
+ * (for a balanced partition: 0 and the number of waves), and the kernel
+ * (1 VALU, 2 or 3 MFMA); any output pointer may be NULL. */
 int pkv_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                     int32_t max_blocks_per_seq, int32_t block_size, int32_t max_q_len,
                     int32_t quant_mode, const pkv_decode_opts_t *opts, int32_t *split_tokens,

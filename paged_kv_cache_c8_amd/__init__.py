@@ -43,7 +43,7 @@ class _CacheT(ctypes.Structure):
 
 class _DecodeOpts(ctypes.Structure):
     _fields_ = [("split_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+                ("partition", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
 
 
 _lib = None
@@ -93,10 +93,14 @@ def _check(status, what):
         raise PkvError(status, what)
 
 
-def _opts(split_tokens=0, kernel=0):
+PARTITION_PLANNED, PARTITION_FIXED, PARTITION_BALANCED = 0, 1, 2
+
+
+def _opts(split_tokens=0, kernel=0, partition=0):
     o = _DecodeOpts()
     o.split_tokens = int(split_tokens)
     o.kernel = int(kernel)
+    o.partition = int(partition)
     return o
 
 
@@ -171,16 +175,16 @@ def dequant(cache: Cache, block_table, context_lengths, *, seq_offsets=None, k_o
 
 
 def decode_workspace_size(batch, num_q_heads, cache: Cache, max_blocks_per_seq, max_q_len=1,
-                          split_tokens=0, kernel=0) -> int:
-    o = _opts(split_tokens, kernel)
+                          split_tokens=0, kernel=0, partition=0) -> int:
+    o = _opts(split_tokens, kernel, partition)
     return int(lib().pkv_decode_workspace_size(batch, num_q_heads, cache.num_kv_heads, cache.head_dim,
                                                max_blocks_per_seq, cache.block_size, max_q_len,
                                                cache.quant_mode, ctypes.byref(o)))
 
 
 def decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
-                max_q_len=1, quant_mode=0, split_tokens=0, kernel=0):
-    o = _opts(split_tokens, kernel)
+                max_q_len=1, quant_mode=0, split_tokens=0, kernel=0, partition=0):
+    o = _opts(split_tokens, kernel, partition)
     a, b, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     st = lib().pkv_decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
                                max_q_len, quant_mode, ctypes.byref(o), ctypes.byref(a), ctypes.byref(b),
@@ -190,7 +194,7 @@ def decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, 
 
 
 def decode_gqa(q, cache: Cache, block_table, context_lengths, scale, *, cu_q_lens=None, max_q_len=1,
-               out=None, lse_out=None, workspace=None, split_tokens=0, kernel=0, stream=None):
+               out=None, lse_out=None, workspace=None, split_tokens=0, kernel=0, partition=0, stream=None):
     """Attention of the new queries ``q`` (bf16 ``[Tq, Hq, D]``) over the paged cache."""
     hq = int(q.shape[1])
     batch = int(context_lengths.shape[0])
@@ -199,12 +203,12 @@ def decode_gqa(q, cache: Cache, block_table, context_lengths, scale, *, cu_q_len
         max_q_len = 1
     if out is None:
         out = torch.empty_like(q)
-    o = _opts(split_tokens, kernel)
+    o = _opts(split_tokens, kernel, partition)
     need = int(lib().pkv_decode_workspace_size(batch, hq, cache.num_kv_heads, cache.head_dim, mbs,
                                                cache.block_size, max_q_len, cache.quant_mode,
                                                ctypes.byref(o)))
     if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # tickets start at zero
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)  # no initial contents needed
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().pkv_decode_gqa(_ptr(q), hq, cache.ref, _ptr(block_table), mbs, _ptr(context_lengths),
                               _ptr(cu_q_lens), batch, int(max_q_len), float(scale), _ptr(out),

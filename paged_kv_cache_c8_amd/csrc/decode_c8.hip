@@ -43,7 +43,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int BLK = 64;                  // keys per block (four 16-key subsets)
 constexpr int MAX_SPLIT = 4096;          // keys per split (planner limit)
 constexpr int MAX_SPLIT_PAGES = MAX_SPLIT / 16;
-constexpr int WPB = 1;                   // independent waves per workgroup
+constexpr int MAX_SK_SEQS = 4096;        // sequences the balanced partition handles (LDS prefix sums)
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
@@ -82,60 +82,25 @@ struct C8V {
     u32x4 v[D / 16];         // per channel tile: the lane group's 16 keys of one channel
 };
 
+// The attention of one work item (sequence b, KV head h, row group starting at row r0) over its
+// keys [t_seg0, t_seg1) (t_seg0 a multiple of 64).  pslot < 0: the segment is the item's whole key
+// range and the result goes to out / lse; else it is a partial, written to rows pslot * prs + j of
+// the workspace for the merge.
 template <int D, int MODE, int J, int RT>
-__global__ __launch_bounds__(64 * WPB) void decode_c8_kernel(DecodeArgs a, int total) {
+__device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, const int h, const int qlen,
+                                           const int qrow0, const int prior, const int r0, const int nvalid,
+                                           const int t_seg0, const int t_seg1, const int64_t pslot,
+                                           int* const bt_s) {
     static_assert(MODE == 0 || MODE == 1, "int8 cache modes only");
     static_assert(J == 1 || RT == 1, "several row tiles only with one subset class");
     constexpr int KSTEP = D / 64;                     // 64-channel steps of the score MFMA
     constexpr int DT = D / 16;                        // 16-channel output tiles
     constexpr int NSLOT = 4 / J;                      // subsets per column per block
-    constexpr int ROWS = J > 1 ? 16 / J : 16 * RT;    // query rows per wave
-    __shared__ int bt_all[WPB][MAX_SPLIT_PAGES];
 
     const int lane = threadIdx.x & 63;
-    int* const bt_s = bt_all[threadIdx.x >> 6];
     const int n = lane & 15;  // column (scores, weights, accumulators); channel (V operand)
     const int g = lane >> 4;  // lane group
     const int jcol = n % J;   // subset class of the lane's column
-
-    // item fastest: consecutive workgroups go round-robin over the XCDs, so each XCD gets an
-    // even share of the items (and of their keys) whatever the number of empty splits
-    int wi = blockIdx.x * WPB + (threadIdx.x >> 6);
-    if (wi >= total) return;
-    const int items = total / a.nsplit;
-    const int s = wi / items;
-    wi %= items;
-    const int item = wi;
-    const int rg = wi % a.nrg;
-    wi /= a.nrg;
-    const int h = wi % a.hkv;
-    const int b = wi / a.hkv;
-
-    const int qlen = a.cu ? a.cu[b + 1] - a.cu[b] : 1;
-    const int qrow0 = a.cu ? a.cu[b] : b;
-    const int ctx = a.ctx[b];
-    const int prior = ctx - qlen;
-    const int nrows = qlen * a.g;
-    const int r0 = rg * ROWS;
-    if (r0 >= nrows) return;
-    const int nvalid = min(ROWS, nrows - r0);
-    const int kmax = prior + (r0 + nvalid - 1) / a.g + 1;  // keys the group's last row sees
-    const int t_begin = s * a.split_len;
-
-    if (kmax <= 0) {  // inactive sequence: zero output, lse = -inf
-        if (s == 0) {
-            for (int o = lane; o < nvalid * D; o += kWave) {
-                const int j = o / D, d = o % D;
-                const int r = r0 + j;
-                const int64_t orow = (int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g;
-                a.out[orow * D + d] = 0;
-                if (d == 0 && a.lse) a.lse[orow] = -INFINITY;
-            }
-        }
-        return;
-    }
-    if (t_begin >= kmax) return;
-    const int t_end = min(t_begin + a.split_len, kmax);
 
     // ---- query rows (B operand of the score MFMA): lane (n, g) holds the 16 * KSTEP channels
     //      g*16*KSTEP .. of its column's row, k-step m taking 16 of them.  The raw bf16 loads are
@@ -149,16 +114,13 @@ __global__ __launch_bounds__(64 * WPB) void decode_c8_kernel(DecodeArgs a, int t
         const bool rv = j < nvalid;
         const int r = r0 + j;
         lim[rt] = rv ? prior + r / a.g : 0x7fffffff;
-        causal |= lim[rt] < t_end - 1;
+        causal |= lim[rt] < t_seg1 - 1;
         const uint16_t* qp = a.q + ((int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g) * D + g * 16 * KSTEP;
 #pragma unroll
         for (int l = 0; l < 2 * KSTEP; ++l) qraw[rt][l] = rv ? load16(qp + 8 * l) : u32x4{0u, 0u, 0u, 0u};
     }
     causal = __any(causal);
 
-    const int blk0 = t_begin >> a.log2bs;
-    const int lastpg = (t_end - 1) >> a.log2bs;
-    const int nblk = lastpg - blk0 + 1;
     const int32_t* btb = a.bt + (int64_t)b * a.mbs;
 
     // ---- per-column softmax state, lazily rescaled: the reference max (log2 units) moves only when
@@ -185,47 +147,6 @@ __global__ __launch_bounds__(64 * WPB) void decode_c8_kernel(DecodeArgs a, int t
     const int k_lane = (rho & 3) * D + g * 16 * KSTEP;      // its channels g*16*KSTEP ..
     const int v_lane = n * a.bs;                           // V operand: channel row n of a tile
 
-    // Page and first slot of the 16-key chunk c of the block at T (keys past the split's last
-    // page read that page again: in bounds, masked later).
-    auto chunk_page = [&](int T, int c) { return min((T + 16 * c) >> a.log2bs, lastpg); };
-    auto load_k_at = [&](int T, int pid, C8Regs<D, J>& R) {
-        const int sl = (T + 16 * kchunk) & (a.bs - 1);
-        const uint8_t* kp = kb + (int64_t)pid * page_bytes + sl * D + k_lane;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int m = 0; m < KSTEP; ++m) {
-                const u32x4 w = load16(kp + (8 * (q >> 1) + 4 * (q & 1)) * D + 16 * m);
-                R.k[q][m] = i4{(int)w.x, (int)w.y, (int)w.z, (int)w.w};
-            }
-        }
-    };
-    auto load_s_at = [&](int T, int pid, C8Regs<D, J>& R) {
-        const int sl = (T + 16 * g) & (a.bs - 1);
-#pragma unroll
-        for (int u = 0; u < NSLOT; ++u) {  // scales of the lane's keys 16g + 8v + 4e + i, s = (v, e)
-            const int q = J * u + jcol;
-            if constexpr (MODE == 0) {
-                const int64_t si = ((int64_t)pid * a.hkv + h) * a.bs + sl + 8 * (q >> 1) + 4 * (q & 1);
-                R.ks[u] = *reinterpret_cast<const f4*>(a.ks + si);
-                R.vs[u] = *reinterpret_cast<const f4*>(a.vs + si);
-            } else {
-                const int64_t si = (int64_t)pid * a.hkv + h;
-                R.ks[u][0] = a.ks[si];
-                R.vs[u][0] = a.vs[si];
-            }
-        }
-    };
-    auto load_v_at = [&](int T, int pid, C8V<D>& R) {
-        const int sl = (T + 16 * g) & (a.bs - 1);
-        const uint8_t* vp = vb + (int64_t)pid * page_bytes + sl + v_lane;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) R.v[dt] = load16(vp + (int64_t)dt * 16 * a.bs);
-    };
-    auto load_k = [&](int T, C8Regs<D, J>& R) { load_k_at(T, bt_s[chunk_page(T, kchunk) - blk0], R); };
-    auto load_s = [&](int T, C8Regs<D, J>& R) { load_s_at(T, bt_s[chunk_page(T, g) - blk0], R); };
-    auto load_v = [&](int T, C8V<D>& R) { load_v_at(T, bt_s[chunk_page(T, g) - blk0], R); };
-
     const uint32_t ones_w[4] = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
     const h8 ones = __builtin_bit_cast(h8, ones_w);
 
@@ -238,226 +159,283 @@ __global__ __launch_bounds__(64 * WPB) void decode_c8_kernel(DecodeArgs a, int t
         const int q = J * u + jcol;
         return T + 16 * g + 8 * (q >> 1) + 4 * (q & 1) + i;
     };
-    // ---- first block: its page ids straight from the block table, its loads issued before the
-    //      block-table slice goes to LDS and before the query is quantized
-    C8Regs<D, J> R;
-    C8V<D> v0, v1;
-    {
-        const int pk = btb[chunk_page(t_begin, kchunk)];
-        const int pv = btb[chunk_page(t_begin, g)];
-        load_v_at(t_begin, pv, v0);
-        load_k_at(t_begin, pk, R);
-        load_s_at(t_begin, pv, R);
-    }
-    // block-table slice of the split (the wave reads back its own LDS writes in order)
-    for (int i = lane; i < nblk; i += kWave) bt_s[i] = btb[blk0 + i];
-    __builtin_amdgcn_wave_barrier();
-
-    // ---- quantize the query rows: q * 2^k rounded to integers in [-2^14, 2^14], split exactly as
-    //      256 hi + lo with int8 hi and lo
     i4 qhi[RT][KSTEP], qlo[RT][KSTEP];
     float rowmul[RT];  // |softmax scale| * log2(e) / 2^k: integer score units -> log2 units
-    const float sgn = a.scale_log2 < 0.0f ? -1.0f : 1.0f;  // a negative scale flips the query
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        float x[16 * KSTEP];
-#pragma unroll
-        for (int l = 0; l < 2 * KSTEP; ++l)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[8 * l + e] = sgn * bf16_at(qraw[rt][l], e);
-        float mx = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 16 * KSTEP; ++e) mx = fmaxf(mx, fabsf(x[e]));
-        mx = col_max(mx);
-        int ex = 0;
-        if (mx > 0.0f) (void)frexpf(mx, &ex);        // mx in [2^(ex-1), 2^ex)
-        const int k = min(120, max(-120, 14 - ex));  // |x| * 2^k < 2^14
-        const float up = ldexpf(1.0f, k);
-#pragma unroll
-        for (int m = 0; m < KSTEP; ++m) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                uint32_t hw = 0, lw = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int qi = (int)__builtin_rintf(x[16 * m + 4 * w + e] * up);  // |qi| <= 2^14
-                    const int lo = ((qi + 128) & 255) - 128;
-                    const int hi = (qi - lo) >> 8;                                  // |hi| <= 64
-                    hw |= (uint32_t)(hi & 255) << (8 * e);
-                    lw |= (uint32_t)(lo & 255) << (8 * e);
-                }
-                qhi[rt][m][w] = (int)hw;
-                qlo[rt][m][w] = (int)lw;
-            }
-        }
-        rowmul[rt] = fabsf(a.scale_log2) * ldexpf(1.0f, -k);
-    }
 
-    auto block = [&](const int T, const C8V<D>& VC, C8V<D>& VN) {
-        // masked: the block runs past the split's keys or past some row's causal limit
-        const bool MASKED = causal || T + BLK > t_end;
-        load_v(T + BLK, VN);  // past the split's end: in-bounds stand-ins, never weighted
-        // keep the next block's loads ahead of this block's waits (the scheduler would otherwise
-        // sink them below the first score MFMA, whose wait then drains every load in flight)
-        __builtin_amdgcn_sched_barrier(0);
+    // The segment is walked in ranges of at most MAX_SPLIT keys, each with its block-table slice in
+    // LDS; the softmax state carries over.
+    for (int tb = t_seg0; tb < t_seg1; tb += MAX_SPLIT) {
+        const int t_begin = tb;
+        const int t_end = min(tb + MAX_SPLIT, t_seg1);
+        const int blk0 = t_begin >> a.log2bs;
+        const int lastpg = (t_end - 1) >> a.log2bs;
+        const int nblk = lastpg - blk0 + 1;
+        if (tb != t_seg0) __builtin_amdgcn_wave_barrier();  // the previous range's LDS reads are done
 
-        // -------------------------------------------- scores: one int32 tile per subset
-        i4 sc[RT][4];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
+        // Page and first slot of the 16-key chunk c of the block at T (keys past the split's last
+        // page read that page again: in bounds, masked later).
+        auto chunk_page = [&](int T, int c) { return min((T + 16 * c) >> a.log2bs, lastpg); };
+        auto load_k_at = [&](int T, int pid, C8Regs<D, J>& R) {
+            const int sl = (T + 16 * kchunk) & (a.bs - 1);
+            const uint8_t* kp = kb + (int64_t)pid * page_bytes + sl * D + k_lane;
+    #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                i4 c = i4{0, 0, 0, 0};
-#pragma unroll
-                for (int m = 0; m < KSTEP; ++m)
-                    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[q][m], qhi[rt][m], c, 0, 0, 0);
-                c = c * 256;
-#pragma unroll
-                for (int m = 0; m < KSTEP; ++m)
-                    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[q][m], qlo[rt][m], c, 0, 0, 0);
-                sc[rt][q] = c;
+    #pragma unroll
+                for (int m = 0; m < KSTEP; ++m) {
+                    const u32x4 w = load16(kp + (8 * (q >> 1) + 4 * (q & 1)) * D + 16 * m);
+                    R.k[q][m] = i4{(int)w.x, (int)w.y, (int)w.z, (int)w.w};
+                }
             }
-        }
-        load_k(T + BLK, R);
-        __builtin_amdgcn_sched_barrier(0);
+        };
+        auto load_s_at = [&](int T, int pid, C8Regs<D, J>& R) {
+            const int sl = (T + 16 * g) & (a.bs - 1);
+    #pragma unroll
+            for (int u = 0; u < NSLOT; ++u) {  // scales of the lane's keys 16g + 8v + 4e + i, s = (v, e)
+                const int q = J * u + jcol;
+                if constexpr (MODE == 0) {
+                    const int64_t si = ((int64_t)pid * a.hkv + h) * a.bs + sl + 8 * (q >> 1) + 4 * (q & 1);
+                    R.ks[u] = *reinterpret_cast<const f4*>(a.ks + si);
+                    R.vs[u] = *reinterpret_cast<const f4*>(a.vs + si);
+                } else {
+                    const int64_t si = (int64_t)pid * a.hkv + h;
+                    R.ks[u][0] = a.ks[si];
+                    R.vs[u][0] = a.vs[si];
+                }
+            }
+        };
+        auto load_v_at = [&](int T, int pid, C8V<D>& R) {
+            const int sl = (T + 16 * g) & (a.bs - 1);
+            const uint8_t* vp = vb + (int64_t)pid * page_bytes + sl + v_lane;
+    #pragma unroll
+            for (int dt = 0; dt < DT; ++dt) R.v[dt] = load16(vp + (int64_t)dt * 16 * a.bs);
+        };
+        auto load_k = [&](int T, C8Regs<D, J>& R) { load_k_at(T, bt_s[chunk_page(T, kchunk) - blk0], R); };
+        auto load_s = [&](int T, C8Regs<D, J>& R) { load_s_at(T, bt_s[chunk_page(T, g) - blk0], R); };
+        auto load_v = [&](int T, C8V<D>& R) { load_v_at(T, bt_s[chunk_page(T, g) - blk0], R); };
 
-        // -------------------------------------------- V-scale reference of the column
-        float vsl[NSLOT][4];
-#pragma unroll
-        for (int u = 0; u < NSLOT; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) vsl[u][i] = MODE == 0 ? R.vs[u][i] : R.vs[u][0];
-        float sf = 1.0f;
-        bool s_moved = false;
+        // ---- first block: its page ids straight from the block table, its loads issued before the
+        //      block-table slice goes to LDS and before the query is quantized
+        C8Regs<D, J> R;
+        C8V<D> v0, v1;
         {
-            float vmax = 0.0f;
-#pragma unroll
-            for (int u = 0; u < NSLOT; ++u)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (!MASKED || key_of(T, u, i) < t_end) vmax = fmaxf(vmax, vsl[u][i]);
-            vmax = col_max(vmax);
-            if (vmax > 16.0f * sref) {  // (also the first block: sref == 0)
-                sf = sref > 0.0f ? sref * __builtin_amdgcn_rcpf(vmax) : 0.0f;
-                sref = vmax;
-                sinv = __builtin_amdgcn_rcpf(vmax);
-                s_moved = true;
-            }
+            const int pk = btb[chunk_page(t_begin, kchunk)];
+            const int pv = btb[chunk_page(t_begin, g)];
+            load_v_at(t_begin, pv, v0);
+            load_k_at(t_begin, pk, R);
+            load_s_at(t_begin, pv, R);
         }
-        // slots past the keys may never have been written: their scales must not reach a weight
-#pragma unroll
-        for (int u = 0; u < NSLOT; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                vsl[u][i] = (!MASKED || key_of(T, u, i) < t_end) ? vsl[u][i] * sinv : 0.0f;
+        // block-table slice of the split (the wave reads back its own LDS writes in order)
+        for (int i = lane; i < nblk; i += kWave) bt_s[i] = btb[blk0 + i];
+        __builtin_amdgcn_wave_barrier();
 
-        // -------------------------------------------- online softmax per column, P operands
-        uint32_t wpk[RT][NSLOT][2];
-        float factor[RT];
-        bool any_rescale = s_moved;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            float x[NSLOT][4];
-            float bmax = -INFINITY;
-#pragma unroll
-            for (int u = 0; u < NSLOT; ++u) {
-                i4 S = sc[rt][J * u];
-#pragma unroll
-                for (int c = 1; c < J; ++c)
-                    if (jcol == c) S = sc[rt][J * u + c];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    x[u][i] = (float)S[i] * (MODE == 0 ? R.ks[u][i] : R.ks[u][0]);
-                    if (MASKED) {
-                        const int t = key_of(T, u, i);
-                        if (!(t < t_end && t <= lim[rt])) x[u][i] = -INFINITY;
+        if (tb == t_seg0) {
+            // ---- quantize the query rows: q * 2^k rounded to integers in [-2^14, 2^14], split exactly as
+            //      256 hi + lo with int8 hi and lo
+            const float sgn = a.scale_log2 < 0.0f ? -1.0f : 1.0f;  // a negative scale flips the query
+        #pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                float x[16 * KSTEP];
+        #pragma unroll
+                for (int l = 0; l < 2 * KSTEP; ++l)
+        #pragma unroll
+                    for (int e = 0; e < 8; ++e) x[8 * l + e] = sgn * bf16_at(qraw[rt][l], e);
+                float mx = 0.0f;
+        #pragma unroll
+                for (int e = 0; e < 16 * KSTEP; ++e) mx = fmaxf(mx, fabsf(x[e]));
+                mx = col_max(mx);
+                int ex = 0;
+                if (mx > 0.0f) (void)frexpf(mx, &ex);        // mx in [2^(ex-1), 2^ex)
+                const int k = min(120, max(-120, 14 - ex));  // |x| * 2^k < 2^14
+                const float up = ldexpf(1.0f, k);
+        #pragma unroll
+                for (int m = 0; m < KSTEP; ++m) {
+        #pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        uint32_t hw = 0, lw = 0;
+        #pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int qi = (int)__builtin_rintf(x[16 * m + 4 * w + e] * up);  // |qi| <= 2^14
+                            const int lo = ((qi + 128) & 255) - 128;
+                            const int hi = (qi - lo) >> 8;                                  // |hi| <= 64
+                            hw |= (uint32_t)(hi & 255) << (8 * e);
+                            lw |= (uint32_t)(lo & 255) << (8 * e);
+                        }
+                        qhi[rt][m][w] = (int)hw;
+                        qlo[rt][m][w] = (int)lw;
                     }
-                    bmax = fmaxf(bmax, x[u][i]);
                 }
+                rowmul[rt] = fabsf(a.scale_log2) * ldexpf(1.0f, -k);
             }
-            bmax = col_max(bmax) * rowmul[rt];
-            float alpha = 1.0f;
-            if (bmax > mr[rt] + 8.0f) {  // (also the first block: mr == -inf)
-                alpha = __builtin_amdgcn_exp2f(mr[rt] - bmax);
-                mr[rt] = bmax;
-            }
-            float ps = 0.0f;
-#pragma unroll
-            for (int u = 0; u < NSLOT; ++u) {
-                float p[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[u][i], rowmul[rt], -mr[rt]));
-                    // a column with no visible key yet keeps mr = -inf: its masked keys weigh 0
-                    if (MASKED && x[u][i] == -INFINITY) p[i] = 0.0f;
-                    ps += p[i];
-                }
-                const h4 w = {(_Float16)(p[0] * vsl[u][0]), (_Float16)(p[1] * vsl[u][1]),
-                              (_Float16)(p[2] * vsl[u][2]), (_Float16)(p[3] * vsl[u][3])};
-                const auto wb = __builtin_bit_cast(uint2, w);
-                wpk[rt][u][0] = wb.x;
-                wpk[rt][u][1] = wb.y;
-            }
-            lsum[rt] = lsum[rt] * alpha + ps;
-            factor[rt] = alpha * sf;
-            any_rescale |= alpha != 1.0f;
+
         }
 
-        load_s(T + BLK, R);
-        __builtin_amdgcn_sched_barrier(0);
+        auto block = [&](const int T, const C8V<D>& VC, C8V<D>& VN) {
+            // masked: the block runs past the split's keys or past some row's causal limit
+            const bool MASKED = causal || T + BLK > t_end;
+            load_v(T + BLK, VN);  // past the split's end: in-bounds stand-ins, never weighted
+            // keep the next block's loads ahead of this block's waits (the scheduler would otherwise
+            // sink them below the first score MFMA, whose wait then drains every load in flight)
+            __builtin_amdgcn_sched_barrier(0);
 
-        // -------------------------------------------- rescale the columns whose references moved
-        if (__any(any_rescale)) {
-#pragma unroll
+            // -------------------------------------------- scores: one int32 tile per subset
+            i4 sc[RT][4];
+    #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= factor[rt];
-                pacc[rt] *= factor[rt];
-            }
-        }
-
-        // -------------------------------------------- P.V (+ weight sums): per lane group, keys
-        //      16g + 8v .. +8 of subset pair (v, 0), (v, 1)
-#pragma unroll
-        for (int v = 0; v < 2; ++v) {
-            h8 bq[RT];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                uint32_t ww[4];
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int q = 2 * v + e;  // subset of keys 16g + 8v + 4e ..
-                    const int u = q / J;
-                    const bool mine = J == 1 || jcol == q % J;  // else the subset is another class's
-                    ww[2 * e] = mine ? wpk[rt][u][0] : 0u;
-                    ww[2 * e + 1] = mine ? wpk[rt][u][1] : 0u;
+    #pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    i4 c = i4{0, 0, 0, 0};
+    #pragma unroll
+                    for (int m = 0; m < KSTEP; ++m)
+                        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[q][m], qhi[rt][m], c, 0, 0, 0);
+                    c = c * 256;
+    #pragma unroll
+                    for (int m = 0; m < KSTEP; ++m)
+                        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[q][m], qlo[rt][m], c, 0, 0, 0);
+                    sc[rt][q] = c;
                 }
-                bq[rt] = __builtin_bit_cast(h8, ww);
             }
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const h8 av = v == 0 ? biased_h8(VC.v[dt].x, VC.v[dt].y) : biased_h8(VC.v[dt].z, VC.v[dt].w);
-#pragma unroll
+            load_k(T + BLK, R);
+            __builtin_amdgcn_sched_barrier(0);
+
+            // -------------------------------------------- V-scale reference of the column
+            float vsl[NSLOT][4];
+    #pragma unroll
+            for (int u = 0; u < NSLOT; ++u)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) vsl[u][i] = MODE == 0 ? R.vs[u][i] : R.vs[u][0];
+            float sf = 1.0f;
+            bool s_moved = false;
+            {
+                float vmax = 0.0f;
+    #pragma unroll
+                for (int u = 0; u < NSLOT; ++u)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (!MASKED || key_of(T, u, i) < t_end) vmax = fmaxf(vmax, vsl[u][i]);
+                vmax = col_max(vmax);
+                if (vmax > 16.0f * sref) {  // (also the first block: sref == 0)
+                    sf = sref > 0.0f ? sref * __builtin_amdgcn_rcpf(vmax) : 0.0f;
+                    sref = vmax;
+                    sinv = __builtin_amdgcn_rcpf(vmax);
+                    s_moved = true;
+                }
+            }
+            // slots past the keys may never have been written: their scales must not reach a weight
+    #pragma unroll
+            for (int u = 0; u < NSLOT; ++u)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    vsl[u][i] = (!MASKED || key_of(T, u, i) < t_end) ? vsl[u][i] * sinv : 0.0f;
+
+            // -------------------------------------------- online softmax per column, P operands
+            uint32_t wpk[RT][NSLOT][2];
+            float factor[RT];
+            bool any_rescale = s_moved;
+    #pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                float x[NSLOT][4];
+                float bmax = -INFINITY;
+    #pragma unroll
+                for (int u = 0; u < NSLOT; ++u) {
+                    i4 S = sc[rt][J * u];
+    #pragma unroll
+                    for (int c = 1; c < J; ++c)
+                        if (jcol == c) S = sc[rt][J * u + c];
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        x[u][i] = (float)S[i] * (MODE == 0 ? R.ks[u][i] : R.ks[u][0]);
+                        if (MASKED) {
+                            const int t = key_of(T, u, i);
+                            if (!(t < t_end && t <= lim[rt])) x[u][i] = -INFINITY;
+                        }
+                        bmax = fmaxf(bmax, x[u][i]);
+                    }
+                }
+                bmax = col_max(bmax) * rowmul[rt];
+                float alpha = 1.0f;
+                if (bmax > mr[rt] + 8.0f) {  // (also the first block: mr == -inf)
+                    alpha = __builtin_amdgcn_exp2f(mr[rt] - bmax);
+                    mr[rt] = bmax;
+                }
+                float ps = 0.0f;
+    #pragma unroll
+                for (int u = 0; u < NSLOT; ++u) {
+                    float p[4];
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[u][i], rowmul[rt], -mr[rt]));
+                        // a column with no visible key yet keeps mr = -inf: its masked keys weigh 0
+                        if (MASKED && x[u][i] == -INFINITY) p[i] = 0.0f;
+                        ps += p[i];
+                    }
+                    const h4 w = {(_Float16)(p[0] * vsl[u][0]), (_Float16)(p[1] * vsl[u][1]),
+                                  (_Float16)(p[2] * vsl[u][2]), (_Float16)(p[3] * vsl[u][3])};
+                    const auto wb = __builtin_bit_cast(uint2, w);
+                    wpk[rt][u][0] = wb.x;
+                    wpk[rt][u][1] = wb.y;
+                }
+                lsum[rt] = lsum[rt] * alpha + ps;
+                factor[rt] = alpha * sf;
+                any_rescale |= alpha != 1.0f;
+            }
+
+            load_s(T + BLK, R);
+            __builtin_amdgcn_sched_barrier(0);
+
+            // -------------------------------------------- rescale the columns whose references moved
+            if (__any(any_rescale)) {
+    #pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+    #pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= factor[rt];
+                    pacc[rt] *= factor[rt];
+                }
+            }
+
+            // -------------------------------------------- P.V (+ weight sums): per lane group, keys
+            //      16g + 8v .. +8 of subset pair (v, 0), (v, 1)
+    #pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                h8 bq[RT];
+    #pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    uint32_t ww[4];
+    #pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int q = 2 * v + e;  // subset of keys 16g + 8v + 4e ..
+                        const int u = q / J;
+                        const bool mine = J == 1 || jcol == q % J;  // else the subset is another class's
+                        ww[2 * e] = mine ? wpk[rt][u][0] : 0u;
+                        ww[2 * e + 1] = mine ? wpk[rt][u][1] : 0u;
+                    }
+                    bq[rt] = __builtin_bit_cast(h8, ww);
+                }
+    #pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const h8 av = v == 0 ? biased_h8(VC.v[dt].x, VC.v[dt].y) : biased_h8(VC.v[dt].z, VC.v[dt].w);
+    #pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bq[rt], acc[rt][dt], 0, 0, 0);
+                }
+    #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
-                    acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bq[rt], acc[rt][dt], 0, 0, 0);
+                    pacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, bq[rt], pacc[rt], 0, 0, 0);
             }
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                pacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, bq[rt], pacc[rt], 0, 0, 0);
+        };
+        for (int T = t_begin;;) {
+            block(T, v0, v1);
+            T += BLK;
+            if (T >= t_end) break;
+            block(T, v1, v0);
+            T += BLK;
+            if (T >= t_end) break;
         }
-    };
-    for (int T = t_begin;;) {
-        block(T, v0, v1);
-        T += BLK;
-        if (T >= t_end) break;
-        block(T, v1, v0);
-        T += BLK;
-        if (T >= t_end) break;
+
     }
 
     // ---- merge the J columns of each row, normalise, write.  Lane (g, n) holds channels
     //      16 dt + 4g + i of column n.
-    const bool split_mode = a.nsplit > 1;
+    const bool split_mode = pslot >= 0;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const float l = col_sum(lsum[rt]);
@@ -486,7 +464,7 @@ __global__ __launch_bounds__(64 * WPB) void decode_c8_kernel(DecodeArgs a, int t
         const float mul = L > 0.0f ? 1.0f / L : 0.0f;
         const int r = r0 + j;
         const int64_t orow = (int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g;
-        const int64_t prow = ((int64_t)item * a.nsplit + s) * a.prs + j;
+        const int64_t prow = pslot * a.prs + j;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             const int d = dt * 16 + 4 * g;
@@ -510,19 +488,286 @@ __global__ __launch_bounds__(64 * WPB) void decode_c8_kernel(DecodeArgs a, int t
     }
 }
 
+// Rows, keys and output position of work item `item` = (sequence b, KV head h, row group rg).
+struct ItemGeo {
+    int b, h, qlen, qrow0, prior, r0, nrows, nvalid, kmax;
+};
+template <int ROWS>
+__device__ __forceinline__ ItemGeo item_geo(const DecodeArgs& a, int item) {
+    ItemGeo it;
+    const int rg = item % a.nrg;
+    const int bh = item / a.nrg;
+    it.h = bh % a.hkv;
+    it.b = bh / a.hkv;
+    it.qlen = a.cu ? a.cu[it.b + 1] - a.cu[it.b] : 1;
+    it.qrow0 = a.cu ? a.cu[it.b] : it.b;
+    it.prior = a.ctx[it.b] - it.qlen;
+    it.nrows = it.qlen * a.g;
+    it.r0 = rg * ROWS;
+    it.nvalid = min(ROWS, it.nrows - it.r0);
+    it.kmax = it.nvalid > 0 ? it.prior + (it.r0 + it.nvalid - 1) / a.g + 1 : 0;  // keys the last row sees
+    return it;
+}
+
+// zero output and lse = -inf for the rows of an item with no key (a sequence of length 0)
+template <int D>
+__device__ __forceinline__ void zero_rows(const DecodeArgs& a, const ItemGeo& it, int lane) {
+    for (int o = lane; o < it.nvalid * D; o += kWave) {
+        const int j = o / D, d = o % D;
+        const int r = it.r0 + j;
+        const int64_t orow = (int64_t)(it.qrow0 + r / a.g) * a.hq + it.h * a.g + r % a.g;
+        a.out[orow * D + d] = 0;
+        if (d == 0 && a.lse) a.lse[orow] = -INFINITY;
+    }
+}
+
+// Fixed partition: one wave per (item, split of split_len keys).  Items go fastest, so
+// consecutive workgroups go round-robin over the XCDs and each XCD gets an even share of the
+// items whatever the number of empty splits.
+template <int D, int MODE, int J, int RT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 1))) void decode_c8_kernel(DecodeArgs a, int total) {
+    constexpr int ROWS = J > 1 ? 16 / J : 16 * RT;
+    __shared__ int bt_s[MAX_SPLIT_PAGES];
+    const int wi = blockIdx.x;
+    if (wi >= total) return;
+    const int items = total / a.nsplit;
+    const int s = wi / items;
+    const int item = wi % items;
+    const ItemGeo it = item_geo<ROWS>(a, item);
+    if (it.nvalid <= 0) return;
+    if (it.kmax <= 0) {
+        if (s == 0) zero_rows<D>(a, it, threadIdx.x);
+        return;
+    }
+    const int t_begin = s * a.split_len;
+    if (t_begin >= it.kmax) return;
+    const int t_end = min(t_begin + a.split_len, it.kmax);
+    c8_segment<D, MODE, J, RT>(a, it.b, it.h, it.qlen, it.qrow0, it.prior, it.r0, it.nvalid, t_begin, t_end,
+                               a.nsplit > 1 ? (int64_t)item * a.nsplit + s : -1, bt_s);
+}
+
+// Balanced partition: with N key blocks (64 keys) over all items and a target of W waves, item i
+// with n_i blocks gets k_i = min(n_i, ceil(n_i W / N)) segments of near-equal length (at most
+// max(1, N / W) blocks each), one wave per segment: about W waves, all of about the same length, so the GPU runs one
+// full round of waves instead of rounds of very different fill.  The grid holds W + items waves
+// (an upper bound of the sum of the k_i); the spare ones return at once.  Wave K_i + s (K = prefix
+// sums of k, items in (sequence, KV head, row group) order) takes segment s of item i; a
+// one-segment item writes its result, others leave a partial in slot K_i + s, and segment 0
+// records K_i and k_i in seg[2i], seg[2i + 1] for the merge.  The plan is computed by every wave
+// from the sequence lengths, per sequence (its KV heads share the counts).
+template <int D, int MODE, int J, int RT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 1))) void decode_c8_sk_kernel(DecodeArgs a, int batch) {
+    constexpr int ROWS = J > 1 ? 16 / J : 16 * RT;
+    __shared__ int bt_s[MAX_SPLIT_PAGES];
+    extern __shared__ int kseq[];  // [batch + 1] prefix sums over sequences of their waves
+    const int lane = threadIdx.x;
+    const int W = a.sk_waves;
+    // blocks of row group rg of sequence b (the same for every KV head)
+    auto group_blocks = [&](int b, int rg) {
+        const int qlen = a.cu ? a.cu[b + 1] - a.cu[b] : 1;
+        const int nrows = qlen * a.g;
+        const int r0 = rg * ROWS;
+        if (r0 >= nrows) return 0;
+        const int nvalid = min(ROWS, nrows - r0);
+        const int kmax = a.ctx[b] - qlen + (r0 + nvalid - 1) / a.g + 1;
+        return kmax > 0 ? (kmax + BLK - 1) / BLK : 0;
+    };
+    // N = total blocks over every item, A = items with at least one block
+    int64_t N = 0;
+    int A = 0;
+    for (int b0 = 0; b0 < batch; b0 += kWave) {
+        int nb = 0, na = 0;
+        if (b0 + lane < batch)
+            for (int rg = 0; rg < a.nrg; ++rg) {
+                const int x = group_blocks(b0 + lane, rg);
+                nb += x;
+                na += x > 0;
+            }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) {
+            nb += __shfl_xor(nb, d, kWave);
+            na += __shfl_xor(na, d, kWave);
+        }
+        N += nb;
+        A += na;
+    }
+    if (N == 0) return;  // every item is empty: the merge writes the zero rows
+    N *= a.hkv;
+    A *= a.hkv;
+    // ceil rounding adds less than one segment per item: planning for W - A waves keeps the total
+    // within the W waves the GPU holds at once (one round)
+    const int64_t Wp = W > 2 * A ? W - A : (W > A ? A : 1);
+    auto segs = [&](int nb, int64_t NN) {
+        return nb > 0 ? (int)min((int64_t)nb, ((int64_t)nb * Wp + NN - 1) / NN) : 0;
+    };
+    // waves of each sequence (all its KV heads and row groups) and their prefix sums
+    int carry = 0;
+    for (int b0 = 0; b0 < batch; b0 += kWave) {
+        const int b = b0 + lane;
+        int x = 0;
+        if (b < batch)
+            for (int rg = 0; rg < a.nrg; ++rg) x += segs(group_blocks(b, rg), N);
+        x *= a.hkv;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {  // inclusive scan over the wave
+            const int y = __shfl_up(x, d, kWave);
+            if (lane >= d) x += y;
+        }
+        if (b < batch) kseq[b + 1] = carry + x;
+        carry += __shfl(x, kWave - 1, kWave);
+    }
+    if (lane == 0) kseq[0] = 0;
+    __builtin_amdgcn_wave_barrier();
+    const int wid = blockIdx.x;
+    if (wid >= carry) return;
+    int lo = 0, hi = batch;  // kseq[lo] <= wid < kseq[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (kseq[mid] <= wid) lo = mid; else hi = mid;
+    }
+    const int b = lo;
+    // within sequence b: items (h, rg) in order, rg fastest
+    int per_head = 0;
+    for (int rg = 0; rg < a.nrg; ++rg) per_head += segs(group_blocks(b, rg), N);
+    const int off = wid - kseq[b];
+    const int h = off / per_head;
+    int rem = off - h * per_head, rg = 0, k = segs(group_blocks(b, 0), N);
+    int first = kseq[b] + h * per_head;
+    while (rem >= k) {
+        rem -= k;
+        first += k;
+        ++rg;
+        k = segs(group_blocks(b, rg), N);
+    }
+    const int seg = rem;
+    const int item = (b * a.hkv + h) * a.nrg + rg;
+    const ItemGeo it = item_geo<ROWS>(a, item);
+    const int nb = (it.kmax + BLK - 1) / BLK;
+    const int b0 = (int)((int64_t)nb * seg / k), b1 = (int)((int64_t)nb * (seg + 1) / k);
+    if (seg == 0 && lane == 0) {
+        a.seg[2 * item] = first;
+        a.seg[2 * item + 1] = k;
+    }
+    c8_segment<D, MODE, J, RT>(a, it.b, it.h, it.qlen, it.qrow0, it.prior, it.r0, it.nvalid, b0 * BLK,
+                               min(b1 * BLK, it.kmax), k == 1 ? -1 : (int64_t)wid, bt_s);
+}
+
+// Merge of the balanced partition: item i's partials sit in slots seg[2i] .. seg[2i] + seg[2i+1] - 1;
+// a one-segment item is already written; an item with no key gets zero rows.  Thread (row j,
+// 8-channel group c), as in the split merge.
+template <int D, int ROWS>
+__global__ __launch_bounds__(1024) void merge_sk_kernel(DecodeArgs a) {
+    constexpr int CG = D / 8;
+    const int item = blockIdx.x;
+    const ItemGeo it = item_geo<ROWS>(a, item);
+    if (it.nvalid <= 0) return;
+    if (it.kmax <= 0) {
+        if (threadIdx.x < kWave) zero_rows<D>(a, it, threadIdx.x);
+        return;
+    }
+    const int k = a.seg[2 * item + 1];
+    if (k <= 1) return;  // one segment: the result is already written
+    const int w0 = a.seg[2 * item], w1 = w0 + k - 1;
+    const int jr = threadIdx.x / CG, cg = threadIdx.x % CG;
+    if (jr >= it.nvalid) return;
+    float M = -INFINITY, wsum = 0.0f;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+    constexpr int CHM = 8;
+    for (int s0 = w0; s0 <= w1; s0 += CHM) {
+        float l2[CHM];
+        float4 p0[CHM], p1[CHM];
+#pragma unroll
+        for (int c = 0; c < CHM; ++c) {
+            const int ww = s0 + c;
+            if (ww <= w1) {
+                const int64_t row = (int64_t)ww * a.prs + jr;
+                l2[c] = a.part_lse[row];
+                const float4* pp = reinterpret_cast<const float4*>(a.part_o + row * D) + 2 * cg;
+                p0[c] = pp[0];
+                p1[c] = pp[1];
+            } else {
+                l2[c] = -INFINITY;
+                p0[c] = p1[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+        float mc = M;
+#pragma unroll
+        for (int c = 0; c < CHM; ++c) mc = fmaxf(mc, l2[c]);
+        if (mc == -INFINITY) continue;
+        const float sc = M == -INFINITY ? 0.0f : exp2f(M - mc);
+        M = mc;
+        wsum *= sc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= sc;
+#pragma unroll
+        for (int c = 0; c < CHM; ++c) {
+            const float wt = l2[c] == -INFINITY ? 0.0f : exp2f(l2[c] - M);
+            wsum += wt;
+            acc[0] = fmaf(wt, p0[c].x, acc[0]);
+            acc[1] = fmaf(wt, p0[c].y, acc[1]);
+            acc[2] = fmaf(wt, p0[c].z, acc[2]);
+            acc[3] = fmaf(wt, p0[c].w, acc[3]);
+            acc[4] = fmaf(wt, p1[c].x, acc[4]);
+            acc[5] = fmaf(wt, p1[c].y, acc[5]);
+            acc[6] = fmaf(wt, p1[c].z, acc[6]);
+            acc[7] = fmaf(wt, p1[c].w, acc[7]);
+        }
+    }
+    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+    const int r = it.r0 + jr;
+    const int64_t orow = (int64_t)(it.qrow0 + r / a.g) * a.hq + it.h * a.g + r % a.g;
+    uint16_t* op = a.out + orow * D + 8 * cg;
+    uint32_t pk[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        pk[e] = f32_to_bf16_rne(acc[2 * e] * inv) | (f32_to_bf16_rne(acc[2 * e + 1] * inv) << 16);
+    if ((reinterpret_cast<uintptr_t>(op) & 15) == 0) {
+        *reinterpret_cast<uint4*>(op) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            op[2 * e] = (uint16_t)(pk[e] & 0xffffu);
+            op[2 * e + 1] = (uint16_t)(pk[e] >> 16);
+        }
+    }
+    if (cg == 0 && a.lse) a.lse[orow] = wsum > 0.0f ? (M + log2f(wsum)) * kLn2 : -INFINITY;
+}
+
 template <int D, int MODE, int J, int RT>
 hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream) {
+    constexpr int ROWS = J > 1 ? 16 / J : 16 * RT;
     const int64_t items = (int64_t)batch * a.hkv * a.nrg;
+    if (items == 0) return hipSuccess;
+    if (a.sk_waves > 0) {  // balanced partition
+        if (batch > MAX_SK_SEQS) return hipErrorInvalidValue;
+        const size_t lds = (size_t)(batch + 1) * sizeof(int);
+        hipLaunchKernelGGL((decode_c8_sk_kernel<D, MODE, J, RT>), dim3((unsigned)(a.sk_waves + items)), dim3(64),
+                           lds, stream, a, batch);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int threads = ((ROWS * D / 8 + kWave - 1) / kWave) * kWave;
+        hipLaunchKernelGGL((merge_sk_kernel<D, ROWS>), dim3((unsigned)items), dim3(threads), 0, stream, a);
+        return hipGetLastError();
+    }
     const int64_t grid = items * a.nsplit;
-    if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    const int64_t wgs = (grid + WPB - 1) / WPB;
-    hipLaunchKernelGGL((decode_c8_kernel<D, MODE, J, RT>), dim3((unsigned)wgs), dim3(64 * WPB), 0, stream, a,
-                       (int)grid);
+    hipLaunchKernelGGL((decode_c8_kernel<D, MODE, J, RT>), dim3((unsigned)grid), dim3(64), 0, stream, a, (int)grid);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
-    constexpr int ROWS = J > 1 ? 16 / J : 16 * RT;
     return launch_merge(a, batch, D, ROWS, stream);
+}
+
+template <int D, int MODE, int J, int RT>
+int sk_waves_one(int batch) {
+    int per_cu = 0;
+    const size_t lds = (size_t)(batch + 1) * sizeof(int);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_c8_sk_kernel<D, MODE, J, RT>, 64, lds) !=
+            hipSuccess ||
+        per_cu <= 0)
+        return 0;
+    return per_cu;
 }
 
 template <int D, int MODE>
@@ -541,11 +786,27 @@ hipError_t launch_mode(const DecodeArgs& a, int batch, int j, int rt, int mode, 
     return hipErrorInvalidValue;
 }
 
+template <int D, int MODE>
+int sk_shape(int j, int rt, int batch) {
+    if (j == 4 && rt == 1) return sk_waves_one<D, MODE, 4, 1>(batch);
+    if (j == 2 && rt == 1) return sk_waves_one<D, MODE, 2, 1>(batch);
+    if (j == 1 && rt == 1) return sk_waves_one<D, MODE, 1, 1>(batch);
+    if (j == 1 && rt == 2) return sk_waves_one<D, MODE, 1, 2>(batch);
+    return 0;
+}
+
 }  // namespace
+
+int decode_c8_waves_per_cu(int head_dim, int classes, int row_tiles, int mode, int batch) {
+    if (batch > MAX_SK_SEQS) return 0;
+    if (head_dim == 64) return mode == 0 ? sk_shape<64, 0>(classes, row_tiles, batch) : sk_shape<64, 1>(classes, row_tiles, batch);
+    if (head_dim == 128) return mode == 0 ? sk_shape<128, 0>(classes, row_tiles, batch) : sk_shape<128, 1>(classes, row_tiles, batch);
+    return 0;
+}
 
 hipError_t launch_decode_c8(const DecodeArgs& a, int batch, int head_dim, int classes, int row_tiles,
                             int mode, hipStream_t stream) {
-    if (a.split_len > MAX_SPLIT || (a.split_len % BLK) != 0) return hipErrorInvalidValue;
+    if (a.sk_waves <= 0 && (a.split_len > MAX_SPLIT || (a.split_len % BLK) != 0)) return hipErrorInvalidValue;
     if (head_dim == 64) return launch_mode<64>(a, batch, classes, row_tiles, mode, stream);
     if (head_dim == 128) return launch_mode<128>(a, batch, classes, row_tiles, mode, stream);
     return hipErrorInvalidValue;

@@ -60,6 +60,7 @@ struct DecodePlan {
     int nrg;
     int nsplit;
     int split_len;
+    int sk_waves;      // kernel 3, no forced split: balanced partition over this many waves
     size_t ws_bytes;
 };
 
@@ -78,8 +79,9 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
     if (max_q_len < 1) max_q_len = 1;
     int kernel = mode == 2 ? 2 : 3;  // int8 pages: exact int8 scores; bf16 pages: bf16 scores
     if (opts) {
-        for (int i = 0; i < 6; ++i)
+        for (int i = 0; i < 5; ++i)
             if (opts->reserved[i] != 0) return PKV_ERR_INVALID_ARG;
+        if (opts->partition < 0 || opts->partition > 2) return PKV_ERR_INVALID_ARG;
         if (opts->split_tokens < 0) return PKV_ERR_INVALID_ARG;
         if (opts->kernel < 0 || opts->kernel > 3) return PKV_ERR_INVALID_ARG;
         if (opts->kernel != 0) kernel = opts->kernel;
@@ -125,14 +127,33 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
     }
     const int64_t max_ctx = (int64_t)mbs * bs;
     const int64_t items = (int64_t)batch * hkv * p->nrg;
+    p->sk_waves = 0;
+    const int partition = opts ? opts->partition : 0;
+    const bool fixed = partition == 1 || (opts && opts->split_tokens > 0);
+    if (kernel == 3 && !fixed && items > 0 && (partition == 2 || max_ctx >= 16384)) {
+        // balanced partition: every key block of every item in one list, cut into as many equal
+        // ranges as the GPU holds waves of the kernel at once (no partly filled rounds of waves).
+        // It pays one more memory round trip per wave (the plan), which only long contexts
+        // amortise, and needs the items to be few against the waves.
+        const int per_cu = pkv::decode_c8_waves_per_cu(head_dim, p->classes, p->rg, mode, batch);
+        if (per_cu > 0 && (partition == 2 || items * 2 <= (int64_t)per_cu * device_cus())) {
+            p->sk_waves = per_cu * device_cus();
+            p->split_len = 0;
+            p->nsplit = p->sk_waves;
+            const size_t slots = (size_t)(p->sk_waves + items) * (size_t)p->prs;
+            p->ws_bytes = slots * (size_t)(head_dim + 1) * 4 + (size_t)items * 2 * 4;
+            return PKV_OK;
+        }
+    }
     int64_t L;
     if (opts && opts->split_tokens > 0) {
         L = cdiv(opts->split_tokens, 128) * 128;
     } else {
-        // Aim for ~16 workgroups per compute unit counting every (possibly empty) split, with
-        // partitions of 256..2048 keys: long enough to amortise the per-workgroup query load and
-        // partial write, short enough to spread a few long sequences over the whole chip.
-        const int64_t target = 16LL * device_cus();
+        // Aim for ~16 (int8-score kernel: ~11) workgroups per compute unit counting every
+        // (possibly empty) split, with partitions of 256..2048 keys: long enough to amortise the
+        // per-workgroup query load and partial write, short enough to spread a few long sequences
+        // over the whole chip.
+        const int64_t target = (kernel == 3 ? 11LL : 16LL) * device_cus();
         const int64_t want_splits = items > 0 ? (target + items - 1) / items : 1;
         L = cdiv(cdiv(max_ctx, want_splits), 128) * 128;
         if (L < 256) L = 256;
@@ -303,8 +324,15 @@ int pkv_decode_gqa(const void* q, int32_t num_q_heads, const pkv_cache_t* cache,
     a.nsplit = p.nsplit;
     a.split_len = p.split_len;
     a.scale_log2 = scale * 1.4426950408889634f;
-    if (p.nsplit > 1) {
-        const int64_t items = (int64_t)batch * a.hkv * p.nrg;
+    const int64_t items = (int64_t)batch * a.hkv * p.nrg;
+    if (p.sk_waves > 0) {
+        float* ws = static_cast<float*>(workspace);
+        const int64_t slots = (p.sk_waves + items) * p.prs;
+        a.part_o = ws;
+        a.part_lse = ws + slots * cache->head_dim;
+        a.seg = reinterpret_cast<int32_t*>(a.part_lse + slots);
+        a.sk_waves = p.sk_waves;
+    } else if (p.nsplit > 1) {
         float* ws = static_cast<float*>(workspace);
         a.part_o = ws;
         a.part_lse = ws + items * p.nsplit * p.prs * cache->head_dim;

@@ -71,6 +71,8 @@ struct DecodeArgs {
     int split_len;
     int prs;           // partial rows per (item, split) in part_o / part_lse
     float scale_log2;  // softmax scale * log2(e)
+    int sk_waves;      // > 0: balanced partition over this many waves (int8-score kernel)
+    int32_t* seg;      // balanced partition: first / last wave of each item [items][2]
 };
 
 hipError_t launch_store(const StoreArgs& a, int head_dim, int mode, hipStream_t stream);
@@ -82,6 +84,8 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int batch, int head_dim, int 
 // int8 cache (modes 0, 1): classes = subset classes per column tile (1, 2, 4), row_tiles = 1 or 2
 hipError_t launch_decode_c8(const DecodeArgs& a, int batch, int head_dim, int classes, int row_tiles,
                             int mode, hipStream_t stream);
+// resident waves per compute unit of the balanced-partition kernel (0: not available)
+int decode_c8_waves_per_cu(int head_dim, int classes, int row_tiles, int mode, int batch);
 // log-sum-exp merge of the split partials; rows_per_item = query rows of one row group
 hipError_t launch_merge(const DecodeArgs& a, int batch, int head_dim, int rows_per_item, hipStream_t stream);
 

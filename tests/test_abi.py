@@ -117,8 +117,10 @@ def test_dequant_and_decode_reject_bad_arguments(pkv):
                ctypes.byref(o), None) == -3
     # reserved option fields must be zero
     o2 = pkv._opts()
-    o2.reserved[0] = 1
+    o2.reserved[1] = 1
     assert dec(P, 4, ctypes.byref(c), P, 8, P, None, 1, 1, 1.0, P, None, P, 1 << 30, ctypes.byref(o2), None) == -1
+    o3 = pkv._opts(partition=3)  # no such partition
+    assert dec(P, 4, ctypes.byref(c), P, 8, P, None, 1, 1, 1.0, P, None, P, 1 << 30, ctypes.byref(o3), None) == -1
     # unsupported head_dim
     bad = _cache_struct(pkv, hd=80)
     assert dec(P, 4, ctypes.byref(bad), P, 8, P, None, 1, 1, 1.0, P, None, P, 1 << 30, ctypes.byref(o), None) == -2

@@ -276,3 +276,60 @@ def test_unwritten_slots_do_not_reach_the_output(mode, kernel):
     out, lse = r.decode(kernel=kernel)
     assert torch.isfinite(out.float()).all()
     r.assert_decode_close(out, lse)
+
+
+def test_balanced_partition_edge_cases():
+    """The planned (balanced) partition of the int8-score kernel: a batch with no key at all, a
+    batch mixing one-block and long sequences (one-segment and many-segment items), a multi-token
+    batch (one subset class, two row tiles), a batch of many short sequences, and more sequences
+    than the balanced partition takes (the fixed-split plan is used)."""
+    # every sequence empty: only the merge writes (zero rows, lse -inf)
+    r = Run(_wl(0, 128, 16, 4, [0, 0, 0], seed=11))
+    r.store_prior()
+    r.store_new()
+    out, lse = r.decode(partition=2)
+    torch.cuda.synchronize()
+    assert bool((out == 0).all()) and bool(torch.isneginf(lse).all())
+    # short and long sequences together
+    r = Run(_wl(0, 128, 16, 4, [1, 5, 64, 65, 2000, 3, 4096, 700], seed=12))
+    r.store_prior()
+    r.store_new()
+    out, lse = r.decode(partition=2)
+    r.assert_decode_close(out, lse)
+    # multi-token rows: 16 x 5 = 80 rows per KV head (two 16-row tiles per row group)
+    r = Run(_wl(1, 128, 16, 5, [40, 700, 17, 1500], [16, 9, 16, 3], seed=13))
+    r.store_prior()
+    r.store_new()
+    out, lse = r.decode(partition=2)
+    r.assert_decode_close(out, lse)
+    # 600 sequences x 8 KV heads, then 4200 sequences: beyond the balanced partition's limit of
+    # 4096 sequences (the fixed-split plan is used)
+    ctx = list(np.random.default_rng(14).integers(0, 40, size=600))
+    r = Run(_wl(0, 64, 16, 4, ctx, hkv=8, seed=14))
+    r.store_prior()
+    r.store_new()
+    out, lse = r.decode(partition=2)
+    r.assert_decode_close(out, lse)
+    ctx = list(np.random.default_rng(16).integers(0, 20, size=4200))
+    r = Run(_wl(0, 64, 16, 4, ctx, hkv=2, seed=16))
+    r.store_prior()
+    r.store_new()
+    out, lse = r.decode(partition=2)
+    r.assert_decode_close(out, lse)
+
+
+def test_planned_partition_matches_fixed_splits():
+    """The balanced partition and fixed splits differ only in rounding (fp16 weights against
+    different running maxima; bf16 output)."""
+    r = Run(_wl(0, 128, 16, 4, [3000, 1200, 4096, 64, 900], seed=15), with_oracle=False)
+    r.store_prior()
+    r.store_new()
+    planned, lp = r.decode(partition=2)
+    fixed, lf = r.decode(split_tokens=4096)
+    planned2, lp2 = r.decode(partition=2)
+    torch.cuda.synchronize()
+    assert torch.equal(planned.view(torch.int16), planned2.view(torch.int16))
+    diff = (planned.float() - fixed.float()).abs()
+    bound = fixed.float().abs() * 2.0 ** -7 + 2.0 ** -10 * float(fixed.float().abs().max())
+    assert bool((diff <= bound).all()), float((diff - bound).max())
+    assert torch.allclose(lp, lf, rtol=1e-5, atol=1e-5)
