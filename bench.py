@@ -224,8 +224,9 @@ def main():
     value = touched / step_s / 1e9
     new_tokens = w.num_new_tokens if not w.decode_only else int((w.context_lengths > 0).sum())
     achieved = decode_bytes / (dec_ms * 1e-3) / 1e9
-    kernel_key = f"decode.config{args.config}"
-    traffic = traffic_record(kernel_key)
+    # the counters were taken with the library's own choice of kernel and split
+    default_plan = args.kernel == 0 and args.split_tokens == 0
+    traffic = traffic_record(f"decode.config{args.config}") if default_plan else None
 
     cpu = None
     if not args.no_cpu_baseline:

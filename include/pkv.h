@@ -33,7 +33,9 @@
  *
  * Cache layout (caller-owned; element (block, kv head, slot, channel)):
  *   K       [num_blocks][num_kv_heads][block_size][head_dim]  (token-major page)
- *   V       [num_blocks][num_kv_heads][head_dim][block_size]  (channel-major page)
+ *   V       [num_blocks][num_kv_heads][block_size/16][head_dim][16]  (the page in
+ *           16-slot tiles, each channel-major: slots 16i .. 16i+15 of one channel are
+ *           16 adjacent elements)
  *   scales  PKV_QUANT_PER_TOKEN: float [num_blocks][num_kv_heads][block_size]
  *           PKV_QUANT_PER_BLOCK: float [num_blocks][num_kv_heads]
  *           PKV_QUANT_NONE_BF16: none (K and V hold bf16)

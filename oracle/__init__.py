@@ -6,7 +6,7 @@ library or its Python binding, and nothing here imports them.
 
 All arrays are numpy arrays on the host.  bf16 data travels as ``uint16``
 bit patterns.  The cache arrays follow the layout the oracle documents:
-K ``[NB, Hkv, BS, D]``, V ``[NB, Hkv, D, BS]`` (channel-major pages), scales
+K ``[NB, Hkv, BS, D]``, V ``[NB, Hkv, BS/16, D, 16]`` (pages of channel-major 16-slot tiles), scales
 ``[NB, Hkv, BS]`` (per token) or ``[NB, Hkv]`` (per block).
 """
 from __future__ import annotations
@@ -82,7 +82,8 @@ class HostCache:
         self.mode, self.nb, self.hkv, self.bs, self.d = mode, num_blocks, num_kv_heads, block_size, head_dim
         dt = np.uint16 if mode == 2 else np.int8
         self.k = np.full((num_blocks, num_kv_heads, block_size, head_dim), fill, dtype=dt)
-        self.v = np.full((num_blocks, num_kv_heads, head_dim, block_size), fill, dtype=dt)
+        vt = 16 if block_size % 16 == 0 else block_size  # slots per V tile
+        self.v = np.full((num_blocks, num_kv_heads, block_size // vt, head_dim, vt), fill, dtype=dt)
         if mode == 0:
             self.k_scale = np.zeros((num_blocks, num_kv_heads, block_size), np.float32)
             self.v_scale = np.zeros((num_blocks, num_kv_heads, block_size), np.float32)

@@ -33,7 +33,10 @@
  *
  * Cache layout (the boundary contract; element (block, head, slot, channel)):
  *   K  [NB][Hkv][BS][D]   int8, or bf16 in mode 2
- *   V  [NB][Hkv][D][BS]   int8, or bf16 in mode 2 (channel-major page)
+ *   V  [NB][Hkv][BS/16][D][16]   int8, or bf16 in mode 2 (the page in 16-slot tiles, each
+ *                                 channel-major: 16 consecutive slots of one channel adjacent;
+ *                                 a block size that is not a multiple of 16 makes one tile of
+ *                                 BS slots, [NB][Hkv][D][BS])
  *   scales mode 0: [NB][Hkv][BS] fp32;  mode 1: [NB][Hkv] fp32;  mode 2: none
  */
 #include <math.h>
@@ -108,7 +111,9 @@ static int64_t k_index(const cache_t *c, int64_t blk, int h, int slot, int ch)
 
 static int64_t v_index(const cache_t *c, int64_t blk, int h, int slot, int ch)
 {
-    return ((blk * c->hkv + h) * (int64_t)c->d + ch) * c->bs + slot;
+    int64_t page = (blk * c->hkv + h) * (int64_t)c->bs * c->d;
+    int t = c->bs % 16 == 0 ? 16 : c->bs; /* slots per tile */
+    return page + ((int64_t)(slot / t) * c->d + ch) * t + slot % t;
 }
 
 static int64_t tok_scale_index(const cache_t *c, int64_t blk, int h, int slot)

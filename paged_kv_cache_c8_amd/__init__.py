@@ -105,8 +105,9 @@ def _opts(split_tokens=0, kernel=0, partition=0):
 
 
 class Cache:
-    """A paged cache in device memory: K ``[NB, Hkv, BS, D]``, V ``[NB, Hkv, D, BS]`` (int8, or
-    bf16 in mode 2), scales ``[NB, Hkv, BS]`` (mode 0) or ``[NB, Hkv]`` (mode 1)."""
+    """A paged cache in device memory: K ``[NB, Hkv, BS, D]``, V ``[NB, Hkv, BS/16, D, 16]`` (pages
+    of channel-major 16-slot tiles; int8, or bf16 in mode 2), scales ``[NB, Hkv, BS]`` (mode 0) or
+    ``[NB, Hkv]`` (mode 1)."""
 
     def __init__(self, quant_mode, num_blocks, num_kv_heads, block_size, head_dim, device="cuda",
                  k=None, v=None, k_scale=None, v_scale=None):
@@ -115,7 +116,7 @@ class Cache:
         self.block_size, self.head_dim = int(block_size), int(head_dim)
         dt = torch.bfloat16 if self.quant_mode == QUANT_NONE_BF16 else torch.int8
         shape_k = (num_blocks, num_kv_heads, block_size, head_dim)
-        shape_v = (num_blocks, num_kv_heads, head_dim, block_size)
+        shape_v = (num_blocks, num_kv_heads, max(1, block_size // 16), head_dim, min(block_size, 16))
         self.k = k if k is not None else torch.zeros(shape_k, dtype=dt, device=device)
         self.v = v if v is not None else torch.zeros(shape_v, dtype=dt, device=device)
         if self.quant_mode == QUANT_PER_TOKEN:

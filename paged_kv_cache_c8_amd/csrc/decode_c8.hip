@@ -11,10 +11,12 @@
 //    accumulates K.lo on top: the exact integer dot product of the codes with q.  The K scale and
 //    the power of two come back in the fp32 softmax.
 //  * Keys are walked in blocks of 64.  Lane group g (lanes 16g .. 16g+15) owns the 16 keys
-//    16g .. 16g+15 of the block: it loads them as 16 consecutive bytes of each channel row of the
-//    channel-major V page (one 16-byte load per 16 channels).  The block is cut into four key
-//    subsets s = (v, e) = (s / 2, s % 2); subset s holds keys 16g + 8v + 4e + i (i < 4) of every
-//    lane group, so that after its score MFMA lane (g, n) holds the weights of exactly those keys.
+//    16g .. 16g+15 of the block, one 16-slot V tile: it loads them as the 16 consecutive bytes of
+//    each channel row of that channel-major tile (one 16-byte load per 16 channels; a block reads
+//    its four tiles whole, so no cache line is fetched for half its bytes).  The block is cut
+//    into four key subsets s = (v, e) = (s / 2, s % 2); subset s holds keys 16g + 8v + 4e + i
+//    (i < 4) of every lane group, so that after its score MFMA lane (g, n) holds the weights of
+//    exactly those keys.
 //  * The 16 columns of every MFMA tile are (row r, subset class j): column n = J r + j with
 //    J = 16 / rows in {1, 2, 4}; class j takes the subsets with s % J == j.  Each column runs its
 //    own online softmax (running max, weight sum, V-scale reference), so every lane's softmax
@@ -145,7 +147,7 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
     const int rho = lane & 15;                             // score A operand: key row slot
     const int kchunk = rho >> 2;                           // ... whose key is 16 kchunk + 8v + 4e + rho % 4
     const int k_lane = (rho & 3) * D + g * 16 * KSTEP;      // its channels g*16*KSTEP ..
-    const int v_lane = n * a.bs;                           // V operand: channel row n of a tile
+    const int v_lane = n * kVTile;                         // V operand: channel row n of a tile
 
     const uint32_t ones_w[4] = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
     const h8 ones = __builtin_bit_cast(h8, ones_w);
@@ -204,10 +206,10 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
             }
         };
         auto load_v_at = [&](int T, int pid, C8V<D>& R) {
-            const int sl = (T + 16 * g) & (a.bs - 1);
-            const uint8_t* vp = vb + (int64_t)pid * page_bytes + sl + v_lane;
+            const int sl = (T + 16 * g) & (a.bs - 1);  // first slot of the lane group's V tile
+            const uint8_t* vp = vb + (int64_t)pid * page_bytes + sl * D + v_lane;
     #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) R.v[dt] = load16(vp + (int64_t)dt * 16 * a.bs);
+            for (int dt = 0; dt < DT; ++dt) R.v[dt] = load16(vp + dt * 16 * kVTile);
         };
         auto load_k = [&](int T, C8Regs<D, J>& R) { load_k_at(T, bt_s[chunk_page(T, kchunk) - blk0], R); };
         auto load_s = [&](int T, C8Regs<D, J>& R) { load_s_at(T, bt_s[chunk_page(T, g) - blk0], R); };

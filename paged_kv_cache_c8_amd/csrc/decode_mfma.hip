@@ -20,7 +20,7 @@
 //   softmax online over blocks, per query row (lane column n; rows meet across lanes n+16k).
 //           The weights p * s_v / S (S = running max of the V scales, so the fp16 weights stay in
 //           [0, 1]) of keys 8g .. 8g+7 are exactly lane (n, g)'s slice of the P operand.
-//   P.V     O (rows x channels) += P . V: the channel-major V page gives the 8 keys of one channel
+//   P.V     O (rows x channels) += P . V: the channel-major V tile gives the 8 keys of one channel
 //           as 8 contiguous bytes - the B operand - with no transpose.  When a row's running max
 //           or S grows, its accumulator row is rescaled (rows 4g+i of lane g; factors fetched from
 //           the lanes that own those rows).
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     const int64_t head_bytes = (int64_t)h * a.bs * D * C::ESZ;
     const int krow_off = 8 * (rho >> 2) + (rho & 3);                 // score tile u adds 4u
     const int k_lane_bytes = kg * C::KB;
-    const int v_lane_bytes = n * a.bs * C::ESZ;                      // channel n of each 16-channel tile
+    const int v_lane_bytes = n * kVTile * C::ESZ;                    // channel n of each 16-channel tile
 
     auto load_block = [&](int T, BlockRegs<D, MODE>& R) {
         {
@@ -243,10 +243,11 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         if (t0 >= t_end) t0 = t_begin;
         const int64_t bt0 = bt_s[(t0 >> a.log2bs) - blk0];
         const int slot0 = t0 & (a.bs - 1);
-        const uint8_t* vp = vbase + bt0 * page_bytes + head_bytes + v_lane_bytes + slot0 * C::ESZ;
+        const uint8_t* vp = vbase + bt0 * page_bytes + head_bytes + v_lane_bytes +
+                            ((slot0 / kVTile) * D * kVTile + slot0 % kVTile) * C::ESZ;
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-            const uint8_t* vpd = vp + (int64_t)dt * 16 * a.bs * C::ESZ;
+            const uint8_t* vpd = vp + dt * 16 * kVTile * C::ESZ;
             if constexpr (C::VW == 2) {
                 const uint2 w = *reinterpret_cast<const uint2*>(vpd);
                 R.v[dt][0] = w.x; R.v[dt][1] = w.y;

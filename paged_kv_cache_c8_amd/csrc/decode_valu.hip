@@ -22,7 +22,7 @@
 //   2. softmax: one wave per row (two when RG = 8) takes the chunk max, rescales the running
 //      sum, and writes the weights of token pairs to LDS: p * s_v / S (fp16; S = the chunk's
 //      largest V scale, applied later in fp32) or p (bf16 pages).
-//   3. P.V: each thread owns NU channels of one token group.  The channel-major V page gives 16
+//   3. P.V: each thread owns NU channels of one token group.  The channel-major V tiles give 16
 //      (8 bf16) consecutive tokens of one channel per 16-byte load, i.e. token pairs for dot2;
 //      the pair weights are LDS broadcasts shared by the NU channels.
 // At the end the token groups' accumulators are summed through LDS.
@@ -242,8 +242,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
         for (int k = 0; k < C::NU; ++k) acc[j][k] = 0.0f;
 
-    // P.V thread mapping: consecutive threads walk a page in memory order (channel-major,
-    // then 16-byte segment), so each load instruction covers contiguous bytes.
+    // P.V thread mapping: consecutive threads take consecutive 16-byte segments of a page's channel
+    // (one per 16-slot V tile), then the next channel.
     const int seg_per_row = a.bs / C::TPU;
     const int pv_seg = tid % seg_per_row;
     const int pv_dl = (tid / seg_per_row) % C::TPT;
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
             for (int k = 0; k < C::NU; ++k) {
                 const int d = pv_dl + k * C::TPT;
-                R.v[k] = load16(vbase + ((page * D + d) * a.bs) * C::ESZ + seg * 16);
+                R.v[k] = load16(vbase + v_elem(page, D, a.bs, d, seg * C::TPU) * C::ESZ);
             }
         }
 #pragma unroll

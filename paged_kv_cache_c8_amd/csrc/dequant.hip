@@ -6,8 +6,9 @@
 // the context lengths.  One workgroup per (sequence, logical block, KV head) page; the reviews'
 // per-sequence .item() and list-concatenation loop becomes a single launch with no host sync.
 //
-// K pages are token-major and stream straight to the output rows.  V pages are channel-major, so
-// each workgroup stages its page in LDS (16-byte loads) and reads it back transposed.
+// K pages are token-major and stream straight to the output rows.  V pages are channel-major
+// within 16-slot tiles, so each workgroup stages its page in LDS (16-byte loads) and reads it
+// back transposed.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
                 } else {
                     const uint16_t* vp = reinterpret_cast<const uint16_t*>(vpage);
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) y[k] = vp[(c0 + k) * a.bs + slot];
+                    for (int k = 0; k < 8; ++k) y[k] = vp[v_elem(0, D, a.bs, c0 + k, slot)];
                 }
             } else {
                 const float s = MODE == 0 ? scales[page * a.bs + slot] : scales[page];
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
                 } else {
                     const int8_t* vp = reinterpret_cast<const int8_t*>(vpage);
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) codes[k] = vp[(c0 + k) * a.bs + slot];
+                    for (int k = 0; k < 8; ++k) codes[k] = vp[v_elem(0, D, a.bs, c0 + k, slot)];
                 }
 #pragma unroll
                 for (int k = 0; k < 8; ++k) y[k] = f32_to_bf16_rne((float)codes[k] * s);

@@ -9,6 +9,18 @@ namespace pkv {
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------------------------------------
+// Cache page layout: K page (block, KV head) is [BS][D] (token rows); V page is [BS/16][D][16]:
+// tiles of 16 slots, each channel-major (the 16 slots of one channel are contiguous).
+// ---------------------------------------------------------------------------------------------
+
+constexpr int kVTile = 16;  // slots per V tile
+
+// element offset of V (page = block * Hkv + head, channel c, slot) from the start of the cache
+__device__ __forceinline__ int64_t v_elem(int64_t page, int D, int bs, int c, int slot) {
+    return page * D * bs + ((int64_t)(slot / kVTile) * D + c) * kVTile + slot % kVTile;
+}
+
+// ---------------------------------------------------------------------------------------------
 // bf16
 // ---------------------------------------------------------------------------------------------
 

@@ -8,7 +8,7 @@
 //   per token (mode 0): one wave per (token, KV head); the wave's lanes hold the head_dim
 //       values, a DPP/shuffle max gives the absmax, scale = fl32(absmax / 127), each lane
 //       divides (IEEE) and rounds half to even.  K rows are written as contiguous bytes; V goes
-//       to the channel-major page (one byte per channel, stride block_size).
+//       to the slot's channel-major 16-slot tile (one byte per channel, stride 16).
 //   per block (mode 1): one workgroup per (sequence, block touched, KV head) - the single writer
 //       of that block's scale.  s = max(s_old, fl32(absmax_new / 127)); when s grows the codes
 //       already in the block are re-quantized from fl32(code * s_old).
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void store_token_kernel(StoreArgs a) {
                 for (int e = 0; e < EPL; ++e) row[e] = (uint16_t)bits[e];
             } else {
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) dst[(page * D + c0 + e) * a.bs + slot] = (uint16_t)bits[e];
+                for (int e = 0; e < EPL; ++e) dst[v_elem(page, D, a.bs, c0 + e, slot)] = (uint16_t)bits[e];
             }
         } else {
             float x[EPL];
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void store_token_kernel(StoreArgs a) {
             } else {
 #pragma unroll
                 for (int e = 0; e < EPL; ++e)
-                    dst[(page * D + c0 + e) * a.bs + slot] = (int8_t)quant_code(x[e], s);
+                    dst[v_elem(page, D, a.bs, c0 + e, slot)] = (int8_t)quant_code(x[e], s);
             }
             if (lane == 0) (which ? a.vs : a.ks)[page * a.bs + slot] = s;
         }
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void store_block_kernel(StoreArgs a) {
             for (int e = threadIdx.x; e < n_old * D; e += blockDim.x) {
                 const int slot = e / D;
                 const int c = e % D;
-                const int64_t idx = which ? (page * D + c) * a.bs + slot : (page * a.bs + slot) * D + c;
+                const int64_t idx = which ? v_elem(page, D, a.bs, c, slot) : (page * a.bs + slot) * D + c;
                 const float old_value = (float)dst[idx] * s_old;
                 dst[idx] = (int8_t)quant_code(old_value, s);
             }
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256) void store_block_kernel(StoreArgs a) {
             const int c = e % D;
             const int slot = p - j * a.bs;
             const float x = bf16_to_f32(src[((int64_t)(t0 + p - prior) * a.hkv + h) * D + c]);
-            const int64_t idx = which ? (page * D + c) * a.bs + slot : (page * a.bs + slot) * D + c;
+            const int64_t idx = which ? v_elem(page, D, a.bs, c, slot) : (page * a.bs + slot) * D + c;
             dst[idx] = (int8_t)quant_code(x, s);
         }
         if (threadIdx.x == 0) sc[page] = s;

@@ -12,7 +12,7 @@ import torch
 import gen
 import oracle
 import paged_kv_cache_c8_amd as pkv
-from tests.helpers import attention_close
+from tests.helpers import attention_close, v_token_major
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
@@ -125,9 +125,8 @@ class Run:
             k, v = k.numpy(), v.numpy()
         # only slots that hold a position of some sequence are defined
         mask = self.defined_slots()
-        for name, got, want in (("K", k, self.hc.k), ("V", v, self.hc.v.transpose(0, 1, 3, 2))):
-            if name == "V":
-                got = got.transpose(0, 1, 3, 2)
+        bs = self.w.block_size
+        for name, got, want in (("K", k, self.hc.k), ("V", v_token_major(v, bs), v_token_major(self.hc.v, bs))):
             diff = (got != want)[mask]
             assert not diff.any(), f"{name} codes differ at {int(diff.sum())} elements"
         if self.w.quant_mode != 2:

@@ -72,3 +72,25 @@ def attention_close(gpu, ref64, atol=1e-2, rtol=1e-2):
     rel = float(np.linalg.norm(g - r) / denom) if denom > 0 else float(np.linalg.norm(g - r))
     elem_ok = bool(np.all(err <= atol + rtol * np.abs(r)))
     return max_abs, rel, elem_ok
+
+
+# ---- V page layout: [NB, Hkv, BS/T, D, T], tiles of T slots, each channel-major (T = 16 for
+#      every block size the GPU library takes; the CPU oracle also takes block sizes that are not
+#      multiples of 16, whose page is then one tile of T = BS slots)
+def vtile(bs: int) -> int:
+    return 16 if bs % 16 == 0 else bs
+
+
+def v_slot(v, blk, h, off, bs):
+    """The head_dim values of slot `off` of page (blk, h): a (writable) strided view."""
+    t = vtile(bs)
+    return v[blk, h, off // t, :, off % t]
+
+
+def v_token_major(v, bs):
+    """V pages rearranged to [NB, Hkv, BS, D] (numpy array or torch tensor, host)."""
+    t = vtile(bs)
+    nb, hkv = v.shape[0], v.shape[1]
+    x = v.reshape(nb, hkv, bs // t, -1, t)
+    x = x.transpose(0, 1, 2, 4, 3) if isinstance(x, np.ndarray) else x.permute(0, 1, 2, 4, 3)
+    return x.reshape(nb, hkv, bs, -1)

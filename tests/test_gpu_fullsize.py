@@ -8,7 +8,7 @@ import torch
 
 import gen
 from tests.gpu_harness import Run, oracle_run, sub_workload
-from tests.helpers import attention_close
+from tests.helpers import attention_close, v_token_major
 
 pytestmark = pytest.mark.gpu
 
@@ -32,10 +32,12 @@ def _check(idx, n_sample, kernel=0):
         blks = torch.as_tensor(w.block_table[b, :nblk].astype(np.int64), device=gk.device)
         n = int(w.context_lengths[b])
         host_blks = w.block_table[b, :nblk]
-        for name, g_arr, h_arr, tok_axis in (("K", gk, hc.k, 2), ("V", gv, hc.v, 3)):
+        for name, g_arr, h_arr, tok_axis in (("K", gk, hc.k, 2), ("V", gv, hc.v, 2)):
             g = g_arr.index_select(0, blks).cpu()
             g = (g.view(torch.int16).numpy().view(np.uint16) if w.quant_mode == 2 else g.numpy())
             h = h_arr[host_blks]
+            if name == "V":
+                g, h = v_token_major(g, w.block_size), v_token_major(h, w.block_size)
             # flatten the block/slot axes to positions and keep the defined ones
             g = np.moveaxis(g, tok_axis, 1).reshape(nblk * w.block_size, *np.moveaxis(g, tok_axis, 1).shape[2:])[:n]
             h = np.moveaxis(h, tok_axis, 1).reshape(nblk * w.block_size, *np.moveaxis(h, tok_axis, 1).shape[2:])[:n]

@@ -333,3 +333,29 @@ def test_planned_partition_matches_fixed_splits():
     bound = fixed.float().abs() * 2.0 ** -7 + 2.0 ** -10 * float(fixed.float().abs().max())
     assert bool((diff <= bound).all()), float((diff - bound).max())
     assert torch.allclose(lp, lf, rtol=1e-5, atol=1e-5)
+
+
+def test_workspace_reused_across_shapes_and_kernels():
+    """One workspace, filled with NaN bytes to start with, serves calls of different shapes,
+    kernels and partitions in turn: no call depends on what an earlier one left there."""
+    ws = torch.full((64 << 20,), 0xFF, dtype=torch.uint8, device="cuda")
+    cases = [
+        (_wl(0, 128, 16, 4, [3000, 1200, 4096, 64, 900], seed=21), dict(split_tokens=256)),
+        (_wl(0, 128, 16, 4, [5000, 10, 2600], hkv=4, seed=22), dict(partition=2)),
+        (_wl(1, 64, 32, 8, [700, 1500, 33], seed=23), dict(split_tokens=256, kernel=2)),
+        (_wl(1, 64, 32, 8, [700, 1500, 33], seed=23), dict(split_tokens=128)),
+        (_wl(0, 128, 16, 4, [3000, 1200, 4096, 64, 900], seed=21), dict(partition=2)),
+        (_wl(1, 128, 16, 5, [40, 700, 17, 1500], [16, 9, 16, 3], seed=24), dict(split_tokens=128)),
+    ]
+    runs = {}
+    for w, kw in cases:
+        key = (w.name, w.seed)
+        if key not in runs:
+            r = Run(w)
+            r.store_prior()
+            r.store_new()
+            runs[key] = r
+        r = runs[key]
+        for _ in range(2):
+            out, lse = r.decode(workspace=ws, **kw)
+            r.assert_decode_close(out, lse)

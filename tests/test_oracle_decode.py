@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from gen import custom_workload
-from tests.helpers import bits_to_f32, torch_bf16_to_bits
+from tests.helpers import bits_to_f32, torch_bf16_to_bits, v_slot
 
 
 def _build(w, seed=0, kv_scale=1.0):
@@ -57,9 +57,9 @@ def _gather_f64(c, w, b, is_v):
         blk, off = w.block_table[b, p // w.block_size], p % w.block_size
         for h in range(w.num_kv_heads):
             if c.mode == 2:
-                row = bits_to_f32(c.v[blk, h, :, off] if is_v else c.k[blk, h, off]).astype(np.float64)
+                row = bits_to_f32(v_slot(c.v, blk, h, off, c.bs) if is_v else c.k[blk, h, off]).astype(np.float64)
             else:
-                codes = (c.v[blk, h, :, off] if is_v else c.k[blk, h, off]).astype(np.float64)
+                codes = (v_slot(c.v, blk, h, off, c.bs) if is_v else c.k[blk, h, off]).astype(np.float64)
                 sc = c.v_scale if is_v else c.k_scale
                 s = float(sc[blk, h, off] if c.mode == 0 else sc[blk, h])
                 row = codes * s
@@ -208,7 +208,7 @@ def test_causal_queries_ignore_later_keys():
     c2 = c.copy()
     blk, off = w.block_table[0, 35 // 16], 35 % 16
     c2.k[blk, 0, off] = -c2.k[blk, 0, off] + 3
-    c2.v[blk, 0, :, off] = 100
+    v_slot(c2.v, blk, 0, off, c2.bs)[:] = 100
     _, pert, _ = _run(c2, w, q, 0.2)
     prior = 40 - 8
     for i in range(8):

@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 from gen import custom_workload
-from tests.helpers import all_finite_bf16_bits, bits_to_f32, nearest_bf16, torch_bf16_to_bits
+from tests.helpers import all_finite_bf16_bits, bits_to_f32, nearest_bf16, torch_bf16_to_bits, v_slot
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -65,7 +65,7 @@ def test_golden_dequant_products():
     for case in spec["cases"]:
         c = oracle.HostCache(0, 1, 1, 16, 1)
         c.k[0, 0, 0, 0] = case["code"]
-        c.v[0, 0, 0, 0] = case["code"]
+        v_slot(c.v, 0, 0, 0, 16)[0] = case["code"]
         c.k_scale[0, 0, 0] = case["scale"]
         c.v_scale[0, 0, 0] = case["scale"]
         k, v = oracle.dequant(c, np.array([[0]], np.int32), np.array([1], np.int32))
@@ -107,12 +107,12 @@ def test_dequant_matches_torch_fp32_product(mode):
             blk, off = w.block_table[b, p // 16], p % 16
             for h in range(2):
                 if mode == 2:
-                    wk, wv = c.k[blk, h, off], c.v[blk, h, :, off]
+                    wk, wv = c.k[blk, h, off], v_slot(c.v, blk, h, off, 16)
                 else:
                     sk = c.k_scale[blk, h, off] if mode == 0 else c.k_scale[blk, h]
                     sv = c.v_scale[blk, h, off] if mode == 0 else c.v_scale[blk, h]
                     tk = torch.from_numpy(c.k[blk, h, off].astype(np.float32)) * torch.tensor(sk)
-                    tv = torch.from_numpy(c.v[blk, h, :, off].astype(np.float32)) * torch.tensor(sv)
+                    tv = torch.from_numpy(v_slot(c.v, blk, h, off, 16).astype(np.float32)) * torch.tensor(sv)
                     wk = torch_bf16_to_bits(tk.to(torch.bfloat16))
                     wv = torch_bf16_to_bits(tv.to(torch.bfloat16))
                 assert np.array_equal(kd[row, h], wk)

@@ -18,7 +18,7 @@ import pytest
 
 import oracle
 from gen import custom_workload
-from tests.helpers import all_finite_bf16_bits, bits_to_f32, f32_to_bits, nearest_f32
+from tests.helpers import all_finite_bf16_bits, bits_to_f32, f32_to_bits, nearest_f32, v_token_major
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -32,7 +32,7 @@ def _store_rows(rows_f32, mode=0, bs=16):
     bits = f32_to_bits(rows).reshape(t, 1, d)
     oracle.store(cache, bits, bits, slot_mapping=np.arange(t, dtype=np.int64))
     k = cache.k.reshape(nb * bs, d)[:t].astype(np.int64)
-    v = cache.v.transpose(0, 1, 3, 2).reshape(nb * bs, d)[:t].astype(np.int64)
+    v = v_token_major(cache.v, bs).reshape(nb * bs, d)[:t].astype(np.int64)
     assert np.array_equal(k, v), "K and V of the same values must quantize identically"
     ks = cache.k_scale.reshape(-1)[:t]
     assert np.array_equal(ks.view(np.uint32), cache.v_scale.reshape(-1)[:t].view(np.uint32))
@@ -198,7 +198,7 @@ def test_golden_per_block_rescale():
         blk = bt[0, 0]
         assert c.k_scale[blk, 0] == np.float32(s["scale"])
         assert c.k[blk, 0, :n].tolist() == s["codes"]
-        assert c.v[blk, 0, :, :n].T.tolist() == s["codes"]
+        assert v_token_major(c.v, c.bs)[blk, 0, :n].tolist() == s["codes"]
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2, 3])
@@ -288,5 +288,5 @@ def test_inactive_decode_slot_stores_nothing():
         ok = (lambda s: s == slot) if mode != 1 else (lambda s: s <= slot)
         changed_k = np.argwhere(c.k != ref.k)
         assert len(changed_k) and all(b == blk and ok(s) for b, _, s, _ in changed_k)
-        changed_v = np.argwhere(c.v != ref.v)
-        assert len(changed_v) and all(b == blk and ok(s) for b, _, _, s in changed_v)
+        changed_v = np.argwhere(v_token_major(c.v, c.bs) != v_token_major(ref.v, ref.bs))
+        assert len(changed_v) and all(b == blk and ok(s) for b, _, s, _ in changed_v)
