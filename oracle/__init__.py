@@ -7,7 +7,7 @@ library or its Python binding, and nothing here imports them.
 All arrays are numpy arrays on the host.  bf16 data travels as ``uint16``
 bit patterns.  The cache arrays follow the layout the oracle documents:
 K ``[NB, Hkv, BS, D]``, V ``[NB, Hkv, BS/16, D, 16]`` (pages of channel-major 16-slot tiles), scales
-``[NB, Hkv, BS]`` (per token) or ``[NB, Hkv]`` (per block).
+``[NB, Hkv, BS]`` (per token), ``[NB, Hkv]`` (per block) or ``[Hkv, D]`` (static per channel).
 """
 from __future__ import annotations
 
@@ -90,6 +90,9 @@ class HostCache:
         elif mode == 1:
             self.k_scale = np.zeros((num_blocks, num_kv_heads), np.float32)
             self.v_scale = np.zeros((num_blocks, num_kv_heads), np.float32)
+        elif mode == 3:  # static per-channel scales: inputs, set by the caller
+            self.k_scale = np.zeros((num_kv_heads, head_dim), np.float32)
+            self.v_scale = np.zeros((num_kv_heads, head_dim), np.float32)
         else:
             self.k_scale = self.v_scale = None
 

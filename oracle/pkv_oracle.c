@@ -23,6 +23,12 @@
  *    float32 before dividing).
  *  - store, per-block mode: one fp32 scale per (block, KV head) ([P2] passes
  *    1 and 2 name a per-block scale layout for quant_mode != 0).
+ *  - store, per-channel mode: static fp32 scales, one per (KV head, channel),
+ *    given by the caller and broadcast over the tokens ([P2] pass 1 Notes: the
+ *    dequant forward handles the per-channel layout scale[..., None, :]; pass 2
+ *    Nits: the store's docstring names a per-channel quantization).  The store
+ *    only writes codes, q = clamp(round_half_even(fl32(x / s_c)), -128, 127),
+ *    which saturates where |x| exceeds the calibrated range.
  *  - dequant: fp32 product of the int8 code and its scale, then bf16 ([P2]
  *    pass 1 and 4 Must fix: the multiply must run in fp32); rows written at a
  *    per-sequence offset that defaults to the exclusive prefix sum of the
@@ -37,7 +43,8 @@
  *                                 channel-major: 16 consecutive slots of one channel adjacent;
  *                                 a block size that is not a multiple of 16 makes one tile of
  *                                 BS slots, [NB][Hkv][D][BS])
- *   scales mode 0: [NB][Hkv][BS] fp32;  mode 1: [NB][Hkv] fp32;  mode 2: none
+ *   scales mode 0: [NB][Hkv][BS] fp32;  mode 1: [NB][Hkv] fp32;  mode 2: none;
+ *          mode 3: [Hkv][D] fp32 (inputs, never written)
  */
 #include <math.h>
 #include <pthread.h>
@@ -48,6 +55,7 @@
 #define MODE_PER_TOKEN 0
 #define MODE_PER_BLOCK 1
 #define MODE_BF16 2
+#define MODE_PER_CHANNEL 3
 
 /* ------------------------------------------------------------------------- */
 /* bf16 <-> floating point                                                    */
@@ -126,6 +134,22 @@ static int64_t blk_scale_index(const cache_t *c, int64_t blk, int h)
     return blk * c->hkv + h;
 }
 
+static int64_t ch_scale_index(const cache_t *c, int h, int ch)
+{
+    return (int64_t)h * c->d + ch;
+}
+
+/* the scale of cache element (blk, h, slot, ch) in the int8 modes */
+static float scale_of(const cache_t *c, int is_v, int64_t blk, int h, int slot, int ch)
+{
+    const float *sc = is_v ? c->vs : c->ks;
+    if (c->mode == MODE_PER_TOKEN)
+        return sc[tok_scale_index(c, blk, h, slot)];
+    if (c->mode == MODE_PER_BLOCK)
+        return sc[blk_scale_index(c, blk, h)];
+    return sc[ch_scale_index(c, h, ch)];
+}
+
 /* ------------------------------------------------------------------------- */
 /* quantization primitives                                                    */
 /* ------------------------------------------------------------------------- */
@@ -153,14 +177,22 @@ static float absmax_scale(float absmax)
 /* store                                                                      */
 /* ------------------------------------------------------------------------- */
 
-/* Per-token (mode 0) and bf16 (mode 2) store of one token of one KV head
- * into (blk, slot). x points at D bf16 values. */
+/* Per-token (mode 0), bf16 (mode 2) and per-channel (mode 3) store of one
+ * token of one KV head into (blk, slot). x points at D bf16 values. */
 static void store_token(cache_t *c, int is_v, int64_t blk, int h, int slot, const uint16_t *x)
 {
     if (c->mode == MODE_BF16) {
         uint16_t *dst = (uint16_t *)(is_v ? c->v : c->k);
         for (int ch = 0; ch < c->d; ch++)
             dst[is_v ? v_index(c, blk, h, slot, ch) : k_index(c, blk, h, slot, ch)] = x[ch];
+        return;
+    }
+    if (c->mode == MODE_PER_CHANNEL) {
+        const float *sc = is_v ? c->vs : c->ks;
+        int8_t *dst = (int8_t *)(is_v ? c->v : c->k);
+        for (int ch = 0; ch < c->d; ch++)
+            dst[is_v ? v_index(c, blk, h, slot, ch) : k_index(c, blk, h, slot, ch)] =
+                quant_one(bf16_to_float(x[ch]), sc[ch_scale_index(c, h, ch)]);
         return;
     }
     float absmax = 0.0f;
@@ -241,7 +273,7 @@ int oracle_store(int mode, int nb, int hkv, int bs, int d, void *k_cache, void *
 {
     cache_t c = {mode, nb, hkv, bs, d, k_cache, v_cache, k_scale, v_scale};
     const int64_t row = (int64_t)hkv * d;
-    if (mode < 0 || mode > 2 || bs <= 0 || d <= 0 || hkv <= 0)
+    if (mode < 0 || mode > 3 || bs <= 0 || d <= 0 || hkv <= 0)
         return -1;
     if (slot_mapping) {
         if (mode == MODE_PER_BLOCK)
@@ -316,9 +348,7 @@ static float deq_f32(const cache_t *c, int is_v, int64_t blk, int h, int slot, i
     int64_t i = is_v ? v_index(c, blk, h, slot, ch) : k_index(c, blk, h, slot, ch);
     if (c->mode == MODE_BF16)
         return bf16_to_float(((const uint16_t *)(is_v ? c->v : c->k))[i]);
-    const float *sc = is_v ? c->vs : c->ks;
-    float s = c->mode == MODE_PER_TOKEN ? sc[tok_scale_index(c, blk, h, slot)]
-                                        : sc[blk_scale_index(c, blk, h)];
+    float s = scale_of(c, is_v, blk, h, slot, ch);
     return (float)((const int8_t *)(is_v ? c->v : c->k))[i] * s;
 }
 
@@ -328,9 +358,7 @@ static double deq_f64(const cache_t *c, int is_v, int64_t blk, int h, int slot, 
     int64_t i = is_v ? v_index(c, blk, h, slot, ch) : k_index(c, blk, h, slot, ch);
     if (c->mode == MODE_BF16)
         return (double)bf16_to_float(((const uint16_t *)(is_v ? c->v : c->k))[i]);
-    const float *sc = is_v ? c->vs : c->ks;
-    float s = c->mode == MODE_PER_TOKEN ? sc[tok_scale_index(c, blk, h, slot)]
-                                        : sc[blk_scale_index(c, blk, h)];
+    float s = scale_of(c, is_v, blk, h, slot, ch);
     return (double)((const int8_t *)(is_v ? c->v : c->k))[i] * (double)s;
 }
 

@@ -31,6 +31,10 @@ def _build(w, seed=0, kv_scale=1.0):
     q = torch_bf16_to_bits(torch.randn(w.num_new_tokens, w.num_q_heads, w.head_dim,
                                        generator=g).to(torch.bfloat16))
     c = oracle.HostCache(w.quant_mode, w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+    if w.quant_mode == 3:  # static per-channel scales (some values of K saturate)
+        rng = np.random.default_rng(seed + 77)
+        c.k_scale[...] = rng.uniform(0.01, 0.03, size=c.k_scale.shape).astype(np.float32) * kv_scale
+        c.v_scale[...] = rng.uniform(0.01, 0.03, size=c.v_scale.shape).astype(np.float32)
     cu_all = np.zeros(w.batch + 1, np.int32)
     cu_all[1:] = np.cumsum(w.context_lengths)
     if w.quant_mode == 1:
@@ -61,7 +65,10 @@ def _gather_f64(c, w, b, is_v):
             else:
                 codes = (v_slot(c.v, blk, h, off, c.bs) if is_v else c.k[blk, h, off]).astype(np.float64)
                 sc = c.v_scale if is_v else c.k_scale
-                s = float(sc[blk, h, off] if c.mode == 0 else sc[blk, h])
+                if c.mode == 3:
+                    s = sc[h].astype(np.float64)
+                else:
+                    s = float(sc[blk, h, off] if c.mode == 0 else sc[blk, h])
                 row = codes * s
             out[p, h] = row
     return out
@@ -80,6 +87,9 @@ def _run(c, w, q, scale, nthreads=1, cu=None):
     (2, 16, 128, 4, [50, 7, 33], None),
     (1, 16, 128, 5, [20, 40, 16], [3, 16, 1]),
     (0, 32, 64, 2, [70, 9], [5, 9]),
+    (3, 16, 128, 4, [37, 100, 5], None),
+    (3, 128, 64, 8, [300, 129], None),
+    (3, 16, 128, 5, [20, 40, 16], [3, 16, 1]),
 ])
 def test_matches_torch_sdpa_fp64(mode, bs, d, g, ctx, ql):
     import torch
@@ -224,3 +234,21 @@ def test_thread_count_does_not_change_bits():
     b = _run(c, w, q, 0.125, nthreads=5)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_per_channel_with_equal_scales_is_the_per_token_attention():
+    """Per-channel scales that are all equal to c give exactly the attention of the per-token mode
+    over the same codes with every token scale c (the fp64 values q * c are the same)."""
+    w3 = custom_workload("pc", batch=2, num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                         quant_mode=3, context_lengths=[45, 130], seed=5)
+    c3, q, _, _ = _build(w3, seed=9)
+    c3.k_scale[...] = np.float32(0.0234375)
+    c3.v_scale[...] = np.float32(0.015625)
+    w0 = custom_workload("pc", batch=2, num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                         quant_mode=0, context_lengths=[45, 130], seed=5)
+    c0 = oracle.HostCache(0, w0.num_blocks, 2, 16, 64)
+    c0.k[...], c0.v[...] = c3.k, c3.v
+    c0.k_scale[...] = np.float32(0.0234375)
+    c0.v_scale[...] = np.float32(0.015625)
+    for a, b in zip(_run(c3, w3, q, 0.125), _run(c0, w0, q, 0.125)):
+        assert np.array_equal(a, b)

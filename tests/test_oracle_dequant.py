@@ -90,7 +90,7 @@ def _random_cache(mode, w, seed):
     return c
 
 
-@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
 def test_dequant_matches_torch_fp32_product(mode):
     """Gather by hand with numpy indexing, multiply in fp32 and cast with torch."""
     import torch
@@ -109,10 +109,13 @@ def test_dequant_matches_torch_fp32_product(mode):
                 if mode == 2:
                     wk, wv = c.k[blk, h, off], v_slot(c.v, blk, h, off, 16)
                 else:
-                    sk = c.k_scale[blk, h, off] if mode == 0 else c.k_scale[blk, h]
-                    sv = c.v_scale[blk, h, off] if mode == 0 else c.v_scale[blk, h]
-                    tk = torch.from_numpy(c.k[blk, h, off].astype(np.float32)) * torch.tensor(sk)
-                    tv = torch.from_numpy(v_slot(c.v, blk, h, off, 16).astype(np.float32)) * torch.tensor(sv)
+                    if mode == 3:  # one scale per channel: a vector over the row
+                        sk, sv = torch.from_numpy(c.k_scale[h]), torch.from_numpy(c.v_scale[h])
+                    else:
+                        sk = torch.tensor(c.k_scale[blk, h, off] if mode == 0 else c.k_scale[blk, h])
+                        sv = torch.tensor(c.v_scale[blk, h, off] if mode == 0 else c.v_scale[blk, h])
+                    tk = torch.from_numpy(c.k[blk, h, off].astype(np.float32)) * sk
+                    tv = torch.from_numpy(v_slot(c.v, blk, h, off, 16).astype(np.float32)) * sv
                     wk = torch_bf16_to_bits(tk.to(torch.bfloat16))
                     wv = torch_bf16_to_bits(tv.to(torch.bfloat16))
                 assert np.array_equal(kd[row, h], wk)

@@ -290,3 +290,58 @@ def test_inactive_decode_slot_stores_nothing():
         assert len(changed_k) and all(b == blk and ok(s) for b, _, s, _ in changed_k)
         changed_v = np.argwhere(v_token_major(c.v, c.bs) != v_token_major(ref.v, ref.bs))
         assert len(changed_v) and all(b == blk and ok(s) for b, _, s, _ in changed_v)
+
+
+def test_per_channel_store_closed_forms():
+    """Static per-channel scales (mode 3): codes are clamp(RNE(x / s_c), -128, 127) with s_c the
+    channel's own scale, nothing else is written.  Scales are powers of two, so x / s_c is exact and
+    every expected code below is written out by hand."""
+    d = 8
+    # channel c has scale 2^(c - 4); the scale array must come back unchanged
+    s = np.array([2.0 ** (c - 4) for c in range(d)], np.float32)
+    # multiples of the scale (exact codes), ties (to even), saturation, zero
+    mult = np.array([0.0, 1.0, -1.0, 2.5, -2.5, 3.5, 127.5, -129.0], np.float32)
+    want = [0, 1, -1, 2, -2, 4, 127, -128]
+    mult2 = np.array([126.0, -127.0, 200.0, -200.0, 0.5, -0.5, 1.5, -128.0], np.float32)
+    want2 = [126, -127, 127, -128, 0, 0, 2, -128]
+    rows = np.stack([mult * s, mult2 * s]).astype(np.float32)  # [2 tokens, d]
+    bits = f32_to_bits(rows).reshape(2, 1, d)
+    assert np.array_equal(bits_to_f32(bits).reshape(2, d), rows)  # every value is exact in bf16
+    c = oracle.HostCache(3, 1, 1, 16, d)
+    c.k_scale[0] = s
+    c.v_scale[0] = s[::-1]
+    oracle.store(c, bits, bits, context_lengths=np.array([2], np.int32), block_table=np.array([[0]], np.int32),
+                 cu_q_lens=np.array([0, 2], np.int32))
+    assert c.k[0, 0, 0].tolist() == want and c.k[0, 0, 1].tolist() == want2
+    assert np.array_equal(c.k_scale[0], s) and np.array_equal(c.v_scale[0], s[::-1])
+    # V uses its own (reversed) scales: channel c of V divides by s[d - 1 - c]
+    vr = v_token_major(c.v, 16)[0, 0, :2].astype(np.int64)
+    exp_v = np.clip(np.rint(rows / s[::-1]), -128, 127).astype(np.int64)  # exact quotients, RNE
+    assert np.array_equal(vr, exp_v)
+    # a zero scale stores 0 whatever the value
+    c.k_scale[0, 3] = 0.0
+    c.k[...] = 9
+    oracle.store(c, bits, bits, context_lengths=np.array([2], np.int32), block_table=np.array([[0]], np.int32),
+                 cu_q_lens=np.array([0, 2], np.int32))
+    assert c.k[0, 0, 0, 3] == 0 and c.k[0, 0, 1, 3] == 0
+
+
+def test_per_channel_codes_depend_on_their_own_channel_scale_only():
+    import torch
+    from tests.helpers import torch_bf16_to_bits
+
+    rng = np.random.default_rng(3)
+    d = 32
+    x = torch_bf16_to_bits(torch.randn(4, 1, d, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16))
+    base = oracle.HostCache(3, 2, 1, 16, d)
+    base.k_scale[0] = rng.uniform(0.005, 0.05, d).astype(np.float32)
+    base.v_scale[0] = base.k_scale[0]
+    bt = np.array([[1]], np.int32)
+    args = dict(context_lengths=np.array([4], np.int32), block_table=bt, cu_q_lens=np.array([0, 4], np.int32))
+    c1 = base.copy()
+    oracle.store(c1, x, x, **args)
+    c2 = base.copy()
+    c2.k_scale[0, 7] *= 3
+    oracle.store(c2, x, x, **args)
+    diff = np.argwhere(c1.k != c2.k)
+    assert len(diff) and all(ch == 7 for _, _, _, ch in diff)
