@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1, help="workload index (0..4); 1 = Qwen3-8B decode")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--quant-mode", type=int, default=None,
+                    help="run the workload's shapes with another cache mode (3 = static per-channel scales)")
     ap.add_argument("--kernel", type=int, default=0, help="0 = library choice, 1 = VALU, 2 = MFMA fp16 scores, 3 = MFMA int8 scores")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-baseline sample")
@@ -79,6 +81,8 @@ def step_bytes(w):
     if w.quant_mode == 0:
         per_tok = hkv * (2 * d + 8)
         kv = int(ctx.sum()) * per_tok
+    elif w.quant_mode == 3:  # static per-channel scales: read once per KV head
+        kv = int(ctx.sum()) * hkv * 2 * d + hkv * d * 4 * 2
     elif w.quant_mode == 1:
         kv = int(ctx.sum()) * hkv * 2 * d + int(np.ceil(ctx / bs).sum()) * hkv * 8
     else:
@@ -92,6 +96,8 @@ def step_bytes(w):
         store = t * hkv * d * 2 * 2 * 2
     elif w.quant_mode == 0:
         store = t * hkv * d * 2 * 2 + t * hkv * (d + 4) * 2
+    elif w.quant_mode == 3:
+        store = t * hkv * d * 2 * 2 + t * hkv * d * 2 + hkv * d * 4 * 2
     else:  # per block: new tokens in and out, plus the touched old codes read and rewritten
         store = t * hkv * d * 2 * 2 + t * hkv * d * 2
     return decode, store
@@ -147,7 +153,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = gen.make_config(args.config)
+    w = gen.make_config(args.config, quant_mode=args.quant_mode)
     t = gen.gen_tensors(w, device=dev)
     k_prior, k_new = gen.split_prior_new(w, t["k_all"])
     v_prior, v_new = gen.split_prior_new(w, t["v_all"])
@@ -162,6 +168,9 @@ def main():
     caches = []
     for _ in range(reps):
         c = pkv.Cache(w.quant_mode, w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, device=dev)
+        if w.quant_mode == gen.QUANT_PER_CHANNEL:
+            c.k_scale.copy_(t["k_scale"])
+            c.v_scale.copy_(t["v_scale"])
         if int(w.prior_lengths.sum()):
             pkv.store_c8(c, k_prior, v_prior, cu_q_lens=cu_prior, context_lengths=prior, block_table=bt,
                          max_q_len=int(w.prior_lengths.max()))
@@ -225,14 +234,14 @@ def main():
     new_tokens = w.num_new_tokens if not w.decode_only else int((w.context_lengths > 0).sum())
     achieved = decode_bytes / (dec_ms * 1e-3) / 1e9
     # the counters were taken with the library's own choice of kernel and split
-    default_plan = args.kernel == 0 and args.split_tokens == 0
+    default_plan = args.kernel == 0 and args.split_tokens == 0 and args.quant_mode is None
     traffic = traffic_record(f"decode.config{args.config}") if default_plan else None
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, t, args.cpu_seconds, touched, new_tokens)
 
-    dtype = {0: "int8", 1: "int8", 2: "bf16"}[w.quant_mode]
+    dtype = {0: "int8", 1: "int8", 2: "bf16", 3: "int8"}[w.quant_mode]
     res = {
         "metric": "decode-attn HBM GB/s (% of peak) + tokens/s, int8 paged-KV GQA",
         "value": round(value, 2),
@@ -316,6 +325,9 @@ def cpu_baseline(w, t, budget_s, touched, new_tokens):
         cu_q = w.cu_q_lens
         qh = bits(t["q"].index_select(0, idx(np.concatenate([np.arange(cu_q[b], cu_q[b + 1]) for b in sel]))))
     hc = oracle.HostCache(w.quant_mode, w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+    if w.quant_mode == 3:
+        hc.k_scale[...] = t["k_scale"].cpu().numpy()
+        hc.v_scale[...] = t["v_scale"].cpu().numpy()
     cu_s = ws.cu_context
     prior = ws.prior_lengths
     pri = np.concatenate([np.arange(cu_s[b], cu_s[b] + prior[b]) for b in range(ws.batch)]).astype(np.int64)

@@ -1,7 +1,8 @@
 """Seeded synthetic inputs for the paged int8 KV-cache path.
 
 This module only draws random numbers and lays out shapes: sequence lengths,
-block tables and bf16 Q/K/V tensors.  It holds none of the method's arithmetic
+block tables, bf16 Q/K/V tensors and (for the per-channel cache mode) static
+per-channel scales, which that mode takes as inputs.  It holds none of the method's arithmetic
 (no quantization, no attention), so both the HIP path and the CPU oracle may
 take their inputs from it.
 
@@ -12,6 +13,7 @@ from it so that, e.g., changing the Q draw never changes the block table:
     stream 1  block-table permutation
     stream 2  Q        stream 3  K        stream 4  V
     stream 5  outlier K channels
+    stream 6  per-channel K scales    stream 7  per-channel V scales
 
 Integer draws use numpy's PCG64 (``numpy.random.default_rng``); the bf16
 tensors use torch's seeded generator on the requested device followed by a
@@ -29,6 +31,7 @@ import numpy as np
 QUANT_PER_TOKEN = 0
 QUANT_PER_BLOCK = 1
 QUANT_NONE_BF16 = 2
+QUANT_PER_CHANNEL = 3
 
 
 def _rng(seed: int, stream: int) -> np.random.Generator:
@@ -153,7 +156,7 @@ CONFIG_NAMES = [
 ]
 
 
-def make_config(index: int, seed: Optional[int] = None) -> Workload:
+def make_config(index: int, seed: Optional[int] = None, quant_mode: Optional[int] = None) -> Workload:
     """The five benchmark workloads, seeded with ``1000 + index`` by default.
 
     0  tiny:        B=2, 8/2 heads, D=64, BS=16, ctx {37, 100}, pool = permutation of 16 blocks
@@ -164,6 +167,9 @@ def make_config(index: int, seed: Optional[int] = None) -> Workload:
     4  chunked:     B=64, q_len ~ U[1, 16], prior ~ U[0, 16384], 40/8 heads, D=128, BS=16,
                     one fp32 scale per 16-token block
     """
+    if quant_mode is not None:  # the same shapes and lengths with another cache mode
+        w = make_config(index, seed)
+        return dataclasses.replace(w, quant_mode=int(quant_mode), name=f"{w.name}-mode{int(quant_mode)}")
     s = 1000 + index if seed is None else seed
     r = _rng(s, 0)
     if index == 0:
@@ -230,7 +236,25 @@ def gen_tensors(w: Workload, device="cpu"):
         kv_idx = torch.as_tensor(w.k_outlier_channels[:, 0], device=device)
         d_idx = torch.as_tensor(w.k_outlier_channels[:, 1], device=device)
         k[:, kv_idx, d_idx] = k[:, kv_idx, d_idx] * w.k_outlier_factor
-    return {"q": q, "k_all": k, "v_all": v}
+    out = {"q": q, "k_all": k, "v_all": v}
+    if w.quant_mode == QUANT_PER_CHANNEL:
+        out["k_scale"], out["v_scale"] = channel_scales(w, device)
+    return out
+
+
+def channel_scales(w: Workload, device="cpu"):
+    """Static per-channel scales [Hkv, D] (fp32) for the per-channel cache mode, as a calibration
+    would supply them: a seeded range of 3 to 4.5 standard deviations per channel over 127
+    (N(0, 1) data; values beyond the range saturate), times the outlier factor on K's outlier
+    channels."""
+    import torch
+
+    shape = (w.num_kv_heads, w.head_dim)
+    ks = _rng(w.seed, 6).uniform(3.0, 4.5, size=shape).astype(np.float32) / np.float32(127)
+    vs = _rng(w.seed, 7).uniform(3.0, 4.5, size=shape).astype(np.float32) / np.float32(127)
+    if w.k_outlier_channels is not None and len(w.k_outlier_channels):
+        ks[w.k_outlier_channels[:, 0], w.k_outlier_channels[:, 1]] *= np.float32(w.k_outlier_factor)
+    return torch.from_numpy(ks).to(device), torch.from_numpy(vs).to(device)
 
 
 def split_prior_new(w: Workload, t_all):

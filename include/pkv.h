@@ -39,6 +39,8 @@
  *   scales  PKV_QUANT_PER_TOKEN: float [num_blocks][num_kv_heads][block_size]
  *           PKV_QUANT_PER_BLOCK: float [num_blocks][num_kv_heads]
  *           PKV_QUANT_NONE_BF16: none (K and V hold bf16)
+ *           PKV_QUANT_PER_CHANNEL: float [num_kv_heads][head_dim], static (set by
+ *           the caller, e.g. from a calibration; the library never writes them)
  *   int8 codes for the quantized modes, bf16 for PKV_QUANT_NONE_BF16.
  *   K, V and the scale arrays: 16-byte aligned.
  *   Supported: head_dim 64 or 128; block_size 16, 32, 64 or 128.
@@ -70,7 +72,13 @@ typedef enum {
        for quant_mode != 0): absmax/127 of every value the block holds */
     PKV_QUANT_PER_BLOCK = 1,
     /* no quantization: K and V pages hold bf16 */
-    PKV_QUANT_NONE_BF16 = 2
+    PKV_QUANT_NONE_BF16 = 2,
+    /* static per-channel scales, one per (KV head, channel), broadcast over the
+       tokens (the scale[..., None, :] layout that PR #379's review passes name
+       for the C8 dequant): code = clamp(rne(fl32(x / s_c)), -128, 127), which
+       saturates values beyond the calibrated range; the store writes codes only.
+       Decoded by the int8-score kernel only (kernel 3). */
+    PKV_QUANT_PER_CHANNEL = 3
 } pkv_quant_mode;
 
 /* A caller-owned paged cache.  Shapes travel with the pointers. */
@@ -123,6 +131,9 @@ int pkv_version(void);
  *   the new tokens are quantized with s.  Precondition: no physical block is
  *   shared between sequences.
  * bf16 (mode 2): the values are copied.
+ * Per channel (mode 3): code = clamp(rne(fl32(x / s_c)), -128, 127) with the
+ *   static scale s_c of the value's (KV head, channel) (code 0 when s_c == 0);
+ *   the scale arrays are read, never written.
  *
  * num_tokens == 0 returns PKV_OK without launching anything.
  */

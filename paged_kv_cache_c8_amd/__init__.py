@@ -14,7 +14,8 @@ import os
 import torch  # loaded first: libpkv binds to the HIP runtime torch has already loaded
 
 __all__ = ["PkvError", "Cache", "lib", "store_c8", "dequant", "decode_gqa", "decode_workspace_size",
-           "decode_plan", "QUANT_PER_TOKEN", "QUANT_PER_BLOCK", "QUANT_NONE_BF16", "EXPORTS"]
+           "decode_plan", "QUANT_PER_TOKEN", "QUANT_PER_BLOCK", "QUANT_NONE_BF16", "QUANT_PER_CHANNEL",
+           "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
@@ -22,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 QUANT_PER_TOKEN = 0
 QUANT_PER_BLOCK = 1
 QUANT_NONE_BF16 = 2
+QUANT_PER_CHANNEL = 3
 
 # every symbol include/pkv.h declares
 EXPORTS = ("pkv_status_string", "pkv_version", "pkv_store_c8", "pkv_dequant",
@@ -106,8 +108,8 @@ def _opts(split_tokens=0, kernel=0, partition=0):
 
 class Cache:
     """A paged cache in device memory: K ``[NB, Hkv, BS, D]``, V ``[NB, Hkv, BS/16, D, 16]`` (pages
-    of channel-major 16-slot tiles; int8, or bf16 in mode 2), scales ``[NB, Hkv, BS]`` (mode 0) or
-    ``[NB, Hkv]`` (mode 1)."""
+    of channel-major 16-slot tiles; int8, or bf16 in mode 2), scales ``[NB, Hkv, BS]`` (mode 0),
+    ``[NB, Hkv]`` (mode 1) or ``[Hkv, D]`` (mode 3: static per-channel scales the caller sets)."""
 
     def __init__(self, quant_mode, num_blocks, num_kv_heads, block_size, head_dim, device="cuda",
                  k=None, v=None, k_scale=None, v_scale=None):
@@ -123,6 +125,8 @@ class Cache:
             sshape = (num_blocks, num_kv_heads, block_size)
         elif self.quant_mode == QUANT_PER_BLOCK:
             sshape = (num_blocks, num_kv_heads)
+        elif self.quant_mode == QUANT_PER_CHANNEL:
+            sshape = (num_kv_heads, head_dim)
         else:
             sshape = None
         if sshape is None:

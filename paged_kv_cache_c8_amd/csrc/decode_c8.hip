@@ -93,7 +93,7 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
                                            const int qrow0, const int prior, const int r0, const int nvalid,
                                            const int t_seg0, const int t_seg1, const int64_t pslot,
                                            int* const bt_s) {
-    static_assert(MODE == 0 || MODE == 1, "int8 cache modes only");
+    static_assert(MODE == 0 || MODE == 1 || MODE == 3, "int8 cache modes only");
     static_assert(J == 1 || RT == 1, "several row tiles only with one subset class");
     constexpr int KSTEP = D / 64;                     // 64-channel steps of the score MFMA
     constexpr int DT = D / 16;                        // 16-channel output tiles
@@ -104,6 +104,13 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
     const int g = lane >> 4;  // lane group
     const int jcol = n % J;   // subset class of the lane's column
 
+    // per-channel mode: the K scales of the lane's query channels (g*16*KSTEP ..)
+    f4 skq[MODE == 3 ? 4 * KSTEP : 1];
+    if constexpr (MODE == 3) {
+        const f4* sp = reinterpret_cast<const f4*>(a.ks + (int64_t)h * D + g * 16 * KSTEP);
+#pragma unroll
+        for (int i = 0; i < 4 * KSTEP; ++i) skq[i] = sp[i];
+    }
     // ---- query rows (B operand of the score MFMA): lane (n, g) holds the 16 * KSTEP channels
     //      g*16*KSTEP .. of its column's row, k-step m taking 16 of them.  The raw bf16 loads are
     //      issued first; they are quantized while the first key block is in flight.
@@ -190,6 +197,7 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
             }
         };
         auto load_s_at = [&](int T, int pid, C8Regs<D, J>& R) {
+            if constexpr (MODE == 3) return;  // per-channel scales: none per key
             const int sl = (T + 16 * g) & (a.bs - 1);
     #pragma unroll
             for (int u = 0; u < NSLOT; ++u) {  // scales of the lane's keys 16g + 8v + 4e + i, s = (v, e)
@@ -241,6 +249,10 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
                 for (int l = 0; l < 2 * KSTEP; ++l)
         #pragma unroll
                     for (int e = 0; e < 8; ++e) x[8 * l + e] = sgn * bf16_at(qraw[rt][l], e);
+                if constexpr (MODE == 3) {  // q . (code * s_K) = (q * s_K) . code: s_K joins the query
+        #pragma unroll
+                    for (int e = 0; e < 16 * KSTEP; ++e) x[e] *= skq[e / 4][e % 4];
+                }
                 float mx = 0.0f;
         #pragma unroll
                 for (int e = 0; e < 16 * KSTEP; ++e) mx = fmaxf(mx, fabsf(x[e]));
@@ -304,7 +316,7 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
     #pragma unroll
             for (int u = 0; u < NSLOT; ++u)
     #pragma unroll
-                for (int i = 0; i < 4; ++i) vsl[u][i] = MODE == 0 ? R.vs[u][i] : R.vs[u][0];
+                for (int i = 0; i < 4; ++i) vsl[u][i] = MODE == 0 ? R.vs[u][i] : (MODE == 1 ? R.vs[u][0] : 1.0f);
             float sf = 1.0f;
             bool s_moved = false;
             {
@@ -345,7 +357,7 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
                         if (jcol == c) S = sc[rt][J * u + c];
     #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        x[u][i] = (float)S[i] * (MODE == 0 ? R.ks[u][i] : R.ks[u][0]);
+                        x[u][i] = (float)S[i] * (MODE == 0 ? R.ks[u][i] : (MODE == 1 ? R.ks[u][0] : 1.0f));
                         if (MASKED) {
                             const int t = key_of(T, u, i);
                             if (!(t < t_end && t <= lim[rt])) x[u][i] = -INFINITY;
@@ -436,7 +448,14 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
     }
 
     // ---- merge the J columns of each row, normalise, write.  Lane (g, n) holds channels
-    //      16 dt + 4g + i of column n.
+    //      16 dt + 4g + i of column n.  Per-channel mode: sum_t w_t code_t,c * s_V,c is the
+    //      accumulator times the channel's V scale (loaded here, in flight during the merge).
+    f4 svc[MODE == 3 ? DT : 1];
+    if constexpr (MODE == 3) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            svc[dt] = *reinterpret_cast<const f4*>(a.vs + (int64_t)h * D + dt * 16 + 4 * g);
+    }
     const bool split_mode = pslot >= 0;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -456,6 +475,7 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float v = (acc[rt][dt][i] - bias) * cm;
+                if constexpr (MODE == 3) v *= svc[dt][i];
                 if constexpr (J >= 2) v += lane_xchg<1>(v);
                 if constexpr (J >= 4) v += lane_xchg<2>(v);
                 o[dt][i] = v;
@@ -785,6 +805,7 @@ template <int D>
 hipError_t launch_mode(const DecodeArgs& a, int batch, int j, int rt, int mode, hipStream_t stream) {
     if (mode == 0) return launch_shape<D, 0>(a, batch, j, rt, stream);
     if (mode == 1) return launch_shape<D, 1>(a, batch, j, rt, stream);
+    if (mode == 3) return launch_shape<D, 3>(a, batch, j, rt, stream);
     return hipErrorInvalidValue;
 }
 
@@ -801,8 +822,12 @@ int sk_shape(int j, int rt, int batch) {
 
 int decode_c8_waves_per_cu(int head_dim, int classes, int row_tiles, int mode, int batch) {
     if (batch > MAX_SK_SEQS) return 0;
-    if (head_dim == 64) return mode == 0 ? sk_shape<64, 0>(classes, row_tiles, batch) : sk_shape<64, 1>(classes, row_tiles, batch);
-    if (head_dim == 128) return mode == 0 ? sk_shape<128, 0>(classes, row_tiles, batch) : sk_shape<128, 1>(classes, row_tiles, batch);
+    if (head_dim == 64)
+        return mode == 0 ? sk_shape<64, 0>(classes, row_tiles, batch)
+                         : (mode == 1 ? sk_shape<64, 1>(classes, row_tiles, batch) : sk_shape<64, 3>(classes, row_tiles, batch));
+    if (head_dim == 128)
+        return mode == 0 ? sk_shape<128, 0>(classes, row_tiles, batch)
+                         : (mode == 1 ? sk_shape<128, 1>(classes, row_tiles, batch) : sk_shape<128, 3>(classes, row_tiles, batch));
     return 0;
 }
 

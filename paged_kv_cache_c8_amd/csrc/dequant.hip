@@ -2,7 +2,7 @@
 //
 // Implements MojoDequantFromPagedKVCache of Mojo Opset PR #379: every position p < ctx_b of
 // sequence b is written at row off_b + p, value bf16_rne(fl32(code * scale)) (the product in
-// fp32, as that PR's reviews require), off_b = caller offsets or the exclusive prefix sum of
+// fp32, as that PR's reviews require; the scale per token, per block, or per channel), off_b = caller offsets or the exclusive prefix sum of
 // the context lengths.  One workgroup per (sequence, logical block, KV head) page; the reviews'
 // per-sequence .item() and list-concatenation loop becomes a single launch with no host sync.
 //
@@ -74,7 +74,6 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
                     for (int k = 0; k < 8; ++k) y[k] = vp[v_elem(0, D, a.bs, c0 + k, slot)];
                 }
             } else {
-                const float s = MODE == 0 ? scales[page * a.bs + slot] : scales[page];
                 int8_t codes[8];
                 if (which == 0) {
                     const int8_t* src = reinterpret_cast<const int8_t*>(a.k) + (page * a.bs + slot) * D + c0;
@@ -89,8 +88,15 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
 #pragma unroll
                     for (int k = 0; k < 8; ++k) codes[k] = vp[v_elem(0, D, a.bs, c0 + k, slot)];
                 }
+                if constexpr (MODE == 3) {  // static per-channel scales [Hkv][D]
+                    const float* sc = scales + (int64_t)h * D + c0;
 #pragma unroll
-                for (int k = 0; k < 8; ++k) y[k] = f32_to_bf16_rne((float)codes[k] * s);
+                    for (int k = 0; k < 8; ++k) y[k] = f32_to_bf16_rne((float)codes[k] * sc[k]);
+                } else {
+                    const float s = MODE == 0 ? scales[page * a.bs + slot] : scales[page];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) y[k] = f32_to_bf16_rne((float)codes[k] * s);
+                }
             }
             uint16_t* dst = out + (row0 + slot) * a.token_stride + (int64_t)h * a.head_stride + c0;
             if (a.vec_ok) {
@@ -117,6 +123,8 @@ hipError_t launch_d(const DequantArgs& a, int mode, hipStream_t stream) {
         hipLaunchKernelGGL((dequant_kernel<D, 0>), dim3((unsigned)grid), dim3(256), 0, stream, a);
     else if (mode == 1)
         hipLaunchKernelGGL((dequant_kernel<D, 1>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+    else if (mode == 3)
+        hipLaunchKernelGGL((dequant_kernel<D, 3>), dim3((unsigned)grid), dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL((dequant_kernel<D, 2>), dim3((unsigned)grid), dim3(256), 0, stream, a);
     return hipGetLastError();

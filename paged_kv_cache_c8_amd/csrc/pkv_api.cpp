@@ -40,7 +40,7 @@ int check_cache(const pkv_cache_t* c) {
     if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return PKV_ERR_INVALID_ARG;
     if (c->head_dim != 64 && c->head_dim != 128) return PKV_ERR_UNSUPPORTED;
     if (!pow2(c->block_size) || c->block_size < 16 || c->block_size > 128) return PKV_ERR_UNSUPPORTED;
-    if (c->quant_mode < 0 || c->quant_mode > 2) return PKV_ERR_UNSUPPORTED;
+    if (c->quant_mode < 0 || c->quant_mode > 3) return PKV_ERR_UNSUPPORTED;
     if (c->quant_mode != PKV_QUANT_NONE_BF16 && (!c->k_scale || !c->v_scale)) return PKV_ERR_INVALID_ARG;
     if (!aligned(c->k, 16) || !aligned(c->v, 16)) return PKV_ERR_INVALID_ARG;
     if (c->k_scale && !aligned(c->k_scale, 16)) return PKV_ERR_INVALID_ARG;
@@ -75,7 +75,7 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
     if (batch < 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || mbs <= 0) return PKV_ERR_INVALID_ARG;
     if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
     if (!pow2(bs) || bs < 16 || bs > 128) return PKV_ERR_UNSUPPORTED;
-    if (mode < 0 || mode > 2) return PKV_ERR_UNSUPPORTED;
+    if (mode < 0 || mode > 3) return PKV_ERR_UNSUPPORTED;
     if (max_q_len < 1) max_q_len = 1;
     int kernel = mode == 2 ? 2 : 3;  // int8 pages: exact int8 scores; bf16 pages: bf16 scores
     if (opts) {
@@ -87,6 +87,7 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
         if (opts->kernel != 0) kernel = opts->kernel;
     }
     if (kernel == 3 && mode == 2) kernel = 2;  // the int8-score kernel needs int8 pages
+    if (mode == 3 && kernel != 3) return PKV_ERR_UNSUPPORTED;  // per-channel scales: int8-score kernel only
     const int g = hq / hkv;
     const int64_t rows = (int64_t)max_q_len * g;
     if (rows > (1 << 20)) return PKV_ERR_UNSUPPORTED;

@@ -88,6 +88,18 @@ __global__ __launch_bounds__(256) void store_token_kernel(StoreArgs a) {
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) dst[v_elem(page, D, a.bs, c0 + e, slot)] = (uint16_t)bits[e];
             }
+        } else if constexpr (MODE == 3) {  // static per-channel scales: codes only
+            const float* sc = (which ? a.vs : a.ks) + (int64_t)h * D + c0;
+            int8_t* dst = reinterpret_cast<int8_t*>(which ? a.v : a.k);
+            if (which == 0) {
+                int8_t* row = dst + (page * a.bs + slot) * D + c0;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) row[e] = (int8_t)quant_code(bf16_to_f32(bits[e]), sc[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e)
+                    dst[v_elem(page, D, a.bs, c0 + e, slot)] = (int8_t)quant_code(bf16_to_f32(bits[e]), sc[e]);
+            }
         } else {
             float x[EPL];
             float am = 0.0f;
@@ -196,6 +208,8 @@ hipError_t launch_store_d(const StoreArgs& a, int mode, hipStream_t stream) {
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     if (mode == 0)
         hipLaunchKernelGGL((store_token_kernel<D, 0>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+    else if (mode == 3)
+        hipLaunchKernelGGL((store_token_kernel<D, 3>), dim3((unsigned)grid), dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL((store_token_kernel<D, 2>), dim3((unsigned)grid), dim3(256), 0, stream, a);
     return hipGetLastError();
