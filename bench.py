@@ -234,8 +234,9 @@ def main():
     new_tokens = w.num_new_tokens if not w.decode_only else int((w.context_lengths > 0).sum())
     achieved = decode_bytes / (dec_ms * 1e-3) / 1e9
     # the counters were taken with the library's own choice of kernel and split
-    default_plan = args.kernel == 0 and args.split_tokens == 0 and args.quant_mode is None
-    traffic = traffic_record(f"decode.config{args.config}") if default_plan else None
+    default_plan = args.kernel == 0 and args.split_tokens == 0
+    mode_key = "" if args.quant_mode is None else f".mode{args.quant_mode}"
+    traffic = traffic_record(f"decode.config{args.config}{mode_key}") if default_plan else None
 
     cpu = None
     if not args.no_cpu_baseline:
