@@ -30,6 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_F16_TFLOPS = 2500.0  # dense fp16 / bf16 matrix-core peak of MI355X
 MALL_BYTES = 256 * 2 ** 20
 
 
@@ -38,7 +39,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1, help="workload index (0..4); 1 = Qwen3-8B decode")
+    ap.add_argument("--config", type=int, default=1,
+                    help="workload index (0..4; 5 = paged prefill, measured in TFLOP/s); 1 = Qwen3-8B decode")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--quant-mode", type=int, default=None,
                     help="run the workload's shapes with another cache mode (3 = static per-channel scales)")
@@ -243,6 +245,28 @@ def main():
         cpu = cpu_baseline(w, t, args.cpu_seconds, touched, new_tokens)
 
     dtype = {0: "int8", 1: "int8", 2: "bf16", 3: "int8"}[w.quant_mode]
+    roofline = {
+        "bound": "hbm",
+        "kernel": "pkv_decode_gqa (split-KV partial + log-sum-exp merge)",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_HBM_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / PEAK_HBM_GBS, 4),
+        "traffic": traffic,
+        "algorithmic_bytes_per_launch": decode_bytes,
+        "avg_launch_ms": round(dec_ms, 5),
+    }
+    if w.name.startswith("paged-prefill"):
+        # a prompt's attention is a dense contraction: 2 * 2 * D flops per visible (query head, key)
+        # pair (Q.K and P.V); the scores run as two int8 passes (hi, lo) and P.V in fp16, both at the
+        # 2.5 PFLOP/s of the dense fp16 / bf16 matrix cores
+        pairs = sum(int(w.q_lens[b]) * (2 * int(w.prior_lengths[b]) + int(w.q_lens[b]) + 1) // 2
+                    for b in range(w.batch))
+        flops = 4.0 * pairs * w.num_q_heads * w.head_dim
+        tflops = flops / (dec_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": roofline["kernel"], "achieved": round(tflops, 2),
+                    "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4),
+                    "traffic": traffic, "flops_per_launch": flops, "avg_launch_ms": round(dec_ms, 5)}
     res = {
         "metric": "decode-attn HBM GB/s (% of peak) + tokens/s, int8 paged-KV GQA",
         "value": round(value, 2),
@@ -270,17 +294,7 @@ def main():
         "kv_tokens_per_s": round(float(w.context_lengths.sum()) / step_s, 1),
         "bytes_per_step": touched,
         "wall_s_timed": round(wall, 4),
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "pkv_decode_gqa (split-KV partial + log-sum-exp merge)",
-            "achieved": round(achieved, 2),
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": decode_bytes,
-            "avg_launch_ms": round(dec_ms, 5),
-        },
+        "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -153,6 +153,7 @@ CONFIG_NAMES = [
     "long-context-decode",
     "bf16-large-batch-decode",
     "chunked-store-multitoken",
+    "paged-prefill",
 ]
 
 
@@ -166,6 +167,9 @@ def make_config(index: int, seed: Optional[int] = None, quant_mode: Optional[int
                     clipped to [64, 8192]
     4  chunked:     B=64, q_len ~ U[1, 16], prior ~ U[0, 16384], 40/8 heads, D=128, BS=16,
                     one fp32 scale per 16-token block
+    5  prefill:     B=4 prompts of 2048 tokens (store and causal attention of every token),
+                    32/8 heads, D=128, BS=16, per-token scales (a measurement workload for the
+                    paged-prefill row, not one of the five above)
     """
     if quant_mode is not None:  # the same shapes and lengths with another cache mode
         w = make_config(index, seed)
@@ -199,6 +203,11 @@ def make_config(index: int, seed: Optional[int] = None, quant_mode: Optional[int
                                block_size=16, quant_mode=QUANT_PER_BLOCK, context_lengths=prior + ql,
                                q_lens=ql, seed=s, max_blocks_per_seq=-(-(16384 + 16) // 16),
                                decode_only=False)
+    if index == 5:
+        ctx = np.full(4, 2048)
+        return custom_workload(CONFIG_NAMES[5], batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                               block_size=16, quant_mode=QUANT_PER_TOKEN, context_lengths=ctx, q_lens=ctx,
+                               seed=s, max_blocks_per_seq=2048 // 16, decode_only=False)
     raise ValueError(f"no config {index}")
 
 

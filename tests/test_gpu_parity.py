@@ -78,6 +78,31 @@ CHUNK_CASES = [
 ]
 
 
+PREFILL_CASES = [
+    # mode, D, BS, G, context lengths, q_lens: whole prompts (prior 0) and long chunks after a prior
+    (0, 128, 16, 4, [512, 300], [512, 300]),
+    (1, 128, 16, 5, [1200, 700], [400, 700]),
+    (3, 128, 128, 8, [1000, 129], [600, 129]),
+    (0, 64, 64, 2, [777, 1], [777, 1]),
+    (2, 128, 16, 4, [700, 250], [350, 250]),
+]
+
+
+@pytest.mark.parametrize("mode,d,bs,g,ctx,ql", PREFILL_CASES)
+def test_paged_prefill_matches_oracle(mode, d, bs, g, ctx, ql):
+    """Paged prefill: hundreds of causal queries per sequence through the same
+    kernels (many row groups per KV head), against the oracle; also with fixed splits."""
+    r = Run(_wl(mode, d, bs, g, ctx, ql, seed=sum(ctx) + mode))
+    r.store_prior()
+    r.store_new()
+    r.assert_cache_equal()
+    ref = r.oracle_decode(nthreads=16)
+    out, lse = r.decode()
+    r.assert_decode_close(out, lse, ref)
+    o2, l2 = r.decode(split_tokens=256)
+    r.assert_decode_close(o2, l2, ref)
+
+
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("mode,d,bs,g,ctx,ql", CHUNK_CASES)
 def test_chunked_store_and_causal_decode(mode, d, bs, g, ctx, ql, kernel):
