@@ -56,7 +56,7 @@ def lib():
                                      ctypes.c_int64, ctypes.c_int64]
         L.oracle_dequant.restype = I
         L.oracle_decode.argtypes = [I, I, I, I, I, P, P, P, P, P, I, P, I, P, P, I,
-                                    ctypes.c_double, P, P, P, I]
+                                    ctypes.c_double, P, P, P, I, I]
         L.oracle_decode.restype = I
         _lib = L
     return _lib
@@ -158,8 +158,9 @@ def dequant(cache: HostCache, block_table, context_lengths, *, seq_offsets=None,
 
 
 def decode(cache: HostCache, q, num_q_heads, block_table, context_lengths, scale, *,
-           cu_q_lens=None, nthreads=1, want_f64=True):
-    """fp64 attention. ``q``: bf16 bits ``uint16 [Tq, Hq, D]``.
+           cu_q_lens=None, nthreads=1, want_f64=True, window=0):
+    """fp64 attention. ``q``: bf16 bits ``uint16 [Tq, Hq, D]``; ``window`` > 0 limits each query to
+    its last ``window`` keys (itself included).
 
     Returns (out_bf16 uint16 [Tq, Hq, D], out_f64 or None, lse fp64 [Tq, Hq]).
     """
@@ -174,7 +175,7 @@ def decode(cache: HostCache, q, num_q_heads, block_table, context_lengths, scale
     lse = np.zeros((tq, num_q_heads), np.float64)
     rc = lib().oracle_decode(*cache.args(), _p(q), num_q_heads, _p(bt), bt.shape[1], _p(ctx),
                              _p(cu), len(ctx), float(scale), _p(out), _p(out64), _p(lse),
-                             int(nthreads))
+                             int(nthreads), int(window))
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
     return out, out64, lse

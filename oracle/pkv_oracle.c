@@ -413,6 +413,7 @@ typedef struct {
     const int32_t *cu_q_lens;
     int batch;
     double scale;
+    int window; /* > 0: a query sees only its last `window` keys (itself included) */
     uint16_t *out;
     double *out_f64;
     double *lse;
@@ -423,7 +424,10 @@ typedef struct {
 /*
  * One (sequence b, KV head h) item.  For each new query i < q_len_b of the
  * sequence and each of the G = Hq/Hkv query heads hq = h*G + g:
- *   keys t = 0 .. prior_b + i (causal; prior_b = ctx_b - q_len_b)
+ *   keys t = t0 .. prior_b + i (causal; prior_b = ctx_b - q_len_b), t0 = 0, or
+ *   with a sliding window of W keys t0 = max(0, prior_b + i - W + 1) (the
+ *   sliding-window paged decode of [P1]'s op list: each query attends to its
+ *   last W positions)
  *   l_t = scale * sum_ch Q[ch] * K^[t][ch]            (fp64)
  *   m = max_t l_t,  w_t = exp(l_t - m),  L = sum_t w_t
  *   out[ch] = (sum_t w_t * V^[t][ch]) / L,  lse = m + ln L
@@ -440,9 +444,10 @@ static void decode_item(decode_job *J, int b, int h, double *l)
     int prior = ctx - qlen;
     double *acc = (double *)malloc(sizeof(double) * (size_t)d);
     for (int i = 0; i < qlen; i++) {
-        int nkeys = prior + i + 1;
+        int nkeys = prior + i + 1; /* keys 0 .. prior + i */
         if (nkeys < 0)
             nkeys = 0;
+        int t0 = J->window > 0 && nkeys > J->window ? nkeys - J->window : 0;
         for (int g = 0; g < g_count; g++) {
             int hq = h * g_count + g;
             int64_t o = ((int64_t)(row0 + i) * J->hq + hq) * d;
@@ -460,7 +465,7 @@ static void decode_item(decode_job *J, int b, int h, double *l)
                 continue;
             }
             double m = -INFINITY;
-            for (int t = 0; t < nkeys; t++) {
+            for (int t = t0; t < nkeys; t++) {
                 int64_t blk = J->block_table[(int64_t)b * J->mbs + t / c->bs];
                 double dot = 0.0;
                 for (int ch = 0; ch < d; ch++)
@@ -470,7 +475,7 @@ static void decode_item(decode_job *J, int b, int h, double *l)
                     m = l[t];
             }
             double sum = 0.0;
-            for (int t = 0; t < nkeys; t++) {
+            for (int t = t0; t < nkeys; t++) {
                 int64_t blk = J->block_table[(int64_t)b * J->mbs + t / c->bs];
                 double w = exp(l[t] - m);
                 sum += w;
@@ -523,9 +528,10 @@ int oracle_decode(int mode, int nb, int hkv, int bs, int d, const void *k_cache,
                   const void *v_cache, const float *k_scale, const float *v_scale,
                   const uint16_t *q, int hq, const int32_t *block_table, int mbs,
                   const int32_t *context_lengths, const int32_t *cu_q_lens, int batch,
-                  double scale, uint16_t *out, double *out_f64, double *lse, int nthreads)
+                  double scale, uint16_t *out, double *out_f64, double *lse, int nthreads,
+                  int window)
 {
-    if (hkv <= 0 || hq % hkv != 0 || !out)
+    if (hkv <= 0 || hq % hkv != 0 || !out || window < 0)
         return -1;
     for (int b = 0; b < batch; b++) {
         if (context_lengths[b] > mbs * bs)
@@ -546,6 +552,7 @@ int oracle_decode(int mode, int nb, int hkv, int bs, int d, const void *k_cache,
     J.cu_q_lens = cu_q_lens;
     J.batch = batch;
     J.scale = scale;
+    J.window = window;
     J.out = out;
     J.out_f64 = out_f64;
     J.lse = lse;

@@ -74,10 +74,10 @@ def _gather_f64(c, w, b, is_v):
     return out
 
 
-def _run(c, w, q, scale, nthreads=1, cu=None):
+def _run(c, w, q, scale, nthreads=1, cu=None, window=0):
     return oracle.decode(c, q, w.num_q_heads, w.block_table, w.context_lengths, scale,
                          cu_q_lens=cu if cu is not None else (None if w.decode_only else w.cu_q_lens),
-                         nthreads=nthreads)
+                         nthreads=nthreads, window=window)
 
 
 @pytest.mark.parametrize("mode,bs,d,g,ctx,ql", [
@@ -251,4 +251,66 @@ def test_per_channel_with_equal_scales_is_the_per_token_attention():
     c0.k_scale[...] = np.float32(0.0234375)
     c0.v_scale[...] = np.float32(0.015625)
     for a, b in zip(_run(c3, w3, q, 0.125), _run(c0, w0, q, 0.125)):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("mode,bs,d,g,ctx,ql,window", [
+    (0, 16, 64, 4, [37, 100, 5], None, 24),
+    (1, 16, 128, 5, [20, 40, 16], [3, 16, 1], 7),
+    (3, 32, 64, 2, [70, 9], [5, 9], 33),
+    (2, 16, 64, 4, [50, 129], None, 64),
+])
+def test_sliding_window_matches_masked_torch_sdpa(mode, bs, d, g, ctx, ql, window):
+    """Sliding window: query at position p sees keys max(0, p - W + 1) .. p; torch's SDPA with that
+    boolean mask on the gathered fp64 values is the reference."""
+    import torch
+    import torch.nn.functional as F
+
+    hkv = 2
+    w = custom_workload("sw", batch=len(ctx), num_q_heads=hkv * g, num_kv_heads=hkv, head_dim=d,
+                        block_size=bs, quant_mode=mode, context_lengths=ctx, q_lens=ql, seed=mode + bs + 3)
+    c, q, _, _ = _build(w, seed=d + bs + 1)
+    scale = 1.0 / np.sqrt(d)
+    out, out64, lse = _run(c, w, q, scale, window=window)
+    qf = bits_to_f32(q).astype(np.float64)
+    cu = w.cu_q_lens
+    for b in range(w.batch):
+        kk = torch.from_numpy(_gather_f64(c, w, b, False)).permute(1, 0, 2)[None]
+        vv = torch.from_numpy(_gather_f64(c, w, b, True)).permute(1, 0, 2)[None]
+        n = int(w.context_lengths[b])
+        qlen = int(w.q_lens[b])
+        qq = torch.from_numpy(qf[cu[b]:cu[b] + qlen]).permute(1, 0, 2)[None]
+        pos = n - qlen + torch.arange(qlen)[:, None]
+        keys = torch.arange(n)[None, :]
+        mask = (keys <= pos) & (keys > pos - window)
+        ref = F.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask, scale=scale, enable_gqa=True)
+        got = out64[cu[b]:cu[b] + qlen]
+        assert np.allclose(got, ref[0].permute(1, 0, 2).numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_sliding_window_special_cases():
+    w = custom_workload("sw2", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=32, block_size=16,
+                        quant_mode=0, context_lengths=[45, 130, 1], seed=21)
+    c, q, _, _ = _build(w, seed=22)
+    base = _run(c, w, q, 0.2)
+    # a window at least as long as every context changes nothing, bit for bit
+    for a, b in zip(base, _run(c, w, q, 0.2, window=130)):
+        assert np.array_equal(a, b)
+    # a window of one key: the output is that key's value, the lse its logit
+    out, out64, lse = _run(c, w, q, 0.2, window=1)
+    qf = bits_to_f32(q).astype(np.float64)
+    for b in range(3):
+        p = int(w.context_lengths[b]) - 1
+        k_self = _gather_f64(c, w, b, False)[p]  # [Hkv, D]
+        v_self = _gather_f64(c, w, b, True)[p]
+        for hq in range(8):
+            assert np.array_equal(out64[b, hq], v_self[hq // 4])
+            assert np.isclose(lse[b, hq], 0.2 * float(qf[b, hq] @ k_self[hq // 4]), rtol=1e-13, atol=1e-13)
+    # keys before the window do not reach the output
+    c2 = c.copy()
+    blk = w.block_table[1, 0]
+    c2.k[blk] = 100
+    v_slot(c2.v, blk, 0, 0, 16)[:] = 100
+    v_slot(c2.v, blk, 1, 3, 16)[:] = -100
+    for a, b in zip(_run(c, w, q, 0.2, window=100), _run(c2, w, q, 0.2, window=100)):
         assert np.array_equal(a, b)
