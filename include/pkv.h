@@ -175,7 +175,11 @@ typedef struct {
                              groups, else fixed splits); 1 = fixed splits of
                              split_tokens keys; 2 = balanced partition whenever the
                              shapes allow it (at most 4096 sequences). */
-    int32_t reserved[5];  /* must be zero */
+    int32_t window;       /* > 0: sliding window, each query attends only to its
+                             last `window` positions (itself included; the
+                             MojoSlidingWindowAttention row of the README's Op
+                             List); 0: every earlier position */
+    int32_t reserved[4];  /* must be zero */
 } pkv_decode_opts_t;
 
 /* Bytes of workspace pkv_decode_gqa needs for these shapes (0 when it needs

@@ -45,7 +45,7 @@ class _CacheT(ctypes.Structure):
 
 class _DecodeOpts(ctypes.Structure):
     _fields_ = [("split_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32),
-                ("partition", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
+                ("partition", ctypes.c_int32), ("window", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4)]
 
 
 _lib = None
@@ -98,11 +98,12 @@ def _check(status, what):
 PARTITION_PLANNED, PARTITION_FIXED, PARTITION_BALANCED = 0, 1, 2
 
 
-def _opts(split_tokens=0, kernel=0, partition=0):
+def _opts(split_tokens=0, kernel=0, partition=0, window=0):
     o = _DecodeOpts()
     o.split_tokens = int(split_tokens)
     o.kernel = int(kernel)
     o.partition = int(partition)
+    o.window = int(window)
     return o
 
 
@@ -180,16 +181,16 @@ def dequant(cache: Cache, block_table, context_lengths, *, seq_offsets=None, k_o
 
 
 def decode_workspace_size(batch, num_q_heads, cache: Cache, max_blocks_per_seq, max_q_len=1,
-                          split_tokens=0, kernel=0, partition=0) -> int:
-    o = _opts(split_tokens, kernel, partition)
+                          split_tokens=0, kernel=0, partition=0, window=0) -> int:
+    o = _opts(split_tokens, kernel, partition, window)
     return int(lib().pkv_decode_workspace_size(batch, num_q_heads, cache.num_kv_heads, cache.head_dim,
                                                max_blocks_per_seq, cache.block_size, max_q_len,
                                                cache.quant_mode, ctypes.byref(o)))
 
 
 def decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
-                max_q_len=1, quant_mode=0, split_tokens=0, kernel=0, partition=0):
-    o = _opts(split_tokens, kernel, partition)
+                max_q_len=1, quant_mode=0, split_tokens=0, kernel=0, partition=0, window=0):
+    o = _opts(split_tokens, kernel, partition, window)
     a, b, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     st = lib().pkv_decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
                                max_q_len, quant_mode, ctypes.byref(o), ctypes.byref(a), ctypes.byref(b),
@@ -199,7 +200,8 @@ def decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, 
 
 
 def decode_gqa(q, cache: Cache, block_table, context_lengths, scale, *, cu_q_lens=None, max_q_len=1,
-               out=None, lse_out=None, workspace=None, split_tokens=0, kernel=0, partition=0, stream=None):
+               out=None, lse_out=None, workspace=None, split_tokens=0, kernel=0, partition=0, window=0,
+               stream=None):
     """Attention of the new queries ``q`` (bf16 ``[Tq, Hq, D]``) over the paged cache."""
     hq = int(q.shape[1])
     batch = int(context_lengths.shape[0])
@@ -208,7 +210,7 @@ def decode_gqa(q, cache: Cache, block_table, context_lengths, scale, *, cu_q_len
         max_q_len = 1
     if out is None:
         out = torch.empty_like(q)
-    o = _opts(split_tokens, kernel, partition)
+    o = _opts(split_tokens, kernel, partition, window)
     need = int(lib().pkv_decode_workspace_size(batch, hq, cache.num_kv_heads, cache.head_dim, mbs,
                                                cache.block_size, max_q_len, cache.quant_mode,
                                                ctypes.byref(o)))

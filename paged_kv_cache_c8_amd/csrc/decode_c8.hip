@@ -87,8 +87,8 @@ struct C8V {
 // The attention of one work item (sequence b, KV head h, row group starting at row r0) over its
 // keys [t_seg0, t_seg1) (t_seg0 a multiple of 64).  pslot < 0: the segment is the item's whole key
 // range and the result goes to out / lse; else it is a partial, written to rows pslot * prs + j of
-// the workspace for the merge.
-template <int D, int MODE, int J, int RT>
+// the workspace for the merge.  WIN: a sliding window (DecodeArgs::window) limits each row's keys.
+template <int D, int MODE, int J, int RT, bool WIN>
 __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, const int h, const int qlen,
                                            const int qrow0, const int prior, const int r0, const int nvalid,
                                            const int t_seg0, const int t_seg1, const int64_t pslot,
@@ -115,6 +115,7 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
     //      g*16*KSTEP .. of its column's row, k-step m taking 16 of them.  The raw bf16 loads are
     //      issued first; they are quantized while the first key block is in flight.
     int lim[RT];  // last key the row may see
+    int lo[RT];   // first key the row may see (sliding window)
     bool causal = false;
     u32x4 qraw[RT][2 * KSTEP];
 #pragma unroll
@@ -123,12 +124,15 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
         const bool rv = j < nvalid;
         const int r = r0 + j;
         lim[rt] = rv ? prior + r / a.g : 0x7fffffff;
+        lo[rt] = WIN && rv ? win_lo(a.window, lim[rt]) : 0;
         causal |= lim[rt] < t_seg1 - 1;
         const uint16_t* qp = a.q + ((int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g) * D + g * 16 * KSTEP;
 #pragma unroll
         for (int l = 0; l < 2 * KSTEP; ++l) qraw[rt][l] = rv ? load16(qp + 8 * l) : u32x4{0u, 0u, 0u, 0u};
     }
     causal = __any(causal);
+    // the largest window start over the group's rows (its last row's): blocks below it are masked
+    const int lo_hi = WIN ? win_lo(a.window, prior + (r0 + nvalid - 1) / a.g) : 0;
 
     const int32_t* btb = a.bt + (int64_t)b * a.mbs;
 
@@ -284,8 +288,9 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
         }
 
         auto block = [&](const int T, const C8V<D>& VC, C8V<D>& VN) {
-            // masked: the block runs past the split's keys or past some row's causal limit
-            const bool MASKED = causal || T + BLK > t_end;
+            // masked: the block runs past the split's keys, past some row's causal limit or below
+            // some row's window start
+            const bool MASKED = causal || T + BLK > t_end || (WIN && T < lo_hi);
             load_v(T + BLK, VN);  // past the split's end: in-bounds stand-ins, never weighted
             // keep the next block's loads ahead of this block's waits (the scheduler would otherwise
             // sink them below the first score MFMA, whose wait then drains every load in flight)
@@ -360,7 +365,7 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
                         x[u][i] = (float)S[i] * (MODE == 0 ? R.ks[u][i] : (MODE == 1 ? R.ks[u][0] : 1.0f));
                         if (MASKED) {
                             const int t = key_of(T, u, i);
-                            if (!(t < t_end && t <= lim[rt])) x[u][i] = -INFINITY;
+                            if (!(t < t_end && t <= lim[rt] && (!WIN || t >= lo[rt]))) x[u][i] = -INFINITY;
                         }
                         bmax = fmaxf(bmax, x[u][i]);
                     }
@@ -512,9 +517,9 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
 
 // Rows, keys and output position of work item `item` = (sequence b, KV head h, row group rg).
 struct ItemGeo {
-    int b, h, qlen, qrow0, prior, r0, nrows, nvalid, kmax;
+    int b, h, qlen, qrow0, prior, r0, nrows, nvalid, kmax, kmin;  // keys [kmin, kmax) (kmin 128-aligned)
 };
-template <int ROWS>
+template <int ROWS, bool WIN = false>
 __device__ __forceinline__ ItemGeo item_geo(const DecodeArgs& a, int item) {
     ItemGeo it;
     const int rg = item % a.nrg;
@@ -528,6 +533,7 @@ __device__ __forceinline__ ItemGeo item_geo(const DecodeArgs& a, int item) {
     it.r0 = rg * ROWS;
     it.nvalid = min(ROWS, it.nrows - it.r0);
     it.kmax = it.nvalid > 0 ? it.prior + (it.r0 + it.nvalid - 1) / a.g + 1 : 0;  // keys the last row sees
+    it.kmin = WIN && it.nvalid > 0 ? win_begin(a.window, it.prior + it.r0 / a.g) : 0;  // first key of the range
     return it;
 }
 
@@ -546,7 +552,7 @@ __device__ __forceinline__ void zero_rows(const DecodeArgs& a, const ItemGeo& it
 // Fixed partition: one wave per (item, split of split_len keys).  Items go fastest, so
 // consecutive workgroups go round-robin over the XCDs and each XCD gets an even share of the
 // items whatever the number of empty splits.
-template <int D, int MODE, int J, int RT>
+template <int D, int MODE, int J, int RT, bool WIN>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 1))) void decode_c8_kernel(DecodeArgs a, int total) {
     constexpr int ROWS = J > 1 ? 16 / J : 16 * RT;
     __shared__ int bt_s[MAX_SPLIT_PAGES];
@@ -555,16 +561,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 
     const int items = total / a.nsplit;
     const int s = wi / items;
     const int item = wi % items;
-    const ItemGeo it = item_geo<ROWS>(a, item);
+    const ItemGeo it = item_geo<ROWS, WIN>(a, item);
     if (it.nvalid <= 0) return;
     if (it.kmax <= 0) {
         if (s == 0) zero_rows<D>(a, it, threadIdx.x);
         return;
     }
-    const int t_begin = s * a.split_len;
+    const int t_begin = it.kmin + s * a.split_len;
     if (t_begin >= it.kmax) return;
     const int t_end = min(t_begin + a.split_len, it.kmax);
-    c8_segment<D, MODE, J, RT>(a, it.b, it.h, it.qlen, it.qrow0, it.prior, it.r0, it.nvalid, t_begin, t_end,
+    c8_segment<D, MODE, J, RT, WIN>(a, it.b, it.h, it.qlen, it.qrow0, it.prior, it.r0, it.nvalid, t_begin, t_end,
                                a.nsplit > 1 ? (int64_t)item * a.nsplit + s : -1, bt_s);
 }
 
@@ -577,7 +583,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 
 // one-segment item writes its result, others leave a partial in slot K_i + s, and segment 0
 // records K_i and k_i in seg[2i], seg[2i + 1] for the merge.  The plan is computed by every wave
 // from the sequence lengths, per sequence (its KV heads share the counts).
-template <int D, int MODE, int J, int RT>
+template <int D, int MODE, int J, int RT, bool WIN>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 1))) void decode_c8_sk_kernel(DecodeArgs a, int batch) {
     constexpr int ROWS = J > 1 ? 16 / J : 16 * RT;
     __shared__ int bt_s[MAX_SPLIT_PAGES];
@@ -592,7 +598,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 
         if (r0 >= nrows) return 0;
         const int nvalid = min(ROWS, nrows - r0);
         const int kmax = a.ctx[b] - qlen + (r0 + nvalid - 1) / a.g + 1;
-        return kmax > 0 ? (kmax + BLK - 1) / BLK : 0;
+        const int kmin = WIN ? win_begin(a.window, a.ctx[b] - qlen + r0 / a.g) : 0;
+        return kmax > 0 ? (kmax - kmin + BLK - 1) / BLK : 0;
     };
     // N = total blocks over every item, A = items with at least one block
     int64_t N = 0;
@@ -663,15 +670,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 
     }
     const int seg = rem;
     const int item = (b * a.hkv + h) * a.nrg + rg;
-    const ItemGeo it = item_geo<ROWS>(a, item);
-    const int nb = (it.kmax + BLK - 1) / BLK;
+    const ItemGeo it = item_geo<ROWS, WIN>(a, item);
+    const int nb = (it.kmax - it.kmin + BLK - 1) / BLK;
     const int b0 = (int)((int64_t)nb * seg / k), b1 = (int)((int64_t)nb * (seg + 1) / k);
     if (seg == 0 && lane == 0) {
         a.seg[2 * item] = first;
         a.seg[2 * item + 1] = k;
     }
-    c8_segment<D, MODE, J, RT>(a, it.b, it.h, it.qlen, it.qrow0, it.prior, it.r0, it.nvalid, b0 * BLK,
-                               min(b1 * BLK, it.kmax), k == 1 ? -1 : (int64_t)wid, bt_s);
+    c8_segment<D, MODE, J, RT, WIN>(a, it.b, it.h, it.qlen, it.qrow0, it.prior, it.r0, it.nvalid, it.kmin + b0 * BLK,
+                               min(it.kmin + b1 * BLK, it.kmax), k == 1 ? -1 : (int64_t)wid, bt_s);
 }
 
 // Merge of the balanced partition: item i's partials sit in slots seg[2i] .. seg[2i] + seg[2i+1] - 1;
@@ -757,15 +764,15 @@ __global__ __launch_bounds__(1024) void merge_sk_kernel(DecodeArgs a) {
     if (cg == 0 && a.lse) a.lse[orow] = wsum > 0.0f ? (M + log2f(wsum)) * kLn2 : -INFINITY;
 }
 
-template <int D, int MODE, int J, int RT>
-hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream) {
+template <int D, int MODE, int J, int RT, bool WIN>
+hipError_t launch_one_w(const DecodeArgs& a, int batch, hipStream_t stream) {
     constexpr int ROWS = J > 1 ? 16 / J : 16 * RT;
     const int64_t items = (int64_t)batch * a.hkv * a.nrg;
     if (items == 0) return hipSuccess;
     if (a.sk_waves > 0) {  // balanced partition
         if (batch > MAX_SK_SEQS) return hipErrorInvalidValue;
         const size_t lds = (size_t)(batch + 1) * sizeof(int);
-        hipLaunchKernelGGL((decode_c8_sk_kernel<D, MODE, J, RT>), dim3((unsigned)(a.sk_waves + items)), dim3(64),
+        hipLaunchKernelGGL((decode_c8_sk_kernel<D, MODE, J, RT, WIN>), dim3((unsigned)(a.sk_waves + items)), dim3(64),
                            lds, stream, a, batch);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -775,20 +782,26 @@ hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream) {
     }
     const int64_t grid = items * a.nsplit;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_c8_kernel<D, MODE, J, RT>), dim3((unsigned)grid), dim3(64), 0, stream, a, (int)grid);
+    hipLaunchKernelGGL((decode_c8_kernel<D, MODE, J, RT, WIN>), dim3((unsigned)grid), dim3(64), 0, stream, a, (int)grid);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     return launch_merge(a, batch, D, ROWS, stream);
 }
 
 template <int D, int MODE, int J, int RT>
-int sk_waves_one(int batch) {
+hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream) {
+    return a.window > 0 ? launch_one_w<D, MODE, J, RT, true>(a, batch, stream)
+                        : launch_one_w<D, MODE, J, RT, false>(a, batch, stream);
+}
+
+template <int D, int MODE, int J, int RT>
+int sk_waves_one(int batch, bool windowed) {
     int per_cu = 0;
     const size_t lds = (size_t)(batch + 1) * sizeof(int);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_c8_sk_kernel<D, MODE, J, RT>, 64, lds) !=
-            hipSuccess ||
-        per_cu <= 0)
-        return 0;
+    const hipError_t e = windowed
+        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_c8_sk_kernel<D, MODE, J, RT, true>, 64, lds)
+        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_c8_sk_kernel<D, MODE, J, RT, false>, 64, lds);
+    if (e != hipSuccess || per_cu <= 0) return 0;
     return per_cu;
 }
 
@@ -810,24 +823,26 @@ hipError_t launch_mode(const DecodeArgs& a, int batch, int j, int rt, int mode, 
 }
 
 template <int D, int MODE>
-int sk_shape(int j, int rt, int batch) {
-    if (j == 4 && rt == 1) return sk_waves_one<D, MODE, 4, 1>(batch);
-    if (j == 2 && rt == 1) return sk_waves_one<D, MODE, 2, 1>(batch);
-    if (j == 1 && rt == 1) return sk_waves_one<D, MODE, 1, 1>(batch);
-    if (j == 1 && rt == 2) return sk_waves_one<D, MODE, 1, 2>(batch);
+int sk_shape(int j, int rt, int batch, bool w) {
+    if (j == 4 && rt == 1) return sk_waves_one<D, MODE, 4, 1>(batch, w);
+    if (j == 2 && rt == 1) return sk_waves_one<D, MODE, 2, 1>(batch, w);
+    if (j == 1 && rt == 1) return sk_waves_one<D, MODE, 1, 1>(batch, w);
+    if (j == 1 && rt == 2) return sk_waves_one<D, MODE, 1, 2>(batch, w);
     return 0;
 }
 
 }  // namespace
 
-int decode_c8_waves_per_cu(int head_dim, int classes, int row_tiles, int mode, int batch) {
+int decode_c8_waves_per_cu(int head_dim, int classes, int row_tiles, int mode, int batch, bool windowed) {
     if (batch > MAX_SK_SEQS) return 0;
+    const int c = classes, r = row_tiles;
+    const bool w = windowed;
     if (head_dim == 64)
-        return mode == 0 ? sk_shape<64, 0>(classes, row_tiles, batch)
-                         : (mode == 1 ? sk_shape<64, 1>(classes, row_tiles, batch) : sk_shape<64, 3>(classes, row_tiles, batch));
+        return mode == 0 ? sk_shape<64, 0>(c, r, batch, w)
+                         : (mode == 1 ? sk_shape<64, 1>(c, r, batch, w) : sk_shape<64, 3>(c, r, batch, w));
     if (head_dim == 128)
-        return mode == 0 ? sk_shape<128, 0>(classes, row_tiles, batch)
-                         : (mode == 1 ? sk_shape<128, 1>(classes, row_tiles, batch) : sk_shape<128, 3>(classes, row_tiles, batch));
+        return mode == 0 ? sk_shape<128, 0>(c, r, batch, w)
+                         : (mode == 1 ? sk_shape<128, 1>(c, r, batch, w) : sk_shape<128, 3>(c, r, batch, w));
     return 0;
 }
 

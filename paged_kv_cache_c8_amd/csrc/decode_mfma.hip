@@ -115,7 +115,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     if (r0 >= nrows) return;
     const int nvalid = min(16 * RT, nrows - r0);
     const int kmax = prior + (r0 + nvalid - 1) / a.g + 1;
-    const int t_begin = s * a.split_len;
+    const int t_begin = win_begin(a.window, prior + r0 / a.g) + s * a.split_len;  // (sliding window)
 
     if (kmax <= 0) {  // inactive sequence: zero output, lse = -inf
         if (s == 0) {
@@ -131,6 +131,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     }
     if (t_begin >= kmax) return;
     const int t_end = min(t_begin + a.split_len, kmax);
+    const int lo_hi = win_lo(a.window, prior + (r0 + nvalid - 1) / a.g);
 
     // ---- query tiles (B operand of the score MFMA): lane (n, g) holds row n's channels
     //      g*8*KS .. +8*KS, k-step m taking the 8 channels g*8*KS + 8m .. +8.
@@ -139,6 +140,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     uint32_t qb[RT][C::KS][4];
     float rowmul[RT], qbias[RT];
     int lim[RT];
+    int lo[RT];           // first key the row may see (sliding window)
     bool causal = false;  // some row of the group cannot see every key of the split
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -146,6 +148,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         const bool rv = j < nvalid;
         const int r = r0 + j;
         lim[rt] = rv ? prior + r / a.g : 0x7fffffff;
+        lo[rt] = rv ? win_lo(a.window, lim[rt]) : 0;
         causal |= lim[rt] < t_end - 1;
         uint32_t raw[C::KS][4];
         if (rv) {
@@ -277,8 +280,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
 
     // One 32-key block on registers R (loaded one block earlier).
     auto process = [&](int T, const BlockRegs<D, MODE>& R) {
-        // masked: the block runs past the split's keys or past a row's causal limit
-        const bool MASKED = causal || T + BLK > t_end;
+        // masked: the block runs past the split's keys, past a row's causal limit or below a row's
+        // window start (the group's last row has the largest)
+        const bool MASKED = causal || T + BLK > t_end || T < lo_hi;
         // -------------------------------------------- scores: two 16-key tiles per row tile
         f4 sc[RT][2];
 #pragma unroll
@@ -341,7 +345,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
                 sv[e] = raw * (R.ks[e] * rowmul[rt]);
                 if (MASKED) {
                     const int t = T + 8 * g + e;
-                    if (!(t < t_end && t <= lim[rt])) sv[e] = -INFINITY;
+                    if (!(t < t_end && t <= lim[rt] && t >= lo[rt])) sv[e] = -INFINITY;
                 }
                 bmax = fmaxf(bmax, sv[e]);
             }

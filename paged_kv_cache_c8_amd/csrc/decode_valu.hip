@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     if (r0 >= nrows) return;
     const int nvalid = min(RG, nrows - r0);
     const int kmax = prior + (r0 + nvalid - 1) / a.g + 1;  // keys the group's last row needs
-    const int t_begin = s * a.split_len;
+    const int t_begin = win_begin(a.window, prior + r0 / a.g) + s * a.split_len;  // (sliding window)
 
     if (kmax <= 0) {  // no keys at all (inactive sequence): zero output, lse = -inf
         if (s == 0) {
@@ -169,7 +169,6 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     }
     if (t_begin >= kmax) return;
     const int t_end = min(t_begin + a.split_len, kmax);
-    const int nact = min(a.nsplit, (kmax + a.split_len - 1) / a.split_len);
 
     // ---- block-table slice of this split
     const int blk0 = t_begin >> a.log2bs;
@@ -335,7 +334,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
                 for (int k = 0; k < C::HELD; ++k) {
                     const int j = c * C::HELD + k;
                     const int lim = prior + (r0 + j) / a.g;
-                    const float v = (valid && j < nvalid && t <= lim) ? part[k] * ks * held_mul[k] : -INFINITY;
+                    const bool seen = t <= lim && t >= win_lo(a.window, lim);
+                    const float v = (valid && j < nvalid && seen) ? part[k] * ks * held_mul[k] : -INFINITY;
                     sc[sc_index(tl, j, RG, C::TPU, C::SCW)] = v;
                 }
             } else {
@@ -343,7 +343,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
                 if (c % DUP == 0) {
                     const int j = c / DUP;
                     const int lim = prior + (r0 + j) / a.g;
-                    const float v = (valid && j < nvalid && t <= lim) ? part[0] * ks * held_mul[0] : -INFINITY;
+                    const bool seen = t <= lim && t >= win_lo(a.window, lim);
+                    const float v = (valid && j < nvalid && seen) ? part[0] * ks * held_mul[0] : -INFINITY;
                     sc[sc_index(tl, j, RG, C::TPU, C::SCW)] = v;
                 }
             }

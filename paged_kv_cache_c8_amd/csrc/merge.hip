@@ -41,7 +41,8 @@ __global__ __launch_bounds__(1024) void merge_kernel(DecodeArgs a, int rows_per_
     const int kmax = prior + (r0 + nvalid - 1) / a.g + 1;  // the split count the partials used
     if (kmax <= 0) return;                                  // written by the partial kernel
     if (jr >= nvalid) return;
-    const int nact = min(a.nsplit, (kmax + a.split_len - 1) / a.split_len);
+    const int kmin = win_begin(a.window, prior + r0 / a.g);  // splits start here (sliding window)
+    const int nact = min(a.nsplit, (kmax - kmin + a.split_len - 1) / a.split_len);
     const int64_t base = (int64_t)item * a.nsplit * a.prs + jr;  // row jr of split 0
 
     float M = -INFINITY, wsum = 0.0f;

@@ -79,8 +79,9 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
     if (max_q_len < 1) max_q_len = 1;
     int kernel = mode == 2 ? 2 : 3;  // int8 pages: exact int8 scores; bf16 pages: bf16 scores
     if (opts) {
-        for (int i = 0; i < 5; ++i)
+        for (int i = 0; i < 4; ++i)
             if (opts->reserved[i] != 0) return PKV_ERR_INVALID_ARG;
+        if (opts->window < 0) return PKV_ERR_INVALID_ARG;
         if (opts->partition < 0 || opts->partition > 2) return PKV_ERR_INVALID_ARG;
         if (opts->split_tokens < 0) return PKV_ERR_INVALID_ARG;
         if (opts->kernel < 0 || opts->kernel > 3) return PKV_ERR_INVALID_ARG;
@@ -126,7 +127,12 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
         p->rows_per_item = 16 * p->rg;
         p->prs = (int)(rows < p->rows_per_item ? rows : p->rows_per_item);
     }
-    const int64_t max_ctx = (int64_t)mbs * bs;
+    // keys one row group can need: the whole table, or with a sliding window of W keys at most
+    // W + (max_q_len - 1) (its rows' positions differ by less than max_q_len) + 127 (the range
+    // starts 128-aligned)
+    int64_t max_ctx = (int64_t)mbs * bs;
+    const int window = opts ? opts->window : 0;
+    if (window > 0 && (int64_t)window + max_q_len - 1 + 127 < max_ctx) max_ctx = (int64_t)window + max_q_len - 1 + 127;
     const int64_t items = (int64_t)batch * hkv * p->nrg;
     p->sk_waves = 0;
     const int partition = opts ? opts->partition : 0;
@@ -136,7 +142,7 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
         // ranges as the GPU holds waves of the kernel at once (no partly filled rounds of waves).
         // It pays one more memory round trip per wave (the plan), which only long contexts
         // amortise, and needs the items to be few against the waves.
-        const int per_cu = pkv::decode_c8_waves_per_cu(head_dim, p->classes, p->rg, mode, batch);
+        const int per_cu = pkv::decode_c8_waves_per_cu(head_dim, p->classes, p->rg, mode, batch, window > 0);
         if (per_cu > 0 && (partition == 2 || items * 2 <= (int64_t)per_cu * device_cus())) {
             p->sk_waves = per_cu * device_cus();
             p->split_len = 0;
@@ -325,6 +331,7 @@ int pkv_decode_gqa(const void* q, int32_t num_q_heads, const pkv_cache_t* cache,
     a.nsplit = p.nsplit;
     a.split_len = p.split_len;
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.window = opts ? opts->window : 0;
     const int64_t items = (int64_t)batch * a.hkv * p.nrg;
     if (p.sk_waves > 0) {
         float* ws = static_cast<float*>(workspace);

@@ -73,7 +73,16 @@ struct DecodeArgs {
     float scale_log2;  // softmax scale * log2(e)
     int sk_waves;      // > 0: balanced partition over this many waves (int8-score kernel)
     int32_t* seg;      // balanced partition: first / last wave of each item [items][2]
+    int window;        // > 0: sliding window, a query sees only its last `window` keys
 };
+
+// Sliding window: the first key a query at position pos sees (key 0 without a window).
+__host__ __device__ inline int win_lo(int window, int pos) {
+    return window > 0 && pos + 1 > window ? pos + 1 - window : 0;
+}
+// First key of the key range of a row group whose first row sits at position pos, aligned down to
+// 128 keys (a multiple of every kernel's block and of every split length).
+__host__ __device__ inline int win_begin(int window, int pos) { return win_lo(window, pos) & ~127; }
 
 hipError_t launch_store(const StoreArgs& a, int head_dim, int mode, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, int head_dim, int mode, hipStream_t stream);
@@ -85,7 +94,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int batch, int head_dim, int 
 hipError_t launch_decode_c8(const DecodeArgs& a, int batch, int head_dim, int classes, int row_tiles,
                             int mode, hipStream_t stream);
 // resident waves per compute unit of the balanced-partition kernel (0: not available)
-int decode_c8_waves_per_cu(int head_dim, int classes, int row_tiles, int mode, int batch);
+int decode_c8_waves_per_cu(int head_dim, int classes, int row_tiles, int mode, int batch, bool windowed);
 // log-sum-exp merge of the split partials; rows_per_item = query rows of one row group
 hipError_t launch_merge(const DecodeArgs& a, int batch, int head_dim, int rows_per_item, hipStream_t stream);
 

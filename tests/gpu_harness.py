@@ -112,12 +112,13 @@ class Run:
                              max_q_len=w.max_q_len, lse_out=lse, **kw)
         return out, lse
 
-    def oracle_decode(self, scale=None, nthreads=8):
+    def oracle_decode(self, scale=None, nthreads=8, window=0):
         w = self.w
         if scale is None:
             scale = 1.0 / np.sqrt(w.head_dim)
         return oracle.decode(self.hc, bits(self.queries()), w.num_q_heads, w.block_table, w.context_lengths,
-                             scale, cu_q_lens=None if w.decode_only else w.cu_q_lens, nthreads=nthreads)
+                             scale, cu_q_lens=None if w.decode_only else w.cu_q_lens, nthreads=nthreads,
+                             window=window)
 
     # ------------------------------------------------------------------------------ checks
     def assert_cache_equal(self):

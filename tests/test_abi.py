@@ -121,8 +121,21 @@ def test_dequant_and_decode_reject_bad_arguments(pkv):
     assert dec(P, 4, ctypes.byref(c), P, 8, P, None, 1, 1, 1.0, P, None, P, 1 << 30, ctypes.byref(o2), None) == -1
     o3 = pkv._opts(partition=3)  # no such partition
     assert dec(P, 4, ctypes.byref(c), P, 8, P, None, 1, 1, 1.0, P, None, P, 1 << 30, ctypes.byref(o3), None) == -1
+    o4 = pkv._opts(window=-1)  # a window is a positive number of keys (0: none)
+    assert dec(P, 4, ctypes.byref(c), P, 8, P, None, 1, 1, 1.0, P, None, P, 1 << 30, ctypes.byref(o4), None) == -1
+    assert ctypes.sizeof(pkv._DecodeOpts) == 32  # split_tokens, kernel, partition, window, reserved[4]
     # unsupported head_dim
     bad = _cache_struct(pkv, hd=80)
     assert dec(P, 4, ctypes.byref(bad), P, 8, P, None, 1, 1, 1.0, P, None, P, 1 << 30, ctypes.byref(o), None) == -2
     # empty batch is a no-op
     assert dec(P, 4, ctypes.byref(c), P, 8, P, None, 0, 1, 1.0, P, None, None, 0, ctypes.byref(o), None) == 0
+
+
+def test_sliding_window_plans_splits_over_the_window_only():
+    """With a window the plan splits only the keys one row group can need (window + the chunk's
+    spread + the 128-key alignment), not the whole block table."""
+    import paged_kv_cache_c8_amd as pkv
+
+    full = pkv.decode_plan(8, 64, 8, 128, 1024, 128, 1, 0, split_tokens=1024)
+    win = pkv.decode_plan(8, 64, 8, 128, 1024, 128, 1, 0, split_tokens=1024, window=4096)
+    assert full["num_splits"] == 128 and win["num_splits"] == 5  # ceil((4096 + 127) / 1024)

@@ -437,3 +437,39 @@ def test_per_channel_unwritten_slots_do_not_reach_the_output():
     out, lse = r.decode()
     assert torch.isfinite(out.float()).all()
     r.assert_decode_close(out, lse)
+
+
+WINDOW_CASES = [
+    # mode, D, BS, G, context lengths, q_lens, window
+    (0, 128, 16, 4, [1, 17, 300, 1000, 2000], None, 256),
+    (0, 128, 128, 8, [129, 700, 1500], None, 100),
+    (1, 128, 16, 5, [20, 400, 16, 300], [3, 16, 1, 7], 64),
+    (2, 128, 16, 4, [50, 700, 129], None, 200),
+    (3, 64, 32, 8, [33, 500, 65], None, 129),
+    (0, 64, 16, 2, [300, 31], [12, 31], 1),
+]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("mode,d,bs,g,ctx,ql,window", WINDOW_CASES)
+def test_sliding_window_matches_oracle(mode, d, bs, g, ctx, ql, window, kernel):
+    """Sliding-window decode: each query sees its last `window` positions; the key
+    ranges start at the window (128-aligned), so only those blocks are read."""
+    if mode == 3 and kernel != 3:
+        pytest.skip("the per-channel mode is served by the int8-score kernel only")
+    r = Run(_wl(mode, d, bs, g, ctx, ql, seed=sum(ctx) + window))
+    r.store_prior()
+    r.store_new()
+    ref = r.oracle_decode(window=window)
+    out, lse = r.decode(kernel=kernel, window=window)
+    r.assert_decode_close(out, lse, ref)
+    o2, l2 = r.decode(kernel=kernel, window=window, split_tokens=128)
+    r.assert_decode_close(o2, l2, ref)
+    if kernel == 3:
+        o3, l3 = r.decode(kernel=kernel, window=window, partition=2)
+        r.assert_decode_close(o3, l3, ref)
+    # a window longer than every context is no window at all, bit for bit
+    full, lf = r.decode(kernel=kernel)
+    big, lb = r.decode(kernel=kernel, window=1 << 30)
+    torch.cuda.synchronize()
+    assert torch.equal(full.view(torch.int16), big.view(torch.int16)) and torch.equal(lf, lb)
