@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--quant-mode", type=int, default=None,
                     help="run the workload's shapes with another cache mode (3 = static per-channel scales)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window: each query attends to its last W positions (0: all)")
     ap.add_argument("--kernel", type=int, default=0, help="0 = library choice, 1 = VALU, 2 = MFMA fp16 scores, 3 = MFMA int8 scores")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-baseline sample")
@@ -74,11 +76,16 @@ def calibrate_copy(steps):
                       "ms_per_launch": round(ms, 4), "gbs_read_plus_write": round(2 * n / ms / 1e6, 1)}))
 
 
-def step_bytes(w):
+def step_bytes(w, window=0):
     """Algorithmic HBM bytes of one step: every cache byte the attention must read once, plus the
     queries, outputs, block-table entries and context lengths it reads, plus the store's input and
-    output.  Split-KV partials are overhead and excluded."""
+    output.  Split-KV partials are overhead and excluded.  With a sliding window of W keys a
+    sequence's attention reads only the keys its queries see: from the first query's window start
+    to its last key."""
     ctx = w.context_lengths.astype(np.int64)
+    if window > 0:
+        first = np.maximum(w.prior_lengths.astype(np.int64) - window + 1, 0)
+        ctx = ctx - np.minimum(first, ctx)
     hkv, d, bs = w.num_kv_heads, w.head_dim, w.block_size
     if w.quant_mode == 0:
         per_tok = hkv * (2 * d + 8)
@@ -163,7 +170,7 @@ def main():
     bt, ctx, prior, cu_prior = i32(w.block_table), i32(w.context_lengths), i32(w.prior_lengths), i32(w.cu_prior)
     cu_q = None if w.decode_only else i32(w.cu_q_lens)
     q = t["q"]
-    decode_bytes, store_bytes = step_bytes(w)
+    decode_bytes, store_bytes = step_bytes(w, args.window)
     touched = decode_bytes + store_bytes
     reps = args.replicas or max(1, int(np.ceil(3 * MALL_BYTES / touched)))
 
@@ -180,11 +187,11 @@ def main():
     scale = 1.0 / float(np.sqrt(w.head_dim))
     mql = w.max_q_len if cu_q is not None else 1
     ws_bytes = pkv.decode_workspace_size(w.batch, w.num_q_heads, caches[0], w.max_blocks_per_seq, mql,
-                                         split_tokens=args.split_tokens, kernel=args.kernel)
+                                         split_tokens=args.split_tokens, kernel=args.kernel, window=args.window)
     workspace = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)  # zero-filled once
     out = torch.empty_like(q)
     plan = pkv.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_blocks_per_seq,
-                           w.block_size, mql, w.quant_mode, split_tokens=args.split_tokens, kernel=args.kernel)
+                           w.block_size, mql, w.quant_mode, split_tokens=args.split_tokens, kernel=args.kernel, window=args.window)
 
     def store(c):
         if w.decode_only:
@@ -195,7 +202,7 @@ def main():
 
     def decode(c):
         pkv.decode_gqa(q, c, bt, ctx, scale, cu_q_lens=cu_q, max_q_len=mql, out=out, workspace=workspace,
-                       split_tokens=args.split_tokens, kernel=args.kernel)
+                       split_tokens=args.split_tokens, kernel=args.kernel, window=args.window)
 
     def step(i):
         c = caches[i % reps]
@@ -236,13 +243,13 @@ def main():
     new_tokens = w.num_new_tokens if not w.decode_only else int((w.context_lengths > 0).sum())
     achieved = decode_bytes / (dec_ms * 1e-3) / 1e9
     # the counters were taken with the library's own choice of kernel and split
-    default_plan = args.kernel == 0 and args.split_tokens == 0
+    default_plan = args.kernel == 0 and args.split_tokens == 0 and args.window == 0
     mode_key = "" if args.quant_mode is None else f".mode{args.quant_mode}"
     traffic = traffic_record(f"decode.config{args.config}{mode_key}") if default_plan else None
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, t, args.cpu_seconds, touched, new_tokens)
+        cpu = cpu_baseline(w, t, args.cpu_seconds, touched, new_tokens, args.window)
 
     dtype = {0: "int8", 1: "int8", 2: "bf16", 3: "int8"}[w.quant_mode]
     roofline = {
@@ -286,6 +293,7 @@ def main():
             "head_dim": w.head_dim, "block_size": w.block_size, "quant_mode": w.quant_mode,
             "sum_context": int(w.context_lengths.sum()), "new_tokens": new_tokens,
             "cache_replicas": reps, "split_tokens": plan["split_tokens"], "num_splits": plan["num_splits"],
+            "window": args.window,
             "kernel": {1: "valu", 2: "mfma-f16", 3: "mfma-i8"}[plan["kernel"]],
             "parallelism": "single-gpu",
         },
@@ -300,7 +308,7 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(w, t, budget_s, touched, new_tokens):
+def cpu_baseline(w, t, budget_s, touched, new_tokens, window=0):
     """The oracle as it stands (plain C, fp64 attention), timed on this host's cores on a bounded
     sample of the same workload: whole steps (store of the new tokens + attention of every query)
     over as many sequences as fit in the time budget."""
@@ -359,12 +367,15 @@ def cpu_baseline(w, t, budget_s, touched, new_tokens):
         s0 = time.perf_counter()
         oracle.store(hc, kn, vn, cu_q_lens=cu, context_lengths=ws.context_lengths, block_table=ws.block_table)
         oracle.decode(hc, qh, ws.num_q_heads, ws.block_table, ws.context_lengths, scale, cu_q_lens=cu,
-                      nthreads=nthreads, want_f64=False)
+                      nthreads=nthreads, want_f64=False, window=window)
         times.append(time.perf_counter() - s0)
         if time.perf_counter() - t_start > budget_s * 0.5 or len(times) >= 2000:
             break
     sec = float(np.median(times))
-    frac = float(ws.context_lengths.sum()) / float(w.context_lengths.sum())
+    # the sample's share of the attention work (keys each sequence's queries see)
+    seen = lambda x: x.context_lengths.astype(np.int64) - (
+        np.minimum(np.maximum(x.prior_lengths.astype(np.int64) - window + 1, 0), x.context_lengths) if window > 0 else 0)
+    frac = float(seen(ws).sum()) / float(seen(w).sum())
     # the sample's step time scaled to the whole batch (attention work is linear in context)
     full_step = sec / frac
     _, store_b = step_bytes(ws)
