@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--quant-mode", type=int, default=None,
                     help="run the workload's shapes with another cache mode (3 = static per-channel scales)")
+    ap.add_argument("--partition", type=int, default=0,
+                    help="int8-score kernel key partition: 0 planned, 1 fixed, 2 balanced")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window: each query attends to its last W positions (0: all)")
     ap.add_argument("--kernel", type=int, default=0, help="0 = library choice, 1 = VALU, 2 = MFMA fp16 scores, 3 = MFMA int8 scores")
@@ -187,11 +189,13 @@ def main():
     scale = 1.0 / float(np.sqrt(w.head_dim))
     mql = w.max_q_len if cu_q is not None else 1
     ws_bytes = pkv.decode_workspace_size(w.batch, w.num_q_heads, caches[0], w.max_blocks_per_seq, mql,
-                                         split_tokens=args.split_tokens, kernel=args.kernel, window=args.window)
+                                         split_tokens=args.split_tokens, kernel=args.kernel, window=args.window,
+                                         partition=args.partition)
     workspace = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)  # zero-filled once
     out = torch.empty_like(q)
     plan = pkv.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_blocks_per_seq,
-                           w.block_size, mql, w.quant_mode, split_tokens=args.split_tokens, kernel=args.kernel, window=args.window)
+                           w.block_size, mql, w.quant_mode, split_tokens=args.split_tokens, kernel=args.kernel, window=args.window,
+                                         partition=args.partition)
 
     def store(c):
         if w.decode_only:
@@ -202,7 +206,8 @@ def main():
 
     def decode(c):
         pkv.decode_gqa(q, c, bt, ctx, scale, cu_q_lens=cu_q, max_q_len=mql, out=out, workspace=workspace,
-                       split_tokens=args.split_tokens, kernel=args.kernel, window=args.window)
+                       split_tokens=args.split_tokens, kernel=args.kernel, window=args.window,
+                                         partition=args.partition)
 
     def step(i):
         c = caches[i % reps]
@@ -243,7 +248,7 @@ def main():
     new_tokens = w.num_new_tokens if not w.decode_only else int((w.context_lengths > 0).sum())
     achieved = decode_bytes / (dec_ms * 1e-3) / 1e9
     # the counters were taken with the library's own choice of kernel and split
-    default_plan = args.kernel == 0 and args.split_tokens == 0 and args.window == 0
+    default_plan = args.kernel == 0 and args.split_tokens == 0 and args.window == 0 and args.partition == 0
     mode_key = "" if args.quant_mode is None else f".mode{args.quant_mode}"
     traffic = traffic_record(f"decode.config{args.config}{mode_key}") if default_plan else None
 
