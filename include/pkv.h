@@ -10,7 +10,10 @@
  *                   (MojoDequantFromPagedKVCache in PR #379).
  *   pkv_decode_gqa  grouped-query attention of the new queries over the paged
  *                   cache (MojoPagedDecodeGQA in the README's Op List), with
- *                   split-KV partitions and a log-sum-exp merge.
+ *                   split-KV partitions and a log-sum-exp merge; decode (one
+ *                   query per sequence), causal chunks and whole-prompt prefill
+ *                   (MojoPagedPrefillGQA), optionally over a sliding window
+ *                   (MojoSlidingWindowAttention).
  *
  * Conventions shared by every call
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The

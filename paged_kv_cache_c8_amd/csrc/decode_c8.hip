@@ -1,5 +1,5 @@
-// decode_c8.hip - grouped-query attention over the int8 paged cache (per-token or per-block
-// scales) on the matrix cores of gfx950.
+// decode_c8.hip - grouped-query attention over the int8 paged cache (per-token, per-block or
+// static per-channel scales) on the matrix cores of gfx950.
 //
 // Same result as decode_valu.hip and decode_mfma.hip (MojoPagedDecodeGQA, Mojo Opset README Op
 // List; the cache of PR #379's MojoStorePagedKVCacheC8), with the vector-ALU work per key cut to
@@ -28,9 +28,12 @@
 //    the end.  The weights are p * s_v / S with S the column's running max V scale, so they stay
 //    in [0, 2^8] in fp16.
 //
-// One wave per (sequence, KV head, row group, key split), no barriers in the loop.  The K, V and
-// scale loads of block k+1 are issued while block k computes; past the split's keys they read
-// in-bounds stand-ins (the split's last page) that the masks give zero weight.
+// One wave per (sequence, KV head, row group, key range), no barriers in the loop; the key ranges
+// are fixed splits or the segments of the balanced partition (below), and start at the window
+// when a sliding window is set.  The K, V and scale loads of block k+1 are issued while block k
+// computes; past the range's keys they read in-bounds stand-ins (the range's last page) that the
+// masks give zero weight.  Per-channel scales: the K scales join the query before it is rounded,
+// the V scales multiply the output channels, and no scale is loaded per key.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
