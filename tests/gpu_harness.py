@@ -197,12 +197,17 @@ def sub_workload(w: gen.Workload, sel, t):
         "k_all": bits(t["k_all"].index_select(0, torch.as_tensor(kv_idx, device=dev))),
         "v_all": bits(t["v_all"].index_select(0, torch.as_tensor(kv_idx, device=dev))),
     }
+    if "k_scale" in t:  # static per-channel scales: the same inputs
+        th["k_scale"], th["v_scale"] = t["k_scale"].cpu().numpy(), t["v_scale"].cpu().numpy()
     return ws, th
 
 
-def oracle_run(ws: gen.Workload, th, nthreads=8):
+def oracle_run(ws: gen.Workload, th, nthreads=8, window=0):
     """Prefill store of the prior tokens, store of the new tokens, fp64 decode - all in the oracle."""
     hc = oracle.HostCache(ws.quant_mode, ws.num_blocks, ws.num_kv_heads, ws.block_size, ws.head_dim)
+    if ws.quant_mode == 3:
+        hc.k_scale[...] = th["k_scale"]
+        hc.v_scale[...] = th["v_scale"]
     cu_ctx = ws.cu_context
     prior = ws.prior_lengths
     pri_idx = np.concatenate([np.arange(cu_ctx[b], cu_ctx[b] + prior[b]) for b in range(ws.batch)] + [[]]).astype(np.int64)
@@ -215,7 +220,7 @@ def oracle_run(ws: gen.Workload, th, nthreads=8):
                  context_lengths=ws.context_lengths, block_table=ws.block_table)
     scale = 1.0 / np.sqrt(ws.head_dim)
     res = oracle.decode(hc, th["q"], ws.num_q_heads, ws.block_table, ws.context_lengths, scale,
-                        cu_q_lens=cu, nthreads=nthreads)
+                        cu_q_lens=cu, nthreads=nthreads, window=window)
     return hc, res
 
 
