@@ -14,6 +14,7 @@ from it so that, e.g., changing the Q draw never changes the block table:
     stream 2  Q        stream 3  K        stream 4  V
     stream 5  outlier K channels
     stream 6  per-channel K scales    stream 7  per-channel V scales
+    MLA workloads: stream 2 latent query, 8 rotary query, 3 latent rows, 9 rotary key rows
 
 Integer draws use numpy's PCG64 (``numpy.random.default_rng``); the bf16
 tensors use torch's seeded generator on the requested device followed by a
@@ -287,3 +288,90 @@ def prior_workload_view(w: Workload):
     """Lengths for storing the prior tokens in one prefill-style call: q_len = prior, ctx = prior."""
     prior = w.prior_lengths
     return prior.copy(), prior.copy()
+
+
+# ----------------------------------------------------------------------------------------------
+# paged MLA (latent cache) workloads
+# ----------------------------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class MLAWorkload:
+    """One decode batch over a paged latent cache: one new token (and query) per sequence, stored
+    at position ``context_lengths[b] - 1``; every query head shares the sequence's latent rows."""
+
+    name: str
+    batch: int
+    num_heads: int
+    latent_dim: int
+    rope_dim: int
+    block_size: int
+    context_lengths: np.ndarray  # int32 [B]
+    num_blocks: int
+    max_blocks_per_seq: int
+    block_table: np.ndarray  # int32 [B, MBS], unused entries -1
+    seed: int
+    softmax_scale: float
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.context_lengths.sum())
+
+    @property
+    def prior_lengths(self) -> np.ndarray:
+        return np.maximum(self.context_lengths - 1, 0).astype(np.int32)
+
+    @property
+    def cu_context(self) -> np.ndarray:
+        cu = np.zeros(self.batch + 1, dtype=np.int64)
+        cu[1:] = np.cumsum(self.context_lengths)
+        return cu
+
+
+def mla_workload(name, *, batch, num_heads, block_size, context_lengths, latent_dim=512, rope_dim=64,
+                 seed=0, pool_factor=2, num_blocks=None, max_blocks_per_seq=None, softmax_scale=None):
+    ctx = np.asarray(context_lengths, dtype=np.int32).reshape(batch)
+    need = int(sum(-(-int(c) // block_size) for c in ctx))
+    if num_blocks is None:
+        num_blocks = max(1, pool_factor * need)
+    if max_blocks_per_seq is None:
+        max_blocks_per_seq = max(1, max(-(-int(c) // block_size) for c in ctx) if batch else 1)
+    bt = make_block_table(ctx, block_size, num_blocks, max_blocks_per_seq, seed)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(latent_dim + rope_dim)
+    return MLAWorkload(name, batch, num_heads, latent_dim, rope_dim, block_size, ctx, int(num_blocks),
+                       int(max_blocks_per_seq), bt, seed, float(softmax_scale))
+
+
+MLA_CONFIG_NAMES = ["mla-tiny-decode", "deepseek-v3-mla-decode"]
+
+
+def make_mla_config(index: int, seed: Optional[int] = None) -> MLAWorkload:
+    """MLA decode workloads, seeded with ``2000 + index`` by default.
+
+    0  tiny:       B=2, 16 heads, latent 512 + rotary 64, BS=16, ctx {37, 100}
+    1  DeepSeek-V3 shaped: B=64, 16 query heads (one GPU's share when the 128 heads are split
+                   8 ways; the latent cache is then read whole by every GPU), latent 512 +
+                   rotary 64, BS=64, ctx ~ U[2048, 8192], softmax scale 1/sqrt(128 + 64) (the
+                   per-head query-key width before absorption)
+    """
+    s = 2000 + index if seed is None else seed
+    r = _rng(s, 0)
+    if index == 0:
+        return mla_workload(MLA_CONFIG_NAMES[0], batch=2, num_heads=16, block_size=16,
+                            context_lengths=[37, 100], seed=s, num_blocks=16, max_blocks_per_seq=7)
+    if index == 1:
+        ctx = r.integers(2048, 8192, size=64, endpoint=True)
+        return mla_workload(MLA_CONFIG_NAMES[1], batch=64, num_heads=16, block_size=64, context_lengths=ctx,
+                            seed=s, max_blocks_per_seq=8192 // 64, softmax_scale=1.0 / math.sqrt(192.0))
+    raise ValueError(f"no MLA config {index}")
+
+
+def gen_mla_tensors(w: MLAWorkload, device="cpu"):
+    """N(0, 1) bf16 draws: q_latent [B, H, Dc], q_rope [B, H, Dr], latent_all [sum(ctx), Dc],
+    rope_all [sum(ctx), Dr] (sequence b's positions start at ``w.cu_context[b]``)."""
+    return {
+        "q_latent": normal_bf16((w.batch, w.num_heads, w.latent_dim), w.seed, 2, device),
+        "q_rope": normal_bf16((w.batch, w.num_heads, w.rope_dim), w.seed, 8, device),
+        "latent_all": normal_bf16((w.total_tokens, w.latent_dim), w.seed, 3, device),
+        "rope_all": normal_bf16((w.total_tokens, w.rope_dim), w.seed, 9, device),
+    }

@@ -58,6 +58,11 @@ def lib():
         L.oracle_decode.argtypes = [I, I, I, I, I, P, P, P, P, P, I, P, I, P, P, I,
                                     ctypes.c_double, P, P, P, I, I]
         L.oracle_decode.restype = I
+        L.oracle_mla_store.argtypes = [I, I, I, I, P, P, P, P, P, P, I, P, P, P, P, I, I]
+        L.oracle_mla_store.restype = I
+        L.oracle_mla_decode.argtypes = [I, I, I, I, P, P, P, P, P, P, I, P, I, P, I,
+                                        ctypes.c_double, P, P, P, I]
+        L.oracle_mla_decode.restype = I
         _lib = L
     return _lib
 
@@ -184,3 +189,67 @@ def decode(cache: HostCache, q, num_q_heads, block_table, context_lengths, scale
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """Reinterpret bf16 bit patterns as fp32 values (exact)."""
     return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+class MLAHostCache:
+    """A host copy of a paged MLA cache: latent codes ``int8 [NB, BS, Dc]``, rotary-key codes
+    ``int8 [NB, BS, Dr]``, and one fp32 scale per token for each, ``[NB, BS]``."""
+
+    def __init__(self, num_blocks, block_size, latent_dim, rope_dim):
+        self.nb, self.bs, self.dc, self.dr = num_blocks, block_size, latent_dim, rope_dim
+        self.latent = np.zeros((num_blocks, block_size, latent_dim), np.int8)
+        self.rope = np.zeros((num_blocks, block_size, rope_dim), np.int8)
+        self.latent_scale = np.zeros((num_blocks, block_size), np.float32)
+        self.rope_scale = np.zeros((num_blocks, block_size), np.float32)
+
+    def args(self):
+        return (self.nb, self.bs, self.dc, self.dr, _p(self.latent), _p(self.rope),
+                _p(self.latent_scale), _p(self.rope_scale))
+
+    def copy(self):
+        c = MLAHostCache.__new__(MLAHostCache)
+        c.__dict__.update(self.__dict__)
+        for k in ("latent", "rope", "latent_scale", "rope_scale"):
+            setattr(c, k, getattr(self, k).copy())
+        return c
+
+
+def mla_store(cache: MLAHostCache, latent_new, rope_new, *, slot_mapping=None, cu_q_lens=None,
+              context_lengths=None, block_table=None):
+    """Quantize and write new tokens (bf16 bits ``uint16 [T, Dc]`` and ``[T, Dr]``)."""
+    _check(latent_new, np.uint16, "latent_new")
+    _check(rope_new, np.uint16, "rope_new")
+    latent_new = np.ascontiguousarray(latent_new)
+    rope_new = np.ascontiguousarray(rope_new)
+    sm = None if slot_mapping is None else np.ascontiguousarray(slot_mapping, np.int64)
+    cu = None if cu_q_lens is None else np.ascontiguousarray(cu_q_lens, np.int32)
+    ctx = None if context_lengths is None else np.ascontiguousarray(context_lengths, np.int32)
+    bt = None if block_table is None else np.ascontiguousarray(block_table, np.int32)
+    batch = 0 if ctx is None else len(ctx)
+    mbs = 0 if bt is None else bt.shape[1]
+    rc = lib().oracle_mla_store(*cache.args(), _p(latent_new), _p(rope_new), latent_new.shape[0],
+                                _p(sm), _p(cu), _p(ctx), _p(bt), batch, mbs)
+    if rc != 0:
+        raise ValueError("oracle_mla_store rejected its arguments")
+
+
+def mla_decode(cache: MLAHostCache, q_latent, q_rope, block_table, context_lengths, scale, *,
+               nthreads=1, want_f64=True):
+    """fp64 latent attention of one query per sequence. ``q_latent``: bf16 bits ``[B, H, Dc]``,
+    ``q_rope``: ``[B, H, Dr]``.  Returns (out_bf16 uint16 [B, H, Dc], out_f64 or None,
+    lse fp64 [B, H])."""
+    _check(q_latent, np.uint16, "q_latent")
+    _check(q_rope, np.uint16, "q_rope")
+    ql = np.ascontiguousarray(q_latent)
+    qr = np.ascontiguousarray(q_rope)
+    bt = np.ascontiguousarray(block_table, np.int32)
+    ctx = np.ascontiguousarray(context_lengths, np.int32)
+    b, h = ql.shape[0], ql.shape[1]
+    out = np.zeros((b, h, cache.dc), np.uint16)
+    out64 = np.zeros((b, h, cache.dc), np.float64) if want_f64 else None
+    lse = np.zeros((b, h), np.float64)
+    rc = lib().oracle_mla_decode(*cache.args(), _p(ql), _p(qr), h, _p(bt), bt.shape[1], _p(ctx),
+                                 len(ctx), float(scale), _p(out), _p(out64), _p(lse), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_mla_decode rejected its arguments")
+    return out, out64, lse

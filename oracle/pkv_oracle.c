@@ -36,6 +36,10 @@
  *  - decode: grouped-query attention of one new query per sequence over the
  *    paged cache ([P1] MojoPagedDecodeGQA), generalised to a causal chunk of
  *    q_len new queries, accumulated in fp64 over the dequantized values.
+ *  - paged MLA store and decode ([P1] MojoStorePagedMLAKVCache,
+ *    MojoPagedDecodeMLA): latent attention over a per-token int8 latent row
+ *    and rotary-key row shared by all heads (the reading is stated at the MLA
+ *    section below).
  *
  * Cache layout (the boundary contract; element (block, head, slot, channel)):
  *   K  [NB][Hkv][BS][D]   int8, or bf16 in mode 2
@@ -565,6 +569,248 @@ int oracle_decode(int mode, int nb, int hkv, int bs, int d, const void *k_cache,
         pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
         for (int i = 0; i < nthreads; i++)
             pthread_create(&th[i], NULL, decode_worker, &J);
+        for (int i = 0; i < nthreads; i++)
+            pthread_join(th[i], NULL);
+        free(th);
+    }
+    pthread_mutex_destroy(&J.mu);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* paged MLA (latent) cache                                                   */
+/* ------------------------------------------------------------------------- */
+/*
+ * [P1] lists MojoStorePagedMLAKVCache (KVCache rows) and MojoPagedDecodeMLA
+ * (Attention rows) next to the GQA ops and says nothing more about them.  The
+ * reading taken here is multi-head latent attention in its absorbed decode
+ * form: every token keeps one compressed latent row c (Dc channels) and one
+ * decoupled rotary key row r (Dr channels), shared by all query heads; a head
+ * scores key t as scale * (q_c . c_t + q_r . r_t) and returns the weighted sum
+ * of the latent rows (Dc channels; the value up-projection that follows is a
+ * separate matrix product).  C8 storage: each of the two rows of a token is
+ * quantized like a per-token row of the GQA cache (its own scale
+ * fl32(absmax / 127), codes round-half-even, clamped), so a token carries two
+ * fp32 scales.
+ *
+ * Layout:
+ *   latent [NB][BS][Dc] int8    rope [NB][BS][Dr] int8
+ *   latent_scale [NB][BS] fp32  rope_scale [NB][BS] fp32
+ */
+
+/* quantize one row of n bf16 values with its own absmax scale */
+static void quant_row(const uint16_t *x, int n, int8_t *codes, float *scale)
+{
+    float absmax = 0.0f;
+    for (int i = 0; i < n; i++) {
+        float a = fabsf(bf16_to_float(x[i]));
+        if (a > absmax)
+            absmax = a;
+    }
+    float s = absmax_scale(absmax);
+    for (int i = 0; i < n; i++)
+        codes[i] = quant_one(bf16_to_float(x[i]), s);
+    *scale = s;
+}
+
+/*
+ * Store T new tokens: latent_new bf16 [T][Dc], rope_new bf16 [T][Dr].  Slots
+ * are resolved as in oracle_store (slot_mapping, or cu_q_lens + context
+ * lengths + block table).  Returns 0, or -1 on an argument it cannot serve.
+ */
+int oracle_mla_store(int nb, int bs, int dc, int dr, int8_t *latent, int8_t *rope,
+                     float *latent_scale, float *rope_scale, const uint16_t *latent_new,
+                     const uint16_t *rope_new, int num_tokens, const int64_t *slot_mapping,
+                     const int32_t *cu_q_lens, const int32_t *context_lengths,
+                     const int32_t *block_table, int batch, int mbs)
+{
+    if (bs <= 0 || dc <= 0 || dr <= 0)
+        return -1;
+    if (slot_mapping) {
+        for (int t = 0; t < num_tokens; t++) {
+            int64_t slot = slot_mapping[t];
+            if (slot < 0)
+                continue; /* padding token */
+            if (slot / bs >= nb)
+                return -1;
+            quant_row(latent_new + (int64_t)t * dc, dc, latent + slot * dc, &latent_scale[slot]);
+            quant_row(rope_new + (int64_t)t * dr, dr, rope + slot * dr, &rope_scale[slot]);
+        }
+        return 0;
+    }
+    if (!context_lengths || !block_table)
+        return -1;
+    for (int b = 0; b < batch; b++) {
+        int qlen = cu_q_lens ? cu_q_lens[b + 1] - cu_q_lens[b] : 1;
+        int t0 = cu_q_lens ? cu_q_lens[b] : b;
+        int prior = context_lengths[b] - qlen;
+        for (int i = 0; i < qlen; i++) {
+            int p = prior + i;
+            if (p < 0)
+                continue; /* inactive decode slot (context length 0): nothing to store */
+            if (p / bs >= mbs)
+                return -1;
+            int64_t blk = block_table[(int64_t)b * mbs + p / bs];
+            if (blk < 0 || blk >= nb)
+                return -1;
+            int64_t slot = blk * bs + p % bs; /* row of the token in the page arrays */
+            quant_row(latent_new + (int64_t)(t0 + i) * dc, dc, latent + slot * dc, &latent_scale[slot]);
+            quant_row(rope_new + (int64_t)(t0 + i) * dr, dr, rope + slot * dr, &rope_scale[slot]);
+        }
+    }
+    return 0;
+}
+
+typedef struct {
+    int nb, bs, dc, dr;
+    const int8_t *latent, *rope;
+    const float *latent_scale, *rope_scale;
+    const uint16_t *q_latent, *q_rope;
+    int heads;
+    const int32_t *block_table;
+    int mbs;
+    const int32_t *context_lengths;
+    int batch;
+    double scale;
+    uint16_t *out;
+    double *out_f64;
+    double *lse;
+    int next_item;
+    pthread_mutex_t mu;
+} mla_job;
+
+/*
+ * Sequence b, head h (one new query per sequence, at the last position; keys
+ * t = 0 .. ctx_b - 1, the new token included):
+ *   c^_t = double(code) * double(latent_scale)   r^_t likewise (exact in fp64)
+ *   l_t = scale * (sum_i q_c[i] c^_t[i] + sum_j q_r[j] r^_t[j])
+ *   m = max_t l_t,  w_t = exp(l_t - m),  L = sum_t w_t
+ *   out[i] = (sum_t w_t c^_t[i]) / L,  lse = m + ln L
+ * No keys: out = 0, lse = -inf.
+ */
+static void mla_item(mla_job *J, int b, int h, double *l, double *acc)
+{
+    int64_t o = ((int64_t)b * J->heads + h);
+    const uint16_t *qc = J->q_latent + o * J->dc;
+    const uint16_t *qr = J->q_rope + o * J->dr;
+    int ctx = J->context_lengths[b];
+    if (ctx <= 0) {
+        for (int i = 0; i < J->dc; i++) {
+            J->out[o * J->dc + i] = oracle_bf16_round(0.0);
+            if (J->out_f64)
+                J->out_f64[o * J->dc + i] = 0.0;
+        }
+        if (J->lse)
+            J->lse[o] = -INFINITY;
+        return;
+    }
+    double m = -INFINITY;
+    for (int t = 0; t < ctx; t++) {
+        int64_t row = (int64_t)J->block_table[(int64_t)b * J->mbs + t / J->bs] * J->bs + t % J->bs;
+        double sc = (double)J->latent_scale[row], sr = (double)J->rope_scale[row];
+        double dot = 0.0;
+        for (int i = 0; i < J->dc; i++)
+            dot += (double)bf16_to_float(qc[i]) * ((double)J->latent[row * J->dc + i] * sc);
+        for (int j = 0; j < J->dr; j++)
+            dot += (double)bf16_to_float(qr[j]) * ((double)J->rope[row * J->dr + j] * sr);
+        l[t] = J->scale * dot;
+        if (l[t] > m)
+            m = l[t];
+    }
+    for (int i = 0; i < J->dc; i++)
+        acc[i] = 0.0;
+    double sum = 0.0;
+    for (int t = 0; t < ctx; t++) {
+        int64_t row = (int64_t)J->block_table[(int64_t)b * J->mbs + t / J->bs] * J->bs + t % J->bs;
+        double sc = (double)J->latent_scale[row];
+        double w = exp(l[t] - m);
+        sum += w;
+        for (int i = 0; i < J->dc; i++)
+            acc[i] += w * ((double)J->latent[row * J->dc + i] * sc);
+    }
+    for (int i = 0; i < J->dc; i++) {
+        double y = acc[i] / sum;
+        J->out[o * J->dc + i] = oracle_bf16_round(y);
+        if (J->out_f64)
+            J->out_f64[o * J->dc + i] = y;
+    }
+    if (J->lse)
+        J->lse[o] = m + log(sum);
+}
+
+static void *mla_worker(void *arg)
+{
+    mla_job *J = (mla_job *)arg;
+    int max_ctx = 1;
+    for (int b = 0; b < J->batch; b++)
+        if (J->context_lengths[b] > max_ctx)
+            max_ctx = J->context_lengths[b];
+    double *l = (double *)malloc(sizeof(double) * (size_t)max_ctx);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)J->dc);
+    int items = J->batch * J->heads;
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int it = J->next_item++;
+        pthread_mutex_unlock(&J->mu);
+        if (it >= items)
+            break;
+        mla_item(J, it / J->heads, it % J->heads, l, acc);
+    }
+    free(acc);
+    free(l);
+    return NULL;
+}
+
+/*
+ * Latent attention of one new query per sequence.  q_latent bf16 [B][H][Dc],
+ * q_rope bf16 [B][H][Dr]; out bf16 [B][H][Dc] (the fp64 result rounded once),
+ * out_f64 (optional) fp64 [B][H][Dc], lse (optional) fp64 [B][H].
+ */
+int oracle_mla_decode(int nb, int bs, int dc, int dr, const int8_t *latent, const int8_t *rope,
+                      const float *latent_scale, const float *rope_scale, const uint16_t *q_latent,
+                      const uint16_t *q_rope, int heads, const int32_t *block_table, int mbs,
+                      const int32_t *context_lengths, int batch, double scale, uint16_t *out,
+                      double *out_f64, double *lse, int nthreads)
+{
+    if (bs <= 0 || dc <= 0 || dr <= 0 || heads <= 0 || !out)
+        return -1;
+    for (int b = 0; b < batch; b++) {
+        if (context_lengths[b] > mbs * bs)
+            return -1;
+        for (int j = 0; j * bs < context_lengths[b]; j++)
+            if (block_table[(int64_t)b * mbs + j] < 0 || block_table[(int64_t)b * mbs + j] >= nb)
+                return -1;
+    }
+    mla_job J;
+    memset(&J, 0, sizeof J);
+    J.nb = nb;
+    J.bs = bs;
+    J.dc = dc;
+    J.dr = dr;
+    J.latent = latent;
+    J.rope = rope;
+    J.latent_scale = latent_scale;
+    J.rope_scale = rope_scale;
+    J.q_latent = q_latent;
+    J.q_rope = q_rope;
+    J.heads = heads;
+    J.block_table = block_table;
+    J.mbs = mbs;
+    J.context_lengths = context_lengths;
+    J.batch = batch;
+    J.scale = scale;
+    J.out = out;
+    J.out_f64 = out_f64;
+    J.lse = lse;
+    pthread_mutex_init(&J.mu, NULL);
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads == 1) {
+        mla_worker(&J);
+    } else {
+        pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+        for (int i = 0; i < nthreads; i++)
+            pthread_create(&th[i], NULL, mla_worker, &J);
         for (int i = 0; i < nthreads; i++)
             pthread_join(th[i], NULL);
         free(th);

@@ -27,7 +27,8 @@ def test_oracle_suite_under_asan(tmp_path):
     env["PKV_ORACLE_LIB"] = str(lib)
     env["LD_PRELOAD"] = _libasan()
     env["ASAN_OPTIONS"] = "detect_leaks=0:verify_asan_link_order=0:abort_on_error=1"
-    tests = ["tests/test_oracle_store.py", "tests/test_oracle_dequant.py", "tests/test_oracle_decode.py"]
+    tests = ["tests/test_oracle_store.py", "tests/test_oracle_dequant.py", "tests/test_oracle_decode.py",
+             "tests/test_oracle_mla.py"]
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", *tests],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
     assert r.returncode == 0, (r.stdout[-3000:] + r.stderr[-3000:])
