@@ -14,6 +14,9 @@
  *                   query per sequence), causal chunks and whole-prompt prefill
  *                   (MojoPagedPrefillGQA), optionally over a sliding window
  *                   (MojoSlidingWindowAttention).
+ *   pkv_mla_store_c8 / pkv_mla_decode  the same for a latent (MLA) cache
+ *                   (MojoStorePagedMLAKVCache, MojoPagedDecodeMLA; see the MLA
+ *                   section below).
  *
  * Conventions shared by every call
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
@@ -226,6 +229,86 @@ int pkv_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, in
                     int32_t max_blocks_per_seq, int32_t block_size, int32_t max_q_len,
                     int32_t quant_mode, const pkv_decode_opts_t *opts, int32_t *split_tokens,
                     int32_t *num_splits, int32_t *kernel);
+
+/* ------------------------------------------------------------------------- */
+/* Paged MLA (latent) cache                                                   */
+/* ------------------------------------------------------------------------- */
+/*
+ * MojoStorePagedMLAKVCache and MojoPagedDecodeMLA (README Op List; the pages
+ * give no definition).  Read as multi-head latent attention in its absorbed
+ * decode form: each token keeps one latent row c (512 channels) and one
+ * rotary-key row r (64 channels), shared by every query head.  Each row is
+ * stored as int8 codes with its own per-token scale, as in
+ * PKV_QUANT_PER_TOKEN: s = fl32(absmax / 127), code = clamp(rne(fl32(x / s)),
+ * -128, 127), 0 when s == 0.
+ *
+ * Layout (caller-owned, 16-byte aligned; row = block * block_size + slot):
+ *   latent        int8  [num_blocks][block_size][512]
+ *   rope          int8  [num_blocks][block_size][64]
+ *   latent_scale  float [num_blocks][block_size]
+ *   rope_scale    float [num_blocks][block_size]
+ * Supported: latent_dim 512, rope_dim 64; block_size 16, 32, 64 or 128.
+ */
+typedef struct {
+    void *latent;
+    void *rope;
+    float *latent_scale;
+    float *rope_scale;
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t latent_dim;  /* 512 */
+    int32_t rope_dim;    /* 64 */
+} pkv_mla_cache_t;
+
+/*
+ * pkv_mla_store_c8 - quantize new tokens' latent rows (bf16 [T][512], 16-byte
+ * aligned) and rotary-key rows (bf16 [T][64]) into the MLA cache.  Slots are
+ * resolved exactly as in pkv_store_c8: slot_mapping[t] (row index block *
+ * block_size + slot; negative = skip), or cu_q_lens / context_lengths /
+ * block_table (cu_q_lens NULL: one token per sequence, num_tokens == batch;
+ * a sequence with context length 0 stores nothing).  num_tokens == 0 launches
+ * nothing.
+ */
+int pkv_mla_store_c8(const pkv_mla_cache_t *cache, const void *latent_new, const void *rope_new,
+                     int32_t num_tokens, const int64_t *slot_mapping, const int32_t *cu_q_lens,
+                     const int32_t *context_lengths, const int32_t *block_table, int32_t batch,
+                     int32_t max_blocks_per_seq, void *stream);
+
+/* Bytes of workspace pkv_mla_decode needs (0 when it needs none; 0 also for
+ * arguments it rejects).  split_tokens: 0 = the library's plan, else keys per
+ * split (rounded up to a multiple of 64).  Depends on the current device's
+ * compute-unit count. */
+size_t pkv_mla_decode_workspace_size(int32_t batch, int32_t num_heads, int32_t max_blocks_per_seq,
+                                     int32_t block_size, int32_t split_tokens);
+
+/* The split plan pkv_mla_decode would use: keys per split and splits per
+ * (sequence, group of 16 heads); either output pointer may be NULL. */
+int pkv_mla_decode_plan(int32_t batch, int32_t num_heads, int32_t max_blocks_per_seq,
+                        int32_t block_size, int32_t split_tokens, int32_t *split_len,
+                        int32_t *num_splits);
+
+/*
+ * pkv_mla_decode - latent attention of one new query per sequence over the
+ * MLA cache (MojoPagedDecodeMLA, README Op List).
+ *
+ * q_latent bf16 [batch][num_heads][512] (the query already multiplied into the
+ *          latent space), q_rope bf16 [batch][num_heads][64]; both 16-byte
+ *          aligned.  Sequence b attends to keys 0 .. context_lengths[b] - 1
+ *          (its new token included):
+ *   l_t = scale * (q_latent . c^_t + q_rope . r^_t)   (c^, r^ dequantized)
+ *   out = sum_t softmax(l)_t c^_t    bf16 [batch][num_heads][512], 16-byte
+ *          aligned (the value up-projection that follows is not part of it)
+ * lse_out  optional fp32 [batch][num_heads]: natural log of the softmax
+ *          denominator; -inf for a sequence with no keys (output 0).
+ * workspace: at least pkv_mla_decode_workspace_size(...) bytes with the same
+ *          split_tokens, 16-byte aligned, no initial contents needed; calls
+ *          that run concurrently must not share it.
+ */
+int pkv_mla_decode(const void *q_latent, const void *q_rope, int32_t num_heads,
+                   const pkv_mla_cache_t *cache, const int32_t *block_table,
+                   int32_t max_blocks_per_seq, const int32_t *context_lengths, int32_t batch,
+                   float scale, void *out, float *lse_out, void *workspace, size_t workspace_bytes,
+                   int32_t split_tokens, void *stream);
 
 #ifdef __cplusplus
 }

@@ -14,7 +14,8 @@ import os
 import torch  # loaded first: libpkv binds to the HIP runtime torch has already loaded
 
 __all__ = ["PkvError", "Cache", "lib", "store_c8", "dequant", "decode_gqa", "decode_workspace_size",
-           "decode_plan", "QUANT_PER_TOKEN", "QUANT_PER_BLOCK", "QUANT_NONE_BF16", "QUANT_PER_CHANNEL",
+           "decode_plan", "MLACache", "mla_store_c8", "mla_decode", "mla_decode_workspace_size",
+           "mla_decode_plan", "QUANT_PER_TOKEN", "QUANT_PER_BLOCK", "QUANT_NONE_BF16", "QUANT_PER_CHANNEL",
            "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,7 +28,11 @@ QUANT_PER_CHANNEL = 3
 
 # every symbol include/pkv.h declares
 EXPORTS = ("pkv_status_string", "pkv_version", "pkv_store_c8", "pkv_dequant",
-           "pkv_decode_workspace_size", "pkv_decode_gqa", "pkv_decode_plan")
+           "pkv_decode_workspace_size", "pkv_decode_gqa", "pkv_decode_plan", "pkv_mla_store_c8",
+           "pkv_mla_decode_workspace_size", "pkv_mla_decode_plan", "pkv_mla_decode")
+
+MLA_LATENT_DIM = 512
+MLA_ROPE_DIM = 64
 
 
 class PkvError(RuntimeError):
@@ -41,6 +46,12 @@ class _CacheT(ctypes.Structure):
                 ("v_scale", ctypes.c_void_p), ("num_blocks", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("quant_mode", ctypes.c_int32)]
+
+
+class _MLACacheT(ctypes.Structure):
+    _fields_ = [("latent", ctypes.c_void_p), ("rope", ctypes.c_void_p), ("latent_scale", ctypes.c_void_p),
+                ("rope_scale", ctypes.c_void_p), ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("latent_dim", ctypes.c_int32), ("rope_dim", ctypes.c_int32)]
 
 
 class _DecodeOpts(ctypes.Structure):
@@ -76,6 +87,14 @@ def lib():
         L.pkv_decode_plan.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32, P,
                                       ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]
         L.pkv_decode_plan.restype = ctypes.c_int
+        L.pkv_mla_store_c8.argtypes = [P, P, P, I32, P, P, P, P, I32, I32, P]
+        L.pkv_mla_store_c8.restype = ctypes.c_int
+        L.pkv_mla_decode_workspace_size.argtypes = [I32, I32, I32, I32, I32]
+        L.pkv_mla_decode_workspace_size.restype = SZ
+        L.pkv_mla_decode_plan.argtypes = [I32, I32, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]
+        L.pkv_mla_decode_plan.restype = ctypes.c_int
+        L.pkv_mla_decode.argtypes = [P, P, I32, P, P, I32, P, I32, ctypes.c_float, P, P, P, SZ, I32, P]
+        L.pkv_mla_decode.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -221,4 +240,73 @@ def decode_gqa(q, cache: Cache, block_table, context_lengths, scale, *, cu_q_len
                               _ptr(cu_q_lens), batch, int(max_q_len), float(scale), _ptr(out),
                               _ptr(lse_out), _ptr(workspace), ws_bytes, ctypes.byref(o), _stream(stream))
     _check(st, "pkv_decode_gqa")
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+# paged MLA (latent) cache
+# ---------------------------------------------------------------------------------------------
+
+class MLACache:
+    """A paged latent cache in the layout include/pkv.h documents: ``latent`` int8
+    ``[NB, BS, 512]``, ``rope`` int8 ``[NB, BS, 64]``, ``latent_scale`` / ``rope_scale`` fp32
+    ``[NB, BS]`` (one per token)."""
+
+    def __init__(self, num_blocks, block_size, device="cuda", latent_dim=MLA_LATENT_DIM, rope_dim=MLA_ROPE_DIM):
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        self.latent_dim, self.rope_dim = int(latent_dim), int(rope_dim)
+        self.latent = torch.zeros((num_blocks, block_size, latent_dim), dtype=torch.int8, device=device)
+        self.rope = torch.zeros((num_blocks, block_size, rope_dim), dtype=torch.int8, device=device)
+        self.latent_scale = torch.zeros((num_blocks, block_size), dtype=torch.float32, device=device)
+        self.rope_scale = torch.zeros((num_blocks, block_size), dtype=torch.float32, device=device)
+        self._c = _MLACacheT(self.latent.data_ptr(), self.rope.data_ptr(), self.latent_scale.data_ptr(),
+                             self.rope_scale.data_ptr(), self.num_blocks, self.block_size, self.latent_dim,
+                             self.rope_dim)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._c)
+
+
+def mla_store_c8(cache: MLACache, latent_new, rope_new, *, slot_mapping=None, cu_q_lens=None,
+                 context_lengths=None, block_table=None, stream=None):
+    """Quantize bf16 latent rows ``[T, 512]`` and rotary-key rows ``[T, 64]`` into the cache."""
+    t = int(latent_new.shape[0])
+    batch = 0 if context_lengths is None else int(context_lengths.shape[0])
+    mbs = 0 if block_table is None else int(block_table.shape[1])
+    st = lib().pkv_mla_store_c8(cache.ref, _ptr(latent_new), _ptr(rope_new), t, _ptr(slot_mapping),
+                                _ptr(cu_q_lens), _ptr(context_lengths), _ptr(block_table), batch, mbs,
+                                _stream(stream))
+    _check(st, "pkv_mla_store_c8")
+
+
+def mla_decode_workspace_size(batch, num_heads, max_blocks_per_seq, block_size, split_tokens=0) -> int:
+    return int(lib().pkv_mla_decode_workspace_size(batch, num_heads, max_blocks_per_seq, block_size,
+                                                   int(split_tokens)))
+
+
+def mla_decode_plan(batch, num_heads, max_blocks_per_seq, block_size, split_tokens=0):
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    st = lib().pkv_mla_decode_plan(batch, num_heads, max_blocks_per_seq, block_size, int(split_tokens),
+                                   ctypes.byref(a), ctypes.byref(b))
+    _check(st, "pkv_mla_decode_plan")
+    return {"split_tokens": a.value, "num_splits": b.value}
+
+
+def mla_decode(q_latent, q_rope, cache: MLACache, block_table, context_lengths, scale, *, out=None,
+               lse_out=None, workspace=None, split_tokens=0, stream=None):
+    """Latent attention of one query per sequence: ``q_latent`` bf16 ``[B, H, 512]``, ``q_rope``
+    bf16 ``[B, H, 64]``; returns bf16 ``[B, H, 512]``."""
+    batch, heads = int(q_latent.shape[0]), int(q_latent.shape[1])
+    mbs = int(block_table.shape[1])
+    if out is None:
+        out = torch.empty_like(q_latent)
+    need = mla_decode_workspace_size(batch, heads, mbs, cache.block_size, split_tokens)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_latent.device)  # no initial contents needed
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().pkv_mla_decode(_ptr(q_latent), _ptr(q_rope), heads, cache.ref, _ptr(block_table), mbs,
+                              _ptr(context_lengths), batch, float(scale), _ptr(out), _ptr(lse_out),
+                              _ptr(workspace), ws_bytes, int(split_tokens), _stream(stream))
+    _check(st, "pkv_mla_decode")
     return out

@@ -1,0 +1,50 @@
+// mla_internal.h - argument block and launchers of the paged MLA (latent cache) kernels, shared
+// between the C-ABI layer (mla_api.cpp) and mla.hip.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kMlaLatent = 512;  // latent channels of a token row
+constexpr int kMlaRope = 64;     // rotary-key channels of a token row
+constexpr int kMlaHeads = 16;    // query heads per work item (one 16-column matrix tile)
+
+struct MlaArgs {
+    // cache: latent [NB][BS][512] and rope [NB][BS][64] int8, one fp32 scale per token for each
+    int8_t* latent;
+    int8_t* rope;
+    float* ls;
+    float* rs;
+    // store
+    const uint16_t* latent_new;  // bf16 [T][512]
+    const uint16_t* rope_new;    // bf16 [T][64]
+    const int64_t* slot_mapping;
+    const int32_t* cu_q;
+    int num_tokens;
+    // decode
+    const uint16_t* ql;  // bf16 [B][H][512]
+    const uint16_t* qr;  // bf16 [B][H][64]
+    uint16_t* out;       // bf16 [B][H][512]
+    float* lse;          // [B][H] or null
+    float* part_o;       // [nsplit][items][16][512]
+    float* part_lse;     // [nsplit][items][16] (base-2 log-sum-exp)
+    // both
+    const int32_t* bt;
+    const int32_t* ctx;
+    int batch;
+    int heads;
+    int nhg;  // head groups of 16 per sequence
+    int bs;
+    int log2bs;
+    int mbs;
+    int nsplit;
+    int split_len;     // keys per split, a multiple of 64
+    float scale_log2;  // softmax scale * log2(e)
+};
+
+hipError_t launch_mla_store(const MlaArgs& a, hipStream_t stream);
+hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);
+
+}  // namespace pkv

@@ -139,3 +139,34 @@ def test_sliding_window_plans_splits_over_the_window_only():
     full = pkv.decode_plan(8, 64, 8, 128, 1024, 128, 1, 0, split_tokens=1024)
     win = pkv.decode_plan(8, 64, 8, 128, 1024, 128, 1, 0, split_tokens=1024, window=4096)
     assert full["num_splits"] == 128 and win["num_splits"] == 5  # ceil((4096 + 127) / 1024)
+
+
+def test_mla_plan_and_argument_checks(pkv):
+    lib = pkv.lib()
+    P = 4096
+    p = pkv.mla_decode_plan(64, 16, 128, 64)
+    assert p == pkv.mla_decode_plan(64, 16, 128, 64)
+    assert p["split_tokens"] % 64 == 0 and p["num_splits"] * p["split_tokens"] >= 128 * 64
+    assert pkv.mla_decode_plan(64, 16, 128, 64, split_tokens=1000) == {"split_tokens": 1024, "num_splits": 8}
+    assert pkv.mla_decode_plan(2, 16, 7, 16, split_tokens=100000)["num_splits"] == 1
+    ws = pkv.mla_decode_workspace_size(64, 16, 128, 64, split_tokens=1024)
+    assert ws == 64 * 8 * 16 * 513 * 4  # partials: (sequence, split) x 16 heads x (512 channels + lse)
+    assert pkv.mla_decode_workspace_size(64, 17, 128, 64, split_tokens=1024) == 2 * ws  # 2 head groups
+    assert pkv.mla_decode_workspace_size(2, 16, 7, 16, split_tokens=100000) == 0
+    c = pkv._MLACacheT(16, 32, 64, 128, 4, 16, 512, 64)
+    st = lambda cache, *a: lib.pkv_mla_store_c8(ctypes.byref(cache), *a)
+    assert st(c, P, P, 0, None, None, P, P, 1, 1, None) == 0    # nothing to do
+    assert st(c, P, P, -1, None, None, P, P, 1, 1, None) == -1  # negative tokens
+    assert st(c, P, P, 2, None, None, P, P, 1, 1, None) == -1   # decode form: T != B
+    assert st(c, P + 8, P, 1, None, None, P, P, 1, 1, None) == -1  # latent rows not 16-byte aligned
+    assert st(pkv._MLACacheT(16, 32, 64, 128, 4, 16, 256, 64), P, P, 1, None, None, P, P, 1, 1, None) == -2
+    assert st(pkv._MLACacheT(16, 32, 64, 128, 4, 24, 512, 64), P, P, 1, None, None, P, P, 1, 1, None) == -2
+    assert st(pkv._MLACacheT(16, 32, 0, 128, 4, 16, 512, 64), P, P, 1, None, None, P, P, 1, 1, None) == -1
+    dec = lambda *a: lib.pkv_mla_decode(*a)
+    assert dec(P, P, 16, ctypes.byref(c), P, 8, P, 1, 1.0, None, None, P, 1 << 30, 0, None) == -1  # no out
+    assert dec(P, P, 0, ctypes.byref(c), P, 8, P, 1, 1.0, P, None, P, 1 << 30, 0, None) == -1  # no heads
+    need = lib.pkv_mla_decode_workspace_size(64, 16, 128, 64, 0)
+    assert need > 0
+    c64 = pkv._MLACacheT(16, 32, 64, 128, 4, 64, 512, 64)
+    assert dec(P, P, 16, ctypes.byref(c64), P, 128, P, 64, 1.0, P, None, P, need - 1, 0, None) == -3
+    assert dec(P, P, 16, ctypes.byref(c64), P, 128, P, 0, 1.0, P, None, None, 0, 0, None) == 0  # empty batch

@@ -1,0 +1,229 @@
+"""GPU parity of the paged MLA (latent cache) path with the oracle: the store bit-exact (codes and
+scales), the decode within 1e-2 (max abs and norm-relative) and its lse within the bound the query
+rounding of the int8 score MFMA allows."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+import paged_kv_cache_c8_amd as pkv
+from tests.helpers import attention_close, bits_to_f32
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def bits(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+class MlaRun:
+    """One MLA workload on the GPU: the prior tokens stored in one prefill-style call, then one new
+    token per sequence (the decode step's store), then the decode."""
+
+    def __init__(self, w):
+        self.w = w
+        self.t = gen.gen_mla_tensors(w, device=DEV)
+        self.cache = pkv.MLACache(w.num_blocks, w.block_size, device=DEV)
+        self.bt = torch.as_tensor(w.block_table, device=DEV)
+        self.ctx = torch.as_tensor(w.context_lengths, device=DEV)
+
+    def store(self):
+        w, t = self.w, self.t
+        prior = w.prior_lengths
+        cu_ctx = w.cu_context
+        pri = np.concatenate([np.arange(cu_ctx[b], cu_ctx[b] + prior[b]) for b in range(w.batch)] + [[]]).astype(np.int64)
+        new = np.array([cu_ctx[b + 1] - 1 for b in range(w.batch) if w.context_lengths[b] > 0], np.int64)
+        pi = torch.as_tensor(pri, device=DEV)
+        cu_p = np.zeros(w.batch + 1, np.int32)
+        cu_p[1:] = np.cumsum(prior)
+        if len(pri):
+            pkv.mla_store_c8(self.cache, t["latent_all"].index_select(0, pi), t["rope_all"].index_select(0, pi),
+                             cu_q_lens=torch.as_tensor(cu_p, device=DEV),
+                             context_lengths=torch.as_tensor(prior, device=DEV), block_table=self.bt)
+        # decode step: one token per sequence (rows of empty sequences are never read)
+        rows = np.array([cu_ctx[b + 1] - 1 if w.context_lengths[b] > 0 else 0 for b in range(w.batch)], np.int64)
+        ri = torch.as_tensor(rows, device=DEV)
+        lat = t["latent_all"].index_select(0, ri).contiguous() if w.batch else t["latent_all"][:0]
+        rot = t["rope_all"].index_select(0, ri).contiguous() if w.batch else t["rope_all"][:0]
+        pkv.mla_store_c8(self.cache, lat, rot, context_lengths=self.ctx, block_table=self.bt)
+        return new
+
+    def decode(self, split_tokens=0, scale=None):
+        w = self.w
+        lse = torch.full((w.batch, w.num_heads), 7.0, dtype=torch.float32, device=DEV)
+        out = pkv.mla_decode(self.t["q_latent"], self.t["q_rope"], self.cache, self.bt, self.ctx,
+                             w.softmax_scale if scale is None else scale, lse_out=lse, split_tokens=split_tokens)
+        return out, lse
+
+
+def oracle_cache(w, t, seqs=None):
+    """The oracle's cache for the sequences ``seqs`` (all by default), stored in one call."""
+    c = oracle.MLAHostCache(w.num_blocks, w.block_size, w.latent_dim, w.rope_dim)
+    seqs = range(w.batch) if seqs is None else seqs
+    cu_ctx = w.cu_context
+    idx = np.concatenate([np.arange(cu_ctx[b], cu_ctx[b + 1]) for b in seqs] + [[]]).astype(np.int64)
+    ctx = w.context_lengths[list(seqs)]
+    cu = np.zeros(len(ctx) + 1, np.int32)
+    cu[1:] = np.cumsum(ctx)
+    ii = torch.as_tensor(idx, device=t["latent_all"].device)
+    oracle.mla_store(c, bits(t["latent_all"].index_select(0, ii)), bits(t["rope_all"].index_select(0, ii)),
+                     cu_q_lens=cu, context_lengths=ctx, block_table=w.block_table[list(seqs)])
+    return c
+
+
+def lse_slack(hc, q_lat_bits, q_rope_bits, w, seqs, scale):
+    """Per (sequence, head) bound of the lse error the query rounding allows: each part of a query
+    row (latent, rotary) is rounded to multiples of step = 2^(e - 14), e the exponent with its
+    max|q| in [2^(e-1), 2^e); key t's logit moves by at most |scale| * (s_c,t * step_c / 2 *
+    sum|c_t| + s_r,t * step_r / 2 * sum|r_t|), the lse by at most the largest move."""
+    out = np.zeros((len(seqs), w.num_heads))
+    for j, b in enumerate(seqs):
+        n = int(w.context_lengths[b])
+        if n == 0:
+            continue
+        pos = np.arange(n)
+        blk = w.block_table[b, pos // w.block_size]
+        off = pos % w.block_size
+        ac = np.abs(hc.latent[blk, off].astype(np.float64)).sum(axis=1) * hc.latent_scale[blk, off]
+        ar = np.abs(hc.rope[blk, off].astype(np.float64)).sum(axis=1) * hc.rope_scale[blk, off]
+        for part, a_t, qb in (("c", ac, q_lat_bits[j]), ("r", ar, q_rope_bits[j])):
+            m = np.abs(bits_to_f32(qb).astype(np.float64)).max(axis=1)  # [H]
+            e = np.frexp(m)[1]
+            step = np.where(m > 0, np.ldexp(1.0, e - 14), 0.0)
+            out[j] += abs(scale) * step / 2 * a_t.max()
+    return out
+
+
+def check_decode(r, out, lse, seqs, hc=None):
+    w = r.w
+    if hc is None:
+        hc = oracle_cache(w, r.t, seqs)
+    sub_bt = w.block_table[list(seqs)]
+    qi = torch.as_tensor(np.asarray(seqs, np.int64), device=DEV)
+    ql, qr = bits(r.t["q_latent"].index_select(0, qi)), bits(r.t["q_rope"].index_select(0, qi))
+    _, o64, olse = oracle.mla_decode(hc, ql, qr, sub_bt, w.context_lengths[list(seqs)], w.softmax_scale,
+                                     nthreads=8)
+    got = out.index_select(0, qi).float().cpu().numpy().astype(np.float64)
+    max_abs, rel, elem_ok = attention_close(got, o64)
+    print(f"{w.name}: max_abs={max_abs:.3e} rel={rel:.3e}", flush=True)
+    assert max_abs <= 1e-2 and rel <= 1e-2 and elem_ok
+    gl = lse.index_select(0, qi).cpu().numpy().astype(np.float64)
+    fin = np.isfinite(olse)
+    assert np.array_equal(np.isfinite(gl), fin)
+    tol = 1e-4 + 1e-5 * np.abs(np.where(fin, olse, 0.0)) + lse_slack(hc, ql, qr, w, seqs, w.softmax_scale)
+    assert np.all(np.abs(gl[fin] - olse[fin]) <= tol[fin])
+    empty = ~fin
+    assert np.all(got[empty] == 0)
+
+
+def test_store_bit_exact():
+    w = gen.mla_workload("store", batch=4, num_heads=16, block_size=16, context_lengths=[1, 37, 100, 16], seed=1)
+    r = MlaRun(w)
+    r.store()
+    torch.cuda.synchronize()
+    hc = oracle_cache(w, r.t)
+    assert np.array_equal(r.cache.latent.cpu().numpy(), hc.latent)
+    assert np.array_equal(r.cache.rope.cpu().numpy(), hc.rope)
+    assert np.array_equal(r.cache.latent_scale.cpu().numpy().view(np.uint32), hc.latent_scale.view(np.uint32))
+    assert np.array_equal(r.cache.rope_scale.cpu().numpy().view(np.uint32), hc.rope_scale.view(np.uint32))
+
+
+def test_store_slot_mapping_and_skips():
+    w = gen.mla_workload("slots", batch=2, num_heads=16, block_size=32, context_lengths=[40, 9], seed=2)
+    t = gen.gen_mla_tensors(w, device=DEV)
+    slots = []
+    for b in range(w.batch):
+        for p in range(int(w.context_lengths[b])):
+            slots.append(int(w.block_table[b, p // 32]) * 32 + p % 32)
+    sm = np.array(slots[:20] + [-1, -1] + slots[20:], np.int64)
+    lat = torch.cat([t["latent_all"][:20], torch.ones(2, 512, dtype=torch.bfloat16, device=DEV), t["latent_all"][20:]])
+    rot = torch.cat([t["rope_all"][:20], torch.ones(2, 64, dtype=torch.bfloat16, device=DEV), t["rope_all"][20:]])
+    c = pkv.MLACache(w.num_blocks, 32, device=DEV)
+    pkv.mla_store_c8(c, lat.contiguous(), rot.contiguous(), slot_mapping=torch.as_tensor(sm, device=DEV))
+    torch.cuda.synchronize()
+    hc = oracle_cache(w, t)
+    assert np.array_equal(c.latent.cpu().numpy(), hc.latent) and np.array_equal(c.rope.cpu().numpy(), hc.rope)
+    assert np.array_equal(c.latent_scale.cpu().numpy().view(np.uint32), hc.latent_scale.view(np.uint32))
+    assert np.array_equal(c.rope_scale.cpu().numpy().view(np.uint32), hc.rope_scale.view(np.uint32))
+
+
+CASES = [
+    # block size, heads, context lengths, split_tokens (0: the library's plan)
+    (16, 16, [37, 100], 0),
+    (16, 16, [37, 100], 64),
+    (64, 16, [1, 63, 64, 65, 130, 1000], 0),
+    (64, 16, [1, 63, 64, 65, 130, 1000], 100000),
+    (16, 8, [300, 17], 128),
+    (32, 32, [700, 5], 256),
+    (128, 128, [513, 129], 0),
+    (16, 16, [0, 50, 0], 0),
+    (16, 16, [0, 50, 0], 64),
+    (128, 24, [2000], 192),
+]
+
+
+@pytest.mark.parametrize("bs,heads,ctx,split", CASES)
+def test_decode_matches_oracle(bs, heads, ctx, split):
+    w = gen.mla_workload(f"mla-{bs}-{heads}-{len(ctx)}-{split}", batch=len(ctx), num_heads=heads, block_size=bs,
+                         context_lengths=ctx, seed=bs + heads + split, softmax_scale=1.0 / np.sqrt(192.0))
+    r = MlaRun(w)
+    r.store()
+    out, lse = r.decode(split_tokens=split)
+    torch.cuda.synchronize()
+    check_decode(r, out, lse, list(range(w.batch)))
+
+
+def test_decode_split_count_agreement_and_determinism():
+    """One split against many: they differ only in rounding (the weights enter the P.V products
+    as fp16, relative rounding <= 2^-11 against a running max that depends on the split
+    boundaries; the output is rounded to bf16, one step <= 2^-7 relative), and the lse is fp32; a
+    repeated call is bit-identical."""
+    w = gen.mla_workload("splits", batch=3, num_heads=16, block_size=64, context_lengths=[900, 2000, 64], seed=9)
+    r = MlaRun(w)
+    r.store()
+    o1, l1 = r.decode(split_tokens=100000)
+    o2, l2 = r.decode(split_tokens=128)
+    o3, l3 = r.decode(split_tokens=128)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o3) and torch.equal(l2, l3)
+    a, b = o1.float(), o2.float()
+    bound = a.abs() * 2.0 ** -7 + 2.0 ** -10 * float(a.abs().max())
+    assert bool(((a - b).abs() <= bound).all()), float(((a - b).abs() - bound).max())
+    assert torch.allclose(l1, l2, rtol=1e-5, atol=1e-5)
+
+
+def test_decode_negative_and_zero_scale():
+    w = gen.mla_workload("scale", batch=2, num_heads=16, block_size=16, context_lengths=[33, 70], seed=12)
+    r = MlaRun(w)
+    r.store()
+    for s in (-0.05, 0.0):
+        out, lse = r.decode(scale=s)
+        torch.cuda.synchronize()
+        w.softmax_scale = s
+        check_decode(r, out, lse, [0, 1])
+
+
+def test_deepseek_shaped_decode_sampled():
+    """The DeepSeek-V3-shaped MLA decode at full size, in the default plan: the store bit-exact over
+    the sampled sequences' pages, their attention against the oracle."""
+    w = gen.make_mla_config(1)
+    r = MlaRun(w)
+    r.store()
+    out, lse = r.decode()
+    torch.cuda.synchronize()
+    seqs = sorted(np.random.default_rng(5).choice(w.batch, 4, replace=False).tolist())
+    print(f"{w.name}: checking sequences {seqs}", flush=True)
+    hc = oracle_cache(w, r.t, seqs)
+    gl, gr = r.cache.latent.cpu().numpy(), r.cache.rope.cpu().numpy()
+    gls, grs = r.cache.latent_scale.cpu().numpy(), r.cache.rope_scale.cpu().numpy()
+    for b in seqs:
+        used = w.block_table[b, : -(-int(w.context_lengths[b]) // w.block_size)]
+        n = int(w.context_lengths[b])
+        flat = lambda a: a[used].reshape(len(used) * w.block_size, *a.shape[2:])[:n]
+        assert np.array_equal(flat(gl), flat(hc.latent)) and np.array_equal(flat(gr), flat(hc.rope))
+        assert np.array_equal(flat(gls).view(np.uint32), flat(hc.latent_scale).view(np.uint32))
+        assert np.array_equal(flat(grs).view(np.uint32), flat(hc.rope_scale).view(np.uint32))
+    check_decode(r, out, lse, seqs, hc=hc)
