@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-baseline sample")
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = auto)")
+    ap.add_argument("--mla", type=int, default=-1,
+                    help="paged MLA (latent cache) workload index instead of the GQA ones (1 = DeepSeek-V3-shaped)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain device copy of known size (for scaling HBM byte counters)")
     return ap.parse_args()
@@ -156,6 +158,9 @@ def main():
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
+    if args.mla >= 0:
+        main_mla(args)
+        return
 
     import torch
 
@@ -311,6 +316,191 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def mla_step_bytes(w):
+    """Algorithmic HBM bytes of one MLA decode step: each key's int8 latent and rotary rows and their
+    two fp32 scales read once (shared by all heads), the queries and outputs, the block-table entries
+    and context lengths; the store reads each new token's bf16 rows and writes its codes and scales."""
+    ctx = w.context_lengths.astype(np.int64)
+    per_key = w.latent_dim + w.rope_dim + 8
+    qo = w.batch * w.num_heads * ((w.latent_dim + w.rope_dim) * 2 + w.latent_dim * 2)
+    meta = int(np.ceil(ctx / w.block_size).sum()) * 4 + w.batch * 4
+    decode = int(ctx.sum()) * per_key + qo + meta
+    t = int((ctx > 0).sum())
+    store = t * ((w.latent_dim + w.rope_dim) * 2 + per_key)
+    return decode, store
+
+
+def main_mla(args):
+    """The paged MLA decode step: store one new latent/rotary token per sequence, then latent
+    attention of every head over the int8 cache (split partials + log-sum-exp merge)."""
+    import torch
+
+    import gen
+    import paged_kv_cache_c8_amd as pkv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = gen.make_mla_config(args.mla)
+    t = gen.gen_mla_tensors(w, device=dev)
+    bt = torch.as_tensor(w.block_table, device=dev)
+    ctx = torch.as_tensor(w.context_lengths, device=dev)
+    prior = w.prior_lengths
+    cu_ctx = w.cu_context
+    pri = torch.as_tensor(np.concatenate([np.arange(cu_ctx[b], cu_ctx[b] + prior[b]) for b in range(w.batch)]),
+                          device=dev)
+    rows = torch.as_tensor(np.array([cu_ctx[b + 1] - 1 for b in range(w.batch)], np.int64), device=dev)
+    cu_p = np.zeros(w.batch + 1, np.int32)
+    cu_p[1:] = np.cumsum(prior)
+    lat_new = t["latent_all"].index_select(0, rows).contiguous()
+    rot_new = t["rope_all"].index_select(0, rows).contiguous()
+    decode_bytes, store_bytes = mla_step_bytes(w)
+    touched = decode_bytes + store_bytes
+    reps = args.replicas or max(1, int(np.ceil(3 * MALL_BYTES / touched)))
+    caches = []
+    for _ in range(reps):
+        c = pkv.MLACache(w.num_blocks, w.block_size, device=dev)
+        pkv.mla_store_c8(c, t["latent_all"].index_select(0, pri), t["rope_all"].index_select(0, pri),
+                         cu_q_lens=torch.as_tensor(cu_p, device=dev), context_lengths=torch.as_tensor(prior, device=dev),
+                         block_table=bt)
+        caches.append(c)
+    del pri
+    ws_bytes = pkv.mla_decode_workspace_size(w.batch, w.num_heads, w.max_blocks_per_seq, w.block_size,
+                                             args.split_tokens)
+    workspace = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(t["q_latent"])
+    plan = pkv.mla_decode_plan(w.batch, w.num_heads, w.max_blocks_per_seq, w.block_size, args.split_tokens)
+
+    def store(c):
+        pkv.mla_store_c8(c, lat_new, rot_new, context_lengths=ctx, block_table=bt)
+
+    def decode(c):
+        pkv.mla_decode(t["q_latent"], t["q_rope"], c, bt, ctx, w.softmax_scale, out=out, workspace=workspace,
+                       split_tokens=args.split_tokens)
+
+    for i in range(args.warmup):
+        store(caches[i % reps])
+        decode(caches[i % reps])
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(args.steps):
+        store(caches[i % reps])
+        decode(caches[i % reps])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        store(caches[i % reps])
+        evs[i][0].record()
+        decode(caches[i % reps])
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    step_s = ms_per_step * 1e-3
+    value = touched / step_s / 1e9
+    achieved = decode_bytes / (dec_ms * 1e-3) / 1e9
+    default_plan = args.split_tokens == 0
+    traffic = traffic_record(f"mla_decode.config{args.mla}") if default_plan else None
+    cpu = None if args.no_cpu_baseline else mla_cpu_baseline(w, t, args.cpu_seconds, touched)
+    res = {
+        "metric": "decode-attn HBM GB/s (% of peak) + tokens/s, int8 paged-KV GQA",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded N(0,1) bf16 latent/rotary rows and queries, random block tables)",
+        "config": {
+            "workload": w.name, "batch": w.batch, "num_heads": w.num_heads, "latent_dim": w.latent_dim,
+            "rope_dim": w.rope_dim, "block_size": w.block_size, "sum_context": int(w.context_lengths.sum()),
+            "new_tokens": w.batch, "cache_replicas": reps, "split_tokens": plan["split_tokens"],
+            "num_splits": plan["num_splits"], "parallelism": "single-gpu",
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(w.batch / step_s, 1),
+        "kv_tokens_per_s": round(float(w.context_lengths.sum()) / step_s, 1),
+        "bytes_per_step": touched,
+        "wall_s_timed": round(wall, 4),
+        "roofline": {
+            "bound": "hbm", "kernel": "pkv_mla_decode (split partial + log-sum-exp merge)",
+            "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": decode_bytes, "avg_launch_ms": round(dec_ms, 5),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def mla_cpu_baseline(w, t, budget_s, touched):
+    """The oracle's MLA store + fp64 latent attention on a bounded sample of the sequences, scaled to
+    the whole batch by context share."""
+    import torch
+
+    import oracle
+
+    model, ncores = cpu_info()
+    nthreads = max(1, min(ncores, 16))
+    bits = lambda x: x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    macs = w.context_lengths.astype(np.float64) * w.num_heads * (2 * w.latent_dim + w.rope_dim)
+    est_rate = 2.0e8 * nthreads
+    sel, acc = [], 0.0
+    for b in range(w.batch):
+        if acc + macs[b] > est_rate * budget_s / 3 and sel:
+            break
+        sel.append(b)
+        acc += macs[b]
+    cu_ctx = w.cu_context
+    ctx_s = w.context_lengths[sel].astype(np.int32)
+    prior_s = np.maximum(ctx_s - 1, 0).astype(np.int32)
+    bt_s = np.ascontiguousarray(w.block_table[sel])
+    dev = t["latent_all"].device
+    pri = torch.as_tensor(np.concatenate([np.arange(cu_ctx[b], cu_ctx[b + 1] - 1) for b in sel]), device=dev)
+    new = torch.as_tensor(np.array([cu_ctx[b + 1] - 1 for b in sel], np.int64), device=dev)
+    hc = oracle.MLAHostCache(w.num_blocks, w.block_size, w.latent_dim, w.rope_dim)
+    cu_p = np.zeros(len(sel) + 1, np.int32)
+    cu_p[1:] = np.cumsum(prior_s)
+    oracle.mla_store(hc, bits(t["latent_all"].index_select(0, pri)), bits(t["rope_all"].index_select(0, pri)),
+                     cu_q_lens=cu_p, context_lengths=prior_s, block_table=bt_s)
+    ln, rn = bits(t["latent_all"].index_select(0, new)), bits(t["rope_all"].index_select(0, new))
+    sel_t = torch.as_tensor(np.array(sel, np.int64), device=dev)
+    ql, qr = bits(t["q_latent"].index_select(0, sel_t)), bits(t["q_rope"].index_select(0, sel_t))
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        s0 = time.perf_counter()
+        oracle.mla_store(hc, ln, rn, context_lengths=ctx_s, block_table=bt_s)
+        oracle.mla_decode(hc, ql, qr, bt_s, ctx_s, w.softmax_scale, nthreads=nthreads, want_f64=False)
+        times.append(time.perf_counter() - s0)
+        if time.perf_counter() - t_start > budget_s * 0.5 or len(times) >= 2000:
+            break
+    sec = float(np.median(times))
+    frac = float(ctx_s.sum()) / float(w.context_lengths.sum())
+    full_step = sec / frac
+    return {
+        "value": round(touched / full_step / 1e9, 4),
+        "unit": "GB/s",
+        "cores": nthreads,
+        "kind": "oracle",
+        "cpu_model": model,
+        "host_cores_visible": ncores,
+        "sample": f"{len(sel)} of {w.batch} sequences ({int(ctx_s.sum())} of {int(w.context_lengths.sum())} "
+                  f"context tokens), {len(times)} timed steps of store + fp64 latent attention; scaled to the "
+                  f"full batch by context share",
+        "sample_step_s": round(sec, 4),
+        "tokens_per_s": round(w.batch / full_step, 2),
+    }
 
 
 def cpu_baseline(w, t, budget_s, touched, new_tokens, window=0):

@@ -276,13 +276,21 @@ int pkv_mla_store_c8(const pkv_mla_cache_t *cache, const void *latent_new, const
 
 /* Bytes of workspace pkv_mla_decode needs (0 when it needs none; 0 also for
  * arguments it rejects).  split_tokens: 0 = the library's plan, else keys per
- * split (rounded up to a multiple of 64).  Depends on the current device's
- * compute-unit count. */
+ * split (rounded up to a multiple of 64).  The library's plan, when the
+ * (sequence, group of 16 heads) items are at most half the decode workgroups
+ * the current device holds at once, is a balanced partition: every 64-key
+ * block of every item in one list, cut into about that many near-equal
+ * segments (the kernel computes each workgroup's segment from
+ * context_lengths, so no host copy of them is needed); otherwise one
+ * workgroup per item (or per fixed split).  Depends on the current device's
+ * compute-unit count and the kernel's occupancy. */
 size_t pkv_mla_decode_workspace_size(int32_t batch, int32_t num_heads, int32_t max_blocks_per_seq,
                                      int32_t block_size, int32_t split_tokens);
 
 /* The split plan pkv_mla_decode would use: keys per split and splits per
- * (sequence, group of 16 heads); either output pointer may be NULL. */
+ * (sequence, group of 16 heads); for the balanced partition, split_len 0 and
+ * num_splits = the workgroups it is planned over.  Either output pointer may
+ * be NULL. */
 int pkv_mla_decode_plan(int32_t batch, int32_t num_heads, int32_t max_blocks_per_seq,
                         int32_t block_size, int32_t split_tokens, int32_t *split_len,
                         int32_t *num_splits);

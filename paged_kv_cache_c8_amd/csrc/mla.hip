@@ -10,7 +10,7 @@
 // Store: one wave per token; 8 latent channels and 1 rotary channel per lane, a cross-lane max
 // for each row's absmax, IEEE division and rintf.
 //
-// Decode: one workgroup of four waves per (sequence, group of 16 heads, key split).  The latent
+// Decode: one workgroup of four waves per (sequence, group of 16 heads, key range).  The latent
 // rows are both the keys and the values, so each 64-key block is read from HBM once and used
 // twice:
 //  * wave w loads keys 16w .. 16w+15 of the block in the A-operand layout of
@@ -30,9 +30,14 @@
 //    j (channel 128w + 8n + j for A row n).  A code c enters as the fp16 value 1152 + c (one byte
 //    permute and one xor per two codes, exact) and 1152 times the weight sums (an all-ones MFMA)
 //    is taken off at the end.
-// Two barriers per block; the latent tile and the weights are double-buffered in LDS.  Keys past
-// the split's end read in-bounds stand-ins (rows of its last page) that get zero weight.
-// Splits are merged by a log-sum-exp pass (mla_merge_kernel).
+// Three barriers per block (the latent tile, the weights and the maxima are single LDS buffers);
+// the key registers are double-buffered (each wave has about two blocks in flight), and the
+// quantized query rows, the same for all four waves, are kept in LDS.  Keys past the range's end read
+// in-bounds stand-ins (rows of its last page) that get zero weight.
+// Key ranges: fixed splits of split_len keys, or (the default) a balanced partition that cuts
+// every block of every (sequence, head group) into as many near-equal segments as the GPU holds
+// workgroups at once, each workgroup finding its own from the context lengths.  The partial
+// results are merged by a log-sum-exp pass (mla_merge_kernel).
 #include "mla_internal.h"
 #include "pkv_device.h"
 
@@ -170,29 +175,137 @@ __device__ __forceinline__ float quant_query(const u32x4* raw, i4* hi, i4* lo, f
 }
 
 struct __align__(16) MlaShared {
-    uint8_t lat[2][MBLK * LROW];  // latent rows of the block (keys x 528 bytes)
-    _Float16 p[2][16][MBLK];      // weights, head-major
-    float mx[2][NW][16];          // per-wave block maximum of each head's logits
-    float vmx[2][NW];             // per-wave largest latent scale
+    uint8_t lat[MBLK * LROW];     // latent rows of the block (keys x 528 bytes)
+    _Float16 p[16][MBLK];         // weights, head-major
+    float mx[NW][16];             // per-wave block maximum of each head's logits
+    float vmx[NW];                // per-wave largest latent scale
     float lsum[NW][16];           // per-wave weight sums, exchanged at the end
+    i4 qhi[QSTEPS][kWave];        // the quantized query rows (B operand of the score MFMA, per
+    i4 qlo[QSTEPS][kWave];        // lane), high and low bytes: the same for every wave
+    int plan[NW][2];              // balanced partition: per-wave partial sums
+    int found[2];                 // balanced partition: the workgroup's sequence and its first slot
 };
+
+// One wave's key registers for a block: A operand rows of the score MFMA (8 latent steps and
+// one rotary step) and the scales of the lane's four score rows.
+struct MlaKRegs {
+    i4 k[QSTEPS];
+    f4 ls, rs;
+};
+
+// Sum over the workgroup (NW waves); every thread gets the total.  Ends with a barrier, so the
+// shared slots can be reused at once.
+__device__ __forceinline__ int wg_sum(int x, int (*red)[2], int slot) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, kWave);
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) red[w][slot] = x;
+    __syncthreads();
+    int t = 0;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) t += red[k][slot];
+    __syncthreads();
+    return t;
+}
+
+// Balanced partition of every key block of every (sequence, head group) item over the W
+// workgroups the GPU holds at once: item i with n_i blocks gets k_i = min(n_i, ceil(n_i Wp / N))
+// contiguous, near-equal segments (N blocks in all; Wp = W - A with A non-empty items, so that
+// the ceilings keep the total within W and the chip runs one round of equally long workgroups).
+// Segments are numbered sequence by sequence, head group by head group.  Workgroup u finds its
+// segment from the context lengths alone (two passes over them); false when u has none.
+__device__ bool mla_balanced_segment(const MlaArgs& a, int u, MlaShared& S, int& b, int& hg, int& t_begin,
+                                     int& t_end, int& kseg, int& first) {
+    const int tid = threadIdx.x;
+    const int W = a.sk_wgs;
+    auto nblk = [&](int c) { return c > 0 ? (c + MBLK - 1) / MBLK : 0; };
+    int n0 = 0;  // blocks of sequence tid (first chunk), kept for the second pass
+    int N = 0, A = 0;
+    for (int c0 = 0; c0 < a.batch; c0 += NW * kWave) {
+        const int bb = c0 + tid;
+        const int nb = bb < a.batch ? nblk(a.ctx[bb]) : 0;
+        if (c0 == 0) n0 = nb;
+        N += wg_sum(nb, S.plan, 0);
+        A += wg_sum(nb > 0 ? 1 : 0, S.plan, 1);
+    }
+    if (N == 0) return false;  // every item is empty: the merge writes the zero rows
+    const int64_t NN = (int64_t)N * a.nhg;
+    const int AA = A * a.nhg;
+    const int64_t Wp = W > 2 * AA ? W - AA : (W > AA ? AA : 1);
+    auto segs = [&](int nb) { return nb > 0 ? (int)min((int64_t)nb, ((int64_t)nb * Wp + NN - 1) / NN) : 0; };
+    int carry = 0;
+    for (int c0 = 0; c0 < a.batch; c0 += NW * kWave) {
+        const int bb = c0 + tid;
+        const int nb = bb < a.batch ? (c0 == 0 ? n0 : nblk(a.ctx[bb])) : 0;
+        const int k = segs(nb) * a.nhg;
+        int x = k;  // inclusive scan over the wave, then over the waves
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int y = __shfl_up(x, d, kWave);
+            if ((tid & (kWave - 1)) >= d) x += y;
+        }
+        const int w = tid / kWave;
+        if ((tid & (kWave - 1)) == kWave - 1) S.plan[w][0] = x;
+        __syncthreads();
+        int off = carry, tot = 0;
+#pragma unroll
+        for (int q = 0; q < NW; ++q) {
+            off += q < w ? S.plan[q][0] : 0;
+            tot += S.plan[q][0];
+        }
+        const int incl = off + x;
+        if (k > 0 && incl - k <= u && u < incl) {
+            S.found[0] = bb;
+            S.found[1] = incl - k;
+        }
+        carry += tot;
+        __syncthreads();
+    }
+    if (u >= carry) return false;
+    b = S.found[0];
+    const int seq_first = S.found[1];
+    const int ctx = a.ctx[b];
+    const int nb = nblk(ctx);
+    kseg = segs(nb);
+    const int off = u - seq_first;
+    hg = off / kseg;
+    const int sg = off - hg * kseg;
+    first = seq_first + hg * kseg;
+    t_begin = (int)((int64_t)nb * sg / kseg) * MBLK;
+    t_end = min(ctx, (int)((int64_t)nb * (sg + 1) / kseg) * MBLK);
+    return true;
+}
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mla_decode_kernel(MlaArgs a, int items) {
     __shared__ MlaShared S;
     const int u = blockIdx.x;
-    const int item = u % items;
-    const int sp = u / items;
-    const int b = item / a.nhg;
-    const int h0 = (item % a.nhg) * 16;
+    int b, hg, t_begin, t_end;
+    int64_t pslot;  // partial slot of this workgroup's output, -1: the output itself
+    if (a.sk_wgs > 0) {
+        int kseg, first;
+        if (!mla_balanced_segment(a, u, S, b, hg, t_begin, t_end, kseg, first)) return;  // uniform
+        if ((int)threadIdx.x == 0 && t_begin == 0) {  // the item's first segment records the item
+            a.seg[2 * (b * a.nhg + hg)] = first;
+            a.seg[2 * (b * a.nhg + hg) + 1] = kseg;
+        }
+        pslot = kseg > 1 ? u : -1;
+    } else {
+        const int item = u % items;
+        const int sp = u / items;
+        b = item / a.nhg;
+        hg = item % a.nhg;
+        const int ctx = a.ctx[b];
+        t_begin = sp * a.split_len;
+        t_end = a.nsplit == 1 ? ctx : min(ctx, t_begin + a.split_len);
+        pslot = a.nsplit > 1 ? u : -1;
+    }
+    const int h0 = hg * 16;
     const int nvalid = min(16, a.heads - h0);
-    const int ctx = a.ctx[b];
-    const int t_begin = sp * a.split_len;
-    const int t_end = a.nsplit == 1 ? ctx : min(ctx, t_begin + a.split_len);
     const int w = threadIdx.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     const int n = lane & 15;  // key row (score A operand), head column (scores, weights, output)
     const int g = lane >> 4;
-    if (t_begin >= t_end) {  // uniform per workgroup
+    if (t_begin >= t_end) {  // uniform per workgroup (fixed splits only)
         if (a.nsplit == 1) {  // a sequence with no key: zero output, lse = -inf
             for (int o = threadIdx.x; o < nvalid * DC; o += blockDim.x)
                 a.out[((int64_t)b * a.heads + h0 + o / DC) * DC + o % DC] = 0;
@@ -203,27 +316,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
 
     // ---- key loads of one block for this wave: key T + 16w + n (the lane's A row), channels
     //      64m + 16g .. of the latent row for m < 8 and 16g .. of the rotary row; the lane's
-    //      scales are those of keys T + 16w + 4g + i (its rows of the score tile)
+    //      scales are those of keys T + 16w + 4g + i (its rows of the score tile).  Two register
+    //      sets: the loads of block k + 2 are issued once block k's codes are in LDS, so every
+    //      wave has about two blocks in flight.
+    //      The page ids (one per wave and block) are loaded one block before the key loads that
+    //      need them, so no key load waits for a block-table round trip.
     const int32_t* btb = a.bt + (int64_t)b * a.mbs;
     const int lastpg = (t_end - 1) >> a.log2bs;
-    i4 kr[QSTEPS];
-    f4 lsv, rsv;
-    auto load_k = [&](int T) {
-        const int64_t pg = (int64_t)btb[min((T + 16 * w) >> a.log2bs, lastpg)] * a.bs;
+    auto page_of = [&](int T) { return btb[min((T + 16 * w) >> a.log2bs, lastpg)]; };
+    auto load_k = [&](int T, int pid, MlaKRegs& R) {
+        const int64_t pg = (int64_t)pid * a.bs;
         const int64_t row = pg + ((T + 16 * w + n) & (a.bs - 1));
         const uint8_t* lp = reinterpret_cast<const uint8_t*>(a.latent) + row * DC + 16 * g;
 #pragma unroll
         for (int m = 0; m < DC / 64; ++m) {
             const u32x4 v = load16(lp + 64 * m);
-            kr[m] = i4{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+            R.k[m] = i4{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
         }
         const u32x4 v = load16(reinterpret_cast<const uint8_t*>(a.rope) + row * DR + 16 * g);
-        kr[DC / 64] = i4{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-        const int64_t srow = pg + ((T + 16 * w + 4 * g) & (a.bs - 1));
-        lsv = *reinterpret_cast<const f4*>(a.ls + srow);
-        rsv = *reinterpret_cast<const f4*>(a.rs + srow);
+        R.k[DC / 64] = i4{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
     };
-    load_k(t_begin);
+    auto load_s = [&](int T, int pid, MlaKRegs& R) {
+        const int64_t pg = (int64_t)pid * a.bs;
+        const int64_t srow = pg + ((T + 16 * w + 4 * g) & (a.bs - 1));
+        R.ls = *reinterpret_cast<const f4*>(a.ls + srow);
+        R.rs = *reinterpret_cast<const f4*>(a.rs + srow);
+    };
+    MlaKRegs R0, R1;
+    {
+        const int p0 = page_of(t_begin);
+        load_k(t_begin, p0, R0);
+        load_s(t_begin, p0, R0);
+    }
+    const int p1 = page_of(t_begin + MBLK);  // (clamped to the range's last page)
+    // pages of the next even and odd blocks' key loads, each loaded two blocks before its use
+    int pe = page_of(t_begin + 2 * MBLK), po = page_of(t_begin + 3 * MBLK);
 
     // ---- query rows (B operand): lane (g, n) holds head h0 + n, channels 64m + 16g .. + 15
     const bool hv = n < nvalid;
@@ -245,6 +372,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     i4 qhi[QSTEPS], qlo[QSTEPS];
     const float rmul_c = quant_query<DC / 64>(qraw, qhi, qlo, sgn, fabsf(a.scale_log2));
     const float rmul_r = quant_query<1>(qraw + 2 * (DC / 64), qhi + DC / 64, qlo + DC / 64, sgn, fabsf(a.scale_log2));
+    // the quantized query is the same for every wave: kept once in LDS instead of in every
+    // wave's registers (room for the second key register set)
+    if (w == 0) {
+#pragma unroll
+        for (int m = 0; m < QSTEPS; ++m) {
+            S.qhi[m][lane] = qhi[m];
+            S.qlo[m][lane] = qlo[m];
+        }
+    }
+    __syncthreads();
+    // the second block's loads, after the raw query registers are free (unconditional: past the
+    // range's end they read stand-ins on its last page)
+    load_k(t_begin + MBLK, p1, R1);
+    load_s(t_begin + MBLK, p1, R1);
 
     const uint32_t ones_w[4] = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
     const h8 ones = __builtin_bit_cast(h8, ones_w);
@@ -257,24 +398,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     for (int j = 0; j < NT; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
     f4 pacc = f4{0.f, 0.f, 0.f, 0.f};
 
-    int bi = 0;
-    for (int T = t_begin; T < t_end; T += MBLK, bi ^= 1) {
+    // one 64-key block at T from register set R; pg: page of block T + 2.  steady: the caller
+    // knows block T + 2 exists (its loads are issued unconditionally)
+    auto block = [&](const bool steady, const int T, MlaKRegs& R, int& pg) {
         // -------------------------------- integer scores of the wave's 16 keys x 16 heads
-        i4 c = i4{0, 0, 0, 0};
+        //                                  (hi and lo as two independent accumulation chains)
+        i4 ch = i4{0, 0, 0, 0}, cl = i4{0, 0, 0, 0};
 #pragma unroll
-        for (int m = 0; m < DC / 64; ++m) c = __builtin_amdgcn_mfma_i32_16x16x64_i8(kr[m], qhi[m], c, 0, 0, 0);
-        c = c * 256;
+        for (int m = 0; m < DC / 64; ++m) {
+            ch = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[m], S.qhi[m][lane], ch, 0, 0, 0);
+            cl = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[m], S.qlo[m][lane], cl, 0, 0, 0);
+        }
+        const i4 c = ch * 256 + cl;  // |score| <= 576 * 128 * 2^14 < 2^31
+        const i4 rh = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[DC / 64], S.qhi[DC / 64][lane], i4{0, 0, 0, 0}, 0, 0, 0);
+        const i4 rl = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[DC / 64], S.qlo[DC / 64][lane], i4{0, 0, 0, 0}, 0, 0, 0);
+        const i4 r = rh * 256 + rl;
+        // -------------------------------- latent rows to LDS (once every wave is done with the
+        //                                  previous block's), loads of the block after next
+        __syncthreads();
+        uint8_t* lrow = &S.lat[(16 * w + n) * LROW + 16 * g];
 #pragma unroll
-        for (int m = 0; m < DC / 64; ++m) c = __builtin_amdgcn_mfma_i32_16x16x64_i8(kr[m], qlo[m], c, 0, 0, 0);
-        i4 r = __builtin_amdgcn_mfma_i32_16x16x64_i8(kr[DC / 64], qhi[DC / 64], i4{0, 0, 0, 0}, 0, 0, 0);
-        r = r * 256;
-        r = __builtin_amdgcn_mfma_i32_16x16x64_i8(kr[DC / 64], qlo[DC / 64], r, 0, 0, 0);
-        // -------------------------------- latent rows to LDS, next block's loads
-        uint8_t* lrow = &S.lat[bi][(16 * w + n) * LROW + 16 * g];
-#pragma unroll
-        for (int m = 0; m < DC / 64; ++m) *reinterpret_cast<i4*>(lrow + 64 * m) = kr[m];
-        const f4 lsc = lsv, rsc = rsv;
-        if (T + MBLK < t_end) load_k(T + MBLK);
+        for (int m = 0; m < DC / 64; ++m) *reinterpret_cast<i4*>(lrow + 64 * m) = R.k[m];
+        const bool more = steady || T + 2 * MBLK < t_end;
+        if (more) load_k(T + 2 * MBLK, pg, R);
 
         // -------------------------------- logits (log2 units) of keys T + 16w + 4g + i
         const bool MASKED = T + MBLK > t_end;
@@ -283,22 +429,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const bool vis = !MASKED || T + 16 * w + 4 * g + i < t_end;
-            x[i] = vis ? __builtin_fmaf((float)c[i] * lsc[i], rmul_c, (float)r[i] * rsc[i] * rmul_r) : -INFINITY;
-            vsl[i] = vis ? lsc[i] : 0.0f;  // stand-in keys' scales never reach a weight
+            x[i] = vis ? __builtin_fmaf((float)c[i] * R.ls[i], rmul_c, (float)r[i] * R.rs[i] * rmul_r) : -INFINITY;
+            vsl[i] = vis ? R.ls[i] : 0.0f;  // stand-in keys' scales never reach a weight
             vm = fmaxf(vm, vsl[i]);
             lmax = fmaxf(lmax, x[i]);
         }
+        // the scales' registers are free once the logits are formed: the next loads go to the same
+        // registers (no instruction moves across this point, so no copy of in-flight loads)
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) {
+            load_s(T + 2 * MBLK, pg, R);
+            pg = page_of(T + 4 * MBLK);
+        }
         lmax = col_max(lmax);
         vm = col_max(vm);
-        if (g == 0) S.mx[bi][w][n] = lmax;
-        if (lane == 0) S.vmx[bi][w] = vm;
+        if (g == 0) S.mx[w][n] = lmax;
+        if (lane == 0) S.vmx[w] = vm;
         __syncthreads();  // the block's latent rows and maxima are visible
 
-        float bmax = S.mx[bi][0][n], vmax = S.vmx[bi][0];
+        float bmax = S.mx[0][n], vmax = S.vmx[0];
 #pragma unroll
         for (int k = 1; k < NW; ++k) {
-            bmax = fmaxf(bmax, S.mx[bi][k][n]);
-            vmax = fmaxf(vmax, S.vmx[bi][k]);
+            bmax = fmaxf(bmax, S.mx[k][n]);
+            vmax = fmaxf(vmax, S.vmx[k]);
         }
         float sf = 1.0f;
         if (vmax > 16.0f * sref) {  // (also the first block: sref == 0)
@@ -320,7 +473,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
             wv[i] = (_Float16)(p * vsl[i] * sinv);
         }
         lsum = lsum * alpha + col_sum(ps);
-        *reinterpret_cast<h4*>(&S.p[bi][n][16 * w + 4 * g]) = wv;
+        *reinterpret_cast<h4*>(&S.p[n][16 * w + 4 * g]) = wv;
         const float factor = alpha * sf;
         if (__any(factor != 1.0f)) {
 #pragma unroll
@@ -332,11 +485,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         // -------------------------------- P.V over the wave's channels, 32 keys per step
 #pragma unroll
         for (int v = 0; v < 2; ++v) {
-            const h8 bq = *reinterpret_cast<const h8*>(&S.p[bi][n][32 * v + 8 * g]);
+            const h8 bq = *reinterpret_cast<const h8*>(&S.p[n][32 * v + 8 * g]);
             uint2 vv[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                vv[j] = *reinterpret_cast<const uint2*>(&S.lat[bi][(32 * v + 8 * g + j) * LROW + CW * w + 8 * n]);
+                vv[j] = *reinterpret_cast<const uint2*>(&S.lat[(32 * v + 8 * g + j) * LROW + CW * w + 8 * n]);
 #pragma unroll
             for (int tj = 0; tj < NT; ++tj) {
                 const uint32_t bsel = tj & 3;
@@ -352,6 +505,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
             }
             pacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, bq, pacc, 0, 0, 0);
         }
+    };
+    // Every block issues the loads of the block after next, past the range's end too (in-bounds
+    // stand-ins on its last page, which the cache holds): with a conditional issue the newest
+    // loads could be any block's, and every wait would drain all of them.
+    for (int T = t_begin;;) {
+        block(true, T, R0, pe);
+        T += MBLK;
+        if (T >= t_end) break;
+        block(true, T, R1, po);
+        T += MBLK;
+        if (T >= t_end) break;
     }
 
     // ---- normalise and write.  Lane (g, n) holds channels 128w + 32g + 8i + j (tile j, row
@@ -362,7 +526,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     const float mul = L > 0.0f ? sref / L : 0.0f;
     const float bias = 1152.0f * pacc[0];
     if (!hv) return;
-    const bool split_mode = a.nsplit > 1;
+    const bool split_mode = pslot >= 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float o[NT];
@@ -377,7 +541,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
             pk.w = f32_to_bf16_rne(o[6]) | (f32_to_bf16_rne(o[7]) << 16);
             *reinterpret_cast<uint4*>(a.out + qrow * DC + ch) = pk;
         } else {
-            float* po = a.part_o + ((int64_t)u * 16 + n) * DC + ch;
+            float* po = a.part_o + (pslot * 16 + n) * DC + ch;
             *reinterpret_cast<f4*>(po) = f4{o[0], o[1], o[2], o[3]};
             *reinterpret_cast<f4*>(po + 4) = f4{o[4], o[5], o[6], o[7]};
         }
@@ -387,29 +551,68 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         if (!split_mode) {
             if (a.lse) a.lse[qrow] = lse2 * kLn2;
         } else {
-            a.part_lse[(int64_t)u * 16 + n] = lse2;
+            a.part_lse[pslot * 16 + n] = lse2;
         }
     }
 }
 
-// Log-sum-exp merge of the splits of one (sequence, head): 128 threads, 4 channels each.
+// Log-sum-exp merge of the partials of one (sequence, head): 128 threads, 4 channels each; the
+// partials are read eight at a time.  Fixed splits: split s of item i in slot s * items + i;
+// balanced partition: the item's segments in slots seg[2i] .. seg[2i] + seg[2i + 1] - 1 (a
+// one-segment item is already written).  A sequence with no key gets a zero row and lse -inf.
 __global__ __launch_bounds__(128) void mla_merge_kernel(MlaArgs a, int items) {
     const int b = blockIdx.x / a.heads;
     const int h = blockIdx.x % a.heads;
     const int item = b * a.nhg + h / 16;
     const int row = h % 16;
     const int ctx = a.ctx[b];
-    const int nact = ctx <= 0 ? 0 : min(a.nsplit, (ctx + a.split_len - 1) / a.split_len);
-    float M = -INFINITY;
-    for (int s = 0; s < nact; ++s) M = fmaxf(M, a.part_lse[((int64_t)s * items + item) * 16 + row]);
+    int nact, first = 0;
+    int64_t stride;
+    if (ctx <= 0) {
+        nact = 0;
+        stride = 0;
+    } else if (a.sk_wgs > 0) {
+        nact = a.seg[2 * item + 1];
+        if (nact <= 1) return;
+        first = a.seg[2 * item];
+        stride = 1;
+    } else {
+        nact = min(a.nsplit, (ctx + a.split_len - 1) / a.split_len);
+        first = item;
+        stride = items;
+    }
     const int c = 4 * threadIdx.x;
+    constexpr int CH = 8;
+    float M = -INFINITY, wsum = 0.0f;
     f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.0f;
-    for (int s = 0; s < nact; ++s) {
-        const int64_t pr = ((int64_t)s * items + item) * 16 + row;
-        const float wt = __builtin_amdgcn_exp2f(a.part_lse[pr] - M);
-        wsum += wt;
-        acc += wt * *reinterpret_cast<const f4*>(a.part_o + pr * DC + c);
+    for (int s0 = 0; s0 < nact; s0 += CH) {
+        float l2[CH];
+        f4 po[CH];
+#pragma unroll
+        for (int q = 0; q < CH; ++q) {
+            if (s0 + q < nact) {
+                const int64_t pr = (first + (int64_t)(s0 + q) * stride) * 16 + row;
+                l2[q] = a.part_lse[pr];
+                po[q] = *reinterpret_cast<const f4*>(a.part_o + pr * DC + c);
+            } else {
+                l2[q] = -INFINITY;
+                po[q] = f4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        float mc = M;
+#pragma unroll
+        for (int q = 0; q < CH; ++q) mc = fmaxf(mc, l2[q]);
+        if (mc == -INFINITY) continue;
+        const float sc = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - mc);
+        M = mc;
+        wsum *= sc;
+        acc *= sc;
+#pragma unroll
+        for (int q = 0; q < CH; ++q) {
+            const float wt = l2[q] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(l2[q] - M);
+            wsum += wt;
+            acc += wt * po[q];
+        }
     }
     const float mul = wsum > 0.0f ? 1.0f / wsum : 0.0f;
     uint2 pk;
@@ -432,15 +635,22 @@ hipError_t launch_mla_store(const MlaArgs& a, hipStream_t stream) {
 
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream) {
     const int64_t items = (int64_t)a.batch * a.nhg;
-    const int64_t units = items * a.nsplit;
+    const int64_t units = a.sk_wgs > 0 ? (items > 0 ? a.sk_wgs + items : 0) : items * a.nsplit;
     if (units == 0) return hipSuccess;
     if (units > 0x7fffffff || (int64_t)a.batch * a.heads > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(mla_decode_kernel, dim3((unsigned)units), dim3(NW * kWave), 0, stream, a, (int)items);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.nsplit == 1) return e;
+    if (e != hipSuccess || (a.sk_wgs == 0 && a.nsplit == 1)) return e;
     hipLaunchKernelGGL(mla_merge_kernel, dim3((unsigned)(a.batch * a.heads)), dim3(DC / 4), 0, stream, a,
                        (int)items);
     return hipGetLastError();
+}
+
+int mla_decode_wgs_per_cu() {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mla_decode_kernel, NW * kWave, 0) != hipSuccess)
+        return 0;
+    return per_cu > 0 ? per_cu : 0;
 }
 
 }  // namespace pkv

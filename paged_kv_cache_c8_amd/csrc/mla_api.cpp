@@ -27,6 +27,19 @@ int device_cus() {
     return n;
 }
 
+std::atomic<int> g_mla_wgs[kMaxDevices];
+
+// Decode workgroups one compute unit of the current device holds at once (cached per device).
+int mla_wgs_per_cu() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int n = g_mla_wgs[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    n = pkv::mla_decode_wgs_per_cu();
+    if (n > 0) g_mla_wgs[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 int ilog2(int x) {
     int l = 0;
@@ -54,6 +67,7 @@ struct MlaPlan {
     int nhg;
     int nsplit;
     int split_len;
+    int sk_wgs;  // > 0: balanced partition over this many workgroups
     size_t ws_bytes;
 };
 
@@ -63,6 +77,22 @@ int mla_plan(int32_t batch, int32_t heads, int32_t mbs, int32_t bs, int32_t spli
     p->nhg = (int)cdiv(heads, pkv::kMlaHeads);
     const int64_t items = (int64_t)batch * p->nhg;
     const int64_t max_ctx = (int64_t)mbs * bs;
+    p->sk_wgs = 0;
+    if (split_tokens == 0 && items > 0) {
+        // balanced partition: all key blocks of all items cut into as many near-equal segments as
+        // the GPU holds workgroups at once (one round, no partly filled second round); only when
+        // the items are few against those workgroups, else one workgroup per item needs no merge
+        const int per_cu = mla_wgs_per_cu();
+        const int64_t W = (int64_t)per_cu * device_cus();
+        if (per_cu > 0 && items * 2 <= W && max_ctx > kMlaBlock) {
+            p->sk_wgs = (int)W;
+            p->split_len = 0;
+            p->nsplit = (int)W;
+            const size_t slots = (size_t)(W + items);
+            p->ws_bytes = slots * pkv::kMlaHeads * (pkv::kMlaLatent + 1) * 4 + (size_t)items * 2 * 4;
+            return PKV_OK;
+        }
+    }
     int64_t L;
     if (split_tokens > 0) {
         L = cdiv(split_tokens, kMlaBlock) * kMlaBlock;
@@ -175,8 +205,15 @@ int pkv_mla_decode(const void* q_latent, const void* q_rope, int32_t num_heads, 
     a.mbs = max_blocks_per_seq;
     a.nsplit = p.nsplit;
     a.split_len = p.split_len;
+    a.sk_wgs = p.sk_wgs;
     a.scale_log2 = scale * 1.4426950408889634f;
-    if (p.nsplit > 1) {
+    if (p.sk_wgs > 0) {
+        float* ws = static_cast<float*>(workspace);
+        const int64_t rows = ((int64_t)p.sk_wgs + (int64_t)batch * p.nhg) * pkv::kMlaHeads;
+        a.part_o = ws;
+        a.part_lse = ws + rows * pkv::kMlaLatent;
+        a.seg = reinterpret_cast<int*>(a.part_lse + rows);
+    } else if (p.nsplit > 1) {
         float* ws = static_cast<float*>(workspace);
         const int64_t rows = (int64_t)batch * p.nhg * p.nsplit * pkv::kMlaHeads;
         a.part_o = ws;

@@ -28,8 +28,9 @@ struct MlaArgs {
     const uint16_t* qr;  // bf16 [B][H][64]
     uint16_t* out;       // bf16 [B][H][512]
     float* lse;          // [B][H] or null
-    float* part_o;       // [nsplit][items][16][512]
-    float* part_lse;     // [nsplit][items][16] (base-2 log-sum-exp)
+    float* part_o;       // fixed splits: [nsplit][items][16][512]; balanced: [slots][16][512]
+    float* part_lse;     // the same rows' base-2 log-sum-exp
+    int* seg;            // balanced partition: per item, its first partial slot and segment count
     // both
     const int32_t* bt;
     const int32_t* ctx;
@@ -41,8 +42,12 @@ struct MlaArgs {
     int mbs;
     int nsplit;
     int split_len;     // keys per split, a multiple of 64
+    int sk_wgs;        // > 0: balanced partition over this many workgroups (split_len unused)
     float scale_log2;  // softmax scale * log2(e)
 };
+
+// Workgroups of the decode kernel one compute unit holds at once (0 if unknown).
+int mla_decode_wgs_per_cu();
 
 hipError_t launch_mla_store(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);

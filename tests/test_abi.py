@@ -146,7 +146,10 @@ def test_mla_plan_and_argument_checks(pkv):
     P = 4096
     p = pkv.mla_decode_plan(64, 16, 128, 64)
     assert p == pkv.mla_decode_plan(64, 16, 128, 64)
-    assert p["split_tokens"] % 64 == 0 and p["num_splits"] * p["split_tokens"] >= 128 * 64
+    # the library's plan: a balanced partition over the GPU's resident workgroups (split length 0),
+    # or, where the device is unknown, fixed splits covering the table
+    assert (p["split_tokens"] == 0 and p["num_splits"] >= 128) or (
+        p["split_tokens"] % 64 == 0 and p["num_splits"] * p["split_tokens"] >= 128 * 64)
     assert pkv.mla_decode_plan(64, 16, 128, 64, split_tokens=1000) == {"split_tokens": 1024, "num_splits": 8}
     assert pkv.mla_decode_plan(2, 16, 7, 16, split_tokens=100000)["num_splits"] == 1
     ws = pkv.mla_decode_workspace_size(64, 16, 128, 64, split_tokens=1024)

@@ -227,3 +227,58 @@ def test_deepseek_shaped_decode_sampled():
         assert np.array_equal(flat(gls).view(np.uint32), flat(hc.latent_scale).view(np.uint32))
         assert np.array_equal(flat(grs).view(np.uint32), flat(hc.rope_scale).view(np.uint32))
     check_decode(r, out, lse, seqs, hc=hc)
+
+
+def test_balanced_partition_garbage_workspace_and_agreement():
+    """The default plan (a balanced partition of every key block over the GPU's resident
+    workgroups) with a workspace full of 0xFF bytes (NaN partials, segment records of -1): items
+    of one segment, of many segments and with no key are all served from what the call itself
+    writes; the result matches the oracle, agrees with one split per sequence to rounding, and a
+    repeated call is bit-identical."""
+    ctx = [0, 1, 64, 65, 3000, 129, 0, 7000, 640, 2]
+    w = gen.mla_workload("balanced", batch=len(ctx), num_heads=32, block_size=32, context_lengths=ctx, seed=31,
+                         softmax_scale=1.0 / np.sqrt(192.0))
+    r = MlaRun(w)
+    r.store()
+    plan = pkv.mla_decode_plan(w.batch, w.num_heads, w.max_blocks_per_seq, w.block_size)
+    assert plan["split_tokens"] == 0 and plan["num_splits"] >= 256, plan  # the balanced partition
+    need = pkv.mla_decode_workspace_size(w.batch, w.num_heads, w.max_blocks_per_seq, w.block_size)
+    ws = torch.full((need,), 255, dtype=torch.uint8, device=DEV)
+    bt, cl = r.bt, r.ctx
+
+    def run(split):
+        lse = torch.full((w.batch, w.num_heads), 7.0, dtype=torch.float32, device=DEV)
+        o = pkv.mla_decode(r.t["q_latent"], r.t["q_rope"], r.cache, bt, cl, w.softmax_scale, lse_out=lse,
+                           workspace=ws if split == 0 else None, split_tokens=split)
+        return o, lse
+
+    o_b, l_b = run(0)
+    torch.cuda.synchronize()
+    check_decode(r, o_b, l_b, list(range(w.batch)))
+    ws.fill_(255)
+    o_b2, l_b2 = run(0)
+    o_1, l_1 = run(100000)
+    torch.cuda.synchronize()
+    assert torch.equal(o_b, o_b2) and torch.equal(l_b, l_b2)
+    a, b = o_1.float(), o_b.float()
+    bound = a.abs() * 2.0 ** -7 + 2.0 ** -10 * float(a.abs().max())
+    assert bool(((a - b).abs() <= bound).all()), float(((a - b).abs() - bound).max())
+    fin = torch.isfinite(l_1)
+    assert torch.equal(fin, torch.isfinite(l_b))
+    assert torch.allclose(l_1[fin], l_b[fin], rtol=1e-5, atol=1e-5)
+
+
+def test_many_sequences_fall_back_to_fixed_splits():
+    """Items too many for a balanced partition (twice the resident workgroups or more) run one
+    workgroup per item with no merge; still within the oracle's tolerance."""
+    rng = np.random.default_rng(77)
+    ctx = rng.integers(1, 200, size=600).tolist()
+    w = gen.mla_workload("many", batch=len(ctx), num_heads=16, block_size=16, context_lengths=ctx, seed=78,
+                         softmax_scale=1.0 / np.sqrt(192.0))
+    plan = pkv.mla_decode_plan(w.batch, w.num_heads, w.max_blocks_per_seq, w.block_size)
+    assert plan["split_tokens"] > 0, plan
+    r = MlaRun(w)
+    r.store()
+    out, lse = r.decode()
+    torch.cuda.synchronize()
+    check_decode(r, out, lse, list(range(0, w.batch, 7)))
