@@ -182,6 +182,7 @@ struct __align__(16) MlaShared {
     float lsum[NW][16];           // per-wave weight sums, exchanged at the end
     i4 qhi[QSTEPS][kWave];        // the quantized query rows (B operand of the score MFMA, per
     i4 qlo[QSTEPS][kWave];        // lane), high and low bytes: the same for every wave
+    int pg[NW][128];              // per wave: page ids of its keys in two 64-block chunks (ring)
     int plan[NW][2];              // balanced partition: per-wave partial sums
     int found[2];                 // balanced partition: the workgroup's sequence and its first slot
 };
@@ -319,11 +320,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     //      scales are those of keys T + 16w + 4g + i (its rows of the score tile).  Two register
     //      sets: the loads of block k + 2 are issued once block k's codes are in LDS, so every
     //      wave has about two blocks in flight.
-    //      The page ids (one per wave and block) are loaded one block before the key loads that
-    //      need them, so no key load waits for a block-table round trip.
+    //      Page ids: each wave keeps those of its keys for two chunks of 64 blocks of the range in
+    //      an LDS ring (entry j = block j mod 128), read with ds_read; chunk c + 1 is loaded at
+    //      the start of chunk c and written to the ring half-way through it.  So no key load
+    //      waits for a block-table round trip, and no wait in the key loop is for a page load.
     const int32_t* btb = a.bt + (int64_t)b * a.mbs;
     const int lastpg = (t_end - 1) >> a.log2bs;
-    auto page_of = [&](int T) { return btb[min((T + 16 * w) >> a.log2bs, lastpg)]; };
+    auto pages_of = [&](int c) {  // (keys past the range's end: its last page, in bounds)
+        const int T = t_begin + MBLK * (64 * c + lane);
+        return btb[min((T + 16 * w) >> a.log2bs, lastpg)];
+    };
+    int pvn = pages_of(1);  // the next chunk's page ids, on their way to the ring
+    S.pg[w][lane] = pages_of(0);
+    S.pg[w][64 + lane] = pvn;
+    __builtin_amdgcn_wave_barrier();
+    auto page_of = [&](int T) { return S.pg[w][((T - t_begin) / MBLK) & 127]; };
     auto load_k = [&](int T, int pid, MlaKRegs& R) {
         const int64_t pg = (int64_t)pid * a.bs;
         const int64_t row = pg + ((T + 16 * w + n) & (a.bs - 1));
@@ -348,9 +359,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         load_k(t_begin, p0, R0);
         load_s(t_begin, p0, R0);
     }
-    const int p1 = page_of(t_begin + MBLK);  // (clamped to the range's last page)
-    // pages of the next even and odd blocks' key loads, each loaded two blocks before its use
-    int pe = page_of(t_begin + 2 * MBLK), po = page_of(t_begin + 3 * MBLK);
+    const int p1 = page_of(t_begin + MBLK);
 
     // ---- query rows (B operand): lane (g, n) holds head h0 + n, channels 64m + 16g .. + 15
     const bool hv = n < nvalid;
@@ -398,9 +407,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     for (int j = 0; j < NT; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
     f4 pacc = f4{0.f, 0.f, 0.f, 0.f};
 
-    // one 64-key block at T from register set R; pg: page of block T + 2.  steady: the caller
-    // knows block T + 2 exists (its loads are issued unconditionally)
-    auto block = [&](const bool steady, const int T, MlaKRegs& R, int& pg) {
+    // one 64-key block at T from register set R.  steady: the loads of block T + 2 are issued
+    // unconditionally (past the range's end they read in-bounds stand-ins)
+    auto block = [&](const bool steady, const int T, MlaKRegs& R) {
+        const int bi = (T - t_begin) / MBLK;
+        if ((bi & 63) == 32) {  // chunk bi/64 + 1 (loaded at the chunk's start) to the ring
+            S.pg[w][((bi / 64 + 1) & 1) * 64 + lane] = pvn;
+            __builtin_amdgcn_wave_barrier();
+        }
+        if ((bi & 63) == 0 && bi > 0) pvn = pages_of(bi / 64 + 1);  // (its ring half is free)
+        const int pg = page_of(T + 2 * MBLK);
         // -------------------------------- integer scores of the wave's 16 keys x 16 heads
         //                                  (hi and lo as two independent accumulation chains)
         i4 ch = i4{0, 0, 0, 0}, cl = i4{0, 0, 0, 0};
@@ -437,10 +453,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         // the scales' registers are free once the logits are formed: the next loads go to the same
         // registers (no instruction moves across this point, so no copy of in-flight loads)
         __builtin_amdgcn_sched_barrier(0);
-        if (more) {
-            load_s(T + 2 * MBLK, pg, R);
-            pg = page_of(T + 4 * MBLK);
-        }
+        if (more) load_s(T + 2 * MBLK, pg, R);
         lmax = col_max(lmax);
         vm = col_max(vm);
         if (g == 0) S.mx[w][n] = lmax;
@@ -510,10 +523,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     // stand-ins on its last page, which the cache holds): with a conditional issue the newest
     // loads could be any block's, and every wait would drain all of them.
     for (int T = t_begin;;) {
-        block(true, T, R0, pe);
+        block(true, T, R0);
         T += MBLK;
         if (T >= t_end) break;
-        block(true, T, R1, po);
+        block(true, T, R1);
         T += MBLK;
         if (T >= t_end) break;
     }

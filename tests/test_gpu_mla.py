@@ -282,3 +282,17 @@ def test_many_sequences_fall_back_to_fixed_splits():
     out, lse = r.decode()
     torch.cuda.synchronize()
     check_decode(r, out, lse, list(range(0, w.batch, 7)))
+
+
+@pytest.mark.parametrize("bs", [16, 128])
+def test_long_ranges_cross_page_id_chunks(bs):
+    """One workgroup walks more than 128 blocks of 64 keys (its page ids come in chunks of 64
+    blocks): one split over 12000- and 9000-key contexts, and fixed 8192-key splits."""
+    w = gen.mla_workload(f"long-{bs}", batch=2, num_heads=16, block_size=bs, context_lengths=[12000, 9000],
+                         seed=40 + bs, softmax_scale=1.0 / np.sqrt(192.0))
+    r = MlaRun(w)
+    r.store()
+    for split in (1 << 20, 8192):
+        out, lse = r.decode(split_tokens=split)
+        torch.cuda.synchronize()
+        check_decode(r, out, lse, [0, 1])
