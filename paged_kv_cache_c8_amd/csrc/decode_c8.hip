@@ -552,18 +552,23 @@ __device__ __forceinline__ void zero_rows(const DecodeArgs& a, const ItemGeo& it
     }
 }
 
-// Fixed partition: one wave per (item, split of split_len keys).  Items go fastest, so
-// consecutive workgroups go round-robin over the XCDs and each XCD gets an even share of the
-// items whatever the number of empty splits.
+// Fixed partition: one wave per (item, split of split_len keys).  Pairs u = (split, sequence x
+// KV head) go fastest, so consecutive workgroups go round-robin over the XCDs and each XCD gets an
+// even share whatever the number of empty splits; the row groups of one pair (which read the
+// same keys) take workgroups 8 apart, so they run on one XCD at about the same time and all but
+// the first read the keys from its L2.  Workgroup 8 (q nrg + rg) + x takes row group rg of pair
+// 8 q + x.
 template <int D, int MODE, int J, int RT, bool WIN>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 1))) void decode_c8_kernel(DecodeArgs a, int total) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 1))) void decode_c8_kernel(DecodeArgs a, int pairs) {
     constexpr int ROWS = J > 1 ? 16 / J : 16 * RT;
     __shared__ int bt_s[MAX_SPLIT_PAGES];
     const int wi = blockIdx.x;
-    if (wi >= total) return;
-    const int items = total / a.nsplit;
-    const int s = wi / items;
-    const int item = wi % items;
+    const int rest = wi >> 3;
+    const int u = (rest / a.nrg) * 8 + (wi & 7);
+    if (u >= pairs) return;
+    const int nbh = pairs / a.nsplit;
+    const int s = u / nbh;
+    const int item = (u % nbh) * a.nrg + rest % a.nrg;
     const ItemGeo it = item_geo<ROWS, WIN>(a, item);
     if (it.nvalid <= 0) return;
     if (it.kmax <= 0) {
@@ -783,9 +788,10 @@ hipError_t launch_one_w(const DecodeArgs& a, int batch, hipStream_t stream) {
         hipLaunchKernelGGL((merge_sk_kernel<D, ROWS>), dim3((unsigned)items), dim3(threads), 0, stream, a);
         return hipGetLastError();
     }
-    const int64_t grid = items * a.nsplit;
+    const int64_t pairs = (int64_t)batch * a.hkv * a.nsplit;  // (split, sequence x KV head)
+    const int64_t grid = (pairs + 7) / 8 * 8 * a.nrg;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_c8_kernel<D, MODE, J, RT, WIN>), dim3((unsigned)grid), dim3(64), 0, stream, a, (int)grid);
+    hipLaunchKernelGGL((decode_c8_kernel<D, MODE, J, RT, WIN>), dim3((unsigned)grid), dim3(64), 0, stream, a, (int)pairs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     return launch_merge(a, batch, D, ROWS, stream);

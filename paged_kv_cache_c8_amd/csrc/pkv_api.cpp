@@ -106,8 +106,13 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
             p->rg = 1;
             p->rows_per_item = 8;
         } else {
+            // 16-row groups for chunks of decode size (up to 96 rows: the 32-row variant needs
+            // more than 256 registers, one wave per SIMD, the 16-row one keeps two; the groups of
+            // one (sequence, KV head) run on one XCD at about the same time, so their repeated
+            // key reads come from its L2); 32-row groups for prompts, where the matrix-core work
+            // per key read dominates (both measured on MI355X)
             p->classes = 1;
-            p->rg = rows <= 16 ? 1 : 2;
+            p->rg = rows <= 96 ? 1 : 2;
             p->rows_per_item = 16 * p->rg;
         }
         p->nrg = (int)cdiv(rows, p->rows_per_item);
@@ -157,14 +162,17 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
         L = cdiv(opts->split_tokens, 128) * 128;
     } else {
         // Aim for ~16 (int8-score kernel: ~11) workgroups per compute unit counting every
-        // (possibly empty) split, with partitions of 256..2048 keys: long enough to amortise the
-        // per-workgroup query load and partial write, short enough to spread a few long sequences
-        // over the whole chip.
+        // (possibly empty) split, with partitions of 256..2048 keys (bf16 matrix-core kernel:
+        // ..4096, measured faster on many mid-length sequences: fewer waves than the GPU holds
+        // at once instead of a second, partly filled round): long enough to amortise the
+        // per-workgroup query load and partial write, short enough to spread a few long
+        // sequences over the whole chip.
         const int64_t target = (kernel == 3 ? 11LL : 16LL) * device_cus();
         const int64_t want_splits = items > 0 ? (target + items - 1) / items : 1;
         L = cdiv(cdiv(max_ctx, want_splits), 128) * 128;
         if (L < 256) L = 256;
-        if (L > 2048) L = 2048;
+        const int64_t cap = kernel == 2 ? 4096 : 2048;
+        if (L > cap) L = cap;
     }
     if (L > kMaxSplit) L = kMaxSplit;
     if (L >= max_ctx) L = cdiv(max_ctx, 128) * 128;
