@@ -11,8 +11,9 @@
 // head's group); the keys of the split are walked in blocks of 32, the next block's K, V and
 // scales in flight while the current one computes.
 //
-//   scores  S^T (keys x rows) = K . Q^T: K is the A operand - lane (rho, kg) holds 32 (int8) /
-//           16 (bf16) contiguous bytes of one token-major K row - and the query tile is B.  The
+//   scores  S^T (keys x rows) = K . Q^T: K is the A operand - lane (rho, kg) holds 32 contiguous
+//           bytes (int8) or four 16-byte pieces 64 bytes apart (bf16: the lane groups of a row
+//           read 64 contiguous bytes per load) of one token-major K row - and the query tile is B.  The
 //           key behind row slot rho of score tile u is 8*(rho/4) + 4u + rho%4, so that in the
 //           output lane (n, g) holds keys 8g .. 8g+7 of query row n.  int8 codes become fp16 exactly
 //           (byte permute into 0x64xx, subtract 1152); the query row is pre-scaled by a power of two
@@ -133,8 +134,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     const int t_end = min(t_begin + a.split_len, kmax);
     const int lo_hi = win_lo(a.window, prior + (r0 + nvalid - 1) / a.g);
 
-    // ---- query tiles (B operand of the score MFMA): lane (n, g) holds row n's channels
-    //      g*8*KS .. +8*KS, k-step m taking the 8 channels g*8*KS + 8m .. +8.
+    // ---- query tiles (B operand of the score MFMA): lane (n, g) holds 8 channels of row n per
+    //      k-step m, the same channels its K operand holds (below).
     //      int8 pages: the K operand carries 1152 + code, so every score carries 1152 * sum(q) of
     //      its row in excess; qbias holds that amount (the row's fp16 values summed in fp32).
     uint32_t qb[RT][C::KS][4];
@@ -152,10 +153,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         causal |= lim[rt] < t_end - 1;
         uint32_t raw[C::KS][4];
         if (rv) {
-            const uint16_t* qp = a.q + ((int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g) * D + g * 8 * C::KS;
+            // k-step m: channels g*8*KS + 8m .. (int8 pages) or 32m + 8g .. (bf16 pages, whose K
+            // loads then read 64 contiguous bytes of a row per lane group and instruction)
+            const uint16_t* qp = a.q + ((int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g) * D +
+                                 (MODE == 2 ? g * 8 : g * 8 * C::KS);
 #pragma unroll
             for (int m = 0; m < C::KS; ++m) {
-                const u32x4 w = load16(qp + 8 * m);
+                const u32x4 w = load16(qp + (MODE == 2 ? 32 : 8) * m);
                 raw[m][0] = w.x; raw[m][1] = w.y; raw[m][2] = w.z; raw[m][3] = w.w;
             }
         } else {
@@ -225,7 +229,11 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     const int64_t page_bytes = (int64_t)a.hkv * a.bs * D * C::ESZ;  // one physical block, all heads
     const int64_t head_bytes = (int64_t)h * a.bs * D * C::ESZ;
     const int krow_off = 8 * (rho >> 2) + (rho & 3);                 // score tile u adds 4u
-    const int k_lane_bytes = kg * C::KB;
+    // bf16 pages: lane group kg holds channels 32m + 8kg .. of k-step m (bytes 64m + 16kg ..), so
+    // the four lane groups of a row read 64 contiguous bytes per load; int8 pages: 32 bytes
+    // (channels kg*32 ..) per lane group
+    const int k_lane_bytes = MODE == 2 ? kg * 16 : kg * C::KB;
+    constexpr int K_LOAD_STRIDE = MODE == 2 ? 64 : 16;
     const int v_lane_bytes = n * kVTile * C::ESZ;                    // channel n of each 16-channel tile
 
     auto load_block = [&](int T, BlockRegs<D, MODE>& R) {
@@ -239,7 +247,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
                 int tu = T + krow_off + 4 * u;
                 const uint8_t* kpu = (tu < t_end) ? kp + u * 4 * D * C::ESZ : kp;
 #pragma unroll
-                for (int l = 0; l < C::KL; ++l) R.k[u][l] = load16(kpu + 16 * l);
+                for (int l = 0; l < C::KL; ++l) R.k[u][l] = load16(kpu + K_LOAD_STRIDE * l);
             }
         }
         int t0 = T + 8 * g;

@@ -75,6 +75,9 @@ CHUNK_CASES = [
     (0, 128, 16, 4, [70, 9, 200], [5, 9, 16]),
     (0, 64, 32, 2, [300, 31], [12, 31]),
     (2, 128, 16, 8, [50, 129], [4, 13]),
+    # three KV heads x three sequences: pairs of (split, sequence x KV head) not a multiple of 8,
+    # up to five 16-row groups each (the workgroup order puts a pair's row groups 8 apart)
+    (1, 128, 16, 5, [500, 37, 260], [16, 11, 6], 3),
 ]
 
 
@@ -104,9 +107,11 @@ def test_paged_prefill_matches_oracle(mode, d, bs, g, ctx, ql):
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
-@pytest.mark.parametrize("mode,d,bs,g,ctx,ql", CHUNK_CASES)
-def test_chunked_store_and_causal_decode(mode, d, bs, g, ctx, ql, kernel):
-    r = Run(_wl(mode, d, bs, g, ctx, ql, seed=sum(ctx)))
+@pytest.mark.parametrize("case", CHUNK_CASES)
+def test_chunked_store_and_causal_decode(case, kernel):
+    mode, d, bs, g, ctx, ql = case[:6]
+    hkv = case[6] if len(case) > 6 else 2
+    r = Run(_wl(mode, d, bs, g, ctx, ql, hkv=hkv, seed=sum(ctx)))
     r.store_prior()
     r.store_new()
     r.assert_cache_equal()
