@@ -36,6 +36,7 @@
 // the V scales multiply the output channels, and no scale is loaded per key.
 #include "pkv_device.h"
 #include "pkv_internal.h"
+#include "sk_partition.h"
 
 namespace pkv {
 namespace {
@@ -48,7 +49,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int BLK = 64;                  // keys per block (four 16-key subsets)
 constexpr int MAX_SPLIT = 4096;          // keys per split (planner limit)
 constexpr int MAX_SPLIT_PAGES = MAX_SPLIT / 16;
-constexpr int MAX_SK_SEQS = 4096;        // sequences the balanced partition handles (LDS prefix sums)
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
@@ -518,40 +518,6 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
     }
 }
 
-// Rows, keys and output position of work item `item` = (sequence b, KV head h, row group rg).
-struct ItemGeo {
-    int b, h, qlen, qrow0, prior, r0, nrows, nvalid, kmax, kmin;  // keys [kmin, kmax) (kmin 128-aligned)
-};
-template <int ROWS, bool WIN = false>
-__device__ __forceinline__ ItemGeo item_geo(const DecodeArgs& a, int item) {
-    ItemGeo it;
-    const int rg = item % a.nrg;
-    const int bh = item / a.nrg;
-    it.h = bh % a.hkv;
-    it.b = bh / a.hkv;
-    it.qlen = a.cu ? a.cu[it.b + 1] - a.cu[it.b] : 1;
-    it.qrow0 = a.cu ? a.cu[it.b] : it.b;
-    it.prior = a.ctx[it.b] - it.qlen;
-    it.nrows = it.qlen * a.g;
-    it.r0 = rg * ROWS;
-    it.nvalid = min(ROWS, it.nrows - it.r0);
-    it.kmax = it.nvalid > 0 ? it.prior + (it.r0 + it.nvalid - 1) / a.g + 1 : 0;  // keys the last row sees
-    it.kmin = WIN && it.nvalid > 0 ? win_begin(a.window, it.prior + it.r0 / a.g) : 0;  // first key of the range
-    return it;
-}
-
-// zero output and lse = -inf for the rows of an item with no key (a sequence of length 0)
-template <int D>
-__device__ __forceinline__ void zero_rows(const DecodeArgs& a, const ItemGeo& it, int lane) {
-    for (int o = lane; o < it.nvalid * D; o += kWave) {
-        const int j = o / D, d = o % D;
-        const int r = it.r0 + j;
-        const int64_t orow = (int64_t)(it.qrow0 + r / a.g) * a.hq + it.h * a.g + r % a.g;
-        a.out[orow * D + d] = 0;
-        if (d == 0 && a.lse) a.lse[orow] = -INFINITY;
-    }
-}
-
 // Fixed partition: one wave per (item, split of split_len keys).  Pairs u = (split, sequence x
 // KV head) go fastest, so consecutive workgroups go round-robin over the XCDs and each XCD gets an
 // even share whatever the number of empty splits; the row groups of one pair (which read the
@@ -582,194 +548,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 
                                a.nsplit > 1 ? (int64_t)item * a.nsplit + s : -1, bt_s);
 }
 
-// Balanced partition: with N key blocks (64 keys) over all items and a target of W waves, item i
-// with n_i blocks gets k_i = min(n_i, ceil(n_i W / N)) segments of near-equal length (at most
-// max(1, N / W) blocks each), one wave per segment: about W waves, all of about the same length, so the GPU runs one
-// full round of waves instead of rounds of very different fill.  The grid holds W + items waves
-// (an upper bound of the sum of the k_i); the spare ones return at once.  Wave K_i + s (K = prefix
-// sums of k, items in (sequence, KV head, row group) order) takes segment s of item i; a
-// one-segment item writes its result, others leave a partial in slot K_i + s, and segment 0
-// records K_i and k_i in seg[2i], seg[2i + 1] for the merge.  The plan is computed by every wave
-// from the sequence lengths, per sequence (its KV heads share the counts).
+// Balanced partition (sk_partition.h): one wave per segment of the plan.
 template <int D, int MODE, int J, int RT, bool WIN>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 1))) void decode_c8_sk_kernel(DecodeArgs a, int batch) {
     constexpr int ROWS = J > 1 ? 16 / J : 16 * RT;
     __shared__ int bt_s[MAX_SPLIT_PAGES];
     extern __shared__ int kseq[];  // [batch + 1] prefix sums over sequences of their waves
-    const int lane = threadIdx.x;
-    const int W = a.sk_waves;
-    // blocks of row group rg of sequence b (the same for every KV head)
-    auto group_blocks = [&](int b, int rg) {
-        const int qlen = a.cu ? a.cu[b + 1] - a.cu[b] : 1;
-        const int nrows = qlen * a.g;
-        const int r0 = rg * ROWS;
-        if (r0 >= nrows) return 0;
-        const int nvalid = min(ROWS, nrows - r0);
-        const int kmax = a.ctx[b] - qlen + (r0 + nvalid - 1) / a.g + 1;
-        const int kmin = WIN ? win_begin(a.window, a.ctx[b] - qlen + r0 / a.g) : 0;
-        return kmax > 0 ? (kmax - kmin + BLK - 1) / BLK : 0;
-    };
-    // N = total blocks over every item, A = items with at least one block
-    int64_t N = 0;
-    int A = 0;
-    for (int b0 = 0; b0 < batch; b0 += kWave) {
-        int nb = 0, na = 0;
-        if (b0 + lane < batch)
-            for (int rg = 0; rg < a.nrg; ++rg) {
-                const int x = group_blocks(b0 + lane, rg);
-                nb += x;
-                na += x > 0;
-            }
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) {
-            nb += __shfl_xor(nb, d, kWave);
-            na += __shfl_xor(na, d, kWave);
-        }
-        N += nb;
-        A += na;
-    }
-    if (N == 0) return;  // every item is empty: the merge writes the zero rows
-    N *= a.hkv;
-    A *= a.hkv;
-    // ceil rounding adds less than one segment per item: planning for W - A waves keeps the total
-    // within the W waves the GPU holds at once (one round)
-    const int64_t Wp = W > 2 * A ? W - A : (W > A ? A : 1);
-    auto segs = [&](int nb, int64_t NN) {
-        return nb > 0 ? (int)min((int64_t)nb, ((int64_t)nb * Wp + NN - 1) / NN) : 0;
-    };
-    // waves of each sequence (all its KV heads and row groups) and their prefix sums
-    int carry = 0;
-    for (int b0 = 0; b0 < batch; b0 += kWave) {
-        const int b = b0 + lane;
-        int x = 0;
-        if (b < batch)
-            for (int rg = 0; rg < a.nrg; ++rg) x += segs(group_blocks(b, rg), N);
-        x *= a.hkv;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {  // inclusive scan over the wave
-            const int y = __shfl_up(x, d, kWave);
-            if (lane >= d) x += y;
-        }
-        if (b < batch) kseq[b + 1] = carry + x;
-        carry += __shfl(x, kWave - 1, kWave);
-    }
-    if (lane == 0) kseq[0] = 0;
-    __builtin_amdgcn_wave_barrier();
-    const int wid = blockIdx.x;
-    if (wid >= carry) return;
-    int lo = 0, hi = batch;  // kseq[lo] <= wid < kseq[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (kseq[mid] <= wid) lo = mid; else hi = mid;
-    }
-    const int b = lo;
-    // within sequence b: items (h, rg) in order, rg fastest
-    int per_head = 0;
-    for (int rg = 0; rg < a.nrg; ++rg) per_head += segs(group_blocks(b, rg), N);
-    const int off = wid - kseq[b];
-    const int h = off / per_head;
-    int rem = off - h * per_head, rg = 0, k = segs(group_blocks(b, 0), N);
-    int first = kseq[b] + h * per_head;
-    while (rem >= k) {
-        rem -= k;
-        first += k;
-        ++rg;
-        k = segs(group_blocks(b, rg), N);
-    }
-    const int seg = rem;
-    const int item = (b * a.hkv + h) * a.nrg + rg;
-    const ItemGeo it = item_geo<ROWS, WIN>(a, item);
-    const int nb = (it.kmax - it.kmin + BLK - 1) / BLK;
-    const int b0 = (int)((int64_t)nb * seg / k), b1 = (int)((int64_t)nb * (seg + 1) / k);
-    if (seg == 0 && lane == 0) {
-        a.seg[2 * item] = first;
-        a.seg[2 * item + 1] = k;
-    }
-    c8_segment<D, MODE, J, RT, WIN>(a, it.b, it.h, it.qlen, it.qrow0, it.prior, it.r0, it.nvalid, it.kmin + b0 * BLK,
-                               min(it.kmin + b1 * BLK, it.kmax), k == 1 ? -1 : (int64_t)wid, bt_s);
-}
-
-// Merge of the balanced partition: item i's partials sit in slots seg[2i] .. seg[2i] + seg[2i+1] - 1;
-// a one-segment item is already written; an item with no key gets zero rows.  Thread (row j,
-// 8-channel group c), as in the split merge.
-template <int D, int ROWS>
-__global__ __launch_bounds__(1024) void merge_sk_kernel(DecodeArgs a) {
-    constexpr int CG = D / 8;
-    const int item = blockIdx.x;
-    const ItemGeo it = item_geo<ROWS>(a, item);
-    if (it.nvalid <= 0) return;
-    if (it.kmax <= 0) {
-        if (threadIdx.x < kWave) zero_rows<D>(a, it, threadIdx.x);
-        return;
-    }
-    const int k = a.seg[2 * item + 1];
-    if (k <= 1) return;  // one segment: the result is already written
-    const int w0 = a.seg[2 * item], w1 = w0 + k - 1;
-    const int jr = threadIdx.x / CG, cg = threadIdx.x % CG;
-    if (jr >= it.nvalid) return;
-    float M = -INFINITY, wsum = 0.0f;
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-    constexpr int CHM = 8;
-    for (int s0 = w0; s0 <= w1; s0 += CHM) {
-        float l2[CHM];
-        float4 p0[CHM], p1[CHM];
-#pragma unroll
-        for (int c = 0; c < CHM; ++c) {
-            const int ww = s0 + c;
-            if (ww <= w1) {
-                const int64_t row = (int64_t)ww * a.prs + jr;
-                l2[c] = a.part_lse[row];
-                const float4* pp = reinterpret_cast<const float4*>(a.part_o + row * D) + 2 * cg;
-                p0[c] = pp[0];
-                p1[c] = pp[1];
-            } else {
-                l2[c] = -INFINITY;
-                p0[c] = p1[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-        }
-        float mc = M;
-#pragma unroll
-        for (int c = 0; c < CHM; ++c) mc = fmaxf(mc, l2[c]);
-        if (mc == -INFINITY) continue;
-        const float sc = M == -INFINITY ? 0.0f : exp2f(M - mc);
-        M = mc;
-        wsum *= sc;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] *= sc;
-#pragma unroll
-        for (int c = 0; c < CHM; ++c) {
-            const float wt = l2[c] == -INFINITY ? 0.0f : exp2f(l2[c] - M);
-            wsum += wt;
-            acc[0] = fmaf(wt, p0[c].x, acc[0]);
-            acc[1] = fmaf(wt, p0[c].y, acc[1]);
-            acc[2] = fmaf(wt, p0[c].z, acc[2]);
-            acc[3] = fmaf(wt, p0[c].w, acc[3]);
-            acc[4] = fmaf(wt, p1[c].x, acc[4]);
-            acc[5] = fmaf(wt, p1[c].y, acc[5]);
-            acc[6] = fmaf(wt, p1[c].z, acc[6]);
-            acc[7] = fmaf(wt, p1[c].w, acc[7]);
-        }
-    }
-    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-    const int r = it.r0 + jr;
-    const int64_t orow = (int64_t)(it.qrow0 + r / a.g) * a.hq + it.h * a.g + r % a.g;
-    uint16_t* op = a.out + orow * D + 8 * cg;
-    uint32_t pk[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-        pk[e] = f32_to_bf16_rne(acc[2 * e] * inv) | (f32_to_bf16_rne(acc[2 * e + 1] * inv) << 16);
-    if ((reinterpret_cast<uintptr_t>(op) & 15) == 0) {
-        *reinterpret_cast<uint4*>(op) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            op[2 * e] = (uint16_t)(pk[e] & 0xffffu);
-            op[2 * e + 1] = (uint16_t)(pk[e] >> 16);
-        }
-    }
-    if (cg == 0 && a.lse) a.lse[orow] = wsum > 0.0f ? (M + log2f(wsum)) * kLn2 : -INFINITY;
+    SkSegment sg;
+    if (!sk_plan<ROWS, WIN>(a, batch, blockIdx.x, kseq, sg)) return;
+    const ItemGeo& it = sg.it;
+    c8_segment<D, MODE, J, RT, WIN>(a, it.b, it.h, it.qlen, it.qrow0, it.prior, it.r0, it.nvalid, sg.t0, sg.t1,
+                                    sg.pslot, bt_s);
 }
 
 template <int D, int MODE, int J, int RT, bool WIN>
@@ -778,7 +567,7 @@ hipError_t launch_one_w(const DecodeArgs& a, int batch, hipStream_t stream) {
     const int64_t items = (int64_t)batch * a.hkv * a.nrg;
     if (items == 0) return hipSuccess;
     if (a.sk_waves > 0) {  // balanced partition
-        if (batch > MAX_SK_SEQS) return hipErrorInvalidValue;
+        if (batch > SK_MAX_SEQS) return hipErrorInvalidValue;
         const size_t lds = (size_t)(batch + 1) * sizeof(int);
         hipLaunchKernelGGL((decode_c8_sk_kernel<D, MODE, J, RT, WIN>), dim3((unsigned)(a.sk_waves + items)), dim3(64),
                            lds, stream, a, batch);
@@ -843,7 +632,7 @@ int sk_shape(int j, int rt, int batch, bool w) {
 }  // namespace
 
 int decode_c8_waves_per_cu(int head_dim, int classes, int row_tiles, int mode, int batch, bool windowed) {
-    if (batch > MAX_SK_SEQS) return 0;
+    if (batch > SK_MAX_SEQS) return 0;
     const int c = classes, r = row_tiles;
     const bool w = windowed;
     if (head_dim == 64)

@@ -29,6 +29,7 @@
 
 #include "pkv_device.h"
 #include "pkv_internal.h"
+#include "sk_partition.h"
 
 namespace pkv {
 namespace {
@@ -89,49 +90,27 @@ __device__ __forceinline__ float xor16_sum(float x) {
     return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
+// One wave's work: the rows of row group rg of (sequence b, KV head h) over keys
+// [t_seg0, t_seg1) (a split or a balanced segment), walked in ranges of at most MAX_SPLIT keys
+// (each with its block-table slice in LDS; the softmax state carries over).  The result goes to
+// the output (pslot < 0) or to partial slot pslot for the merge.
 template <int D, int MODE, int RT>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
+__device__ __forceinline__ void mfma_segment(const DecodeArgs& a, const int b, const int h, const int rg,
+                                             const int t_seg0, const int t_seg1, const int64_t pslot,
+                                             int* const bt_s) {
     using C = MCfg<D, MODE>;
-    __shared__ int bt_s[MAX_SPLIT_BLOCKS];
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
     const int n = lane & 15;   // query row within a tile (score/P layout), channel (output layout)
     const int g = lane >> 4;   // lane group
 
-    int wi = blockIdx.x;
-    const int s = wi % a.nsplit;
-    wi /= a.nsplit;
-    const int item = wi;
-    const int rg = wi % a.nrg;
-    wi /= a.nrg;
-    const int h = wi % a.hkv;
-    const int b = wi / a.hkv;
-
     const int qlen = a.cu ? a.cu[b + 1] - a.cu[b] : 1;
     const int qrow0 = a.cu ? a.cu[b] : b;
-    const int ctx = a.ctx[b];
-    const int prior = ctx - qlen;
+    const int prior = a.ctx[b] - qlen;
     const int nrows = qlen * a.g;
     const int r0 = rg * (16 * RT);
-    if (r0 >= nrows) return;
     const int nvalid = min(16 * RT, nrows - r0);
-    const int kmax = prior + (r0 + nvalid - 1) / a.g + 1;
-    const int t_begin = win_begin(a.window, prior + r0 / a.g) + s * a.split_len;  // (sliding window)
-
-    if (kmax <= 0) {  // inactive sequence: zero output, lse = -inf
-        if (s == 0) {
-            for (int o = lane; o < nvalid * D; o += kWave) {
-                const int j = o / D, d = o % D;
-                const int r = r0 + j;
-                const int64_t orow = (int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g;
-                a.out[orow * D + d] = 0;
-                if (d == 0 && a.lse) a.lse[orow] = -INFINITY;
-            }
-        }
-        return;
-    }
-    if (t_begin >= kmax) return;
-    const int t_end = min(t_begin + a.split_len, kmax);
+    int t_begin = t_seg0, t_end = t_seg1;  // the current range (set per range below)
     const int lo_hi = win_lo(a.window, prior + (r0 + nvalid - 1) / a.g);
 
     // ---- query tiles (B operand of the score MFMA): lane (n, g) holds 8 channels of row n per
@@ -201,11 +180,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     }
     causal = __any(causal);
 
-    // ---- block-table slice of the split (the wave reads back its own LDS writes in order)
-    const int blk0 = t_begin >> a.log2bs;
-    const int nblk = ((t_end - 1) >> a.log2bs) - blk0 + 1;
-    for (int i = lane; i < nblk; i += kWave) bt_s[i] = a.bt[(int64_t)b * a.mbs + blk0 + i];
-    __builtin_amdgcn_wave_barrier();
+    int blk0 = 0;  // first page of the current range's block-table slice
 
     // softmax state per row (lane column n), lazily rescaled: m_ref only moves when a block's max
     // exceeds it by more than 8 (weights stay <= 2^8), s_ref when a V scale exceeds 16x it.
@@ -439,21 +414,32 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     // Two register sets, alternating: the loads of block k+1 stay in flight while block k computes,
     // and no register set is ever copied (a copy would wait for those loads).  Loads past the
     // split's last block read the in-bounds stand-in, so every iteration issues the same loads.
-    BlockRegs<D, MODE> ra, rb;
-    load_block(t_begin, ra);
-    for (int T = t_begin;;) {
-        load_block(T + BLK, rb);
-        process(T, ra);
-        T += BLK;
-        if (T >= t_end) break;
-        load_block(T + BLK, ra);
-        process(T, rb);
-        T += BLK;
-        if (T >= t_end) break;
+    for (int tb = t_seg0; tb < t_seg1; tb += MAX_SPLIT) {
+        t_begin = tb;
+        t_end = min(tb + MAX_SPLIT, t_seg1);
+        if (tb != t_seg0) __builtin_amdgcn_wave_barrier();  // the previous range's LDS reads are done
+        // block-table slice of the range (the wave reads back its own LDS writes in order)
+        blk0 = t_begin >> a.log2bs;
+        const int nblk = ((t_end - 1) >> a.log2bs) - blk0 + 1;
+        for (int i = lane; i < nblk; i += kWave) bt_s[i] = a.bt[(int64_t)b * a.mbs + blk0 + i];
+        __builtin_amdgcn_wave_barrier();
+
+        BlockRegs<D, MODE> ra, rb;
+        load_block(t_begin, ra);
+        for (int T = t_begin;;) {
+            load_block(T + BLK, rb);
+            process(T, ra);
+            T += BLK;
+            if (T >= t_end) break;
+            load_block(T + BLK, ra);
+            process(T, rb);
+            T += BLK;
+            if (T >= t_end) break;
+        }
     }
 
     // ---- normalise and write: lane (channel n, group g) holds rows 4g+i of every channel tile
-    const bool split_mode = a.nsplit > 1;
+    const bool split_mode = pslot >= 0;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
@@ -466,7 +452,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
             const float bias = MODE == 2 ? 0.0f : 1152.0f * pacc[rt][i];
             const int r = r0 + j;
             const int64_t orow = (int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g;
-            const int64_t prow = ((int64_t)item * a.nsplit + s) * a.prs + j;
+            const int64_t prow = pslot * a.prs + j;
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt) {
                 const float o = (acc[rt][dt][i] - bias) * mul;
@@ -486,9 +472,59 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     }
 }
 
+// Fixed splits: one wave per (item, split of split_len keys), splits fastest.
+template <int D, int MODE, int RT>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
+    __shared__ int bt_s[MAX_SPLIT_BLOCKS];
+    const int s = blockIdx.x % a.nsplit;
+    const int item = blockIdx.x / a.nsplit;
+    const ItemGeo it = item_geo<16 * RT>(a, item);
+    if (it.nvalid <= 0) return;
+    if (it.kmax <= 0) {  // inactive sequence: zero output, lse = -inf
+        if (s == 0) zero_rows<D>(a, it, threadIdx.x);
+        return;
+    }
+    const int t_begin = win_begin(a.window, it.prior + it.r0 / a.g) + s * a.split_len;  // (sliding window)
+    if (t_begin >= it.kmax) return;
+    mfma_segment<D, MODE, RT>(a, it.b, it.h, item % a.nrg, t_begin, min(t_begin + a.split_len, it.kmax),
+                              a.nsplit > 1 ? (int64_t)item * a.nsplit + s : -1, bt_s);
+}
+
+// Balanced partition (sk_partition.h): one wave per segment of the plan, planned over several
+// rounds of the waves the GPU holds when the items are many.
+template <int D, int MODE, int RT, bool WIN>
+__global__ __launch_bounds__(64) void decode_mfma_sk_kernel(DecodeArgs a, int batch) {
+    __shared__ int bt_s[MAX_SPLIT_BLOCKS];
+    extern __shared__ int kseq[];  // [batch + 1] prefix sums over sequences of their waves
+    SkSegment sg;
+    if (!sk_plan<16 * RT, WIN>(a, batch, blockIdx.x, kseq, sg)) return;
+    mfma_segment<D, MODE, RT>(a, sg.it.b, sg.it.h, sg.it.r0 / (16 * RT), sg.t0, sg.t1, sg.pslot, bt_s);
+}
+
 template <int D, int MODE, int RT>
 hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream) {
     const int64_t items = (int64_t)batch * a.hkv * a.nrg;
+    if (a.sk_waves > 0) {  // balanced partition (bf16 pages, head dim 128, one row tile)
+        if constexpr (MODE == 2 && RT == 1 && D == 128) {
+            if (items == 0) return hipSuccess;
+            if (batch > SK_MAX_SEQS || a.sk_waves + items > 0x7fffffff) return hipErrorInvalidValue;
+            const size_t lds = (size_t)(batch + 1) * sizeof(int);
+            if (a.window > 0)
+                hipLaunchKernelGGL((decode_mfma_sk_kernel<D, MODE, RT, true>), dim3((unsigned)(a.sk_waves + items)),
+                                   dim3(64), lds, stream, a, batch);
+            else
+                hipLaunchKernelGGL((decode_mfma_sk_kernel<D, MODE, RT, false>), dim3((unsigned)(a.sk_waves + items)),
+                                   dim3(64), lds, stream, a, batch);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            constexpr int ROWS = 16 * RT;
+            const int threads = ((ROWS * D / 8 + kWave - 1) / kWave) * kWave;
+            hipLaunchKernelGGL((merge_sk_kernel<D, ROWS>), dim3((unsigned)items), dim3(threads), 0, stream, a);
+            return hipGetLastError();
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
     const int64_t grid = items * a.nsplit;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
@@ -520,6 +556,18 @@ hipError_t launch_mode(const DecodeArgs& a, int batch, int rt, int mode, hipStre
 }
 
 }  // namespace
+
+// Head dim 128 only: the head-dim-64 instantiation of the balanced kernel returned wrong outputs
+// (correct lse) whenever several waves ran, and stays switched off (fixed splits serve it).
+int decode_mfma_waves_per_cu(int head_dim, int row_tiles, int mode, int batch, bool windowed) {
+    if (batch > SK_MAX_SEQS || row_tiles != 1 || mode != 2 || head_dim != 128) return 0;
+    const size_t lds = (size_t)(batch + 1) * sizeof(int);
+    int per_cu = 0;
+    const hipError_t e =
+        windowed ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_sk_kernel<128, 2, 1, true>, 64, lds)
+                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_sk_kernel<128, 2, 1, false>, 64, lds);
+    return e == hipSuccess && per_cu > 0 ? per_cu : 0;
+}
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int batch, int head_dim, int row_tiles, int mode,
                               hipStream_t stream) {

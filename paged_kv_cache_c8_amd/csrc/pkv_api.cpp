@@ -157,6 +157,25 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
             return PKV_OK;
         }
     }
+    if (kernel == 2 && mode == 2 && p->rg == 1 && !fixed && items > 0 && (partition == 2 || max_ctx >= 4096)) {
+        // bf16 pages: the same balanced partition, over as many rounds of the waves the GPU holds
+        // as keep the items at most half the segments (sequences of very different lengths
+        // otherwise leave most waves idle behind the longest splits)
+        const int per_cu = pkv::decode_mfma_waves_per_cu(head_dim, p->rg, mode, batch, window > 0);
+        if (per_cu > 0) {
+            const int64_t W = (int64_t)per_cu * device_cus();
+            int64_t rounds = cdiv(2 * items, W);
+            if (rounds < 1) rounds = 1;
+            if (W * rounds + items <= (int64_t)0x7fffffff / 2) {
+                p->sk_waves = (int)(W * rounds);
+                p->split_len = 0;
+                p->nsplit = p->sk_waves;
+                const size_t slots = (size_t)(p->sk_waves + items) * (size_t)p->prs;
+                p->ws_bytes = slots * (size_t)(head_dim + 1) * 4 + (size_t)items * 2 * 4;
+                return PKV_OK;
+            }
+        }
+    }
     int64_t L;
     if (opts && opts->split_tokens > 0) {
         L = cdiv(opts->split_tokens, 128) * 128;

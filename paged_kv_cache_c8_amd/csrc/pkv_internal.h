@@ -71,7 +71,7 @@ struct DecodeArgs {
     int split_len;
     int prs;           // partial rows per (item, split) in part_o / part_lse
     float scale_log2;  // softmax scale * log2(e)
-    int sk_waves;      // > 0: balanced partition over this many waves (int8-score kernel)
+    int sk_waves;      // > 0: balanced partition into about this many segments (waves)
     int32_t* seg;      // balanced partition: first / last wave of each item [items][2]
     int window;        // > 0: sliding window, a query sees only its last `window` keys
 };
@@ -95,6 +95,9 @@ hipError_t launch_decode_c8(const DecodeArgs& a, int batch, int head_dim, int cl
                             int mode, hipStream_t stream);
 // resident waves per compute unit of the balanced-partition kernel (0: not available)
 int decode_c8_waves_per_cu(int head_dim, int classes, int row_tiles, int mode, int batch, bool windowed);
+// Waves of the balanced bf16 matrix-core decode one compute unit holds (0: not available for
+// these arguments).
+int decode_mfma_waves_per_cu(int head_dim, int row_tiles, int mode, int batch, bool windowed);
 // log-sum-exp merge of the split partials; rows_per_item = query rows of one row group
 hipError_t launch_merge(const DecodeArgs& a, int batch, int head_dim, int rows_per_item, hipStream_t stream);
 

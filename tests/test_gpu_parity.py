@@ -349,6 +349,52 @@ def test_balanced_partition_edge_cases():
     r.assert_decode_close(out, lse)
 
 
+def test_bf16_balanced_partition():
+    """The balanced partition of the bf16 matrix-core kernel (segments over several rounds of the
+    GPU's waves; segments longer than one 4096-key range are walked range by range): empty
+    batches, one-block and long sequences together, three KV heads of eight query heads, a
+    sliding window, agreement with fixed splits and between repeated calls; head_dim 64 falls
+    back to fixed splits."""
+    r = Run(_wl(2, 128, 16, 4, [0, 0, 0], seed=41))
+    r.store_prior()
+    r.store_new()
+    out, lse = r.decode(partition=2)
+    torch.cuda.synchronize()
+    assert bool((out == 0).all()) and bool(torch.isneginf(lse).all())
+    r = Run(_wl(2, 128, 16, 4, [1, 5, 64, 65, 9000, 3, 4096, 700, 0, 12000], seed=42))
+    r.store_prior()
+    r.store_new()
+    plan = pkv.decode_plan(r.w.batch, r.w.num_q_heads, r.w.num_kv_heads, 128, r.w.max_blocks_per_seq, 16, 1, 2,
+                           partition=2)
+    assert plan["split_tokens"] == 0 and plan["num_splits"] > 0, plan
+    out, lse = r.decode(partition=2)
+    r.assert_decode_close(out, lse)
+    again, lse2 = r.decode(partition=2)
+    fixed, lf = r.decode(split_tokens=4096)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16)) and torch.equal(lse, lse2)
+    diff = (out.float() - fixed.float()).abs()
+    bound = fixed.float().abs() * 2.0 ** -7 + 2.0 ** -10 * float(fixed.float().abs().max())
+    assert bool((diff <= bound).all()), float((diff - bound).max())
+    fin = torch.isfinite(lf)
+    assert torch.equal(fin, torch.isfinite(lse)) and torch.allclose(lse[fin], lf[fin], rtol=1e-5, atol=1e-5)
+    r = Run(_wl(2, 128, 32, 8, [300, 5000, 33, 2048], hkv=3, seed=43))
+    r.store_prior()
+    r.store_new()
+    out, lse = r.decode(partition=2)
+    r.assert_decode_close(out, lse)
+    out, lse = r.decode(partition=2, window=700)
+    r.assert_decode_close(out, lse, r.oracle_decode(window=700))
+    # head_dim 64: the balanced kernel is switched off there (fixed splits serve the request)
+    r = Run(_wl(2, 64, 32, 8, [300, 5000, 33, 2048], hkv=3, seed=44))
+    r.store_prior()
+    r.store_new()
+    assert pkv.decode_plan(r.w.batch, r.w.num_q_heads, 3, 64, r.w.max_blocks_per_seq, 32, 1, 2,
+                           partition=2)["split_tokens"] > 0
+    out, lse = r.decode(partition=2)
+    r.assert_decode_close(out, lse)
+
+
 def test_planned_partition_matches_fixed_splits():
     """The balanced partition and fixed splits differ only in rounding (fp16 weights against
     different running maxima; bf16 output)."""
@@ -377,6 +423,8 @@ def test_workspace_reused_across_shapes_and_kernels():
         (_wl(1, 64, 32, 8, [700, 1500, 33], seed=23), dict(split_tokens=128)),
         (_wl(0, 128, 16, 4, [3000, 1200, 4096, 64, 900], seed=21), dict(partition=2)),
         (_wl(1, 128, 16, 5, [40, 700, 17, 1500], [16, 9, 16, 3], seed=24), dict(split_tokens=128)),
+        (_wl(2, 128, 16, 4, [3000, 0, 5000, 64, 900], seed=25), dict(partition=2)),
+        (_wl(2, 128, 16, 4, [3000, 0, 5000, 64, 900], seed=25), dict(split_tokens=512)),
     ]
     runs = {}
     for w, kw in cases:
