@@ -169,18 +169,25 @@ typedef struct {
     int32_t split_tokens; /* keys per fixed split-KV partition, rounded up to a multiple
                              of 128, at most 4096; 0 = sized from the shapes.  A value
                              > 0 selects fixed splits.  The balanced partition cuts all
-                             key blocks of all query groups into as many equal ranges as
-                             the GPU holds waves of the kernel at once. */
+                             64-key blocks of all query groups into near-equal ranges,
+                             as many as the GPU holds waves of the kernel at once (or a
+                             multiple of that, several rounds, when the query groups
+                             are not few against those waves). */
     int32_t kernel;       /* 0 = choose (3 for int8 caches, 2 for bf16); 1 = VALU split-KV kernel
                              (dot2 + DPP reductions); 2 = MFMA kernel with fp16 / bf16
                              scores; 3 = MFMA kernel with exact int8 scores and key
                              subsets packed into the tile columns (int8 caches; a bf16
                              cache falls back to 2) */
-    int32_t partition;    /* how the keys are cut into work (int8-score kernel):
-                             0 = planned (balanced for long contexts with few query
-                             groups, else fixed splits); 1 = fixed splits of
-                             split_tokens keys; 2 = balanced partition whenever the
-                             shapes allow it (at most 4096 sequences). */
+    int32_t partition;    /* how the keys are cut into work (kernels 3 and 2):
+                             0 = planned: kernel 3 takes the balanced partition for
+                             contexts of 16384 keys or more with query groups at most
+                             half its resident waves, kernel 2 (bf16 caches, head_dim
+                             128, one 16-row tile) for contexts of 4096 keys or more,
+                             planned over several rounds; otherwise fixed splits;
+                             1 = fixed splits of split_tokens keys; 2 = balanced
+                             partition whenever the shapes allow it (at most 4096
+                             sequences; kernel 2: bf16, head_dim 128, up to 16 query
+                             rows per KV head). */
     int32_t window;       /* > 0: sliding window, each query attends only to its
                              last `window` positions (itself included; the
                              MojoSlidingWindowAttention row of the README's Op
