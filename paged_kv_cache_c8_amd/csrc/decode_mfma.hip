@@ -6,10 +6,12 @@
 // both contractions of every key block run as v_mfma_f32_16x16x32_{f16,bf16} and the vector
 // ALUs only convert codes and do the softmax bookkeeping.
 //
-// One wave per (sequence, KV head, row group, key split); no barriers in the main loop.  A row
-// group is RT tiles of 16 query rows (row r = i * G + g: query i of the chunk, head g of the KV
-// head's group); the keys of the split are walked in blocks of 32, the next block's K, V and
-// scales in flight while the current one computes.
+// One wave per (sequence, KV head, row group, key range): a fixed split, or a segment of the
+// balanced partition (sk_partition.h; bf16 pages at head_dim 128, planned over several rounds of
+// the resident waves); no barriers in the main loop.  A row group is RT tiles of 16 query rows
+// (row r = i * G + g: query i of the chunk, head g of the KV head's group); the keys of the range
+// are walked in blocks of 32, the next block's K, V and scales in flight while the current one
+// computes.
 //
 //   scores  S^T (keys x rows) = K . Q^T: K is the A operand - lane (rho, kg) holds 32 contiguous
 //           bytes (int8) or four 16-byte pieces 64 bytes apart (bf16: the lane groups of a row
