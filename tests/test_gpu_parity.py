@@ -395,6 +395,33 @@ def test_bf16_balanced_partition():
     r.assert_decode_close(out, lse)
 
 
+def test_balanced_partitions_with_causal_chunks():
+    """Causal multi-token chunks through both balanced partitions: bf16 pages with up to 16 rows
+    per KV head (the balanced bf16 kernel), with and without a sliding window; and int8 per-block
+    pages with more row groups than half the resident waves, where a forced balanced partition is
+    planned over several rounds."""
+    r = Run(_wl(2, 128, 16, 4, [300, 5000, 70, 2100, 4], [4, 1, 3, 2, 4], seed=51))
+    r.store_prior()
+    r.store_new()
+    assert pkv.decode_plan(r.w.batch, r.w.num_q_heads, 2, 128, r.w.max_blocks_per_seq, 16, 4, 2,
+                           partition=2)["split_tokens"] == 0
+    out, lse = r.decode(partition=2)
+    r.assert_decode_close(out, lse)
+    out, lse = r.decode(partition=2, window=600)
+    r.assert_decode_close(out, lse, r.oracle_decode(window=600))
+    rng = np.random.default_rng(52)
+    ql = rng.integers(1, 17, size=40)
+    ctx = ql + rng.integers(0, 700, size=40)
+    r = Run(_wl(1, 128, 16, 5, list(ctx), list(ql), hkv=8, seed=53))
+    r.store_prior()
+    r.store_new()
+    plan = pkv.decode_plan(r.w.batch, r.w.num_q_heads, 8, 128, r.w.max_blocks_per_seq, 16, int(ql.max()), 1,
+                           partition=2)
+    assert plan["split_tokens"] == 0 and plan["num_splits"] > 2048, plan  # several rounds
+    out, lse = r.decode(partition=2)
+    r.assert_decode_close(out, lse)
+
+
 def test_planned_partition_matches_fixed_splits():
     """The balanced partition and fixed splits differ only in rounding (fp16 weights against
     different running maxima; bf16 output)."""
