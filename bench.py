@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0
 PEAK_MFMA_F16_TFLOPS = 2500.0  # dense fp16 / bf16 matrix-core peak of MI355X
 MALL_BYTES = 256 * 2 ** 20
+MAX_REPLICAS = 64  # tiny workloads are latency-bound: a few replicas suffice
 
 
 def parse():
@@ -179,7 +180,7 @@ def main():
     q = t["q"]
     decode_bytes, store_bytes = step_bytes(w, args.window)
     touched = decode_bytes + store_bytes
-    reps = args.replicas or max(1, int(np.ceil(3 * MALL_BYTES / touched)))
+    reps = args.replicas or min(MAX_REPLICAS, max(1, int(np.ceil(3 * MALL_BYTES / touched))))
 
     caches = []
     for _ in range(reps):
@@ -357,7 +358,7 @@ def main_mla(args):
     rot_new = t["rope_all"].index_select(0, rows).contiguous()
     decode_bytes, store_bytes = mla_step_bytes(w)
     touched = decode_bytes + store_bytes
-    reps = args.replicas or max(1, int(np.ceil(3 * MALL_BYTES / touched)))
+    reps = args.replicas or min(MAX_REPLICAS, max(1, int(np.ceil(3 * MALL_BYTES / touched))))
     caches = []
     for _ in range(reps):
         c = pkv.MLACache(w.num_blocks, w.block_size, device=dev)
