@@ -103,3 +103,23 @@ def test_sliding_window_full_sizes():
     (1024 and 32768 tokens) shorter than most of their sequences."""
     _check(1, 32, window=1024)
     _check(2, 2, window=32768)
+
+
+def test_bf16_balanced_matches_fixed_splits_everywhere():
+    """The bf16 large-batch decode at full size: the balanced partition (the default plan here)
+    against fixed 4096-key splits on every output element of every sequence and head, within the
+    bound two split plans can differ by (bf16 weights against different running maxima; bf16
+    output), and the lse within 1e-5 relative."""
+    w = gen.make_config(3)
+    r = Run(w, with_oracle=False)
+    r.store_prior()
+    r.store_new()
+    bal, lb = r.decode()
+    fixed, lf = r.decode(split_tokens=4096)
+    torch.cuda.synchronize()
+    a, b = fixed.float(), bal.float()
+    bound = a.abs() * 2.0 ** -7 + 2.0 ** -10 * float(a.abs().max())
+    excess = ((a - b).abs() - bound).max()
+    print(f"{w.name}: balanced vs fixed, largest excess over the bound {float(excess):.3e}", flush=True)
+    assert bool(((a - b).abs() <= bound).all()), float(excess)
+    assert torch.allclose(lb, lf, rtol=1e-5, atol=1e-5)
