@@ -573,9 +573,7 @@ hipError_t launch_one_w(const DecodeArgs& a, int batch, hipStream_t stream) {
                            lds, stream, a, batch);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        const int threads = ((ROWS * D / 8 + kWave - 1) / kWave) * kWave;
-        hipLaunchKernelGGL((merge_sk_kernel<D, ROWS>), dim3((unsigned)items), dim3(threads), 0, stream, a);
-        return hipGetLastError();
+        return launch_merge_sk<D, ROWS>(a, items, stream);
     }
     const int64_t pairs = (int64_t)batch * a.hkv * a.nsplit;  // (split, sequence x KV head)
     const int64_t grid = (pairs + 7) / 8 * 8 * a.nrg;

@@ -520,9 +520,7 @@ hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream) {
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             constexpr int ROWS = 16 * RT;
-            const int threads = ((ROWS * D / 8 + kWave - 1) / kWave) * kWave;
-            hipLaunchKernelGGL((merge_sk_kernel<D, ROWS>), dim3((unsigned)items), dim3(threads), 0, stream, a);
-            return hipGetLastError();
+            return launch_merge_sk<D, ROWS>(a, items, stream);
         } else {
             return hipErrorInvalidValue;
         }

@@ -163,10 +163,18 @@ __device__ __forceinline__ bool sk_plan(const DecodeArgs& a, int batch, int wid,
 
 // Merge of the balanced partition: item i's partials sit in slots seg[2i] .. seg[2i] + seg[2i+1] - 1;
 // a one-segment item is already written; an item with no key gets zero rows.  Thread (row j,
-// 8-channel group c), as in the split merge.
+// 8-channel group c) of thread group g takes the item's segments in chunks of SK_MERGE_CH,
+// chunks g, g + ng, ..., so that a long item has all its partials in flight at once (one group
+// alone would walk them in as many dependent rounds of loads as it has chunks).  With ng > 1 the
+// groups' running (max, weight sum, accumulators) meet in dynamic LDS of 10 * ng * ROWS * D / 8
+// floats and group 0 combines them.
+constexpr int SK_MERGE_CH = 8;
+constexpr int SK_MERGE_THREADS = 1024;
+
 template <int D, int ROWS>
-__global__ __launch_bounds__(1024) void merge_sk_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(SK_MERGE_THREADS) void merge_sk_kernel(DecodeArgs a, int ng) {
     constexpr int CG = D / 8;
+    constexpr int TPR = ROWS * CG;  // threads of one group
     const int item = blockIdx.x;
     const ItemGeo it = item_geo<ROWS>(a, item);
     if (it.nvalid <= 0) return;
@@ -177,14 +185,15 @@ __global__ __launch_bounds__(1024) void merge_sk_kernel(DecodeArgs a) {
     const int k = a.seg[2 * item + 1];
     if (k <= 1) return;  // one segment: the result is already written
     const int w0 = a.seg[2 * item], w1 = w0 + k - 1;
-    const int jr = threadIdx.x / CG, cg = threadIdx.x % CG;
-    if (jr >= it.nvalid) return;
+    const int grp = threadIdx.x / TPR, t = threadIdx.x % TPR;
+    const int jr = t / CG, cg = t % CG;
+    const bool active = grp < ng && jr < it.nvalid;
     float M = -INFINITY, wsum = 0.0f;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-    constexpr int CHM = 8;
-    for (int s0 = w0; s0 <= w1; s0 += CHM) {
+    constexpr int CHM = SK_MERGE_CH;
+    for (int s0 = w0 + grp * CHM; active && s0 <= w1; s0 += ng * CHM) {
         float l2[CHM];
         float4 p0[CHM], p1[CHM];
 #pragma unroll
@@ -224,6 +233,41 @@ __global__ __launch_bounds__(1024) void merge_sk_kernel(DecodeArgs a) {
             acc[7] = fmaf(wt, p1[c].w, acc[7]);
         }
     }
+    if (ng > 1) {
+        // every thread of the workgroup reaches this barrier (the returns above are per item)
+        extern __shared__ float msh[];
+        const int nt = ng * TPR;
+        float* sm = msh;
+        float* sw = msh + nt;
+        float* sa = msh + 2 * nt;
+        if (grp < ng) {
+            sm[threadIdx.x] = M;
+            sw[threadIdx.x] = wsum;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sa[e * nt + threadIdx.x] = acc[e];
+        }
+        __syncthreads();
+        if (grp != 0 || !active) return;
+        float mt = M;
+        for (int g2 = 1; g2 < ng; ++g2) mt = fmaxf(mt, sm[g2 * TPR + t]);
+        if (mt != -INFINITY) {
+            const float sc = M == -INFINITY ? 0.0f : exp2f(M - mt);
+            wsum *= sc;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] *= sc;
+            for (int g2 = 1; g2 < ng; ++g2) {
+                const float mg = sm[g2 * TPR + t];
+                if (mg == -INFINITY) continue;
+                const float f = exp2f(mg - mt);
+                wsum = fmaf(f, sw[g2 * TPR + t], wsum);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = fmaf(f, sa[e * nt + g2 * TPR + t], acc[e]);
+            }
+            M = mt;
+        }
+    } else if (!active) {
+        return;
+    }
     const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
     const int r = it.r0 + jr;
     const int64_t orow = (int64_t)(it.qrow0 + r / a.g) * a.hq + it.h * a.g + r % a.g;
@@ -242,6 +286,21 @@ __global__ __launch_bounds__(1024) void merge_sk_kernel(DecodeArgs a) {
         }
     }
     if (cg == 0 && a.lse) a.lse[orow] = wsum > 0.0f ? (M + log2f(wsum)) * 0.6931471805599453f : -INFINITY;
+}
+
+// Launch of the balanced merge: as many thread groups (a power of two, at most 8 and 1024
+// threads) as an item of average segment count needs to have its chunks in flight together.
+template <int D, int ROWS>
+hipError_t launch_merge_sk(const DecodeArgs& a, int64_t items, hipStream_t stream) {
+    constexpr int TPR = ROWS * D / 8;
+    static_assert(TPR <= SK_MERGE_THREADS, "one group must fit a workgroup");
+    const int64_t avg = ((int64_t)a.sk_waves + 2 * items - 1) / items;  // segments per item, rounded up
+    int ng = 1;
+    while (ng < 8 && (int64_t)ng * SK_MERGE_CH < avg && 2 * ng * TPR <= SK_MERGE_THREADS) ng *= 2;
+    const int threads = ((ng * TPR + kWave - 1) / kWave) * kWave;
+    const size_t lds = ng > 1 ? (size_t)ng * TPR * 10 * sizeof(float) : 0;
+    hipLaunchKernelGGL((merge_sk_kernel<D, ROWS>), dim3((unsigned)items), dim3(threads), lds, stream, a, ng);
+    return hipGetLastError();
 }
 
 }  // namespace
