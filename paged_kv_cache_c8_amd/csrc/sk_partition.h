@@ -176,15 +176,18 @@ __global__ __launch_bounds__(SK_MERGE_THREADS) void merge_sk_kernel(DecodeArgs a
     constexpr int CG = D / 8;
     constexpr int TPR = ROWS * CG;  // threads of one group
     const int item = blockIdx.x;
+    // the item's segment record is read together with its geometry (one round trip less); it is
+    // only used once the item is known to have keys, i.e. once this call's decode has written it
+    const int k = a.seg[2 * item + 1];
+    const int w0 = a.seg[2 * item];
     const ItemGeo it = item_geo<ROWS>(a, item);
     if (it.nvalid <= 0) return;
     if (it.kmax <= 0) {
         if (threadIdx.x < kWave) zero_rows<D>(a, it, threadIdx.x);
         return;
     }
-    const int k = a.seg[2 * item + 1];
     if (k <= 1) return;  // one segment: the result is already written
-    const int w0 = a.seg[2 * item], w1 = w0 + k - 1;
+    const int w1 = w0 + k - 1;
     const int grp = threadIdx.x / TPR, t = threadIdx.x % TPR;
     const int jr = t / CG, cg = t % CG;
     const bool active = grp < ng && jr < it.nvalid;
