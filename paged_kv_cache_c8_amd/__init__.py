@@ -4,6 +4,12 @@ Every step of the store / dequant / decode path runs in the HIP kernels of ``lib
 module passes device pointers (``tensor.data_ptr()``) and the current HIP stream, and raises
 ``PkvError`` on a non-zero status.  PyTorch supplies device memory and streams.
 
+Before any call reaches the library, every tensor argument is checked on the host for dtype, shape,
+contiguity and device (``ValueError`` otherwise): the kernels trust the sizes they are given, so a
+wrong one would make them read or write out of bounds.  Outputs and scratch space that this module
+allocates itself are allocated on the stream the call runs on, so the caching allocator cannot hand
+their memory to other work while the kernels still use it.
+
 There is no fallback: if ``libpkv.so`` has not been built, ``lib()`` raises.
 """
 from __future__ import annotations
@@ -109,6 +115,44 @@ def _stream(stream=None):
     return stream.cuda_stream
 
 
+def _on_stream(stream):
+    """Context in which this module allocates the tensors a call will use on ``stream``."""
+    import contextlib
+
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
+def _want(t, name, dtype, shape=None, ndim=None, optional=False):
+    """Host-side check of one tensor argument: dtype, shape (None entries match any size),
+    contiguity.  The device is checked separately (``_same_device``), after every shape, so that
+    a wrong shape is reported as such whatever the device."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: {t.dim()} dimensions, expected {ndim}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(g) != int(w) for g, w in zip(t.shape, shape)):
+            want = "[" + ", ".join("*" if w is None else str(int(w)) for w in shape) + "]"
+            raise ValueError(f"{name}: shape {list(t.shape)}, expected {want}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _same_device(ref, **tensors):
+    """Every given tensor on the GPU that holds ``ref`` (the cache)."""
+    if ref.device.type != "cuda":
+        raise ValueError(f"the cache is on {ref.device}: libpkv works on GPU memory only")
+    for name, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, the cache on {ref.device}")
+
+
 def _check(status, what):
     if status != 0:
         raise PkvError(status, what)
@@ -154,9 +198,14 @@ class Cache:
         else:
             self.k_scale = k_scale if k_scale is not None else torch.zeros(sshape, dtype=torch.float32, device=device)
             self.v_scale = v_scale if v_scale is not None else torch.zeros(sshape, dtype=torch.float32, device=device)
-        for t in (self.k, self.v, self.k_scale, self.v_scale):
-            if t is not None and not t.is_contiguous():
-                raise ValueError("cache tensors must be contiguous")
+        _want(self.k, "cache.k", dt, shape_k)
+        _want(self.v, "cache.v", dt, shape_v)
+        if sshape is not None:
+            _want(self.k_scale, "cache.k_scale", torch.float32, sshape)
+            _want(self.v_scale, "cache.v_scale", torch.float32, sshape)
+        for t in (self.v, self.k_scale, self.v_scale):
+            if t is not None and t.device != self.k.device:
+                raise ValueError("cache tensors must share one device")
         self._c = _CacheT(self.k.data_ptr(), self.v.data_ptr(), _ptr(self.k_scale), _ptr(self.v_scale),
                           self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim,
                           self.quant_mode)
@@ -169,9 +218,25 @@ class Cache:
 def store_c8(cache: Cache, k_new, v_new, *, slot_mapping=None, cu_q_lens=None, context_lengths=None,
              block_table=None, max_q_len=0, stream=None):
     """Quantize (or copy, mode 2) bf16 ``[T, Hkv, D]`` tokens into the cache."""
+    _want(k_new, "k_new", torch.bfloat16, (None, cache.num_kv_heads, cache.head_dim))
     t = int(k_new.shape[0])
-    batch = 0 if context_lengths is None else int(context_lengths.shape[0])
-    mbs = 0 if block_table is None else int(block_table.shape[1])
+    _want(v_new, "v_new", torch.bfloat16, (t, cache.num_kv_heads, cache.head_dim))
+    if slot_mapping is not None:
+        _want(slot_mapping, "slot_mapping", torch.int64, (t,))
+        batch, mbs = 0, 0
+        for name, x in (("cu_q_lens", cu_q_lens), ("context_lengths", context_lengths), ("block_table", block_table)):
+            if x is not None:
+                raise ValueError(f"{name} must be None when slot_mapping is given")
+    else:
+        _want(context_lengths, "context_lengths", torch.int32, ndim=1)
+        batch = int(context_lengths.shape[0])
+        _want(block_table, "block_table", torch.int32, (batch, None))
+        mbs = int(block_table.shape[1])
+        _want(cu_q_lens, "cu_q_lens", torch.int32, (batch + 1,), optional=True)
+        if cu_q_lens is None and t != batch:
+            raise ValueError(f"without cu_q_lens every sequence stores one token: {t} tokens for {batch} sequences")
+    _same_device(cache.k, k_new=k_new, v_new=v_new, slot_mapping=slot_mapping, cu_q_lens=cu_q_lens,
+                 context_lengths=context_lengths, block_table=block_table)
     st = lib().pkv_store_c8(cache.ref, _ptr(k_new), _ptr(v_new), t, _ptr(slot_mapping), _ptr(cu_q_lens),
                             _ptr(context_lengths), _ptr(block_table), batch, mbs, int(max_q_len),
                             cache.quant_mode, _stream(stream))
@@ -179,15 +244,27 @@ def store_c8(cache: Cache, k_new, v_new, *, slot_mapping=None, cu_q_lens=None, c
 
 
 def dequant(cache: Cache, block_table, context_lengths, *, seq_offsets=None, k_out=None, v_out=None,
-            token_stride=None, head_stride=None, stream=None):
-    """Gather to bf16 rows.  Default outputs: packed ``[sum(ctx), Hkv, D]`` tensors (this shape
-    needs the context lengths on the host, which the call itself never reads)."""
+            token_stride=None, head_stride=None, num_rows=None, stream=None):
+    """Gather to bf16 rows.  Default outputs: packed ``[num_rows, Hkv, D]`` tensors; without
+    ``num_rows`` (the rows the sequences span) the lengths are read back to size them, which waits
+    for the GPU.  Given outputs must hold every row the lengths and offsets address (a precondition,
+    like the lengths themselves: the library does not read them on the host)."""
+    _want(context_lengths, "context_lengths", torch.int32, ndim=1)
+    batch = int(context_lengths.shape[0])
+    _want(block_table, "block_table", torch.int32, (batch, None))
+    _want(seq_offsets, "seq_offsets", torch.int64, (batch,), optional=True)
+    _want(k_out, "k_out", torch.bfloat16, optional=True)
+    _want(v_out, "v_out", torch.bfloat16, optional=True)
+    _same_device(cache.k, block_table=block_table, context_lengths=context_lengths, seq_offsets=seq_offsets,
+                 k_out=k_out, v_out=v_out)
     if k_out is None and v_out is None:
-        rows = int(context_lengths.sum().item()) if seq_offsets is None else \
-            int((seq_offsets + context_lengths.to(seq_offsets.dtype)).max().item())
-        k_out = torch.empty((max(rows, 1), cache.num_kv_heads, cache.head_dim), dtype=torch.bfloat16,
-                            device=cache.k.device)
-        v_out = torch.empty_like(k_out)
+        if num_rows is None:  # (sizing from the lengths synchronises with the GPU)
+            num_rows = int(context_lengths.sum().item()) if seq_offsets is None else \
+                int((seq_offsets + context_lengths.to(seq_offsets.dtype)).max().item())
+        with _on_stream(stream):
+            k_out = torch.empty((max(int(num_rows), 1), cache.num_kv_heads, cache.head_dim), dtype=torch.bfloat16,
+                                device=cache.k.device)
+            v_out = torch.empty_like(k_out)
     if token_stride is None:
         token_stride = cache.num_kv_heads * cache.head_dim
     if head_stride is None:
@@ -222,19 +299,33 @@ def decode_gqa(q, cache: Cache, block_table, context_lengths, scale, *, cu_q_len
                out=None, lse_out=None, workspace=None, split_tokens=0, kernel=0, partition=0, window=0,
                stream=None):
     """Attention of the new queries ``q`` (bf16 ``[Tq, Hq, D]``) over the paged cache."""
-    hq = int(q.shape[1])
+    _want(q, "q", torch.bfloat16, (None, None, cache.head_dim))
+    tq, hq = int(q.shape[0]), int(q.shape[1])
+    if hq % cache.num_kv_heads != 0:
+        raise ValueError(f"{hq} query heads are not a multiple of {cache.num_kv_heads} KV heads")
+    _want(context_lengths, "context_lengths", torch.int32, ndim=1)
     batch = int(context_lengths.shape[0])
+    _want(block_table, "block_table", torch.int32, (batch, None))
     mbs = int(block_table.shape[1])
+    _want(cu_q_lens, "cu_q_lens", torch.int32, (batch + 1,), optional=True)
     if cu_q_lens is None:
         max_q_len = 1
-    if out is None:
-        out = torch.empty_like(q)
+        if tq != batch:
+            raise ValueError(f"without cu_q_lens q holds one row per sequence: {tq} rows for {batch} sequences")
+    _want(out, "out", torch.bfloat16, (tq, hq, cache.head_dim), optional=True)
+    _want(lse_out, "lse_out", torch.float32, (tq, hq), optional=True)
+    _want(workspace, "workspace", torch.uint8, ndim=1, optional=True)
+    _same_device(cache.k, q=q, block_table=block_table, context_lengths=context_lengths, cu_q_lens=cu_q_lens,
+                 out=out, lse_out=lse_out, workspace=workspace)
     o = _opts(split_tokens, kernel, partition, window)
     need = int(lib().pkv_decode_workspace_size(batch, hq, cache.num_kv_heads, cache.head_dim, mbs,
                                                cache.block_size, max_q_len, cache.quant_mode,
                                                ctypes.byref(o)))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)  # no initial contents needed
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)  # no initial contents needed
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().pkv_decode_gqa(_ptr(q), hq, cache.ref, _ptr(block_table), mbs, _ptr(context_lengths),
                               _ptr(cu_q_lens), batch, int(max_q_len), float(scale), _ptr(out),
@@ -271,9 +362,22 @@ class MLACache:
 def mla_store_c8(cache: MLACache, latent_new, rope_new, *, slot_mapping=None, cu_q_lens=None,
                  context_lengths=None, block_table=None, stream=None):
     """Quantize bf16 latent rows ``[T, 512]`` and rotary-key rows ``[T, 64]`` into the cache."""
+    _want(latent_new, "latent_new", torch.bfloat16, (None, cache.latent_dim))
     t = int(latent_new.shape[0])
-    batch = 0 if context_lengths is None else int(context_lengths.shape[0])
-    mbs = 0 if block_table is None else int(block_table.shape[1])
+    _want(rope_new, "rope_new", torch.bfloat16, (t, cache.rope_dim))
+    if slot_mapping is not None:
+        _want(slot_mapping, "slot_mapping", torch.int64, (t,))
+        batch, mbs = 0, 0
+    else:
+        _want(context_lengths, "context_lengths", torch.int32, ndim=1)
+        batch = int(context_lengths.shape[0])
+        _want(block_table, "block_table", torch.int32, (batch, None))
+        mbs = int(block_table.shape[1])
+        _want(cu_q_lens, "cu_q_lens", torch.int32, (batch + 1,), optional=True)
+        if cu_q_lens is None and t != batch:
+            raise ValueError(f"without cu_q_lens every sequence stores one token: {t} tokens for {batch} sequences")
+    _same_device(cache.latent, latent_new=latent_new, rope_new=rope_new, slot_mapping=slot_mapping,
+                 cu_q_lens=cu_q_lens, context_lengths=context_lengths, block_table=block_table)
     st = lib().pkv_mla_store_c8(cache.ref, _ptr(latent_new), _ptr(rope_new), t, _ptr(slot_mapping),
                                 _ptr(cu_q_lens), _ptr(context_lengths), _ptr(block_table), batch, mbs,
                                 _stream(stream))
@@ -297,13 +401,23 @@ def mla_decode(q_latent, q_rope, cache: MLACache, block_table, context_lengths, 
                lse_out=None, workspace=None, split_tokens=0, stream=None):
     """Latent attention of one query per sequence: ``q_latent`` bf16 ``[B, H, 512]``, ``q_rope``
     bf16 ``[B, H, 64]``; returns bf16 ``[B, H, 512]``."""
+    _want(q_latent, "q_latent", torch.bfloat16, (None, None, cache.latent_dim))
     batch, heads = int(q_latent.shape[0]), int(q_latent.shape[1])
+    _want(q_rope, "q_rope", torch.bfloat16, (batch, heads, cache.rope_dim))
+    _want(context_lengths, "context_lengths", torch.int32, (batch,))
+    _want(block_table, "block_table", torch.int32, (batch, None))
     mbs = int(block_table.shape[1])
-    if out is None:
-        out = torch.empty_like(q_latent)
+    _want(out, "out", torch.bfloat16, (batch, heads, cache.latent_dim), optional=True)
+    _want(lse_out, "lse_out", torch.float32, (batch, heads), optional=True)
+    _want(workspace, "workspace", torch.uint8, ndim=1, optional=True)
+    _same_device(cache.latent, q_latent=q_latent, q_rope=q_rope, context_lengths=context_lengths,
+                 block_table=block_table, out=out, lse_out=lse_out, workspace=workspace)
     need = mla_decode_workspace_size(batch, heads, mbs, cache.block_size, split_tokens)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q_latent.device)  # no initial contents needed
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty_like(q_latent)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q_latent.device)  # no initial contents needed
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().pkv_mla_decode(_ptr(q_latent), _ptr(q_rope), heads, cache.ref, _ptr(block_table), mbs,
                               _ptr(context_lengths), batch, float(scale), _ptr(out), _ptr(lse_out),

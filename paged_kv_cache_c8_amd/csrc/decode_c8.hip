@@ -6,10 +6,12 @@
 // what the HBM roofline of MI355X leaves room for:
 //
 //  * Scores on the int8 matrix cores, with no conversion of the K codes.  Each query row is
-//    multiplied by a power of two and rounded to integers q in [-2^14, 2^14]; q = 256 hi + lo
-//    with int8 hi and lo (exact), and v_mfma_i32_16x16x64_i8 forms K.hi, shifted left by 8, then
-//    accumulates K.lo on top: the exact integer dot product of the codes with q.  The K scale and
-//    the power of two come back in the fp32 softmax.
+//    multiplied by a power of two and rounded to integers q in [-2^22, 2^22] (relative rounding
+//    2^-23 of the row's largest element, so a row with one channel hundreds of times larger than
+//    the rest keeps the small channels' precision); q = 65536 hi + 256 mid + lo with int8 digits
+//    (exact).  v_mfma_i32_16x16x64_i8 forms K.hi, shifted left by 8, then accumulates K.mid on
+//    top (an exact int32 below 2^28), and K.lo in a second accumulator; the two are joined in
+//    fp32 as 256 c1 + c2.  The K scale and the power of two come back in the fp32 softmax.
 //  * Keys are walked in blocks of 64.  Lane group g (lanes 16g .. 16g+15) owns the 16 keys
 //    16g .. 16g+15 of the block, one 16-slot V tile: it loads them as the 16 consecutive bytes of
 //    each channel row of that channel-major tile (one 16-byte load per 16 channels; a block reads
@@ -91,11 +93,15 @@ struct C8V {
 // keys [t_seg0, t_seg1) (t_seg0 a multiple of 64).  pslot < 0: the segment is the item's whole key
 // range and the result goes to out / lse; else it is a partial, written to rows pslot * prs + j of
 // the workspace for the merge.  WIN: a sliding window (DecodeArgs::window) limits each row's keys.
+// qs: the wave's LDS for its quantized query rows, QS_I4<D, RT> 16-byte entries.
+template <int D, int RT>
+constexpr int QS_I4 = 3 * (D / 64) * RT * kWave;
+
 template <int D, int MODE, int J, int RT, bool WIN>
 __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, const int h, const int qlen,
                                            const int qrow0, const int prior, const int r0, const int nvalid,
                                            const int t_seg0, const int t_seg1, const int64_t pslot,
-                                           int* const bt_s) {
+                                           int* const bt_s, i4* const qs) {
     static_assert(MODE == 0 || MODE == 1 || MODE == 3, "int8 cache modes only");
     static_assert(J == 1 || RT == 1, "several row tiles only with one subset class");
     constexpr int KSTEP = D / 64;                     // 64-channel steps of the score MFMA
@@ -175,7 +181,10 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
         const int q = J * u + jcol;
         return T + 16 * g + 8 * (q >> 1) + 4 * (q & 1) + i;
     };
-    i4 qhi[RT][KSTEP], qlo[RT][KSTEP];
+    // the quantized query rows, digit p (0 hi, 1 mid, 2 lo) of k-step m of row tile rt, are the
+    // B operands of the score MFMAs; they live in the wave's LDS (qs) and are read back per block,
+    // which keeps them out of the registers the key loop needs
+    auto qslot = [&](int p, int rt, int m) -> i4& { return qs[((p * RT + rt) * KSTEP + m) * kWave + lane]; };
     float rowmul[RT];  // |softmax scale| * log2(e) / 2^k: integer score units -> log2 units
 
     // The segment is walked in ranges of at most MAX_SPLIT keys, each with its block-table slice in
@@ -246,8 +255,8 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
         __builtin_amdgcn_wave_barrier();
 
         if (tb == t_seg0) {
-            // ---- quantize the query rows: q * 2^k rounded to integers in [-2^14, 2^14], split exactly as
-            //      256 hi + lo with int8 hi and lo
+            // ---- quantize the query rows: q * 2^k rounded to integers in [-2^22, 2^22], split exactly as
+            //      65536 hi + 256 mid + lo with int8 digits
             const float sgn = a.scale_log2 < 0.0f ? -1.0f : 1.0f;  // a negative scale flips the query
         #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
@@ -266,24 +275,32 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
                 mx = col_max(mx);
                 int ex = 0;
                 if (mx > 0.0f) (void)frexpf(mx, &ex);        // mx in [2^(ex-1), 2^ex)
-                const int k = min(120, max(-120, 14 - ex));  // |x| * 2^k < 2^14
+                const int k = min(120, max(-120, 22 - ex));  // |x| * 2^k < 2^22
                 const float up = ldexpf(1.0f, k);
         #pragma unroll
                 for (int m = 0; m < KSTEP; ++m) {
+                    i4 qh, qm, ql;
         #pragma unroll
                     for (int w = 0; w < 4; ++w) {
-                        uint32_t hw = 0, lw = 0;
+                        uint32_t hw = 0, mw = 0, lw = 0;
         #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const int qi = (int)__builtin_rintf(x[16 * m + 4 * w + e] * up);  // |qi| <= 2^14
+                            const int qi = (int)__builtin_rintf(x[16 * m + 4 * w + e] * up);  // |qi| <= 2^22
                             const int lo = ((qi + 128) & 255) - 128;
-                            const int hi = (qi - lo) >> 8;                                  // |hi| <= 64
+                            const int r1 = (qi - lo) >> 8;                                  // |r1| <= 2^14
+                            const int md = ((r1 + 128) & 255) - 128;
+                            const int hi = (r1 - md) >> 8;                                  // |hi| <= 64
                             hw |= (uint32_t)(hi & 255) << (8 * e);
+                            mw |= (uint32_t)(md & 255) << (8 * e);
                             lw |= (uint32_t)(lo & 255) << (8 * e);
                         }
-                        qhi[rt][m][w] = (int)hw;
-                        qlo[rt][m][w] = (int)lw;
+                        qh[w] = (int)hw;
+                        qm[w] = (int)mw;
+                        ql[w] = (int)lw;
                     }
+                    qslot(0, rt, m) = qh;
+                    qslot(1, rt, m) = qm;
+                    qslot(2, rt, m) = ql;
                 }
                 rowmul[rt] = fabsf(a.scale_log2) * ldexpf(1.0f, -k);
             }
@@ -299,21 +316,38 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
             // sink them below the first score MFMA, whose wait then drains every load in flight)
             __builtin_amdgcn_sched_barrier(0);
 
-            // -------------------------------------------- scores: one int32 tile per subset
-            i4 sc[RT][4];
+            // -------------------------------------------- scores: two int32 tiles per subset,
+            //      c1 = 256 K.hi + K.mid and c2 = K.lo (the score is 256 c1 + c2)
+            i4 sc[RT][4], sc2[RT][4];
     #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
+                i4 qb[KSTEP];
+    #pragma unroll
+                for (int m = 0; m < KSTEP; ++m) qb[m] = qslot(0, rt, m);
     #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     i4 c = i4{0, 0, 0, 0};
     #pragma unroll
                     for (int m = 0; m < KSTEP; ++m)
-                        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[q][m], qhi[rt][m], c, 0, 0, 0);
-                    c = c * 256;
+                        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[q][m], qb[m], c, 0, 0, 0);
+                    sc[rt][q] = c * 256;
+                }
+    #pragma unroll
+                for (int m = 0; m < KSTEP; ++m) qb[m] = qslot(1, rt, m);
+    #pragma unroll
+                for (int q = 0; q < 4; ++q)
     #pragma unroll
                     for (int m = 0; m < KSTEP; ++m)
-                        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[q][m], qlo[rt][m], c, 0, 0, 0);
-                    sc[rt][q] = c;
+                        sc[rt][q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[q][m], qb[m], sc[rt][q], 0, 0, 0);
+    #pragma unroll
+                for (int m = 0; m < KSTEP; ++m) qb[m] = qslot(2, rt, m);
+    #pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    i4 c2 = i4{0, 0, 0, 0};
+    #pragma unroll
+                    for (int m = 0; m < KSTEP; ++m)
+                        c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[q][m], qb[m], c2, 0, 0, 0);
+                    sc2[rt][q] = c2;
                 }
             }
             load_k(T + BLK, R);
@@ -359,13 +393,17 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
                 float bmax = -INFINITY;
     #pragma unroll
                 for (int u = 0; u < NSLOT; ++u) {
-                    i4 S = sc[rt][J * u];
+                    i4 S = sc[rt][J * u], S2 = sc2[rt][J * u];
     #pragma unroll
                     for (int c = 1; c < J; ++c)
-                        if (jcol == c) S = sc[rt][J * u + c];
+                        if (jcol == c) {
+                            S = sc[rt][J * u + c];
+                            S2 = sc2[rt][J * u + c];
+                        }
     #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        x[u][i] = (float)S[i] * (MODE == 0 ? R.ks[u][i] : (MODE == 1 ? R.ks[u][0] : 1.0f));
+                        const float si = __builtin_fmaf((float)S[i], 256.0f, (float)S2[i]);
+                        x[u][i] = si * (MODE == 0 ? R.ks[u][i] : (MODE == 1 ? R.ks[u][0] : 1.0f));
                         if (MASKED) {
                             const int t = key_of(T, u, i);
                             if (!(t < t_end && t <= lim[rt] && (!WIN || t >= lo[rt]))) x[u][i] = -INFINITY;
@@ -528,6 +566,7 @@ template <int D, int MODE, int J, int RT, bool WIN>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 1))) void decode_c8_kernel(DecodeArgs a, int pairs) {
     constexpr int ROWS = J > 1 ? 16 / J : 16 * RT;
     __shared__ int bt_s[MAX_SPLIT_PAGES];
+    __shared__ i4 qs[QS_I4<D, RT>];
     const int wi = blockIdx.x;
     const int rest = wi >> 3;
     const int u = (rest / a.nrg) * 8 + (wi & 7);
@@ -545,7 +584,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 
     if (t_begin >= it.kmax) return;
     const int t_end = min(t_begin + a.split_len, it.kmax);
     c8_segment<D, MODE, J, RT, WIN>(a, it.b, it.h, it.qlen, it.qrow0, it.prior, it.r0, it.nvalid, t_begin, t_end,
-                               a.nsplit > 1 ? (int64_t)item * a.nsplit + s : -1, bt_s);
+                               a.nsplit > 1 ? (int64_t)item * a.nsplit + s : -1, bt_s, qs);
 }
 
 // Balanced partition (sk_partition.h): one wave per segment of the plan.
@@ -553,12 +592,13 @@ template <int D, int MODE, int J, int RT, bool WIN>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 1))) void decode_c8_sk_kernel(DecodeArgs a, int batch) {
     constexpr int ROWS = J > 1 ? 16 / J : 16 * RT;
     __shared__ int bt_s[MAX_SPLIT_PAGES];
+    __shared__ i4 qs[QS_I4<D, RT>];
     extern __shared__ int kseq[];  // [batch + 1] prefix sums over sequences of their waves
     SkSegment sg;
     if (!sk_plan<ROWS, WIN>(a, batch, blockIdx.x, kseq, sg)) return;
     const ItemGeo& it = sg.it;
     c8_segment<D, MODE, J, RT, WIN>(a, it.b, it.h, it.qlen, it.qrow0, it.prior, it.r0, it.nvalid, sg.t0, sg.t1,
-                                    sg.pslot, bt_s);
+                                    sg.pslot, bt_s, qs);
 }
 
 template <int D, int MODE, int J, int RT, bool WIN>

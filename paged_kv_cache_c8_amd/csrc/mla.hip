@@ -16,9 +16,11 @@
 //  * wave w loads keys 16w .. 16w+15 of the block in the A-operand layout of
 //    v_mfma_i32_16x16x64_i8 (lane (g, n): key 16w + n, 16 bytes of channels 64m + 16g for step m)
 //    and scores them against the 16 heads with exact integer dot products: each query row is
-//    scaled by a power of two and rounded to integers in [-2^14, 2^14], split as 256 hi + lo with
-//    int8 hi and lo; the latent part (eight 64-channel steps) and the rotary part (one step) are
-//    summed separately, since their scales differ per token.
+//    scaled by a power of two and rounded to integers in [-2^22, 2^22] (relative rounding 2^-23
+//    of the row's largest element), split as 65536 hi + 256 mid + lo with int8 digits; 256 K.hi +
+//    K.mid and K.lo are accumulated apart (int32) and joined in fp32; the latent part (eight
+//    64-channel steps) and the rotary part (one step) are summed separately, since their scales
+//    differ per token.
 //  * the same registers go to LDS (one 528-byte row per key), and the next block's loads are
 //    issued at once.
 //  * the block's maximum logit per head and the largest latent scale are exchanged through LDS;
@@ -137,10 +139,10 @@ __device__ __forceinline__ float col_sum(float x) {
 }
 
 // Quantize NS 64-channel steps of the lane's query row (16 channels per step, raw bf16 in
-// raw[2m], raw[2m+1]): x * 2^k rounded to integers in [-2^14, 2^14] (k from the row's absmax over
-// the four lanes of the column), split exactly as 256 hi + lo.  Returns 2^-k * mul.
+// raw[2m], raw[2m+1]): x * 2^k rounded to integers in [-2^22, 2^22] (k from the row's absmax over
+// the four lanes of the column), split exactly as 65536 hi + 256 mid + lo.  Returns 2^-k * mul.
 template <int NS>
-__device__ __forceinline__ float quant_query(const u32x4* raw, i4* hi, i4* lo, float sgn, float mul) {
+__device__ __forceinline__ float quant_query(const u32x4* raw, i4* hi, i4* md, i4* lo, float sgn, float mul) {
     float x[16 * NS];
 #pragma unroll
     for (int l = 0; l < 2 * NS; ++l)
@@ -152,22 +154,26 @@ __device__ __forceinline__ float quant_query(const u32x4* raw, i4* hi, i4* lo, f
     mx = col_max(mx);
     int ex = 0;
     if (mx > 0.0f) (void)frexpf(mx, &ex);        // mx in [2^(ex-1), 2^ex)
-    const int k = min(120, max(-120, 14 - ex));  // |x| * 2^k < 2^14
+    const int k = min(120, max(-120, 22 - ex));  // |x| * 2^k < 2^22
     const float up = ldexpf(1.0f, k);
 #pragma unroll
     for (int m = 0; m < NS; ++m) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            uint32_t hw = 0, lw = 0;
+            uint32_t hw = 0, mw = 0, lw = 0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int qi = (int)__builtin_rintf(x[16 * m + 4 * w + e] * up);  // |qi| <= 2^14
+                const int qi = (int)__builtin_rintf(x[16 * m + 4 * w + e] * up);  // |qi| <= 2^22
                 const int l8 = ((qi + 128) & 255) - 128;
-                const int h8v = (qi - l8) >> 8;                                  // |h8v| <= 64
+                const int r1 = (qi - l8) >> 8;                                   // |r1| <= 2^14
+                const int m8 = ((r1 + 128) & 255) - 128;
+                const int h8v = (r1 - m8) >> 8;                                  // |h8v| <= 64
                 hw |= (uint32_t)(h8v & 255) << (8 * e);
+                mw |= (uint32_t)(m8 & 255) << (8 * e);
                 lw |= (uint32_t)(l8 & 255) << (8 * e);
             }
             hi[m][w] = (int)hw;
+            md[m][w] = (int)mw;
             lo[m][w] = (int)lw;
         }
     }
@@ -181,7 +187,8 @@ struct __align__(16) MlaShared {
     float vmx[NW];                // per-wave largest latent scale
     float lsum[NW][16];           // per-wave weight sums, exchanged at the end
     i4 qhi[QSTEPS][kWave];        // the quantized query rows (B operand of the score MFMA, per
-    i4 qlo[QSTEPS][kWave];        // lane), high and low bytes: the same for every wave
+    i4 qmd[QSTEPS][kWave];        // lane), high, middle and low bytes: the same for every wave
+    i4 qlo[QSTEPS][kWave];
     int pg[NW][128];              // per wave: page ids of its keys in two 64-block chunks (ring)
     int plan[NW][2];              // balanced partition: per-wave partial sums
     int found[2];                 // balanced partition: the workgroup's sequence and its first slot
@@ -378,15 +385,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         qraw[2 * QSTEPS - 1] = hv ? load16(qrp + 8) : z;
     }
     const float sgn = a.scale_log2 < 0.0f ? -1.0f : 1.0f;  // a negative scale flips the query
-    i4 qhi[QSTEPS], qlo[QSTEPS];
-    const float rmul_c = quant_query<DC / 64>(qraw, qhi, qlo, sgn, fabsf(a.scale_log2));
-    const float rmul_r = quant_query<1>(qraw + 2 * (DC / 64), qhi + DC / 64, qlo + DC / 64, sgn, fabsf(a.scale_log2));
+    i4 qhi[QSTEPS], qmd[QSTEPS], qlo[QSTEPS];
+    const float rmul_c = quant_query<DC / 64>(qraw, qhi, qmd, qlo, sgn, fabsf(a.scale_log2));
+    const float rmul_r = quant_query<1>(qraw + 2 * (DC / 64), qhi + DC / 64, qmd + DC / 64, qlo + DC / 64, sgn,
+                                        fabsf(a.scale_log2));
     // the quantized query is the same for every wave: kept once in LDS instead of in every
     // wave's registers (room for the second key register set)
     if (w == 0) {
 #pragma unroll
         for (int m = 0; m < QSTEPS; ++m) {
             S.qhi[m][lane] = qhi[m];
+            S.qmd[m][lane] = qmd[m];
             S.qlo[m][lane] = qlo[m];
         }
     }
@@ -419,16 +428,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         const int pg = page_of(T + 2 * MBLK);
         // -------------------------------- integer scores of the wave's 16 keys x 16 heads
         //                                  (hi and lo as two independent accumulation chains)
-        i4 ch = i4{0, 0, 0, 0}, cl = i4{0, 0, 0, 0};
+        i4 ch = i4{0, 0, 0, 0}, cm = i4{0, 0, 0, 0}, cl = i4{0, 0, 0, 0};
 #pragma unroll
         for (int m = 0; m < DC / 64; ++m) {
             ch = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[m], S.qhi[m][lane], ch, 0, 0, 0);
+            cm = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[m], S.qmd[m][lane], cm, 0, 0, 0);
             cl = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[m], S.qlo[m][lane], cl, 0, 0, 0);
         }
-        const i4 c = ch * 256 + cl;  // |score| <= 576 * 128 * 2^14 < 2^31
+        const i4 c1 = ch * 256 + cm;  // |256 K.hi + K.mid| <= 512 * 128 * 2^14 = 2^30
         const i4 rh = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[DC / 64], S.qhi[DC / 64][lane], i4{0, 0, 0, 0}, 0, 0, 0);
+        const i4 rm = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[DC / 64], S.qmd[DC / 64][lane], i4{0, 0, 0, 0}, 0, 0, 0);
         const i4 rl = __builtin_amdgcn_mfma_i32_16x16x64_i8(R.k[DC / 64], S.qlo[DC / 64][lane], i4{0, 0, 0, 0}, 0, 0, 0);
-        const i4 r = rh * 256 + rl;
+        const i4 r1 = rh * 256 + rm;
         // -------------------------------- latent rows to LDS (once every wave is done with the
         //                                  previous block's), loads of the block after next
         __syncthreads();
@@ -445,7 +456,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const bool vis = !MASKED || T + 16 * w + 4 * g + i < t_end;
-            x[i] = vis ? __builtin_fmaf((float)c[i] * R.ls[i], rmul_c, (float)r[i] * R.rs[i] * rmul_r) : -INFINITY;
+            const float cs = __builtin_fmaf((float)c1[i], 256.0f, (float)cl[i]);  // latent score
+            const float rs = __builtin_fmaf((float)r1[i], 256.0f, (float)rl[i]);  // rotary score
+            x[i] = vis ? __builtin_fmaf(cs * R.ls[i], rmul_c, rs * R.rs[i] * rmul_r) : -INFINITY;
             vsl[i] = vis ? R.ls[i] : 0.0f;  // stand-in keys' scales never reach a weight
             vm = fmaxf(vm, vsl[i]);
             lmax = fmaxf(lmax, x[i]);

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import gen
-from tests.gpu_harness import Run, lse_slack, oracle_run, sub_workload
+from tests.gpu_harness import Run, lse_bar, oracle_run, sub_workload
 from tests.helpers import attention_close, v_token_major
 
 pytestmark = pytest.mark.gpu
@@ -64,7 +64,7 @@ def _check(idx, n_sample, kernel=0, quant_mode=None, window=0):
     print(f"config {idx}: max_abs={max_abs:.3e} rel={rel:.3e}", flush=True)
     assert max_abs <= 1e-2 and rel <= 1e-2 and elem_ok
     gl = lse[torch.as_tensor(rows, device=lse.device)].cpu().numpy().astype(np.float64)
-    slack = lse_slack(hc, th["q"], ws, 1.0 / np.sqrt(w.head_dim)) if w.quant_mode != 2 else 0.0
+    slack = lse_bar(hc, th["q"], ws, 1.0 / np.sqrt(w.head_dim))
     fin = np.isfinite(olse)
     assert np.array_equal(np.isfinite(gl), fin)
     tol = np.broadcast_to(1e-4 + 1e-5 * np.abs(np.where(fin, olse, 0.0)) + slack, olse.shape)

@@ -1,6 +1,6 @@
 """GPU parity of the paged MLA (latent cache) path with the oracle: the store bit-exact (codes and
-scales), the decode within 1e-2 (max abs and norm-relative) and its lse within the bound the query
-rounding of the int8 score MFMA allows."""
+scales), the decode within 1e-2 (max abs and norm-relative) and its lse within 1e-4 + 1e-5|lse|
+plus the error bound of an fp32 evaluation of the logits (lse_bar)."""
 import numpy as np
 import pytest
 import torch
@@ -74,11 +74,10 @@ def oracle_cache(w, t, seqs=None):
     return c
 
 
-def lse_slack(hc, q_lat_bits, q_rope_bits, w, seqs, scale):
-    """Per (sequence, head) bound of the lse error the query rounding allows: each part of a query
-    row (latent, rotary) is rounded to multiples of step = 2^(e - 14), e the exponent with its
-    max|q| in [2^(e-1), 2^e); key t's logit moves by at most |scale| * (s_c,t * step_c / 2 *
-    sum|c_t| + s_r,t * step_r / 2 * sum|r_t|), the lse by at most the largest move."""
+def lse_bar(hc, q_lat_bits, q_rope_bits, w, seqs, scale):
+    """The part of the lse tolerance that grows with the logits, per (sequence, head): the error
+    bound of evaluating the definition in fp32, (512 + 64) * 2^-24 * |scale| * max_t (sum |q_c| |c_t|
+    + sum |q_r| |r_t|) over the sequence's keys.  It depends on the inputs only."""
     out = np.zeros((len(seqs), w.num_heads))
     for j, b in enumerate(seqs):
         n = int(w.context_lengths[b])
@@ -87,14 +86,12 @@ def lse_slack(hc, q_lat_bits, q_rope_bits, w, seqs, scale):
         pos = np.arange(n)
         blk = w.block_table[b, pos // w.block_size]
         off = pos % w.block_size
-        ac = np.abs(hc.latent[blk, off].astype(np.float64)).sum(axis=1) * hc.latent_scale[blk, off]
-        ar = np.abs(hc.rope[blk, off].astype(np.float64)).sum(axis=1) * hc.rope_scale[blk, off]
-        for part, a_t, qb in (("c", ac, q_lat_bits[j]), ("r", ar, q_rope_bits[j])):
-            m = np.abs(bits_to_f32(qb).astype(np.float64)).max(axis=1)  # [H]
-            e = np.frexp(m)[1]
-            step = np.where(m > 0, np.ldexp(1.0, e - 14), 0.0)
-            out[j] += abs(scale) * step / 2 * a_t.max()
-    return out
+        c = np.abs(hc.latent[blk, off].astype(np.float64)) * hc.latent_scale[blk, off][:, None]
+        r = np.abs(hc.rope[blk, off].astype(np.float64)) * hc.rope_scale[blk, off][:, None]
+        qc = np.abs(bits_to_f32(q_lat_bits[j]).astype(np.float64))   # [H, 512]
+        qr = np.abs(bits_to_f32(q_rope_bits[j]).astype(np.float64))  # [H, 64]
+        out[j] = (qc @ c.T + qr @ r.T).max(axis=1)
+    return (w.latent_dim + w.rope_dim) * 2.0 ** -24 * abs(scale) * out
 
 
 def check_decode(r, out, lse, seqs, hc=None):
@@ -113,7 +110,9 @@ def check_decode(r, out, lse, seqs, hc=None):
     gl = lse.index_select(0, qi).cpu().numpy().astype(np.float64)
     fin = np.isfinite(olse)
     assert np.array_equal(np.isfinite(gl), fin)
-    tol = 1e-4 + 1e-5 * np.abs(np.where(fin, olse, 0.0)) + lse_slack(hc, ql, qr, w, seqs, w.softmax_scale)
+    tol = 1e-4 + 1e-5 * np.abs(np.where(fin, olse, 0.0)) + lse_bar(hc, ql, qr, w, seqs, w.softmax_scale)
+    if fin.any():
+        print(f"{w.name}: lse max_err={float(np.abs(gl[fin] - olse[fin]).max()):.2e}", flush=True)
     assert np.all(np.abs(gl[fin] - olse[fin]) <= tol[fin])
     empty = ~fin
     assert np.all(got[empty] == 0)

@@ -2,8 +2,8 @@
 
 Bars: int8 codes and fp32 scales bit-exact; dequant bit-exact; attention within max-abs 1e-2 and
 norm-relative 1e-2 of the oracle's fp64 result (elementwise |g - o| <= 1e-2 + 1e-2 |o|); lse within
-1e-4 + 1e-5 |lse| plus the bound that the int8-score kernel's rounding of the query allows
-(gpu_harness.lse_slack).  Sizes span several 128-key chunks, several splits and ragged tails.
+1e-4 + 1e-5 |lse| plus the error bound of an fp32 evaluation of the logits (gpu_harness.lse_bar).
+Sizes span several 128-key chunks, several splits and ragged tails.
 """
 import numpy as np
 import pytest
@@ -177,11 +177,11 @@ def test_inactive_sequences_give_zero_and_minus_inf(kernel):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_exhaustive_bf16_sweep_through_store(d):
-    """Every finite bf16 value as the absmax of one token (others: seeded values below it)."""
+    """Every finite bf16 value as the absmax of one token (others: seeded values below it); the
+    two zeros give all-zero tokens (scale 0, codes 0)."""
     b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     b = b[((b >> 7) & 0xFF) != 0xFF]
     vals = (b.astype(np.uint32) << 16).view(np.float32)
-    vals = vals[vals != 0]
     rng = np.random.default_rng(d)
     frac = rng.uniform(-1, 1, size=(len(vals), d - 1)).astype(np.float32)
     others = ((np.abs(vals)[:, None] * frac).view(np.uint32) & 0xFFFF0000).view(np.float32)
@@ -202,6 +202,9 @@ def test_exhaustive_bf16_sweep_through_store(d):
     assert np.array_equal(cache.v.cpu().numpy(), hc.v)
     assert np.array_equal(cache.k_scale.cpu().numpy().view(np.uint32), hc.k_scale.view(np.uint32))
     assert np.array_equal(cache.v_scale.cpu().numpy().view(np.uint32), hc.v_scale.view(np.uint32))
+    zero = np.flatnonzero(vals == 0)  # +0 and -0: scale 0 and every code 0
+    assert len(zero) == 2 and np.all(hc.k_scale.reshape(-1)[zero] == 0)
+    assert np.all(cache.k.cpu().numpy().reshape(t, d)[zero] == 0)
 
 
 def test_slot_mapping_store_with_skips():
