@@ -35,7 +35,8 @@
  *    [context_lengths[b] - q_len_b, context_lengths[b]).
  *  - Results are deterministic: fixed split plan, fixed merge order, no
  *    floating-point atomics.  Calls are reentrant; the only state kept is the
- *    device's compute-unit count.
+ *    device's compute-unit count (and, for pkv_decode_gqa_noalloc, the address
+ *    of its per-device scratch array, whose calls share that array).
  *
  * Cache layout (caller-owned; element (block, kv head, slot, channel)):
  *   K       [num_blocks][num_kv_heads][block_size][head_dim]  (token-major page)
@@ -236,6 +237,36 @@ int pkv_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, in
                     int32_t max_blocks_per_seq, int32_t block_size, int32_t max_q_len,
                     int32_t quant_mode, const pkv_decode_opts_t *opts, int32_t *split_tokens,
                     int32_t *num_splits, int32_t *kernel);
+
+/* Size of the fixed device array that pkv_decode_gqa_noalloc takes its
+ * workspace from (one copy per GPU, held until the process ends). */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * pkv_decode_gqa_noalloc - pkv_decode_gqa for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments and result as pkv_decode_gqa, minus
+ * the workspace: the split partials go to a file-scope device array of
+ * PKV_NOALLOC_SCRATCH_BYTES inside the library.  The call allocates nothing
+ * (no hipMalloc, no hipFree).
+ *
+ * Limits and errors:
+ *  - PKV_ERR_WORKSPACE (nothing launched) when the plan needs more than
+ *    PKV_NOALLOC_SCRATCH_BYTES (pkv_decode_workspace_size tells beforehand).
+ *    32 MiB covers every single-token decode plan up to 8192 (batch x KV head)
+ *    items; the chunked multi-token plans of many sequences may need more.
+ *  - The stream must belong to the current device (PKV_ERR_INVALID_ARG
+ *    otherwise): the array's address is the current device's.
+ *  - Every call on one GPU shares that GPU's array and the array keeps the
+ *    last call's contents (the decode needs no initial contents).  Calls that
+ *    overlap in time on one GPU (other streams, other threads) race on it.
+ *  - Otherwise as pkv_decode_gqa.
+ */
+int pkv_decode_gqa_noalloc(const void *q, int32_t num_q_heads, const pkv_cache_t *cache,
+                           const int32_t *block_table, int32_t max_blocks_per_seq,
+                           const int32_t *context_lengths, const int32_t *cu_q_lens, int32_t batch,
+                           int32_t max_q_len, float scale, void *out, float *lse_out,
+                           const pkv_decode_opts_t *opts, void *stream);
 
 /* ------------------------------------------------------------------------- */
 /* Paged MLA (latent) cache                                                   */

@@ -19,7 +19,8 @@ import os
 
 import torch  # loaded first: libpkv binds to the HIP runtime torch has already loaded
 
-__all__ = ["PkvError", "Cache", "lib", "store_c8", "dequant", "decode_gqa", "decode_workspace_size",
+__all__ = ["PkvError", "Cache", "lib", "store_c8", "dequant", "decode_gqa", "decode_gqa_noalloc",
+           "decode_workspace_size", "NOALLOC_SCRATCH_BYTES",
            "decode_plan", "MLACache", "mla_store_c8", "mla_decode", "mla_decode_workspace_size",
            "mla_decode_plan", "QUANT_PER_TOKEN", "QUANT_PER_BLOCK", "QUANT_NONE_BF16", "QUANT_PER_CHANNEL",
            "EXPORTS"]
@@ -35,7 +36,9 @@ QUANT_PER_CHANNEL = 3
 # every symbol include/pkv.h declares
 EXPORTS = ("pkv_status_string", "pkv_version", "pkv_store_c8", "pkv_dequant",
            "pkv_decode_workspace_size", "pkv_decode_gqa", "pkv_decode_plan", "pkv_mla_store_c8",
-           "pkv_mla_decode_workspace_size", "pkv_mla_decode_plan", "pkv_mla_decode")
+           "pkv_mla_decode_workspace_size", "pkv_mla_decode_plan", "pkv_mla_decode", "pkv_decode_gqa_noalloc")
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # PKV_NOALLOC_SCRATCH_BYTES
 
 MLA_LATENT_DIM = 512
 MLA_ROPE_DIM = 64
@@ -90,6 +93,8 @@ def lib():
         L.pkv_decode_gqa.argtypes = [P, I32, P, P, I32, P, P, I32, I32, ctypes.c_float, P, P, P, SZ,
                                      P, P]
         L.pkv_decode_gqa.restype = ctypes.c_int
+        L.pkv_decode_gqa_noalloc.argtypes = [P, I32, P, P, I32, P, P, I32, I32, ctypes.c_float, P, P, P, P]
+        L.pkv_decode_gqa_noalloc.restype = ctypes.c_int
         L.pkv_decode_plan.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32, P,
                                       ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]
         L.pkv_decode_plan.restype = ctypes.c_int
@@ -331,6 +336,35 @@ def decode_gqa(q, cache: Cache, block_table, context_lengths, scale, *, cu_q_len
                               _ptr(cu_q_lens), batch, int(max_q_len), float(scale), _ptr(out),
                               _ptr(lse_out), _ptr(workspace), ws_bytes, ctypes.byref(o), _stream(stream))
     _check(st, "pkv_decode_gqa")
+    return out
+
+
+def decode_gqa_noalloc(q, cache: Cache, block_table, context_lengths, scale, out, *, cu_q_lens=None, max_q_len=1,
+                       lse_out=None, split_tokens=0, kernel=0, partition=0, window=0, stream=None):
+    """``decode_gqa`` through ``pkv_decode_gqa_noalloc``: no workspace, and nothing allocated here
+    either (``out`` is required).  Its scratch space is one fixed array per GPU, shared by every
+    such call on that GPU (calls that overlap in time race)."""
+    _want(q, "q", torch.bfloat16, (None, None, cache.head_dim))
+    tq, hq = int(q.shape[0]), int(q.shape[1])
+    if hq % cache.num_kv_heads != 0:
+        raise ValueError(f"{hq} query heads are not a multiple of {cache.num_kv_heads} KV heads")
+    _want(context_lengths, "context_lengths", torch.int32, ndim=1)
+    batch = int(context_lengths.shape[0])
+    _want(block_table, "block_table", torch.int32, (batch, None))
+    _want(cu_q_lens, "cu_q_lens", torch.int32, (batch + 1,), optional=True)
+    if cu_q_lens is None:
+        max_q_len = 1
+        if tq != batch:
+            raise ValueError(f"without cu_q_lens q holds one row per sequence: {tq} rows for {batch} sequences")
+    _want(out, "out", torch.bfloat16, (tq, hq, cache.head_dim))
+    _want(lse_out, "lse_out", torch.float32, (tq, hq), optional=True)
+    _same_device(cache.k, q=q, block_table=block_table, context_lengths=context_lengths, cu_q_lens=cu_q_lens,
+                 out=out, lse_out=lse_out)
+    o = _opts(split_tokens, kernel, partition, window)
+    st = lib().pkv_decode_gqa_noalloc(_ptr(q), hq, cache.ref, _ptr(block_table), int(block_table.shape[1]),
+                                      _ptr(context_lengths), _ptr(cu_q_lens), batch, int(max_q_len), float(scale),
+                                      _ptr(out), _ptr(lse_out), ctypes.byref(o), _stream(stream))
+    _check(st, "pkv_decode_gqa_noalloc")
     return out
 
 
