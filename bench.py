@@ -57,6 +57,9 @@ def parse():
                     help="paged MLA (latent cache) workload index instead of the GQA ones (1 = DeepSeek-V3-shaped)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain device copy of known size (for scaling HBM byte counters)")
+    ap.add_argument("--op", default="decode", choices=["decode", "store-fill", "dequant"],
+                    help="decode: the decode step (default); store-fill: the prompt-style store of every "
+                         "prior token of the workload; dequant: the gather of the whole cache to bf16 rows")
     return ap.parse_args()
 
 
@@ -161,6 +164,9 @@ def main():
         sys.exit(2)
     if args.mla >= 0:
         main_mla(args)
+        return
+    if args.op != "decode":
+        main_codec(args)
         return
 
     import torch
@@ -315,6 +321,113 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def codec_bytes(w, op):
+    """Algorithmic HBM bytes of one launch of the store (every prior token of the workload, stored
+    in one prompt-style call) or of the dequant (every position of every sequence gathered to bf16
+    rows): each input byte read once, each output byte written once."""
+    hkv, d, bs = w.num_kv_heads, w.head_dim, w.block_size
+    if op == "store-fill":
+        t = int(w.prior_lengths.sum())
+        if w.quant_mode == 2:
+            out = t * hkv * d * 2 * 2
+        elif w.quant_mode == 0:
+            out = t * hkv * (2 * d + 8)
+        elif w.quant_mode == 3:
+            out = t * hkv * 2 * d + hkv * d * 4 * 2
+        else:
+            out = t * hkv * 2 * d + int(np.ceil(w.prior_lengths / bs).sum()) * hkv * 8
+        meta = w.batch * 4 * 2 + int(np.ceil(w.prior_lengths / bs).sum()) * 4
+        return t * hkv * d * 2 * 2, out + meta, t
+    n = int(w.context_lengths.sum())
+    if w.quant_mode == 2:
+        rd = n * hkv * d * 2 * 2
+    elif w.quant_mode == 0:
+        rd = n * hkv * (2 * d + 8)
+    elif w.quant_mode == 3:
+        rd = n * hkv * 2 * d + hkv * d * 4 * 2
+    else:
+        rd = n * hkv * 2 * d + int(np.ceil(w.context_lengths / bs).sum()) * hkv * 8
+    rd += w.batch * 4 + int(np.ceil(w.context_lengths / bs).sum()) * 4
+    return rd, n * hkv * d * 2 * 2, n
+
+
+def main_codec(args):
+    """The store of a whole prompt (the workload's prior tokens, one call) or the dequant of the
+    whole cache, timed alone with HIP events on the launch stream; inputs and outputs resident in
+    HBM.  Two input copies and two caches alternate so the 256 MB Infinity Cache cannot serve a
+    launch from the previous one."""
+    import torch
+
+    import gen
+    import paged_kv_cache_c8_amd as pkv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = gen.make_config(args.config, quant_mode=args.quant_mode)
+    t = gen.gen_tensors(w, device=dev)
+    k_prior, _ = gen.split_prior_new(w, t["k_all"])
+    v_prior, _ = gen.split_prior_new(w, t["v_all"])
+    del t["k_all"], t["v_all"]
+    i32 = lambda x: torch.as_tensor(np.ascontiguousarray(x, dtype=np.int32), device=dev)
+    bt, ctx, prior, cu_prior = i32(w.block_table), i32(w.context_lengths), i32(w.prior_lengths), i32(w.cu_prior)
+    read_b, write_b, units = codec_bytes(w, args.op)
+    caches = []
+    for _ in range(2):
+        c = pkv.Cache(w.quant_mode, w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, device=dev)
+        if w.quant_mode == gen.QUANT_PER_CHANNEL:
+            c.k_scale.copy_(t["k_scale"])
+            c.v_scale.copy_(t["v_scale"])
+        caches.append(c)
+    mql = int(w.prior_lengths.max())
+    if args.op == "store-fill":
+        ins = [(k_prior, v_prior), (k_prior.clone(), v_prior.clone())]
+
+        def launch(i):
+            k, v = ins[i % 2]
+            pkv.store_c8(caches[i % 2], k, v, cu_q_lens=cu_prior, context_lengths=prior, block_table=bt,
+                         max_q_len=mql)
+        kernel = "pkv_store_c8 (prompt-style store of every prior token)"
+    else:
+        for c in caches:
+            pkv.store_c8(c, k_prior, v_prior, cu_q_lens=cu_prior, context_lengths=prior, block_table=bt,
+                         max_q_len=mql)
+        del k_prior, v_prior
+        rows = int(w.context_lengths.sum())
+        outs = [(torch.empty((rows, w.num_kv_heads, w.head_dim), dtype=torch.bfloat16, device=dev),
+                 torch.empty((rows, w.num_kv_heads, w.head_dim), dtype=torch.bfloat16, device=dev))
+                for _ in range(2)]
+        # the dequant reads every position < context length: the prior tokens plus the new ones,
+        # which hold whatever the pool held (timing only)
+
+        def launch(i):
+            ko, vo = outs[i % 2]
+            pkv.dequant(caches[i % 2], bt, ctx, k_out=ko, v_out=vo)
+        kernel = "pkv_dequant (gather of every position to bf16 rows)"
+    steps = max(args.steps // 10, 5)
+    for i in range(max(args.warmup // 5, 2)):
+        launch(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(stream)
+        launch(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    times = [a.elapsed_time(b) for a, b in evs]
+    ms = float(np.median(times))
+    achieved = (read_b + write_b) / (ms * 1e-3) / 1e9
+    res = {
+        "op": args.op, "workload": w.name, "quant_mode": w.quant_mode,
+        "tokens": units, "bytes_read": read_b, "bytes_written": write_b,
+        "ms_median": round(ms, 5), "ms_mean": round(float(np.mean(times)), 5), "launches": steps,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes_per_launch": read_b + write_b, "avg_launch_ms": round(ms, 5)},
     }
     print(json.dumps(res), flush=True)
 

@@ -264,6 +264,10 @@ int pkv_store_c8(const pkv_cache_t* cache, const void* k_new, const void* v_new,
     int q = cu_q_lens ? (max_q_len > 0 ? max_q_len : num_tokens) : 1;
     a.nbt = (int)((q + cache->block_size - 2) / cache->block_size + 1);
     if (a.nbt > max_blocks_per_seq && !slot_mapping) a.nbt = max_blocks_per_seq;
+    // chunks of more than one token per sequence are stored by 16-slot tiles (q tokens from any
+    // position touch at most (q + 14) / 16 + 1 tiles); single tokens by the per-token kernel
+    a.ntile = (cu_q_lens && !slot_mapping && q > 1) ? (int)((q + 14) / 16 + 1) : 0;
+    if (a.ntile > max_blocks_per_seq * (cache->block_size / 16)) a.ntile = max_blocks_per_seq * (cache->block_size / 16);
     return hip_status(pkv::launch_store(a, cache->head_dim, quant_mode, static_cast<hipStream_t>(stream)));
 }
 

@@ -24,7 +24,8 @@ struct StoreArgs {
     int log2bs;
     int mbs;
     int batch;
-    int nbt;  // blocks a sequence's new tokens can touch (per-block launch)
+    int nbt;    // blocks a sequence's new tokens can touch (per-block launch)
+    int ntile;  // 16-slot tiles a sequence's new tokens can touch (tile launch; 0: per-token kernel)
 };
 
 struct DequantArgs {
