@@ -105,17 +105,21 @@ __global__ __launch_bounds__(256) void mla_store_kernel(MlaArgs a) {
         am = fmaxf(am, fabsf(x[e]));
     }
     const float s = absmax_scale(group_max<kWave>(am));
+    int codes[8];
+    quant_row_absmax<8>(x, s, codes);
     uint32_t c0 = 0, c1 = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        c0 |= (uint32_t)(quant_code(x[e], s) & 255) << (8 * e);
-        c1 |= (uint32_t)(quant_code(x[4 + e], s) & 255) << (8 * e);
+        c0 |= (uint32_t)(codes[e] & 255) << (8 * e);
+        c1 |= (uint32_t)(codes[4 + e] & 255) << (8 * e);
     }
     *reinterpret_cast<uint2*>(a.latent + row * DC + 8 * lane) = make_uint2(c0, c1);
     // rotary row: channel lane
     const float xr = bf16_to_f32(a.rope_new[(int64_t)t * DR + lane]);
     const float sr = absmax_scale(group_max<kWave>(fabsf(xr)));
-    a.rope[row * DR + lane] = (int8_t)quant_code(xr, sr);
+    int cr;
+    quant_row_absmax<1>(&xr, sr, &cr);
+    a.rope[row * DR + lane] = (int8_t)cr;
     if (lane == 0) {
         a.ls[row] = s;
         a.rs[row] = sr;

@@ -301,6 +301,7 @@ int pkv_dequant(const pkv_cache_t* cache, const int32_t* block_table, int32_t ma
     a.batch = batch;
     a.vec_ok = (token_stride % 8 == 0) && (head_stride % 8 == 0) && (!k_out || aligned(k_out, 16)) &&
                (!v_out || aligned(v_out, 16));
+    a.nchunk = (int)cdiv((int64_t)max_blocks_per_seq * cache->block_size, 128);
     return hip_status(pkv::launch_dequant(a, cache->head_dim, cache->quant_mode, static_cast<hipStream_t>(stream)));
 }
 

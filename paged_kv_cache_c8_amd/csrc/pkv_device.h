@@ -52,6 +52,31 @@ __device__ __forceinline__ int quant_code(float x, float s) {
 
 __device__ __forceinline__ float absmax_scale(float absmax) { return absmax / 127.0f; }
 
+// The same codes as quant_code for the values x of a row whose scale is an absmax scale,
+// s = fl32(A / 127) of a bf16 A >= |x| (per-token rows, per-block rows, MLA rows), with one IEEE
+// division per row instead of one per value: r = fl32(1 / s), and per value Markstein's correction
+// step (P. Markstein, IBM J. Res. Develop. 34(1), 1990): q0 = fl32(x r), e = x - q0 s (one fused
+// rounding), q = fl32(q0 + e r).  q can differ from fl32(x / s) in its last bit, but rint(q) never
+// differs from rint(fl32(x / s)) on that domain when s >= 2^-100 (checked on the host for every such
+// bf16 pair, about 1.05e9); smaller scales (and s == 0) take quant_code itself.
+template <int N>
+__device__ __forceinline__ void quant_row_absmax(const float* x, float s, int* codes) {
+    if (s >= 0x1p-100f) {
+        const float r = 1.0f / s;
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+            const float q0 = x[e] * r;
+            const float er = __builtin_fmaf(-q0, s, x[e]);
+            float q = __builtin_rintf(__builtin_fmaf(er, r, q0));
+            q = fminf(fmaxf(q, -128.0f), 127.0f);
+            codes[e] = (int)q;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < N; ++e) codes[e] = quant_code(x[e], s);
+    }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Cross-lane exchange.  Within a row of 16 lanes, DPP moves data without LDS traffic:
 //   stride 1: quad_perm [1,0,3,2]     stride 2: quad_perm [2,3,0,1]

@@ -46,6 +46,7 @@ struct DequantArgs {
     int mbs;
     int batch;
     int vec_ok;  // outputs and strides allow 16-byte stores
+    int nchunk;  // 128-position chunks of the longest sequence the block table holds
 };
 
 struct DecodeArgs {

@@ -7,13 +7,13 @@
 //
 //   Chunk and prompt stores (cu_q_lens given, up to more than one token per sequence) go by
 //   16-slot tiles, the unit of the V page: one wave per (sequence, tile of 16 positions, KV head).
-//   Lane (s, q) = (lane / 4, lane % 4) loads channels q D/4 .. of slot s's new token as 16-byte
-//   bf16 loads; a quad DPP max gives each token's absmax, scale = fl32(absmax / 127), each lane
-//   divides (IEEE) and rounds half to even.  The K rows of the tile are 16 D contiguous bytes,
-//   written 16 bytes per store; the V codes go through 16 D bytes of LDS (token rows in,
-//   channel columns out), so each lane writes whole 16-slot channel rows of the channel-major V
-//   tile, 16 bytes per store.  A tile the call fills only in part keeps the bytes of its other
-//   slots (read back and merged; one wave is the tile's only writer).
+//   In each step the wave reads whole token rows of its tile (16-byte bf16 loads; a row's lanes
+//   meet in a DPP max for its absmax; scale = fl32(absmax / 127); codes rounded half to even from
+//   one reciprocal per row, the same codes as IEEE division) and writes whole 128-byte K rows; the
+//   V codes go through 16 D bytes of LDS (token rows in, channel rows out), so each 16-byte store
+//   covers 64 consecutive channel rows of the channel-major V tile.  A tile the call fills only in
+//   part keeps the bytes of its other slots (read back and merged; one wave is the tile's only
+//   writer).
 //   per token (mode 0): as above.  Decode-size stores (one token per sequence) and the
 //       slot_mapping form keep one wave per (token, KV head): each token is its own tile row.
 //   per block (mode 1): one workgroup per (sequence, block touched, KV head) - the single writer
@@ -119,15 +119,16 @@ __global__ __launch_bounds__(256) void store_token_kernel(StoreArgs a) {
             }
             am = group_max<kWave>(am);
             const float s = absmax_scale(am);
+            int codes[EPL];
+            quant_row_absmax<EPL>(x, s, codes);
             int8_t* dst = reinterpret_cast<int8_t*>(which ? a.v : a.k);
             if (which == 0) {
                 int8_t* row = dst + (page * a.bs + slot) * D + c0;
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) row[e] = (int8_t)quant_code(x[e], s);
+                for (int e = 0; e < EPL; ++e) row[e] = (int8_t)codes[e];
             } else {
 #pragma unroll
-                for (int e = 0; e < EPL; ++e)
-                    dst[v_elem(page, D, a.bs, c0 + e, slot)] = (int8_t)quant_code(x[e], s);
+                for (int e = 0; e < EPL; ++e) dst[v_elem(page, D, a.bs, c0 + e, slot)] = (int8_t)codes[e];
             }
             if (lane == 0) (which ? a.vs : a.ks)[page * a.bs + slot] = s;
         }
@@ -136,32 +137,38 @@ __global__ __launch_bounds__(256) void store_token_kernel(StoreArgs a) {
 
 // =============================================================================================
 // Tile stores
+//
+// A tile wave walks the tile's 16 token rows in steps: in step j, lane L takes the 8-channel chunk
+// L % CH of row j RPI + L / CH (CH = D / 8 chunks per row, RPI = 64 / CH rows per step), so each
+// load of the bf16 input rows and each store of K code rows covers RPI whole rows, and a row's
+// absmax is a max over its CH lanes.  The V codes go to LDS as token rows and come back out as
+// channel rows: lane L writes channels L + 64 c, so each 16-byte store covers 64 consecutive
+// 16-slot channel rows of the tile.  A tile the call fills only in part keeps the bytes of its other
+// slots (read back and merged; one wave is the tile's only writer).
 // =============================================================================================
 
 constexpr int TS = kVTile;  // slots per tile
 
-template <int N>
-__device__ __forceinline__ void load_bf16_row(const uint16_t* src, bool on, float* x) {
+template <int D>
+struct TileMap {
+    static constexpr int CH = D / 8;        // 8-channel chunks per row
+    static constexpr int RPI = kWave / CH;  // rows per step
+    static constexpr int NJ = TS / RPI;     // steps per tile
+    static constexpr int CPW = D / 64;      // V channel rows per lane
+};
+
+__device__ __forceinline__ void unpack_bf16x8(const u32x4& w, float* x) {
 #pragma unroll
-    for (int l = 0; l < N / 8; ++l) {
-        const u32x4 w = on ? load16(src + 8 * l) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[8 * l + e] = bf16_at(w, e);
-    }
+    for (int e = 0; e < 8; ++e) x[e] = bf16_at(w, e);
 }
 
-// N int8 codes (N a multiple of 16) packed four to a dword and stored as 16-byte pieces
-template <int N>
-__device__ __forceinline__ void store_codes(uint8_t* dst, const int* c) {
+__device__ __forceinline__ uint2 pack_codes8(const int* c) {
+    uint32_t w[2];
 #pragma unroll
-    for (int l = 0; l < N / 16; ++l) {
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            w[i] = (uint32_t)(c[16 * l + 4 * i] & 255) | ((uint32_t)(c[16 * l + 4 * i + 1] & 255) << 8) |
-                   ((uint32_t)(c[16 * l + 4 * i + 2] & 255) << 16) | ((uint32_t)(c[16 * l + 4 * i + 3] & 255) << 24);
-        *reinterpret_cast<uint4*>(dst + 16 * l) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
+    for (int i = 0; i < 2; ++i)
+        w[i] = (uint32_t)(c[4 * i] & 255) | ((uint32_t)(c[4 * i + 1] & 255) << 8) |
+               ((uint32_t)(c[4 * i + 2] & 255) << 16) | ((uint32_t)(c[4 * i + 3] & 255) << 24);
+    return make_uint2(w[0], w[1]);
 }
 
 // byte mask of dword w (slots 4w .. 4w+3) of a 16-slot int8 channel row: slots in [lo, hi)
@@ -172,39 +179,27 @@ __device__ __forceinline__ uint32_t slot_mask8(int w, int lo, int hi) {
     return m;
 }
 
-// The V codes of the tile, written row-major (slot s, channels q D/4 ..) to lds by the lanes that
-// hold a slot, read back as the channel rows this lane writes: channels (D/64) lane .. + D/64 - 1,
-// 16 slots each, four dwords per channel (byte i of dword w = slot 4w + i).
+// The tile's V codes from LDS token rows (byte slot * D + channel) to the lane's channel rows,
+// channels lane + 64 cc: four dwords of 16 slots each (byte i of dword w = slot 4w + i).
 template <int D>
-__device__ __forceinline__ void transpose_codes(uint8_t* lds, int lane, bool on, const int* codes,
-                                                uint32_t (*col)[4]) {
-    constexpr int CPL = D / 4;
-    if (on) store_codes<CPL>(lds + (lane >> 2) * D + (lane & 3) * CPL, codes);
-    __syncthreads();
+__device__ __forceinline__ void lds_channel_rows(const uint8_t* lds, int lane, uint32_t (*col)[4]) {
+    constexpr int CPW = TileMap<D>::CPW;
 #pragma unroll
-    for (int cc = 0; cc < D / 64; ++cc)
+    for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
         for (int w = 0; w < 4; ++w) col[cc][w] = 0u;
 #pragma unroll
-    for (int sl = 0; sl < TS; ++sl) {
-        if constexpr (D == 128) {
-            const uint32_t v = *reinterpret_cast<const uint16_t*>(lds + sl * D + 2 * lane);
-            col[0][sl >> 2] |= (v & 0xffu) << (8 * (sl & 3));
-            col[1][sl >> 2] |= ((v >> 8) & 0xffu) << (8 * (sl & 3));
-        } else {
-            const uint32_t v = lds[sl * D + lane];
-            col[0][sl >> 2] |= v << (8 * (sl & 3));
-        }
-    }
-    __syncthreads();  // lds is free again
+    for (int t = 0; t < TS; ++t)
+#pragma unroll
+        for (int cc = 0; cc < CPW; ++cc) col[cc][t >> 2] |= (uint32_t)lds[t * D + lane + 64 * cc] << (8 * (t & 3));
 }
 
 // One wave per (sequence, 16-position tile, KV head) of a chunk store; modes 0 (per token), 3 (per
 // channel) and 2 (bf16).
 template <int D, int MODE>
 __global__ __launch_bounds__(64) void store_tile_kernel(StoreArgs a) {
+    using M = TileMap<D>;
     constexpr int ESZ = MODE == 2 ? 2 : 1;
-    constexpr int CPL = D / 4;
     __shared__ __attribute__((aligned(16))) uint8_t lds[TS * D * ESZ];
     int r = blockIdx.x;
     const int h = r % a.hkv;
@@ -223,102 +218,104 @@ __global__ __launch_bounds__(64) void store_tile_kernel(StoreArgs a) {
     const int64_t page = (int64_t)a.bt[(int64_t)b * a.mbs + (p0 >> a.log2bs)] * a.hkv + h;
     const int sib = p0 & (a.bs - 1);  // the tile's first slot in its block
     const int lane = threadIdx.x;
-    const int sl = lane >> 2, q = lane & 3;
-    const bool on = sl >= lo && sl < hi;
-    const int64_t tok = (int64_t)a.cu_q[b] + (p0 + sl - prior);  // (only read when on)
+    const int rl = lane / M::CH, c8 = (lane % M::CH) * 8;
     const bool partial = lo > 0 || hi < TS;
     const int64_t vtile = page * D * a.bs + (int64_t)(sib / TS) * D * TS;  // element offset of the V tile
+    const int64_t tok0 = (int64_t)a.cu_q[b] + (p0 - prior);                // token of slot 0
 
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
-        const uint16_t* src = (which ? a.v_new : a.k_new) + (tok * a.hkv + h) * D + q * CPL;
+        const uint16_t* src = which ? a.v_new : a.k_new;
         if constexpr (MODE == 2) {
             uint16_t* kd = reinterpret_cast<uint16_t*>(a.k);
-            uint16_t* vd = reinterpret_cast<uint16_t*>(a.v);
-            u32x4 raw[CPL / 8];
 #pragma unroll
-            for (int l = 0; l < CPL / 8; ++l) raw[l] = on ? load16(src + 8 * l) : u32x4{0u, 0u, 0u, 0u};
-            if (which == 0) {
-                if (on) {
-                    uint16_t* row = kd + (page * a.bs + sib + sl) * D + q * CPL;
-#pragma unroll
-                    for (int l = 0; l < CPL / 8; ++l)
-                        *reinterpret_cast<uint4*>(row + 8 * l) = make_uint4(raw[l].x, raw[l].y, raw[l].z, raw[l].w);
+            for (int j = 0; j < M::NJ; ++j) {
+                const int sl = j * M::RPI + rl;
+                const bool on = sl >= lo && sl < hi;
+                const u32x4 v = on ? load16(src + ((tok0 + sl) * a.hkv + h) * D + c8) : u32x4{0u, 0u, 0u, 0u};
+                if (which == 0) {
+                    if (on) *reinterpret_cast<uint4*>(kd + (page * a.bs + sib + sl) * D + c8) = make_uint4(v.x, v.y, v.z, v.w);
+                } else {
+                    *reinterpret_cast<uint4*>(lds + (sl * D + c8) * 2) = make_uint4(v.x, v.y, v.z, v.w);
                 }
-                continue;
             }
-            // V: rows of bf16 to LDS, channel rows of 16 slots (32 bytes) out
-            if (on) {
+            if (which == 0) continue;
+            __builtin_amdgcn_wave_barrier();
+            // channel rows out: step k, lane L: channel 32 k + L / 2, slots 8 (L % 2) .. + 8
+            uint16_t* vd = reinterpret_cast<uint16_t*>(a.v);
 #pragma unroll
-                for (int l = 0; l < CPL / 8; ++l)
-                    *reinterpret_cast<uint4*>(lds + (sl * D + q * CPL + 8 * l) * 2) =
-                        make_uint4(raw[l].x, raw[l].y, raw[l].z, raw[l].w);
-            }
-            __syncthreads();
+            for (int k = 0; k < D / 32; ++k) {
+                const int c = 32 * k + (lane >> 1), s0 = 8 * (lane & 1);
+                uint32_t o[4];
 #pragma unroll
-            for (int cc = 0; cc < D / 64; ++cc) {
-                const int c = lane * (D / 64) + cc;
-                uint32_t o[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint32_t e0 = *reinterpret_cast<const uint16_t*>(lds + ((2 * i) * D + c) * 2);
-                    const uint32_t e1 = *reinterpret_cast<const uint16_t*>(lds + ((2 * i + 1) * D + c) * 2);
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t e0 = *reinterpret_cast<const uint16_t*>(lds + ((s0 + 2 * i) * D + c) * 2);
+                    const uint32_t e1 = *reinterpret_cast<const uint16_t*>(lds + ((s0 + 2 * i + 1) * D + c) * 2);
                     o[i] = e0 | (e1 << 16);
                 }
-                uint16_t* dst = vd + vtile + (int64_t)c * TS;
+                uint16_t* dst = vd + vtile + (int64_t)c * TS + s0;
                 if (partial) {
-                    const u32x4 o0 = load16(dst), o1 = load16(dst + 8);
-                    const uint32_t old[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+                    const u32x4 ov = load16(dst);
+                    const uint32_t old[4] = {ov.x, ov.y, ov.z, ov.w};
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const uint32_t m = ((2 * i >= lo && 2 * i < hi) ? 0xffffu : 0u) |
-                                           ((2 * i + 1 >= lo && 2 * i + 1 < hi) ? 0xffff0000u : 0u);
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = s0 + 2 * i;
+                        const uint32_t m = ((t >= lo && t < hi) ? 0xffffu : 0u) | ((t + 1 >= lo && t + 1 < hi) ? 0xffff0000u : 0u);
                         o[i] = (o[i] & m) | (old[i] & ~m);
                     }
                 }
                 *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-                *reinterpret_cast<uint4*>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
             }
         } else {
-            float x[CPL];
-            load_bf16_row<CPL>(src, on, x);
-            int codes[CPL];
-            float s = 0.0f;
-            if constexpr (MODE == 3) {  // static per-channel scales
-                const float* sc = (which ? a.vs : a.ks) + (int64_t)h * D + q * CPL;
+            float* scales = which ? a.vs : a.ks;
+            uint8_t* kd = reinterpret_cast<uint8_t*>(a.k);
 #pragma unroll
-                for (int e = 0; e < CPL; ++e) codes[e] = quant_code(x[e], sc[e]);
-            } else {
-                float am = 0.0f;
+            for (int j = 0; j < M::NJ; ++j) {
+                const int sl = j * M::RPI + rl;
+                const bool on = sl >= lo && sl < hi;
+                float x[8];
+                unpack_bf16x8(on ? load16(src + ((tok0 + sl) * a.hkv + h) * D + c8) : u32x4{0u, 0u, 0u, 0u}, x);
+                int codes[8];
+                float s = 0.0f;
+                if constexpr (MODE == 3) {  // static per-channel scales
+                    const float* sc = scales + (int64_t)h * D + c8;
 #pragma unroll
-                for (int e = 0; e < CPL; ++e) am = fmaxf(am, fabsf(x[e]));
-                am = group_max<4>(am);  // the four lanes of the slot
-                s = absmax_scale(am);
+                    for (int e = 0; e < 8; ++e) codes[e] = quant_code(x[e], sc[e]);
+                } else {
+                    float am = 0.0f;
 #pragma unroll
-                for (int e = 0; e < CPL; ++e) codes[e] = quant_code(x[e], s);
-            }
-            if (which == 0) {
-                if (on) store_codes<CPL>(reinterpret_cast<uint8_t*>(a.k) + (page * a.bs + sib + sl) * D + q * CPL, codes);
-            } else {
-                uint32_t col[D / 64][4];
-                transpose_codes<D>(lds, lane, on, codes, col);
-#pragma unroll
-                for (int cc = 0; cc < D / 64; ++cc) {
-                    uint8_t* dst = reinterpret_cast<uint8_t*>(a.v) + vtile + (int64_t)(lane * (D / 64) + cc) * TS;
-                    if (partial) {
-                        const u32x4 o = load16(dst);
-                        const uint32_t old[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-                        for (int w = 0; w < 4; ++w) {
-                            const uint32_t m = slot_mask8(w, lo, hi);
-                            col[cc][w] = (col[cc][w] & m) | (old[w] & ~m);
-                        }
-                    }
-                    *reinterpret_cast<uint4*>(dst) = make_uint4(col[cc][0], col[cc][1], col[cc][2], col[cc][3]);
+                    for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(x[e]));
+                    am = group_max<M::CH>(am);  // the row's CH lanes
+                    s = absmax_scale(am);
+                    quant_row_absmax<8>(x, s, codes);
+                }
+                const uint2 pk = pack_codes8(codes);
+                if (which == 0) {
+                    if (on) *reinterpret_cast<uint2*>(kd + (page * a.bs + sib + sl) * D + c8) = pk;
+                } else {
+                    *reinterpret_cast<uint2*>(lds + sl * D + c8) = pk;
+                }
+                if constexpr (MODE == 0) {
+                    if (on && (lane % M::CH) == 0) scales[page * a.bs + sib + sl] = s;
                 }
             }
-            if constexpr (MODE == 0) {
-                if (on && q == 0) (which ? a.vs : a.ks)[page * a.bs + sib + sl] = s;
+            if (which == 0) continue;
+            __builtin_amdgcn_wave_barrier();
+            uint32_t col[M::CPW][4];
+            lds_channel_rows<D>(lds, lane, col);
+#pragma unroll
+            for (int cc = 0; cc < M::CPW; ++cc) {
+                uint8_t* dst = reinterpret_cast<uint8_t*>(a.v) + vtile + (int64_t)(lane + 64 * cc) * TS;
+                if (partial) {
+                    const u32x4 o = load16(dst);
+                    const uint32_t old[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const uint32_t m = slot_mask8(w, lo, hi);
+                        col[cc][w] = (col[cc][w] & m) | (old[w] & ~m);
+                    }
+                }
+                *reinterpret_cast<uint4*>(dst) = make_uint4(col[cc][0], col[cc][1], col[cc][2], col[cc][3]);
             }
         }
     }
@@ -327,7 +324,7 @@ __global__ __launch_bounds__(64) void store_tile_kernel(StoreArgs a) {
 // Per-block scales: one workgroup of bs/16 tile waves per (sequence, block touched, KV head).
 template <int D>
 __global__ __launch_bounds__(512) void store_block_tiles_kernel(StoreArgs a) {
-    constexpr int CPL = D / 4;
+    using M = TileMap<D>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_all[];  // [bs / 16][TS * D]
     __shared__ float red[8];
     __shared__ float sold_s;
@@ -356,24 +353,28 @@ __global__ __launch_bounds__(512) void store_block_tiles_kernel(StoreArgs a) {
     const int p0 = j * a.bs + w * TS;
     const int nlo = min(max(lo_pos - p0, 0), TS), nhi = min(max(hi_pos - p0, 0), TS);  // new slots
     const int nold = min(max(n_old - w * TS, 0), TS);                                  // old slots [0, nold)
-    const int sl = lane >> 2, q = lane & 3;
-    const bool on = sl >= nlo && sl < nhi;
-    const int64_t tok = (int64_t)t0 + (p0 + sl - prior);
+    const int rl = lane / M::CH, c8 = (lane % M::CH) * 8;
+    const int64_t tok0 = (int64_t)t0 + (p0 - prior);
     const int64_t vtile = page * D * a.bs + (int64_t)w * D * TS;
-    const int64_t krow = (page * a.bs + w * TS + sl) * D + q * CPL;
+    const int64_t krow0 = (page * a.bs + w * TS) * D + c8;
 
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
-        const uint16_t* src = (which ? a.v_new : a.k_new) + (tok * a.hkv + h) * D + q * CPL;
+        const uint16_t* src = which ? a.v_new : a.k_new;
         float* sc = which ? a.vs : a.ks;
         uint8_t* dst = reinterpret_cast<uint8_t*>(which ? a.v : a.k);
         // the block's scale is read by thread 0 only (which also writes it last) and shared via LDS
         if (threadIdx.x == 0) sold_s = n_old > 0 ? sc[page] : 0.0f;
-        float x[CPL];
-        load_bf16_row<CPL>(src, on, x);
+        float x[M::NJ][8];
         float am = 0.0f;
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) am = fmaxf(am, fabsf(x[e]));
+        for (int jj2 = 0; jj2 < M::NJ; ++jj2) {
+            const int sl = jj2 * M::RPI + rl;
+            const bool on = sl >= nlo && sl < nhi;
+            unpack_bf16x8(on ? load16(src + ((tok0 + sl) * a.hkv + h) * D + c8) : u32x4{0u, 0u, 0u, 0u}, x[jj2]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(x[jj2][e]));
+        }
         am = group_max<kWave>(am);
         if (lane == 0) red[w] = am;
         __syncthreads();
@@ -382,59 +383,62 @@ __global__ __launch_bounds__(512) void store_block_tiles_kernel(StoreArgs a) {
         for (int i = 1; i < nw; ++i) a_new = fmaxf(a_new, red[i]);
         const float s = fmaxf(s_old, absmax_scale(a_new));
         const bool requant = n_old > 0 && s > s_old;
-        int codes[CPL];
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) codes[e] = quant_code(x[e], s);
-        if (which == 0) {
-            if (on) {
-                store_codes<CPL>(dst + krow, codes);
-            } else if (requant && sl < nold) {  // an old row: re-quantize its codes to the new scale
-                int old[CPL];
+        for (int jj2 = 0; jj2 < M::NJ; ++jj2) {
+            const int sl = jj2 * M::RPI + rl;
+            const bool on = sl >= nlo && sl < nhi;
+            int codes[8];
+            quant_row_absmax<8>(x[jj2], s, codes);  // s is fl32(A / 127) of the block's bf16 absmax A >= |x|
+            if (which == 0) {
+                if (on) {
+                    *reinterpret_cast<uint2*>(dst + krow0 + sl * D) = pack_codes8(codes);
+                } else if (requant && sl < nold) {  // an old row: re-quantize its codes to the new scale
+                    const uint2 ov = *reinterpret_cast<const uint2*>(dst + krow0 + sl * D);
+                    int oc[8];
 #pragma unroll
-                for (int l = 0; l < CPL / 16; ++l) {
-                    const u32x4 v = load16(dst + krow + 16 * l);
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) old[16 * l + e] = quant_code((float)(int8_t)((word(v, e >> 2) >> (8 * (e & 3))) & 0xffu) * s_old, s);
+                    for (int e = 0; e < 8; ++e)
+                        oc[e] = quant_code((float)(int8_t)(((e < 4 ? ov.x : ov.y) >> (8 * (e & 3))) & 0xffu) * s_old, s);
+                    *reinterpret_cast<uint2*>(dst + krow0 + sl * D) = pack_codes8(oc);
                 }
-                store_codes<CPL>(dst + krow, old);
+            } else {
+                *reinterpret_cast<uint2*>(lds + sl * D + c8) = pack_codes8(codes);
             }
-        } else {
-            uint32_t col[D / 64][4];
-            transpose_codes<D>(lds, lane, on, codes, col);
-            const bool any_new = nhi > nlo;
-            if (any_new || (requant && nold > 0)) {
+        }
+        if (which == 1 && (nhi > nlo || (requant && nold > 0))) {
+            __builtin_amdgcn_wave_barrier();
+            uint32_t col[M::CPW][4];
+            lds_channel_rows<D>(lds, lane, col);
 #pragma unroll
-                for (int cc = 0; cc < D / 64; ++cc) {
-                    uint8_t* vd = dst + vtile + (int64_t)(lane * (D / 64) + cc) * TS;
-                    if (nlo > 0 || nhi < TS) {  // other slots: kept, or re-quantized when old and the scale grew
-                        const u32x4 o = load16(vd);
-                        uint32_t old[4] = {o.x, o.y, o.z, o.w};
-                        if (requant) {
-#pragma unroll
-                            for (int ww = 0; ww < 4; ++ww) {
-                                uint32_t nw8 = 0;
-#pragma unroll
-                                for (int i = 0; i < 4; ++i) {
-                                    const int slot = 4 * ww + i;
-                                    uint32_t byte = (old[ww] >> (8 * i)) & 0xffu;
-                                    if (slot < nold) byte = (uint32_t)(quant_code((float)(int8_t)byte * s_old, s) & 255);
-                                    nw8 |= byte << (8 * i);
-                                }
-                                old[ww] = nw8;
-                            }
-                        }
+            for (int cc = 0; cc < M::CPW; ++cc) {
+                uint8_t* vd = dst + vtile + (int64_t)(lane + 64 * cc) * TS;
+                if (nlo > 0 || nhi < TS) {  // other slots: kept, or re-quantized when old and the scale grew
+                    const u32x4 o = load16(vd);
+                    uint32_t old[4] = {o.x, o.y, o.z, o.w};
+                    if (requant) {
 #pragma unroll
                         for (int ww = 0; ww < 4; ++ww) {
-                            const uint32_t m = slot_mask8(ww, nlo, nhi);
-                            col[cc][ww] = (col[cc][ww] & m) | (old[ww] & ~m);
+                            uint32_t nw8 = 0;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int slot = 4 * ww + i;
+                                uint32_t byte = (old[ww] >> (8 * i)) & 0xffu;
+                                if (slot < nold) byte = (uint32_t)(quant_code((float)(int8_t)byte * s_old, s) & 255);
+                                nw8 |= byte << (8 * i);
+                            }
+                            old[ww] = nw8;
                         }
                     }
-                    *reinterpret_cast<uint4*>(vd) = make_uint4(col[cc][0], col[cc][1], col[cc][2], col[cc][3]);
+#pragma unroll
+                    for (int ww = 0; ww < 4; ++ww) {
+                        const uint32_t m = slot_mask8(ww, nlo, nhi);
+                        col[cc][ww] = (col[cc][ww] & m) | (old[ww] & ~m);
+                    }
                 }
+                *reinterpret_cast<uint4*>(vd) = make_uint4(col[cc][0], col[cc][1], col[cc][2], col[cc][3]);
             }
         }
         if (threadIdx.x == 0) sc[page] = s;
-        __syncthreads();  // red[] is reused by the V pass
+        __syncthreads();  // red[] and sold_s are reused by the V pass
     }
 }
 

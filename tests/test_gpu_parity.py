@@ -13,6 +13,7 @@ import gen
 import oracle
 import paged_kv_cache_c8_amd as pkv
 from tests.gpu_harness import Run, bits, i32
+from tests.helpers import v_token_major
 
 pytestmark = pytest.mark.gpu
 
@@ -204,7 +205,25 @@ def test_exhaustive_bf16_sweep_through_store(d):
     assert np.array_equal(cache.v_scale.cpu().numpy().view(np.uint32), hc.v_scale.view(np.uint32))
     zero = np.flatnonzero(vals == 0)  # +0 and -0: scale 0 and every code 0
     assert len(zero) == 2 and np.all(hc.k_scale.reshape(-1)[zero] == 0)
-    assert np.all(cache.k.cpu().numpy().reshape(t, d)[zero] == 0)
+    assert np.all(cache.k.cpu().numpy().reshape(-1, d)[:t][zero] == 0)
+    # the same rows as one prompt of a single sequence (the 16-slot tile kernel), and split into
+    # ragged chunks of several sequences (tiles the call fills in part)
+    bt = torch.arange(nb, dtype=torch.int32, device=dev).view(1, nb)
+    for lens in ([t], [5, 700, t - 705]):
+        cache2 = pkv.Cache(0, nb, 1, bs, d, device=dev)
+        cache2.v.fill_(77)  # slots of a partly filled tile keep what they held
+        done = 0
+        for n in lens:
+            pkv.store_c8(cache2, x[done:done + n], x[done:done + n], cu_q_lens=torch.tensor([0, n], dtype=torch.int32, device=dev),
+                         context_lengths=torch.tensor([done + n], dtype=torch.int32, device=dev), block_table=bt,
+                         max_q_len=n)
+            done += n
+        torch.cuda.synchronize()
+        assert np.array_equal(cache2.k.cpu().numpy(), hc.k)
+        assert np.array_equal(cache2.k_scale.cpu().numpy().view(np.uint32), hc.k_scale.view(np.uint32))
+        assert np.array_equal(cache2.v_scale.cpu().numpy().view(np.uint32), hc.v_scale.view(np.uint32))
+        vt = v_token_major(cache2.v.cpu().numpy(), bs).reshape(-1, d)[:t]
+        assert np.array_equal(vt, v_token_major(hc.v, bs).reshape(-1, d)[:t])
 
 
 def test_slot_mapping_store_with_skips():
