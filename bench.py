@@ -57,6 +57,10 @@ def parse():
                     help="paged MLA (latent cache) workload index instead of the GQA ones (1 = DeepSeek-V3-shaped)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain device copy of known size (for scaling HBM byte counters)")
+    ap.add_argument("--separate-store", action="store_true",
+                    help="a decode batch's store as its own call before the decode (default: one call)")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="the default run measures the long-context decode too and reports it as 'secondary'")
     ap.add_argument("--op", default="decode", choices=["decode", "store-fill", "dequant"],
                     help="decode: the decode step (default); store-fill: the prompt-style store of every "
                          "prior token of the workload; dequant: the gather of the whole cache to bf16 rows")
@@ -168,6 +172,20 @@ def main():
     if args.op != "decode":
         main_codec(args)
         return
+    res = run_decode(args, args.config, args.quant_mode, not args.no_cpu_baseline)
+    default_flags = (args.kernel == 0 and args.split_tokens == 0 and args.window == 0 and args.partition == 0
+                     and args.quant_mode is None and not args.separate_store)
+    if args.config == 1 and default_flags and not args.no_secondary:
+        # the other target workload, measured the same way (no CPU leg), reported beside the first
+        sec = run_decode(args, 2, None, False)
+        res["secondary"] = {k: sec[k] for k in ("value", "unit", "ms_per_step", "ms_per_step_median", "pct_of_peak",
+                                                "tokens_per_s", "kv_tokens_per_s", "bytes_per_step", "roofline")}
+        res["secondary"]["workload"] = sec["config"]["workload"]
+    print(json.dumps(res), flush=True)
+
+
+def run_decode(args, config_index, quant_mode, with_cpu):
+    """One workload's decode step, timed; returns the result record."""
 
     import torch
 
@@ -176,7 +194,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = gen.make_config(args.config, quant_mode=args.quant_mode)
+    w = gen.make_config(config_index, quant_mode=quant_mode)
     t = gen.gen_tensors(w, device=dev)
     k_prior, k_new = gen.split_prior_new(w, t["k_all"])
     v_prior, v_new = gen.split_prior_new(w, t["v_all"])
@@ -221,10 +239,21 @@ def main():
                        split_tokens=args.split_tokens, kernel=args.kernel, window=args.window,
                                          partition=args.partition)
 
+    # a decode batch (one new token per sequence) runs its store and attention as one call
+    fused = w.decode_only and not args.separate_store
+
+    def store_decode(c):
+        pkv.store_decode_gqa(q, k_new, v_new, c, bt, ctx, scale, out=out, workspace=workspace,
+                             split_tokens=args.split_tokens, kernel=args.kernel, window=args.window,
+                             partition=args.partition)
+
     def step(i):
         c = caches[i % reps]
-        store(c)
-        decode(c)
+        if fused:
+            store_decode(c)
+        else:
+            store(c)
+            decode(c)
 
     for i in range(args.warmup):
         step(i)
@@ -243,42 +272,53 @@ def main():
     wall = time.perf_counter() - wall0
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
-    # ---- dominant kernel: the decode call, bracketed by events on the launch stream
+    # ---- dominant call: the store + decode call (a decode batch) or the decode call, bracketed by
+    #      events on the launch stream (the current stream)
+    stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     for i in range(args.steps):
         c = caches[i % reps]
-        store(c)
-        evs[i][0].record()
-        decode(c)
-        evs[i][1].record()
+        if not fused:
+            store(c)
+        evs[i][0].record(stream)
+        if fused:
+            store_decode(c)
+        else:
+            decode(c)
+        evs[i][1].record(stream)
     torch.cuda.synchronize()
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    call_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_ms = float(np.mean(call_ms))
+    call_bytes = decode_bytes + (store_bytes if fused else 0)
 
     step_s = ms_per_step * 1e-3
     value = touched / step_s / 1e9
     new_tokens = w.num_new_tokens if not w.decode_only else int((w.context_lengths > 0).sum())
-    achieved = decode_bytes / (dec_ms * 1e-3) / 1e9
+    achieved = call_bytes / (dec_ms * 1e-3) / 1e9
     # the counters were taken with the library's own choice of kernel and split
-    default_plan = args.kernel == 0 and args.split_tokens == 0 and args.window == 0 and args.partition == 0
-    mode_key = "" if args.quant_mode is None else f".mode{args.quant_mode}"
-    traffic = traffic_record(f"decode.config{args.config}{mode_key}") if default_plan else None
+    default_plan = (args.kernel == 0 and args.split_tokens == 0 and args.window == 0 and args.partition == 0
+                    and not args.separate_store)
+    mode_key = "" if quant_mode is None else f".mode{quant_mode}"
+    traffic = traffic_record(f"decode.config{config_index}{mode_key}") if default_plan else None
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if with_cpu:
         cpu = cpu_baseline(w, t, args.cpu_seconds, touched, new_tokens, args.window)
 
     dtype = {0: "int8", 1: "int8", 2: "bf16", 3: "int8"}[w.quant_mode]
     roofline = {
         "bound": "hbm",
-        "kernel": "pkv_decode_gqa (split-KV partial + log-sum-exp merge)",
+        "kernel": ("pkv_store_decode_gqa (new-token store + split-KV partial, log-sum-exp merge)" if fused
+                   else "pkv_decode_gqa (split-KV partial + log-sum-exp merge)"),
         "achieved": round(achieved, 2),
         "peak": PEAK_HBM_GBS,
         "unit": "GB/s",
         "frac": round(achieved / PEAK_HBM_GBS, 4),
         "traffic": traffic,
-        "algorithmic_bytes_per_launch": decode_bytes,
+        "algorithmic_bytes_per_launch": call_bytes,
         "avg_launch_ms": round(dec_ms, 5),
+        "median_launch_ms": round(float(np.median(call_ms)), 5),
     }
     if w.name.startswith("paged-prefill"):
         # a prompt's attention is a dense contraction: 2 * 2 * D flops per visible (query head, key)
@@ -299,6 +339,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_median": round(float(np.median(call_ms)), 5) if fused else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -312,6 +353,7 @@ def main():
             "cache_replicas": reps, "split_tokens": plan["split_tokens"], "num_splits": plan["num_splits"],
             "window": args.window,
             "kernel": {1: "valu", 2: "mfma-f16", 3: "mfma-i8"}[plan["kernel"]],
+            "store": "in the decode call" if fused else "separate call",
             "parallelism": "single-gpu",
         },
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
@@ -322,7 +364,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(res), flush=True)
+    return res
 
 
 def codec_bytes(w, op):
@@ -620,7 +662,10 @@ def mla_cpu_baseline(w, t, budget_s, touched):
 def cpu_baseline(w, t, budget_s, touched, new_tokens, window=0):
     """The oracle as it stands (plain C, fp64 attention), timed on this host's cores on a bounded
     sample of the same workload: whole steps (store of the new tokens + attention of every query)
-    over as many sequences as fit in the time budget."""
+    over as many sequences as fit in the time budget, with every core the process may use, and on
+    one thread over a smaller sample."""
+    import dataclasses
+
     import torch
 
     import oracle
@@ -628,66 +673,66 @@ def cpu_baseline(w, t, budget_s, touched, new_tokens, window=0):
     model, ncores = cpu_info()
     nthreads = max(1, min(ncores, 16))
     bits = lambda x: x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
-    # a sample of sequences small enough for the budget: estimate fp64 multiply-adds per sequence
     g = w.num_q_heads // w.num_kv_heads
     qlen = np.maximum(w.q_lens, 1)
     macs = w.context_lengths.astype(np.float64) * w.num_kv_heads * g * qlen * 2 * w.head_dim
-    est_rate = 2.0e8 * nthreads  # conservative multiply-adds per second
-    order = np.arange(w.batch)
-    sel, acc = [], 0.0
-    for b in order:
-        if acc + macs[b] > est_rate * budget_s / 3 and sel:
-            break
-        sel.append(b)
-        acc += macs[b]
-    sel = np.array(sel)
-    import dataclasses
-
-    ws = dataclasses.replace(w, batch=len(sel), context_lengths=w.context_lengths[sel].copy(),
-                             q_lens=w.q_lens[sel].copy(), block_table=w.block_table[sel].copy())
-    cu_ctx = w.cu_context
-    kv_idx = np.concatenate([np.arange(cu_ctx[b], cu_ctx[b + 1]) for b in sel])
-    dev = t["q"].device
-    idx = lambda a: torch.as_tensor(a, device=dev)
-    k_all = bits(t["k_all"].index_select(0, idx(kv_idx)))
-    v_all = bits(t["v_all"].index_select(0, idx(kv_idx)))
-    if w.decode_only:
-        qh = bits(t["q"].index_select(0, idx(sel)))
-    else:
-        cu_q = w.cu_q_lens
-        qh = bits(t["q"].index_select(0, idx(np.concatenate([np.arange(cu_q[b], cu_q[b + 1]) for b in sel]))))
-    hc = oracle.HostCache(w.quant_mode, w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
-    if w.quant_mode == 3:
-        hc.k_scale[...] = t["k_scale"].cpu().numpy()
-        hc.v_scale[...] = t["v_scale"].cpu().numpy()
-    cu_s = ws.cu_context
-    prior = ws.prior_lengths
-    pri = np.concatenate([np.arange(cu_s[b], cu_s[b] + prior[b]) for b in range(ws.batch)]).astype(np.int64)
-    new = np.concatenate([np.arange(cu_s[b] + prior[b], cu_s[b + 1]) for b in range(ws.batch)]).astype(np.int64)
-    if len(pri):
-        oracle.store(hc, k_all[pri], v_all[pri], cu_q_lens=ws.cu_prior.astype(np.int32), context_lengths=prior,
-                     block_table=ws.block_table)
-    cu = None if ws.decode_only else ws.cu_q_lens
-    kn, vn = np.ascontiguousarray(k_all[new]), np.ascontiguousarray(v_all[new])
-    scale = 1.0 / np.sqrt(w.head_dim)
-    times = []
-    t_start = time.perf_counter()
-    while True:
-        s0 = time.perf_counter()
-        oracle.store(hc, kn, vn, cu_q_lens=cu, context_lengths=ws.context_lengths, block_table=ws.block_table)
-        oracle.decode(hc, qh, ws.num_q_heads, ws.block_table, ws.context_lengths, scale, cu_q_lens=cu,
-                      nthreads=nthreads, want_f64=False, window=window)
-        times.append(time.perf_counter() - s0)
-        if time.perf_counter() - t_start > budget_s * 0.5 or len(times) >= 2000:
-            break
-    sec = float(np.median(times))
-    # the sample's share of the attention work (keys each sequence's queries see)
     seen = lambda x: x.context_lengths.astype(np.int64) - (
         np.minimum(np.maximum(x.prior_lengths.astype(np.int64) - window + 1, 0), x.context_lengths) if window > 0 else 0)
-    frac = float(seen(ws).sum()) / float(seen(w).sum())
-    # the sample's step time scaled to the whole batch (attention work is linear in context)
-    full_step = sec / frac
-    _, store_b = step_bytes(ws)
+    dev = t["q"].device
+    idx = lambda a: torch.as_tensor(a, device=dev)
+    scale = 1.0 / np.sqrt(w.head_dim)
+
+    def timed(threads, seconds):
+        # a sample of sequences small enough for the budget (conservative multiply-add rate)
+        est_rate = 2.0e8 * threads
+        sel, acc = [], 0.0
+        for b in range(w.batch):
+            if acc + macs[b] > est_rate * seconds / 3 and sel:
+                break
+            sel.append(b)
+            acc += macs[b]
+        sel = np.array(sel)
+        ws = dataclasses.replace(w, batch=len(sel), context_lengths=w.context_lengths[sel].copy(),
+                                 q_lens=w.q_lens[sel].copy(), block_table=w.block_table[sel].copy())
+        cu_ctx = w.cu_context
+        kv_idx = np.concatenate([np.arange(cu_ctx[b], cu_ctx[b + 1]) for b in sel])
+        k_all = bits(t["k_all"].index_select(0, idx(kv_idx)))
+        v_all = bits(t["v_all"].index_select(0, idx(kv_idx)))
+        if w.decode_only:
+            qh = bits(t["q"].index_select(0, idx(sel)))
+        else:
+            cu_q = w.cu_q_lens
+            qh = bits(t["q"].index_select(0, idx(np.concatenate([np.arange(cu_q[b], cu_q[b + 1]) for b in sel]))))
+        hc = oracle.HostCache(w.quant_mode, w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+        if w.quant_mode == 3:
+            hc.k_scale[...] = t["k_scale"].cpu().numpy()
+            hc.v_scale[...] = t["v_scale"].cpu().numpy()
+        cu_s = ws.cu_context
+        prior = ws.prior_lengths
+        pri = np.concatenate([np.arange(cu_s[b], cu_s[b] + prior[b]) for b in range(ws.batch)]).astype(np.int64)
+        new = np.concatenate([np.arange(cu_s[b] + prior[b], cu_s[b + 1]) for b in range(ws.batch)]).astype(np.int64)
+        if len(pri):
+            oracle.store(hc, k_all[pri], v_all[pri], cu_q_lens=ws.cu_prior.astype(np.int32), context_lengths=prior,
+                         block_table=ws.block_table)
+        cu = None if ws.decode_only else ws.cu_q_lens
+        kn, vn = np.ascontiguousarray(k_all[new]), np.ascontiguousarray(v_all[new])
+        times = []
+        t_start = time.perf_counter()
+        while True:
+            s0 = time.perf_counter()
+            oracle.store(hc, kn, vn, cu_q_lens=cu, context_lengths=ws.context_lengths, block_table=ws.block_table)
+            oracle.decode(hc, qh, ws.num_q_heads, ws.block_table, ws.context_lengths, scale, cu_q_lens=cu,
+                          nthreads=threads, want_f64=False, window=window)
+            times.append(time.perf_counter() - s0)
+            if time.perf_counter() - t_start > seconds * 0.5 or len(times) >= 2000:
+                break
+        sec = float(np.median(times))
+        # the sample's step time scaled to the whole batch (attention work is linear in the keys seen)
+        frac = float(seen(ws).sum()) / float(seen(w).sum())
+        return sec, sec / frac, ws, len(times)
+
+    sec, full_step, ws, n = timed(nthreads, budget_s * 0.75)
+    sec1, full1, ws1, n1 = timed(1, budget_s * 0.25)
     return {
         "value": round(touched / full_step / 1e9, 4),
         "unit": "GB/s",
@@ -695,11 +740,15 @@ def cpu_baseline(w, t, budget_s, touched, new_tokens, window=0):
         "kind": "oracle",
         "cpu_model": model,
         "host_cores_visible": ncores,
-        "sample": f"{len(sel)} of {w.batch} sequences ({int(ws.context_lengths.sum())} of "
-                  f"{int(w.context_lengths.sum())} context tokens), {len(times)} timed steps of store + "
-                  f"fp64 attention; scaled to the full batch by context share",
+        "sample": f"{ws.batch} of {w.batch} sequences ({int(ws.context_lengths.sum())} of "
+                  f"{int(w.context_lengths.sum())} context tokens), {n} timed steps of store + "
+                  f"fp64 attention; scaled to the full batch by the keys the queries see",
         "sample_step_s": round(sec, 4),
         "tokens_per_s": round(new_tokens / full_step, 2),
+        "value_1thread": round(touched / full1 / 1e9, 4),
+        "sample_1thread": f"{ws1.batch} sequences ({int(ws1.context_lengths.sum())} context tokens), {n1} timed "
+                          f"steps on one thread, scaled the same way",
+        "sample_step_s_1thread": round(sec1, 4),
     }
 
 

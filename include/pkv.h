@@ -229,6 +229,30 @@ int pkv_decode_gqa(const void *q, int32_t num_q_heads, const pkv_cache_t *cache,
                    int32_t max_q_len, float scale, void *out, float *lse_out, void *workspace,
                    size_t workspace_bytes, const pkv_decode_opts_t *opts, void *stream);
 
+/*
+ * pkv_store_decode_gqa - one decode step in one call: store each sequence's
+ * new K/V token, then attend (MojoStorePagedKVCacheC8 of PR #379 followed by
+ * MojoPagedDecodeGQA of the README's Op List, one query per sequence).
+ *
+ * The result equals pkv_store_c8(cache, k_new, v_new, batch, NULL, NULL,
+ * context_lengths, block_table, batch, max_blocks_per_seq, 1, mode) followed
+ * by pkv_decode_gqa(q, ..., cu_q_lens = NULL, max_q_len = 1, ...):
+ * k_new, v_new  bf16 [batch][num_kv_heads][head_dim], 4-byte aligned; the
+ *               token of sequence b goes to position context_lengths[b] - 1
+ *               (a sequence with context length 0 stores nothing).
+ * Other arguments, the workspace and errors as pkv_decode_gqa.  For per-token
+ * and per-channel caches decoded by the int8-score kernel with one row group
+ * per KV head (up to 16 query heads per KV head) the store happens inside the
+ * decode launch: the wave that attends to the new position quantizes the
+ * token, writes it to the cache and uses its codes directly; otherwise a
+ * store launch precedes the decode.
+ */
+int pkv_store_decode_gqa(const void *q, const void *k_new, const void *v_new, int32_t num_q_heads,
+                         const pkv_cache_t *cache, const int32_t *block_table,
+                         int32_t max_blocks_per_seq, const int32_t *context_lengths, int32_t batch,
+                         float scale, void *out, float *lse_out, void *workspace,
+                         size_t workspace_bytes, const pkv_decode_opts_t *opts, void *stream);
+
 /* The split plan pkv_decode_gqa would use, for tests and benchmarks.
  * Writes the keys per partition and the number of partitions per row group
  * (for a balanced partition: 0 and the number of waves), and the kernel

@@ -19,7 +19,7 @@ import os
 
 import torch  # loaded first: libpkv binds to the HIP runtime torch has already loaded
 
-__all__ = ["PkvError", "Cache", "lib", "store_c8", "dequant", "decode_gqa", "decode_gqa_noalloc",
+__all__ = ["PkvError", "Cache", "lib", "store_c8", "dequant", "decode_gqa", "decode_gqa_noalloc", "store_decode_gqa",
            "decode_workspace_size", "NOALLOC_SCRATCH_BYTES",
            "decode_plan", "MLACache", "mla_store_c8", "mla_decode", "mla_decode_workspace_size",
            "mla_decode_plan", "QUANT_PER_TOKEN", "QUANT_PER_BLOCK", "QUANT_NONE_BF16", "QUANT_PER_CHANNEL",
@@ -36,7 +36,8 @@ QUANT_PER_CHANNEL = 3
 # every symbol include/pkv.h declares
 EXPORTS = ("pkv_status_string", "pkv_version", "pkv_store_c8", "pkv_dequant",
            "pkv_decode_workspace_size", "pkv_decode_gqa", "pkv_decode_plan", "pkv_mla_store_c8",
-           "pkv_mla_decode_workspace_size", "pkv_mla_decode_plan", "pkv_mla_decode", "pkv_decode_gqa_noalloc")
+           "pkv_mla_decode_workspace_size", "pkv_mla_decode_plan", "pkv_mla_decode", "pkv_decode_gqa_noalloc",
+           "pkv_store_decode_gqa")
 
 NOALLOC_SCRATCH_BYTES = 32 << 20  # PKV_NOALLOC_SCRATCH_BYTES
 
@@ -95,6 +96,8 @@ def lib():
         L.pkv_decode_gqa.restype = ctypes.c_int
         L.pkv_decode_gqa_noalloc.argtypes = [P, I32, P, P, I32, P, P, I32, I32, ctypes.c_float, P, P, P, P]
         L.pkv_decode_gqa_noalloc.restype = ctypes.c_int
+        L.pkv_store_decode_gqa.argtypes = [P, P, P, I32, P, P, I32, P, I32, ctypes.c_float, P, P, P, SZ, P, P]
+        L.pkv_store_decode_gqa.restype = ctypes.c_int
         L.pkv_decode_plan.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32, P,
                                       ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]
         L.pkv_decode_plan.restype = ctypes.c_int
@@ -336,6 +339,40 @@ def decode_gqa(q, cache: Cache, block_table, context_lengths, scale, *, cu_q_len
                               _ptr(cu_q_lens), batch, int(max_q_len), float(scale), _ptr(out),
                               _ptr(lse_out), _ptr(workspace), ws_bytes, ctypes.byref(o), _stream(stream))
     _check(st, "pkv_decode_gqa")
+    return out
+
+
+def store_decode_gqa(q, k_new, v_new, cache: Cache, block_table, context_lengths, scale, *, out=None,
+                     lse_out=None, workspace=None, split_tokens=0, kernel=0, partition=0, window=0, stream=None):
+    """One decode step: store each sequence's new token (bf16 ``[B, Hkv, D]``, at position
+    ``context_lengths[b] - 1``) and attend with its one query ``q`` (bf16 ``[B, Hq, D]``)."""
+    _want(q, "q", torch.bfloat16, (None, None, cache.head_dim))
+    batch, hq = int(q.shape[0]), int(q.shape[1])
+    if hq % cache.num_kv_heads != 0:
+        raise ValueError(f"{hq} query heads are not a multiple of {cache.num_kv_heads} KV heads")
+    _want(k_new, "k_new", torch.bfloat16, (batch, cache.num_kv_heads, cache.head_dim))
+    _want(v_new, "v_new", torch.bfloat16, (batch, cache.num_kv_heads, cache.head_dim))
+    _want(context_lengths, "context_lengths", torch.int32, (batch,))
+    _want(block_table, "block_table", torch.int32, (batch, None))
+    mbs = int(block_table.shape[1])
+    _want(out, "out", torch.bfloat16, (batch, hq, cache.head_dim), optional=True)
+    _want(lse_out, "lse_out", torch.float32, (batch, hq), optional=True)
+    _want(workspace, "workspace", torch.uint8, ndim=1, optional=True)
+    _same_device(cache.k, q=q, k_new=k_new, v_new=v_new, block_table=block_table, context_lengths=context_lengths,
+                 out=out, lse_out=lse_out, workspace=workspace)
+    o = _opts(split_tokens, kernel, partition, window)
+    need = int(lib().pkv_decode_workspace_size(batch, hq, cache.num_kv_heads, cache.head_dim, mbs,
+                                               cache.block_size, 1, cache.quant_mode, ctypes.byref(o)))
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)  # no initial contents needed
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().pkv_store_decode_gqa(_ptr(q), _ptr(k_new), _ptr(v_new), hq, cache.ref, _ptr(block_table), mbs,
+                                    _ptr(context_lengths), batch, float(scale), _ptr(out), _ptr(lse_out),
+                                    _ptr(workspace), ws_bytes, ctypes.byref(o), _stream(stream))
+    _check(st, "pkv_store_decode_gqa")
     return out
 
 

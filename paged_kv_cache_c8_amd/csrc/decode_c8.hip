@@ -97,17 +97,84 @@ struct C8V {
 template <int D, int RT>
 constexpr int QS_I4 = 3 * (D / 64) * RT * kWave;
 
+// Bytes of the wave's LDS for a new token it stores: K codes [D], V codes [D], K and V scales.
+template <int D>
+constexpr int NT_BYTES = 2 * D + 16;
+
+// Quantize the new token of (sequence b, KV head h) at position pos, as the per-token store does
+// (per-token absmax scale, or the static per-channel scales), write its codes and scale into the
+// cache, and keep them in nt (LDS) for the wave's own attention: the wave then reads them from
+// there, not from the memory it has just written.  Lane l takes channels D/64 l ..
+template <int D, int MODE>
+__device__ __forceinline__ void store_new_token(const DecodeArgs& a, int b, int h, int pos, uint8_t* nt) {
+    constexpr int EPL = D / kWave;
+    const int lane = threadIdx.x & 63;
+    const int64_t page = (int64_t)a.bt[(int64_t)b * a.mbs + (pos >> a.log2bs)] * a.hkv + h;
+    const int slot = pos & (a.bs - 1);
+    float* nts = reinterpret_cast<float*>(nt + 2 * D);
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        const uint16_t* src = (which ? a.v_new : a.k_new) + ((int64_t)b * a.hkv + h) * D + lane * EPL;
+        float x[EPL];
+        if constexpr (EPL == 2) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(src);
+            x[0] = bf16_to_f32(w & 0xffffu);
+            x[1] = bf16_to_f32(w >> 16);
+        } else {
+            x[0] = bf16_to_f32(src[0]);
+        }
+        // the cache is the caller's writable memory (read through const pointers elsewhere)
+        float* scales = const_cast<float*>(which ? a.vs : a.ks);
+        uint8_t* cache = reinterpret_cast<uint8_t*>(const_cast<void*>(which ? a.v : a.k));
+        int codes[EPL];
+        float s = 0.0f;
+        if constexpr (MODE == 3) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) codes[e] = quant_code(x[e], scales[(int64_t)h * D + lane * EPL + e]);
+        } else {
+            float am = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) am = fmaxf(am, fabsf(x[e]));
+            am = group_max<kWave>(am);
+            s = absmax_scale(am);
+            quant_row_absmax<EPL>(x, s, codes);
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const int c = lane * EPL + e;
+            if (which == 0) cache[(page * a.bs + slot) * D + c] = (uint8_t)codes[e];
+            else cache[v_elem(page, D, a.bs, c, slot)] = (uint8_t)codes[e];
+            nt[which * D + c] = (uint8_t)codes[e];
+        }
+        if constexpr (MODE == 0) {
+            if (lane == 0) {
+                scales[page * a.bs + slot] = s;
+                nts[which] = s;
+            }
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
 template <int D, int MODE, int J, int RT, bool WIN>
-__device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, const int h, const int qlen,
-                                           const int qrow0, const int prior, const int r0, const int nvalid,
-                                           const int t_seg0, const int t_seg1, const int64_t pslot,
-                                           int* const bt_s, i4* const qs) {
+__device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b_, const int h_, const int qlen_,
+                                           const int qrow0_, const int prior_, const int r0_, const int nvalid_,
+                                           const int t_seg0_, const int t_seg1_, const int64_t pslot,
+                                           int* const bt_s, i4* const qs, uint8_t* const nt) {
     static_assert(MODE == 0 || MODE == 1 || MODE == 3, "int8 cache modes only");
     static_assert(J == 1 || RT == 1, "several row tiles only with one subset class");
     constexpr int KSTEP = D / 64;                     // 64-channel steps of the score MFMA
     constexpr int DT = D / 16;                        // 16-channel output tiles
     constexpr int NSLOT = 4 / J;                      // subsets per column per block
 
+    // the item's and segment's values are the same in every lane: kept in scalar registers, so the
+    // key loop and every branch on them are uniform control flow (lane-divergent control flow
+    // around the matrix-core instructions, which read every lane's operands, must not arise)
+    const int b = __builtin_amdgcn_readfirstlane(b_), h = __builtin_amdgcn_readfirstlane(h_);
+    const int qlen = __builtin_amdgcn_readfirstlane(qlen_), qrow0 = __builtin_amdgcn_readfirstlane(qrow0_);
+    const int prior = __builtin_amdgcn_readfirstlane(prior_), r0 = __builtin_amdgcn_readfirstlane(r0_);
+    const int nvalid = __builtin_amdgcn_readfirstlane(nvalid_);
+    const int t_seg0 = __builtin_amdgcn_readfirstlane(t_seg0_), t_seg1 = __builtin_amdgcn_readfirstlane(t_seg1_);
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;  // column (scores, weights, accumulators); channel (V operand)
     const int g = lane >> 4;  // lane group
@@ -140,6 +207,13 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
         for (int l = 0; l < 2 * KSTEP; ++l) qraw[rt][l] = rv ? load16(qp + 8 * l) : u32x4{0u, 0u, 0u, 0u};
     }
     causal = __any(causal);
+    // one decode step with its store: the wave whose keys end at the new token's position stores it
+    // (one query per sequence: the position is the item's last key, prior == t_seg1 - 1)
+    bool own_new = false;
+    if constexpr (MODE == 0 || MODE == 3) {
+        own_new = a.k_new != nullptr && prior >= t_seg0 && prior < t_seg1;
+        if (own_new) store_new_token<D, MODE>(a, b, h, prior, nt);
+    }
     // the largest window start over the group's rows (its last row's): blocks below it are masked
     const int lo_hi = WIN ? win_lo(a.window, prior + (r0 + nvalid - 1) / a.g) : 0;
 
@@ -482,16 +556,59 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b, con
                     pacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, bq[rt], pacc[rt], 0, 0, 0);
             }
         };
+        // The block that holds the stored new token takes its codes and scales from nt (the cache
+        // was written by this wave a moment ago; its loads of that slot are replaced, not trusted).
+        // The block is the same for the whole wave; which lanes hold the key depends on the lane,
+        // so the replacement is made of selects, with no lane-divergent branch.
+        auto patch_new = [&](const int T, C8V<D>& VC) {
+            const int kk = prior - T;  // the new key within the block
+            const int kc = kk >> 4, qn = 2 * ((kk >> 3) & 1) + ((kk >> 2) & 1), ii = kk & 3;
+            const bool krow = rho == 4 * kc + ii;  // K: the score row of that key, channels g 16 KSTEP ..
+    #pragma unroll
+            for (int m = 0; m < KSTEP; ++m) {
+                const uint4 w = *reinterpret_cast<const uint4*>(nt + g * 16 * KSTEP + 16 * m);
+                const i4 val = i4{(int)w.x, (int)w.y, (int)w.z, (int)w.w};
+    #pragma unroll
+                for (int qq = 0; qq < 4; ++qq) R.k[qq][m] = krow && qq == qn ? val : R.k[qq][m];
+            }
+            const bool vgrp = g == kc;  // the lane group whose keys hold it
+            if constexpr (MODE == 0) {  // its K and V scales
+                const float* nts = reinterpret_cast<const float*>(nt + 2 * D);
+                const float ksn = nts[0], vsn = nts[1];
+                const bool col = vgrp && jcol == qn % J;
+    #pragma unroll
+                for (int u = 0; u < NSLOT; ++u)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool hit = col && u == qn / J && i == ii;
+                        R.ks[u][i] = hit ? ksn : R.ks[u][i];
+                        R.vs[u][i] = hit ? vsn : R.vs[u][i];
+                    }
+            }
+            // V: byte kk % 16 of the lane's 16-slot rows of channels n + 16 dt
+            const int sh = 8 * (kk & 3), wd = (kk >> 2) & 3;
+            const uint32_t keep = ~(0xffu << sh);
+    #pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const uint32_t put = (uint32_t)nt[D + n + 16 * dt] << sh;
+                const u32x4 o = VC.v[dt];
+                VC.v[dt] = u32x4{vgrp && wd == 0 ? (o.x & keep) | put : o.x, vgrp && wd == 1 ? (o.y & keep) | put : o.y,
+                                 vgrp && wd == 2 ? (o.z & keep) | put : o.z, vgrp && wd == 3 ? (o.w & keep) | put : o.w};
+            }
+        };
         for (int T = t_begin;;) {
+            if (own_new && prior >= T && prior < T + BLK) patch_new(T, v0);
             block(T, v0, v1);
             T += BLK;
             if (T >= t_end) break;
+            if (own_new && prior >= T && prior < T + BLK) patch_new(T, v1);
             block(T, v1, v0);
             T += BLK;
             if (T >= t_end) break;
         }
 
     }
+
 
     // ---- merge the J columns of each row, normalise, write.  Lane (g, n) holds channels
     //      16 dt + 4g + i of column n.  Per-channel mode: sum_t w_t code_t,c * s_V,c is the
@@ -567,6 +684,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 
     constexpr int ROWS = J > 1 ? 16 / J : 16 * RT;
     __shared__ int bt_s[MAX_SPLIT_PAGES];
     __shared__ i4 qs[QS_I4<D, RT>];
+    __shared__ __attribute__((aligned(16))) uint8_t nt[NT_BYTES<D>];
     const int wi = blockIdx.x;
     const int rest = wi >> 3;
     const int u = (rest / a.nrg) * 8 + (wi & 7);
@@ -584,7 +702,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 
     if (t_begin >= it.kmax) return;
     const int t_end = min(t_begin + a.split_len, it.kmax);
     c8_segment<D, MODE, J, RT, WIN>(a, it.b, it.h, it.qlen, it.qrow0, it.prior, it.r0, it.nvalid, t_begin, t_end,
-                               a.nsplit > 1 ? (int64_t)item * a.nsplit + s : -1, bt_s, qs);
+                               a.nsplit > 1 ? (int64_t)item * a.nsplit + s : -1, bt_s, qs, nt);
 }
 
 // Balanced partition (sk_partition.h): one wave per segment of the plan.
@@ -593,12 +711,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 
     constexpr int ROWS = J > 1 ? 16 / J : 16 * RT;
     __shared__ int bt_s[MAX_SPLIT_PAGES];
     __shared__ i4 qs[QS_I4<D, RT>];
+    __shared__ __attribute__((aligned(16))) uint8_t nt[NT_BYTES<D>];
     extern __shared__ int kseq[];  // [batch + 1] prefix sums over sequences of their waves
     SkSegment sg;
     if (!sk_plan<ROWS, WIN>(a, batch, blockIdx.x, kseq, sg)) return;
     const ItemGeo& it = sg.it;
     c8_segment<D, MODE, J, RT, WIN>(a, it.b, it.h, it.qlen, it.qrow0, it.prior, it.r0, it.nvalid, sg.t0, sg.t1,
-                                    sg.pslot, bt_s, qs);
+                                    sg.pslot, bt_s, qs, nt);
 }
 
 template <int D, int MODE, int J, int RT, bool WIN>

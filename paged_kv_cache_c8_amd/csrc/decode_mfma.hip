@@ -7,7 +7,7 @@
 // ALUs only convert codes and do the softmax bookkeeping.
 //
 // One wave per (sequence, KV head, row group, key range): a fixed split, or a segment of the
-// balanced partition (sk_partition.h; bf16 pages at head_dim 128, planned over several rounds of
+// balanced partition (sk_partition.h; bf16 pages, planned over several rounds of
 // the resident waves); no barriers in the main loop.  A row group is RT tiles of 16 query rows
 // (row r = i * G + g: query i of the chunk, head g of the KV head's group); the keys of the range
 // are walked in blocks of 32, the next block's K, V and scales in flight while the current one
@@ -379,18 +379,20 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, const int b, c
         }
 
         // -------------------------------------------- P.V over the 32 keys (+ the weight sums)
+        // bf16 slots past the keys may hold any bit pattern: the lane's 8 keys as a mask per dword
+        // (selects, no lane-divergent branch in the key loop)
+        uint32_t vkeep[4] = {~0u, ~0u, ~0u, ~0u};
+        if constexpr (MODE == 2) {
+            const int tk = T + 8 * g;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2)
+                vkeep[e2] = tk + 2 * e2 + 1 < t_end ? ~0u : (tk + 2 * e2 < t_end ? 0xffffu : 0u);
+        }
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
             if constexpr (MODE == 2) {
-                uint32_t r[4] = {R.v[dt][0], R.v[dt][1], R.v[dt][2], R.v[dt][3]};
-                if (MASKED) {  // bf16 slots past the keys may hold any bit pattern
-                    const int tk = T + 8 * g;
-#pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2) {
-                        if (tk + 2 * e2 >= t_end) r[e2] = 0;
-                        else if (tk + 2 * e2 + 1 >= t_end) r[e2] &= 0xffffu;
-                    }
-                }
+                const uint32_t r[4] = {R.v[dt][0] & vkeep[0], R.v[dt][1] & vkeep[1], R.v[dt][2] & vkeep[2],
+                                       R.v[dt][3] & vkeep[3]};
                 const b8 bv = __builtin_bit_cast(b8, r);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
@@ -506,8 +508,8 @@ __global__ __launch_bounds__(64) void decode_mfma_sk_kernel(DecodeArgs a, int ba
 template <int D, int MODE, int RT>
 hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream) {
     const int64_t items = (int64_t)batch * a.hkv * a.nrg;
-    if (a.sk_waves > 0) {  // balanced partition (bf16 pages, head dim 128, one row tile)
-        if constexpr (MODE == 2 && RT == 1 && D == 128) {
+    if (a.sk_waves > 0) {  // balanced partition (bf16 pages, one row tile)
+        if constexpr (MODE == 2 && RT == 1) {
             if (items == 0) return hipSuccess;
             if (batch > SK_MAX_SEQS || a.sk_waves + items > 0x7fffffff) return hipErrorInvalidValue;
             const size_t lds = (size_t)(batch + 1) * sizeof(int);
@@ -557,15 +559,18 @@ hipError_t launch_mode(const DecodeArgs& a, int batch, int rt, int mode, hipStre
 
 }  // namespace
 
-// Head dim 128 only: the head-dim-64 instantiation of the balanced kernel returned wrong outputs
-// (correct lse) whenever several waves ran, and stays switched off (fixed splits serve it).
+// Waves of the balanced bf16 kernel one compute unit holds (bf16 pages, one row tile).
 int decode_mfma_waves_per_cu(int head_dim, int row_tiles, int mode, int batch, bool windowed) {
-    if (batch > SK_MAX_SEQS || row_tiles != 1 || mode != 2 || head_dim != 128) return 0;
+    if (batch > SK_MAX_SEQS || row_tiles != 1 || mode != 2 || (head_dim != 64 && head_dim != 128)) return 0;
     const size_t lds = (size_t)(batch + 1) * sizeof(int);
     int per_cu = 0;
-    const hipError_t e =
-        windowed ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_sk_kernel<128, 2, 1, true>, 64, lds)
-                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_sk_kernel<128, 2, 1, false>, 64, lds);
+    hipError_t e;
+    if (head_dim == 64)
+        e = windowed ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_sk_kernel<64, 2, 1, true>, 64, lds)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_sk_kernel<64, 2, 1, false>, 64, lds);
+    else
+        e = windowed ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_sk_kernel<128, 2, 1, true>, 64, lds)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_sk_kernel<128, 2, 1, false>, 64, lds);
     return e == hipSuccess && per_cu > 0 ? per_cu : 0;
 }
 

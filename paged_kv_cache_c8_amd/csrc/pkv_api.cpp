@@ -329,13 +329,26 @@ int pkv_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, in
     return PKV_OK;
 }
 
-int pkv_decode_gqa(const void* q, int32_t num_q_heads, const pkv_cache_t* cache, const int32_t* block_table,
-                   int32_t max_blocks_per_seq, const int32_t* context_lengths, const int32_t* cu_q_lens,
-                   int32_t batch, int32_t max_q_len, float scale, void* out, float* lse_out,
-                   void* workspace, size_t workspace_bytes, const pkv_decode_opts_t* opts, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// pkv_decode_gqa, and with k_new / v_new (one decode step's new tokens, cu_q_lens NULL) the store
+// of those tokens first: fused into the int8-score decode where it serves the call (per-token and
+// per-channel caches, one row group per KV head), else a store launch before the decode.  Every
+// argument is checked before anything is launched.
+int decode_impl(const void* q, int32_t num_q_heads, const pkv_cache_t* cache, const int32_t* block_table,
+                int32_t max_blocks_per_seq, const int32_t* context_lengths, const int32_t* cu_q_lens,
+                int32_t batch, int32_t max_q_len, float scale, void* out, float* lse_out,
+                void* workspace, size_t workspace_bytes, const pkv_decode_opts_t* opts, void* stream,
+                const void* k_new, const void* v_new) {
     int st = check_cache(cache);
     if (st != PKV_OK) return st;
     if (!q || !out || !block_table || !context_lengths) return PKV_ERR_INVALID_ARG;
+    if (k_new || v_new) {
+        if (!k_new || !v_new || cu_q_lens || !aligned(k_new, 4) || !aligned(v_new, 4)) return PKV_ERR_INVALID_ARG;
+        if (batch < 0 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID_ARG;
+    }
     if (!aligned(q, 16) || !aligned(out, 2) || (lse_out && !aligned(lse_out, 4))) return PKV_ERR_INVALID_ARG;
     if (!cu_q_lens) max_q_len = 1;
     if (max_q_len < 1) return PKV_ERR_INVALID_ARG;
@@ -384,12 +397,61 @@ int pkv_decode_gqa(const void* q, int32_t num_q_heads, const pkv_cache_t* cache,
     }
     a.prs = p.prs;
     hipStream_t st_ = static_cast<hipStream_t>(stream);
+    if (k_new) {
+        const bool fused = p.kernel == 3 && p.nrg == 1 &&
+                           (cache->quant_mode == PKV_QUANT_PER_TOKEN || cache->quant_mode == PKV_QUANT_PER_CHANNEL);
+        if (fused) {
+            a.k_new = static_cast<const uint16_t*>(k_new);
+            a.v_new = static_cast<const uint16_t*>(v_new);
+        } else {
+            pkv::StoreArgs sa;
+            std::memset(&sa, 0, sizeof sa);
+            sa.k = cache->k;
+            sa.v = cache->v;
+            sa.ks = cache->k_scale;
+            sa.vs = cache->v_scale;
+            sa.k_new = static_cast<const uint16_t*>(k_new);
+            sa.v_new = static_cast<const uint16_t*>(v_new);
+            sa.ctx = context_lengths;
+            sa.bt = block_table;
+            sa.num_tokens = batch;
+            sa.hkv = cache->num_kv_heads;
+            sa.bs = cache->block_size;
+            sa.log2bs = ilog2(cache->block_size);
+            sa.mbs = max_blocks_per_seq;
+            sa.batch = batch;
+            sa.nbt = 1;
+            const hipError_t e = pkv::launch_store(sa, cache->head_dim, cache->quant_mode, st_);
+            if (e != hipSuccess) return PKV_ERR_HIP;
+        }
+    }
     if (p.kernel == 1)
         return hip_status(pkv::launch_decode_valu(a, batch, cache->head_dim, p.rg, cache->quant_mode, st_));
     if (p.kernel == 3)
         return hip_status(
             pkv::launch_decode_c8(a, batch, cache->head_dim, p.classes, p.rg, cache->quant_mode, st_));
     return hip_status(pkv::launch_decode_mfma(a, batch, cache->head_dim, p.rg, cache->quant_mode, st_));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_decode_gqa(const void* q, int32_t num_q_heads, const pkv_cache_t* cache, const int32_t* block_table,
+                   int32_t max_blocks_per_seq, const int32_t* context_lengths, const int32_t* cu_q_lens,
+                   int32_t batch, int32_t max_q_len, float scale, void* out, float* lse_out,
+                   void* workspace, size_t workspace_bytes, const pkv_decode_opts_t* opts, void* stream) {
+    return decode_impl(q, num_q_heads, cache, block_table, max_blocks_per_seq, context_lengths, cu_q_lens, batch,
+                       max_q_len, scale, out, lse_out, workspace, workspace_bytes, opts, stream, nullptr, nullptr);
+}
+
+int pkv_store_decode_gqa(const void* q, const void* k_new, const void* v_new, int32_t num_q_heads,
+                         const pkv_cache_t* cache, const int32_t* block_table, int32_t max_blocks_per_seq,
+                         const int32_t* context_lengths, int32_t batch, float scale, void* out, float* lse_out,
+                         void* workspace, size_t workspace_bytes, const pkv_decode_opts_t* opts, void* stream) {
+    if (!k_new || !v_new) return PKV_ERR_INVALID_ARG;
+    return decode_impl(q, num_q_heads, cache, block_table, max_blocks_per_seq, context_lengths, nullptr, batch, 1,
+                       scale, out, lse_out, workspace, workspace_bytes, opts, stream, k_new, v_new);
 }
 
 }  // extern "C"

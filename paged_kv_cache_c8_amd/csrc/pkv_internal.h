@@ -76,6 +76,10 @@ struct DecodeArgs {
     int sk_waves;      // > 0: balanced partition into about this many segments (waves)
     int32_t* seg;      // balanced partition: first / last wave of each item [items][2]
     int window;        // > 0: sliding window, a query sees only its last `window` keys
+    // one decode step's new tokens (bf16 [batch][hkv][D], position ctx - 1 of each sequence), stored
+    // by the decode itself (int8-score kernel, one query per sequence); nullptr: nothing to store
+    const uint16_t* k_new;
+    const uint16_t* v_new;
 };
 
 // Sliding window: the first key a query at position pos sees (key 0 without a window).

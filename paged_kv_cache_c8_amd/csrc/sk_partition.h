@@ -154,10 +154,25 @@ __device__ __forceinline__ bool sk_plan(const DecodeArgs& a, int batch, int wid,
         a.seg[2 * item] = first;
         a.seg[2 * item + 1] = k;
     }
-    out.it = it;
-    out.t0 = it.kmin + (int)((int64_t)nb * seg / k) * SK_BLK;
-    out.t1 = min(it.kmin + (int)((int64_t)nb * (seg + 1) / k) * SK_BLK, it.kmax);
-    out.pslot = k == 1 ? -1 : (int64_t)wid;
+    // Every value of the segment is the same in all lanes, but it was read from LDS and memory at
+    // lane-varying addresses as far as the compiler can tell: made wave-uniform (scalar registers)
+    // here, so that the kernel's key loop and branches are uniform control flow.  Lane-divergent
+    // control flow around the matrix-core instructions (which read every lane's operands) is what
+    // the key loops must not have.
+    auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+    out.it.b = uni(it.b);
+    out.it.h = uni(it.h);
+    out.it.qlen = uni(it.qlen);
+    out.it.qrow0 = uni(it.qrow0);
+    out.it.prior = uni(it.prior);
+    out.it.r0 = uni(it.r0);
+    out.it.nrows = uni(it.nrows);
+    out.it.nvalid = uni(it.nvalid);
+    out.it.kmax = uni(it.kmax);
+    out.it.kmin = uni(it.kmin);
+    out.t0 = uni(it.kmin + (int)((int64_t)nb * seg / k) * SK_BLK);
+    out.t1 = uni(min(it.kmin + (int)((int64_t)nb * (seg + 1) / k) * SK_BLK, it.kmax));
+    out.pslot = uni(k) == 1 ? -1 : (int64_t)wid;
     return true;
 }
 

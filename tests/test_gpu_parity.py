@@ -375,8 +375,7 @@ def test_bf16_balanced_partition():
     """The balanced partition of the bf16 matrix-core kernel (segments over several rounds of the
     GPU's waves; segments longer than one 4096-key range are walked range by range): empty
     batches, one-block and long sequences together, three KV heads of eight query heads, a
-    sliding window, agreement with fixed splits and between repeated calls; head_dim 64 falls
-    back to fixed splits."""
+    sliding window, agreement with fixed splits and between repeated calls, and head_dim 64."""
     r = Run(_wl(2, 128, 16, 4, [0, 0, 0], seed=41))
     r.store_prior()
     r.store_new()
@@ -407,14 +406,38 @@ def test_bf16_balanced_partition():
     r.assert_decode_close(out, lse)
     out, lse = r.decode(partition=2, window=700)
     r.assert_decode_close(out, lse, r.oracle_decode(window=700))
-    # head_dim 64: the balanced kernel is switched off there (fixed splits serve the request)
+    # head_dim 64: every output channel (its last channel tile once came out wrong beside a right
+    # lse), one-segment and many-segment items, against the oracle and against fixed splits
     r = Run(_wl(2, 64, 32, 8, [300, 5000, 33, 2048], hkv=3, seed=44))
     r.store_prior()
     r.store_new()
     assert pkv.decode_plan(r.w.batch, r.w.num_q_heads, 3, 64, r.w.max_blocks_per_seq, 32, 1, 2,
-                           partition=2)["split_tokens"] > 0
+                           partition=2)["split_tokens"] == 0
     out, lse = r.decode(partition=2)
     r.assert_decode_close(out, lse)
+    fixed, _ = r.decode(split_tokens=512)
+    torch.cuda.synchronize()
+    diff = (out.float() - fixed.float()).abs()
+    bound = fixed.float().abs() * 2.0 ** -7 + 2.0 ** -10 * float(fixed.float().abs().max())
+    assert bool((diff <= bound).all()), float((diff - bound).max())
+
+
+@pytest.mark.parametrize("mode,g,bs,ctx", [(0, 8, 32, [33, 4097, 65]), (3, 8, 32, [33, 1000, 65]),
+                                             (0, 4, 16, [33, 4097, 65]), (1, 4, 16, [5000, 3000]),
+                                             (0, 8, 32, [600, 4097])])
+def test_balanced_partition_head_dim_64(mode, g, bs, ctx):
+    """The int8-score kernel's balanced partition at head_dim 64 with items of one and of many
+    segments (their partials merged by several thread groups): every output channel within the bar,
+    not only the lse (wrong outputs beside a right lse have been seen here)."""
+    r = Run(_wl(mode, 64, bs, g, ctx, seed=sum(ctx) + g + mode))
+    r.store_prior()
+    r.store_new()
+    plan = pkv.decode_plan(r.w.batch, r.w.num_q_heads, 2, 64, r.w.max_blocks_per_seq, bs, 1, mode, partition=2)
+    assert plan["split_tokens"] == 0 and plan["kernel"] == 3, plan
+    ref = r.oracle_decode()
+    for kw in (dict(partition=2), dict(partition=1)):
+        out, lse = r.decode(**kw)
+        r.assert_decode_close(out, lse, ref)
 
 
 def test_balanced_partitions_with_causal_chunks():
