@@ -469,6 +469,7 @@ def main_codec(args):
         "ms_median": round(ms, 5), "ms_mean": round(float(np.mean(times)), 5), "launches": steps,
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_record(f"{args.op}.config{args.config}.mode{w.quant_mode}"),
                      "algorithmic_bytes_per_launch": read_b + write_b, "avg_launch_ms": round(ms, 5)},
     }
     print(json.dumps(res), flush=True)
