@@ -61,9 +61,11 @@ def parse():
                     help="a decode batch's store as its own call before the decode (default: one call)")
     ap.add_argument("--no-secondary", action="store_true",
                     help="the default run measures the long-context decode too and reports it as 'secondary'")
-    ap.add_argument("--op", default="decode", choices=["decode", "store-fill", "dequant"],
+    ap.add_argument("--op", default="decode", choices=["decode", "store-fill", "dequant", "walk"],
                     help="decode: the decode step (default); store-fill: the prompt-style store of every "
-                         "prior token of the workload; dequant: the gather of the whole cache to bf16 rows")
+                         "prior token of the workload; dequant: the gather of the whole cache to bf16 rows; "
+                         "walk: only the cache reads of the int8 decode (its read ceiling, pkv_cache_walk)")
+    ap.add_argument("--walk-depth", type=int, default=1, help="walk: 64-key blocks in flight per wave (1..3)")
     return ap.parse_args()
 
 
@@ -168,6 +170,9 @@ def main():
         sys.exit(2)
     if args.mla >= 0:
         main_mla(args)
+        return
+    if args.op == "walk":
+        main_walk(args)
         return
     if args.op != "decode":
         main_codec(args)
@@ -395,6 +400,95 @@ def codec_bytes(w, op):
         rd = n * hkv * 2 * d + int(np.ceil(w.context_lengths / bs).sum()) * hkv * 8
     rd += w.batch * 4 + int(np.ceil(w.context_lengths / bs).sum()) * 4
     return rd, n * hkv * d * 2 * 2, n
+
+
+def walk_bytes(w, split):
+    """Bytes pkv_cache_walk reads: every K row of every position, the whole 16-slot V tiles that
+    hold them, the per-token scales (per-block: each page once per wave that touches it), and the
+    block-table entries each wave stages."""
+    hkv, d, bs = w.num_kv_heads, w.head_dim, w.block_size
+    total = 0
+    for c in w.context_lengths.astype(np.int64):
+        for t0 in range(0, int(c), split):
+            t1 = min(t0 + split, int(c))
+            pages = (t1 - 1) // bs - t0 // bs + 1
+            total += (t1 - t0) * d + ((t1 - t0 + 15) // 16) * 16 * d + pages * 4
+            if w.quant_mode == 0:
+                total += (t1 - t0) * 8
+            elif w.quant_mode == 1:
+                total += pages * 8
+    return total * hkv
+
+
+def main_walk(args):
+    """The int8 decode's cache reads alone (pkv_cache_walk): same pages, same layout, same wave
+    order and keys per wave as the decode's fixed partition, nothing computed.  Its rate is the
+    read ceiling of the access pattern, the number the decode's own HBM fraction is judged by."""
+    import torch
+
+    import gen
+    import paged_kv_cache_c8_amd as pkv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = gen.make_config(args.config, quant_mode=args.quant_mode)
+    if w.quant_mode == gen.QUANT_NONE_BF16:
+        raise SystemExit("--op walk: int8 caches only")
+    t = gen.gen_tensors(w, device=dev)
+    k_prior, _ = gen.split_prior_new(w, t["k_all"])
+    v_prior, _ = gen.split_prior_new(w, t["v_all"])
+    del t["k_all"], t["v_all"]
+    i32 = lambda x: torch.as_tensor(np.ascontiguousarray(x, dtype=np.int32), device=dev)
+    bt, ctx, prior, cu_prior = i32(w.block_table), i32(w.context_lengths), i32(w.prior_lengths), i32(w.cu_prior)
+    split = args.split_tokens
+    if split <= 0:
+        mq = 1 if w.decode_only else int(np.diff(w.cu_q_lens).max())
+        split = pkv.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_blocks_per_seq,
+                                w.block_size, mq, w.quant_mode)["split_tokens"] or 256
+    read_b = walk_bytes(w, split)
+    reps = args.replicas or min(MAX_REPLICAS, max(1, int(np.ceil(3 * MALL_BYTES / read_b))))
+    caches = []
+    mql = int(w.prior_lengths.max())
+    for _ in range(reps):
+        c = pkv.Cache(w.quant_mode, w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, device=dev)
+        if w.quant_mode == gen.QUANT_PER_CHANNEL:
+            c.k_scale.copy_(t["k_scale"])
+            c.v_scale.copy_(t["v_scale"])
+        if mql > 0:  # positions past the prior tokens hold whatever the pool held (timing only)
+            pkv.store_c8(c, k_prior, v_prior, cu_q_lens=cu_prior, context_lengths=prior, block_table=bt,
+                         max_q_len=mql)
+        caches.append(c)
+    del k_prior, v_prior
+    nsplit = -(-w.max_blocks_per_seq * w.block_size // split)
+    outs = [torch.empty((w.batch, w.num_kv_heads, nsplit), dtype=torch.int32, device=dev) for _ in range(reps)]
+
+    def launch(i):
+        pkv.cache_walk(caches[i % reps], bt, ctx, split, depth=args.walk_depth, out=outs[i % reps])
+    for i in range(max(args.warmup, 2)):
+        launch(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    steps = max(args.steps, 5)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(stream)
+        launch(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    times = [a.elapsed_time(b) for a, b in evs]
+    ms = float(np.median(times))
+    achieved = read_b / (ms * 1e-3) / 1e9
+    res = {
+        "op": "walk", "workload": w.name, "quant_mode": w.quant_mode, "split_tokens": split,
+        "depth": args.walk_depth, "waves": int(w.batch * w.num_kv_heads * nsplit), "cache_replicas": reps,
+        "bytes_read": read_b, "ms_median": round(ms, 5), "ms_mean": round(float(np.mean(times)), 5),
+        "launches": steps,
+        "roofline": {"bound": "hbm", "kernel": "pkv_cache_walk (the decode's cache reads only)",
+                     "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_launch": read_b,
+                     "avg_launch_ms": round(ms, 5)},
+    }
+    print(json.dumps(res), flush=True)
 
 
 def main_codec(args):

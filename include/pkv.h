@@ -165,10 +165,33 @@ int pkv_dequant(const pkv_cache_t *cache, const int32_t *block_table, int32_t ma
                 const int32_t *context_lengths, const int64_t *seq_offsets, int32_t batch,
                 void *k_out, void *v_out, int64_t token_stride, int64_t head_stride, void *stream);
 
+/*
+ * pkv_cache_walk - a measurement aid: the read ceiling of the int8 decode's
+ * access pattern over this cache (not an operation of the pages).
+ *
+ * One wave per (sequence b, KV head h, split s of split_tokens keys), launched
+ * in the order of pkv_decode_gqa's fixed partition, reads what the decode of
+ * keys [s * split_tokens, min((s + 1) * split_tokens, context_lengths[b])) reads
+ * from the cache - their K rows, the whole 16-slot V tiles that hold them, and
+ * their per-token K and V scales (mode 0) or the per-block scales of the pages
+ * they touch, each page once per wave (mode 1; none in mode 3) - and computes
+ * nothing else, with `depth` (1..3) blocks of 64 keys in flight per wave (the
+ * decode keeps 1).  out[(b * num_kv_heads + h) * nsplit + s] receives the
+ * wrapping uint32 sum of the 32-bit words that wave read (0 for a split past
+ * the context), nsplit = ceil(max_blocks_per_seq * block_size / split_tokens);
+ * out holds batch * num_kv_heads * nsplit entries (device, 4-byte aligned).
+ * split_tokens: a multiple of 64 in [64, 4096].  Int8 modes only (mode 2:
+ * PKV_ERR_UNSUPPORTED).  Errors as pkv_dequant.
+ */
+int pkv_cache_walk(const pkv_cache_t *cache, const int32_t *block_table, int32_t max_blocks_per_seq,
+                   const int32_t *context_lengths, int32_t batch, int32_t split_tokens, int32_t depth,
+                   uint32_t *out, void *stream);
+
 /* Optional knobs of pkv_decode_gqa (pass NULL for the defaults). */
 typedef struct {
     int32_t split_tokens; /* keys per fixed split-KV partition, rounded up to a multiple
-                             of 128, at most 4096; 0 = sized from the shapes.  A value
+                             of 128 (64 for kernel 3), at most 4096; 0 = sized from the
+                             shapes.  A value
                              > 0 selects fixed splits.  The balanced partition cuts all
                              64-key blocks of all query groups into near-equal ranges,
                              as many as the GPU holds waves of the kernel at once (or a

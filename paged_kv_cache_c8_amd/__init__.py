@@ -19,7 +19,7 @@ import os
 
 import torch  # loaded first: libpkv binds to the HIP runtime torch has already loaded
 
-__all__ = ["PkvError", "Cache", "lib", "store_c8", "dequant", "decode_gqa", "decode_gqa_noalloc", "store_decode_gqa",
+__all__ = ["PkvError", "Cache", "lib", "store_c8", "dequant", "decode_gqa", "decode_gqa_noalloc", "store_decode_gqa", "cache_walk",
            "decode_workspace_size", "NOALLOC_SCRATCH_BYTES",
            "decode_plan", "MLACache", "mla_store_c8", "mla_decode", "mla_decode_workspace_size",
            "mla_decode_plan", "QUANT_PER_TOKEN", "QUANT_PER_BLOCK", "QUANT_NONE_BF16", "QUANT_PER_CHANNEL",
@@ -37,7 +37,7 @@ QUANT_PER_CHANNEL = 3
 EXPORTS = ("pkv_status_string", "pkv_version", "pkv_store_c8", "pkv_dequant",
            "pkv_decode_workspace_size", "pkv_decode_gqa", "pkv_decode_plan", "pkv_mla_store_c8",
            "pkv_mla_decode_workspace_size", "pkv_mla_decode_plan", "pkv_mla_decode", "pkv_decode_gqa_noalloc",
-           "pkv_store_decode_gqa")
+           "pkv_store_decode_gqa", "pkv_cache_walk")
 
 NOALLOC_SCRATCH_BYTES = 32 << 20  # PKV_NOALLOC_SCRATCH_BYTES
 
@@ -89,6 +89,8 @@ def lib():
         L.pkv_store_c8.restype = ctypes.c_int
         L.pkv_dequant.argtypes = [P, P, I32, P, P, I32, P, P, I64, I64, P]
         L.pkv_dequant.restype = ctypes.c_int
+        L.pkv_cache_walk.argtypes = [P, P, I32, P, I32, I32, I32, P, P]
+        L.pkv_cache_walk.restype = ctypes.c_int
         L.pkv_decode_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32, P]
         L.pkv_decode_workspace_size.restype = SZ
         L.pkv_decode_gqa.argtypes = [P, I32, P, P, I32, P, P, I32, I32, ctypes.c_float, P, P, P, SZ,
@@ -282,6 +284,26 @@ def dequant(cache: Cache, block_table, context_lengths, *, seq_offsets=None, k_o
                            int(token_stride), int(head_stride), _stream(stream))
     _check(st, "pkv_dequant")
     return k_out, v_out
+
+
+def cache_walk(cache: Cache, block_table, context_lengths, split_tokens, *, depth=1, out=None, stream=None):
+    """Read what the int8 decode of these sequences reads from the cache, with ``split_tokens`` keys
+    per wave, and nothing more (a read-ceiling measurement).  Returns the per-wave word sums, uint32
+    bit patterns in an int32 tensor ``[batch, Hkv, nsplit]``."""
+    _want(context_lengths, "context_lengths", torch.int32, ndim=1)
+    batch = int(context_lengths.shape[0])
+    _want(block_table, "block_table", torch.int32, (batch, None))
+    mbs = int(block_table.shape[1])
+    nsplit = -(-mbs * cache.block_size // int(split_tokens)) if split_tokens > 0 else 0
+    _want(out, "out", torch.int32, (batch, cache.num_kv_heads, nsplit), optional=True)
+    _same_device(cache.k, block_table=block_table, context_lengths=context_lengths, out=out)
+    if out is None:
+        with _on_stream(stream):
+            out = torch.empty((batch, cache.num_kv_heads, max(nsplit, 1)), dtype=torch.int32, device=cache.k.device)
+    st = lib().pkv_cache_walk(cache.ref, _ptr(block_table), mbs, _ptr(context_lengths), batch, int(split_tokens),
+                              int(depth), _ptr(out), _stream(stream))
+    _check(st, "pkv_cache_walk")
+    return out
 
 
 def decode_workspace_size(batch, num_q_heads, cache: Cache, max_blocks_per_seq, max_q_len=1,

@@ -183,7 +183,8 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
     }
     int64_t L;
     if (opts && opts->split_tokens > 0) {
-        L = cdiv(opts->split_tokens, 128) * 128;
+        const int64_t gran = kernel == 3 ? 64 : 128;  // the int8-score kernel walks 64-key blocks
+        L = cdiv(opts->split_tokens, gran) * gran;
     } else {
         // Aim for ~16 (int8-score kernel: ~11) workgroups per compute unit counting every
         // (possibly empty) split, with partitions of 256..2048 keys (bf16 matrix-core kernel:
@@ -303,6 +304,35 @@ int pkv_dequant(const pkv_cache_t* cache, const int32_t* block_table, int32_t ma
                (!v_out || aligned(v_out, 16));
     a.nchunk = (int)cdiv((int64_t)max_blocks_per_seq * cache->block_size, 128);
     return hip_status(pkv::launch_dequant(a, cache->head_dim, cache->quant_mode, static_cast<hipStream_t>(stream)));
+}
+
+int pkv_cache_walk(const pkv_cache_t* cache, const int32_t* block_table, int32_t max_blocks_per_seq,
+                   const int32_t* context_lengths, int32_t batch, int32_t split_tokens, int32_t depth,
+                   uint32_t* out, void* stream) {
+    int st = check_cache(cache);
+    if (st != PKV_OK) return st;
+    if (cache->quant_mode == PKV_QUANT_NONE_BF16) return PKV_ERR_UNSUPPORTED;
+    if (!block_table || !context_lengths || !out || batch < 0 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID_ARG;
+    if (split_tokens < 64 || split_tokens > 4096 || split_tokens % 64 != 0) return PKV_ERR_INVALID_ARG;
+    if (depth < 1 || depth > 3 || !aligned(out, 4)) return PKV_ERR_INVALID_ARG;
+    if (batch == 0) return PKV_OK;
+    pkv::WalkArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.k = cache->k;
+    a.v = cache->v;
+    a.ks = cache->k_scale;
+    a.vs = cache->v_scale;
+    a.bt = block_table;
+    a.ctx = context_lengths;
+    a.out = out;
+    a.hkv = cache->num_kv_heads;
+    a.bs = cache->block_size;
+    a.log2bs = ilog2(cache->block_size);
+    a.mbs = max_blocks_per_seq;
+    a.split_len = split_tokens;
+    a.nsplit = (int)cdiv((int64_t)max_blocks_per_seq * cache->block_size, split_tokens);
+    return hip_status(pkv::launch_walk(a, batch, cache->head_dim, cache->quant_mode, depth,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 size_t pkv_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -49,6 +49,22 @@ struct DequantArgs {
     int nchunk;  // 128-position chunks of the longest sequence the block table holds
 };
 
+struct WalkArgs {
+    const void* k;
+    const void* v;
+    const float* ks;
+    const float* vs;
+    const int32_t* bt;
+    const int32_t* ctx;
+    uint32_t* out;
+    int hkv;
+    int bs;
+    int log2bs;
+    int mbs;
+    int split_len;
+    int nsplit;
+};
+
 struct DecodeArgs {
     const uint16_t* q;
     const void* k;
@@ -92,6 +108,7 @@ __host__ __device__ inline int win_begin(int window, int pos) { return win_lo(wi
 
 hipError_t launch_store(const StoreArgs& a, int head_dim, int mode, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, int head_dim, int mode, hipStream_t stream);
+hipError_t launch_walk(const WalkArgs& a, int batch, int head_dim, int mode, int depth, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs& a, int batch, int head_dim, int rg, int mode,
                               hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int batch, int head_dim, int row_tiles, int mode,
