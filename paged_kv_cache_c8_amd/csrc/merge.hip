@@ -4,13 +4,11 @@
 // (weights taken against a common zero point).  The row's result is
 //     out = sum_s 2^(L_s - M) o_s / sum_s 2^(L_s - M),   lse = M + log2 sum_s 2^(L_s - M),
 // M = max_s L_s, combined in a fixed order (deterministic).  Splits past the row's keys were
-// never written; their workspace rows may be loaded with the first round and are then dropped.
+// never written and are never read.
 //
-// One workgroup per (sequence, KV head, row group); thread (row j, group c of CPT channels).  The
-// sequence's lengths and the partials of the first CH splits are loaded together (rows of splits
-// the item did not use lie inside the workspace: read, then ignored), so a decode's merge costs
-// one memory round trip; further splits are folded in CH at a time into a running (max, sum,
-// accumulator).  CPT = 4 (CH = 16) for groups of up to 256 threads, else 8 (CH = 8).
+// One workgroup per (sequence, KV head, row group); thread (row j, 8-channel group c).  The loads
+// of eight splits are issued together, then folded into a running (max, sum, accumulator) so that
+// any number of splits costs one memory round trip per eight.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -18,12 +16,11 @@ namespace pkv {
 namespace {
 
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int CH = 8;  // splits per load round
 
-template <int D, int CPT>
-__global__ __launch_bounds__(CPT == 4 ? 256 : 1024) void merge_kernel(DecodeArgs a, int rows_per_item) {
-    constexpr int CG = D / CPT;       // channel groups per row
-    constexpr int CH = CPT == 4 ? 16 : 8;  // splits per load round
-    constexpr int NV = CPT / 4;       // float4 per split and thread
+template <int D>
+__global__ __launch_bounds__(1024) void merge_kernel(DecodeArgs a, int rows_per_item) {
+    constexpr int CG = D / 8;  // 8-channel groups per row
     const int tid = threadIdx.x;
     const int jr = tid / CG;
     const int cg = tid % CG;
@@ -34,25 +31,6 @@ __global__ __launch_bounds__(CPT == 4 ? 256 : 1024) void merge_kernel(DecodeArgs
     wi /= a.nrg;
     const int h = wi % a.hkv;
     const int b = wi / a.hkv;
-    // ---- loads: lengths, and the first CH splits' partials of row jr (in the workspace for any jr < prs)
-    const int64_t base = (int64_t)item * a.nsplit * a.prs + jr;  // row jr of split 0
-    const bool rowok = jr < a.prs;
-    float l2[CH];
-    float4 p[CH][NV];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-        if (rowok && c < a.nsplit) {
-            const int64_t row = base + (int64_t)c * a.prs;
-            l2[c] = a.part_lse[row];
-            const float4* pp = reinterpret_cast<const float4*>(a.part_o + row * D) + NV * cg;
-#pragma unroll
-            for (int v = 0; v < NV; ++v) p[c][v] = pp[v];
-        } else {
-            l2[c] = -INFINITY;
-#pragma unroll
-            for (int v = 0; v < NV; ++v) p[c][v] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    }
     const int qlen = a.cu ? a.cu[b + 1] - a.cu[b] : 1;
     const int qrow0 = a.cu ? a.cu[b] : b;
     const int prior = a.ctx[b] - qlen;
@@ -65,34 +43,29 @@ __global__ __launch_bounds__(CPT == 4 ? 256 : 1024) void merge_kernel(DecodeArgs
     if (jr >= nvalid) return;
     const int kmin = win_begin(a.window, prior + r0 / a.g);  // splits start here (sliding window)
     const int nact = min(a.nsplit, (kmax - kmin + a.split_len - 1) / a.split_len);
+    const int64_t base = (int64_t)item * a.nsplit * a.prs + jr;  // row jr of split 0
 
     float M = -INFINITY, wsum = 0.0f;
-    float acc[CPT];
+    float acc[8];
 #pragma unroll
-    for (int e = 0; e < CPT; ++e) acc[e] = 0.0f;
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
     for (int s0 = 0; s0 < nact; s0 += CH) {
-        if (s0 > 0) {
+        float l2[CH];
+        float4 p0[CH], p1[CH];
 #pragma unroll
-            for (int c = 0; c < CH; ++c) {
-                const int s = s0 + c;
-                if (s < nact) {
-                    const int64_t row = base + (int64_t)s * a.prs;
-                    l2[c] = a.part_lse[row];
-                    const float4* pp = reinterpret_cast<const float4*>(a.part_o + row * D) + NV * cg;
-#pragma unroll
-                    for (int v = 0; v < NV; ++v) p[c][v] = pp[v];
-                }
+        for (int c = 0; c < CH; ++c) {
+            const int s = s0 + c;
+            if (s < nact) {
+                const int64_t row = base + (int64_t)s * a.prs;
+                l2[c] = a.part_lse[row];
+                const float4* pp = reinterpret_cast<const float4*>(a.part_o + row * D) + 2 * cg;
+                p0[c] = pp[0];
+                p1[c] = pp[1];
+            } else {
+                l2[c] = -INFINITY;
+                p0[c] = p1[c] = make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
-        // splits past the row's keys were never written this call: whatever their rows hold (NaN
-        // included) must reach neither the max nor the sums
-#pragma unroll
-        for (int c = 0; c < CH; ++c)
-            if (s0 + c >= nact) {
-                l2[c] = -INFINITY;
-#pragma unroll
-                for (int v = 0; v < NV; ++v) p[c][v] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
         float mc = M;
 #pragma unroll
         for (int c = 0; c < CH; ++c) mc = fmaxf(mc, l2[c]);
@@ -101,63 +74,39 @@ __global__ __launch_bounds__(CPT == 4 ? 256 : 1024) void merge_kernel(DecodeArgs
         M = mc;
         wsum *= sc;
 #pragma unroll
-        for (int e = 0; e < CPT; ++e) acc[e] *= sc;
+        for (int e = 0; e < 8; ++e) acc[e] *= sc;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const float w = l2[c] == -INFINITY ? 0.0f : exp2f(l2[c] - M);
             wsum += w;
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                acc[4 * v + 0] = fmaf(w, p[c][v].x, acc[4 * v + 0]);
-                acc[4 * v + 1] = fmaf(w, p[c][v].y, acc[4 * v + 1]);
-                acc[4 * v + 2] = fmaf(w, p[c][v].z, acc[4 * v + 2]);
-                acc[4 * v + 3] = fmaf(w, p[c][v].w, acc[4 * v + 3]);
-            }
+            acc[0] = fmaf(w, p0[c].x, acc[0]);
+            acc[1] = fmaf(w, p0[c].y, acc[1]);
+            acc[2] = fmaf(w, p0[c].z, acc[2]);
+            acc[3] = fmaf(w, p0[c].w, acc[3]);
+            acc[4] = fmaf(w, p1[c].x, acc[4]);
+            acc[5] = fmaf(w, p1[c].y, acc[5]);
+            acc[6] = fmaf(w, p1[c].z, acc[6]);
+            acc[7] = fmaf(w, p1[c].w, acc[7]);
         }
     }
     const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
     const int r = r0 + jr;
     const int64_t orow = (int64_t)(qrow0 + r / a.g) * a.hq + h * a.g + r % a.g;
-    uint16_t* op = a.out + orow * D + CPT * cg;
-    uint32_t pk[CPT / 2];
+    uint16_t* op = a.out + orow * D + 8 * cg;
+    uint32_t pk[4];
 #pragma unroll
-    for (int e = 0; e < CPT / 2; ++e)
+    for (int e = 0; e < 4; ++e)
         pk[e] = f32_to_bf16_rne(acc[2 * e] * inv) | (f32_to_bf16_rne(acc[2 * e + 1] * inv) << 16);
-    if constexpr (CPT == 8) {
-        if ((reinterpret_cast<uintptr_t>(op) & 15) == 0) {
-            *reinterpret_cast<uint4*>(op) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                op[2 * e] = (uint16_t)(pk[e] & 0xffffu);
-                op[2 * e + 1] = (uint16_t)(pk[e] >> 16);
-            }
-        }
+    if ((reinterpret_cast<uintptr_t>(op) & 15) == 0) {
+        *reinterpret_cast<uint4*>(op) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
     } else {
-        if ((reinterpret_cast<uintptr_t>(op) & 7) == 0) {
-            *reinterpret_cast<uint2*>(op) = make_uint2(pk[0], pk[1]);
-        } else {
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                op[2 * e] = (uint16_t)(pk[e] & 0xffffu);
-                op[2 * e + 1] = (uint16_t)(pk[e] >> 16);
-            }
+        for (int e = 0; e < 4; ++e) {
+            op[2 * e] = (uint16_t)(pk[e] & 0xffffu);
+            op[2 * e + 1] = (uint16_t)(pk[e] >> 16);
         }
     }
     if (cg == 0 && a.lse) a.lse[orow] = wsum > 0.0f ? (M + log2f(wsum)) * kLn2 : -INFINITY;
-}
-
-template <int D>
-hipError_t launch_merge_d(const DecodeArgs& a, int64_t grid, int rows_per_item, hipStream_t stream) {
-    const int t4 = ((rows_per_item * D / 4 + kWave - 1) / kWave) * kWave;
-    const int t8 = ((rows_per_item * D / 8 + kWave - 1) / kWave) * kWave;
-    if (t4 <= 256)
-        hipLaunchKernelGGL((merge_kernel<D, 4>), dim3((unsigned)grid), dim3(t4), 0, stream, a, rows_per_item);
-    else if (t8 <= 1024)
-        hipLaunchKernelGGL((merge_kernel<D, 8>), dim3((unsigned)grid), dim3(t8), 0, stream, a, rows_per_item);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
 }
 
 }  // namespace
@@ -166,9 +115,15 @@ hipError_t launch_merge(const DecodeArgs& a, int batch, int head_dim, int rows_p
     const int64_t grid = (int64_t)batch * a.hkv * a.nrg;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    if (head_dim == 64) return launch_merge_d<64>(a, grid, rows_per_item, stream);
-    if (head_dim == 128) return launch_merge_d<128>(a, grid, rows_per_item, stream);
-    return hipErrorInvalidValue;
+    const int threads = ((rows_per_item * head_dim / 8 + kWave - 1) / kWave) * kWave;
+    if (threads > 1024) return hipErrorInvalidValue;
+    if (head_dim == 64)
+        hipLaunchKernelGGL((merge_kernel<64>), dim3((unsigned)grid), dim3(threads), 0, stream, a, rows_per_item);
+    else if (head_dim == 128)
+        hipLaunchKernelGGL((merge_kernel<128>), dim3((unsigned)grid), dim3(threads), 0, stream, a, rows_per_item);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 }  // namespace pkv

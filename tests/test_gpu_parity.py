@@ -47,6 +47,10 @@ DECODE_CASES = [
     (2, 64, 128, 8, [200, 1, 129]),
     (1, 128, 16, 4, [20, 129, 300]),
     (1, 64, 64, 8, [65, 1, 200]),
+    # more than 16 query heads per KV head: two 16-row groups sharing each key block (the second
+    # one partly filled), per token and per block
+    (0, 128, 16, 32, [300, 1025, 1]),
+    (1, 64, 16, 24, [70, 500]),
 ]
 
 
@@ -79,6 +83,9 @@ CHUNK_CASES = [
     # three KV heads x three sequences: pairs of (split, sequence x KV head) not a multiple of 8,
     # up to five 16-row groups each (the workgroup order puts a pair's row groups 8 apart)
     (1, 128, 16, 5, [500, 37, 260], [16, 11, 6], 3),
+    # six 16-row groups of one (sequence, KV head) sharing their keys, static per-channel scales;
+    # a short sequence whose later row groups hold no rows
+    (3, 128, 32, 6, [100, 1000, 3], [16, 16, 3]),
 ]
 
 
@@ -112,6 +119,8 @@ def test_paged_prefill_matches_oracle(mode, d, bs, g, ctx, ql):
 def test_chunked_store_and_causal_decode(case, kernel):
     mode, d, bs, g, ctx, ql = case[:6]
     hkv = case[6] if len(case) > 6 else 2
+    if mode == 3 and kernel != 3:
+        pytest.skip("static per-channel scales are decoded by the int8-score kernel only")
     r = Run(_wl(mode, d, bs, g, ctx, ql, hkv=hkv, seed=sum(ctx)))
     r.store_prior()
     r.store_new()
