@@ -147,7 +147,12 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
         // ranges as the GPU holds waves of the kernel at once (no partly filled rounds of waves).
         // It pays one more memory round trip per wave (the plan), which only long contexts
         // amortise, and needs the items to be few against the waves.
-        const int per_cu = pkv::decode_c8_waves_per_cu(head_dim, p->classes, p->rg, mode, batch, window > 0);
+        // one wave per SIMD (four per compute unit) even where two fit: on the long-context decode
+        // the segments are then twice as long, their merge half as large, and no wave shares its
+        // SIMD (measured on MI355X: 284 against 290 us; three or four per CU are best, two and
+        // five slower)
+        const int fit = pkv::decode_c8_waves_per_cu(head_dim, p->classes, p->rg, mode, batch, window > 0);
+        const int per_cu = fit < 4 ? fit : 4;
         const int64_t W = (int64_t)per_cu * device_cus();
         // more items than half the waves: the library's plan takes fixed splits (measured faster
         // on the chunked multi-token decode: 397 against 483 us); a forced balanced partition
