@@ -156,7 +156,7 @@ __device__ __forceinline__ void store_new_token(const DecodeArgs& a, int b, int 
     __builtin_amdgcn_wave_barrier();
 }
 
-template <int D, int MODE, int J, int RT, bool WIN>
+template <int D, int MODE, int J, int RT, bool WIN, int KD = 1>
 __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b_, const int h_, const int qlen_,
                                            const int qrow0_, const int prior_, const int r0_, const int nvalid_,
                                            const int t_seg0_, const int t_seg1_, const int64_t pslot,
@@ -315,18 +315,23 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b_, co
 
         // ---- first block: its page ids straight from the block table, its loads issued before the
         //      block-table slice goes to LDS and before the query is quantized
-        C8Regs<D, J> R;
+        // K and the scales alternate between KD register sets (KD = 2: loaded two blocks ahead)
+        C8Regs<D, J> Ra, Rb;
         C8V<D> v0, v1;
         {
             const int pk = btb[chunk_page(t_begin, kchunk)];
             const int pv = btb[chunk_page(t_begin, g)];
             load_v_at(t_begin, pv, v0);
-            load_k_at(t_begin, pk, R);
-            load_s_at(t_begin, pv, R);
+            load_k_at(t_begin, pk, Ra);
+            load_s_at(t_begin, pv, Ra);
         }
         // block-table slice of the split (the wave reads back its own LDS writes in order)
         for (int i = lane; i < nblk; i += kWave) bt_s[i] = btb[blk0 + i];
         __builtin_amdgcn_wave_barrier();
+        if constexpr (KD == 2) {  // the second block's K and scales (past the range: in-bounds stand-ins)
+            load_k(t_begin + BLK, Rb);
+            load_s(t_begin + BLK, Rb);
+        }
 
         if (tb == t_seg0) {
             // ---- quantize the query rows: q * 2^k rounded to integers in [-2^22, 2^22], split exactly as
@@ -381,7 +386,7 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b_, co
 
         }
 
-        auto block = [&](const int T, const C8V<D>& VC, C8V<D>& VN) {
+        auto block = [&](const int T, const C8V<D>& VC, C8V<D>& VN, C8Regs<D, J>& R) {
             // masked: the block runs past the split's keys, past some row's causal limit or below
             // some row's window start
             const bool MASKED = causal || T + BLK > t_end || (WIN && T < lo_hi);
@@ -424,7 +429,7 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b_, co
                     sc2[rt][q] = c2;
                 }
             }
-            load_k(T + BLK, R);
+            load_k(T + KD * BLK, R);
             __builtin_amdgcn_sched_barrier(0);
 
             // -------------------------------------------- V-scale reference of the column
@@ -513,7 +518,7 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b_, co
                 any_rescale |= alpha != 1.0f;
             }
 
-            load_s(T + BLK, R);
+            load_s(T + KD * BLK, R);
             __builtin_amdgcn_sched_barrier(0);
 
             // -------------------------------------------- rescale the columns whose references moved
@@ -560,7 +565,7 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b_, co
         // was written by this wave a moment ago; its loads of that slot are replaced, not trusted).
         // The block is the same for the whole wave; which lanes hold the key depends on the lane,
         // so the replacement is made of selects, with no lane-divergent branch.
-        auto patch_new = [&](const int T, C8V<D>& VC) {
+        auto patch_new = [&](const int T, C8V<D>& VC, C8Regs<D, J>& R) {
             const int kk = prior - T;  // the new key within the block
             const int kc = kk >> 4, qn = 2 * ((kk >> 3) & 1) + ((kk >> 2) & 1), ii = kk & 3;
             const bool krow = rho == 4 * kc + ii;  // K: the score row of that key, channels g 16 KSTEP ..
@@ -597,12 +602,12 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b_, co
             }
         };
         for (int T = t_begin;;) {
-            if (own_new && prior >= T && prior < T + BLK) patch_new(T, v0);
-            block(T, v0, v1);
+            if (own_new && prior >= T && prior < T + BLK) patch_new(T, v0, Ra);
+            block(T, v0, v1, Ra);
             T += BLK;
             if (T >= t_end) break;
-            if (own_new && prior >= T && prior < T + BLK) patch_new(T, v1);
-            block(T, v1, v0);
+            if (own_new && prior >= T && prior < T + BLK) patch_new(T, v1, KD == 2 ? Rb : Ra);
+            block(T, v1, v0, KD == 2 ? Rb : Ra);
             T += BLK;
             if (T >= t_end) break;
         }
@@ -707,7 +712,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 
 
 // Balanced partition (sk_partition.h): one wave per segment of the plan.
 template <int D, int MODE, int J, int RT, bool WIN>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 1))) void decode_c8_sk_kernel(DecodeArgs a, int batch) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1))) void decode_c8_sk_kernel(DecodeArgs a, int batch) {
     constexpr int ROWS = J > 1 ? 16 / J : 16 * RT;
     __shared__ int bt_s[MAX_SPLIT_PAGES];
     __shared__ i4 qs[QS_I4<D, RT>];
@@ -716,7 +721,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 
     SkSegment sg;
     if (!sk_plan<ROWS, WIN>(a, batch, blockIdx.x, kseq, sg)) return;
     const ItemGeo& it = sg.it;
-    c8_segment<D, MODE, J, RT, WIN>(a, it.b, it.h, it.qlen, it.qrow0, it.prior, it.r0, it.nvalid, sg.t0, sg.t1,
+    // one wave per SIMD (the planner's choice) leaves registers for K two blocks ahead; measured on
+    // MI355X: 284.6 -> 282.0 us on the long-context decode with per-token scales, while with
+    // static per-channel scales (no scale loads per key) it measured slower (269.5 -> 272.8 us)
+    constexpr int KD = RT == 1 && MODE != 3 ? 2 : 1;
+    c8_segment<D, MODE, J, RT, WIN, KD>(a, it.b, it.h, it.qlen, it.qrow0, it.prior, it.r0, it.nvalid, sg.t0, sg.t1,
                                     sg.pslot, bt_s, qs, nt);
 }
 
