@@ -207,6 +207,12 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b_, co
         for (int l = 0; l < 2 * KSTEP; ++l) qraw[rt][l] = rv ? load16(qp + 8 * l) : u32x4{0u, 0u, 0u, 0u};
     }
     causal = __any(causal);
+    // the lowest causal limit over the wave's rows: blocks wholly at or below it need no mask
+    int lim_lo = 0x7fffffff;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) lim_lo = min(lim_lo, lim[rt]);
+    for (int sh = 1; sh < kWave; sh <<= 1) lim_lo = min(lim_lo, __shfl_xor(lim_lo, sh, kWave));
+    lim_lo = __builtin_amdgcn_readfirstlane(lim_lo);
     // one decode step with its store: the wave whose keys end at the new token's position stores it
     // (one query per sequence: the position is the item's last key, prior == t_seg1 - 1)
     bool own_new = false;
@@ -389,7 +395,7 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b_, co
         auto block = [&](const int T, const C8V<D>& VC, C8V<D>& VN, C8Regs<D, J>& R) {
             // masked: the block runs past the split's keys, past some row's causal limit or below
             // some row's window start
-            const bool MASKED = causal || T + BLK > t_end || (WIN && T < lo_hi);
+            const bool MASKED = (causal && T + BLK - 1 > lim_lo) || T + BLK > t_end || (WIN && T < lo_hi);
             load_v(T + BLK, VN);  // past the split's end: in-bounds stand-ins, never weighted
             // keep the next block's loads ahead of this block's waits (the scheduler would otherwise
             // sink them below the first score MFMA, whose wait then drains every load in flight)
