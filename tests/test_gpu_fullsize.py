@@ -7,18 +7,26 @@ import pytest
 import torch
 
 import gen
+import paged_kv_cache_c8_amd as pkv
 from tests.gpu_harness import Run, lse_bar, oracle_run, sub_workload
 from tests.helpers import attention_close, v_token_major
 
 pytestmark = pytest.mark.gpu
 
 
-def _check(idx, n_sample, kernel=0, quant_mode=None, window=0):
+def _check(idx, n_sample, kernel=0, quant_mode=None, window=0, fused=False):
     w = gen.make_config(idx, quant_mode=quant_mode)
     r = Run(w, with_oracle=False)
     r.store_prior()
-    r.store_new()
-    out, lse = r.decode(kernel=kernel, window=window)
+    if fused:  # the decode step with its store in one call, as bench.py times it by default
+        assert w.decode_only
+        q = r.queries()
+        kn, vn = r._decode_rows(r.k_new), r._decode_rows(r.v_new)
+        lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=q.device)
+        out = pkv.store_decode_gqa(q, kn, vn, r.cache, r.bt, r.ctx, 1.0 / np.sqrt(w.head_dim), lse_out=lse)
+    else:
+        r.store_new()
+        out, lse = r.decode(kernel=kernel, window=window)
     torch.cuda.synchronize()
     rng = np.random.default_rng(100 + idx)
     sel = np.arange(w.batch) if n_sample >= w.batch else np.sort(rng.choice(w.batch, n_sample, replace=False))
@@ -69,6 +77,15 @@ def _check(idx, n_sample, kernel=0, quant_mode=None, window=0):
     assert np.array_equal(np.isfinite(gl), fin)
     tol = np.broadcast_to(1e-4 + 1e-5 * np.abs(np.where(fin, olse, 0.0)) + slack, olse.shape)
     assert np.all(np.abs(gl[fin] - olse[fin]) <= tol[fin])
+
+
+def test_qwen3_8b_step_with_store_full():
+    """The benchmark's default step: every sequence's new token stored by the decode call itself."""
+    _check(1, 32, fused=True)
+
+
+def test_long_context_step_with_store_sampled():
+    _check(2, 2, fused=True)
 
 
 def test_qwen3_8b_decode_full():
