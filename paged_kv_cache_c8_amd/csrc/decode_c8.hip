@@ -387,7 +387,10 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b_, co
                     qslot(1, rt, m) = qm;
                     qslot(2, rt, m) = ql;
                 }
-                rowmul[rt] = fabsf(a.scale_log2) * ldexpf(1.0f, -k);
+                // floored at 2^-126: a hidden key's -inf score must stay -inf (a zero scale would
+                // make it NaN), and below the floor every logit difference is far under fp32's
+                // resolution of exp2 near 1, so a zero scale still weighs every visible key 1
+                rowmul[rt] = fmaxf(fabsf(a.scale_log2) * ldexpf(1.0f, -k), 0x1p-126f);
             }
 
         }
@@ -438,44 +441,10 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b_, co
             load_k(T + KD * BLK, R);
             __builtin_amdgcn_sched_barrier(0);
 
-            // -------------------------------------------- V-scale reference of the column
-            float vsl[NSLOT][4];
+            // -------------------------------------------- scores in integer units times the K scales
+            float x[RT][NSLOT][4];
     #pragma unroll
-            for (int u = 0; u < NSLOT; ++u)
-    #pragma unroll
-                for (int i = 0; i < 4; ++i) vsl[u][i] = MODE == 0 ? R.vs[u][i] : (MODE == 1 ? R.vs[u][0] : 1.0f);
-            float sf = 1.0f;
-            bool s_moved = false;
-            {
-                float vmax = 0.0f;
-    #pragma unroll
-                for (int u = 0; u < NSLOT; ++u)
-    #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (!MASKED || key_of(T, u, i) < t_end) vmax = fmaxf(vmax, vsl[u][i]);
-                vmax = col_max(vmax);
-                if (vmax > 16.0f * sref) {  // (also the first block: sref == 0)
-                    sf = sref > 0.0f ? sref * __builtin_amdgcn_rcpf(vmax) : 0.0f;
-                    sref = vmax;
-                    sinv = __builtin_amdgcn_rcpf(vmax);
-                    s_moved = true;
-                }
-            }
-            // slots past the keys may never have been written: their scales must not reach a weight
-    #pragma unroll
-            for (int u = 0; u < NSLOT; ++u)
-    #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    vsl[u][i] = (!MASKED || key_of(T, u, i) < t_end) ? vsl[u][i] * sinv : 0.0f;
-
-            // -------------------------------------------- online softmax per column, P operands
-            uint32_t wpk[RT][NSLOT][2];
-            float factor[RT];
-            bool any_rescale = s_moved;
-    #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                float x[NSLOT][4];
-                float bmax = -INFINITY;
+            for (int rt = 0; rt < RT; ++rt)
     #pragma unroll
                 for (int u = 0; u < NSLOT; ++u) {
                     i4 S = sc[rt][J * u], S2 = sc2[rt][J * u];
@@ -488,29 +457,79 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b_, co
     #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const float si = __builtin_fmaf((float)S[i], 256.0f, (float)S2[i]);
-                        x[u][i] = si * (MODE == 0 ? R.ks[u][i] : (MODE == 1 ? R.ks[u][0] : 1.0f));
-                        if (MASKED) {
-                            const int t = key_of(T, u, i);
-                            if (!(t < t_end && t <= lim[rt] && (!WIN || t >= lo[rt]))) x[u][i] = -INFINITY;
-                        }
-                        bmax = fmaxf(bmax, x[u][i]);
+                        x[rt][u][i] = si * (MODE == 0 ? R.ks[u][i] : (MODE == 1 ? R.ks[u][0] : 1.0f));
                     }
                 }
+            float vsl[NSLOT][4];
+    #pragma unroll
+            for (int u = 0; u < NSLOT; ++u)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) vsl[u][i] = MODE == 0 ? R.vs[u][i] : (MODE == 1 ? R.vs[u][0] : 1.0f);
+            // -------------------------------------------- the mask, one scalar branch for the whole block:
+            //      hidden keys score -inf; slots past the keys may never have been written, so their
+            //      (possibly non-finite) V scales must not reach a weight or the column's reference
+            if (MASKED) {
+    #pragma unroll
+                for (int u = 0; u < NSLOT; ++u)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = key_of(T, u, i);
+                        if (!(t < t_end)) vsl[u][i] = 0.0f;
+    #pragma unroll
+                        for (int rt = 0; rt < RT; ++rt)
+                            if (!(t < t_end && t <= lim[rt] && (!WIN || t >= lo[rt]))) x[rt][u][i] = -INFINITY;
+                    }
+            }
+
+            // -------------------------------------------- V-scale reference of the column
+            float sf = 1.0f;
+            bool s_moved = false;
+            {
+                float vmax = 0.0f;
+    #pragma unroll
+                for (int u = 0; u < NSLOT; ++u)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) vmax = fmaxf(vmax, vsl[u][i]);
+                vmax = col_max(vmax);
+                if (vmax > 16.0f * sref) {  // (also the first block: sref == 0)
+                    sf = sref > 0.0f ? sref * __builtin_amdgcn_rcpf(vmax) : 0.0f;
+                    sref = vmax;
+                    sinv = __builtin_amdgcn_rcpf(vmax);
+                    s_moved = true;
+                }
+            }
+    #pragma unroll
+            for (int u = 0; u < NSLOT; ++u)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) vsl[u][i] *= sinv;
+
+            // -------------------------------------------- online softmax per column, P operands
+            uint32_t wpk[RT][NSLOT][2];
+            float factor[RT];
+            bool any_rescale = s_moved;
+    #pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                float bmax = -INFINITY;
+    #pragma unroll
+                for (int u = 0; u < NSLOT; ++u)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, x[rt][u][i]);
                 bmax = col_max(bmax) * rowmul[rt];
                 float alpha = 1.0f;
                 if (bmax > mr[rt] + 8.0f) {  // (also the first block: mr == -inf)
                     alpha = __builtin_amdgcn_exp2f(mr[rt] - bmax);
                     mr[rt] = bmax;
                 }
+                // a column with no visible key yet keeps mr = -inf; its weights are taken against 0,
+                // so that a hidden key (-inf times the positive rowmul) weighs exactly 0
+                const float mref = mr[rt] == -INFINITY ? 0.0f : mr[rt];
                 float ps = 0.0f;
     #pragma unroll
                 for (int u = 0; u < NSLOT; ++u) {
                     float p[4];
     #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[u][i], rowmul[rt], -mr[rt]));
-                        // a column with no visible key yet keeps mr = -inf: its masked keys weigh 0
-                        if (MASKED && x[u][i] == -INFINITY) p[i] = 0.0f;
+                        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[rt][u][i], rowmul[rt], -mref));
                         ps += p[i];
                     }
                     const h4 w = {(_Float16)(p[0] * vsl[u][0]), (_Float16)(p[1] * vsl[u][1]),
