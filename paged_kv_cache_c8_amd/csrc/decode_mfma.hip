@@ -295,6 +295,46 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, const int b, c
             }
         }
 
+        // -------------------------------------------- scores in log2 units
+        float sv[RT][8];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float raw = sc[rt][e >> 2][e & 3] - qbias[rt];
+                sv[rt][e] = raw * (R.ks[e] * rowmul[rt]);
+            }
+        float vs[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vs[e] = R.vs[e];
+        // -------------------------------------------- the mask, one scalar branch for the whole block:
+        //      hidden keys score -inf; slots past the keys may never have been written, so their
+        //      scales (and bf16 values) must not reach a weight or the V-scale reference
+        uint32_t vcode[C::DT][C::VW];  // this block's V operand words (bf16: cleared past the keys)
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < C::VW; ++i) vcode[dt][i] = R.v[dt][i];
+        if (MASKED) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int t = T + 8 * g + e;
+                if (!(t < t_end)) vs[e] = 0.0f;
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    if (!(t < t_end && t <= lim[rt] && t >= lo[rt])) sv[rt][e] = -INFINITY;
+            }
+            if constexpr (MODE == 2) {  // the lane's 8 keys, two per dword of each channel's V
+                const int tk = T + 8 * g;
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const uint32_t keep = tk + 2 * e2 + 1 < t_end ? ~0u : (tk + 2 * e2 < t_end ? 0xffffu : 0u);
+#pragma unroll
+                    for (int dt = 0; dt < C::DT; ++dt) vcode[dt][e2] &= keep;
+                }
+            }
+        }
+
         // -------------------------------------------- V-scale reference
         float sf = 1.0f;
         bool s_moved = false;
@@ -302,8 +342,7 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, const int b, c
         if constexpr (MODE != 2) {
             float vmax = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (!MASKED || T + 8 * g + e < t_end) vmax = fmaxf(vmax, R.vs[e]);
+            for (int e = 0; e < 8; ++e) vmax = fmaxf(vmax, vs[e]);
             vmax = xor16_max(vmax);
             if (vmax > 16.0f * s_ref) {  // (also the first block: s_ref == 0)
                 sf = s_ref > 0.0f ? s_ref * __builtin_amdgcn_rcpf(vmax) : 0.0f;
@@ -311,9 +350,8 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, const int b, c
                 s_moved = true;
             }
             const float inv = s_ref > 0.0f ? __builtin_amdgcn_rcpf(s_ref) : 0.0f;
-            // slots past the keys may never have been written: their scales must not reach the weights
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vscale[e] = (!MASKED || T + 8 * g + e < t_end) ? R.vs[e] * inv : 0.0f;
+            for (int e = 0; e < 8; ++e) vscale[e] = vs[e] * inv;
         }
 
         // -------------------------------------------- online softmax, P operand
@@ -322,31 +360,23 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, const int b, c
         bool any_rescale = s_moved;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            float sv[8];
             float bmax = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float raw = sc[rt][e >> 2][e & 3] - qbias[rt];
-                sv[e] = raw * (R.ks[e] * rowmul[rt]);
-                if (MASKED) {
-                    const int t = T + 8 * g + e;
-                    if (!(t < t_end && t <= lim[rt] && t >= lo[rt])) sv[e] = -INFINITY;
-                }
-                bmax = fmaxf(bmax, sv[e]);
-            }
+            for (int e = 0; e < 8; ++e) bmax = fmaxf(bmax, sv[rt][e]);
             bmax = xor16_max(bmax);
             float alpha = 1.0f;
             if (bmax > m_ref[rt] + 8.0f) {  // (also the first block: m_ref == -inf)
                 alpha = __builtin_amdgcn_exp2f(m_ref[rt] - bmax);
                 m_ref[rt] = bmax;
             }
+            // a row with no visible key yet keeps m_ref = -inf; its weights are taken against 0, so
+            // that its hidden keys (-inf) weigh exactly 0
+            const float mref = m_ref[rt] == -INFINITY ? 0.0f : m_ref[rt];
             float p[8];
             float psum = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                p[e] = __builtin_amdgcn_exp2f(sv[e] - m_ref[rt]);
-                // a row with no visible key yet keeps m_ref = -inf: its masked keys weigh 0
-                if (MASKED && sv[e] == -INFINITY) p[e] = 0.0f;
+                p[e] = __builtin_amdgcn_exp2f(sv[rt][e] - mref);
                 psum += p[e];
             }
             psum = xor16_sum(psum);
@@ -379,27 +409,17 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, const int b, c
         }
 
         // -------------------------------------------- P.V over the 32 keys (+ the weight sums)
-        // bf16 slots past the keys may hold any bit pattern: the lane's 8 keys as a mask per dword
-        // (selects, no lane-divergent branch in the key loop)
-        uint32_t vkeep[4] = {~0u, ~0u, ~0u, ~0u};
-        if constexpr (MODE == 2) {
-            const int tk = T + 8 * g;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2)
-                vkeep[e2] = tk + 2 * e2 + 1 < t_end ? ~0u : (tk + 2 * e2 < t_end ? 0xffffu : 0u);
-        }
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
             if constexpr (MODE == 2) {
-                const uint32_t r[4] = {R.v[dt][0] & vkeep[0], R.v[dt][1] & vkeep[1], R.v[dt][2] & vkeep[2],
-                                       R.v[dt][3] & vkeep[3]};
+                const uint32_t r[4] = {vcode[dt][0], vcode[dt][1], vcode[dt][2], vcode[dt][3]};
                 const b8 bv = __builtin_bit_cast(b8, r);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
                     acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, pa[rt]), bv,
                                                                           acc[rt][dt], 0, 0, 0);
             } else {
-                const h8 bv = biased_h8(R.v[dt][0], R.v[dt][1]);
+                const h8 bv = biased_h8(vcode[dt][0], vcode[dt][1]);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
                     acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, pa[rt]), bv,
