@@ -29,7 +29,8 @@
  *    been launched.
  *  - Device-resident index data (block_table, context_lengths, cu_q_lens,
  *    slot_mapping, seq_offsets) are preconditions, not checked: reading them
- *    on the host would need a synchronisation.  They must be in range.
+ *    on the host would need a synchronisation.  They must be in range
+ *    (pkv_check_indices checks them on the device, for debugging).
  *  - context_lengths[b] counts every position of sequence b AFTER the call's
  *    new tokens are stored; the new tokens of b occupy positions
  *    [context_lengths[b] - q_len_b, context_lengths[b]).
@@ -186,6 +187,47 @@ int pkv_dequant(const pkv_cache_t *cache, const int32_t *block_table, int32_t ma
 int pkv_cache_walk(const pkv_cache_t *cache, const int32_t *block_table, int32_t max_blocks_per_seq,
                    const int32_t *context_lengths, int32_t batch, int32_t split_tokens, int32_t depth,
                    uint32_t *out, void *stream);
+
+/* Bits of pkv_check_indices' result[0]. */
+enum {
+    PKV_CHECK_CONTEXT = 1, /* a context length outside [0, max_blocks_per_seq * block_size] */
+    PKV_CHECK_BLOCK = 2,   /* a block-table entry the context reaches outside [0, num_blocks) */
+    PKV_CHECK_QLEN = 4,    /* cu_q_lens[0] != 0, cu_q_lens decreasing, or a q_len above the
+                              sequence's context length or above max_q_len (when > 0) */
+    PKV_CHECK_SLOT = 8     /* a slot-mapping entry >= num_blocks * block_size */
+};
+
+/*
+ * pkv_check_indices - optional debug validator (not an operation of the pages):
+ * checks on the device the index arrays that the other calls take as unchecked
+ * preconditions (see "Device-resident index data" above), before a call that
+ * would read out of bounds with them is made.
+ *
+ * num_blocks, block_size  the pool's size (a pkv_cache_t's or an MLA cache's).
+ * block_table   int32 [batch][max_blocks_per_seq] or NULL; entries j with
+ *               j * block_size < context_lengths[b] are checked (the calls read
+ *               no others).  Needs context_lengths.
+ * context_lengths  int32 [batch] or NULL.
+ * cu_q_lens     int32 [batch + 1] or NULL; max_q_len <= 0: no upper bound.
+ * slot_mapping  int64 [num_tokens] or NULL (negative entries are valid: the
+ *               store skips them).
+ * result        device int32 [4], 4-byte aligned, fully written by the call:
+ *               [0] the PKV_CHECK_* bits of every violated condition (0: all
+ *               hold), [1] the lowest offending sequence (-1: none), [2] the
+ *               lowest offending token of slot_mapping (-1: none), [3] 0.
+ * One launch of one workgroup, asynchronous on `stream`; the caller reads
+ * `result` once the stream has reached the call.  The check reads only inside
+ * the arrays' stated sizes, whatever their contents.  Not checked: that no
+ * physical block is shared between sequences (pkv_store_c8's per-block mode).
+ * Errors (nothing launched): PKV_ERR_INVALID_ARG for a NULL or misaligned
+ * result, negative sizes, a block table without context lengths, batch > 0
+ * with no array to check, or num_tokens > 0 without slot_mapping.
+ */
+int pkv_check_indices(int32_t num_blocks, int32_t block_size, const int32_t *block_table,
+                      int32_t max_blocks_per_seq, const int32_t *context_lengths,
+                      const int32_t *cu_q_lens, int32_t max_q_len, int32_t batch,
+                      const int64_t *slot_mapping, int32_t num_tokens, int32_t *result,
+                      void *stream);
 
 /* Optional knobs of pkv_decode_gqa (pass NULL for the defaults). */
 typedef struct {

@@ -11,6 +11,13 @@ allocates itself are allocated on the stream the call runs on, so the caching al
 their memory to other work while the kernels still use it.
 
 There is no fallback: if ``libpkv.so`` has not been built, ``lib()`` raises.
+
+Debug-only environment overrides (read at each call): ``PKV_CHECK=1`` runs ``check_indices`` (the
+device-side bounds check of the block table, context lengths, query-length prefix sums and slot
+mapping) before every store, dequant, walk and decode call and raises ``PkvIndexError`` instead of
+making a call that would read out of bounds (it waits for the GPU: tests and debugging only);
+``PKV_SPLIT_TOKENS=n`` and ``PKV_DECODE_PATH=valu|mfma|c8`` stand in for the GQA decode's
+``split_tokens`` and ``kernel`` arguments where a call leaves them at 0.
 """
 from __future__ import annotations
 
@@ -19,7 +26,8 @@ import os
 
 import torch  # loaded first: libpkv binds to the HIP runtime torch has already loaded
 
-__all__ = ["PkvError", "Cache", "lib", "store_c8", "dequant", "decode_gqa", "decode_gqa_noalloc", "store_decode_gqa", "cache_walk",
+__all__ = ["PkvError", "PkvIndexError", "check_indices", "CHECK_CONTEXT", "CHECK_BLOCK", "CHECK_QLEN",
+           "CHECK_SLOT", "Cache", "lib", "store_c8", "dequant", "decode_gqa", "decode_gqa_noalloc", "store_decode_gqa", "cache_walk",
            "decode_workspace_size", "NOALLOC_SCRATCH_BYTES",
            "decode_plan", "MLACache", "mla_store_c8", "mla_decode", "mla_decode_workspace_size",
            "mla_decode_plan", "QUANT_PER_TOKEN", "QUANT_PER_BLOCK", "QUANT_NONE_BF16", "QUANT_PER_CHANNEL",
@@ -37,7 +45,7 @@ QUANT_PER_CHANNEL = 3
 EXPORTS = ("pkv_status_string", "pkv_version", "pkv_store_c8", "pkv_dequant",
            "pkv_decode_workspace_size", "pkv_decode_gqa", "pkv_decode_plan", "pkv_mla_store_c8",
            "pkv_mla_decode_workspace_size", "pkv_mla_decode_plan", "pkv_mla_decode", "pkv_decode_gqa_noalloc",
-           "pkv_store_decode_gqa", "pkv_cache_walk")
+           "pkv_store_decode_gqa", "pkv_cache_walk", "pkv_check_indices")
 
 NOALLOC_SCRATCH_BYTES = 32 << 20  # PKV_NOALLOC_SCRATCH_BYTES
 
@@ -91,6 +99,8 @@ def lib():
         L.pkv_dequant.restype = ctypes.c_int
         L.pkv_cache_walk.argtypes = [P, P, I32, P, I32, I32, I32, P, P]
         L.pkv_cache_walk.restype = ctypes.c_int
+        L.pkv_check_indices.argtypes = [I32, I32, P, I32, P, P, I32, I32, P, I32, P, P]
+        L.pkv_check_indices.restype = ctypes.c_int
         L.pkv_decode_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32, P]
         L.pkv_decode_workspace_size.restype = SZ
         L.pkv_decode_gqa.argtypes = [P, I32, P, P, I32, P, P, I32, I32, ctypes.c_float, P, P, P, SZ,
@@ -170,8 +180,63 @@ def _check(status, what):
 
 PARTITION_PLANNED, PARTITION_FIXED, PARTITION_BALANCED = 0, 1, 2
 
+CHECK_CONTEXT, CHECK_BLOCK, CHECK_QLEN, CHECK_SLOT = 1, 2, 4, 8  # PKV_CHECK_* of include/pkv.h
+
+
+class PkvIndexError(ValueError):
+    """An index array failed ``check_indices`` (raised under ``PKV_CHECK=1`` before the call)."""
+
+
+def check_indices(cache, block_table=None, context_lengths=None, *, cu_q_lens=None, max_q_len=0,
+                  slot_mapping=None, stream=None):
+    """Bounds-check on the device the index arrays a call on ``cache`` (a ``Cache`` or ``MLACache``)
+    would read; waits for the result.  Returns ``(flags, first_sequence, first_token)``: the
+    ``CHECK_*`` bits of every violated condition (0 when all hold) and the lowest offending
+    sequence and slot-mapping token (-1: none)."""
+    ref = cache.k if isinstance(cache, Cache) else cache.latent
+    _want(context_lengths, "context_lengths", torch.int32, ndim=1, optional=True)
+    batch = int(context_lengths.shape[0]) if context_lengths is not None else \
+        (int(cu_q_lens.shape[0]) - 1 if cu_q_lens is not None else 0)
+    _want(block_table, "block_table", torch.int32, (batch, None), optional=True)
+    _want(cu_q_lens, "cu_q_lens", torch.int32, (batch + 1,), optional=True)
+    _want(slot_mapping, "slot_mapping", torch.int64, ndim=1, optional=True)
+    _same_device(ref, block_table=block_table, context_lengths=context_lengths, cu_q_lens=cu_q_lens,
+                 slot_mapping=slot_mapping)
+    with _on_stream(stream):
+        result = torch.empty(4, dtype=torch.int32, device=ref.device)
+    mbs = int(block_table.shape[1]) if block_table is not None else 0
+    ntok = int(slot_mapping.shape[0]) if slot_mapping is not None else 0
+    st = lib().pkv_check_indices(cache.num_blocks, cache.block_size, _ptr(block_table), mbs,
+                                 _ptr(context_lengths), _ptr(cu_q_lens), int(max_q_len), batch,
+                                 _ptr(slot_mapping), ntok, _ptr(result), _stream(stream))
+    _check(st, "pkv_check_indices")
+    r = result.cpu().tolist()  # (waits for the check)
+    return int(r[0]), int(r[1]), int(r[2])
+
+
+def _debug_check(cache, what, **arrays):
+    """Under PKV_CHECK=1: raise PkvIndexError before ``what`` if its index arrays are out of range."""
+    if os.environ.get("PKV_CHECK", "0") in ("", "0"):
+        return
+    flags, seq, tok = check_indices(cache, **arrays)
+    if flags:
+        names = [n for n, bit in (("context length", CHECK_CONTEXT), ("block-table entry", CHECK_BLOCK),
+                                  ("query lengths", CHECK_QLEN), ("slot mapping", CHECK_SLOT)) if flags & bit]
+        where = f"sequence {seq}" if seq >= 0 else f"token {tok}"
+        raise PkvIndexError(f"{what}: {', '.join(names)} out of range (first at {where}; PKV_CHECK flags {flags})")
+
+
+_DECODE_PATHS = {"valu": 1, "mfma": 2, "c8": 3}
+
 
 def _opts(split_tokens=0, kernel=0, partition=0, window=0):
+    if int(split_tokens) == 0 and os.environ.get("PKV_SPLIT_TOKENS"):
+        split_tokens = int(os.environ["PKV_SPLIT_TOKENS"])
+    if int(kernel) == 0 and os.environ.get("PKV_DECODE_PATH"):
+        path = os.environ["PKV_DECODE_PATH"]
+        if path not in _DECODE_PATHS:
+            raise ValueError(f"PKV_DECODE_PATH={path!r}: expected one of {sorted(_DECODE_PATHS)}")
+        kernel = _DECODE_PATHS[path]
     o = _DecodeOpts()
     o.split_tokens = int(split_tokens)
     o.kernel = int(kernel)
@@ -247,6 +312,8 @@ def store_c8(cache: Cache, k_new, v_new, *, slot_mapping=None, cu_q_lens=None, c
             raise ValueError(f"without cu_q_lens every sequence stores one token: {t} tokens for {batch} sequences")
     _same_device(cache.k, k_new=k_new, v_new=v_new, slot_mapping=slot_mapping, cu_q_lens=cu_q_lens,
                  context_lengths=context_lengths, block_table=block_table)
+    _debug_check(cache, "pkv_store_c8", block_table=block_table, context_lengths=context_lengths,
+                 cu_q_lens=cu_q_lens, max_q_len=max_q_len, slot_mapping=slot_mapping)
     st = lib().pkv_store_c8(cache.ref, _ptr(k_new), _ptr(v_new), t, _ptr(slot_mapping), _ptr(cu_q_lens),
                             _ptr(context_lengths), _ptr(block_table), batch, mbs, int(max_q_len),
                             cache.quant_mode, _stream(stream))
@@ -267,6 +334,7 @@ def dequant(cache: Cache, block_table, context_lengths, *, seq_offsets=None, k_o
     _want(v_out, "v_out", torch.bfloat16, optional=True)
     _same_device(cache.k, block_table=block_table, context_lengths=context_lengths, seq_offsets=seq_offsets,
                  k_out=k_out, v_out=v_out)
+    _debug_check(cache, "pkv_dequant", block_table=block_table, context_lengths=context_lengths)
     if k_out is None and v_out is None:
         if num_rows is None:  # (sizing from the lengths synchronises with the GPU)
             num_rows = int(context_lengths.sum().item()) if seq_offsets is None else \
@@ -300,6 +368,7 @@ def cache_walk(cache: Cache, block_table, context_lengths, split_tokens, *, dept
     if out is None:
         with _on_stream(stream):
             out = torch.empty((batch, cache.num_kv_heads, max(nsplit, 1)), dtype=torch.int32, device=cache.k.device)
+    _debug_check(cache, "pkv_cache_walk", block_table=block_table, context_lengths=context_lengths)
     st = lib().pkv_cache_walk(cache.ref, _ptr(block_table), mbs, _ptr(context_lengths), batch, int(split_tokens),
                               int(depth), _ptr(out), _stream(stream))
     _check(st, "pkv_cache_walk")
@@ -357,6 +426,8 @@ def decode_gqa(q, cache: Cache, block_table, context_lengths, scale, *, cu_q_len
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)  # no initial contents needed
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _debug_check(cache, "pkv_decode_gqa", block_table=block_table, context_lengths=context_lengths,
+                 cu_q_lens=cu_q_lens, max_q_len=max_q_len)
     st = lib().pkv_decode_gqa(_ptr(q), hq, cache.ref, _ptr(block_table), mbs, _ptr(context_lengths),
                               _ptr(cu_q_lens), batch, int(max_q_len), float(scale), _ptr(out),
                               _ptr(lse_out), _ptr(workspace), ws_bytes, ctypes.byref(o), _stream(stream))
@@ -391,6 +462,7 @@ def store_decode_gqa(q, k_new, v_new, cache: Cache, block_table, context_lengths
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)  # no initial contents needed
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _debug_check(cache, "pkv_store_decode_gqa", block_table=block_table, context_lengths=context_lengths)
     st = lib().pkv_store_decode_gqa(_ptr(q), _ptr(k_new), _ptr(v_new), hq, cache.ref, _ptr(block_table), mbs,
                                     _ptr(context_lengths), batch, float(scale), _ptr(out), _ptr(lse_out),
                                     _ptr(workspace), ws_bytes, ctypes.byref(o), _stream(stream))
@@ -420,6 +492,8 @@ def decode_gqa_noalloc(q, cache: Cache, block_table, context_lengths, scale, out
     _same_device(cache.k, q=q, block_table=block_table, context_lengths=context_lengths, cu_q_lens=cu_q_lens,
                  out=out, lse_out=lse_out)
     o = _opts(split_tokens, kernel, partition, window)
+    _debug_check(cache, "pkv_decode_gqa_noalloc", block_table=block_table, context_lengths=context_lengths,
+                 cu_q_lens=cu_q_lens, max_q_len=max_q_len)
     st = lib().pkv_decode_gqa_noalloc(_ptr(q), hq, cache.ref, _ptr(block_table), int(block_table.shape[1]),
                                       _ptr(context_lengths), _ptr(cu_q_lens), batch, int(max_q_len), float(scale),
                                       _ptr(out), _ptr(lse_out), ctypes.byref(o), _stream(stream))
@@ -471,6 +545,8 @@ def mla_store_c8(cache: MLACache, latent_new, rope_new, *, slot_mapping=None, cu
             raise ValueError(f"without cu_q_lens every sequence stores one token: {t} tokens for {batch} sequences")
     _same_device(cache.latent, latent_new=latent_new, rope_new=rope_new, slot_mapping=slot_mapping,
                  cu_q_lens=cu_q_lens, context_lengths=context_lengths, block_table=block_table)
+    _debug_check(cache, "pkv_mla_store_c8", block_table=block_table, context_lengths=context_lengths,
+                 cu_q_lens=cu_q_lens, slot_mapping=slot_mapping)
     st = lib().pkv_mla_store_c8(cache.ref, _ptr(latent_new), _ptr(rope_new), t, _ptr(slot_mapping),
                                 _ptr(cu_q_lens), _ptr(context_lengths), _ptr(block_table), batch, mbs,
                                 _stream(stream))
@@ -512,6 +588,7 @@ def mla_decode(q_latent, q_rope, cache: MLACache, block_table, context_lengths, 
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=q_latent.device)  # no initial contents needed
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _debug_check(cache, "pkv_mla_decode", block_table=block_table, context_lengths=context_lengths)
     st = lib().pkv_mla_decode(_ptr(q_latent), _ptr(q_rope), heads, cache.ref, _ptr(block_table), mbs,
                               _ptr(context_lengths), batch, float(scale), _ptr(out), _ptr(lse_out),
                               _ptr(workspace), ws_bytes, int(split_tokens), _stream(stream))

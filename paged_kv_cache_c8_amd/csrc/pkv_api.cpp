@@ -340,6 +340,32 @@ int pkv_cache_walk(const pkv_cache_t* cache, const int32_t* block_table, int32_t
                                        static_cast<hipStream_t>(stream)));
 }
 
+int pkv_check_indices(int32_t num_blocks, int32_t block_size, const int32_t* block_table,
+                      int32_t max_blocks_per_seq, const int32_t* context_lengths, const int32_t* cu_q_lens,
+                      int32_t max_q_len, int32_t batch, const int64_t* slot_mapping, int32_t num_tokens,
+                      int32_t* result, void* stream) {
+    if (!result || !aligned(result, 4)) return PKV_ERR_INVALID_ARG;
+    if (num_blocks < 0 || block_size <= 0 || batch < 0 || num_tokens < 0) return PKV_ERR_INVALID_ARG;
+    if (block_table && (!context_lengths || max_blocks_per_seq <= 0)) return PKV_ERR_INVALID_ARG;
+    if (context_lengths && max_blocks_per_seq < 0) return PKV_ERR_INVALID_ARG;
+    if (batch > 0 && !context_lengths && !cu_q_lens && !slot_mapping) return PKV_ERR_INVALID_ARG;
+    if (num_tokens > 0 && !slot_mapping) return PKV_ERR_INVALID_ARG;
+    pkv::CheckArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.bt = block_table;
+    a.ctx = context_lengths;
+    a.cu = cu_q_lens;
+    a.slot = slot_mapping;
+    a.result = result;
+    a.num_blocks = num_blocks;
+    a.bs = block_size;
+    a.mbs = max_blocks_per_seq;
+    a.batch = batch;
+    a.max_q_len = max_q_len;
+    a.num_tokens = slot_mapping ? num_tokens : 0;
+    return hip_status(pkv::launch_check(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t pkv_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
                                  int32_t max_q_len, int32_t quant_mode, const pkv_decode_opts_t* opts) {

@@ -109,6 +109,24 @@ __host__ __device__ inline int win_begin(int window, int pos) { return win_lo(wi
 hipError_t launch_store(const StoreArgs& a, int head_dim, int mode, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, int head_dim, int mode, hipStream_t stream);
 hipError_t launch_walk(const WalkArgs& a, int batch, int head_dim, int mode, int depth, hipStream_t stream);
+
+// pkv_check_indices (check.hip): the arrays to check (NULL: not checked) and the sizes that bound them
+struct CheckArgs {
+    const int32_t* bt;
+    const int32_t* ctx;
+    const int32_t* cu;
+    const int64_t* slot;
+    int32_t* result;
+    int num_blocks;
+    int bs;
+    int mbs;
+    int batch;
+    int max_q_len;
+    int num_tokens;
+};
+// result bits (the same values as pkv.h's PKV_CHECK_*)
+constexpr int kCheckContext = 1, kCheckBlock = 2, kCheckQlen = 4, kCheckSlot = 8;
+hipError_t launch_check(const CheckArgs& a, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs& a, int batch, int head_dim, int rg, int mode,
                               hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int batch, int head_dim, int row_tiles, int mode,

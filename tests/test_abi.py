@@ -173,3 +173,36 @@ def test_mla_plan_and_argument_checks(pkv):
     c64 = pkv._MLACacheT(16, 32, 64, 128, 4, 64, 512, 64)
     assert dec(P, P, 16, ctypes.byref(c64), P, 128, P, 64, 1.0, P, None, P, need - 1, 0, None) == -3
     assert dec(P, P, 16, ctypes.byref(c64), P, 128, P, 0, 1.0, P, None, None, 0, 0, None) == 0  # empty batch
+
+
+def test_check_indices_rejects_bad_arguments(pkv):
+    """pkv_check_indices: argument errors are reported before anything is launched."""
+    lib = pkv.lib()
+    P = 4096
+    chk = lambda *a: lib.pkv_check_indices(*a)
+    #      num_blocks, bs, bt, mbs, ctx, cu, max_q, batch, slot, ntok, result, stream
+    assert chk(8, 16, P, 4, P, None, 0, 2, None, 0, None, None) == -1  # no result
+    assert chk(8, 16, P, 4, P, None, 0, 2, None, 0, P + 2, None) == -1  # misaligned result
+    assert chk(8, 16, P, 4, None, None, 0, 2, None, 0, P, None) == -1  # block table without lengths
+    assert chk(8, 16, P, 0, P, None, 0, 2, None, 0, P, None) == -1  # block table without a row size
+    assert chk(8, 16, None, 0, None, None, 0, 2, None, 0, P, None) == -1  # nothing to check
+    assert chk(8, 16, None, 0, None, None, 0, 0, None, 3, P, None) == -1  # tokens without slots
+    assert chk(-1, 16, P, 4, P, None, 0, 2, None, 0, P, None) == -1
+    assert chk(8, 0, P, 4, P, None, 0, 2, None, 0, P, None) == -1
+
+
+def test_debug_environment_overrides(pkv, monkeypatch):
+    """PKV_SPLIT_TOKENS and PKV_DECODE_PATH stand in for arguments left at 0, never for given ones."""
+    base = pkv.decode_plan(8, 64, 8, 128, 1024, 128, 1, 0)
+    monkeypatch.setenv("PKV_SPLIT_TOKENS", "1000")
+    assert pkv.decode_plan(8, 64, 8, 128, 1024, 128, 1, 0)["split_tokens"] == 1024
+    assert pkv.decode_plan(8, 64, 8, 128, 1024, 128, 1, 0, split_tokens=512)["split_tokens"] == 512
+    monkeypatch.delenv("PKV_SPLIT_TOKENS")
+    assert pkv.decode_plan(8, 64, 8, 128, 1024, 128, 1, 0) == base
+    for path, kernel in (("valu", 1), ("mfma", 2), ("c8", 3)):
+        monkeypatch.setenv("PKV_DECODE_PATH", path)
+        assert pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 0)["kernel"] == kernel
+    assert pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 0, kernel=2)["kernel"] == 2
+    monkeypatch.setenv("PKV_DECODE_PATH", "cuda")
+    with pytest.raises(ValueError):
+        pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 0)
