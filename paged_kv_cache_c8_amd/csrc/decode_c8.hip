@@ -713,8 +713,10 @@ __device__ __forceinline__ void c8_segment(const DecodeArgs& a, const int b_, co
 // KV head) go fastest, so consecutive workgroups go round-robin over the XCDs and each XCD gets an
 // even share whatever the number of empty splits; the row groups of one pair (which read the
 // same keys) take workgroups 8 apart, so they run on one XCD at about the same time and all but
-// the first read the keys from its L2.  Workgroup 8 (q nrg + rg) + x takes row group rg of pair
-// 8 q + x.
+// the first read the keys from its L2.  Workgroup 8 (q nrg + c) + x takes row group nrg - 1 - c of
+// pair 8 q + x: a causal chunk's or prompt's last row groups, which see the most keys, start first
+// and the short ones fill the end of the launch (measured on a 4 x 2048-token prefill: 323 against
+// 358 us with the short ones first).
 template <int D, int MODE, int J, int RT, bool WIN>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 1))) void decode_c8_kernel(DecodeArgs a, int pairs) {
     constexpr int ROWS = J > 1 ? 16 / J : 16 * RT;
@@ -727,7 +729,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(J > 1 ? 2 : 
     if (u >= pairs) return;
     const int nbh = pairs / a.nsplit;
     const int s = u / nbh;
-    const int item = (u % nbh) * a.nrg + rest % a.nrg;
+    const int item = (u % nbh) * a.nrg + (a.nrg - 1 - rest % a.nrg);
     const ItemGeo it = item_geo<ROWS, WIN>(a, item);
     if (it.nvalid <= 0) return;
     if (it.kmax <= 0) {
