@@ -326,9 +326,10 @@ def run_decode(args, config_index, quant_mode, with_cpu):
         "median_launch_ms": round(float(np.median(call_ms)), 5),
     }
     if w.name.startswith("paged-prefill"):
-        # a prompt's attention is a dense contraction: 2 * 2 * D flops per visible (query head, key)
-        # pair (Q.K and P.V); the scores run as two int8 passes (hi, lo) and P.V in fp16, both at the
-        # 2.5 PFLOP/s of the dense fp16 / bf16 matrix cores
+        # a prompt's attention is a dense contraction: 2 * 2 * D algorithmic flops per visible
+        # (query head, key) pair (Q.K and P.V), against the 2.5 PFLOP/s of the dense fp16 / bf16
+        # matrix cores (the kernel runs the scores as three int8 passes, one per query digit, and
+        # P.V in fp16; only the algorithmic flops count)
         pairs = sum(int(w.q_lens[b]) * (2 * int(w.prior_lengths[b]) + int(w.q_lens[b]) + 1) // 2
                     for b in range(w.batch))
         flops = 4.0 * pairs * w.num_q_heads * w.head_dim
