@@ -101,7 +101,7 @@ PREFILL_CASES = [
 
 @pytest.mark.parametrize("mode,d,bs,g,ctx,ql", PREFILL_CASES)
 def test_paged_prefill_matches_oracle(mode, d, bs, g, ctx, ql):
-    """Paged prefill: hundreds of causal queries per sequence through the same
+    """Paged prefill (MojoPagedPrefillGQA, Mojo Opset README Op List): hundreds of causal queries per sequence through the same
     kernels (many row groups per KV head), against the oracle; also with fixed splits."""
     r = Run(_wl(mode, d, bs, g, ctx, ql, seed=sum(ctx) + mode))
     r.store_prior()
@@ -587,7 +587,7 @@ WINDOW_CASES = [
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("mode,d,bs,g,ctx,ql,window", WINDOW_CASES)
 def test_sliding_window_matches_oracle(mode, d, bs, g, ctx, ql, window, kernel):
-    """Sliding-window decode: each query sees its last `window` positions; the key
+    """Sliding-window decode (MojoSlidingWindowAttention, Mojo Opset README Op List): each query sees its last `window` positions; the key
     ranges start at the window (128-aligned), so only those blocks are read."""
     if mode == 3 and kernel != 3:
         pytest.skip("the per-channel mode is served by the int8-score kernel only")
