@@ -586,7 +586,8 @@ def mla_step_bytes(w):
 
 def main_mla(args):
     """The paged MLA decode step: store one new latent/rotary token per sequence, then latent
-    attention of every head over the int8 cache (split partials + log-sum-exp merge)."""
+    attention of every head over the int8 cache (split partials + log-sum-exp merge), as one call
+    (pkv_mla_store_decode; --separate-store: the store and the decode as two calls)."""
     import torch
 
     import gen
@@ -631,34 +632,50 @@ def main_mla(args):
         pkv.mla_decode(t["q_latent"], t["q_rope"], c, bt, ctx, w.softmax_scale, out=out, workspace=workspace,
                        split_tokens=args.split_tokens)
 
+    fused = not args.separate_store
+
+    def store_decode(c):
+        pkv.mla_store_decode(t["q_latent"], t["q_rope"], lat_new, rot_new, c, bt, ctx, w.softmax_scale, out=out,
+                             workspace=workspace, split_tokens=args.split_tokens)
+
+    def step(c):
+        if fused:
+            store_decode(c)
+        else:
+            store(c)
+            decode(c)
+
     for i in range(args.warmup):
-        store(caches[i % reps])
-        decode(caches[i % reps])
+        step(caches[i % reps])
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t0.record()
     for i in range(args.steps):
-        store(caches[i % reps])
-        decode(caches[i % reps])
+        step(caches[i % reps])
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = t0.elapsed_time(t1) / args.steps
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.steps):
-        store(caches[i % reps])
+        if not fused:
+            store(caches[i % reps])
         evs[i][0].record()
-        decode(caches[i % reps])
+        if fused:
+            store_decode(caches[i % reps])
+        else:
+            decode(caches[i % reps])
         evs[i][1].record()
     torch.cuda.synchronize()
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     step_s = ms_per_step * 1e-3
     value = touched / step_s / 1e9
-    achieved = decode_bytes / (dec_ms * 1e-3) / 1e9
+    call_bytes = decode_bytes + (store_bytes if fused else 0)
+    achieved = call_bytes / (dec_ms * 1e-3) / 1e9
     default_plan = args.split_tokens == 0
-    traffic = traffic_record(f"mla_decode.config{args.mla}") if default_plan else None
+    traffic = traffic_record(f"mla_decode.config{args.mla}") if default_plan and fused else None
     cpu = None if args.no_cpu_baseline else mla_cpu_baseline(w, t, args.cpu_seconds, touched)
     res = {
         "metric": "decode-attn HBM GB/s (% of peak) + tokens/s, int8 paged-KV GQA",
@@ -677,7 +694,8 @@ def main_mla(args):
             "workload": w.name, "batch": w.batch, "num_heads": w.num_heads, "latent_dim": w.latent_dim,
             "rope_dim": w.rope_dim, "block_size": w.block_size, "sum_context": int(w.context_lengths.sum()),
             "new_tokens": w.batch, "cache_replicas": reps, "split_tokens": plan["split_tokens"],
-            "num_splits": plan["num_splits"], "parallelism": "single-gpu",
+            "num_splits": plan["num_splits"], "store": "in the decode call" if fused else "separate call",
+            "parallelism": "single-gpu",
         },
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "tokens_per_s": round(w.batch / step_s, 1),
@@ -685,10 +703,12 @@ def main_mla(args):
         "bytes_per_step": touched,
         "wall_s_timed": round(wall, 4),
         "roofline": {
-            "bound": "hbm", "kernel": "pkv_mla_decode (split partial + log-sum-exp merge)",
+            "bound": "hbm",
+            "kernel": ("pkv_mla_store_decode (new-token store + split partial, log-sum-exp merge)" if fused
+                       else "pkv_mla_decode (split partial + log-sum-exp merge)"),
             "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-            "algorithmic_bytes_per_launch": decode_bytes, "avg_launch_ms": round(dec_ms, 5),
+            "algorithmic_bytes_per_launch": call_bytes, "avg_launch_ms": round(dec_ms, 5),
         },
         "cpu_baseline": cpu,
     }

@@ -445,6 +445,30 @@ int pkv_mla_decode(const void *q_latent, const void *q_rope, int32_t num_heads,
                    float scale, void *out, float *lse_out, void *workspace, size_t workspace_bytes,
                    int32_t split_tokens, void *stream);
 
+/*
+ * pkv_mla_store_decode - one MLA decode step in one call: store each
+ * sequence's new latent and rotary token, then attend (MojoStorePagedMLAKVCache
+ * followed by MojoPagedDecodeMLA, README Op List).
+ *
+ * The result equals pkv_mla_store_c8(cache, latent_new, rope_new, batch, NULL,
+ * NULL, context_lengths, block_table, batch, max_blocks_per_seq) followed by
+ * pkv_mla_decode(q_latent, q_rope, ...):
+ * latent_new, rope_new  bf16 [batch][512] (16-byte aligned) and [batch][64];
+ *               the token of sequence b goes to position context_lengths[b] - 1
+ *               (a sequence with context length 0 stores nothing).
+ * Other arguments, the workspace and errors as pkv_mla_decode.  With up to 16
+ * heads (one head group per sequence) the store happens inside the decode
+ * launch: the workgroup whose keys end at the new position quantizes the
+ * token, writes it to the cache and uses its codes directly; otherwise a store
+ * launch precedes the decode.
+ */
+int pkv_mla_store_decode(const void *q_latent, const void *q_rope, const void *latent_new,
+                         const void *rope_new, int32_t num_heads, const pkv_mla_cache_t *cache,
+                         const int32_t *block_table, int32_t max_blocks_per_seq,
+                         const int32_t *context_lengths, int32_t batch, float scale, void *out,
+                         float *lse_out, void *workspace, size_t workspace_bytes,
+                         int32_t split_tokens, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,7 @@ import torch  # loaded first: libpkv binds to the HIP runtime torch has already 
 __all__ = ["PkvError", "PkvIndexError", "check_indices", "CHECK_CONTEXT", "CHECK_BLOCK", "CHECK_QLEN",
            "CHECK_SLOT", "Cache", "lib", "store_c8", "dequant", "decode_gqa", "decode_gqa_noalloc", "store_decode_gqa", "cache_walk",
            "decode_workspace_size", "NOALLOC_SCRATCH_BYTES",
-           "decode_plan", "MLACache", "mla_store_c8", "mla_decode", "mla_decode_workspace_size",
+           "decode_plan", "MLACache", "mla_store_c8", "mla_decode", "mla_store_decode", "mla_decode_workspace_size",
            "mla_decode_plan", "QUANT_PER_TOKEN", "QUANT_PER_BLOCK", "QUANT_NONE_BF16", "QUANT_PER_CHANNEL",
            "EXPORTS"]
 
@@ -45,7 +45,7 @@ QUANT_PER_CHANNEL = 3
 EXPORTS = ("pkv_status_string", "pkv_version", "pkv_store_c8", "pkv_dequant",
            "pkv_decode_workspace_size", "pkv_decode_gqa", "pkv_decode_plan", "pkv_mla_store_c8",
            "pkv_mla_decode_workspace_size", "pkv_mla_decode_plan", "pkv_mla_decode", "pkv_decode_gqa_noalloc",
-           "pkv_store_decode_gqa", "pkv_cache_walk", "pkv_check_indices")
+           "pkv_store_decode_gqa", "pkv_cache_walk", "pkv_check_indices", "pkv_mla_store_decode")
 
 NOALLOC_SCRATCH_BYTES = 32 << 20  # PKV_NOALLOC_SCRATCH_BYTES
 
@@ -121,6 +121,8 @@ def lib():
         L.pkv_mla_decode_plan.restype = ctypes.c_int
         L.pkv_mla_decode.argtypes = [P, P, I32, P, P, I32, P, I32, ctypes.c_float, P, P, P, SZ, I32, P]
         L.pkv_mla_decode.restype = ctypes.c_int
+        L.pkv_mla_store_decode.argtypes = [P, P, P, P, I32, P, P, I32, P, I32, ctypes.c_float, P, P, P, SZ, I32, P]
+        L.pkv_mla_store_decode.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -593,4 +595,37 @@ def mla_decode(q_latent, q_rope, cache: MLACache, block_table, context_lengths, 
                               _ptr(context_lengths), batch, float(scale), _ptr(out), _ptr(lse_out),
                               _ptr(workspace), ws_bytes, int(split_tokens), _stream(stream))
     _check(st, "pkv_mla_decode")
+    return out
+
+
+def mla_store_decode(q_latent, q_rope, latent_new, rope_new, cache: MLACache, block_table, context_lengths, scale,
+                     *, out=None, lse_out=None, workspace=None, split_tokens=0, stream=None):
+    """One MLA decode step: store each sequence's new latent row (bf16 ``[B, 512]``) and rotary row
+    (bf16 ``[B, 64]``) at position ``context_lengths[b] - 1``, then attend with its query."""
+    _want(q_latent, "q_latent", torch.bfloat16, (None, None, cache.latent_dim))
+    batch, heads = int(q_latent.shape[0]), int(q_latent.shape[1])
+    _want(q_rope, "q_rope", torch.bfloat16, (batch, heads, cache.rope_dim))
+    _want(latent_new, "latent_new", torch.bfloat16, (batch, cache.latent_dim))
+    _want(rope_new, "rope_new", torch.bfloat16, (batch, cache.rope_dim))
+    _want(context_lengths, "context_lengths", torch.int32, (batch,))
+    _want(block_table, "block_table", torch.int32, (batch, None))
+    mbs = int(block_table.shape[1])
+    _want(out, "out", torch.bfloat16, (batch, heads, cache.latent_dim), optional=True)
+    _want(lse_out, "lse_out", torch.float32, (batch, heads), optional=True)
+    _want(workspace, "workspace", torch.uint8, ndim=1, optional=True)
+    _same_device(cache.latent, q_latent=q_latent, q_rope=q_rope, latent_new=latent_new, rope_new=rope_new,
+                 context_lengths=context_lengths, block_table=block_table, out=out, lse_out=lse_out,
+                 workspace=workspace)
+    need = mla_decode_workspace_size(batch, heads, mbs, cache.block_size, split_tokens)
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty_like(q_latent)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q_latent.device)  # no initial contents needed
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _debug_check(cache, "pkv_mla_store_decode", block_table=block_table, context_lengths=context_lengths)
+    st = lib().pkv_mla_store_decode(_ptr(q_latent), _ptr(q_rope), _ptr(latent_new), _ptr(rope_new), heads, cache.ref,
+                                    _ptr(block_table), mbs, _ptr(context_lengths), batch, float(scale), _ptr(out),
+                                    _ptr(lse_out), _ptr(workspace), ws_bytes, int(split_tokens), _stream(stream))
+    _check(st, "pkv_mla_store_decode")
     return out

@@ -89,14 +89,16 @@ __device__ __forceinline__ bool mla_row(const MlaArgs& a, int t, int64_t& row) {
     return true;
 }
 
-__global__ __launch_bounds__(256) void mla_store_kernel(MlaArgs a) {
+// Bytes a workgroup keeps of a token it stores for its own decode: latent codes [512], rotary
+// codes [64], the latent and rotary scales (fp32).
+constexpr int NT_BYTES = DC + DR + 8;
+
+// Quantize token t of latent_new / rope_new (one wave: latent channels 8 lane .., rotary channel
+// lane) into cache row `row`; with nt, also keep its codes and scales there (LDS).
+__device__ __forceinline__ void mla_quantize_token(const MlaArgs& a, int64_t t, int64_t row, uint8_t* nt) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
-    if (t >= a.num_tokens) return;  // uniform per wave
-    int64_t row;
-    if (!mla_row(a, t, row)) return;
     // latent row: channels 8 lane .. 8 lane + 7
-    const u32x4 w = load16(a.latent_new + (int64_t)t * DC + 8 * lane);
+    const u32x4 w = load16(a.latent_new + t * DC + 8 * lane);
     float x[8];
     float am = 0.0f;
 #pragma unroll
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(256) void mla_store_kernel(MlaArgs a) {
     }
     *reinterpret_cast<uint2*>(a.latent + row * DC + 8 * lane) = make_uint2(c0, c1);
     // rotary row: channel lane
-    const float xr = bf16_to_f32(a.rope_new[(int64_t)t * DR + lane]);
+    const float xr = bf16_to_f32(a.rope_new[t * DR + lane]);
     const float sr = absmax_scale(group_max<kWave>(fabsf(xr)));
     int cr;
     quant_row_absmax<1>(&xr, sr, &cr);
@@ -124,6 +126,22 @@ __global__ __launch_bounds__(256) void mla_store_kernel(MlaArgs a) {
         a.ls[row] = s;
         a.rs[row] = sr;
     }
+    if (nt) {
+        *reinterpret_cast<uint2*>(nt + 8 * lane) = make_uint2(c0, c1);
+        nt[DC + lane] = (uint8_t)cr;
+        if (lane == 0) {
+            reinterpret_cast<float*>(nt + DC + DR)[0] = s;
+            reinterpret_cast<float*>(nt + DC + DR)[1] = sr;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void mla_store_kernel(MlaArgs a) {
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= a.num_tokens) return;  // uniform per wave
+    int64_t row;
+    if (!mla_row(a, t, row)) return;
+    mla_quantize_token(a, t, row, nullptr);
 }
 
 // ------------------------------------------------------------------------------------ decode
@@ -196,6 +214,7 @@ struct __align__(16) MlaShared {
     int pg[NW][128];              // per wave: page ids of its keys in two 64-block chunks (ring)
     int plan[NW][2];              // balanced partition: per-wave partial sums
     int found[2];                 // balanced partition: the workgroup's sequence and its first slot
+    __align__(16) uint8_t nt[NT_BYTES];  // a decode step's new token, stored by this workgroup
 };
 
 // One wave's key registers for a block: A operand rows of the score MFMA (8 latent steps and
@@ -324,6 +343,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
             if ((int)threadIdx.x < nvalid && a.lse) a.lse[(int64_t)b * a.heads + h0 + threadIdx.x] = -INFINITY;
         }
         return;
+    }
+    // one decode step with its store (one head group per sequence): the workgroup whose keys end at
+    // the new token's position, ctx - 1, quantizes and writes the token and keeps its codes in LDS
+    // (its own loads of that slot may predate the write: the block holding it is patched below)
+    const int pos = a.fuse_store ? __builtin_amdgcn_readfirstlane(a.ctx[b]) - 1 : -1;
+    const bool own_new = pos >= __builtin_amdgcn_readfirstlane(t_begin) && pos < __builtin_amdgcn_readfirstlane(t_end);
+    if (own_new) {
+        if (w == 0) {
+            const int64_t row = (int64_t)a.bt[(int64_t)b * a.mbs + (pos >> a.log2bs)] * a.bs + (pos & (a.bs - 1));
+            mla_quantize_token(a, b, row, S.nt);
+        }
+        __syncthreads();
     }
 
     // ---- key loads of one block for this wave: key T + 16w + n (the lane's A row), channels
@@ -539,10 +570,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     // Every block issues the loads of the block after next, past the range's end too (in-bounds
     // stand-ins on its last page, which the cache holds): with a conditional issue the newest
     // loads could be any block's, and every wait would drain all of them.
+    // the block holding the stored token takes its codes and scales from LDS: wave wk's lanes of
+    // key row kn (all channel groups) and, for the scales, lane group gk's entry ik
+    auto patch_new = [&](const int T, MlaKRegs& R) {
+        const int kk = pos - T;
+        if (w != (kk >> 4)) return;  // (uniform per wave)
+        const bool krow = n == (kk & 15);
+#pragma unroll
+        for (int m = 0; m < DC / 64; ++m) {
+            const i4 v = *reinterpret_cast<const i4*>(S.nt + 64 * m + 16 * g);
+            R.k[m] = krow ? v : R.k[m];
+        }
+        const i4 vr = *reinterpret_cast<const i4*>(S.nt + DC + 16 * g);
+        R.k[DC / 64] = krow ? vr : R.k[DC / 64];
+        const float* ns = reinterpret_cast<const float*>(S.nt + DC + DR);
+        const float nls = ns[0], nrs = ns[1];
+        const bool sgrp = g == ((kk & 15) >> 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool hit = sgrp && i == (kk & 3);
+            R.ls[i] = hit ? nls : R.ls[i];
+            R.rs[i] = hit ? nrs : R.rs[i];
+        }
+    };
     for (int T = t_begin;;) {
+        if (own_new && pos >= T && pos < T + MBLK) patch_new(T, R0);
         block(true, T, R0);
         T += MBLK;
         if (T >= t_end) break;
+        if (own_new && pos >= T && pos < T + MBLK) patch_new(T, R1);
         block(true, T, R1);
         T += MBLK;
         if (T >= t_end) break;

@@ -116,6 +116,75 @@ int mla_plan(int32_t batch, int32_t heads, int32_t mbs, int32_t bs, int32_t spli
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 
+// The decode, and with latent_new / rope_new (bf16 [batch][512] / [batch][64]) one decode step: each
+// sequence's new token stored at position context_lengths[b] - 1 first.  With one head group per
+// sequence the decode launch stores it (the workgroup whose keys end there); otherwise a store
+// launch precedes the decode.
+int mla_decode_impl(const void* q_latent, const void* q_rope, const void* latent_new, const void* rope_new,
+                    int32_t num_heads, const pkv_mla_cache_t* cache, const int32_t* block_table,
+                    int32_t max_blocks_per_seq, const int32_t* context_lengths, int32_t batch, float scale,
+                    void* out, float* lse_out, void* workspace, size_t workspace_bytes, int32_t split_tokens,
+                    void* stream) {
+    int st = check_mla_cache(cache);
+    if (st != PKV_OK) return st;
+    if (!q_latent || !q_rope || !out || !block_table || !context_lengths) return PKV_ERR_INVALID_ARG;
+    if (!aligned(q_latent, 16) || !aligned(q_rope, 16) || !aligned(out, 16) || (lse_out && !aligned(lse_out, 4)))
+        return PKV_ERR_INVALID_ARG;
+    if (latent_new && (!aligned(latent_new, 16) || !aligned(rope_new, 2))) return PKV_ERR_INVALID_ARG;
+    MlaPlan p;
+    st = mla_plan(batch, num_heads, max_blocks_per_seq, cache->block_size, split_tokens, &p);
+    if (st != PKV_OK) return st;
+    if (batch == 0) return PKV_OK;
+    if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 16)))
+        return PKV_ERR_WORKSPACE;
+    pkv::MlaArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.latent = static_cast<int8_t*>(cache->latent);
+    a.rope = static_cast<int8_t*>(cache->rope);
+    a.ls = cache->latent_scale;
+    a.rs = cache->rope_scale;
+    a.ql = static_cast<const uint16_t*>(q_latent);
+    a.qr = static_cast<const uint16_t*>(q_rope);
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse_out;
+    a.bt = block_table;
+    a.ctx = context_lengths;
+    a.batch = batch;
+    a.heads = num_heads;
+    a.nhg = p.nhg;
+    a.bs = cache->block_size;
+    a.log2bs = ilog2(cache->block_size);
+    a.mbs = max_blocks_per_seq;
+    a.nsplit = p.nsplit;
+    a.split_len = p.split_len;
+    a.sk_wgs = p.sk_wgs;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    if (p.sk_wgs > 0) {
+        float* ws = static_cast<float*>(workspace);
+        const int64_t rows = ((int64_t)p.sk_wgs + (int64_t)batch * p.nhg) * pkv::kMlaHeads;
+        a.part_o = ws;
+        a.part_lse = ws + rows * pkv::kMlaLatent;
+        a.seg = reinterpret_cast<int*>(a.part_lse + rows);
+    } else if (p.nsplit > 1) {
+        float* ws = static_cast<float*>(workspace);
+        const int64_t rows = (int64_t)batch * p.nhg * p.nsplit * pkv::kMlaHeads;
+        a.part_o = ws;
+        a.part_lse = ws + rows * pkv::kMlaLatent;
+    }
+    if (latent_new) {
+        a.latent_new = static_cast<const uint16_t*>(latent_new);
+        a.rope_new = static_cast<const uint16_t*>(rope_new);
+        if (p.nhg == 1) {
+            a.fuse_store = 1;
+        } else {  // several head groups read the new key: store it first
+            a.num_tokens = batch;
+            const hipError_t e = pkv::launch_mla_store(a, static_cast<hipStream_t>(stream));
+            if (e != hipSuccess) return PKV_ERR_HIP;
+        }
+    }
+    return hip_status(pkv::launch_mla_decode(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -174,52 +243,20 @@ int pkv_mla_decode(const void* q_latent, const void* q_rope, int32_t num_heads, 
                    const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lengths,
                    int32_t batch, float scale, void* out, float* lse_out, void* workspace,
                    size_t workspace_bytes, int32_t split_tokens, void* stream) {
-    int st = check_mla_cache(cache);
-    if (st != PKV_OK) return st;
-    if (!q_latent || !q_rope || !out || !block_table || !context_lengths) return PKV_ERR_INVALID_ARG;
-    if (!aligned(q_latent, 16) || !aligned(q_rope, 16) || !aligned(out, 16) || (lse_out && !aligned(lse_out, 4)))
-        return PKV_ERR_INVALID_ARG;
-    MlaPlan p;
-    st = mla_plan(batch, num_heads, max_blocks_per_seq, cache->block_size, split_tokens, &p);
-    if (st != PKV_OK) return st;
-    if (batch == 0) return PKV_OK;
-    if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 16)))
-        return PKV_ERR_WORKSPACE;
-    pkv::MlaArgs a;
-    std::memset(&a, 0, sizeof a);
-    a.latent = static_cast<int8_t*>(cache->latent);
-    a.rope = static_cast<int8_t*>(cache->rope);
-    a.ls = cache->latent_scale;
-    a.rs = cache->rope_scale;
-    a.ql = static_cast<const uint16_t*>(q_latent);
-    a.qr = static_cast<const uint16_t*>(q_rope);
-    a.out = static_cast<uint16_t*>(out);
-    a.lse = lse_out;
-    a.bt = block_table;
-    a.ctx = context_lengths;
-    a.batch = batch;
-    a.heads = num_heads;
-    a.nhg = p.nhg;
-    a.bs = cache->block_size;
-    a.log2bs = ilog2(cache->block_size);
-    a.mbs = max_blocks_per_seq;
-    a.nsplit = p.nsplit;
-    a.split_len = p.split_len;
-    a.sk_wgs = p.sk_wgs;
-    a.scale_log2 = scale * 1.4426950408889634f;
-    if (p.sk_wgs > 0) {
-        float* ws = static_cast<float*>(workspace);
-        const int64_t rows = ((int64_t)p.sk_wgs + (int64_t)batch * p.nhg) * pkv::kMlaHeads;
-        a.part_o = ws;
-        a.part_lse = ws + rows * pkv::kMlaLatent;
-        a.seg = reinterpret_cast<int*>(a.part_lse + rows);
-    } else if (p.nsplit > 1) {
-        float* ws = static_cast<float*>(workspace);
-        const int64_t rows = (int64_t)batch * p.nhg * p.nsplit * pkv::kMlaHeads;
-        a.part_o = ws;
-        a.part_lse = ws + rows * pkv::kMlaLatent;
-    }
-    return hip_status(pkv::launch_mla_decode(a, static_cast<hipStream_t>(stream)));
+    return mla_decode_impl(q_latent, q_rope, nullptr, nullptr, num_heads, cache, block_table, max_blocks_per_seq,
+                           context_lengths, batch, scale, out, lse_out, workspace, workspace_bytes, split_tokens,
+                           stream);
+}
+
+int pkv_mla_store_decode(const void* q_latent, const void* q_rope, const void* latent_new, const void* rope_new,
+                         int32_t num_heads, const pkv_mla_cache_t* cache, const int32_t* block_table,
+                         int32_t max_blocks_per_seq, const int32_t* context_lengths, int32_t batch, float scale,
+                         void* out, float* lse_out, void* workspace, size_t workspace_bytes, int32_t split_tokens,
+                         void* stream) {
+    if (!latent_new || !rope_new) return PKV_ERR_INVALID_ARG;
+    return mla_decode_impl(q_latent, q_rope, latent_new, rope_new, num_heads, cache, block_table, max_blocks_per_seq,
+                           context_lengths, batch, scale, out, lse_out, workspace, workspace_bytes, split_tokens,
+                           stream);
 }
 
 }  // extern "C"

@@ -44,6 +44,7 @@ struct MlaArgs {
     int split_len;     // keys per split, a multiple of 64
     int sk_wgs;        // > 0: balanced partition over this many workgroups (split_len unused)
     float scale_log2;  // softmax scale * log2(e)
+    int fuse_store;    // decode: also store latent_new / rope_new row b at position ctx[b] - 1 (nhg == 1)
 };
 
 // Workgroups of the decode kernel one compute unit holds at once (0 if unknown).

@@ -4,7 +4,7 @@ records them as they are.  Each captured call is replayed several times with new
 between the replays (eager work, then a synchronisation), and every replay must equal, bit for
 bit, the same call made eagerly: the decode (fixed splits, the balanced partition, causal chunks,
 bf16 pages), the decode with no workspace (the entry point for callers that cannot allocate), and
-the one-call decode step whose store rewrites the cache on every replay."""
+the one-call decode steps (GQA and MLA) whose store rewrites the cache on every replay."""
 import numpy as np
 import pytest
 import torch
@@ -136,3 +136,43 @@ def test_captured_decode_step_replays_equal_eager(mode):
             if a is not None:
                 assert torch.equal(a.view(torch.uint8) if a.dtype != torch.float32 else a.view(torch.int32),
                                    b.view(torch.uint8) if b.dtype != torch.float32 else b.view(torch.int32)), (mode, i, name)
+
+
+def test_captured_mla_decode_step_replays_equal_eager():
+    """The MLA decode step (its store inside the decode launch), captured and replayed with new
+    tokens and queries, against the same step made eagerly on a second cache."""
+    w = gen.mla_workload("graph-mla", batch=4, num_heads=16, block_size=64, context_lengths=[1, 300, 1025, 4000],
+                         seed=8, softmax_scale=0.07)
+    t = gen.gen_mla_tensors(w, device="cuda")
+    bt = torch.as_tensor(w.block_table, device="cuda")
+    ctx = torch.as_tensor(w.context_lengths, device="cuda")
+    caches = [pkv.MLACache(w.num_blocks, w.block_size) for _ in range(2)]
+    prior = w.prior_lengths
+    cu = w.cu_context
+    rows = torch.as_tensor(np.concatenate([np.arange(cu[b], cu[b] + prior[b]) for b in range(w.batch)]), device="cuda")
+    cu_p = torch.as_tensor(np.concatenate([[0], np.cumsum(prior)]).astype(np.int32), device="cuda")
+    for c in caches:
+        pkv.mla_store_c8(c, t["latent_all"].index_select(0, rows), t["rope_all"].index_select(0, rows), cu_q_lens=cu_p,
+                         context_lengths=torch.as_tensor(prior.astype(np.int32), device="cuda"), block_table=bt)
+    shapes = [(4, 16, 512), (4, 16, 64), (4, 512), (4, 64)]
+    ins = [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+    out_g = torch.empty(shapes[0], dtype=torch.bfloat16, device="cuda")
+    need = pkv.mla_decode_workspace_size(4, 16, w.max_blocks_per_seq, w.block_size)
+    ws_g = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    step = lambda c, x, out, ws: pkv.mla_store_decode(x[0], x[1], x[2], x[3], c, bt, ctx, 0.07, out=out, workspace=ws)
+    step(caches[0], ins, out_g, ws_g)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(caches[0], ins, out_g, ws_g)
+    gq = torch.Generator(device="cuda").manual_seed(24)
+    for i in range(REPLAYS):
+        xs = [_bf16(s, gq) for s in shapes]
+        for dst, src in zip(ins, xs):
+            dst.copy_(src)
+        graph.replay()
+        out_e = step(caches[1], xs, torch.empty_like(out_g), torch.empty_like(ws_g))
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.view(torch.int16), out_e.view(torch.int16)), i
+        for name in ("latent", "rope", "latent_scale", "rope_scale"):
+            assert torch.equal(getattr(caches[0], name).view(torch.uint8), getattr(caches[1], name).view(torch.uint8)), (i, name)

@@ -295,3 +295,97 @@ def test_long_ranges_cross_page_id_chunks(bs):
         out, lse = r.decode(split_tokens=split)
         torch.cuda.synchronize()
         check_decode(r, out, lse, [0, 1])
+
+
+def _new_rows(w, t):
+    """The decode step's new latent and rotary rows, one per sequence (zero rows for empty ones)."""
+    cu_ctx = w.cu_context
+    rows = np.array([cu_ctx[b + 1] - 1 if w.context_lengths[b] > 0 else 0 for b in range(w.batch)], np.int64)
+    ri = torch.as_tensor(rows, device=DEV)
+    return t["latent_all"].index_select(0, ri).contiguous(), t["rope_all"].index_select(0, ri).contiguous()
+
+
+def _store_prior(r):
+    w, t = r.w, r.t
+    prior = w.prior_lengths
+    cu_ctx = w.cu_context
+    pri = np.concatenate([np.arange(cu_ctx[b], cu_ctx[b] + prior[b]) for b in range(w.batch)] + [[]]).astype(np.int64)
+    if len(pri):
+        pi = torch.as_tensor(pri, device=DEV)
+        cu_p = np.zeros(w.batch + 1, np.int32)
+        cu_p[1:] = np.cumsum(prior)
+        pkv.mla_store_c8(r.cache, t["latent_all"].index_select(0, pi), t["rope_all"].index_select(0, pi),
+                         cu_q_lens=torch.as_tensor(cu_p, device=DEV),
+                         context_lengths=torch.as_tensor(prior, device=DEV), block_table=r.bt)
+
+
+def _assert_same_cache(c1, c2):
+    for name in ("latent", "rope", "latent_scale", "rope_scale"):
+        a, b = getattr(c1, name), getattr(c2, name)
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
+
+
+STEP_CASES = [
+    # block size, heads, context lengths (new token at ctx - 1), split_tokens (0: the plan)
+    (16, 16, [37, 100, 1, 0, 64, 65, 130, 129], 0),    # balanced, stored inside the decode
+    (64, 16, [1, 63, 64, 65, 1000, 2049], 128),         # fixed splits, stored inside the decode
+    (128, 16, [2000, 5000, 64], 0),
+    (16, 32, [300, 17, 1], 0),                          # two head groups: a store launch first
+    (32, 8, [700, 5], 256),
+]
+
+
+@pytest.mark.parametrize("bs,heads,ctx,split", STEP_CASES)
+def test_store_decode_equals_store_then_decode(bs, heads, ctx, split):
+    """pkv_mla_store_decode against pkv_mla_store_c8 + pkv_mla_decode: the cache bytes, outputs
+    and lse bit for bit the same (inside the decode launch the workgroup whose keys end at the new
+    position quantizes the token itself and patches its codes into the block that holds it)."""
+    w = gen.mla_workload(f"mla-step-{bs}-{heads}", batch=len(ctx), num_heads=heads, block_size=bs,
+                         context_lengths=ctx, seed=bs + heads + len(ctx), softmax_scale=1.0 / np.sqrt(192.0))
+    fused, two = MlaRun(w), MlaRun(w)
+    two.t = fused.t
+    _store_prior(fused)
+    two.store()
+    lat, rot = _new_rows(w, fused.t)
+    lse_f = torch.full((w.batch, heads), 7.0, dtype=torch.float32, device=DEV)
+    out_f = pkv.mla_store_decode(fused.t["q_latent"], fused.t["q_rope"], lat, rot, fused.cache, fused.bt, fused.ctx,
+                                 w.softmax_scale, lse_out=lse_f, split_tokens=split)
+    out_t, lse_t = two.decode(split_tokens=split)
+    torch.cuda.synchronize()
+    _assert_same_cache(fused.cache, two.cache)
+    assert torch.equal(out_f.view(torch.int16), out_t.view(torch.int16))
+    assert torch.equal(lse_f.view(torch.int32), lse_t.view(torch.int32))
+
+
+def test_store_decode_repeated_steps():
+    """Several MLA decode steps in a row, each storing one more token per sequence (the new token of
+    one step is an ordinary cached key of the next), against the two-call path."""
+    ctx0 = np.array([100, 1023, 4000, 1, 64])
+    steps = 4
+    w = gen.mla_workload("mla-steps", batch=len(ctx0), num_heads=16, block_size=64,
+                         context_lengths=list(ctx0 + steps - 1), seed=17, softmax_scale=1.0 / np.sqrt(192.0))
+    t = gen.gen_mla_tensors(w, device=DEV)
+    bt = torch.as_tensor(w.block_table, device=DEV)
+    caches = [pkv.MLACache(w.num_blocks, w.block_size, device=DEV) for _ in range(2)]
+    cu = w.cu_context
+    rows = torch.as_tensor(np.concatenate([np.arange(cu[b], cu[b] + ctx0[b] - 1) for b in range(w.batch)]),
+                           device=DEV)
+    cu_p = torch.as_tensor(np.concatenate([[0], np.cumsum(ctx0 - 1)]).astype(np.int32), device=DEV)
+    for c in caches:
+        pkv.mla_store_c8(c, t["latent_all"].index_select(0, rows), t["rope_all"].index_select(0, rows),
+                         cu_q_lens=cu_p, context_lengths=torch.as_tensor((ctx0 - 1).astype(np.int32), device=DEV),
+                         block_table=bt)
+    gq = torch.Generator(device=DEV).manual_seed(19)
+    for step in range(steps):
+        ctx = torch.as_tensor((ctx0 + step).astype(np.int32), device=DEV)
+        new = torch.as_tensor(np.array([cu[b] + ctx0[b] - 1 + step for b in range(w.batch)]), device=DEV)
+        lat = t["latent_all"].index_select(0, new).contiguous()
+        rot = t["rope_all"].index_select(0, new).contiguous()
+        ql = torch.randn((w.batch, 16, 512), generator=gq, device=DEV).to(torch.bfloat16)
+        qr = torch.randn((w.batch, 16, 64), generator=gq, device=DEV).to(torch.bfloat16)
+        out_f = pkv.mla_store_decode(ql, qr, lat, rot, caches[0], bt, ctx, 0.07)
+        pkv.mla_store_c8(caches[1], lat, rot, context_lengths=ctx, block_table=bt)
+        out_t = pkv.mla_decode(ql, qr, caches[1], bt, ctx, 0.07)
+        torch.cuda.synchronize()
+        assert torch.equal(out_f.view(torch.int16), out_t.view(torch.int16)), step
+        _assert_same_cache(caches[0], caches[1])
