@@ -60,6 +60,7 @@ constexpr int LROW = DC + 16;    // LDS pitch of a latent row (bytes): rows star
 constexpr int CW = DC / NW;      // output channels per wave
 constexpr int NT = CW / 16;      // 16 x 16 output tiles per wave
 constexpr int QSTEPS = DC / 64 + DR / 64;  // 64-channel score steps: 8 latent + 1 rotary
+static_assert(DC / 8 == kWave, "the merge is one wave of 8 latent channels per lane");
 
 // ------------------------------------------------------------------------------------- store
 
@@ -213,7 +214,7 @@ struct __align__(16) MlaShared {
     i4 qlo[QSTEPS][kWave];
     int pg[NW][128];              // per wave: page ids of its keys in two 64-block chunks (ring)
     int plan[NW][2];              // balanced partition: per-wave partial sums
-    int found[2];                 // balanced partition: the workgroup's sequence and its first slot
+    int found[3];                 // balanced partition: the workgroup's sequence, its first slot and length
     __align__(16) uint8_t nt[NT_BYTES];  // a decode step's new token, stored by this workgroup
 };
 
@@ -244,18 +245,20 @@ __device__ __forceinline__ int wg_sum(int x, int (*red)[2], int slot) {
 // contiguous, near-equal segments (N blocks in all; Wp = W - A with A non-empty items, so that
 // the ceilings keep the total within W and the chip runs one round of equally long workgroups).
 // Segments are numbered sequence by sequence, head group by head group.  Workgroup u finds its
-// segment from the context lengths alone (two passes over them); false when u has none.
+// segment from the context lengths alone (two passes over them); false when u has none.  ctx: the
+// context length of the segment's sequence.
 __device__ bool mla_balanced_segment(const MlaArgs& a, int u, MlaShared& S, int& b, int& hg, int& t_begin,
-                                     int& t_end, int& kseg, int& first) {
+                                     int& t_end, int& kseg, int& first, int& ctx) {
     const int tid = threadIdx.x;
     const int W = a.sk_wgs;
     auto nblk = [&](int c) { return c > 0 ? (c + MBLK - 1) / MBLK : 0; };
-    int n0 = 0;  // blocks of sequence tid (first chunk), kept for the second pass
+    int c_first = 0;  // context length of sequence tid (first chunk), kept for the second pass
     int N = 0, A = 0;
     for (int c0 = 0; c0 < a.batch; c0 += NW * kWave) {
         const int bb = c0 + tid;
-        const int nb = bb < a.batch ? nblk(a.ctx[bb]) : 0;
-        if (c0 == 0) n0 = nb;
+        const int cb = bb < a.batch ? a.ctx[bb] : 0;
+        const int nb = nblk(cb);
+        if (c0 == 0) c_first = cb;
         N += wg_sum(nb, S.plan, 0);
         A += wg_sum(nb > 0 ? 1 : 0, S.plan, 1);
     }
@@ -267,7 +270,8 @@ __device__ bool mla_balanced_segment(const MlaArgs& a, int u, MlaShared& S, int&
     int carry = 0;
     for (int c0 = 0; c0 < a.batch; c0 += NW * kWave) {
         const int bb = c0 + tid;
-        const int nb = bb < a.batch ? (c0 == 0 ? n0 : nblk(a.ctx[bb])) : 0;
+        const int cb = bb < a.batch ? (c0 == 0 ? c_first : a.ctx[bb]) : 0;
+        const int nb = nblk(cb);
         const int k = segs(nb) * a.nhg;
         int x = k;  // inclusive scan over the wave, then over the waves
 #pragma unroll
@@ -288,6 +292,7 @@ __device__ bool mla_balanced_segment(const MlaArgs& a, int u, MlaShared& S, int&
         if (k > 0 && incl - k <= u && u < incl) {
             S.found[0] = bb;
             S.found[1] = incl - k;
+            S.found[2] = cb;
         }
         carry += tot;
         __syncthreads();
@@ -295,7 +300,7 @@ __device__ bool mla_balanced_segment(const MlaArgs& a, int u, MlaShared& S, int&
     if (u >= carry) return false;
     b = S.found[0];
     const int seq_first = S.found[1];
-    const int ctx = a.ctx[b];
+    ctx = S.found[2];
     const int nb = nblk(ctx);
     kseg = segs(nb);
     const int off = u - seq_first;
@@ -310,11 +315,11 @@ __device__ bool mla_balanced_segment(const MlaArgs& a, int u, MlaShared& S, int&
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mla_decode_kernel(MlaArgs a, int items) {
     __shared__ MlaShared S;
     const int u = blockIdx.x;
-    int b, hg, t_begin, t_end;
+    int b, hg, t_begin, t_end, ctx;
     int64_t pslot;  // partial slot of this workgroup's output, -1: the output itself
     if (a.sk_wgs > 0) {
         int kseg, first;
-        if (!mla_balanced_segment(a, u, S, b, hg, t_begin, t_end, kseg, first)) return;  // uniform
+        if (!mla_balanced_segment(a, u, S, b, hg, t_begin, t_end, kseg, first, ctx)) return;  // uniform
         if ((int)threadIdx.x == 0 && t_begin == 0) {  // the item's first segment records the item
             a.seg[2 * (b * a.nhg + hg)] = first;
             a.seg[2 * (b * a.nhg + hg) + 1] = kseg;
@@ -325,7 +330,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         const int sp = u / items;
         b = item / a.nhg;
         hg = item % a.nhg;
-        const int ctx = a.ctx[b];
+        ctx = a.ctx[b];
         t_begin = sp * a.split_len;
         t_end = a.nsplit == 1 ? ctx : min(ctx, t_begin + a.split_len);
         pslot = a.nsplit > 1 ? u : -1;
@@ -347,15 +352,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     // one decode step with its store (one head group per sequence): the workgroup whose keys end at
     // the new token's position, ctx - 1, quantizes and writes the token and keeps its codes in LDS
     // (its own loads of that slot may predate the write: the block holding it is patched below)
-    const int pos = a.fuse_store ? __builtin_amdgcn_readfirstlane(a.ctx[b]) - 1 : -1;
+    const int pos = a.fuse_store ? __builtin_amdgcn_readfirstlane(ctx) - 1 : -1;
     const bool own_new = pos >= __builtin_amdgcn_readfirstlane(t_begin) && pos < __builtin_amdgcn_readfirstlane(t_end);
-    if (own_new) {
-        if (w == 0) {
-            const int64_t row = (int64_t)a.bt[(int64_t)b * a.mbs + (pos >> a.log2bs)] * a.bs + (pos & (a.bs - 1));
-            mla_quantize_token(a, b, row, S.nt);
-        }
-        __syncthreads();
-    }
 
     // ---- key loads of one block for this wave: key T + 16w + n (the lane's A row), channels
     //      64m + 16g .. of the latent row for m < 8 and 16g .. of the rotary row; the lane's
@@ -366,14 +364,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     //      an LDS ring (entry j = block j mod 128), read with ds_read; chunk c + 1 is loaded at
     //      the start of chunk c and written to the ring half-way through it.  So no key load
     //      waits for a block-table round trip, and no wait in the key loop is for a page load.
+    //      Start-up: the first two chunks' page ids and the query rows are requested together, the
+    //      first block's keys as soon as the page ids are in, and the query is quantized while
+    //      those keys are on their way.  (The groups stay in this order, so that each wait
+    //      covers only its own group and the ones before it.)
     const int32_t* btb = a.bt + (int64_t)b * a.mbs;
     const int lastpg = (t_end - 1) >> a.log2bs;
     auto pages_of = [&](int c) {  // (keys past the range's end: its last page, in bounds)
         const int T = t_begin + MBLK * (64 * c + lane);
         return btb[min((T + 16 * w) >> a.log2bs, lastpg)];
     };
+    const int pv0 = pages_of(0);
     int pvn = pages_of(1);  // the next chunk's page ids, on their way to the ring
-    S.pg[w][lane] = pages_of(0);
+
+    // ---- query rows (B operand): lane (g, n) holds head h0 + n, channels 64m + 16g .. + 15 (lanes
+    //      of heads past the group's end read head h0's row and use zeros)
+    const bool hv = n < nvalid;
+    const int64_t qrow = (int64_t)b * a.heads + h0 + (hv ? n : 0);
+    u32x4 qraw[2 * QSTEPS];
+    __builtin_amdgcn_sched_barrier(0);
+    {
+        const uint16_t* qlp = a.ql + qrow * DC + 16 * g;
+        const uint16_t* qrp = a.qr + qrow * DR + 16 * g;
+#pragma unroll
+        for (int m = 0; m < DC / 64; ++m) {
+            qraw[2 * m] = load16(qlp + 64 * m);
+            qraw[2 * m + 1] = load16(qlp + 64 * m + 8);
+        }
+        qraw[2 * (QSTEPS - 1)] = load16(qrp);
+        qraw[2 * QSTEPS - 1] = load16(qrp + 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    S.pg[w][lane] = pv0;
     S.pg[w][64 + lane] = pvn;
     __builtin_amdgcn_wave_barrier();
     auto page_of = [&](int T) { return S.pg[w][((T - t_begin) / MBLK) & 127]; };
@@ -402,22 +424,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         load_s(t_begin, p0, R0);
     }
     const int p1 = page_of(t_begin + MBLK);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- query rows (B operand): lane (g, n) holds head h0 + n, channels 64m + 16g .. + 15
-    const bool hv = n < nvalid;
-    const int64_t qrow = (int64_t)b * a.heads + h0 + n;
-    u32x4 qraw[2 * QSTEPS];
-    {
-        const uint16_t* qlp = a.ql + qrow * DC + 16 * g;
-        const uint16_t* qrp = a.qr + qrow * DR + 16 * g;
+    if (!hv) {
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int m = 0; m < DC / 64; ++m) {
-            qraw[2 * m] = hv ? load16(qlp + 64 * m) : z;
-            qraw[2 * m + 1] = hv ? load16(qlp + 64 * m + 8) : z;
-        }
-        qraw[2 * (QSTEPS - 1)] = hv ? load16(qrp) : z;
-        qraw[2 * QSTEPS - 1] = hv ? load16(qrp + 8) : z;
+        for (int i = 0; i < 2 * QSTEPS; ++i) qraw[i] = z;
     }
     const float sgn = a.scale_log2 < 0.0f ? -1.0f : 1.0f;  // a negative scale flips the query
     i4 qhi[QSTEPS], qmd[QSTEPS], qlo[QSTEPS];
@@ -434,7 +446,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
             S.qlo[m][lane] = qlo[m];
         }
     }
-    __syncthreads();
+    // the new token, by wave 1 while the first block's keys are on their way
+    if (own_new && w == 1) {
+        const int64_t row = (int64_t)btb[pos >> a.log2bs] * a.bs + (pos & (a.bs - 1));
+        mla_quantize_token(a, b, row, S.nt);
+    }
+    __syncthreads();  // the quantized query and a stored token are visible
     // the second block's loads, after the raw query registers are free (unconditional: past the
     // range's end they read stand-ins on its last page)
     load_k(t_begin + MBLK, p1, R1);
@@ -609,10 +626,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     if (g == 0) S.lsum[w][n] = lsum;
     __syncthreads();
     const float L = S.lsum[0][n] + S.lsum[1][n] + S.lsum[2][n] + S.lsum[3][n];
-    const float mul = L > 0.0f ? sref / L : 0.0f;
+    const bool split_mode = pslot >= 0;
+    // the output (bf16), or a partial in latent-code units (fp16: every latent scale of the range
+    // is within 16x sref, so |partial| <= 127 * 16) whose scale sref the merge applies
+    const float mul = L > 0.0f ? (split_mode ? 1.0f : sref) / L : 0.0f;
     const float bias = 1152.0f * pacc[0];
     if (!hv) return;
-    const bool split_mode = pslot >= 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float o[NT];
@@ -627,9 +646,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
             pk.w = f32_to_bf16_rne(o[6]) | (f32_to_bf16_rne(o[7]) << 16);
             *reinterpret_cast<uint4*>(a.out + qrow * DC + ch) = pk;
         } else {
-            float* po = a.part_o + (pslot * 16 + n) * DC + ch;
-            *reinterpret_cast<f4*>(po) = f4{o[0], o[1], o[2], o[3]};
-            *reinterpret_cast<f4*>(po + 4) = f4{o[4], o[5], o[6], o[7]};
+            h8 ph;
+#pragma unroll
+            for (int j = 0; j < NT; ++j) ph[j] = (_Float16)o[j];
+            *reinterpret_cast<h8*>(a.part_o + (pslot * 16 + n) * DC + ch) = ph;
         }
     }
     if (w == 0 && g == 0) {
@@ -637,52 +657,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         if (!split_mode) {
             if (a.lse) a.lse[qrow] = lse2 * kLn2;
         } else {
-            a.part_lse[pslot * 16 + n] = lse2;
+            *reinterpret_cast<float2*>(a.part_lse + 2 * (pslot * 16 + n)) = make_float2(lse2, sref);
         }
     }
 }
 
-// Log-sum-exp merge of the partials of one (sequence, head): 128 threads, 4 channels each; the
+// Log-sum-exp merge of the partials of one (sequence, head): one wave, 8 channels per lane; the
 // partials are read eight at a time.  Fixed splits: split s of item i in slot s * items + i;
 // balanced partition: the item's segments in slots seg[2i] .. seg[2i] + seg[2i + 1] - 1 (a
 // one-segment item is already written).  A sequence with no key gets a zero row and lse -inf.
-__global__ __launch_bounds__(128) void mla_merge_kernel(MlaArgs a, int items) {
+__global__ __launch_bounds__(kWave) void mla_merge_kernel(MlaArgs a, int items) {
     const int b = blockIdx.x / a.heads;
     const int h = blockIdx.x % a.heads;
     const int item = b * a.nhg + h / 16;
     const int row = h % 16;
+    // the context length and the item's slot range are requested together (the range is stale
+    // for an item with no key, and then not used)
     const int ctx = a.ctx[b];
+    const int2 range = a.sk_wgs > 0 ? *reinterpret_cast<const int2*>(a.seg + 2 * item) : make_int2(0, 0);
     int nact, first = 0;
     int64_t stride;
     if (ctx <= 0) {
         nact = 0;
         stride = 0;
     } else if (a.sk_wgs > 0) {
-        nact = a.seg[2 * item + 1];
+        nact = range.y;
         if (nact <= 1) return;
-        first = a.seg[2 * item];
+        first = range.x;
         stride = 1;
     } else {
         nact = min(a.nsplit, (ctx + a.split_len - 1) / a.split_len);
         first = item;
         stride = items;
     }
-    const int c = 4 * threadIdx.x;
+    const int c = 8 * threadIdx.x;
     constexpr int CH = 8;
     float M = -INFINITY, wsum = 0.0f;
-    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+    f4 acc0 = f4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
     for (int s0 = 0; s0 < nact; s0 += CH) {
-        float l2[CH];
-        f4 po[CH];
+        float l2[CH], sr[CH];
+        h8 po[CH];
 #pragma unroll
         for (int q = 0; q < CH; ++q) {
             if (s0 + q < nact) {
                 const int64_t pr = (first + (int64_t)(s0 + q) * stride) * 16 + row;
-                l2[q] = a.part_lse[pr];
-                po[q] = *reinterpret_cast<const f4*>(a.part_o + pr * DC + c);
+                const float2 ls = *reinterpret_cast<const float2*>(a.part_lse + 2 * pr);
+                l2[q] = ls.x;
+                sr[q] = ls.y;
+                po[q] = *reinterpret_cast<const h8*>(a.part_o + pr * DC + c);
             } else {
                 l2[q] = -INFINITY;
-                po[q] = f4{0.f, 0.f, 0.f, 0.f};
+                sr[q] = 0.0f;
+                po[q] = h8{};
             }
         }
         float mc = M;
@@ -692,19 +718,24 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(MlaArgs a, int items) {
         const float sc = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - mc);
         M = mc;
         wsum *= sc;
-        acc *= sc;
+        acc0 *= sc;
+        acc1 *= sc;
 #pragma unroll
         for (int q = 0; q < CH; ++q) {
             const float wt = l2[q] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(l2[q] - M);
+            const float ws = wt * sr[q];
             wsum += wt;
-            acc += wt * po[q];
+            acc0 += ws * f4{(float)po[q][0], (float)po[q][1], (float)po[q][2], (float)po[q][3]};
+            acc1 += ws * f4{(float)po[q][4], (float)po[q][5], (float)po[q][6], (float)po[q][7]};
         }
     }
     const float mul = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-    uint2 pk;
-    pk.x = f32_to_bf16_rne(acc[0] * mul) | (f32_to_bf16_rne(acc[1] * mul) << 16);
-    pk.y = f32_to_bf16_rne(acc[2] * mul) | (f32_to_bf16_rne(acc[3] * mul) << 16);
-    *reinterpret_cast<uint2*>(a.out + ((int64_t)b * a.heads + h) * DC + c) = pk;
+    uint4 pk;
+    pk.x = f32_to_bf16_rne(acc0[0] * mul) | (f32_to_bf16_rne(acc0[1] * mul) << 16);
+    pk.y = f32_to_bf16_rne(acc0[2] * mul) | (f32_to_bf16_rne(acc0[3] * mul) << 16);
+    pk.z = f32_to_bf16_rne(acc1[0] * mul) | (f32_to_bf16_rne(acc1[1] * mul) << 16);
+    pk.w = f32_to_bf16_rne(acc1[2] * mul) | (f32_to_bf16_rne(acc1[3] * mul) << 16);
+    *reinterpret_cast<uint4*>(a.out + ((int64_t)b * a.heads + h) * DC + c) = pk;
     if (threadIdx.x == 0 && a.lse)
         a.lse[(int64_t)b * a.heads + h] = wsum > 0.0f ? (M + log2f(wsum)) * kLn2 : -INFINITY;
 }
@@ -727,7 +758,7 @@ hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(mla_decode_kernel, dim3((unsigned)units), dim3(NW * kWave), 0, stream, a, (int)items);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || (a.sk_wgs == 0 && a.nsplit == 1)) return e;
-    hipLaunchKernelGGL(mla_merge_kernel, dim3((unsigned)(a.batch * a.heads)), dim3(DC / 4), 0, stream, a,
+    hipLaunchKernelGGL(mla_merge_kernel, dim3((unsigned)(a.batch * a.heads)), dim3(DC / 8), 0, stream, a,
                        (int)items);
     return hipGetLastError();
 }

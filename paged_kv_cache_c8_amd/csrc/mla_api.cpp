@@ -62,6 +62,9 @@ int check_mla_cache(const pkv_mla_cache_t* c) {
 
 constexpr int64_t kMlaBlock = 64;        // keys per block of the decode kernel
 constexpr int64_t kMaxSplits = 1 << 16;  // key splits per (sequence, head group)
+// workspace bytes per partial row (one head of one split): 512 fp16 channels, then (after all
+// rows) its log-sum-exp and latent scale
+constexpr size_t kPartRowBytes = pkv::kMlaLatent * 2 + 2 * 4;
 
 struct MlaPlan {
     int nhg;
@@ -89,7 +92,7 @@ int mla_plan(int32_t batch, int32_t heads, int32_t mbs, int32_t bs, int32_t spli
             p->split_len = 0;
             p->nsplit = (int)W;
             const size_t slots = (size_t)(W + items);
-            p->ws_bytes = slots * pkv::kMlaHeads * (pkv::kMlaLatent + 1) * 4 + (size_t)items * 2 * 4;
+            p->ws_bytes = slots * pkv::kMlaHeads * kPartRowBytes + (size_t)items * 2 * 4;
             return PKV_OK;
         }
     }
@@ -98,8 +101,8 @@ int mla_plan(int32_t batch, int32_t heads, int32_t mbs, int32_t bs, int32_t spli
         L = cdiv(split_tokens, kMlaBlock) * kMlaBlock;
     } else {
         // about four workgroups per compute unit counting every (possibly empty) split, with
-        // splits of 256 .. 8192 keys: a split's partial output (16 heads x 512 fp32) costs as
-        // much HBM traffic as ~56 of its keys, so splits stay long
+        // splits of 256 .. 8192 keys: a split's partial output (16 heads x 512 fp16, written and
+        // read back) costs as much HBM traffic as ~56 of its keys, so splits stay long
         const int64_t target = 4LL * device_cus();
         const int64_t want = items > 0 ? cdiv(target, items) : 1;
         L = cdiv(cdiv(max_ctx, want), kMlaBlock) * kMlaBlock;
@@ -110,7 +113,7 @@ int mla_plan(int32_t batch, int32_t heads, int32_t mbs, int32_t bs, int32_t spli
     if (cdiv(max_ctx, L) > kMaxSplits) return PKV_ERR_UNSUPPORTED;
     p->split_len = (int)L;
     p->nsplit = (int)cdiv(max_ctx, L);
-    p->ws_bytes = p->nsplit > 1 ? (size_t)(items * p->nsplit) * pkv::kMlaHeads * (pkv::kMlaLatent + 1) * 4 : 0;
+    p->ws_bytes = p->nsplit > 1 ? (size_t)(items * p->nsplit) * pkv::kMlaHeads * kPartRowBytes : 0;
     return PKV_OK;
 }
 
@@ -160,16 +163,16 @@ int mla_decode_impl(const void* q_latent, const void* q_rope, const void* latent
     a.sk_wgs = p.sk_wgs;
     a.scale_log2 = scale * 1.4426950408889634f;
     if (p.sk_wgs > 0) {
-        float* ws = static_cast<float*>(workspace);
+        uint16_t* ws = static_cast<uint16_t*>(workspace);
         const int64_t rows = ((int64_t)p.sk_wgs + (int64_t)batch * p.nhg) * pkv::kMlaHeads;
         a.part_o = ws;
-        a.part_lse = ws + rows * pkv::kMlaLatent;
-        a.seg = reinterpret_cast<int*>(a.part_lse + rows);
+        a.part_lse = reinterpret_cast<float*>(ws + rows * pkv::kMlaLatent);
+        a.seg = reinterpret_cast<int*>(a.part_lse + 2 * rows);
     } else if (p.nsplit > 1) {
-        float* ws = static_cast<float*>(workspace);
+        uint16_t* ws = static_cast<uint16_t*>(workspace);
         const int64_t rows = (int64_t)batch * p.nhg * p.nsplit * pkv::kMlaHeads;
         a.part_o = ws;
-        a.part_lse = ws + rows * pkv::kMlaLatent;
+        a.part_lse = reinterpret_cast<float*>(ws + rows * pkv::kMlaLatent);
     }
     if (latent_new) {
         a.latent_new = static_cast<const uint16_t*>(latent_new);

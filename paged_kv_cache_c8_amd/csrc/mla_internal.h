@@ -28,8 +28,9 @@ struct MlaArgs {
     const uint16_t* qr;  // bf16 [B][H][64]
     uint16_t* out;       // bf16 [B][H][512]
     float* lse;          // [B][H] or null
-    float* part_o;       // fixed splits: [nsplit][items][16][512]; balanced: [slots][16][512]
-    float* part_lse;     // the same rows' base-2 log-sum-exp
+    uint16_t* part_o;    // fp16, in latent-code units: fixed splits [nsplit][items][16][512];
+                         // balanced: [slots][16][512]
+    float* part_lse;     // per row of part_o: its base-2 log-sum-exp and its latent scale
     int* seg;            // balanced partition: per item, its first partial slot and segment count
     // both
     const int32_t* bt;

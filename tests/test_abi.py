@@ -153,7 +153,8 @@ def test_mla_plan_and_argument_checks(pkv):
     assert pkv.mla_decode_plan(64, 16, 128, 64, split_tokens=1000) == {"split_tokens": 1024, "num_splits": 8}
     assert pkv.mla_decode_plan(2, 16, 7, 16, split_tokens=100000)["num_splits"] == 1
     ws = pkv.mla_decode_workspace_size(64, 16, 128, 64, split_tokens=1024)
-    assert ws == 64 * 8 * 16 * 513 * 4  # partials: (sequence, split) x 16 heads x (512 channels + lse)
+    # partials: (sequence, split) x 16 heads x (512 fp16 channels + fp32 lse and latent scale)
+    assert ws == 64 * 8 * 16 * (512 * 2 + 2 * 4)
     assert pkv.mla_decode_workspace_size(64, 17, 128, 64, split_tokens=1024) == 2 * ws  # 2 head groups
     assert pkv.mla_decode_workspace_size(2, 16, 7, 16, split_tokens=100000) == 0
     c = pkv._MLACacheT(16, 32, 64, 128, 4, 16, 512, 64)
