@@ -169,7 +169,10 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     if args.mla >= 0:
-        main_mla(args)
+        if args.op == "walk":
+            main_mla_walk(args)
+        else:
+            main_mla(args)
         return
     if args.op == "walk":
         main_walk(args)
@@ -711,6 +714,70 @@ def main_mla(args):
             "algorithmic_bytes_per_launch": call_bytes, "avg_launch_ms": round(dec_ms, 5),
         },
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def main_mla_walk(args):
+    """The MLA decode's cache reads alone (pkv_mla_cache_walk): the latent and rotary rows and scales
+    of every key, with the decode's lane layout and two blocks in flight per wave, nothing computed;
+    one workgroup per split of --split-tokens keys (default: the decode's keys per workgroup, about
+    the number of workgroups its balanced partition runs).  Its rate is the read ceiling of the MLA
+    decode's access pattern."""
+    import torch
+
+    import gen
+    import paged_kv_cache_c8_amd as pkv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = gen.make_mla_config(args.mla)
+    t = gen.gen_mla_tensors(w, device=dev)
+    bt = torch.as_tensor(w.block_table, device=dev)
+    ctx = torch.as_tensor(w.context_lengths, device=dev)
+    cu = torch.as_tensor(np.asarray(w.cu_context, np.int32), device=dev)
+    read_b = int(w.context_lengths.sum()) * (w.latent_dim + w.rope_dim + 8)
+    reps = args.replicas or min(MAX_REPLICAS, max(1, int(np.ceil(3 * MALL_BYTES / read_b))))
+    caches = []
+    for _ in range(reps):
+        c = pkv.MLACache(w.num_blocks, w.block_size, device=dev)
+        pkv.mla_store_c8(c, t["latent_all"], t["rope_all"], cu_q_lens=cu, context_lengths=ctx, block_table=bt)
+        caches.append(c)
+    del t
+    split = args.split_tokens
+    if split <= 0:
+        plan = pkv.mla_decode_plan(w.batch, w.num_heads, w.max_blocks_per_seq, w.block_size)
+        blocks = int(sum(-(-int(c) // 64) for c in w.context_lengths))
+        wgs = plan["num_splits"] if plan["split_tokens"] == 0 else 512
+        split = min(4096, 64 * -(-blocks // max(wgs, 1)))
+    nsplit = -(-w.max_blocks_per_seq * w.block_size // split)
+    outs = [torch.empty((w.batch, nsplit), dtype=torch.int32, device=dev) for _ in range(reps)]
+
+    def launch(i):
+        pkv.mla_cache_walk(caches[i % reps], bt, ctx, split, out=outs[i % reps])
+    for i in range(max(args.warmup, 2)):
+        launch(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    steps = max(args.steps, 5)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(stream)
+        launch(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    times = [a.elapsed_time(b) for a, b in evs]
+    ms = float(np.median(times))
+    achieved = read_b / (ms * 1e-3) / 1e9
+    workgroups = int(sum(-(-int(c) // split) for c in w.context_lengths))
+    res = {
+        "op": "walk", "workload": w.name, "split_tokens": split, "workgroups": workgroups,
+        "cache_replicas": reps, "bytes_read": read_b, "ms_median": round(ms, 5),
+        "ms_mean": round(float(np.mean(times)), 5), "launches": steps,
+        "roofline": {"bound": "hbm", "kernel": "pkv_mla_cache_walk (the MLA decode's cache reads only)",
+                     "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_launch": read_b,
+                     "avg_launch_ms": round(ms, 5)},
     }
     print(json.dumps(res), flush=True)
 

@@ -469,6 +469,25 @@ int pkv_mla_store_decode(const void *q_latent, const void *q_rope, const void *l
                          float *lse_out, void *workspace, size_t workspace_bytes,
                          int32_t split_tokens, void *stream);
 
+/*
+ * pkv_mla_cache_walk - a measurement aid: the read ceiling of the MLA decode's
+ * access pattern over this cache (not an operation of the pages).
+ *
+ * One workgroup of four waves per (sequence b, split s of split_tokens keys),
+ * the splits of one sequence launched consecutively, reads what the decode of
+ * keys [s * split_tokens, min((s + 1) * split_tokens, context_lengths[b]))
+ * reads from the cache - their latent and rotary rows and their two scales,
+ * with the decode's lane layout and two 64-key blocks in flight per wave - and
+ * computes nothing else.  out[b * nsplit + s] receives the wrapping uint32 sum
+ * of the 32-bit words of those keys' rows and scales (0 for a split past the
+ * context), nsplit = ceil(max_blocks_per_seq * block_size / split_tokens); out
+ * holds batch * nsplit entries (device, 4-byte aligned).  split_tokens: a
+ * multiple of 64 in [64, 4096].  Errors as pkv_mla_store_c8.
+ */
+int pkv_mla_cache_walk(const pkv_mla_cache_t *cache, const int32_t *block_table,
+                       int32_t max_blocks_per_seq, const int32_t *context_lengths, int32_t batch,
+                       int32_t split_tokens, uint32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

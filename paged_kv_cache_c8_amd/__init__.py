@@ -29,7 +29,7 @@ import torch  # loaded first: libpkv binds to the HIP runtime torch has already 
 __all__ = ["PkvError", "PkvIndexError", "check_indices", "CHECK_CONTEXT", "CHECK_BLOCK", "CHECK_QLEN",
            "CHECK_SLOT", "Cache", "lib", "store_c8", "dequant", "decode_gqa", "decode_gqa_noalloc", "store_decode_gqa", "cache_walk",
            "decode_workspace_size", "NOALLOC_SCRATCH_BYTES",
-           "decode_plan", "MLACache", "mla_store_c8", "mla_decode", "mla_store_decode", "mla_decode_workspace_size",
+           "decode_plan", "MLACache", "mla_store_c8", "mla_decode", "mla_store_decode", "mla_decode_workspace_size", "mla_cache_walk",
            "mla_decode_plan", "QUANT_PER_TOKEN", "QUANT_PER_BLOCK", "QUANT_NONE_BF16", "QUANT_PER_CHANNEL",
            "EXPORTS"]
 
@@ -45,7 +45,8 @@ QUANT_PER_CHANNEL = 3
 EXPORTS = ("pkv_status_string", "pkv_version", "pkv_store_c8", "pkv_dequant",
            "pkv_decode_workspace_size", "pkv_decode_gqa", "pkv_decode_plan", "pkv_mla_store_c8",
            "pkv_mla_decode_workspace_size", "pkv_mla_decode_plan", "pkv_mla_decode", "pkv_decode_gqa_noalloc",
-           "pkv_store_decode_gqa", "pkv_cache_walk", "pkv_check_indices", "pkv_mla_store_decode")
+           "pkv_store_decode_gqa", "pkv_cache_walk", "pkv_check_indices", "pkv_mla_store_decode",
+           "pkv_mla_cache_walk")
 
 NOALLOC_SCRATCH_BYTES = 32 << 20  # PKV_NOALLOC_SCRATCH_BYTES
 
@@ -123,6 +124,8 @@ def lib():
         L.pkv_mla_decode.restype = ctypes.c_int
         L.pkv_mla_store_decode.argtypes = [P, P, P, P, I32, P, P, I32, P, I32, ctypes.c_float, P, P, P, SZ, I32, P]
         L.pkv_mla_store_decode.restype = ctypes.c_int
+        L.pkv_mla_cache_walk.argtypes = [P, P, I32, P, I32, I32, P, P]
+        L.pkv_mla_cache_walk.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -553,6 +556,27 @@ def mla_store_c8(cache: MLACache, latent_new, rope_new, *, slot_mapping=None, cu
                                 _ptr(cu_q_lens), _ptr(context_lengths), _ptr(block_table), batch, mbs,
                                 _stream(stream))
     _check(st, "pkv_mla_store_c8")
+
+
+def mla_cache_walk(cache: MLACache, block_table, context_lengths, split_tokens, *, out=None, stream=None):
+    """Read what the MLA decode of these sequences reads from the latent cache, ``split_tokens`` keys
+    per workgroup, and nothing more (a read-ceiling measurement).  Returns the per-workgroup word
+    sums, uint32 bit patterns in an int32 tensor ``[batch, nsplit]``."""
+    _want(context_lengths, "context_lengths", torch.int32, ndim=1)
+    batch = int(context_lengths.shape[0])
+    _want(block_table, "block_table", torch.int32, (batch, None))
+    mbs = int(block_table.shape[1])
+    nsplit = -(-mbs * cache.block_size // int(split_tokens)) if split_tokens > 0 else 0
+    _want(out, "out", torch.int32, (batch, nsplit), optional=True)
+    _same_device(cache.latent, block_table=block_table, context_lengths=context_lengths, out=out)
+    if out is None:
+        with _on_stream(stream):
+            out = torch.empty((batch, max(nsplit, 1)), dtype=torch.int32, device=cache.latent.device)
+    _debug_check(cache, "pkv_mla_cache_walk", block_table=block_table, context_lengths=context_lengths)
+    st = lib().pkv_mla_cache_walk(cache.ref, _ptr(block_table), mbs, _ptr(context_lengths), batch,
+                                  int(split_tokens), _ptr(out), _stream(stream))
+    _check(st, "pkv_mla_cache_walk")
+    return out
 
 
 def mla_decode_workspace_size(batch, num_heads, max_blocks_per_seq, block_size, split_tokens=0) -> int:

@@ -262,4 +262,30 @@ int pkv_mla_store_decode(const void* q_latent, const void* q_rope, const void* l
                            stream);
 }
 
+int pkv_mla_cache_walk(const pkv_mla_cache_t* cache, const int32_t* block_table, int32_t max_blocks_per_seq,
+                       const int32_t* context_lengths, int32_t batch, int32_t split_tokens, uint32_t* out,
+                       void* stream) {
+    int st = check_mla_cache(cache);
+    if (st != PKV_OK) return st;
+    if (!block_table || !context_lengths || !out || batch < 0 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID_ARG;
+    if (split_tokens < 64 || split_tokens > 4096 || split_tokens % 64 != 0 || !aligned(out, 4))
+        return PKV_ERR_INVALID_ARG;
+    if (batch == 0) return PKV_OK;
+    pkv::MlaWalkArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.latent = static_cast<const int8_t*>(cache->latent);
+    a.rope = static_cast<const int8_t*>(cache->rope);
+    a.ls = cache->latent_scale;
+    a.rs = cache->rope_scale;
+    a.bt = block_table;
+    a.ctx = context_lengths;
+    a.out = out;
+    a.bs = cache->block_size;
+    a.log2bs = ilog2(cache->block_size);
+    a.mbs = max_blocks_per_seq;
+    a.split_len = split_tokens;
+    a.nsplit = (int)cdiv((int64_t)max_blocks_per_seq * cache->block_size, split_tokens);
+    return hip_status(pkv::launch_mla_walk(a, batch, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -48,10 +48,29 @@ struct MlaArgs {
     int fuse_store;    // decode: also store latent_new / rope_new row b at position ctx[b] - 1 (nhg == 1)
 };
 
+// The MLA decode's cache reads alone (pkv_mla_cache_walk): one workgroup of four waves per
+// (sequence, split of split_len keys); out[b * nsplit + s] gets the wrapping sum of the 32-bit
+// words of the keys' latent rows, rotary rows and scales.
+struct MlaWalkArgs {
+    const int8_t* latent;
+    const int8_t* rope;
+    const float* ls;
+    const float* rs;
+    const int32_t* bt;
+    const int32_t* ctx;
+    uint32_t* out;
+    int bs;
+    int log2bs;
+    int mbs;
+    int split_len;  // a multiple of 64, at most 4096
+    int nsplit;
+};
+
 // Workgroups of the decode kernel one compute unit holds at once (0 if unknown).
 int mla_decode_wgs_per_cu();
 
 hipError_t launch_mla_store(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);
+hipError_t launch_mla_walk(const MlaWalkArgs& a, int batch, hipStream_t stream);
 
 }  // namespace pkv

@@ -11,6 +11,7 @@
 // are in flight while one is summed (the decode keeps one).  The sum of the 32-bit words a wave
 // read (wrapping) is its checksum, out[(b * hkv + h) * nsplit + s]; keys past the context are not
 // read, except for the rest of a V tile that starts inside it (the decode reads whole tiles).
+#include "mla_internal.h"
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -141,7 +142,90 @@ hipError_t launch_d(const WalkArgs& a, int pairs, int depth, hipStream_t stream)
     return hipGetLastError();
 }
 
+// The MLA decode's reads (latent cache): one workgroup of four waves per (sequence b, split s),
+// launched with the splits of one sequence consecutive, as the decode numbers its segments.  Wave
+// w reads keys T + 16w .. T + 16w + 15 of each 64-key block with the decode's lane layout: lane
+// (g, n) the 16-byte pieces 64m + 16g of key n's latent row (m < 8) and piece 16g of its rotary
+// row, and the latent and rotary scales of keys 16w + 4g .. + 3.  Two blocks in flight per wave,
+// the loads of block k + 2 issued once block k is summed (past the range's end they read the
+// range's last key again); only keys inside the range are summed.
+constexpr int MW_WAVES = 4;
+constexpr int MW_BLK = 16 * MW_WAVES;
+
+struct MlaWalkBuf {
+    u32x4 k[kMlaLatent / 64 + 1];
+    float4 ls, rs;
+};
+
+__global__ __launch_bounds__(MW_WAVES * kWave) void mla_walk_kernel(MlaWalkArgs a, int units) {
+    __shared__ int bt_s[MAX_SPLIT / 16 + 1];
+    __shared__ uint32_t red[MW_WAVES];
+    const int u = blockIdx.x;
+    if (u >= units) return;
+    const int b = u / a.nsplit, s = u % a.nsplit;
+    const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int n = lane & 15, g = lane >> 4;
+    const int ctx = __builtin_amdgcn_readfirstlane(a.ctx[b]);
+    const int t0 = s * a.split_len;
+    uint32_t acc = 0;
+    if (t0 < ctx) {  // uniform per workgroup
+        const int t1 = min(t0 + a.split_len, ctx);
+        const int blk0 = t0 >> a.log2bs;
+        const int nblk = ((t1 - 1) >> a.log2bs) - blk0 + 1;
+        for (int i = threadIdx.x; i < nblk; i += blockDim.x) bt_s[i] = a.bt[(int64_t)b * a.mbs + blk0 + i];
+        __syncthreads();
+        auto row_of = [&](int t) {  // cache row of key t (past the range: its last key)
+            const int tt = min(t, t1 - 1);
+            return (int64_t)bt_s[(tt >> a.log2bs) - blk0] * a.bs + (tt & (a.bs - 1));
+        };
+        auto load = [&](int T, MlaWalkBuf& R) {
+            const int64_t row = row_of(T + 16 * w + n);
+            const uint8_t* lp = reinterpret_cast<const uint8_t*>(a.latent) + row * kMlaLatent + 16 * g;
+#pragma unroll
+            for (int m = 0; m < kMlaLatent / 64; ++m) R.k[m] = load16(lp + 64 * m);
+            R.k[kMlaLatent / 64] = load16(reinterpret_cast<const uint8_t*>(a.rope) + row * kMlaRope + 16 * g);
+            // the four scales of keys 16w + 4g .. share one 4-aligned group of a page's rows
+            const int64_t srow = row_of(T + 16 * w + 4 * g) & ~(int64_t)3;
+            R.ls = *reinterpret_cast<const float4*>(a.ls + srow);
+            R.rs = *reinterpret_cast<const float4*>(a.rs + srow);
+        };
+        auto sum = [&](int T, const MlaWalkBuf& R) {
+            if (T + 16 * w + n < t1) {
+#pragma unroll
+                for (int m = 0; m <= kMlaLatent / 64; ++m) acc += sum4(R.k[m]);
+            }
+            const int tk = T + 16 * w + 4 * g;
+            const float el[4] = {R.ls.x, R.ls.y, R.ls.z, R.ls.w};
+            const float er[4] = {R.rs.x, R.rs.y, R.rs.z, R.rs.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (n == 0 && tk + i < t1) acc += __float_as_uint(el[i]) + __float_as_uint(er[i]);
+        };
+        MlaWalkBuf R0, R1;
+        load(t0, R0);
+        load(t0 + MW_BLK, R1);
+        for (int T = t0; T < t1; T += 2 * MW_BLK) {
+            sum(T, R0);
+            load(T + 2 * MW_BLK, R0);
+            if (T + MW_BLK < t1) sum(T + MW_BLK, R1);
+            load(T + 3 * MW_BLK, R1);
+        }
+    }
+    for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d, kWave);
+    if (lane == 0) red[w] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) a.out[u] = red[0] + red[1] + red[2] + red[3];
+}
+
 }  // namespace
+
+hipError_t launch_mla_walk(const MlaWalkArgs& a, int batch, hipStream_t stream) {
+    const int64_t units = (int64_t)batch * a.nsplit;
+    if (units == 0) return hipSuccess;
+    if (units > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(mla_walk_kernel, dim3((unsigned)units), dim3(MW_WAVES * kWave), 0, stream, a, (int)units);
+    return hipGetLastError();
+}
 
 hipError_t launch_walk(const WalkArgs& a, int batch, int head_dim, int mode, int depth, hipStream_t stream) {
     const int pairs = batch * a.hkv;

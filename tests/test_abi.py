@@ -174,6 +174,14 @@ def test_mla_plan_and_argument_checks(pkv):
     c64 = pkv._MLACacheT(16, 32, 64, 128, 4, 64, 512, 64)
     assert dec(P, P, 16, ctypes.byref(c64), P, 128, P, 64, 1.0, P, None, P, need - 1, 0, None) == -3
     assert dec(P, P, 16, ctypes.byref(c64), P, 128, P, 0, 1.0, P, None, None, 0, 0, None) == 0  # empty batch
+    walk = lambda cache, *a: lib.pkv_mla_cache_walk(ctypes.byref(cache), *a)
+    assert walk(c64, P, 128, P, 0, 640, P, None) == 0       # empty batch: nothing launched
+    assert walk(c64, P, 128, P, -1, 640, P, None) == -1     # negative batch
+    assert walk(c64, P, 128, P, 1, 96, P, None) == -1       # split not a multiple of 64
+    assert walk(c64, P, 128, P, 1, 8192, P, None) == -1     # split above 4096
+    assert walk(c64, P, 128, P, 1, 640, P + 2, None) == -1  # out not 4-byte aligned
+    assert walk(c64, None, 128, P, 1, 640, P, None) == -1   # no block table
+    assert walk(pkv._MLACacheT(16, 32, 64, 128, 4, 64, 256, 64), P, 128, P, 1, 640, P, None) == -2
 
 
 def test_check_indices_rejects_bad_arguments(pkv):

@@ -79,3 +79,51 @@ def test_walk_rejects_bf16_and_bad_splits():
     for split, depth in ((96, 1), (0, 1), (8192, 1), (64, 4), (64, 0)):
         with pytest.raises(pkv.PkvError):
             pkv.cache_walk(r.cache, r.bt, r.ctx, split, depth=depth)
+
+
+def mla_expected_sums(cache, w, split):
+    """Per (sequence, split): the wrapping sum of the 32-bit words of the latent row, the rotary row
+    and the two scales of every key in the split's range, from the cache's bytes."""
+    lat = cache.latent.view(torch.uint8).cpu().numpy().reshape(w.num_blocks * w.block_size, -1)
+    rope = cache.rope.view(torch.uint8).cpu().numpy().reshape(w.num_blocks * w.block_size, -1)
+    ls = cache.latent_scale.cpu().numpy().reshape(-1).view(np.uint32).astype(np.uint64)
+    rs = cache.rope_scale.cpu().numpy().reshape(-1).view(np.uint32).astype(np.uint64)
+    row_words = (np.ascontiguousarray(lat).view(np.uint32).sum(axis=1, dtype=np.uint64)
+                 + np.ascontiguousarray(rope).view(np.uint32).sum(axis=1, dtype=np.uint64) + ls + rs)
+    bs = w.block_size
+    nsplit = -(-w.max_blocks_per_seq * bs // split)
+    out = np.zeros((w.batch, nsplit), dtype=np.uint64)
+    for b in range(w.batch):
+        ctx = int(w.context_lengths[b])
+        pos = np.arange(ctx)
+        rows = w.block_table[b, pos // bs].astype(np.int64) * bs + pos % bs
+        for s in range(nsplit):
+            t0, t1 = s * split, min((s + 1) * split, ctx)
+            if t0 < t1:
+                out[b, s] = int(row_words[rows[t0:t1]].sum(dtype=np.uint64)) & 0xffffffff
+    return out.astype(np.uint32)
+
+
+@pytest.mark.parametrize("bs,ctx,split", [
+    (16, [0, 1, 63, 64, 65, 1000, 3000], 64),
+    (64, [37, 2048, 4095, 130], 640),
+    (128, [1, 700, 8192], 4096),
+    (32, [200, 17], 192),   # splits start inside pages
+])
+def test_mla_walk_checksums(bs, ctx, split):
+    from tests.test_gpu_mla import MlaRun
+
+    w = gen.mla_workload(f"mla-walk-{bs}", batch=len(ctx), num_heads=16, block_size=bs, context_lengths=ctx,
+                         seed=sum(ctx) + bs)
+    r = MlaRun(w)
+    # unwritten rows hold nonzero bytes and scales, so a read past a context changes a sum
+    r.cache.latent.fill_(53)
+    r.cache.rope.fill_(-7)
+    r.cache.latent_scale.fill_(0.25)
+    r.cache.rope_scale.fill_(3.0)
+    r.store()
+    want = mla_expected_sums(r.cache, w, split)
+    got = pkv.mla_cache_walk(r.cache, r.bt, r.ctx, split)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5].tolist()
