@@ -49,7 +49,7 @@ def parse():
                     help="int8-score kernel key partition: 0 planned, 1 fixed, 2 balanced")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window: each query attends to its last W positions (0: all)")
-    ap.add_argument("--kernel", type=int, default=0, help="0 = library choice, 1 = VALU, 2 = MFMA fp16 scores, 3 = MFMA int8 scores")
+    ap.add_argument("--kernel", type=int, default=0, help="0 = library choice, 1 = VALU, 2 = MFMA fp16 scores, 3 = MFMA int8 scores, 4 = tile (many rows per KV head)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-baseline sample")
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = auto)")
@@ -361,7 +361,7 @@ def run_decode(args, config_index, quant_mode, with_cpu):
             "sum_context": int(w.context_lengths.sum()), "new_tokens": new_tokens,
             "cache_replicas": reps, "split_tokens": plan["split_tokens"], "num_splits": plan["num_splits"],
             "window": args.window,
-            "kernel": {1: "valu", 2: "mfma-f16", 3: "mfma-i8"}[plan["kernel"]],
+            "kernel": {1: "valu", 2: "mfma-f16", 3: "mfma-i8", 4: "tile"}[plan["kernel"]],
             "store": "in the decode call" if fused else "separate call",
             "parallelism": "single-gpu",
         },

@@ -16,7 +16,7 @@ Debug-only environment overrides (read at each call): ``PKV_CHECK=1`` runs ``che
 device-side bounds check of the block table, context lengths, query-length prefix sums and slot
 mapping) before every store, dequant, walk and decode call and raises ``PkvIndexError`` instead of
 making a call that would read out of bounds (it waits for the GPU: tests and debugging only);
-``PKV_SPLIT_TOKENS=n`` and ``PKV_DECODE_PATH=valu|mfma|c8`` stand in for the GQA decode's
+``PKV_SPLIT_TOKENS=n`` and ``PKV_DECODE_PATH=valu|mfma|c8|tile`` stand in for the GQA decode's
 ``split_tokens`` and ``kernel`` arguments where a call leaves them at 0.
 """
 from __future__ import annotations
@@ -231,7 +231,7 @@ def _debug_check(cache, what, **arrays):
         raise PkvIndexError(f"{what}: {', '.join(names)} out of range (first at {where}; PKV_CHECK flags {flags})")
 
 
-_DECODE_PATHS = {"valu": 1, "mfma": 2, "c8": 3}
+_DECODE_PATHS = {"valu": 1, "mfma": 2, "c8": 3, "tile": 4}
 
 
 def _opts(split_tokens=0, kernel=0, partition=0, window=0):

@@ -1,0 +1,388 @@
+// decode_tile.hip - grouped-query attention of many query rows per KV head over the int8 paged cache
+// (paged prefill and multi-token chunks; MojoPagedPrefillGQA / MojoPagedDecodeGQA, Mojo Opset README
+// Op List), on the matrix cores of gfx950.
+//
+// The per-wave decode kernels stream every key block once per row group; with tens or hundreds of
+// query rows per KV head the same block is then read (and its V codes converted) once per group.
+// Here one workgroup of four waves takes a tile of 128 query rows of one (sequence, KV head), 32
+// rows per wave, and walks the keys the tile's last row sees in blocks of 64:
+//   * the four waves load each block together (16 bytes of K, 16 of V and one scale per thread
+//     per load, two blocks in flight), convert the int8 codes to fp16 once (exact: code and
+//     1152 + code are both fp16 integers) and store K token-major and V channel-major in LDS,
+//     double-buffered, with one workgroup barrier per block;
+//   * each wave forms its rows' scores on the matrix cores in fp16 (v_mfma_f32_16x16x32_f16):
+//     S^T (keys x rows) = K . Q^T, the query rows pre-scaled by a power of two into fp16's range
+//     (the factor and the per-key K scale applied to the fp32 scores);
+//   * online softmax per row, lazily rescaled (the reference max moves only when a block's max
+//     passes it by more than 8, the V-scale reference when a V scale passes 16x it);
+//   * O^T (channels x rows) += V^T . P^T, so that every lane holds channels of its own row and the
+//     rescaling never leaves the lane.
+// No key splits and no merge: each tile's rows go straight to the output.  The library uses it
+// where tiles are many (the planner's choice); the block-table slice of the tile's keys is staged
+// in LDS whole (at most kTileMaxPages pages).  Per-token and per-block scales only: with static
+// per-channel scales the K scale sits inside each dot product, and folding it into an fp16 query
+// would round it to 11 bits (the int8-score kernel serves those caches).
+#include "pkv_device.h"
+#include "pkv_internal.h"
+#include "sk_partition.h"
+
+namespace pkv {
+namespace {
+
+typedef _Float16 th8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int TD = 128;          // head dim
+constexpr int TW = 4;            // waves per workgroup
+constexpr int TROWS = 32 * TW;   // query rows per tile
+constexpr int TBLK = 64;         // keys per block
+constexpr int KP = TD + 8;       // LDS pitch of a K row (halves): rows start 4 banks apart
+constexpr int VP = TBLK + 8;     // LDS pitch of a V channel row (halves)
+constexpr float kLn2t = 0.6931471805599453f;
+
+struct __align__(16) TileShared {
+    _Float16 k[2][TBLK][KP];   // K codes of the block, token-major (rows in score-operand order)
+    _Float16 v[2][TD][VP];     // V codes of the block, channel-major
+    float ks[2][TBLK];         // per-key K scale (0 past the keys)
+    float vs[2][TBLK];         // per-key V scale (0 past the keys)
+    int bt[kTileMaxPages];     // the tile's block-table slice
+};
+
+// the raw loads of one block by one thread: 32 K codes (a quarter of a key row), 32 V codes (two
+// channel rows of a 16-slot tile) and one scale
+struct TileRaw {
+    u32x4 k0, k1, v0, v1;
+    float s;
+};
+
+// eight int8 codes (two dwords) -> eight fp16 values, exactly: the byte permute makes 1152 + code,
+// one packed subtraction removes 1152
+__device__ __forceinline__ th8 codes_h8(uint32_t w0, uint32_t w1) {
+    const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;  // code + 128 as unsigned bytes
+    const uint32_t r[4] = {__builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u),
+                           __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u),
+                           __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u),
+                           __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)};
+    const th8 bias = {(_Float16)1152.0f, (_Float16)1152.0f, (_Float16)1152.0f, (_Float16)1152.0f,
+                      (_Float16)1152.0f, (_Float16)1152.0f, (_Float16)1152.0f, (_Float16)1152.0f};
+    return __builtin_bit_cast(th8, r) - bias;
+}
+
+// max / sum over the four lanes n, n+16, n+32, n+48 (one query row), by permlane swaps
+__device__ __forceinline__ float row_max4(float x) {
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+__device__ __forceinline__ float row_sum4(float x) {
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+__device__ __forceinline__ int wave_min(int x) {
+    for (int d = 1; d < kWave; d <<= 1) x = min(x, __shfl_xor(x, d, kWave));
+    return __builtin_amdgcn_readfirstlane(x);
+}
+__device__ __forceinline__ int wave_max(int x) {
+    for (int d = 1; d < kWave; d <<= 1) x = max(x, __shfl_xor(x, d, kWave));
+    return __builtin_amdgcn_readfirstlane(x);
+}
+
+// Workgroup u takes row tile nrg - 1 - u / (batch * hkv) of pair u % (batch * hkv): the tiles that
+// see the most keys (a chunk's last rows) first.
+template <int MODE>
+__global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2))) void decode_tile_kernel(
+    DecodeArgs a, int nbh) {
+    __shared__ TileShared S;
+    const int u = blockIdx.x;
+    const int item = (u % nbh) * a.nrg + (a.nrg - 1 - u / nbh);
+    const ItemGeo it = item_geo<TROWS, false>(a, item);
+    if (it.nvalid <= 0) return;  // uniform per workgroup
+    const int b = it.b, h = it.h;
+    const int kmax = it.kmax;  // keys [0, kmax): what the tile's last row sees
+    const int tid = threadIdx.x;
+    const int w = tid / kWave;
+    const int lane = tid & (kWave - 1);
+    const int n = lane & 15;
+    const int g = lane >> 4;
+
+    // ---- the block-table slice of the tile's keys
+    const int npg = ((kmax - 1) >> a.log2bs) + 1;
+    for (int i = tid; i < npg; i += TW * kWave) S.bt[i] = a.bt[(int64_t)b * a.mbs + i];
+    __syncthreads();
+
+    // ---- cooperative loads of the block at T: thread tid takes key T + tid / 4 (bytes 32 (tid % 4)
+    //      .. of its K row), channels 2 (tid % 64), + 1 of V tile tid / 64, and (tid % 4 < 2) the
+    //      key's K (0) or V (1) scale.  Keys past kmax read the last key's row and the V tile
+    //      holding it (in bounds), and get scale 0.
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k);
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v);
+    const int64_t hd = (int64_t)a.bs * TD;  // bytes of one (page, head)
+    auto load_raw = [&](int T, TileRaw& R) __attribute__((always_inline)) {
+        const int key = min(T + (tid >> 2), kmax - 1);
+        const int64_t pk = (int64_t)S.bt[key >> a.log2bs] * a.hkv + h;
+        const uint8_t* kp = kbase + pk * hd + (key & (a.bs - 1)) * TD + (tid & 3) * 32;
+        R.k0 = load16(kp);
+        R.k1 = load16(kp + 16);
+        const int tt = min(T + 16 * (tid >> 6), (kmax - 1) & ~15);  // first key of the V tile
+        const int64_t pv = (int64_t)S.bt[tt >> a.log2bs] * a.hkv + h;
+        const uint8_t* vp = vbase + pv * hd + ((tt & (a.bs - 1)) >> 4) * (TD * kVTile) + (tid & 63) * 32;
+        R.v0 = load16(vp);
+        R.v1 = load16(vp + 16);
+        R.s = 0.0f;
+        if constexpr (MODE == 0) {
+            if ((tid & 2) == 0) R.s = ((tid & 1) ? a.vs : a.ks)[pk * a.bs + (key & (a.bs - 1))];
+        } else {
+            if ((tid & 2) == 0) R.s = ((tid & 1) ? a.vs : a.ks)[pk];
+        }
+    };
+    auto store_lds = [&](const TileRaw& R, int buf, int T) __attribute__((always_inline)) {
+        const int kl = tid >> 2;
+        // key kl of the block goes to row 32 hf + 16 u + rho, the row slot rho of score tile u of
+        // half hf that holds it (kl = 32 hf + 8 (rho / 4) + 4 u + rho % 4): a tile's 16 lanes then
+        // read 16 consecutive rows, 4 banks apart, without conflicts
+        const int krow_l = (kl & 32) + ((kl & 4) << 2) + ((kl & 24) >> 1) + (kl & 3);
+        _Float16* kd = &S.k[buf][krow_l][(tid & 3) * 32];
+        *reinterpret_cast<th8*>(kd) = codes_h8(R.k0.x, R.k0.y);
+        *reinterpret_cast<th8*>(kd + 8) = codes_h8(R.k0.z, R.k0.w);
+        *reinterpret_cast<th8*>(kd + 16) = codes_h8(R.k1.x, R.k1.y);
+        *reinterpret_cast<th8*>(kd + 24) = codes_h8(R.k1.z, R.k1.w);
+        const int c = 2 * (tid & 63), s0 = 16 * (tid >> 6);
+        *reinterpret_cast<th8*>(&S.v[buf][c][s0]) = codes_h8(R.v0.x, R.v0.y);
+        *reinterpret_cast<th8*>(&S.v[buf][c][s0 + 8]) = codes_h8(R.v0.z, R.v0.w);
+        *reinterpret_cast<th8*>(&S.v[buf][c + 1][s0]) = codes_h8(R.v1.x, R.v1.y);
+        *reinterpret_cast<th8*>(&S.v[buf][c + 1][s0 + 8]) = codes_h8(R.v1.z, R.v1.w);
+        if ((tid & 2) == 0) {
+            const bool in = T + kl < kmax;  // past the keys: 0, so that nothing unwritten is used
+            ((tid & 1) ? S.vs[buf] : S.ks[buf])[kl] = in ? R.s : 0.0f;
+        }
+    };
+
+    // ---- this wave's query rows (B operand of the score MFMA): rows 32w + 16rt + n of the tile;
+    //      lane (n, g) holds channels 32m + 8g .. + 7 of k-step m, scaled by 2^k into fp16's range
+    //      (exact: a bf16 value times a power of two fits fp16's 11 significant bits)
+    uint32_t qf[2][4][4];
+    float rowmul[2];  // softmax scale * log2(e) / 2^k
+    int lim[2];       // last key the row sees (invalid rows: none masked, nothing written)
+    bool rowv[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const int j = 32 * w + 16 * rt + n;
+        rowv[rt] = j < it.nvalid;
+        const int r = it.r0 + j;
+        lim[rt] = rowv[rt] ? it.prior + r / a.g : 0x7fffffff;
+        float x[32];
+        if (rowv[rt]) {
+            const uint16_t* qp = a.q + ((int64_t)(it.qrow0 + r / a.g) * a.hq + h * a.g + r % a.g) * TD + 8 * g;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const u32x4 v = load16(qp + 32 * m);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[8 * m + e] = bf16_at(v, e);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 32; ++e) x[e] = 0.0f;
+        }
+        float mx = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) mx = fmaxf(mx, fabsf(x[e]));
+        mx = row_max4(mx);
+        int ex = 0;
+        if (mx > 0.0f) (void)frexpf(mx, &ex);       // mx in [2^(ex-1), 2^ex)
+        const int k = min(120, max(-120, 15 - ex));  // mx * 2^k in [2^14, 2^15)
+        const float up = ldexpf(1.0f, k);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const _Float16 lo = (_Float16)(x[8 * m + 2 * e2] * up), hi = (_Float16)(x[8 * m + 2 * e2 + 1] * up);
+                qf[rt][m][e2] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+            }
+        rowmul[rt] = ldexpf(a.scale_log2, -k);
+    }
+    // the wave's lowest and highest causal limits over its valid rows
+    const int lim_lo = wave_min(min(lim[0], lim[1]));
+    const int lim_hi = wave_max(max(rowv[0] ? lim[0] : -1, rowv[1] ? lim[1] : -1));
+
+    float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
+    f4 acc[2][8];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) acc[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+    float s_ref = 0.0f, s_inv = 0.0f;
+
+
+    // one block from LDS buffer buf: the wave's 32 rows against its 64 keys, in two halves of 32
+    // keys, each its own online-softmax step
+    auto compute = [&](const int T, const int buf) __attribute__((always_inline)) {
+        if (T > lim_hi) return;  // no valid row of the wave sees these keys (uniform)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int T0 = T + 32 * hf;
+            if (T0 > lim_hi) break;  // (uniform)
+            const bool MASKED = T0 + 31 > lim_lo;
+            // ---------------------------- scores: tile u holds keys T0 + 8g' + 4u + i of row n
+            f4 sc[2][2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) sc[rt][0] = sc[rt][1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int uu = 0; uu < 2; ++uu) {
+                const _Float16* kr = &S.k[buf][32 * hf + 16 * uu + n][8 * g];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const th8 av = *reinterpret_cast<const th8*>(kr + 32 * m);
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt)
+                        sc[rt][uu] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(th8, qf[rt][m]),
+                                                                            sc[rt][uu], 0, 0, 0);
+                }
+            }
+            // ---------------------------- logits (log2 units) of keys T0 + 8g + e, their V scales
+            const f4 k0 = *reinterpret_cast<const f4*>(&S.ks[buf][32 * hf + 8 * g]);
+            const f4 k1 = *reinterpret_cast<const f4*>(&S.ks[buf][32 * hf + 8 * g + 4]);
+            const f4 v0 = *reinterpret_cast<const f4*>(&S.vs[buf][32 * hf + 8 * g]);
+            const f4 v1 = *reinterpret_cast<const f4*>(&S.vs[buf][32 * hf + 8 * g + 4]);
+            const float kss[8] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+            const float vss[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            // ---------------------------- V-scale reference (the same for every row of the wave)
+            float vmax = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vmax = fmaxf(vmax, vss[e]);
+            vmax = row_max4(vmax);
+            float sf = 1.0f;
+            if (vmax > 16.0f * s_ref) {  // (also the first half-block: s_ref == 0)
+                sf = s_ref > 0.0f ? s_ref * __builtin_amdgcn_rcpf(vmax) : 0.0f;
+                s_ref = vmax;
+                s_inv = __builtin_amdgcn_rcpf(vmax);
+            }
+            float vr[8];  // the keys' V scales over the reference
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vr[e] = vss[e] * s_inv;
+            // ---------------------------- online softmax, P^T operand (lane (n, g): row n, keys
+            //                              T0 + 8g .. + 7)
+            uint32_t pb[2][4];
+            float factor[2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = sc[rt][e >> 2][e & 3] * (kss[e] * rowmul[rt]);
+                if (MASKED) {  // hidden keys score -inf (keys past kmax are past every valid row's limit)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (T0 + 8 * g + e > lim[rt]) x[e] = -INFINITY;
+                }
+                float bmax = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bmax = fmaxf(bmax, x[e]);
+                bmax = row_max4(bmax);
+                float alpha = 1.0f;
+                if (bmax > m_ref[rt] + 8.0f) {  // (also the first block: m_ref == -inf)
+                    alpha = __builtin_amdgcn_exp2f(m_ref[rt] - bmax);
+                    m_ref[rt] = bmax;
+                }
+                // a row with no visible key yet keeps m_ref = -inf: its weights are taken against
+                // 0, so that its hidden keys (-inf) weigh exactly 0
+                const float mref = m_ref[rt] == -INFINITY ? 0.0f : m_ref[rt];
+                float ps = 0.0f;
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const float p0 = __builtin_amdgcn_exp2f(x[2 * e2] - mref);
+                    const float p1 = __builtin_amdgcn_exp2f(x[2 * e2 + 1] - mref);
+                    ps += p0 + p1;
+                    const _Float16 w0 = (_Float16)(p0 * vr[2 * e2]), w1 = (_Float16)(p1 * vr[2 * e2 + 1]);
+                    pb[rt][e2] = (uint32_t)__builtin_bit_cast(uint16_t, w0) |
+                                 ((uint32_t)__builtin_bit_cast(uint16_t, w1) << 16);
+                }
+                l_run[rt] = l_run[rt] * alpha + row_sum4(ps);
+                factor[rt] = alpha * sf;
+            }
+            if (__any(factor[0] != 1.0f || factor[1] != 1.0f)) {
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < 8; ++ct) acc[rt][ct] *= factor[rt];
+            }
+            // ---------------------------- O^T += V^T . P^T over the 32 keys, channel tile ct
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) {
+                const th8 av = *reinterpret_cast<const th8*>(&S.v[buf][16 * ct + n][32 * hf + 8 * g]);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+                    acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(th8, pb[rt]),
+                                                                         acc[rt][ct], 0, 0, 0);
+            }
+        }
+    };
+
+    // ---- the key loop: block k computes from LDS buffer k % 2 while the raw loads of blocks k + 1
+    //      (register set (k + 1) % 2) and k + 2 (set k % 2, issued at its start) are in flight; block
+    //      k + 1 goes to LDS after block k's compute, then one barrier.  Blocks in pairs, one loop
+    //      exit, so the register sets and buffers are fixed per half of the pair.
+    const int nblk = (kmax + TBLK - 1) / TBLK;
+    TileRaw R0, R1;
+    load_raw(0, R0);
+    load_raw(TBLK, R1);  // (past kmax: in-bounds stand-ins)
+    store_lds(R0, 0, 0);
+    __syncthreads();
+    auto step = [&](const int T, const int buf, TileRaw& Rcur, TileRaw& Rnext) __attribute__((always_inline)) {
+        load_raw(T + 2 * TBLK, Rcur);  // block k + 2 into the set block k came from (already in LDS)
+        compute(T, buf);
+        store_lds(Rnext, buf ^ 1, T + TBLK);  // block k + 1
+        __syncthreads();
+    };
+    int T = 0;
+    for (int i = 1; i < nblk; i += 2) {
+        step(T, 0, R0, R1);
+        step(T + TBLK, 1, R1, R0);
+        T += 2 * TBLK;
+    }
+    if (nblk & 1) compute(T, 0);
+
+    // ---- normalise and write: lane (n, g) holds channels 16ct + 4g + i of row 32w + 16rt + n
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        if (!rowv[rt]) continue;
+        const int j = 32 * w + 16 * rt + n;
+        const int r = it.r0 + j;
+        const int64_t orow = (int64_t)(it.qrow0 + r / a.g) * a.hq + h * a.g + r % a.g;
+        const float l = l_run[rt];
+        const float mul = l > 0.0f ? s_ref / l : 0.0f;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const int c = 16 * ct + 4 * g;
+            float o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = acc[rt][ct][i] * mul;
+            uint2 pk;
+            pk.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
+            pk.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
+            *reinterpret_cast<uint2*>(a.out + orow * TD + c) = pk;
+        }
+        if (g == 0 && a.lse) a.lse[orow] = l > 0.0f ? (m_ref[rt] + log2f(l)) * kLn2t : -INFINITY;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_tile(const DecodeArgs& a, int batch, int head_dim, int mode, hipStream_t stream) {
+    if (head_dim != TD) return hipErrorInvalidValue;
+    const int64_t nbh = (int64_t)batch * a.hkv;
+    const int64_t grid = nbh * a.nrg;
+    if (grid == 0) return hipSuccess;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 gd((unsigned)grid), bd(TW * kWave);
+    if (mode == 0)
+        hipLaunchKernelGGL(decode_tile_kernel<0>, gd, bd, 0, stream, a, (int)nbh);
+    else if (mode == 1)
+        hipLaunchKernelGGL(decode_tile_kernel<1>, gd, bd, 0, stream, a, (int)nbh);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace pkv

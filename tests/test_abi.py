@@ -63,6 +63,30 @@ def test_plan_is_deterministic_and_bounded(pkv):
     assert pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 2, kernel=3)["kernel"] == 2
     assert pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 0, kernel=1)["kernel"] == 1
     assert pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 0, kernel=2)["kernel"] == 2
+    # the tile kernel: one pass over each tile's keys, no splits, no workspace; int8 pages, head_dim
+    # 128, no window, no forced splits, tables of at most 1152 pages
+    tile = pkv.decode_plan(4, 32, 8, 128, 128, 16, 2048, 0, kernel=4)
+    assert tile["kernel"] == 4 and tile["num_splits"] == 1
+    assert pkv.decode_plan(4, 32, 8, 128, 128, 16, 2048, 1, kernel=4)["kernel"] == 4
+    assert pkv.decode_workspace_size(4, 32, _py_cache(pkv), 128, max_q_len=2048, kernel=4) == 0
+    for args, kw in (((4, 32, 8, 64, 128, 16, 2048, 0), {}),          # head_dim 64
+                     ((4, 32, 8, 128, 128, 16, 2048, 2), {}),         # bf16 pages
+                     ((4, 32, 8, 128, 128, 16, 2048, 3), {}),         # static per-channel scales
+                     ((4, 32, 8, 128, 1153, 16, 2048, 0), {}),        # table past 1152 pages
+                     ((4, 32, 8, 128, 128, 16, 2048, 0), {"window": 256}),
+                     ((4, 32, 8, 128, 128, 16, 2048, 0), {"split_tokens": 512}),
+                     ((4, 32, 8, 128, 128, 16, 2048, 0), {"partition": 2})):
+        with pytest.raises(pkv.PkvError):
+            pkv.decode_plan(*args, kernel=4, **kw)
+    with pytest.raises(pkv.PkvError):
+        pkv.decode_plan(2, 8, 2, 128, 7, 16, 1, 0, kernel=5)
+
+
+def _py_cache(pkv):
+    """A Cache object describing a 128-dim int8 cache without device memory (sizes only)."""
+    c = pkv.Cache.__new__(pkv.Cache)
+    c.num_kv_heads, c.head_dim, c.block_size, c.quant_mode = 8, 128, 16, 0
+    return c
 
 
 def _cache_struct(pkv, mode=0, hd=128, bs=16, k=16, v=32, ks=64, vs=128):

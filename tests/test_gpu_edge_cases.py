@@ -35,6 +35,16 @@ def _kernels(mode):
     return [3] if mode == 3 else KERNELS
 
 
+def _runs(mode, d, kws):
+    """(kernel, options) pairs: every kernel serving the mode with each of the key-partition options,
+    and the tile kernel (kernel 4: one pass over the keys, no partition options) where it serves
+    (head_dim 128, per-token or per-block scales)."""
+    runs = [(k, kw) for k in _kernels(mode) for kw in kws]
+    if d == 128 and mode in (0, 1):
+        runs.append((4, {}))
+    return runs
+
+
 def _zero_positions(w, t, which, seq_pos):
     """Zero the bf16 rows of ``which`` ("k", "v" or "kv") at (sequence, position, KV head) triples
     (head None: every head) in the drawn tensors, before anything is stored."""
@@ -77,10 +87,9 @@ def test_all_zero_tokens_store_and_decode(mode):
             blk, off = w.block_table[b, p // 16], p % 16
             assert np.all(vs[blk, slice(None) if h is None else h, off] == 0)
     ref = r.oracle_decode()
-    for kernel in _kernels(mode):
-        for kw in (dict(), dict(split_tokens=128), dict(partition=2)):
-            out, lse = r.decode(kernel=kernel, **kw)
-            r.assert_decode_close(out, lse, ref)
+    for kernel, kw in _runs(mode, w.head_dim, (dict(), dict(split_tokens=128), dict(partition=2))):
+        out, lse = r.decode(kernel=kernel, **kw)
+        r.assert_decode_close(out, lse, ref)
 
 
 def test_all_zero_blocks_per_block_mode():
@@ -110,10 +119,9 @@ def test_all_zero_blocks_per_block_mode():
     assert np.all(ks[bt[1, 2]] == 0)  # written by zeros only
     assert np.all(ks[bt[2, 0]] == 0) and np.all(ks[bt[2, 1]] == 0)
     ref = r.oracle_decode()
-    for kernel in KERNELS:
-        for kw in (dict(), dict(split_tokens=128)):
-            out, lse = r.decode(kernel=kernel, **kw)
-            r.assert_decode_close(out, lse, ref)
+    for kernel, kw in _runs(1, w.head_dim, (dict(), dict(split_tokens=128))):
+        out, lse = r.decode(kernel=kernel, **kw)
+        r.assert_decode_close(out, lse, ref)
 
 
 def test_mla_store_all_zero_rows():
@@ -169,10 +177,9 @@ def test_softmax_scale_zero_and_negative(mode, d, bs, g, ctx, ql):
                                np.concatenate([r.w.prior_lengths[b] + 1 + np.arange(r.w.q_lens[b])
                                                for b in range(r.w.batch)]), r.w.num_q_heads).reshape(ref[2].shape)
             assert np.allclose(ref[2][fin], np.log(counts[fin]), rtol=0, atol=1e-12)
-        for kernel in _kernels(mode):
-            for kw in (dict(), dict(split_tokens=128), dict(partition=2)):
-                out, lse = r.decode(scale=scale, kernel=kernel, **kw)
-                r.assert_decode_close(out, lse, ref, scale=scale)
+        for kernel, kw in _runs(mode, d, (dict(), dict(split_tokens=128), dict(partition=2))):
+            out, lse = r.decode(scale=scale, kernel=kernel, **kw)
+            r.assert_decode_close(out, lse, ref, scale=scale)
 
 
 OUTLIER_CASES = [
@@ -204,11 +211,10 @@ def test_query_outlier_channels(mode, d, bs, g, ctx, ql, factor):
     r.store_prior()
     r.store_new()
     ref = r.oracle_decode()
-    for kernel in _kernels(mode):
-        for kw in (dict(), dict(split_tokens=256), dict(partition=2)):
-            out, lse = r.decode(kernel=kernel, **kw)
-            max_abs, rel = r.assert_decode_close(out, lse, ref)
-            print(f"  outlier x{factor} mode {mode} kernel {kernel} {kw}: max_abs={max_abs:.2e} rel={rel:.2e}")
+    for kernel, kw in _runs(mode, d, (dict(), dict(split_tokens=256), dict(partition=2))):
+        out, lse = r.decode(kernel=kernel, **kw)
+        max_abs, rel = r.assert_decode_close(out, lse, ref)
+        print(f"  outlier x{factor} mode {mode} kernel {kernel} {kw}: max_abs={max_abs:.2e} rel={rel:.2e}")
 
 
 @pytest.mark.parametrize("factor", [64, 256])
