@@ -31,6 +31,8 @@ namespace {
 
 typedef _Float16 th8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float tf2 __attribute__((ext_vector_type(2)));
+typedef _Float16 th2 __attribute__((ext_vector_type(2)));
 
 constexpr int TD = 128;          // head dim
 constexpr int TW = 4;            // waves per workgroup
@@ -294,9 +296,8 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
                     const float p0 = __builtin_amdgcn_exp2f(x[2 * e2] - mref);
                     const float p1 = __builtin_amdgcn_exp2f(x[2 * e2 + 1] - mref);
                     ps += p0 + p1;
-                    const _Float16 w0 = (_Float16)(p0 * vr[2 * e2]), w1 = (_Float16)(p1 * vr[2 * e2 + 1]);
-                    pb[rt][e2] = (uint32_t)__builtin_bit_cast(uint16_t, w0) |
-                                 ((uint32_t)__builtin_bit_cast(uint16_t, w1) << 16);
+                    const tf2 wv = {p0 * vr[2 * e2], p1 * vr[2 * e2 + 1]};  // one packed conversion (RNE)
+                    pb[rt][e2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(wv, th2));
                 }
                 l_run[rt] = l_run[rt] * alpha + row_sum4(ps);
                 factor[rt] = alpha * sf;
