@@ -166,7 +166,8 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     //      lane (n, g) holds channels 32m + 8g .. + 7 of k-step m, scaled by 2^k into fp16's range
     //      (exact: a bf16 value times a power of two fits fp16's 11 significant bits)
     uint32_t qf[2][4][4];
-    float rowmul[2];  // softmax scale * log2(e) / 2^k
+    float rowmul[2];  // |softmax scale| * log2(e) / 2^k, floored at 2^-126 (below)
+    const float sgn = a.scale_log2 < 0.0f ? -1.0f : 1.0f;  // a negative scale flips the query
     int lim[2];       // last key the row sees (invalid rows: none masked, nothing written)
     bool rowv[2];
 #pragma unroll
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
             for (int m = 0; m < 4; ++m) {
                 const u32x4 v = load16(qp + 32 * m);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[8 * m + e] = bf16_at(v, e);
+                for (int e = 0; e < 8; ++e) x[8 * m + e] = sgn * bf16_at(v, e);
             }
         } else {
 #pragma unroll
@@ -203,7 +204,10 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
                 const _Float16 lo = (_Float16)(x[8 * m + 2 * e2] * up), hi = (_Float16)(x[8 * m + 2 * e2 + 1] * up);
                 qf[rt][m][e2] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
             }
-        rowmul[rt] = ldexpf(a.scale_log2, -k);
+        // floored at 2^-126: a hidden key's -inf score times the row's factor must stay -inf (a zero
+        // scale would make it NaN), and below the floor every logit difference is far under fp32's
+        // resolution of exp2 near 1, so a zero scale still weighs every visible key 1
+        rowmul[rt] = fmaxf(ldexpf(fabsf(a.scale_log2), -k), 0x1p-126f);
     }
     // the wave's lowest and highest causal limits over its valid rows
     const int lim_lo = wave_min(min(lim[0], lim[1]));
@@ -270,18 +274,20 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
             float factor[2];
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                float x[8];
+                // y: the score times the key's K scale; the logit (log2 units) is y times the row's
+                // factor rowmul >= 0, which joins the exponent's FMA (and commutes with the max)
+                float y[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = sc[rt][e >> 2][e & 3] * (kss[e] * rowmul[rt]);
+                for (int e = 0; e < 8; ++e) y[e] = sc[rt][e >> 2][e & 3] * kss[e];
                 if (MASKED) {  // hidden keys score -inf (keys past kmax are past every valid row's limit)
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        if (T0 + 8 * g + e > lim[rt]) x[e] = -INFINITY;
+                        if (T0 + 8 * g + e > lim[rt]) y[e] = -INFINITY;
                 }
-                float bmax = -INFINITY;
+                float ymax = -INFINITY;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) bmax = fmaxf(bmax, x[e]);
-                bmax = row_max4(bmax);
+                for (int e = 0; e < 8; ++e) ymax = fmaxf(ymax, y[e]);
+                const float bmax = row_max4(ymax) * rowmul[rt];
                 float alpha = 1.0f;
                 if (bmax > m_ref[rt] + 8.0f) {  // (also the first block: m_ref == -inf)
                     alpha = __builtin_amdgcn_exp2f(m_ref[rt] - bmax);
@@ -293,8 +299,8 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
                 float ps = 0.0f;
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
-                    const float p0 = __builtin_amdgcn_exp2f(x[2 * e2] - mref);
-                    const float p1 = __builtin_amdgcn_exp2f(x[2 * e2 + 1] - mref);
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(y[2 * e2], rowmul[rt], -mref));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(y[2 * e2 + 1], rowmul[rt], -mref));
                     ps += p0 + p1;
                     const tf2 wv = {p0 * vr[2 * e2], p1 * vr[2 * e2 + 1]};  // one packed conversion (RNE)
                     pb[rt][e2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(wv, th2));
