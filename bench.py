@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--config", type=int, default=1,
                     help="workload index (0..4; 5 = paged prefill, measured in TFLOP/s); 1 = Qwen3-8B decode")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--prompt-len", type=int, default=0,
+                    help="paged prefill (--config 5): prompts of this many tokens, 8192 // N of them (0: 4 x 2048)")
     ap.add_argument("--quant-mode", type=int, default=None,
                     help="run the workload's shapes with another cache mode (3 = static per-channel scales)")
     ap.add_argument("--partition", type=int, default=0,
@@ -202,7 +204,7 @@ def run_decode(args, config_index, quant_mode, with_cpu):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = gen.make_config(config_index, quant_mode=quant_mode)
+    w = gen.make_config(config_index, quant_mode=quant_mode, prompt_len=args.prompt_len)
     t = gen.gen_tensors(w, device=dev)
     k_prior, k_new = gen.split_prior_new(w, t["k_all"])
     v_prior, v_new = gen.split_prior_new(w, t["v_all"])
@@ -308,7 +310,8 @@ def run_decode(args, config_index, quant_mode, with_cpu):
     default_plan = (args.kernel == 0 and args.split_tokens == 0 and args.window == 0 and args.partition == 0
                     and not args.separate_store)
     mode_key = "" if quant_mode is None else f".mode{quant_mode}"
-    traffic = traffic_record(f"decode.config{config_index}{mode_key}") if default_plan else None
+    plen_key = f".p{args.prompt_len}" if args.prompt_len > 0 else ""
+    traffic = traffic_record(f"decode.config{config_index}{mode_key}{plen_key}") if default_plan else None
 
     cpu = None
     if with_cpu:
@@ -318,7 +321,9 @@ def run_decode(args, config_index, quant_mode, with_cpu):
     roofline = {
         "bound": "hbm",
         "kernel": ("pkv_store_decode_gqa (new-token store + split-KV partial, log-sum-exp merge)" if fused
-                   else "pkv_decode_gqa (split-KV partial + log-sum-exp merge)"),
+                   else "pkv_decode_gqa (tile kernel, 128 query rows per workgroup"
+                   + (", key splits + log-sum-exp merge)" if plan["num_splits"] > 1 else ")")
+                   if plan["kernel"] == 4 else "pkv_decode_gqa (split-KV partial + log-sum-exp merge)"),
         "achieved": round(achieved, 2),
         "peak": PEAK_HBM_GBS,
         "unit": "GB/s",
@@ -331,8 +336,8 @@ def run_decode(args, config_index, quant_mode, with_cpu):
     if w.name.startswith("paged-prefill"):
         # a prompt's attention is a dense contraction: 2 * 2 * D algorithmic flops per visible
         # (query head, key) pair (Q.K and P.V), against the 2.5 PFLOP/s of the dense fp16 / bf16
-        # matrix cores (the kernel runs the scores as three int8 passes, one per query digit, and
-        # P.V in fp16; only the algorithmic flops count)
+        # matrix cores (the tile kernel runs Q.K and P.V in fp16 on the matrix cores; only the
+        # algorithmic flops count)
         pairs = sum(int(w.q_lens[b]) * (2 * int(w.prior_lengths[b]) + int(w.q_lens[b]) + 1) // 2
                     for b in range(w.batch))
         flops = 4.0 * pairs * w.num_q_heads * w.head_dim
@@ -435,7 +440,7 @@ def main_walk(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = gen.make_config(args.config, quant_mode=args.quant_mode)
+    w = gen.make_config(args.config, quant_mode=args.quant_mode, prompt_len=args.prompt_len)
     if w.quant_mode == gen.QUANT_NONE_BF16:
         raise SystemExit("--op walk: int8 caches only")
     t = gen.gen_tensors(w, device=dev)
@@ -507,7 +512,7 @@ def main_codec(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = gen.make_config(args.config, quant_mode=args.quant_mode)
+    w = gen.make_config(args.config, quant_mode=args.quant_mode, prompt_len=args.prompt_len)
     t = gen.gen_tensors(w, device=dev)
     k_prior, _ = gen.split_prior_new(w, t["k_all"])
     v_prior, _ = gen.split_prior_new(w, t["v_all"])

@@ -158,7 +158,8 @@ CONFIG_NAMES = [
 ]
 
 
-def make_config(index: int, seed: Optional[int] = None, quant_mode: Optional[int] = None) -> Workload:
+def make_config(index: int, seed: Optional[int] = None, quant_mode: Optional[int] = None,
+                prompt_len: int = 0) -> Workload:
     """The five benchmark workloads, seeded with ``1000 + index`` by default.
 
     0  tiny:        B=2, 8/2 heads, D=64, BS=16, ctx {37, 100}, pool = permutation of 16 blocks
@@ -170,10 +171,11 @@ def make_config(index: int, seed: Optional[int] = None, quant_mode: Optional[int
                     one fp32 scale per 16-token block
     5  prefill:     B=4 prompts of 2048 tokens (store and causal attention of every token),
                     32/8 heads, D=128, BS=16, per-token scales (a measurement workload for the
-                    paged-prefill row, not one of the five above)
+                    paged-prefill row, not one of the five above); prompt_len > 0: prompts of
+                    that many tokens instead, max(1, 8192 // prompt_len) of them
     """
     if quant_mode is not None:  # the same shapes and lengths with another cache mode
-        w = make_config(index, seed)
+        w = make_config(index, seed, prompt_len=prompt_len)
         return dataclasses.replace(w, quant_mode=int(quant_mode), name=f"{w.name}-mode{int(quant_mode)}")
     s = 1000 + index if seed is None else seed
     r = _rng(s, 0)
@@ -205,10 +207,12 @@ def make_config(index: int, seed: Optional[int] = None, quant_mode: Optional[int
                                q_lens=ql, seed=s, max_blocks_per_seq=-(-(16384 + 16) // 16),
                                decode_only=False)
     if index == 5:
-        ctx = np.full(4, 2048)
-        return custom_workload(CONFIG_NAMES[5], batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        n = int(prompt_len) if prompt_len > 0 else 2048
+        ctx = np.full(max(1, 8192 // n) if prompt_len > 0 else 4, n)
+        name = CONFIG_NAMES[5] if prompt_len <= 0 else f"{CONFIG_NAMES[5]}-{n}"
+        return custom_workload(name, batch=len(ctx), num_q_heads=32, num_kv_heads=8, head_dim=128,
                                block_size=16, quant_mode=QUANT_PER_TOKEN, context_lengths=ctx, q_lens=ctx,
-                               seed=s, max_blocks_per_seq=2048 // 16, decode_only=False)
+                               seed=s, max_blocks_per_seq=-(-n // 16), decode_only=False)
     raise ValueError(f"no config {index}")
 
 

@@ -246,10 +246,10 @@ typedef struct {
                              cache falls back to 2); 4 = tile kernel for many query rows
                              per KV head (prompts, multi-token chunks): one workgroup per
                              128 rows of a (sequence, KV head), each 64-key block loaded
-                             once per workgroup and shared through LDS, fp16 scores, no
-                             key splits and no workspace (per-token or per-block int8
-                             caches, head_dim 128, no window, split_tokens 0, partition 0,
-                             max_blocks_per_seq at most 1152; otherwise
+                             once per workgroup and shared through LDS, fp16 scores;
+                             contexts above 4096 keys (or split_tokens > 0) in key splits
+                             with a log-sum-exp merge (per-token or per-block int8 caches,
+                             head_dim 128, no window, partition 0; otherwise
                              PKV_ERR_UNSUPPORTED) */
     int32_t partition;    /* how the keys are cut into work (kernels 3 and 2):
                              0 = planned: kernel 3 takes the balanced partition for

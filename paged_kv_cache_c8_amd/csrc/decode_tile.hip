@@ -5,7 +5,9 @@
 // The per-wave decode kernels stream every key block once per row group; with tens or hundreds of
 // query rows per KV head the same block is then read (and its V codes converted) once per group.
 // Here one workgroup of four waves takes a tile of 128 query rows of one (sequence, KV head), 32
-// rows per wave, and walks the keys the tile's last row sees in blocks of 64:
+// rows per wave (rows 16w .. 16w + 15 and 64 + 16w .. 64 + 16w + 15, so that a tile partly filled
+// still spreads over the four SIMDs; a wave whose second 16 rows are all past the tile's rows does
+// the work of its first 16 only), and walks the keys the tile's last row sees in blocks of 64:
 //   * the four waves load each block together (16 bytes of K, 16 of V and one scale per thread
 //     per load, two blocks in flight), convert the int8 codes to fp16 once (exact: code and
 //     1152 + code are both fp16 integers) and store K token-major and V channel-major in LDS,
@@ -17,11 +19,14 @@
 //     passes it by more than 8, the V-scale reference when a V scale passes 16x it);
 //   * O^T (channels x rows) += V^T . P^T, so that every lane holds channels of its own row and the
 //     rescaling never leaves the lane.
-// No key splits and no merge: each tile's rows go straight to the output.  The library uses it
-// where tiles are many (the planner's choice); the block-table slice of the tile's keys is staged
-// in LDS whole (at most kTileMaxPages pages).  Per-token and per-block scales only: with static
+// Key splits: with a.nsplit > 1 the workgroup takes split s (keys [s L, (s + 1) L) of the tile's
+// range, L = a.split_len <= 4096) and writes partials that the log-sum-exp merge combines; the
+// rows' causal limits are clamped to the split's last key.  The block-table slice of the split's
+// keys is staged in LDS (at most kTileMaxPages pages).  Per-token and per-block scales only: with static
 // per-channel scales the K scale sits inside each dot product, and folding it into an fp16 query
 // would round it to 11 bits (the int8-score kernel serves those caches).
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 #include "sk_partition.h"
@@ -92,27 +97,37 @@ __device__ __forceinline__ int wave_max(int x) {
     return __builtin_amdgcn_readfirstlane(x);
 }
 
-// Workgroup u takes row tile nrg - 1 - u / (batch * hkv) of pair u % (batch * hkv): the tiles that
-// see the most keys (a chunk's last rows) first.
+// Workgroup u takes split u / V of row tile nrg - 1 - v / (batch * hkv) of pair v % (batch * hkv),
+// v = u % V, V = batch * hkv * nrg: the tiles that see the most keys (a chunk's last rows) first,
+// split-major.  Workgroups go to the XCDs round-robin, so with batch * hkv a multiple of 8 every
+// tile and split of a (sequence, KV head) pair lands on one XCD, whose L2 then serves that pair's
+// keys to all of them (with the splits of a tile adjacent, each XCD would take one key range of
+// every pair instead: about twice the time per block on long prompts).
 template <int MODE>
 __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2))) void decode_tile_kernel(
     DecodeArgs a, int nbh) {
     __shared__ TileShared S;
-    const int u = blockIdx.x;
-    const int item = (u % nbh) * a.nrg + (a.nrg - 1 - u / nbh);
+    const int nv = nbh * a.nrg;
+    const int sp = blockIdx.x / nv;
+    const int v = blockIdx.x % nv;
+    const int item = (v % nbh) * a.nrg + (a.nrg - 1 - v / nbh);
     const ItemGeo it = item_geo<TROWS, false>(a, item);
     if (it.nvalid <= 0) return;  // uniform per workgroup
     const int b = it.b, h = it.h;
-    const int kmax = it.kmax;  // keys [0, kmax): what the tile's last row sees
+    // keys [t0, kmax): this split of what the tile's last row sees (nsplit 1: all of it)
+    const int t0 = sp * a.split_len;
+    if (t0 >= it.kmax) return;  // (uniform; the merge reads no partial past the keys)
+    const int kmax = a.nsplit > 1 ? min(t0 + a.split_len, it.kmax) : it.kmax;
+    const int blk0 = t0 >> a.log2bs;
     const int tid = threadIdx.x;
     const int w = tid / kWave;
     const int lane = tid & (kWave - 1);
     const int n = lane & 15;
     const int g = lane >> 4;
 
-    // ---- the block-table slice of the tile's keys
-    const int npg = ((kmax - 1) >> a.log2bs) + 1;
-    for (int i = tid; i < npg; i += TW * kWave) S.bt[i] = a.bt[(int64_t)b * a.mbs + i];
+    // ---- the block-table slice of the split's keys
+    const int npg = ((kmax - 1) >> a.log2bs) - blk0 + 1;
+    for (int i = tid; i < npg; i += TW * kWave) S.bt[i] = a.bt[(int64_t)b * a.mbs + blk0 + i];
     __syncthreads();
 
     // ---- cooperative loads of the block at T: thread tid takes key T + tid / 4 (bytes 32 (tid % 4)
@@ -124,12 +139,12 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     const int64_t hd = (int64_t)a.bs * TD;  // bytes of one (page, head)
     auto load_raw = [&](int T, TileRaw& R) __attribute__((always_inline)) {
         const int key = min(T + (tid >> 2), kmax - 1);
-        const int64_t pk = (int64_t)S.bt[key >> a.log2bs] * a.hkv + h;
+        const int64_t pk = (int64_t)S.bt[(key >> a.log2bs) - blk0] * a.hkv + h;
         const uint8_t* kp = kbase + pk * hd + (key & (a.bs - 1)) * TD + (tid & 3) * 32;
         R.k0 = load16(kp);
         R.k1 = load16(kp + 16);
         const int tt = min(T + 16 * (tid >> 6), (kmax - 1) & ~15);  // first key of the V tile
-        const int64_t pv = (int64_t)S.bt[tt >> a.log2bs] * a.hkv + h;
+        const int64_t pv = (int64_t)S.bt[(tt >> a.log2bs) - blk0] * a.hkv + h;
         const uint8_t* vp = vbase + pv * hd + ((tt & (a.bs - 1)) >> 4) * (TD * kVTile) + (tid & 63) * 32;
         R.v0 = load16(vp);
         R.v1 = load16(vp + 16);
@@ -162,7 +177,7 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
         }
     };
 
-    // ---- this wave's query rows (B operand of the score MFMA): rows 32w + 16rt + n of the tile;
+    // ---- this wave's query rows (B operand of the score MFMA): rows 64rt + 16w + n of the tile;
     //      lane (n, g) holds channels 32m + 8g .. + 7 of k-step m, scaled by 2^k into fp16's range
     //      (exact: a bf16 value times a power of two fits fp16's 11 significant bits)
     uint32_t qf[2][4][4];
@@ -172,10 +187,11 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     bool rowv[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-        const int j = 32 * w + 16 * rt + n;
+        const int j = 64 * rt + 16 * w + n;
         rowv[rt] = j < it.nvalid;
         const int r = it.r0 + j;
-        lim[rt] = rowv[rt] ? it.prior + r / a.g : 0x7fffffff;
+        // (a split: clamped to its last key, so that the next split's keys are masked like causal ones)
+        lim[rt] = rowv[rt] ? min(it.prior + r / a.g, kmax - 1) : 0x7fffffff;
         float x[32];
         if (rowv[rt]) {
             const uint16_t* qp = a.q + ((int64_t)(it.qrow0 + r / a.g) * a.hq + h * a.g + r % a.g) * TD + 8 * g;
@@ -212,6 +228,8 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     // the wave's lowest and highest causal limits over its valid rows
     const int lim_lo = wave_min(min(lim[0], lim[1]));
     const int lim_hi = wave_max(max(rowv[0] ? lim[0] : -1, rowv[1] ? lim[1] : -1));
+    // whether any of the wave's second 16 rows is a row of the tile (uniform)
+    const bool rt1_live = __builtin_amdgcn_readfirstlane((int)__any(rowv[1])) != 0;
 
     float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
     f4 acc[2][8];
@@ -222,9 +240,10 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     float s_ref = 0.0f, s_inv = 0.0f;
 
 
-    // one block from LDS buffer buf: the wave's 32 rows against its 64 keys, in two halves of 32
-    // keys, each its own online-softmax step
-    auto compute = [&](const int T, const int buf) __attribute__((always_inline)) {
+    // one block from LDS buffer buf: the wave's 32 rows (nrt = 1: its first 16) against its 64 keys,
+    // in two halves of 32 keys, each its own online-softmax step
+    auto compute = [&](const int T, const int buf, auto nrt) __attribute__((always_inline)) {
+        constexpr int NRT = decltype(nrt)::value;
         if (T > lim_hi) return;  // no valid row of the wave sees these keys (uniform)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -234,7 +253,7 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
             // ---------------------------- scores: tile u holds keys T0 + 8g' + 4u + i of row n
             f4 sc[2][2];
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) sc[rt][0] = sc[rt][1] = f4{0.f, 0.f, 0.f, 0.f};
+            for (int rt = 0; rt < NRT; ++rt) sc[rt][0] = sc[rt][1] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int uu = 0; uu < 2; ++uu) {
                 const _Float16* kr = &S.k[buf][32 * hf + 16 * uu + n][8 * g];
@@ -242,7 +261,7 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
                 for (int m = 0; m < 4; ++m) {
                     const th8 av = *reinterpret_cast<const th8*>(kr + 32 * m);
 #pragma unroll
-                    for (int rt = 0; rt < 2; ++rt)
+                    for (int rt = 0; rt < NRT; ++rt)
                         sc[rt][uu] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(th8, qf[rt][m]),
                                                                             sc[rt][uu], 0, 0, 0);
                 }
@@ -273,7 +292,7 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
             uint32_t pb[2][4];
             float factor[2];
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
+            for (int rt = 0; rt < NRT; ++rt) {
                 // y: the score times the key's K scale; the logit (log2 units) is y times the row's
                 // factor rowmul >= 0, which joins the exponent's FMA (and commutes with the max)
                 float y[8];
@@ -308,9 +327,9 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
                 l_run[rt] = l_run[rt] * alpha + row_sum4(ps);
                 factor[rt] = alpha * sf;
             }
-            if (__any(factor[0] != 1.0f || factor[1] != 1.0f)) {
+            if (__any(factor[0] != 1.0f || (NRT > 1 && factor[NRT - 1] != 1.0f))) {
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
+                for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
                     for (int ct = 0; ct < 8; ++ct) acc[rt][ct] *= factor[rt];
             }
@@ -319,7 +338,7 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
             for (int ct = 0; ct < 8; ++ct) {
                 const th8 av = *reinterpret_cast<const th8*>(&S.v[buf][16 * ct + n][32 * hf + 8 * g]);
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
+                for (int rt = 0; rt < NRT; ++rt)
                     acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(th8, pb[rt]),
                                                                          acc[rt][ct], 0, 0, 0);
             }
@@ -329,34 +348,53 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     // ---- the key loop: block k computes from LDS buffer k % 2 while the raw loads of blocks k + 1
     //      (register set (k + 1) % 2) and k + 2 (set k % 2, issued at its start) are in flight; block
     //      k + 1 goes to LDS after block k's compute, then one barrier.  Blocks in pairs, one loop
-    //      exit, so the register sets and buffers are fixed per half of the pair.
-    const int nblk = (kmax + TBLK - 1) / TBLK;
-    TileRaw R0, R1;
-    load_raw(0, R0);
-    load_raw(TBLK, R1);  // (past kmax: in-bounds stand-ins)
-    store_lds(R0, 0, 0);
-    __syncthreads();
-    auto step = [&](const int T, const int buf, TileRaw& Rcur, TileRaw& Rnext) __attribute__((always_inline)) {
-        load_raw(T + 2 * TBLK, Rcur);  // block k + 2 into the set block k came from (already in LDS)
-        compute(T, buf);
-        store_lds(Rnext, buf ^ 1, T + TBLK);  // block k + 1
+    //      exit, so the register sets and buffers are fixed per half of the pair.  The loop is
+    //      written out once per count of live row tiles (the choice is uniform per wave), so that
+    //      each copy gets its own register allocation.
+    const int nblk = (kmax - t0 + TBLK - 1) / TBLK;
+    auto key_loop = [&](auto nrt) __attribute__((always_inline)) {
+        TileRaw R0, R1;
+        load_raw(t0, R0);
+        load_raw(t0 + TBLK, R1);  // (past kmax: in-bounds stand-ins)
+        store_lds(R0, 0, t0);
         __syncthreads();
+        auto step = [&](const int T, const int buf, TileRaw& Rcur, TileRaw& Rnext) __attribute__((always_inline)) {
+            load_raw(T + 2 * TBLK, Rcur);  // block k + 2 into the set block k came from (already in LDS)
+            compute(T, buf, nrt);
+            store_lds(Rnext, buf ^ 1, T + TBLK);  // block k + 1
+            __syncthreads();
+        };
+        int T = t0;
+        for (int i = 1; i < nblk; i += 2) {
+            step(T, 0, R0, R1);
+            step(T + TBLK, 1, R1, R0);
+            T += 2 * TBLK;
+        }
+        if (nblk & 1) compute(T, 0, nrt);
     };
-    int T = 0;
-    for (int i = 1; i < nblk; i += 2) {
-        step(T, 0, R0, R1);
-        step(T + TBLK, 1, R1, R0);
-        T += 2 * TBLK;
-    }
-    if (nblk & 1) compute(T, 0);
+    // (waves of one workgroup may take different copies: both run the same blocks and the same
+    // number of workgroup barriers, which count arrivals, so they stay in step)
+    if (rt1_live)
+        key_loop(std::integral_constant<int, 2>{});
+    else
+        key_loop(std::integral_constant<int, 1>{});
 
-    // ---- normalise and write: lane (n, g) holds channels 16ct + 4g + i of row 32w + 16rt + n
+    // ---- normalise and write: lane (n, g) holds channels 16ct + 4g + i of row 64rt + 16w + n.
+    //      Splits: fp32 partials and base-2 lse, laid out for a merge of 64-row items: half j / 64
+    //      of the tile is item 2 (tile) + j / 64, its row j % 64 of split sp in row
+    //      ((item2 * nsplit + sp) * 64 + j % 64).
+    //      The lane's indices are taken afresh from an opaque copy of the thread id, so that the
+    //      compiler keeps none of the prologue's row offsets live (and spilled) across the loop.
+    const bool split_mode = a.nsplit > 1;
+    int tid_e = tid;
+    asm volatile("" : "+v"(tid_e));
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
         if (!rowv[rt]) continue;
-        const int j = 32 * w + 16 * rt + n;
+        const int j = 64 * rt + 16 * (tid_e / kWave) + (tid_e & 15);
         const int r = it.r0 + j;
         const int64_t orow = (int64_t)(it.qrow0 + r / a.g) * a.hq + h * a.g + r % a.g;
+        const int64_t prow = ((int64_t)(2 * item + (j >> 6)) * a.nsplit + sp) * 64 + (j & 63);
         const float l = l_run[rt];
         const float mul = l > 0.0f ? s_ref / l : 0.0f;
 #pragma unroll
@@ -365,12 +403,23 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
             float o[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = acc[rt][ct][i] * mul;
-            uint2 pk;
-            pk.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
-            pk.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
-            *reinterpret_cast<uint2*>(a.out + orow * TD + c) = pk;
+            if (!split_mode) {
+                uint2 pk;
+                pk.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
+                pk.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
+                *reinterpret_cast<uint2*>(a.out + orow * TD + c) = pk;
+            } else {
+                *reinterpret_cast<f4*>(a.part_o + prow * TD + c) = f4{o[0], o[1], o[2], o[3]};
+            }
         }
-        if (g == 0 && a.lse) a.lse[orow] = l > 0.0f ? (m_ref[rt] + log2f(l)) * kLn2t : -INFINITY;
+        if (g == 0) {
+            const float lse2 = l > 0.0f ? m_ref[rt] + log2f(l) : -INFINITY;
+            if (!split_mode) {
+                if (a.lse) a.lse[orow] = lse2 * kLn2t;
+            } else {
+                a.part_lse[prow] = lse2;
+            }
+        }
     }
 }
 
@@ -379,7 +428,7 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 hipError_t launch_decode_tile(const DecodeArgs& a, int batch, int head_dim, int mode, hipStream_t stream) {
     if (head_dim != TD) return hipErrorInvalidValue;
     const int64_t nbh = (int64_t)batch * a.hkv;
-    const int64_t grid = nbh * a.nrg;
+    const int64_t grid = nbh * a.nrg * a.nsplit;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 gd((unsigned)grid), bd(TW * kWave);
@@ -389,7 +438,13 @@ hipError_t launch_decode_tile(const DecodeArgs& a, int batch, int head_dim, int 
         hipLaunchKernelGGL(decode_tile_kernel<1>, gd, bd, 0, stream, a, (int)nbh);
     else
         return hipErrorInvalidValue;
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    // the partials as 64-row items (two per tile), merged by the decode's log-sum-exp merge
+    DecodeArgs m = a;
+    m.nrg = 2 * a.nrg;
+    m.prs = 64;
+    return launch_merge(m, batch, head_dim, 64, stream);
 }
 
 }  // namespace pkv

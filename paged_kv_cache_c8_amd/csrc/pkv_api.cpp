@@ -95,7 +95,7 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
     // int8-score kernel, whose key splits balance long contexts (64 chunks of up to 16 tokens over
     // up to 16K keys: 444 against 698 us per step).
     if ((!opts || opts->kernel == 0) && kernel == 3 && (mode == 0 || mode == 1) && head_dim == 128 &&
-        mbs <= pkv::kTileMaxPages && !(opts && (opts->window > 0 || opts->split_tokens > 0 || opts->partition != 0))) {
+        !(opts && (opts->window > 0 || opts->split_tokens > 0 || opts->partition != 0))) {
         const int64_t rows_hkv = (int64_t)max_q_len * (hq / hkv);
         const int64_t tiles = (int64_t)batch * hkv * cdiv(rows_hkv, 128);
         if (rows_hkv >= 128 && tiles >= 2LL * device_cus()) kernel = 4;
@@ -107,17 +107,24 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
     p->kernel = kernel;
     p->classes = 1;
     if (kernel == 4) {
-        // one workgroup per 128-row tile over all the keys its rows see: no splits, no workspace
-        if (head_dim != 128 || (mode != 0 && mode != 1) || mbs > pkv::kTileMaxPages) return PKV_ERR_UNSUPPORTED;
-        if (opts && (opts->window > 0 || opts->split_tokens > 0 || opts->partition != 0)) return PKV_ERR_UNSUPPORTED;
+        // one workgroup per 128-row tile and key split; the partials as two 64-row items per tile
+        // for the merge
+        if (head_dim != 128 || (mode != 0 && mode != 1)) return PKV_ERR_UNSUPPORTED;
+        if (opts && (opts->window > 0 || opts->partition != 0)) return PKV_ERR_UNSUPPORTED;
         p->rg = 8;
         p->rows_per_item = 128;
         p->nrg = (int)cdiv(rows, 128);
-        p->prs = (int)(rows < 128 ? rows : 128);
+        p->prs = 64;
         p->sk_waves = 0;
-        p->nsplit = 1;
-        p->split_len = (int)(cdiv((int64_t)mbs * bs, 64) * 64);
-        p->ws_bytes = 0;
+        const int64_t max_ctx = (int64_t)mbs * bs;
+        int64_t L = opts && opts->split_tokens > 0 ? cdiv(opts->split_tokens, 64) * 64 : kMaxSplit;
+        if (L > kMaxSplit) L = kMaxSplit;
+        if (L >= max_ctx) L = cdiv(max_ctx, 64) * 64;
+        if (cdiv(max_ctx, L) > kMaxSplits) return PKV_ERR_UNSUPPORTED;
+        p->split_len = (int)L;
+        p->nsplit = (int)cdiv(max_ctx, L);
+        const int64_t pitems = 2LL * batch * hkv * p->nrg;
+        p->ws_bytes = p->nsplit > 1 ? (size_t)(pitems * p->nsplit * 64) * (size_t)(head_dim + 1) * 4 : 0;
         return PKV_OK;
     }
     if (kernel == 3) {
@@ -480,8 +487,9 @@ int decode_impl(const void* q, int32_t num_q_heads, const pkv_cache_t* cache, co
         a.sk_waves = p.sk_waves;
     } else if (p.nsplit > 1) {
         float* ws = static_cast<float*>(workspace);
+        const int64_t pitems = p.kernel == 4 ? 2 * items : items;  // the tile kernel: two 64-row items per tile
         a.part_o = ws;
-        a.part_lse = ws + items * p.nsplit * p.prs * cache->head_dim;
+        a.part_lse = ws + pitems * p.nsplit * p.prs * cache->head_dim;
     }
     a.prs = p.prs;
     hipStream_t st_ = static_cast<hipStream_t>(stream);

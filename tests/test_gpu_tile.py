@@ -2,8 +2,9 @@
 head), each 64-key block loaded once per workgroup and shared through LDS) with the oracle.
 
 Cases: whole prompts and chunks after a prior, per-token and per-block scales, tiles partly filled, one and
-sixteen query heads per KV head, block-edge lengths, a sequence with no query; softmax scales 0 and
-negative; query rows with an outlier channel; arguments the kernel does not serve.  Same bars as
+sixteen query heads per KV head, block-edge lengths, a sequence with no query; key splits (contexts
+past 4096 keys, forced split sizes, splits that start inside a page) merged by the log-sum-exp merge;
+softmax scales 0 and negative; query rows with an outlier channel; arguments the kernel does not serve.  Same bars as
 test_gpu_parity (attention 1e-2, lse 1e-4 + 1e-5 |lse| + the fp32 evaluation bound)."""
 import numpy as np
 import pytest
@@ -49,6 +50,31 @@ def test_tile_kernel_matches_oracle(case):
     out, lse = r.decode(kernel=TILE)
     max_abs, rel = r.assert_decode_close(out, lse, ref)
     print(f"  tile mode {mode} bs {bs} g {g}: max_abs={max_abs:.2e} rel={rel:.2e}")
+
+
+SPLIT_CASES = [
+    # mode, BS, G, context lengths, q_lens, KV heads, split_tokens (0: the planner's 4096 past 4096 keys)
+    (1, 16, 5, [5000, 9000, 300, 4097], [16, 9, 3, 1], 2, 0),   # chunk-sized queries on long contexts
+    (0, 16, 4, [4500, 70], [300, 70], 1, 0),                     # a prompt chunk over 2 splits
+    (0, 16, 4, [9000, 4000], [600, 300], 2, 2048),               # long prompt chunks, 5 splits
+    (0, 16, 4, [1200, 700, 40], [400, 700, 3], 2, 64),           # one 64-key block per split
+    (1, 16, 5, [1200, 700, 40], [400, 700, 3], 2, 256),
+    (1, 16, 6, [3000, 1000, 0], [128, 16, 0], 2, 1024),          # and a sequence with no key
+    (1, 128, 8, [1000, 129], [600, 129], 1, 64),                 # splits that start inside a page
+    (0, 64, 1, [2000, 65, 1], [2000, 65, 1], 2, 100),            # rounded up to 128 keys
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES)
+def test_tile_kernel_key_splits_match_oracle(case):
+    mode, bs, g, ctx, ql, hkv, split = case
+    r = Run(_wl(mode, bs, g, ctx, ql, hkv=hkv, seed=sum(ctx) + 11 * mode + split))
+    r.store_prior()
+    r.store_new()
+    ref = r.oracle_decode(nthreads=16)
+    out, lse = r.decode(kernel=TILE, split_tokens=split)
+    max_abs, rel = r.assert_decode_close(out, lse, ref)
+    print(f"  tile splits {split or 'auto'} mode {mode} bs {bs} g {g}: max_abs={max_abs:.2e} rel={rel:.2e}")
 
 
 @pytest.mark.parametrize("case", [c for c in SCALE_CASES if c[0] in (0, 1) and c[1] == 128])
@@ -121,6 +147,6 @@ def test_tile_kernel_rejects_what_it_does_not_serve():
             r.decode(kernel=TILE)
     w = _wl(0, 16, 4, [300], [300], seed=3)
     r = Run(w, with_oracle=False)
-    for kw in (dict(window=128), dict(split_tokens=256), dict(partition=1)):
+    for kw in (dict(window=128), dict(partition=1)):
         with pytest.raises(pkv.PkvError):
             r.decode(kernel=TILE, **kw)
