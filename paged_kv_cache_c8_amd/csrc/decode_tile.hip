@@ -25,6 +25,7 @@
 // keys is staged in LDS (at most kTileMaxPages pages).  Per-token and per-block scales only: with static
 // per-channel scales the K scale sits inside each dot product, and folding it into an fp16 query
 // would round it to 11 bits (the int8-score kernel serves those caches).
+#include <cstddef>
 #include <type_traits>
 
 #include "pkv_device.h"
@@ -38,6 +39,8 @@ typedef _Float16 th8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float tf2 __attribute__((ext_vector_type(2)));
 typedef _Float16 th2 __attribute__((ext_vector_type(2)));
+typedef const float __attribute__((address_space(3))) lds_cf;  // LDS pointers (32-bit)
+typedef const f4 __attribute__((address_space(3))) lds_cf4;
 
 constexpr int TD = 128;          // head dim
 constexpr int TW = 4;            // waves per workgroup
@@ -54,6 +57,8 @@ struct __align__(16) TileShared {
     float vs[2][TBLK];         // per-key V scale (0 past the keys)
     int bt[kTileMaxPages];     // the tile's block-table slice
 };
+static_assert(offsetof(TileShared, vs) == offsetof(TileShared, ks) + 2 * TBLK * sizeof(float),
+              "the V scales follow the K scales");
 
 // the raw loads of one block by one thread: 32 K codes (a quarter of a key row), 32 V codes (two
 // channel rows of a 16-slot tile) and one scale
@@ -267,10 +272,14 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
                 }
             }
             // ---------------------------- logits (log2 units) of keys T0 + 8g + e, their V scales
-            const f4 k0 = *reinterpret_cast<const f4*>(&S.ks[buf][32 * hf + 8 * g]);
-            const f4 k1 = *reinterpret_cast<const f4*>(&S.ks[buf][32 * hf + 8 * g + 4]);
-            const f4 v0 = *reinterpret_cast<const f4*>(&S.vs[buf][32 * hf + 8 * g]);
-            const f4 v1 = *reinterpret_cast<const f4*>(&S.vs[buf][32 * hf + 8 * g + 4]);
+            //      (one LDS base made opaque here, so that the four reads take immediate offsets
+            //      from it rather than sixteen precomputed addresses held across the key loop)
+            lds_cf* sp = (lds_cf*)&S.ks[0][8 * g];
+            asm volatile("" : "+v"(sp));
+            const f4 k0 = *(lds_cf4*)(sp + buf * TBLK + 32 * hf);
+            const f4 k1 = *(lds_cf4*)(sp + buf * TBLK + 32 * hf + 4);
+            const f4 v0 = *(lds_cf4*)(sp + (2 + buf) * TBLK + 32 * hf);
+            const f4 v1 = *(lds_cf4*)(sp + (2 + buf) * TBLK + 32 * hf + 4);
             const float kss[8] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
             const float vss[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
             // ---------------------------- V-scale reference (the same for every row of the wave)
