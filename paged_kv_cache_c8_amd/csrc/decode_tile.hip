@@ -20,9 +20,10 @@
 //   * O^T (channels x rows) += V^T . P^T, so that every lane holds channels of its own row and the
 //     rescaling never leaves the lane.
 // Key splits: with a.nsplit > 1 the workgroup takes split s (keys [s L, (s + 1) L) of the tile's
-// range, L = a.split_len <= 4096) and writes partials that the log-sum-exp merge combines; the
-// rows' causal limits are clamped to the split's last key.  The block-table slice of the split's
-// keys is staged in LDS (at most kTileMaxPages pages).  Per-token and per-block scales only: with static
+// range, L = a.split_len) and writes partials that the log-sum-exp merge combines; the
+// rows' causal limits are clamped to the split's last key.  Each thread loads the two block-table
+// entries its loads of a block need one block ahead of those loads (no table slice in LDS, no
+// limit on the context).  Per-token and per-block scales only: with static
 // per-channel scales the K scale sits inside each dot product, and folding it into an fp16 query
 // would round it to 11 bits (the int8-score kernel serves those caches).
 #include <cstddef>
@@ -55,7 +56,6 @@ struct __align__(16) TileShared {
     _Float16 v[2][TD][VP];     // V codes of the block, channel-major
     float ks[2][TBLK];         // per-key K scale (0 past the keys)
     float vs[2][TBLK];         // per-key V scale (0 past the keys)
-    int bt[kTileMaxPages];     // the tile's block-table slice
 };
 static_assert(offsetof(TileShared, vs) == offsetof(TileShared, ks) + 2 * TBLK * sizeof(float),
               "the V scales follow the K scales");
@@ -65,6 +65,11 @@ static_assert(offsetof(TileShared, vs) == offsetof(TileShared, ks) + 2 * TBLK * 
 struct TileRaw {
     u32x4 k0, k1, v0, v1;
     float s;
+};
+
+// the block-table entries of one thread's loads of a block: the page of its key (K) and of its V tile
+struct TilePg {
+    int k, v;
 };
 
 // eight int8 codes (two dwords) -> eight fp16 values, exactly: the byte permute makes 1152 + code,
@@ -123,17 +128,11 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     const int t0 = sp * a.split_len;
     if (t0 >= it.kmax) return;  // (uniform; the merge reads no partial past the keys)
     const int kmax = a.nsplit > 1 ? min(t0 + a.split_len, it.kmax) : it.kmax;
-    const int blk0 = t0 >> a.log2bs;
     const int tid = threadIdx.x;
     const int w = tid / kWave;
     const int lane = tid & (kWave - 1);
     const int n = lane & 15;
     const int g = lane >> 4;
-
-    // ---- the block-table slice of the split's keys
-    const int npg = ((kmax - 1) >> a.log2bs) - blk0 + 1;
-    for (int i = tid; i < npg; i += TW * kWave) S.bt[i] = a.bt[(int64_t)b * a.mbs + blk0 + i];
-    __syncthreads();
 
     // ---- cooperative loads of the block at T: thread tid takes key T + tid / 4 (bytes 32 (tid % 4)
     //      .. of its K row), channels 2 (tid % 64), + 1 of V tile tid / 64, and (tid % 4 < 2) the
@@ -142,14 +141,21 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k);
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v);
     const int64_t hd = (int64_t)a.bs * TD;  // bytes of one (page, head)
-    auto load_raw = [&](int T, TileRaw& R) __attribute__((always_inline)) {
+    const int32_t* btrow = a.bt + (int64_t)b * a.mbs;
+    auto load_pg = [&](int T, TilePg& P) __attribute__((always_inline)) {
         const int key = min(T + (tid >> 2), kmax - 1);
-        const int64_t pk = (int64_t)S.bt[(key >> a.log2bs) - blk0] * a.hkv + h;
+        const int tt = min(T + 16 * (tid >> 6), (kmax - 1) & ~15);  // first key of the V tile
+        P.k = btrow[key >> a.log2bs];
+        P.v = btrow[tt >> a.log2bs];
+    };
+    auto load_raw = [&](int T, const TilePg& P, TileRaw& R) __attribute__((always_inline)) {
+        const int key = min(T + (tid >> 2), kmax - 1);
+        const int64_t pk = (int64_t)P.k * a.hkv + h;
         const uint8_t* kp = kbase + pk * hd + (key & (a.bs - 1)) * TD + (tid & 3) * 32;
         R.k0 = load16(kp);
         R.k1 = load16(kp + 16);
         const int tt = min(T + 16 * (tid >> 6), (kmax - 1) & ~15);  // first key of the V tile
-        const int64_t pv = (int64_t)S.bt[(tt >> a.log2bs) - blk0] * a.hkv + h;
+        const int64_t pv = (int64_t)P.v * a.hkv + h;
         const uint8_t* vp = vbase + pv * hd + ((tt & (a.bs - 1)) >> 4) * (TD * kVTile) + (tid & 63) * 32;
         R.v0 = load16(vp);
         R.v1 = load16(vp + 16);
@@ -356,27 +362,37 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 
     // ---- the key loop: block k computes from LDS buffer k % 2 while the raw loads of blocks k + 1
     //      (register set (k + 1) % 2) and k + 2 (set k % 2, issued at its start) are in flight; block
-    //      k + 1 goes to LDS after block k's compute, then one barrier.  Blocks in pairs, one loop
-    //      exit, so the register sets and buffers are fixed per half of the pair.  The loop is
-    //      written out once per count of live row tiles (the choice is uniform per wave), so that
-    //      each copy gets its own register allocation.
+    //      k + 1 goes to LDS after block k's compute, then one barrier.  The block-table entries of
+    //      block k + 3 are loaded at the start of block k, before its raw loads, so that waiting
+    //      for them (at block k + 1) never waits for raw loads issued after them.  Blocks in pairs,
+    //      one loop exit, so the register sets and buffers are fixed per half of the pair.  The
+    //      loop is written out once per count of live row tiles (the choice is uniform per wave),
+    //      so that each copy gets its own register allocation.
     const int nblk = (kmax - t0 + TBLK - 1) / TBLK;
     auto key_loop = [&](auto nrt) __attribute__((always_inline)) {
         TileRaw R0, R1;
-        load_raw(t0, R0);
-        load_raw(t0 + TBLK, R1);  // (past kmax: in-bounds stand-ins)
+        TilePg P0, P1;
+        // (in the order a step leaves them outstanding: entries of block k + 2, then the raw
+        // loads of block k + 1, so that the loop's wait counts hold from its first trip)
+        load_pg(t0, P0);
+        load_pg(t0 + TBLK, P1);
+        load_raw(t0, P0, R0);
+        load_pg(t0 + 2 * TBLK, P0);
+        load_raw(t0 + TBLK, P1, R1);  // (past kmax: in-bounds stand-ins)
         store_lds(R0, 0, t0);
         __syncthreads();
-        auto step = [&](const int T, const int buf, TileRaw& Rcur, TileRaw& Rnext) __attribute__((always_inline)) {
-            load_raw(T + 2 * TBLK, Rcur);  // block k + 2 into the set block k came from (already in LDS)
+        auto step = [&](const int T, const int buf, TileRaw& Rcur, TileRaw& Rnext, TilePg& Pcur, TilePg& Pnext)
+                        __attribute__((always_inline)) {
+            load_pg(T + 3 * TBLK, Pnext);       // block k + 3's entries (set k + 1's were used)
+            load_raw(T + 2 * TBLK, Pcur, Rcur);  // block k + 2 into the set block k came from (already in LDS)
             compute(T, buf, nrt);
             store_lds(Rnext, buf ^ 1, T + TBLK);  // block k + 1
             __syncthreads();
         };
         int T = t0;
         for (int i = 1; i < nblk; i += 2) {
-            step(T, 0, R0, R1);
-            step(T + TBLK, 1, R1, R0);
+            step(T, 0, R0, R1, P0, P1);
+            step(T + TBLK, 1, R1, R0, P1, P0);
             T += 2 * TBLK;
         }
         if (nblk & 1) compute(T, 0, nrt);

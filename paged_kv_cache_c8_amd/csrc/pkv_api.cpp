@@ -108,7 +108,8 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
     p->classes = 1;
     if (kernel == 4) {
         // one workgroup per 128-row tile and key split; the partials as two 64-row items per tile
-        // for the merge
+        // for the merge.  No splits where the tiles alone fill the GPU twice (prompts: splits only
+        // add partials), splits of 4096 keys where they do not and a context exceeds 4096
         if (head_dim != 128 || (mode != 0 && mode != 1)) return PKV_ERR_UNSUPPORTED;
         if (opts && (opts->window > 0 || opts->partition != 0)) return PKV_ERR_UNSUPPORTED;
         p->rg = 8;
@@ -117,8 +118,10 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
         p->prs = 64;
         p->sk_waves = 0;
         const int64_t max_ctx = (int64_t)mbs * bs;
-        int64_t L = opts && opts->split_tokens > 0 ? cdiv(opts->split_tokens, 64) * 64 : kMaxSplit;
-        if (L > kMaxSplit) L = kMaxSplit;
+        const int64_t tiles = (int64_t)batch * hkv * cdiv(rows, 128);
+        int64_t L = opts && opts->split_tokens > 0 ? cdiv(opts->split_tokens, 64) * 64
+                                                   : (tiles >= 2LL * device_cus() ? max_ctx : kMaxSplit);
+        if (opts && opts->split_tokens > 0 && L > kMaxSplit) L = kMaxSplit;
         if (L >= max_ctx) L = cdiv(max_ctx, 64) * 64;
         if (cdiv(max_ctx, L) > kMaxSplits) return PKV_ERR_UNSUPPORTED;
         p->split_len = (int)L;

@@ -134,10 +134,9 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int batch, int head_dim, int 
 // int8 cache (modes 0, 1): classes = subset classes per column tile (1, 2, 4), row_tiles = 1 or 2
 hipError_t launch_decode_c8(const DecodeArgs& a, int batch, int head_dim, int classes, int row_tiles,
                             int mode, hipStream_t stream);
-// Many query rows per KV head (prompts, multi-token chunks): one workgroup per 128-row tile and key
-// split of at most 4096 keys, key blocks shared through LDS (decode_tile.hip); head_dim 128, int8
-// modes 0 and 1, no window.  A split's block-table slice: at most kTileMaxPages pages.
-constexpr int kTileMaxPages = 4096 / 16 + 8;
+// Many query rows per KV head (prompts, multi-token chunks): one workgroup per 128-row tile (and key
+// split, where tiles are few), key blocks shared through LDS (decode_tile.hip); head_dim 128, int8
+// modes 0 and 1, no window.
 hipError_t launch_decode_tile(const DecodeArgs& a, int batch, int head_dim, int mode, hipStream_t stream);
 // resident waves per compute unit of the balanced-partition kernel (0: not available)
 int decode_c8_waves_per_cu(int head_dim, int classes, int row_tiles, int mode, int batch, bool windowed);

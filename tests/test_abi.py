@@ -63,18 +63,21 @@ def test_plan_is_deterministic_and_bounded(pkv):
     assert pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 2, kernel=3)["kernel"] == 2
     assert pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 0, kernel=1)["kernel"] == 1
     assert pkv.decode_plan(2, 8, 2, 64, 7, 16, 1, 0, kernel=2)["kernel"] == 2
-    # the tile kernel: int8 pages, head_dim 128, no window; contexts of at most 4096 keys in one
-    # pass with no workspace, longer ones (or forced splits) in key splits of 4096 (forced: rounded up
-    # to 64, at most 4096) whose partials are two 64-row items per 128-row tile
+    # the tile kernel: int8 pages, head_dim 128, no window; one pass over each tile's keys with no
+    # workspace where the tiles fill the GPU twice (prompts), whatever the context; otherwise, and
+    # past 4096 keys, key splits of 4096 (forced: rounded up to 64, at most 4096) whose partials are
+    # two 64-row items per 128-row tile
     tile = pkv.decode_plan(4, 32, 8, 128, 128, 16, 2048, 0, kernel=4)
     assert tile["kernel"] == 4 and tile["num_splits"] == 1
     assert pkv.decode_plan(4, 32, 8, 128, 128, 16, 2048, 1, kernel=4)["kernel"] == 4
     assert pkv.decode_workspace_size(4, 32, _py_cache(pkv), 128, max_q_len=2048, kernel=4) == 0
-    long = pkv.decode_plan(4, 32, 8, 128, 1153, 16, 2048, 0, kernel=4)  # 18448 keys
-    assert long["split_tokens"] == 4096 and long["num_splits"] == 5
-    tiles = 4 * 8 * (2048 * 4 // 128)
-    assert pkv.decode_workspace_size(4, 32, _py_cache(pkv), 1153, max_q_len=2048, kernel=4) == \
-        2 * tiles * 5 * 64 * (128 + 1) * 4
+    long = pkv.decode_plan(4, 32, 8, 128, 1153, 16, 2048, 0, kernel=4)  # 2048 tiles, 18448 keys
+    assert long["num_splits"] == 1 and long["split_tokens"] == 18496
+    assert pkv.decode_workspace_size(4, 32, _py_cache(pkv), 1153, max_q_len=2048, kernel=4) == 0
+    few = pkv.decode_plan(1, 8, 8, 128, 1153, 16, 16, 0, kernel=4)  # 8 tiles
+    assert few["split_tokens"] == 4096 and few["num_splits"] == 5
+    assert pkv.decode_workspace_size(1, 8, _py_cache(pkv), 1153, max_q_len=16, kernel=4) == \
+        2 * 8 * 5 * 64 * (128 + 1) * 4
     forced = pkv.decode_plan(4, 32, 8, 128, 128, 16, 2048, 0, kernel=4, split_tokens=100)
     assert forced["split_tokens"] == 128 and forced["num_splits"] == 16
     capped = pkv.decode_plan(4, 32, 8, 128, 1153, 16, 2048, 0, kernel=4, split_tokens=100000)

@@ -3,7 +3,8 @@ head), each 64-key block loaded once per workgroup and shared through LDS) with 
 
 Cases: whole prompts and chunks after a prior, per-token and per-block scales, tiles partly filled, one and
 sixteen query heads per KV head, block-edge lengths, a sequence with no query; key splits (contexts
-past 4096 keys, forced split sizes, splits that start inside a page) merged by the log-sum-exp merge;
+past 4096 keys with few tiles, forced split sizes, splits that start inside a page) merged by the
+log-sum-exp merge; a long prompt in one pass per tile;
 softmax scales 0 and negative; query rows with an outlier channel; arguments the kernel does not serve.  Same bars as
 test_gpu_parity (attention 1e-2, lse 1e-4 + 1e-5 |lse| + the fp32 evaluation bound)."""
 import numpy as np
@@ -53,7 +54,8 @@ def test_tile_kernel_matches_oracle(case):
 
 
 SPLIT_CASES = [
-    # mode, BS, G, context lengths, q_lens, KV heads, split_tokens (0: the planner's 4096 past 4096 keys)
+    # mode, BS, G, context lengths, q_lens, KV heads, split_tokens (0: the planner's; these few tiles
+    # take splits of 4096 past 4096 keys)
     (1, 16, 5, [5000, 9000, 300, 4097], [16, 9, 3, 1], 2, 0),   # chunk-sized queries on long contexts
     (0, 16, 4, [4500, 70], [300, 70], 1, 0),                     # a prompt chunk over 2 splits
     (0, 16, 4, [9000, 4000], [600, 300], 2, 2048),               # long prompt chunks, 5 splits
@@ -129,6 +131,25 @@ def test_tile_kernel_matches_int8_score_kernel_on_the_prefill_workload():
     r.store_new()
     o3, l3 = r.decode(kernel=3)
     o4, l4 = r.decode(kernel=TILE)
+    a, b = o3.float(), o4.float()
+    err = (a - b).abs()
+    assert torch.all(err <= 2e-2 + 2e-2 * a.abs()), float(err.max())
+    assert torch.allclose(l3, l4, rtol=1e-4, atol=1e-3), float((l3 - l4).abs().max())
+
+
+def test_tile_kernel_unsplit_long_prompt_matches_int8_score_kernel():
+    """One prompt of 8192 tokens (2048 tiles, enough to fill the GPU: one pass over up to 8192 keys
+    per tile, no key splits, the block-table entries loaded per thread) on both kernels, every
+    element within the attention bar of the other."""
+    w = gen.make_config(5, prompt_len=8192)
+    plan = pkv.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_blocks_per_seq,
+                           w.block_size, w.max_q_len, w.quant_mode)
+    assert plan["kernel"] == TILE and plan["num_splits"] == 1
+    r = Run(w, with_oracle=False)
+    r.store_prior()
+    r.store_new()
+    o3, l3 = r.decode(kernel=3)
+    o4, l4 = r.decode()
     a, b = o3.float(), o4.float()
     err = (a - b).abs()
     assert torch.all(err <= 2e-2 + 2e-2 * a.abs()), float(err.max())
