@@ -196,6 +196,7 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     const float sgn = a.scale_log2 < 0.0f ? -1.0f : 1.0f;  // a negative scale flips the query
     int lim[2];       // last key the row sees (invalid rows: none masked, nothing written)
     bool rowv[2];
+    u32x4 qraw[2][4];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
         const int j = 64 * rt + 16 * w + n;
@@ -203,19 +204,33 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
         const int r = it.r0 + j;
         // (a split: clamped to its last key, so that the next split's keys are masked like causal ones)
         lim[rt] = rowv[rt] ? min(it.prior + r / a.g, kmax - 1) : 0x7fffffff;
+        // (loaded unconditionally, so that nothing waits for them before the conversion: a row
+        // past the tile's rows reads its last row, in bounds, and is zeroed below)
+        const int rq = it.r0 + min(j, it.nvalid - 1);
+        const uint16_t* qp = a.q + ((int64_t)(it.qrow0 + rq / a.g) * a.hq + h * a.g + rq % a.g) * TD + 8 * g;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) qraw[rt][m] = load16(qp + 32 * m);
+    }
+    // ---- the key loop's first loads, issued behind the query's: the block-table entries of blocks
+    //      0 and 1 travel with the query rows, and the raw loads of blocks 0 and 1 (then block 2's
+    //      entries) fly while the query is converted.  The order is the one a step of the loop
+    //      leaves outstanding (entries of block k + 2, then the raw loads of block k + 1), so that
+    //      the loop's wait counts hold from its first trip.
+    TileRaw R0, R1;
+    TilePg P0, P1;
+    load_pg(t0, P0);
+    load_pg(t0 + TBLK, P1);
+    load_raw(t0, P0, R0);
+    load_pg(t0 + 2 * TBLK, P0);
+    load_raw(t0 + TBLK, P1, R1);  // (past kmax: in-bounds stand-ins)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const float sq = rowv[rt] ? sgn : 0.0f;
         float x[32];
-        if (rowv[rt]) {
-            const uint16_t* qp = a.q + ((int64_t)(it.qrow0 + r / a.g) * a.hq + h * a.g + r % a.g) * TD + 8 * g;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const u32x4 v = load16(qp + 32 * m);
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[8 * m + e] = sgn * bf16_at(v, e);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 32; ++e) x[e] = 0.0f;
-        }
+            for (int e = 0; e < 8; ++e) x[8 * m + e] = sq * bf16_at(qraw[rt][m], e);
         float mx = 0.0f;
 #pragma unroll
         for (int e = 0; e < 32; ++e) mx = fmaxf(mx, fabsf(x[e]));
@@ -369,18 +384,9 @@ __global__ __launch_bounds__(TW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     //      loop is written out once per count of live row tiles (the choice is uniform per wave),
     //      so that each copy gets its own register allocation.
     const int nblk = (kmax - t0 + TBLK - 1) / TBLK;
+    store_lds(R0, 0, t0);
+    __syncthreads();
     auto key_loop = [&](auto nrt) __attribute__((always_inline)) {
-        TileRaw R0, R1;
-        TilePg P0, P1;
-        // (in the order a step leaves them outstanding: entries of block k + 2, then the raw
-        // loads of block k + 1, so that the loop's wait counts hold from its first trip)
-        load_pg(t0, P0);
-        load_pg(t0 + TBLK, P1);
-        load_raw(t0, P0, R0);
-        load_pg(t0 + 2 * TBLK, P0);
-        load_raw(t0 + TBLK, P1, R1);  // (past kmax: in-bounds stand-ins)
-        store_lds(R0, 0, t0);
-        __syncthreads();
         auto step = [&](const int T, const int buf, TileRaw& Rcur, TileRaw& Rnext, TilePg& Pcur, TilePg& Pnext)
                         __attribute__((always_inline)) {
             load_pg(T + 3 * TBLK, Pnext);       // block k + 3's entries (set k + 1's were used)
