@@ -108,8 +108,10 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
     p->classes = 1;
     if (kernel == 4) {
         // one workgroup per 128-row tile and key split; the partials as two 64-row items per tile
-        // for the merge.  No splits where the tiles alone fill the GPU twice (prompts: splits only
-        // add partials), splits of 4096 keys where they do not and a context exceeds 4096
+        // for the merge.  No splits where the tiles fill two rounds of the GPU's workgroups (two
+        // per CU; prompts: splits would only add partials, and the longest tiles start first),
+        // splits of 4096 keys where they do not and a context exceeds 4096 (one round of tiles
+        // would wait on its longest: 698 against 443 us on the chunked multi-token decode)
         if (head_dim != 128 || (mode != 0 && mode != 1)) return PKV_ERR_UNSUPPORTED;
         if (opts && (opts->window > 0 || opts->partition != 0)) return PKV_ERR_UNSUPPORTED;
         p->rg = 8;
@@ -120,7 +122,7 @@ int make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t 
         const int64_t max_ctx = (int64_t)mbs * bs;
         const int64_t tiles = (int64_t)batch * hkv * cdiv(rows, 128);
         int64_t L = opts && opts->split_tokens > 0 ? cdiv(opts->split_tokens, 64) * 64
-                                                   : (tiles >= 2LL * device_cus() ? max_ctx : kMaxSplit);
+                                                   : (tiles >= 4LL * device_cus() ? max_ctx : kMaxSplit);
         if (opts && opts->split_tokens > 0 && L > kMaxSplit) L = kMaxSplit;
         if (L >= max_ctx) L = cdiv(max_ctx, 64) * 64;
         if (cdiv(max_ctx, L) > kMaxSplits) return PKV_ERR_UNSUPPORTED;

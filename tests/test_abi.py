@@ -76,6 +76,8 @@ def test_plan_is_deterministic_and_bounded(pkv):
     assert pkv.decode_workspace_size(4, 32, _py_cache(pkv), 1153, max_q_len=2048, kernel=4) == 0
     few = pkv.decode_plan(1, 8, 8, 128, 1153, 16, 16, 0, kernel=4)  # 8 tiles
     assert few["split_tokens"] == 4096 and few["num_splits"] == 5
+    one_round = pkv.decode_plan(64, 40, 8, 128, 1024, 16, 16, 1, kernel=4)  # 512 tiles: one round
+    assert one_round["split_tokens"] == 4096 and one_round["num_splits"] == 4
     assert pkv.decode_workspace_size(1, 8, _py_cache(pkv), 1153, max_q_len=16, kernel=4) == \
         2 * 8 * 5 * 64 * (128 + 1) * 4
     forced = pkv.decode_plan(4, 32, 8, 128, 128, 16, 2048, 0, kernel=4, split_tokens=100)
