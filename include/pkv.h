@@ -247,9 +247,11 @@ typedef struct {
                              per KV head (prompts, multi-token chunks): one workgroup per
                              128 rows of a (sequence, KV head), each 64-key block loaded
                              once per workgroup and shared through LDS, fp16 scores;
-                             contexts above 4096 keys (or split_tokens > 0) in key splits
-                             with a log-sum-exp merge (per-token or per-block int8 caches,
-                             head_dim 128, no window, partition 0; otherwise
+                             one pass over each tile's keys where the tiles fill two rounds
+                             of the GPU's workgroups (4 per CU), else contexts above 4096
+                             keys (and split_tokens > 0 always) in key splits with a
+                             log-sum-exp merge and a workspace (per-token or per-block int8
+                             caches, head_dim 128, no window, partition 0; otherwise
                              PKV_ERR_UNSUPPORTED) */
     int32_t partition;    /* how the keys are cut into work (kernels 3 and 2):
                              0 = planned: kernel 3 takes the balanced partition for
