@@ -64,6 +64,8 @@ SPLIT_CASES = [
     (1, 16, 6, [3000, 1000, 0], [128, 16, 0], 2, 1024),          # and a sequence with no key
     (1, 128, 8, [1000, 129], [600, 129], 1, 64),                 # splits that start inside a page
     (0, 64, 1, [2000, 65, 1], [2000, 65, 1], 2, 100),            # rounded up to 128 keys
+    (1, 32, 4, [6000, 100, 4096], [40, 100, 33], 2, 0),          # 32-slot pages, per-block scales
+    (0, 64, 8, [2500, 2600, 17], [16, 2600, 17], 1, 512),        # 64-slot pages, eight heads per KV head
 ]
 
 
